@@ -1,0 +1,200 @@
+"""Pins of the oracle's elementwise pieces and of its decode step.
+
+Sources: gemma4-12b card architecture notes (dual RoPE: sliding theta 1e4 on
+all pairs, full theta 1e6 on the first 64 of 256 pairs; attention_k_eq_v with
+a scale-free V RMSNorm; layer_scalar; tied embeddings; final softcap).  The
+readings the pages leave open are "parity unpinned" against a real model and
+pinned here only by invariants and by special cases that reduce to library
+routines (torch rms_norm, gelu, numpy matmul/tanh).
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from int4_q4_gemv_amd import synth, bytemodel
+
+GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "page_numbers.json")))
+
+
+# ---------------------------------------------------------------- RoPE ----
+def test_rope_identity_at_zero_and_norm_preserving(orc):
+    rng = np.random.default_rng(0)
+    x = rng.normal(0, 1, 256)
+    assert np.array_equal(orc.rope(x, 0, 1e4, 128), x)
+    for pos in (1, 77, 131071):
+        y = orc.rope(x, pos, 1e4, 128)
+        pairs = lambda z: z[:128] ** 2 + z[128:] ** 2
+        assert np.allclose(pairs(y), pairs(x), rtol=1e-12)
+
+
+def test_rope_first_pair_turns_by_position_radians(orc):
+    D = 512
+    for pos in (1, 3, 1000, 131071):
+        e0 = np.zeros(D); e0[0] = 1.0
+        y = orc.rope(e0, pos, 1e6, 64)
+        assert np.isclose(y[0], np.cos(pos), atol=1e-12) and np.isclose(y[256], np.sin(pos), atol=1e-12)
+        assert np.count_nonzero(y) <= 2
+
+
+def test_rope_relative_position_property(orc):
+    rng = np.random.default_rng(1)
+    q, k = rng.normal(0, 1, 256), rng.normal(0, 1, 256)
+    for a, b, c in ((5, 2, 100), (1000, 10, 7), (131071, 131000, -5000)):
+        d1 = orc.rope(q, a, 1e4, 128) @ orc.rope(k, b, 1e4, 128)
+        d2 = orc.rope(q, a + c, 1e4, 128) @ orc.rope(k, b + c, 1e4, 128)
+        assert np.isclose(d1, d2, rtol=1e-8, atol=1e-8)
+
+
+def test_rope_proportional_leaves_nope_pairs(orc):
+    rng = np.random.default_rng(2)
+    x = rng.normal(0, 1, 512)
+    y = orc.rope(x, 12345, 1e6, 64)
+    assert np.array_equal(y[64:256], x[64:256]) and np.array_equal(y[320:], x[320:])
+    assert not np.array_equal(y[:64], x[:64])
+
+
+# ------------------------------------------------------------- RMSNorm ----
+def test_rmsnorm_matches_torch(orc):
+    rng = np.random.default_rng(3)
+    x = rng.normal(0, 3, 384)
+    w = rng.normal(1, 0.1, 384).astype(np.float32)
+    got = orc.rmsnorm(x, w, 1e-6)
+    ref = torch.nn.functional.rms_norm(torch.tensor(x), (384,), torch.tensor(w, dtype=torch.float64), eps=1e-6)
+    assert np.allclose(got, ref.numpy(), rtol=1e-13)
+    unit = orc.rmsnorm(x * 1000, None, 0.0)
+    assert np.isclose(np.sqrt(np.mean(unit ** 2)), 1.0, rtol=1e-13)
+    assert np.array_equal(orc.rmsnorm(np.zeros(8), None, 1e-6), np.zeros(8))
+
+
+def test_gelu_and_softcap_match_library(orc):
+    xs = np.linspace(-8, 8, 101)
+    ref = torch.nn.functional.gelu(torch.tensor(xs), approximate="tanh").numpy()
+    assert np.allclose([orc.gelu_tanh(x) for x in xs], ref, rtol=1e-13, atol=1e-15)
+    for z in (-1e4, -31.0, -1.0, 0.0, 0.5, 29.0, 1e4):
+        s = orc.softcap(z, 30.0)
+        assert np.isclose(s, 30.0 * np.tanh(z / 30.0), rtol=1e-14) and abs(s) <= 30.0
+
+
+# ---------------------------------------------------------- byte model ----
+def test_byte_model_reproduces_page_numbers():
+    g = GOLD["kv_bytes"]
+    per_tok = bytemodel.cache_bytes(8, 1, 1, 1, 512)
+    assert per_tok == g["global_bytes_per_token"]
+    assert bytemodel.cache_bytes(40, 1, 8, 1024, 256) == g["ring_1024_bytes"] == 0.3125 * 2 ** 30
+    assert round(bytemodel.cache_bytes(40, 1, 8, 2048, 256) / 1e6) == g["ring_2048_mb"]
+    assert int(bytemodel.cache_bytes(40, 1, 8, 1024, 256) / 1e6) == g["ring_1024_mb"]
+    assert (g["tier_large"] - g["tier_small"]) * per_tok == g["tier_gap_bytes"]
+    assert bytemodel.cache_bytes(48, 1, 8, 1, 512) == g["dense2in_bytes_per_token"]
+    assert round(4096 * g["dense2in_bytes_per_token"] / 1e9, 2) == g["dense2in_gb_at_4096"]
+    assert round(131072 * per_tok / 1e9, 3) == g["full_8_layers_gb_at_131072"]
+    assert round(bytemodel.cache_bytes(40, 1, 8, 1024, 256) / 1e9, 3) == g["sliding_40_layers_gb"]
+    assert bytemodel.cache_bytes(1, 16, 1, 512, pair=False) == g["full_q_bytes"]
+    cfg = synth.FULL48
+    assert bytemodel.full_pos_bytes(cfg) * bytemodel.n_full(cfg) == per_tok
+    # ~7 GB per token: int4 body plus an int4 vocab table
+    int4_head = bytemodel.q4_matrix_bytes(cfg.vocab, cfg.hidden)
+    assert round((bytemodel.weight_bytes(cfg) + int4_head) / 1e9) == GOLD["weights"]["gb_per_token_int4_about"]
+    assert bytemodel.weight_bytes(cfg) == 6_131_220_480
+    assert bytemodel.step_bytes(cfg, 32767) == 9_016_901_632
+    assert bytemodel.step_bytes(cfg, 131071) == 10_627_514_368
+
+
+# --------------------------------------------------------- decode step ----
+def build_oracle_model(orc, cfg, seed, ctx, zero_out_mats=False, last_scalar=None):
+    layers = []
+    for l in range(cfg.n_layers):
+        lp = synth.layer_params(cfg, l, seed)
+        blocks = {}
+        for name, w in lp.mats.items():
+            if zero_out_mats and name in ("wo", "wd"):
+                w = torch.zeros_like(w)
+            blocks[name] = orc.q4_pack(w.numpy())
+        k, v = synth.layer_cache(cfg, l, seed, ctx)
+        scal = lp.layer_scalar
+        if last_scalar is not None and l == cfg.n_layers - 1:
+            scal = last_scalar
+        layers.append(orc.OracleLayer(
+            is_full=cfg.is_full(l), v_norm=cfg.is_full(l) or cfg.sl_v_norm,
+            wq=blocks["wq"], wk=blocks["wk"], wv=blocks.get("wv"), wo=blocks["wo"],
+            wg=blocks["wg"], wu=blocks["wu"], wd=blocks["wd"],
+            attn_norm=lp.norms["attn_norm"].numpy(), q_norm=lp.norms["q_norm"].numpy(),
+            k_norm=lp.norms["k_norm"].numpy(), post_attn_norm=lp.norms["post_attn_norm"].numpy(),
+            pre_ff_norm=lp.norms["pre_ff_norm"].numpy(), post_ff_norm=lp.norms["post_ff_norm"].numpy(),
+            layer_scalar=scal, k_cache=synth.f16_bits(k).copy(), v_cache=synth.f16_bits(v).copy()))
+    return orc.OracleModel(
+        hidden=cfg.hidden, n_heads=cfg.n_heads, inter=cfg.inter, vocab=cfg.vocab,
+        sl_kv_heads=cfg.sl_kv_heads, sl_head_dim=cfg.sl_head_dim, full_head_dim=cfg.full_head_dim,
+        window=cfg.window, ring=cfg.ring, full_cap=cfg.full_cap,
+        sl_theta=cfg.sl_theta, full_theta=cfg.full_theta,
+        sl_rot_pairs=cfg.sl_rot_pairs, full_rot_pairs=cfg.full_rot_pairs,
+        sl_scale=cfg.sl_scale, full_scale=cfg.full_scale, eps=cfg.eps, softcap=cfg.softcap,
+        embed=synth.f16_bits(synth.embed_table(cfg, seed)),
+        final_norm=synth.final_norm(cfg, seed).numpy(), layers=layers)
+
+
+def clone(model):
+    import copy
+    m = copy.copy(model)
+    m.layers = [copy.copy(L) for L in model.layers]
+    for L in m.layers:
+        L.k_cache = L.k_cache.copy()
+        L.v_cache = L.v_cache.copy()
+    return m
+
+
+def test_verify_block_equals_sequential_steps(orc):
+    cfg = synth.TOY
+    m = build_oracle_model(orc, cfg, 0, 200)
+    toks = synth.tokens(cfg, 4, 0)
+    a = clone(m)
+    blk, am_blk = a.decode_step(toks, 200)
+    b = clone(m)
+    for i in range(4):
+        one, am = b.decode_step(toks[i:i + 1], 200 + i)
+        assert np.array_equal(one[0], blk[i]) and am[0] == am_blk[i]
+    for La, Lb in zip(a.layers, b.layers):
+        assert np.array_equal(La.k_cache, Lb.k_cache) and np.array_equal(La.v_cache, Lb.v_cache)
+
+
+def test_stateful_steps_equal_stateless_recompute(orc):
+    cfg = synth.TOY
+    m = build_oracle_model(orc, cfg, 1, 0)   # empty caches
+    toks = synth.tokens(cfg, 9, 1)
+    seq = clone(m)
+    for i in range(9):
+        last, _ = seq.decode_step(toks[i:i + 1], i)
+    full, _ = clone(m).decode_step(toks, 0)   # whole prefix in one call
+    assert np.allclose(last[0], full[-1], rtol=0, atol=1e-12)
+
+
+def test_zero_last_layer_scalar_gives_zero_logits(orc):
+    cfg = synth.TOY
+    m = build_oracle_model(orc, cfg, 2, 150, last_scalar=0.0)
+    logits, am = m.decode_step(synth.tokens(cfg, 1, 2), 150)
+    assert np.all(logits == 0.0) and am[0] == 0
+
+
+def test_identity_layers_reduce_to_embedding_head(orc):
+    """With zero output and down projections every layer leaves h alone, so
+    the logits are softcap(E . fp16(rms_norm(E[tok] * sqrt(H), w_final)))."""
+    cfg = synth.TOY
+    m = build_oracle_model(orc, cfg, 3, 120, zero_out_mats=True)
+    tok = synth.tokens(cfg, 2, 3)
+    logits, am = m.decode_step(tok, 120)
+    E = m.embed.view(np.float16).astype(np.float64)
+    h = torch.tensor(E[tok] * np.sqrt(cfg.hidden))
+    x = torch.nn.functional.rms_norm(h, (cfg.hidden,), torch.tensor(m.final_norm, dtype=torch.float64), eps=cfg.eps)
+    x16 = x.numpy().astype(np.float16).astype(np.float64)
+    ref = cfg.softcap * np.tanh((x16 @ E.T) / cfg.softcap)
+    assert np.allclose(logits, ref, rtol=1e-12, atol=1e-12)
+    assert np.array_equal(am, np.argmax(ref, axis=1))
+
+
+def test_logits_bounded_by_softcap(orc):
+    cfg = synth.TOY
+    m = build_oracle_model(orc, cfg, 4, 60)
+    logits, _ = m.decode_step(synth.tokens(cfg, 1, 4), 60)
+    assert np.all(np.abs(logits) < cfg.softcap) and np.isfinite(logits).all()
