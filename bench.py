@@ -1,0 +1,215 @@
+#!/usr/bin/env python3
+"""Benchmark: batch-1 48-layer decode step (12B shapes, int4 q4_0 weights,
+fp16 KV) at context 32768 on one MI355X.
+
+Prints ONE JSON line.  `value` = decode tokens/s (one token per step, inputs
+resident in HBM).  Extra fields: whole-step achieved HBM bandwidth from the
+algorithmic byte model, the dominant kernel's roofline (the batch-1 q4 GEMV
+at 12B shapes, timed live with HIP events on its stream), context-131072 and
+width-4 verify figures, and the CPU oracle timed on the host cores on a
+bounded sample.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--mode full|gemv|step]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_GBPS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--mode", default="full", choices=["full", "gemv", "step"])
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    return ap.parse_args()
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def time_gemv(q4, torch, model, reps=3):
+    """Average launch time of the batch-1 q4 GEMV at 12B shapes: the gate and
+    up matrices of all 48 layers (3.2 GB, so every launch streams from HBM),
+    captured once into a graph and replayed back to back between two HIP
+    events on the current stream (so host launch cost is not timed)."""
+    cfg = model.cfg
+    N, K = cfg.inter, cfg.hidden
+    g = q4.Gemv(N, K, 1)
+    x = torch.randn(1, K, device="cuda", generator=torch.Generator("cuda").manual_seed(7)).half()
+    y = torch.empty(1, N, device="cuda")
+    mats = [L[nm] for L in model.layers for nm in ("wg", "wu")]
+    for m in mats[:8]:
+        g(m, x, y)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=torch.cuda.current_stream()):
+        for m in mats:
+            g(m, x, y)
+    graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        graph.replay()
+    e1.record()
+    e1.synchronize()
+    launches = reps * len(mats)
+    avg_s = e0.elapsed_time(e1) * 1e-3 / launches
+    return avg_s, launches, q4.packed_bytes(N, K)
+
+
+def time_steps(torch, model, toks, pos, steps, warmup):
+    for i in range(warmup):
+        model.step(toks[i % len(toks)], pos, want_logits=False)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(steps):
+        model.step(toks[i % len(toks)], pos, want_logits=False)
+    e1.record()
+    e1.synchronize()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e-3
+
+
+def cpu_baseline(model, torch):
+    """The oracle on the host cores, on a bounded sample of the same workload:
+    layer 0 (sliding) and layer 5 (full, context 32768) of the same weights,
+    plus the vocab head; per-token time = 40 t_sliding + 8 t_full + t_head."""
+    import numpy as np
+    import oracle
+    from int4_q4_gemv_amd import synth
+    cfg = model.cfg
+    seed = 5
+    blk = {}
+    for l in (0, 5):
+        lp = synth.layer_params(cfg, l, seed, device="cuda")
+        blk[l] = {n: oracle.q4_pack(w.cpu().numpy()) for n, w in lp.mats.items()}
+        del lp
+    f16 = lambda t: t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16).copy()
+    emb = f16(model.embed)
+
+    def om(ls):
+        layers = []
+        for l in ls:
+            L = model.layers[l]
+            layers.append(oracle.OracleLayer(
+                is_full=bool(L["is_full"]), v_norm=bool(L["v_norm"]), wq=blk[l]["wq"], wk=blk[l]["wk"],
+                wv=blk[l].get("wv"), wo=blk[l]["wo"], wg=blk[l]["wg"], wu=blk[l]["wu"], wd=blk[l]["wd"],
+                attn_norm=L["attn_norm"].cpu().numpy(), q_norm=L["q_norm"].cpu().numpy(),
+                k_norm=L["k_norm"].cpu().numpy(), post_attn_norm=L["post_attn_norm"].cpu().numpy(),
+                pre_ff_norm=L["pre_ff_norm"].cpu().numpy(), post_ff_norm=L["post_ff_norm"].cpu().numpy(),
+                layer_scalar=1.0, k_cache=f16(L["k_cache"]), v_cache=f16(L["v_cache"])))
+        return oracle.OracleModel(
+            hidden=cfg.hidden, n_heads=cfg.n_heads, inter=cfg.inter, vocab=cfg.vocab,
+            sl_kv_heads=cfg.sl_kv_heads, sl_head_dim=cfg.sl_head_dim, full_head_dim=cfg.full_head_dim,
+            window=cfg.window, ring=cfg.ring, full_cap=cfg.full_cap, sl_theta=cfg.sl_theta,
+            full_theta=cfg.full_theta, sl_rot_pairs=cfg.sl_rot_pairs, full_rot_pairs=cfg.full_rot_pairs,
+            sl_scale=cfg.sl_scale, full_scale=cfg.full_scale, eps=cfg.eps, softcap=cfg.softcap,
+            embed=emb, final_norm=model.final_norm.cpu().numpy(), layers=layers)
+
+    tok = [1234]
+    pos = 32767
+    m_s, m_sf = om([0]), om([0, 5])
+    x = np.zeros((1, cfg.hidden), np.uint16)
+    t = time.perf_counter(); oracle.f16_gemv(emb, x); t_h = time.perf_counter() - t
+    t = time.perf_counter(); m_s.decode_step(tok, pos, want_logits=False); t_c = time.perf_counter() - t
+    t = time.perf_counter(); m_sf.decode_step(tok, pos, want_logits=False); t_a = time.perf_counter() - t
+    t_s = max(t_c - t_h, 1e-9)
+    t_f = max(t_a - t_c, 1e-9)
+    per_tok = 40 * t_s + 8 * t_f + t_h
+    return {"value": 1.0 / per_tok, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": ("one decode step of layer 0 (sliding) and of layers 0+5 (full, ctx 32768) of the "
+                       "same 12B-shape weights plus one vocab-head product; tokens/s = 1/(40 t_sliding + "
+                       "8 t_full + t_head)"),
+            "t_sliding_s": t_s, "t_full_s": t_f, "t_head_s": t_h,
+            "wall_s": t_h + t_c + t_a}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (this build has no multi-GPU path); got --gpus {args.gpus}",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import int4_q4_gemv_amd as q4
+    from int4_q4_gemv_amd import bytemodel, synth
+    from dataclasses import replace
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    ctx_hi = 131072
+    cfg = replace(synth.FULL48, full_cap=ctx_hi + 8)
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        t0 = time.perf_counter()
+        log("building the 48-layer model on the GPU ...")
+        model = q4.build_decode_model(cfg, 5, ctx_hi - 1, device="cuda", gen_device="cuda")
+        torch.cuda.synchronize()
+        log(f"model ready in {time.perf_counter() - t0:.1f} s")
+        toks = [[int(t)] for t in synth.tokens(cfg, 64, 5)]
+        out = {}
+        if args.mode in ("full", "gemv"):
+            avg_s, launches, nbytes = time_gemv(q4, torch, model)
+            ach = nbytes / avg_s / 1e9
+            out["roofline"] = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_GBPS, "unit": "GB/s",
+                               "frac": round(ach / PEAK_GBPS, 4), "traffic": None,
+                               "kernel": "k_q4_gemv<1,0,16> (q4_gemv, B=1, 3840->15360)",
+                               "bytes_per_launch": nbytes, "avg_launch_us": round(avg_s * 1e6, 3),
+                               "launches": launches}
+            log(f"q4_gemv 3840->15360: {avg_s * 1e6:.2f} us/launch, {ach:.0f} GB/s")
+            if args.mode == "gemv":
+                print(json.dumps(out))
+                return
+        pos = 32767
+        secs = time_steps(torch, model, toks, pos, args.steps, args.warmup)
+        ms = secs * 1e3 / args.steps
+        tok_s = args.steps / secs
+        step_bytes = bytemodel.step_bytes(cfg, pos)
+        log(f"decode ctx 32768: {ms:.3f} ms/step, {tok_s:.1f} tok/s")
+        extra = {}
+        if args.mode == "full":
+            k2 = max(5, args.steps // 5)
+            s131 = time_steps(torch, model, toks, ctx_hi - 1, k2, 2)
+            extra["ctx131072"] = {"ms_per_step": round(s131 * 1e3 / k2, 4),
+                                  "tokens_per_s": round(k2 / s131, 2),
+                                  "achieved_GBps": round(bytemodel.step_bytes(cfg, ctx_hi - 1) * k2 / s131 / 1e9, 1)}
+            blocks = [[int(t) for t in synth.tokens(cfg, 4, 50 + i)] for i in range(8)]
+            sv = time_steps(torch, model, blocks, 32764, k2, 2)
+            extra["verify4_ctx32768"] = {"ms_per_block": round(sv * 1e3 / k2, 4),
+                                         "rows_per_s": round(4 * k2 / sv, 2),
+                                         "achieved_GBps": round(step_bytes * k2 / sv / 1e9, 1)}
+            log(f"ctx 131072: {extra['ctx131072']}; verify4: {extra['verify4_ctx32768']}")
+    res = {
+        "metric": "decode tokens/s (batch 1, 48 layers) + achieved HBM GB/s as % of peak",
+        "value": round(tok_s, 2), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "int4(q4_0) x f16 -> f32", "data": "synthetic",
+        "config": {"workload": "48-layer 12B-shape decode step (40 sliding + 8 full layers), batch 1, "
+                               "context 32768 (every timed step decodes position 32767)",
+                   "layers": 48, "hidden": 3840, "inter": 15360, "vocab": 262144, "ctx": 32768,
+                   "batch": 1, "window": 1024, "ring": 2048},
+        "step_hbm": {"algorithmic_bytes": step_bytes,
+                     "achieved_GBps": round(step_bytes / (ms * 1e-3) / 1e9, 1),
+                     "frac_of_peak": round(step_bytes / (ms * 1e-3) / 1e9 / PEAK_GBPS, 4)},
+    }
+    res.update(out)
+    res.update(extra)
+    if args.mode == "full" and not args.no_cpu:
+        log("timing the CPU oracle on a bounded sample ...")
+        res["cpu_baseline"] = cpu_baseline(model, torch)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,219 @@
+/*
+ * q4dec.h -- C ABI of the MI355X (gfx950) int4 q4_0 decode-step library.
+ *
+ * The library computes the batch-1 (or width-4 speculative verify) decode step
+ * of a Gemma-4-12B-style dense decoder that interleaves sliding-window and full
+ * attention layers:
+ *   - a weight-streaming matrix-vector product over per-block-32 absmax
+ *     symmetric int4 weights on the q4_0 grid [-8, 7] with one fp16 scale per
+ *     block (gemma4-12b card, intro: q4_0 = per-block-32 absmax symmetric int4;
+ *     gemma-4-E4B-CoreAI card, Provenance: symmetric with clipping);
+ *   - flash-decode attention over a sliding-window ring of R slots, where slot
+ *     j holds implied position p = q - ((q - j) mod R) and is admitted only if
+ *     q - p < W (Gemma-4-12B-CoreAI card, "v5/ -- ring extent R = 2W"), and
+ *     over a full-attention cache with one KV head whose value is the raw key
+ *     projection after a scale-free RMSNorm (gemma4-12b card, architecture
+ *     notes: attention_k_eq_v; "The fix": mask-free GQA flash decode, scale 1).
+ *
+ * Conventions (every entry point):
+ *   - Pointers marked "device" are HIP device pointers; "host" pointers are
+ *     read during the call only.  The library keeps no pointer after a call
+ *     returns, except the captured decode-step graphs (see q4dec_release).
+ *   - The library never allocates device memory; workspaces come from the
+ *     caller.  All work is enqueued on `stream` (a hipStream_t; NULL is the
+ *     default stream) and calls never synchronise the device.
+ *   - Argument checks are synchronous and host-only: on a non-zero status no
+ *     kernel has been launched.  A failed launch returns Q4_EHIP.
+ *   - fp16 values are IEEE binary16 bit patterns in uint16_t.
+ *   - Device pointers must be 16-byte aligned (Q4_EALIGN otherwise).
+ */
+#ifndef Q4DEC_H
+#define Q4DEC_H
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int q4_status;
+#define Q4_OK        0
+#define Q4_EINVAL   -1   /* null pointer where one is required, bad enum      */
+#define Q4_ESHAPE   -2   /* unsupported or inconsistent sizes                  */
+#define Q4_EALIGN   -3   /* device pointer not 16-byte aligned                 */
+#define Q4_ERANGE   -4   /* position / capacity / window out of range          */
+#define Q4_ENOSPACE -5   /* buffer or workspace smaller than required          */
+#define Q4_EHIP     -6   /* a HIP runtime call or kernel launch failed         */
+
+/* Human-readable name of a status code (static string). */
+const char* q4dec_status_str(q4_status s);
+/* Library version string (static). */
+const char* q4dec_version(void);
+
+/* ------------------------------------------------------------------------ */
+/* q4_0 packing                                                              */
+/* ------------------------------------------------------------------------ */
+enum { Q4_F32 = 0, Q4_BF16 = 1 };
+
+/* Bytes of the packed form of an [N, K] matrix: ceil(N/64)*64 * K/32 * 18.
+ * Returns 0 when K is not a positive multiple of 32 or N < 1. */
+size_t q4_packed_bytes(int N, int K);
+
+/* Quantises W (device, row-major [N, K], fp32 or bf16) onto the q4_0 grid
+ * (gemma4-12b card, intro; gemma-4-E4B-CoreAI card, Provenance): for each row
+ * and block of 32 weights, d = fp16_rne(absmax / 8) and
+ * q = clamp(round_half_away(w / d), -8, 7) with w / d an IEEE fp32 quotient
+ * taken against the stored fp16 scale (d == 0 gives q = 0).
+ * `packed` (device, packed_bytes >= q4_packed_bytes(N, K)) receives the
+ * device layout: 64-row tiles; codes [tile][K/32][64 rows][16 B] followed by
+ * scales [tile][K/32][64 rows] fp16; rows past N are zero.
+ * `nonfinite` (device int32, may be NULL) is incremented once per block that
+ * holds a non-finite weight or whose scale overflows fp16 (such blocks get
+ * d = 0 and q = 0); it is data-dependent, so it is read after a sync.
+ * Errors: Q4_EINVAL (null w/packed, bad dtype), Q4_ESHAPE (N < 1, K % 32),
+ * Q4_ENOSPACE (packed_bytes too small), Q4_EALIGN, Q4_EHIP. */
+q4_status q4_pack(const void* w, int w_dtype, int N, int K, void* packed,
+                  size_t packed_bytes, int32_t* nonfinite, void* stream);
+
+/* Exports the packed matrix in the canonical q4_0 block format (test and
+ * interchange use): `blocks` (device) receives N*K/32 blocks of 18 bytes,
+ * row-major [N][K/32]; each block is the fp16 scale (little endian) followed
+ * by 16 code bytes, byte j holding element j (low nibble) and element j+16
+ * (high nibble) as q + 8. */
+q4_status q4_unpack(const void* packed, int N, int K, uint8_t* blocks, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* int4 matrix-vector product                                                */
+/* ------------------------------------------------------------------------ */
+/* Workspace bytes q4_gemv needs for an [N, K] matrix and B rows. */
+size_t q4_gemv_workspace_size(int N, int K, int B);
+
+/* y[b][n] = sum_k (d * q)[n][k] * x[b][k] for b < B, fp32 accumulation
+ * (the weight stream of the decode step; gemma4-12b card, Throughput:
+ * "decode is otherwise weight-bandwidth-bound").
+ * packed: device, from q4_pack(N, K).  x: device fp16 [B][K].  y: device fp32
+ * [B][N].  B in 1..4 (4 = the width-4 verify block; B > 1 runs on MFMA).
+ * ws: device workspace of q4_gemv_workspace_size(N, K, B) bytes; it must be
+ * zero-filled before its first use and every completed call leaves it
+ * zero-filled again.  Calls sharing one workspace must not overlap.
+ * Errors: Q4_EINVAL, Q4_ESHAPE (K % 32, B outside 1..4), Q4_ENOSPACE,
+ * Q4_EALIGN, Q4_EHIP. */
+q4_status q4_gemv(const void* packed, int N, int K, const uint16_t* x, int B,
+                  float* y, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* flash-decode attention                                                    */
+/* ------------------------------------------------------------------------ */
+/* Workspace bytes for flash_decode_full / flash_decode_ring. */
+size_t flash_decode_workspace_size(int n_seq, int n_rows, int Hq, int D);
+
+/* Full-attention flash decode (gemma4-12b card, "The fix": one global KV head,
+ * every written key attended, fp32 online softmax; split-K over positions with
+ * a log-sum-exp combine).  For sequence s and row i (position pos0[s] + i):
+ *   out[s][i][h] = sum_t softmax_t(scale * q[s][i][h] . k[s][t]) v[s][t],
+ *   t in [0, pos0[s] + i]   (row i of a verify block is causal).
+ * q: device fp16 [n_seq][n_rows][Hq][D].  k, v: device fp16, sequence s at
+ * k + s*seq_stride, rows [cap][D] (one KV head).  pos0: host int32 [n_seq].
+ * out: device fp32 [n_seq][n_rows][Hq][D].  Hq in 1..16, D in {64,128,256,512},
+ * n_rows in 1..4, n_seq in 1..64.
+ * Errors: Q4_ERANGE if pos0[s] < 0 or pos0[s] + n_rows - 1 >= cap;
+ * Q4_ESHAPE, Q4_EINVAL, Q4_ENOSPACE, Q4_EALIGN, Q4_EHIP. */
+q4_status flash_decode_full(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                            int64_t seq_stride, int cap, int Hq, int D,
+                            const int32_t* pos0, int n_seq, int n_rows, float scale,
+                            float* out, void* ws, size_t ws_bytes, void* stream);
+
+/* Sliding-window flash decode over a ring (Gemma-4-12B-CoreAI card, "v5/ --
+ * ring extent R = 2W"; gemma-4-E4B-CoreAI card, ring/: written, causal,
+ * in-window slots).  Row i of sequence s sits at position P = pos0[s] + i and
+ * attends the slots j whose implied position p = P - ((P - j) mod R) satisfies
+ * p >= 0 and P - p < W, i.e. positions max(0, P-W+1) .. P at slots p mod R.
+ * Query head h reads KV head h / (Hq / Hkv).
+ * q: device fp16 [n_seq][n_rows][Hq][D].  k_ring, v_ring: device fp16,
+ * sequence s at +s*seq_stride, [Hkv][R][D].  pos0: host int32 [n_seq].
+ * out: device fp32 [n_seq][n_rows][Hq][D].  Hq % Hkv == 0, Hq/Hkv <= 16.
+ * Errors: Q4_ERANGE if W < 1, W > R, R < W + n_rows - 1 (the rows of a
+ * verify block written after row i must stay outside row i's window) or
+ * pos0[s] < 0; Q4_ESHAPE, Q4_EINVAL, Q4_ENOSPACE, Q4_EALIGN, Q4_EHIP. */
+q4_status flash_decode_ring(const uint16_t* q, const uint16_t* k_ring, const uint16_t* v_ring,
+                            int64_t seq_stride, int Hq, int Hkv, int D, int R, int W,
+                            const int32_t* pos0, int n_seq, int n_rows, float scale,
+                            float* out, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* decode step                                                               */
+/* ------------------------------------------------------------------------ */
+/* One decoder layer.  Weight pointers are device buffers produced by q4_pack
+ * with the shapes given in q4dec_model; norm vectors are device fp32. */
+typedef struct q4dec_layer {
+  int32_t is_full;              /* 1: full attention layer; 0: sliding ring layer   */
+  int32_t v_norm;               /* 1: scale-free RMSNorm on the V rows              */
+  const void* wq;               /* [Hq*D, hidden]                                    */
+  const void* wk;               /* [Hkv*D, hidden]; full layers: Hkv = 1             */
+  const void* wv;               /* [Hkv*D, hidden]; NULL on full layers (V = raw k)  */
+  const void* wo;               /* [hidden, Hq*D]                                    */
+  const void* wg;               /* [inter, hidden]                                   */
+  const void* wu;               /* [inter, hidden]                                   */
+  const void* wd;               /* [hidden, inter]                                   */
+  const float* attn_norm;       /* [hidden] */
+  const float* q_norm;          /* [D]      */
+  const float* k_norm;          /* [D]      */
+  const float* post_attn_norm;  /* [hidden] */
+  const float* pre_ff_norm;     /* [hidden] */
+  const float* post_ff_norm;    /* [hidden] */
+  float layer_scalar;           /* h <- h * layer_scalar at the end of the layer    */
+  uint16_t* k_cache;            /* fp16; sliding [Hkv][R][D]; full [full_cap][D]     */
+  uint16_t* v_cache;            /* same shape as k_cache                             */
+} q4dec_layer;
+
+typedef struct q4dec_model {
+  int32_t hidden, n_heads, inter, vocab, n_layers;
+  int32_t sl_kv_heads, sl_head_dim, full_head_dim;
+  int32_t window, ring, full_cap;
+  int32_t sl_rot_pairs, full_rot_pairs;  /* pairs (i, i+D/2), i < rot_pairs, rotate */
+  double sl_theta, full_theta;           /* RoPE bases (1e4 sliding, 1e6 full)         */
+  float sl_scale, full_scale;            /* softmax scales (1.0 on the pages)          */
+  float eps;                             /* RMSNorm epsilon                            */
+  float softcap;                         /* final logit softcap c: c * tanh(z / c)     */
+  const uint16_t* embed;                 /* device fp16 [vocab][hidden], tied head      */
+  const float* final_norm;               /* device fp32 [hidden]                        */
+  const q4dec_layer* layers;             /* host array [n_layers]                       */
+} q4dec_model;
+
+/* Workspace bytes decode_step needs for `m` and n rows. */
+size_t decode_step_workspace_size(const q4dec_model* m, int n);
+
+/* Runs n rows (tokens[i] at position pos0 + i) through the model: embedding
+ * times sqrt(hidden); per layer RMSNorm, q/k/v projections, per-head q/k
+ * RMSNorm and dual RoPE (gemma4-12b card, architecture notes), fp16 K/V
+ * written at ring slot P mod R or full row P, flash-decode attention, output
+ * projection with post-norm residual, gated-GELU MLP with post-norm
+ * residual, h *= layer_scalar; then final RMSNorm, the tied fp16 head and the
+ * softcap.  All n rows' K/V are written before any row attends; row i sees
+ * positions <= pos0 + i only.
+ * tokens: host int32 [n].  logits: device fp32 [n][vocab] or NULL.
+ * argmax: device int32 [n] or NULL (greedy id, lowest index on ties).
+ * ws: device workspace of decode_step_workspace_size(m, n) bytes.
+ * The first call for a given (model, caches, n, ws, outputs, stream) captures a
+ * HIP graph of the step; later calls replay it (positions and tokens are read
+ * on the device, so one graph serves every position).
+ * Errors: Q4_ERANGE (pos0 < 0; pos0 + n - 1 >= full_cap; R < W + n - 1;
+ * token outside [0, vocab)); Q4_ESHAPE (n outside 1..4 or unsupported
+ * dimensions); Q4_EINVAL; Q4_ENOSPACE; Q4_EALIGN; Q4_EHIP. */
+q4_status decode_step(const q4dec_model* m, const int32_t* tokens, int n, int pos0,
+                      float* logits, int32_t* argmax, void* ws, size_t ws_bytes,
+                      void* stream);
+
+/* Same step without graph capture (every kernel launched directly). */
+q4_status decode_step_eager(const q4dec_model* m, const int32_t* tokens, int n, int pos0,
+                            float* logits, int32_t* argmax, void* ws, size_t ws_bytes,
+                            void* stream);
+
+/* Destroys every captured decode-step graph.  Call before freeing buffers a
+ * graph refers to if the same addresses may be reused for a different model. */
+q4_status q4dec_release(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* Q4DEC_H */

@@ -1,0 +1,66 @@
+"""Shared helpers for the GPU parity tests (comparison bar, oracle models)."""
+import numpy as np
+import torch
+
+# Tolerance on fp32-accumulated outputs: |gpu - oracle| <= ATOL + RTOL * |oracle|
+ATOL = 2e-3
+RTOL = 1e-3
+
+
+def assert_close(gpu, ref, atol=ATOL, rtol=RTOL, what=""):
+    g = gpu.detach().double().cpu().numpy() if torch.is_tensor(gpu) else np.asarray(gpu, np.float64)
+    r = np.asarray(ref, dtype=np.float64)
+    assert g.shape == r.shape, (what, g.shape, r.shape)
+    assert np.isfinite(g).all(), f"{what}: non-finite GPU output"
+    err = np.abs(g - r)
+    bound = atol + rtol * np.abs(r)
+    bad = err > bound
+    if bad.any():
+        i = np.unravel_index(np.argmax(err - bound), err.shape)
+        raise AssertionError(f"{what}: {bad.sum()} of {bad.size} outside tolerance; worst at {i}: "
+                             f"gpu {g[i]!r} oracle {r[i]!r}")
+
+
+def f16bits(t):
+    return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def oracle_model_from_device(orc, cfg, gm, blocks):
+    """Oracle model over the same inputs as the GPU model ``gm``: the oracle's
+    own q4_0 blocks (``blocks[l][name]``, packed by the oracle from the fp32
+    weights), host copies of the norms, table and caches."""
+    layers = []
+    for l, L in enumerate(gm.layers):
+        layers.append(orc.OracleLayer(
+            is_full=bool(L["is_full"]), v_norm=bool(L["v_norm"]),
+            wq=blocks[l]["wq"], wk=blocks[l]["wk"], wv=blocks[l].get("wv"), wo=blocks[l]["wo"],
+            wg=blocks[l]["wg"], wu=blocks[l]["wu"], wd=blocks[l]["wd"],
+            attn_norm=L["attn_norm"].cpu().numpy(), q_norm=L["q_norm"].cpu().numpy(),
+            k_norm=L["k_norm"].cpu().numpy(), post_attn_norm=L["post_attn_norm"].cpu().numpy(),
+            pre_ff_norm=L["pre_ff_norm"].cpu().numpy(), post_ff_norm=L["post_ff_norm"].cpu().numpy(),
+            layer_scalar=float(L["layer_scalar"]),
+            k_cache=f16bits(L["k_cache"]).copy(), v_cache=f16bits(L["v_cache"]).copy()))
+    return orc.OracleModel(
+        hidden=cfg.hidden, n_heads=cfg.n_heads, inter=cfg.inter, vocab=cfg.vocab,
+        sl_kv_heads=cfg.sl_kv_heads, sl_head_dim=cfg.sl_head_dim, full_head_dim=cfg.full_head_dim,
+        window=cfg.window, ring=cfg.ring, full_cap=cfg.full_cap,
+        sl_theta=cfg.sl_theta, full_theta=cfg.full_theta,
+        sl_rot_pairs=cfg.sl_rot_pairs, full_rot_pairs=cfg.full_rot_pairs,
+        sl_scale=cfg.sl_scale, full_scale=cfg.full_scale, eps=cfg.eps, softcap=cfg.softcap,
+        embed=f16bits(gm.embed), final_norm=gm.final_norm.cpu().numpy(), layers=layers)
+
+
+def check_argmax(gpu_logits, gpu_argmax, ref_logits, tol_margin):
+    """The greedy id is unique only where the oracle's top-2 margin is clear;
+    otherwise it must be a valid near-maximum.  Always: the GPU id is the
+    lowest index of the GPU logits' maximum."""
+    gl = gpu_logits.detach().cpu().numpy()
+    ga = gpu_argmax.detach().cpu().numpy()
+    for i in range(ga.shape[0]):
+        assert ga[i] == int(np.argmax(gl[i])), "argmax is not the first maximum of the logits"
+        r = ref_logits[i]
+        top = np.sort(r)[-2:]
+        if top[1] - top[0] > tol_margin:
+            assert ga[i] == int(np.argmax(r)), (i, ga[i], int(np.argmax(r)))
+        else:
+            assert r[ga[i]] >= top[1] - tol_margin

@@ -1,0 +1,94 @@
+"""The C-ABI library loads and exports every entry point include/q4dec.h
+declares; host-side argument checks reject bad calls before any HIP work.
+No compute call is made here (this runs without a GPU)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+import int4_q4_gemv_amd as q4
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "q4dec.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\**\s+([a-z_0-9]+)\s*\(", src, re.M)))
+
+
+def test_header_declares_the_boundary():
+    fns = declared_functions()
+    for name in ("q4_pack", "q4_gemv", "flash_decode_full", "flash_decode_ring", "decode_step"):
+        assert name in fns
+    assert set(fns) == set(q4.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = q4.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_status_strings_and_sizes():
+    L = q4.lib()
+    assert L.q4dec_status_str(0) == b"Q4_OK"
+    for s in (-1, -2, -3, -4, -5, -6):
+        assert L.q4dec_status_str(s).startswith(b"Q4_E")
+    assert q4.packed_bytes(3840, 15360) == 33_177_600
+    assert q4.packed_bytes(100, 64) == 128 * 2 * 18        # rows padded to the 64-row tile
+    assert q4.packed_bytes(10, 48) == 0                     # K not a multiple of 32
+    assert L.q4_gemv_workspace_size(3840, 15360, 5) == 0    # B outside 1..4
+    assert L.flash_decode_workspace_size(1, 1, 16, 96) == 0  # unsupported head_dim
+
+
+def test_argument_checks_fail_before_launch():
+    L = q4.lib()
+    fake = C.c_void_p(0x10000)      # never dereferenced: every call below fails its checks
+    odd = C.c_void_p(0x10008)
+    assert L.q4_pack(None, 0, 64, 64, fake, 1 << 20, None, None) == q4.Q4_EINVAL
+    assert L.q4_pack(fake, 7, 64, 64, fake, 1 << 20, None, None) == q4.Q4_EINVAL
+    assert L.q4_pack(fake, 0, 64, 48, fake, 1 << 20, None, None) == q4.Q4_ESHAPE
+    assert L.q4_pack(fake, 0, 64, 64, fake, 10, None, None) == q4.Q4_ENOSPACE
+    assert L.q4_pack(odd, 0, 64, 64, fake, 1 << 20, None, None) == q4.Q4_EALIGN
+    assert L.q4_gemv(fake, 64, 64, fake, 5, fake, fake, 1 << 20, None) == q4.Q4_ESHAPE
+    assert L.q4_gemv(fake, 64, 64, fake, 1, fake, fake, 0, None) == q4.Q4_ENOSPACE
+    pos = (C.c_int32 * 1)(100)
+    ws = 1 << 30
+    # position beyond capacity
+    assert L.flash_decode_full(fake, fake, fake, 0, 100, 16, 512, pos, 1, 1, C.c_float(1.0),
+                               fake, fake, ws, None) == q4.Q4_ERANGE
+    # ring too short for a 4-row verify block: R < W + n - 1
+    assert L.flash_decode_ring(fake, fake, fake, 0, 16, 8, 256, 1026, 1024, pos, 1, 4,
+                               C.c_float(1.0), fake, fake, ws, None) == q4.Q4_ERANGE
+    assert L.flash_decode_ring(fake, fake, fake, 0, 16, 8, 256, 2048, 4096, pos, 1, 1,
+                               C.c_float(1.0), fake, fake, ws, None) == q4.Q4_ERANGE
+    assert L.flash_decode_ring(fake, fake, fake, 0, 16, 5, 256, 2048, 1024, pos, 1, 1,
+                               C.c_float(1.0), fake, fake, ws, None) == q4.Q4_ESHAPE
+
+
+def test_decode_step_checks():
+    from int4_q4_gemv_amd import synth
+    cfg = synth.TOY
+    L = q4.lib()
+    fake = 0x10000
+    lay = (q4.Layer * 2)()
+    for i in range(2):
+        lay[i] = q4.Layer(int(cfg.is_full(i)), 1, *([fake] * 13), 1.0, fake, fake)
+    m = q4.Model(cfg.hidden, cfg.n_heads, cfg.inter, cfg.vocab, 2, cfg.sl_kv_heads, cfg.sl_head_dim,
+                 cfg.full_head_dim, cfg.window, cfg.ring, cfg.full_cap, cfg.sl_rot_pairs,
+                 cfg.full_rot_pairs, cfg.sl_theta, cfg.full_theta, 1.0, 1.0, 1e-6, 30.0, fake, fake, lay)
+    need = L.decode_step_workspace_size(C.byref(m), 1)
+    assert need > 0
+    tok = (C.c_int32 * 4)(1, 2, 3, 4)
+    big = C.c_size_t(need * 2)
+    f = C.c_void_p(fake)
+    assert L.decode_step(C.byref(m), tok, 5, 0, f, f, f, big, None) == q4.Q4_ESHAPE
+    assert L.decode_step(C.byref(m), tok, 1, -1, f, f, f, big, None) == q4.Q4_ERANGE
+    assert L.decode_step(C.byref(m), tok, 1, cfg.full_cap, f, f, f, big, None) == q4.Q4_ERANGE
+    assert L.decode_step(C.byref(m), tok, 1, 5, f, f, f, C.c_size_t(16), None) == q4.Q4_ENOSPACE
+    bad = (C.c_int32 * 1)(cfg.vocab)
+    assert L.decode_step(C.byref(m), bad, 1, 5, f, f, f, big, None) == q4.Q4_ERANGE
+    m.ring = cfg.window + 2      # a 4-row block needs R >= W + 3
+    assert L.decode_step(C.byref(m), tok, 4, 5, f, f, f, big, None) == q4.Q4_ERANGE
