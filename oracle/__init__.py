@@ -78,6 +78,12 @@ def _declare(L):
     L.orc_decode_step.restype = _i
     L.orc_decode_step.argtypes = [_p, _p, _i, _i64, _p, _p]
     L.orc_num_threads.restype = _i
+    L.orc_embed.restype = _i
+    L.orc_embed.argtypes = [_p, _p, _i, _p]
+    L.orc_run_layer.restype = _i
+    L.orc_run_layer.argtypes = [_p, _i, _p, _i, _i64]
+    L.orc_head.restype = _i
+    L.orc_head.argtypes = [_p, _p, _i, _p, _p]
 
 
 def _ptr(a: np.ndarray):
@@ -310,6 +316,32 @@ class OracleModel:
                    self.sl_scale, self.full_scale, self.eps, self.softcap,
                    emb.ctypes.data, fn.ctypes.data, arr)
         return m, keep
+
+    def embed_tokens(self, tokens) -> np.ndarray:
+        tokens = np.ascontiguousarray(tokens, dtype=np.int32)
+        m, keep = self._struct()
+        h = np.empty((tokens.size, self.hidden), dtype=np.float64)
+        if lib().orc_embed(C.byref(m), _ptr(tokens), tokens.size, _ptr(h)) != 0:
+            raise ValueError("oracle embed rejected its arguments")
+        return h
+
+    def run_layer(self, l: int, h, pos0: int) -> np.ndarray:
+        """Layer l applied to a copy of h [n, hidden] (writes layer l's cache)."""
+        h = np.array(h, dtype=np.float64, copy=True, order="C")
+        m, keep = self._struct()
+        if lib().orc_run_layer(C.byref(m), l, _ptr(h), h.shape[0], pos0) != 0:
+            raise ValueError("oracle layer rejected its arguments")
+        return h
+
+    def run_head(self, h, want_logits: bool = True):
+        h = np.ascontiguousarray(h, dtype=np.float64)
+        n = h.shape[0]
+        m, keep = self._struct()
+        logits = np.empty((n, self.vocab), dtype=np.float64) if want_logits else None
+        am = np.empty(n, dtype=np.int32)
+        if lib().orc_head(C.byref(m), _ptr(h), n, _ptr(logits) if logits is not None else None, _ptr(am)) != 0:
+            raise ValueError("oracle head rejected its arguments")
+        return logits, am
 
     def decode_step(self, tokens, pos0: int, want_logits: bool = True):
         """Run len(tokens) rows at positions pos0.. (writes the caches).

@@ -295,112 +295,128 @@ double orc_softcap(double z, double c) { return c * tanh(z / c); }
 /* ------------------------------------------------------------------------ */
 static void to_f16(const double* x, int64_t n, uint16_t* out) { orc_f64_to_f16_array(x, n, out); }
 
-int orc_decode_step(const orc_model* m, const int32_t* tokens, int n, int64_t pos0,
-                    double* logits, int32_t* argmax) {
-  if (!m || !tokens || n < 1 || pos0 < 0) return -1;
-  const int H = m->hidden, Hq = m->n_heads, I = m->inter, V = m->vocab;
+static int check_rows(const orc_model* m, int l, int n, int64_t pos0) {
+  if (!m || n < 1 || pos0 < 0 || l < 0 || l >= m->n_layers) return -1;
+  if (m->window > m->ring || m->ring < m->window + n - 1) return -1;
+  if (m->layers[l].is_full && pos0 + n - 1 >= m->full_cap) return -1;
+  return 0;
+}
+
+/* embedding: fp16 row of the tied table times sqrt(hidden) (reading) */
+int orc_embed(const orc_model* m, const int32_t* tokens, int n, double* h) {
+  if (!m || !tokens || n < 1) return -1;
+  const int H = m->hidden;
+  for (int i = 0; i < n; i++) if (tokens[i] < 0 || tokens[i] >= m->vocab) return -1;
+  const double emb_scale = sqrt((double)H);
+  for (int i = 0; i < n; i++)
+    for (int c = 0; c < H; c++)
+      h[(int64_t)i * H + c] = orc_f16_to_f64(m->embed[(int64_t)tokens[i] * H + c]) * emb_scale;
+  return 0;
+}
+
+/* One decoder layer on the residual stream h [n][hidden] (updated in place);
+ * row i sits at position pos0 + i; the layer's cache receives every row's
+ * K/V before any row attends. */
+int orc_run_layer(const orc_model* m, int l, double* h, int n, int64_t pos0) {
+  if (check_rows(m, l, n, pos0)) return -1;
+  const int H = m->hidden, Hq = m->n_heads, I = m->inter;
   const int Hs = m->sl_kv_heads, Ds = m->sl_head_dim, Df = m->full_head_dim;
   const int64_t R = m->ring, W = m->window;
-  for (int i = 0; i < n; i++) if (tokens[i] < 0 || tokens[i] >= V) return -1;
-  if (W > R || R < W + n - 1) return -1;
-  if (pos0 + n - 1 >= m->full_cap) {
-    for (int l = 0; l < m->n_layers; l++) if (m->layers[l].is_full) return -1;
-  }
   const int Dmax = Ds > Df ? Ds : Df;
   const int64_t qdim = (int64_t)Hq * Dmax;
-  double* h = (double*)calloc((size_t)n * H, sizeof(double));
-  double* t0 = (double*)malloc(sizeof(double) * (size_t)(H > I ? H : I) * 2);
-  uint16_t* x16 = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)n * (H > I ? H : I));
+  const int HI = H > I ? H : I;
+  double* t0 = (double*)malloc(sizeof(double) * (size_t)HI);
+  uint16_t* x16 = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)n * HI);
   double* qv = (double*)malloc(sizeof(double) * (size_t)n * qdim);
   double* kv = (double*)malloc(sizeof(double) * (size_t)n * Hs * Dmax);
   double* vv = (double*)malloc(sizeof(double) * (size_t)n * Hs * Dmax);
   uint16_t* q16 = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)n * qdim);
   double* att = (double*)malloc(sizeof(double) * (size_t)n * qdim);
-  double* y = (double*)malloc(sizeof(double) * (size_t)n * (H > I ? H : I));
+  double* y = (double*)malloc(sizeof(double) * (size_t)n * HI);
   double* g = (double*)malloc(sizeof(double) * (size_t)n * I);
   double* u = (double*)malloc(sizeof(double) * (size_t)n * I);
   double* tmp = (double*)malloc(sizeof(double) * (size_t)(Dmax > H ? Dmax : H));
 
-  /* embedding: fp16 row of the tied table times sqrt(hidden) (reading) */
-  const double emb_scale = sqrt((double)H);
-  for (int i = 0; i < n; i++)
-    for (int c = 0; c < H; c++)
-      h[(int64_t)i * H + c] = orc_f16_to_f64(m->embed[(int64_t)tokens[i] * H + c]) * emb_scale;
+  const orc_layer* L = &m->layers[l];
+  const int full = L->is_full;
+  const int D = full ? Df : Ds;
+  const int Hkv = full ? 1 : Hs;
+  const double theta = full ? m->full_theta : m->sl_theta;
+  const int rot = full ? m->full_rot_pairs : m->sl_rot_pairs;
+  const double scale = full ? m->full_scale : m->sl_scale;
 
-  for (int l = 0; l < m->n_layers; l++) {
-    const orc_layer* L = &m->layers[l];
-    const int full = L->is_full;
-    const int D = full ? Df : Ds;
-    const int Hkv = full ? 1 : Hs;
-    const double theta = full ? m->full_theta : m->sl_theta;
-    const int rot = full ? m->full_rot_pairs : m->sl_rot_pairs;
-    const double scale = full ? m->full_scale : m->sl_scale;
+  /* attention input norm, fp16 activations into the projections */
+  for (int i = 0; i < n; i++) {
+    orc_rmsnorm(h + (int64_t)i * H, L->attn_norm, H, m->eps, t0);
+    to_f16(t0, H, x16 + (int64_t)i * H);
+  }
+  orc_q4_gemv(L->wq, (int64_t)Hq * D, H, x16, n, qv);
+  orc_q4_gemv(L->wk, (int64_t)Hkv * D, H, x16, n, kv);
+  if (full) memcpy(vv, kv, sizeof(double) * (size_t)n * Hkv * D); /* attention_k_eq_v: raw k_proj */
+  else orc_q4_gemv(L->wv, (int64_t)Hkv * D, H, x16, n, vv);
 
-    /* attention input norm, fp16 activations into the projections */
-    for (int i = 0; i < n; i++) {
-      orc_rmsnorm(h + (int64_t)i * H, L->attn_norm, H, m->eps, t0);
-      to_f16(t0, H, x16 + (int64_t)i * H);
+  for (int i = 0; i < n; i++) {
+    const int64_t P = pos0 + i;
+    for (int hh = 0; hh < Hq; hh++) {
+      double* qh = qv + (int64_t)i * Hq * D + (int64_t)hh * D;
+      orc_rmsnorm(qh, L->q_norm, D, m->eps, tmp);
+      orc_rope(tmp, D, P, theta, rot);
+      to_f16(tmp, D, q16 + (int64_t)i * Hq * D + (int64_t)hh * D);
     }
-    orc_q4_gemv(L->wq, (int64_t)Hq * D, H, x16, n, qv);
-    orc_q4_gemv(L->wk, (int64_t)Hkv * D, H, x16, n, kv);
-    if (full) memcpy(vv, kv, sizeof(double) * (size_t)n * Hkv * D); /* attention_k_eq_v: raw k_proj */
-    else orc_q4_gemv(L->wv, (int64_t)Hkv * D, H, x16, n, vv);
-
-    for (int i = 0; i < n; i++) {
-      const int64_t P = pos0 + i;
-      for (int hh = 0; hh < Hq; hh++) {
-        double* qh = qv + (int64_t)i * Hq * D + (int64_t)hh * D;
-        orc_rmsnorm(qh, L->q_norm, D, m->eps, tmp);
-        orc_rope(tmp, D, P, theta, rot);
-        to_f16(tmp, D, q16 + (int64_t)i * Hq * D + (int64_t)hh * D);
+    for (int gg = 0; gg < Hkv; gg++) {
+      double* kh = kv + (int64_t)i * Hkv * D + (int64_t)gg * D;
+      double* vh = vv + (int64_t)i * Hkv * D + (int64_t)gg * D;
+      orc_rmsnorm(kh, L->k_norm, D, m->eps, tmp);
+      orc_rope(tmp, D, P, theta, rot);
+      uint16_t* kdst; uint16_t* vdst;
+      if (full) { kdst = L->k_cache + P * D; vdst = L->v_cache + P * D; }
+      else {
+        int64_t slot = P % R;
+        kdst = L->k_cache + ((int64_t)gg * R + slot) * D;
+        vdst = L->v_cache + ((int64_t)gg * R + slot) * D;
       }
-      for (int gg = 0; gg < Hkv; gg++) {
-        double* kh = kv + (int64_t)i * Hkv * D + (int64_t)gg * D;
-        double* vh = vv + (int64_t)i * Hkv * D + (int64_t)gg * D;
-        orc_rmsnorm(kh, L->k_norm, D, m->eps, tmp);
-        orc_rope(tmp, D, P, theta, rot);
-        uint16_t* kdst; uint16_t* vdst;
-        if (full) { kdst = L->k_cache + P * D; vdst = L->v_cache + P * D; }
-        else {
-          int64_t slot = P % R;
-          kdst = L->k_cache + ((int64_t)gg * R + slot) * D;
-          vdst = L->v_cache + ((int64_t)gg * R + slot) * D;
-        }
-        to_f16(tmp, D, kdst);
-        if (L->v_norm) { orc_rmsnorm(vh, NULL, D, m->eps, tmp); to_f16(tmp, D, vdst); }
-        else to_f16(vh, D, vdst);
-      }
-    }
-    if (full) orc_flash_full(q16, L->k_cache, L->v_cache, m->full_cap, Hq, D, pos0, n, scale, att);
-    else orc_flash_ring(q16, L->k_cache, L->v_cache, Hq, Hkv, D, R, W, pos0, n, scale, att);
-
-    /* output projection, post-attention norm, residual */
-    to_f16(att, (int64_t)n * Hq * D, q16);
-    orc_q4_gemv(L->wo, H, (int64_t)Hq * D, q16, n, y);
-    for (int i = 0; i < n; i++) {
-      orc_rmsnorm(y + (int64_t)i * H, L->post_attn_norm, H, m->eps, t0);
-      for (int c = 0; c < H; c++) h[(int64_t)i * H + c] += t0[c];
-    }
-    /* gated MLP */
-    for (int i = 0; i < n; i++) {
-      orc_rmsnorm(h + (int64_t)i * H, L->pre_ff_norm, H, m->eps, t0);
-      to_f16(t0, H, x16 + (int64_t)i * H);
-    }
-    orc_q4_gemv(L->wg, I, H, x16, n, g);
-    orc_q4_gemv(L->wu, I, H, x16, n, u);
-    for (int64_t e = 0; e < (int64_t)n * I; e++) g[e] = orc_gelu_tanh(g[e]) * u[e];
-    to_f16(g, (int64_t)n * I, x16);
-    orc_q4_gemv(L->wd, H, I, x16, n, y);
-    for (int i = 0; i < n; i++) {
-      orc_rmsnorm(y + (int64_t)i * H, L->post_ff_norm, H, m->eps, t0);
-      for (int c = 0; c < H; c++) {
-        double* hc = &h[(int64_t)i * H + c];
-        *hc = (*hc + t0[c]) * (double)L->layer_scalar;
-      }
+      to_f16(tmp, D, kdst);
+      if (L->v_norm) { orc_rmsnorm(vh, NULL, D, m->eps, tmp); to_f16(tmp, D, vdst); }
+      else to_f16(vh, D, vdst);
     }
   }
+  if (full) orc_flash_full(q16, L->k_cache, L->v_cache, m->full_cap, Hq, D, pos0, n, scale, att);
+  else orc_flash_ring(q16, L->k_cache, L->v_cache, Hq, Hkv, D, R, W, pos0, n, scale, att);
 
-  /* final norm, tied fp16 head, softcap, greedy argmax */
+  /* output projection, post-attention norm, residual */
+  to_f16(att, (int64_t)n * Hq * D, q16);
+  orc_q4_gemv(L->wo, H, (int64_t)Hq * D, q16, n, y);
+  for (int i = 0; i < n; i++) {
+    orc_rmsnorm(y + (int64_t)i * H, L->post_attn_norm, H, m->eps, t0);
+    for (int c = 0; c < H; c++) h[(int64_t)i * H + c] += t0[c];
+  }
+  /* gated MLP */
+  for (int i = 0; i < n; i++) {
+    orc_rmsnorm(h + (int64_t)i * H, L->pre_ff_norm, H, m->eps, t0);
+    to_f16(t0, H, x16 + (int64_t)i * H);
+  }
+  orc_q4_gemv(L->wg, I, H, x16, n, g);
+  orc_q4_gemv(L->wu, I, H, x16, n, u);
+  for (int64_t e = 0; e < (int64_t)n * I; e++) g[e] = orc_gelu_tanh(g[e]) * u[e];
+  to_f16(g, (int64_t)n * I, x16);
+  orc_q4_gemv(L->wd, H, I, x16, n, y);
+  for (int i = 0; i < n; i++) {
+    orc_rmsnorm(y + (int64_t)i * H, L->post_ff_norm, H, m->eps, t0);
+    for (int c = 0; c < H; c++) {
+      double* hc = &h[(int64_t)i * H + c];
+      *hc = (*hc + t0[c]) * (double)L->layer_scalar;
+    }
+  }
+  free(t0); free(x16); free(qv); free(kv); free(vv); free(q16); free(att); free(y); free(g); free(u); free(tmp);
+  return 0;
+}
+
+/* final norm, tied fp16 head, softcap, greedy argmax (lowest index on ties) */
+int orc_head(const orc_model* m, const double* h, int n, double* logits, int32_t* argmax) {
+  if (!m || n < 1) return -1;
+  const int H = m->hidden, V = m->vocab;
+  double* t0 = (double*)malloc(sizeof(double) * (size_t)H);
+  uint16_t* x16 = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)n * H);
   for (int i = 0; i < n; i++) {
     orc_rmsnorm(h + (int64_t)i * H, m->final_norm, H, m->eps, t0);
     to_f16(t0, H, x16 + (int64_t)i * H);
@@ -417,7 +433,18 @@ int orc_decode_step(const orc_model* m, const int32_t* tokens, int n, int64_t po
     if (argmax) argmax[i] = best;
   }
   if (logits) memcpy(logits, z, sizeof(double) * (size_t)n * V);
-  free(z); free(h); free(t0); free(x16); free(qv); free(kv); free(vv); free(q16);
-  free(att); free(y); free(g); free(u); free(tmp);
+  free(z); free(t0); free(x16);
   return 0;
+}
+
+int orc_decode_step(const orc_model* m, const int32_t* tokens, int n, int64_t pos0,
+                    double* logits, int32_t* argmax) {
+  if (!m || !tokens || n < 1 || pos0 < 0) return -1;
+  for (int l = 0; l < m->n_layers; l++) if (check_rows(m, l, n, pos0)) return -1;
+  double* h = (double*)calloc((size_t)n * m->hidden, sizeof(double));
+  int rc = orc_embed(m, tokens, n, h);
+  for (int l = 0; l < m->n_layers && rc == 0; l++) rc = orc_run_layer(m, l, h, n, pos0);
+  if (rc == 0) rc = orc_head(m, h, n, logits, argmax);
+  free(h);
+  return rc;
 }

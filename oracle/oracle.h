@@ -104,6 +104,14 @@ typedef struct {
   orc_layer* layers;          /* [n_layers] */
 } orc_model;
 
+/* The step in three parts (used alone for teacher-forced checks):
+ * orc_embed: h[i] = fp16 table row of tokens[i] times sqrt(hidden);
+ * orc_run_layer: layer l on h [n][hidden] in place, rows at pos0 + i;
+ * orc_head: final RMSNorm, fp16 tied head, softcap, argmax. */
+int orc_embed(const orc_model* m, const int32_t* tokens, int n, double* h);
+int orc_run_layer(const orc_model* m, int l, double* h, int n, int64_t pos0);
+int orc_head(const orc_model* m, const double* h, int n, double* logits, int32_t* argmax);
+
 /* Runs n rows (tokens[i] at position pos0+i) through the model, writing K/V
  * of every row into the caches first and then attending with per-row
  * causality.  logits [n][vocab] (softcapped), argmax [n] (lowest index on

@@ -198,3 +198,19 @@ def test_logits_bounded_by_softcap(orc):
     m = build_oracle_model(orc, cfg, 4, 60)
     logits, _ = m.decode_step(synth.tokens(cfg, 1, 4), 60)
     assert np.all(np.abs(logits) < cfg.softcap) and np.isfinite(logits).all()
+
+
+def test_layerwise_parts_compose_to_the_step(orc):
+    """embed + every layer + head equals the whole step bit for bit (the parts
+    are what the teacher-forced GPU checks call)."""
+    cfg = synth.TOY
+    m = build_oracle_model(orc, cfg, 5, 90)
+    toks = synth.tokens(cfg, 2, 5)
+    a = clone(m)
+    whole, am = a.decode_step(toks, 90)
+    b = clone(m)
+    h = b.embed_tokens(toks)
+    for l in range(cfg.n_layers):
+        h = b.run_layer(l, h, 90)
+    parts, am2 = b.run_head(h)
+    assert np.array_equal(whole, parts) and np.array_equal(am, am2)
