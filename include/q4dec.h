@@ -55,8 +55,10 @@ const char* q4dec_version(void);
 /* ------------------------------------------------------------------------ */
 enum { Q4_F32 = 0, Q4_BF16 = 1 };
 
-/* Bytes of the packed form of an [N, K] matrix: ceil(N/64)*64 * K/32 * 18.
- * Returns 0 when K is not a positive multiple of 32 or N < 1. */
+/* Bytes of the packed form of an [N, K] matrix:
+ * ceil(N/16)*16 rows * ceil(K/128)*4 blocks * 18 bytes (= N*K/32*18 when N is a
+ * multiple of 16 and K of 128).  Returns 0 when K is not a positive multiple
+ * of 32 or N < 1. */
 size_t q4_packed_bytes(int N, int K);
 
 /* Quantises W (device, row-major [N, K], fp32 or bf16) onto the q4_0 grid
@@ -65,8 +67,10 @@ size_t q4_packed_bytes(int N, int K);
  * q = clamp(round_half_away(w / d), -8, 7) with w / d an IEEE fp32 quotient
  * taken against the stored fp16 scale (d == 0 gives q = 0).
  * `packed` (device, packed_bytes >= q4_packed_bytes(N, K)) receives the
- * device layout: 64-row tiles; codes [tile][K/32][64 rows][16 B] followed by
- * scales [tile][K/32][64 rows] fp16; rows past N are zero.
+ * device layout: "quads" of 16 rows x 4 blocks, one 1 KB wave-wide load each;
+ * codes [N/16][K/128][64 lanes][16 B] (lane l: row l % 16, block l / 16 of
+ * the quad) followed by scales [N/16][K/128][64 lanes] fp16; padding rows and
+ * blocks have zero scale.
  * `nonfinite` (device int32, may be NULL) is incremented once per block that
  * holds a non-finite weight or whose scale overflows fp16 (such blocks get
  * d = 0 and q = 0); it is data-dependent, so it is read after a sync.
@@ -85,21 +89,17 @@ q4_status q4_unpack(const void* packed, int N, int K, uint8_t* blocks, void* str
 /* ------------------------------------------------------------------------ */
 /* int4 matrix-vector product                                                */
 /* ------------------------------------------------------------------------ */
-/* Workspace bytes q4_gemv needs for an [N, K] matrix and B rows. */
-size_t q4_gemv_workspace_size(int N, int K, int B);
-
 /* y[b][n] = sum_k (d * q)[n][k] * x[b][k] for b < B, fp32 accumulation
  * (the weight stream of the decode step; gemma4-12b card, Throughput:
  * "decode is otherwise weight-bandwidth-bound").
  * packed: device, from q4_pack(N, K).  x: device fp16 [B][K].  y: device fp32
  * [B][N].  B in 1..4 (4 = the width-4 verify block; B > 1 runs on MFMA).
- * ws: device workspace of q4_gemv_workspace_size(N, K, B) bytes; it must be
- * zero-filled before its first use and every completed call leaves it
- * zero-filled again.  Calls sharing one workspace must not overlap.
- * Errors: Q4_EINVAL, Q4_ESHAPE (K % 32, B outside 1..4), Q4_ENOSPACE,
+ * K <= 16384 (B == 1) or 15360 (B > 1).  No workspace; each 16-row tile is
+ * finished by one workgroup, so results are deterministic.
+ * Errors: Q4_EINVAL, Q4_ESHAPE (K % 32, K too large, B outside 1..4),
  * Q4_EALIGN, Q4_EHIP. */
 q4_status q4_gemv(const void* packed, int N, int K, const uint16_t* x, int B,
-                  float* y, void* ws, size_t ws_bytes, void* stream);
+                  float* y, void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* flash-decode attention                                                    */
@@ -203,6 +203,13 @@ size_t decode_step_workspace_size(const q4dec_model* m, int n);
 q4_status decode_step(const q4dec_model* m, const int32_t* tokens, int n, int pos0,
                       float* logits, int32_t* argmax, void* ws, size_t ws_bytes,
                       void* stream);
+
+/* Copies the residual stream after the last layer (before the final norm)
+ * of the most recent step run with workspace `ws`: device fp32 [n][hidden].
+ * This is the hidden state a drafter reads; the tests use it to check every
+ * layer of the step.  Errors: Q4_EINVAL, Q4_ESHAPE, Q4_ENOSPACE, Q4_EHIP. */
+q4_status decode_step_hidden(const q4dec_model* m, const void* ws, size_t ws_bytes, int n,
+                             float* h_out, void* stream);
 
 /* Same step without graph capture (every kernel launched directly). */
 q4_status decode_step_eager(const q4dec_model* m, const int32_t* tokens, int n, int pos0,

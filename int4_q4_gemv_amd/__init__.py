@@ -96,10 +96,8 @@ def _declare(L):
     L.q4_pack.argtypes = [_p, _i, _i, _i, _p, _sz, _p, _p]
     L.q4_unpack.restype = _i
     L.q4_unpack.argtypes = [_p, _i, _i, _p, _p]
-    L.q4_gemv_workspace_size.restype = _sz
-    L.q4_gemv_workspace_size.argtypes = [_i, _i, _i]
     L.q4_gemv.restype = _i
-    L.q4_gemv.argtypes = [_p, _i, _i, _p, _i, _p, _p, _sz, _p]
+    L.q4_gemv.argtypes = [_p, _i, _i, _p, _i, _p, _p]
     L.flash_decode_workspace_size.restype = _sz
     L.flash_decode_workspace_size.argtypes = [_i, _i, _i, _i]
     L.flash_decode_full.restype = _i
@@ -112,12 +110,14 @@ def _declare(L):
         fn.restype = _i
         fn.argtypes = [C.POINTER(Model), _p, _i, _i, _p, _p, _p, _sz, _p]
     L.q4dec_release.restype = _i
+    L.decode_step_hidden.restype = _i
+    L.decode_step_hidden.argtypes = [C.POINTER(Model), _p, _sz, _i, _p, _p]
 
 
 EXPORTS = ["q4dec_status_str", "q4dec_version", "q4_packed_bytes", "q4_pack", "q4_unpack",
-           "q4_gemv_workspace_size", "q4_gemv", "flash_decode_workspace_size",
-           "flash_decode_full", "flash_decode_ring", "decode_step_workspace_size",
-           "decode_step", "decode_step_eager", "q4dec_release"]
+           "q4_gemv", "flash_decode_workspace_size", "flash_decode_full", "flash_decode_ring",
+           "decode_step_workspace_size", "decode_step", "decode_step_hidden", "decode_step_eager",
+           "q4dec_release"]
 
 
 def _check(fn: str, rc: int):
@@ -168,14 +168,10 @@ def q4_unpack(packed: torch.Tensor, N: int, K: int) -> torch.Tensor:
 
 
 class Gemv:
-    """q4_gemv with its own zero-initialised workspace."""
+    """q4_gemv for one matrix shape (kept for call sites that reuse it)."""
 
     def __init__(self, N: int, K: int, B: int, device="cuda"):
         self.N, self.K, self.B = N, K, B
-        n = int(lib().q4_gemv_workspace_size(N, K, B))
-        if n == 0:
-            raise Q4Error("q4_gemv_workspace_size", Q4_ESHAPE)
-        self.ws = torch.zeros(n, dtype=torch.uint8, device=device)
 
     def __call__(self, packed, x, y=None):
         _need_cuda(packed, x)
@@ -183,8 +179,7 @@ class Gemv:
         B = x.shape[0]
         if y is None:
             y = torch.empty((B, self.N), dtype=torch.float32, device=x.device)
-        _check("q4_gemv", lib().q4_gemv(_ptr(packed), self.N, self.K, _ptr(x), B, _ptr(y),
-                                         _ptr(self.ws), self.ws.numel(), _stream()))
+        _check("q4_gemv", lib().q4_gemv(_ptr(packed), self.N, self.K, _ptr(x), B, _ptr(y), _stream()))
         return y
 
 
@@ -292,6 +287,17 @@ class DecodeModel:
         _check("decode_step", fn(C.byref(self.desc), tk, n, int(pos0), _ptr(logits), _ptr(argmax),
                                  _ptr(ws), ws.numel(), _stream()))
         return logits, argmax
+
+
+def _hidden(self, n: int) -> torch.Tensor:
+    ws = self.workspace(n)
+    out = torch.empty((n, self.cfg.hidden), dtype=torch.float32, device=self.embed.device)
+    _check("decode_step_hidden", lib().decode_step_hidden(C.byref(self.desc), _ptr(ws), ws.numel(), n,
+                                                          _ptr(out), _stream()))
+    return out
+
+
+DecodeModel.hidden = _hidden
 
 
 def release():

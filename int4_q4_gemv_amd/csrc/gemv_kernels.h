@@ -1,36 +1,34 @@
 // gemv_kernels.h -- int4 q4_0 matrix-vector products for gfx950, and the fp16
 // tied-head product with softcap and argmax.
 //
-// Work split: a 64-row tile of one matrix is cut along K into chunks of CB
-// blocks; each wave streams one chunk (one 16-byte load per lane per block,
-// so every wave-wide load is 1 KB contiguous) and a workgroup of 4 waves
-// takes 4 consecutive chunks of the same tile.  Partial sums meet in LDS
-// (fixed order), and when a tile spans G > 1 workgroups the last one to
-// finish adds the G partials in fixed order, so results are deterministic.
+// Work split: one workgroup owns a 16-row tile of a matrix over one of S
+// runs of K (S = 1 for most products).  Partial sums never meet across
+// workgroups inside a kernel (on gfx950 the L2 writeback such a handoff
+// needs costs more than the product itself): with S > 1 the S partial
+// products are written side by side and the next kernel, which reads the
+// product anyway, adds them in a fixed order.  The W waves of a workgroup
+// split its run into CQ quads each (a quad = 16 rows x 4 q4 blocks = one
+// 1 KB wave-wide load, see pack_kernels.h); partial sums meet in LDS in a
+// fixed order, so results are deterministic.  Every wave issues all of its
+// weight loads before anything else, and the grid is sized so that all of
+// its waves are resident at once: the whole matrix is in flight from the
+// first microseconds of the kernel.
 //
-// Batch 1: each lane owns one row; the activation is wave-uniform and is read
-// through the scalar cache; dequantisation is the fp16 magic-number trick
+// Batch 1: lane l works on row (l & 15) and block (l >> 4) of each quad; the
+// activation comes from LDS; dequantisation is the fp16 magic-number trick
 // (1024 + u, 64 + u) minus the bias, exact, then v_dot2_f32_f16.
 // Batch 2..4 (the width-4 verify block): v_mfma_f32_4x4x4_16b_f16 with the
-// 64 rows as 16 blocks of 4, the batch as the 4 columns; each lane still
-// dequantises only its own row, and per-block scales are applied to the
-// fp32 accumulator, so the dequantised weights stay exact.
+// 64 lanes as 16 blocks of 4 rows and the batch as the 4 columns; each lane
+// still dequantises only its own 32 weights and the per-block scale is
+// applied to the fp32 accumulator, so the dequantised weights stay exact.
+//
+// The activation comes in as fp16; where it is a normalised residual stream
+// it is formed once per row by k_norm_rows (RMSNorm of the previous product
+// added to the residual, then the input RMSNorm).
 #pragma once
 #include "device_common.h"
 
 namespace q4k {
-
-
-struct GemvSeg {
-  const u4v* codes;
-  const uint16_t* scales;
-  int N;        // rows of this matrix
-  int T;        // 64-row tiles
-  int tile0;    // first global tile index
-  int out_off;  // first output column in the concatenated output row
-};
-
-enum { EPI_STORE = 0, EPI_QKV = 1, EPI_GATEUP = 2, EPI_RESID = 3 };
 
 struct StepParams {       // written on the device at the start of every step
   int pos0;
@@ -38,43 +36,47 @@ struct StepParams {       // written on the device at the start of every step
   int tokens[4];
 };
 
-struct EpiArgs {
-  const StepParams* sp;   // decode step: positions and row count (NULL otherwise)
-  unsigned* grp_cnt;      // per output group completion counters
-  int grp_tiles;          // tiles per group
-  // QKV
-  int Hq, Hkv, D, is_full, v_norm, rot_pairs, R;
-  double theta;
-  float eps;
-  const float* q_norm;
-  const float* k_norm;
-  uint16_t* q_out;        // fp16 [4][Hq][D]
-  uint16_t* k_cache;
-  uint16_t* v_cache;
-  // GATEUP
-  int inter;
-  uint16_t* a_out;        // fp16 [4][inter]
-  // RESID
-  int H;
-  float* h;               // fp32 [4][H]
-  const float* w_post;
-  const float* w_next;
-  float scalar;
-  uint16_t* x_out;        // fp16 [4][H]
+struct GemvSeg {
+  const u4v* codes;
+  const uint16_t* scales;
+  int N;        // rows of this matrix
+  int T;        // 16-row tiles
+  int tile0;    // first global tile index (segments are laid end to end)
+  int out_off;  // first output column in the concatenated output row
 };
+
+// x = fp16(RMSNorm(h_new) * w_in), h_new = (h_src + RMSNorm(y) * w_post) * scalar
+// (y == NULL: h_new = h_src * scalar), where y is the sum, in order, of ny
+// (<= 4) partial products laid y_split floats apart.  h_new goes to h_dst.
+struct NormIn {
+  const float* h_src;
+  const float* y;
+  int ny;
+  long y_split;
+  const float* w_post;
+  float scalar;
+  const float* w_in;
+  float* h_dst;
+  int H;
+  float eps;
+};
+
+enum { EPI_STORE = 0, EPI_GATEUP = 1 };
 
 struct GemvArgs {
   GemvSeg seg[3];
   int nseg;
-  int K, NB, CB, G;
-  const uint16_t* x;      // fp16 [B][ldx]
+  int K, NQ, W;           // K, quads per row, waves per matrix tile
+  int NQs;                // quads per split (blockIdx.y = split; NQ when unsplit)
+  long y_split;           // EPI_STORE: floats between the partial products
+  const uint16_t* x;      // fp16 [rows][ldx]
   int ldx;
-  float* y;               // fp32 output / stage, [B][ldy]
+  float* y;               // EPI_STORE: fp32 [rows][ldy]
   int ldy;
-  float* partial;         // [tiles][G][B][64]
-  unsigned* tile_cnt;     // [tiles]
-  int n_rows;             // rows of x actually used (<= B); ignored when sp given
-  EpiArgs e;
+  uint16_t* a_out;        // EPI_GATEUP: fp16 [rows][inter] = GELU(gate) * up
+  int inter;
+  int n_rows;             // rows of x (<= B); replaced by sp->n when sp is set
+  const StepParams* sp;
 };
 
 Q4_DEV float gelu_tanh(float g) {
@@ -100,172 +102,85 @@ Q4_DEV void dq_word(uint32_t q, h2_t& v0, h2_t& v1, h2_t& v2, h2_t& v3) {
   v3 = as_h2(and_or(t, 0x00F000F0u, 0x54005400u)) - b64;
 }
 
-// ------------------------------------------------------------ epilogues ----
-// Per-head q/k/v finishing of the decode step (gemma4-12b card, architecture
-// notes): q, k get RMSNorm with learned scale then RoPE; V on full layers is
-// the raw k projection after a scale-free RMSNorm (attention_k_eq_v).
-Q4_DEV void epi_head(const GemvArgs& a, int head, float* lds) {
-  const EpiArgs& e = a.e;
-  const int D = e.D, tid = threadIdx.x;
-  const int n = e.sp->n;
-  float* buf = lds;          // D floats
-  float* red = lds + 512;    // 4 floats
-  for (int b = 0; b < n; b++) {
-    const int P = e.sp->pos0 + b;
-    const float* src;
-    int kind;   // 0 q, 1 k, 2 v
-    int g;
-    if (head < e.Hq) { kind = 0; g = head; src = a.y + (long)b * a.ldy + head * D; }
-    else if (head < e.Hq + e.Hkv) { kind = 1; g = head - e.Hq; src = a.y + (long)b * a.ldy + head * D; }
-    else { kind = 2; g = head - e.Hq - e.Hkv; src = a.y + (long)b * a.ldy + head * D; }
-    float v0 = tid < D ? src[tid] : 0.f;
-    float v1 = tid + 256 < D ? src[tid + 256] : 0.f;
-    const float ss = block_sum<256>(v0 * v0 + v1 * v1, red);
-    const float inv = 1.0f / sqrtf(ss / (float)D + e.eps);
-    long slot_off;
-    if (e.is_full) slot_off = (long)P * D;
-    else slot_off = ((long)g * e.R + (P % e.R)) * D;
-    if (kind == 2) {      // sliding V row
-      uint16_t* dst = e.v_cache + slot_off;
-      if (e.v_norm) {
-        if (tid < D) dst[tid] = f2h(v0 * inv);
-        if (tid + 256 < D) dst[tid + 256] = f2h(v1 * inv);
-      } else {
-        if (tid < D) dst[tid] = f2h(v0);
-        if (tid + 256 < D) dst[tid + 256] = f2h(v1);
-      }
-      __syncthreads();
-      continue;
-    }
-    if (kind == 1 && e.is_full) {   // V = scale-free RMSNorm of the raw key row
-      uint16_t* dst = e.v_cache + slot_off;
-      if (tid < D) dst[tid] = f2h(e.v_norm ? v0 * inv : v0);
-      if (tid + 256 < D) dst[tid + 256] = f2h(e.v_norm ? v1 * inv : v1);
-    }
-    const float* wn = kind == 0 ? e.q_norm : e.k_norm;
-    if (tid < D) buf[tid] = v0 * inv * wn[tid];
-    if (tid + 256 < D) buf[tid + 256] = v1 * inv * wn[tid + 256];
-    __syncthreads();
-    const int half = D >> 1;
-    uint16_t* dst = (kind == 0) ? e.q_out + ((long)b * e.Hq + g) * D : e.k_cache + slot_off;
-    if (tid < half) {
-      float x0 = buf[tid], x1 = buf[tid + half];
-      if (tid < e.rot_pairs) {
-        // angle P * theta^(-2i/D) in fp64, cos/sin rounded to fp32
-        const double inv_freq = pow(e.theta, -2.0 * (double)tid / (double)D);
-        const double ang = (double)P * inv_freq;
-        const float c = (float)cos(ang), s = (float)sin(ang);
-        const float y0 = x0 * c - x1 * s;
-        const float y1 = x1 * c + x0 * s;
-        x0 = y0; x1 = y1;
-      }
-      dst[tid] = f2h(x0);
-      dst[tid + half] = f2h(x1);
-    }
-    __syncthreads();
-  }
-}
-
-// h <- (h + RMSNorm(y) * w_post) * scalar;  x_out <- fp16(RMSNorm(h) * w_next)
-Q4_DEV void epi_resid(const GemvArgs& a, float* lds) {
-  const EpiArgs& e = a.e;
-  const int H = e.H, tid = threadIdx.x;
-  const int n = e.sp->n;
-  float* red = lds + 512;
-  for (int b = 0; b < n; b++) {
-    const float* y = a.y + (long)b * a.ldy;
-    float* h = e.h + (long)b * H;
-    float ss = 0.f;
-    for (int i = tid; i < H; i += 256) { float v = y[i]; ss += v * v; }
-    ss = block_sum<256>(ss, red);
-    const float inv = 1.0f / sqrtf(ss / (float)H + e.eps);
-    float ss2 = 0.f;
-    for (int i = tid; i < H; i += 256) {
-      float hn = (h[i] + y[i] * inv * e.w_post[i]) * e.scalar;
-      h[i] = hn;
-      ss2 += hn * hn;
-    }
-    ss2 = block_sum<256>(ss2, red);
-    const float inv2 = 1.0f / sqrtf(ss2 / (float)H + e.eps);
-    uint16_t* xo = e.x_out + (long)b * H;
-    for (int i = tid; i < H; i += 256) xo[i] = f2h(h[i] * inv2 * e.w_next[i]);
-    __syncthreads();
-  }
+// Block-wide sum for any blockDim.x multiple of 64 (<= 1024); red: 16 floats.
+Q4_DEV float block_sum_dyn(float v, float* red) {
+  v = wave_sum(v);
+  const int w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  float s = 0.f;
+  for (int i = 0; i < nw; i++) s += red[i];
+  return s;
 }
 
 // ------------------------------------------------------------ the kernel ----
-template <int B, int EPI, int CB>
-__global__ void __launch_bounds__(256) k_q4_gemv(GemvArgs a) {
-  __shared__ float red[4 * B * 64];
-  __shared__ float elds[520];
-  __shared__ int flag;
-  __shared__ __align__(16) uint16_t xs[B * 4 * CB * 32];   // [B][4 waves * CB * 32]
+// Grid: (tiles, S).  Block: 64 * W threads (EPI_GATEUP: 64 * 2W, the first W
+// waves on the gate tile, the rest on the up tile; S = 1).  Dynamic LDS:
+// B * NQs * 128 halves of activation.
+template <int B, int EPI, int CQ>
+__global__ void __launch_bounds__(B == 1 ? 1024 : 512) k_q4_gemv(GemvArgs a) {
+  extern __shared__ __align__(16) unsigned char smem_g[];
+  const int ldxs = a.NQs * 128;                 // staged activation row (halves)
+  uint16_t* xs = reinterpret_cast<uint16_t*>(smem_g);
+  __shared__ float red[16 * B * 16];
 
-  const int tile = blockIdx.x / a.G;
-  const int g = blockIdx.x - tile * a.G;
-  int s = 0;
-  if (a.nseg > 1 && tile >= a.seg[1].tile0) s = 1;
-  if (a.nseg > 2 && tile >= a.seg[2].tile0) s = 2;
-  const GemvSeg& sg = a.seg[s];
-  const int lt = tile - sg.tile0;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  const int chunk = g * 4 + wave;
-  const int b0raw = chunk * CB;
-  const int nb = max(0, min(CB, a.NB - b0raw));
-  const int b0 = nb > 0 ? b0raw : 0;
-  const long tb = (long)lt * a.NB + b0;
-  const u4v* cp = sg.codes + tb * 64 + lane;
-  const int nrow = a.e.sp ? a.e.sp->n : a.n_rows;
+  const int g = lane >> 4;
+  const int half = (EPI == EPI_GATEUP) ? wave / a.W : 0;
+  const int wq = wave - half * a.W;
+  const int tile = blockIdx.x, split = blockIdx.y;
+  int s = half, lt = tile;
+  if constexpr (EPI != EPI_GATEUP) {
+    s = 0;
+    if (a.nseg > 1 && tile >= a.seg[1].tile0) s = 1;
+    if (a.nseg > 2 && tile >= a.seg[2].tile0) s = 2;
+    lt = tile - a.seg[s].tile0;
+  }
+  const int qs0 = split * a.NQs;                // first quad of this split
+  const int qend = min(a.NQ, qs0 + a.NQs);
+  const int q0raw = qs0 + wq * CQ;
+  const int nq = max(0, min(CQ, qend - q0raw));
+  const int q0 = nq > 0 ? q0raw : qs0;          // idle waves load (and ignore) valid quads
+  const long tq = (long)lt * a.NQ + q0;
 
-  // this workgroup's slice of x (every batch row): fetched first, stored to
-  // LDS after the weight loads are in flight
-  constexpr int span = 4 * CB * 32;
-  constexpr int XPT = (B * span / 8 + 255) / 256;
-  uint4 xv_stage[XPT];
+  // ---- every weight load of this wave, first
+  u4v c[CQ];
+  uint16_t sr[CQ];   // batch 1: this lane's scales
+  u2v s4[CQ];        // batch 4: the scales of this lane's 4 MFMA rows
   {
-    const int kw0 = g * span;
-    const int kwn = min(span, a.K - kw0);
+    const u4v* cp = a.seg[s].codes + tq * 64 + lane;
 #pragma unroll
-    for (int r = 0; r < XPT; r++) {
-      const int i = threadIdx.x + 256 * r;
-      const int bb = i / (span / 8);
-      const int kk = (i - bb * (span / 8)) * 8;
-      uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (i < B * span / 8 && bb < nrow && kk < kwn)
-        v = *reinterpret_cast<const uint4*>(a.x + (long)bb * a.ldx + kw0 + kk);
-      xv_stage[r] = v;
+    for (int i = 0; i < CQ; i++) c[i] = __builtin_nontemporal_load(cp + (long)(i < nq ? i : 0) * 64);
+    const uint16_t* spp = a.seg[s].scales + tq * 64 + (B == 1 ? lane : (lane & ~3));
+#pragma unroll
+    for (int i = 0; i < CQ; i++) {
+      const long o = (long)(i < nq ? i : 0) * 64;
+      if constexpr (B == 1) sr[i] = spp[o];
+      else s4[i] = *reinterpret_cast<const u2v*>(spp + o);
     }
   }
-  auto stage_x = [&]() {
-#pragma unroll
-    for (int r = 0; r < XPT; r++) {
-      const int i = threadIdx.x + 256 * r;
-      if (i < B * span / 8) {
-        const int bb = i / (span / 8);
-        const int kk = (i - bb * (span / 8)) * 8;
-        *reinterpret_cast<uint4*>(&xs[bb * span + kk]) = xv_stage[r];
-      }
+  // ---- the activation run into LDS, while the weights are in flight
+  const int nrow = a.sp ? a.sp->n : a.n_rows;
+  {
+    const int n8 = ldxs / 8;
+    for (int i = threadIdx.x; i < B * n8; i += blockDim.x) {
+      const int bb = i / n8, k = qs0 * 128 + (i - bb * n8) * 8;
+      u4v v = {0u, 0u, 0u, 0u};
+      if (bb < nrow && k < a.K) v = *reinterpret_cast<const u4v*>(a.x + (long)bb * a.ldx + k);
+      *reinterpret_cast<u4v*>(&xs[bb * ldxs + (i - bb * n8) * 8]) = v;
     }
-    __syncthreads();
-  };
+  }
+  __syncthreads();
 
+  const int qx = q0 - qs0;                      // quad index inside the staged run
   if constexpr (B == 1) {
-    const uint16_t* sp = sg.scales + tb * 64 + lane;
-    u4v c[CB];
-    uint16_t sraw[CB];
-#pragma unroll
-    for (int i = 0; i < CB; i++) {
-      const int ii = i < nb ? i : 0;
-      c[i] = __builtin_nontemporal_load(cp + (long)ii * 64);
-      sraw[i] = sp[(long)ii * 64];
-    }
-    stage_x();
     float acc = 0.f;
-    const uint16_t* xl = xs + wave * CB * 32;
 #pragma unroll
-    for (int i = 0; i < CB; i++) {
-      const u4v* xv = reinterpret_cast<const u4v*>(xl + i * 32);
+    for (int i = 0; i < CQ; i++) {
+      const int ii = i < nq ? i : 0;
+      const u4v* xv = reinterpret_cast<const u4v*>(xs + ((qx + ii) * 4 + g) * 32);
       const uint32_t qw[4] = {c[i].x, c[i].y, c[i].z, c[i].w};
       float bs = 0.f;
 #pragma unroll
@@ -278,113 +193,148 @@ __global__ void __launch_bounds__(256) k_q4_gemv(GemvArgs a) {
         bs = __builtin_amdgcn_fdot2(v2, as_h2(xx.z), bs, false);
         bs = __builtin_amdgcn_fdot2(v3, as_h2(xx.w), bs, false);
       }
-      const float d = i < nb ? h2f(sraw[i]) : 0.f;
+      const float d = i < nq ? h2f(sr[i]) : 0.f;
       acc = fmaf(d, bs, acc);
     }
-    red[wave * 64 + lane] = acc;
+    // the 4 lane groups hold the same 16 rows over different blocks
+    acc += __shfl_xor(acc, 16, 64);
+    acc += __shfl_xor(acc, 32, 64);
+    if (lane < 16) red[wave * 16 + lane] = acc;
   } else {
-    const uint16_t* sp = sg.scales + tb * 64 + (lane & ~3);
-    u4v c[CB];
-    u2v sc4[CB];
-#pragma unroll
-    for (int i = 0; i < CB; i++) {
-      const int ii = i < nb ? i : 0;
-      c[i] = __builtin_nontemporal_load(cp + (long)ii * 64);
-      sc4[i] = *reinterpret_cast<const u2v*>(sp + (long)ii * 64);
-    }
-    stage_x();
+    // MFMA block m = lane / 4 holds rows 4m..4m+3 (mod 16) of lane group m / 4
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
-    const uint16_t* xl = xs + (lane & 3) * span + wave * CB * 32;
+    const uint16_t* xl = xs + (lane & 3) * ldxs;
 #pragma unroll
-    for (int i = 0; i < CB; i++) {
+    for (int i = 0; i < CQ; i++) {
+      const int ii = i < nq ? i : 0;
+      const uint16_t* xb = xl + ((qx + ii) * 4 + g) * 32;
       const uint32_t qw[4] = {c[i].x, c[i].y, c[i].z, c[i].w};
       f4_t cb = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int w = 0; w < 4; w++) {
         h2_t v0, v1, v2, v3;
         dq_word(qw[w], v0, v1, v2, v3);
-        const u2v xa = *reinterpret_cast<const u2v*>(xl + i * 32 + 8 * w);
-        const u2v xb = *reinterpret_cast<const u2v*>(xl + i * 32 + 8 * w + 4);
+        const u2v xa = *reinterpret_cast<const u2v*>(xb + 8 * w);
+        const u2v xc = *reinterpret_cast<const u2v*>(xb + 8 * w + 4);
         const h4_t A0 = {v0.x, v0.y, v1.x, v1.y};
         const h4_t A1 = {v2.x, v2.y, v3.x, v3.y};
         cb = __builtin_amdgcn_mfma_f32_4x4x4f16(A0, __builtin_bit_cast(h4_t, xa), cb, 0, 0, 0);
-        cb = __builtin_amdgcn_mfma_f32_4x4x4f16(A1, __builtin_bit_cast(h4_t, xb), cb, 0, 0, 0);
+        cb = __builtin_amdgcn_mfma_f32_4x4x4f16(A1, __builtin_bit_cast(h4_t, xc), cb, 0, 0, 0);
       }
-      const bool ok = i < nb;
-      const uint32_t s01 = sc4[i].x, s23 = sc4[i].y;
+      const bool ok = i < nq;
+      const uint32_t s01 = s4[i].x, s23 = s4[i].y;
       acc[0] = fmaf(ok ? h2f((uint16_t)(s01 & 0xFFFF)) : 0.f, cb[0], acc[0]);
       acc[1] = fmaf(ok ? h2f((uint16_t)(s01 >> 16)) : 0.f, cb[1], acc[1]);
       acc[2] = fmaf(ok ? h2f((uint16_t)(s23 & 0xFFFF)) : 0.f, cb[2], acc[2]);
       acc[3] = fmaf(ok ? h2f((uint16_t)(s23 >> 16)) : 0.f, cb[3], acc[3]);
     }
-    // lane holds rows 4*(lane/4)+r for batch lane%4
 #pragma unroll
     for (int r = 0; r < 4; r++) {
-      const int row = (lane & ~3) + r, bb = lane & 3;
-      if (bb < B) red[(wave * B + bb) * 64 + row] = acc[r];
+      acc[r] += __shfl_xor(acc[r], 16, 64);
+      acc[r] += __shfl_xor(acc[r], 32, 64);
+    }
+    if (lane < 16) {
+      const int bb = lane & 3;
+#pragma unroll
+      for (int r = 0; r < 4; r++)
+        if (bb < B) red[(wave * B + bb) * 16 + (lane & ~3) + r] = acc[r];
     }
   }
   __syncthreads();
-
-  // ---- reduce the 4 waves, then the G workgroups of the tile
+  // ---- sum the waves in fixed order, then the epilogue
   const int t = threadIdx.x;
-  float v = 0.f;
-  if (t < B * 64) {
-    const int bb = t >> 6, row = t & 63;
-#pragma unroll
-    for (int w = 0; w < 4; w++) v += red[(w * B + bb) * 64 + row];
-  }
-  if (a.G > 1) {
-    float* pt = a.partial + (long)tile * a.G * B * 64;
-    if (t < B * 64) pt[g * B * 64 + t] = v;
-    if (!last_arrival(a.tile_cnt + tile, (unsigned)a.G, &flag)) return;
-    if (t < B * 64) {
-      v = 0.f;
-      for (int j = 0; j < a.G; j++) v += __builtin_nontemporal_load(pt + j * B * 64 + t);
-    }
-  }
-  // ---- epilogue
-  if (t < B * 64) {
-    const int bb = t >> 6, row = lt * 64 + (t & 63);
-    if (row < sg.N && bb < nrow) a.y[(long)bb * a.ldy + sg.out_off + row] = v;
-  }
-  if constexpr (EPI == EPI_STORE) return;
-  int grp;
-  unsigned expect;
-  if constexpr (EPI == EPI_QKV) { grp = (sg.out_off + lt * 64) / (a.e.grp_tiles * 64); expect = a.e.grp_tiles; }
-  else if constexpr (EPI == EPI_GATEUP) { grp = lt; expect = 2; }
-  else { grp = 0; expect = (unsigned)(a.seg[0].T); }
-  if (!last_arrival(a.e.grp_cnt + grp, expect, &flag)) return;
-  if constexpr (EPI == EPI_QKV) {
-    epi_head(a, grp, elds);
-  } else if constexpr (EPI == EPI_GATEUP) {
-    const int n = a.e.sp->n;
-    for (int i = threadIdx.x; i < n * 64; i += 256) {
-      const int bb = i >> 6, row = grp * 64 + (i & 63);
-      if (row < a.e.inter) {
-        const float gv = a.y[(long)bb * a.ldy + row];
-        const float uv = a.y[(long)bb * a.ldy + a.e.inter + row];
-        a.e.a_out[(long)bb * a.e.inter + row] = f2h(gelu_tanh(gv) * uv);
+  if (t < B * 16) {
+    const int bb = t >> 4, rr = t & 15;
+    const int row = lt * 16 + rr;
+    if constexpr (EPI == EPI_GATEUP) {
+      float gv = 0.f, uv = 0.f;
+      for (int w = 0; w < a.W; w++) {
+        gv += red[(w * B + bb) * 16 + rr];
+        uv += red[((a.W + w) * B + bb) * 16 + rr];
       }
+      if (row < a.inter && bb < nrow) a.a_out[(long)bb * a.inter + row] = f2h(gelu_tanh(gv) * uv);
+    } else {
+      float v = 0.f;
+      for (int w = 0; w < a.W; w++) v += red[(w * B + bb) * 16 + rr];
+      if (row < a.seg[s].N && bb < nrow) a.y[split * a.y_split + (long)bb * a.ldy + a.seg[s].out_off + row] = v;
     }
-  } else {
-    epi_resid(a, elds);
+  }
+}
+
+// ------------------------------------------------------------- RMSNorm ----
+// One workgroup of 1024 threads per row (H <= 4096): h_new as in NormIn,
+// stored to h_dst (when set), and x = fp16(RMSNorm(h_new) * w_in), the input
+// of the next product.  Every global load of the row is issued up front; the
+// two mean squares are block sums in a fixed order.
+__global__ void __launch_bounds__(1024) k_norm_rows(NormIn p, const StepParams* sp, int n_rows, uint16_t* x) {
+  constexpr int E = 4;
+  __shared__ float nred[16];
+  const int b = blockIdx.x;
+  if (b >= (sp ? sp->n : n_rows)) return;
+  const int H = p.H, tid = threadIdx.x;
+  const float* hs = p.h_src + (long)b * H;
+  const float* y = p.y ? p.y + (long)b * H : nullptr;
+  float hv[E], yv[E], wp[E], wi[E];
+#pragma unroll
+  for (int e = 0; e < E; e++) {
+    const int k = tid + 1024 * e;
+    const bool ok = k < H;
+    hv[e] = ok ? hs[k] : 0.f;
+    wi[e] = ok ? p.w_in[k] : 0.f;
+    yv[e] = 0.f;
+    wp[e] = 0.f;
+    if (y && ok) {
+      float v = y[k];
+      if (p.ny > 1) v += y[p.y_split + k];
+      if (p.ny > 2) v += y[2 * p.y_split + k];
+      if (p.ny > 3) v += y[3 * p.y_split + k];
+      yv[e] = v;
+      wp[e] = p.w_post[k];
+    }
+  }
+  float inv_y = 0.f;
+  if (y) {
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < E; e++) ss += yv[e] * yv[e];
+    ss = block_sum_dyn(ss, nred);
+    inv_y = 1.0f / sqrtf(ss / (float)H + p.eps);
+  }
+  float ss2 = 0.f;
+#pragma unroll
+  for (int e = 0; e < E; e++) {
+    float v = hv[e];
+    if (y) v += yv[e] * inv_y * wp[e];
+    v *= p.scalar;
+    hv[e] = v;
+    ss2 += v * v;
+  }
+  ss2 = block_sum_dyn(ss2, nred);
+  const float inv_h = 1.0f / sqrtf(ss2 / (float)H + p.eps);
+  float* hd = p.h_dst ? p.h_dst + (long)b * H : nullptr;
+#pragma unroll
+  for (int e = 0; e < E; e++) {
+    const int k = tid + 1024 * e;
+    if (k < H) {
+      if (hd) hd[k] = hv[e];
+      x[(long)b * H + k] = f2h(hv[e] * inv_h * wi[e]);
+    }
   }
 }
 
 // ------------------------------------------------------- fp16 tied head ----
 // z[b][r] = E[r] . x[b]; logits = c * tanh(z / c); greedy argmax with the
 // lowest index on ties (gemma4-12b card: tied embeddings, final softcap;
-// 128k card, Limitations: the head emits a greedy argmax id).
+// 128k card, Limitations: the head emits a greedy argmax id).  The argmax is
+// reduced with 64-bit atomicMax on (order key << 32 | ~index) and read out by
+// k_argmax_out after the kernel.
 struct HeadArgs {
   const uint16_t* E;       // [V][H]
   const uint16_t* x;       // [4][H]
   int V, H;
   float softcap;
   float* logits;           // [n][V] or NULL
-  unsigned long long* best;  // [4] packed (key << 32 | ~idx), zeroed before
-  unsigned* cnt;
-  int32_t* argmax;         // [n] or NULL
+  unsigned long long* best;  // [4], zeroed before the kernel
   const StepParams* sp;
   int n_rows;
   int rows_per_wave;
@@ -393,7 +343,6 @@ struct HeadArgs {
 template <int B>
 __global__ void __launch_bounds__(256) k_head(HeadArgs a) {
   __shared__ unsigned long long sbest[4][4];
-  __shared__ int flag;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int n = a.sp ? a.sp->n : a.n_rows;
   const int nchunk = a.H >> 3;           // 16-byte chunks per row
@@ -466,10 +415,16 @@ __global__ void __launch_bounds__(256) k_head(HeadArgs a) {
     for (int w = 0; w < 4; w++) m = sbest[w][threadIdx.x] > m ? sbest[w][threadIdx.x] : m;
     atomicMax(a.best + threadIdx.x, m);
   }
-  if (!last_arrival(a.cnt, gridDim.x, &flag)) return;
-  if (threadIdx.x < n) {
-    const unsigned long long m = atomicExch(a.best + threadIdx.x, 0ull);
-    if (a.argmax) a.argmax[threadIdx.x] = (int32_t)(0xFFFFFFFFu - (uint32_t)(m & 0xFFFFFFFFull));
+}
+
+// Reads the argmax slots out and clears them for the next step.
+__global__ void k_argmax_out(unsigned long long* best, const StepParams* sp, int n_rows, int32_t* argmax) {
+  const int n = sp ? sp->n : n_rows;
+  const int i = threadIdx.x;
+  if (i < 4) {
+    const unsigned long long m = best[i];
+    best[i] = 0ull;
+    if (i < n && argmax) argmax[i] = (int32_t)(0xFFFFFFFFu - (uint32_t)(m & 0xFFFFFFFFull));
   }
 }
 

@@ -6,10 +6,12 @@
 // d = fp16_rne(absmax / 8); q = clamp(round_half_away(w / d), -8, 7), the
 // quotient an IEEE fp32 division against the stored fp16 scale.
 //
-// Device layout (this library's; designed so one wave-wide 16-byte load
-// fetches one q4 block for each of 64 consecutive rows):
-//   codes  [T = ceil(N/64)][NB = K/32][64 rows][16 bytes]
-//   scales [T][NB][64 rows] fp16, right after the codes.
+// Device layout (this library's): one wave-wide 16-byte load fetches a
+// "quad" = 16 consecutive rows x 4 consecutive q4 blocks, lane l holding row
+// (l & 15) and block (l >> 4) of the quad:
+//   codes  [T = ceil(N/16)][NQ = ceil(K/128)][64 lanes][16 bytes]
+//   scales [T][NQ][64 lanes] fp16, right after the codes.
+// Rows past N and blocks past K/32 are padding with zero scale.
 // Inside a block's 16 bytes, 32-bit word w holds elements 8w..8w+7 with the
 // nibble of element 8w+k at bit (k & 1) * 16 + (k >> 1) * 4, so that
 //   (word & 0x000F000F) | 0x64006400  -> fp16 pair (1024 + u0, 1024 + u1)
@@ -27,18 +29,19 @@ __global__ void __launch_bounds__(256) k_q4_pack(const void* __restrict__ w, int
                                                  u4v* __restrict__ codes,
                                                  uint16_t* __restrict__ scales, int T,
                                                  int32_t* nonfinite) {
-  const int NB = K >> 5;
+  const int NB = K >> 5, NQ = (NB + 3) >> 2;
   const long gid = blockIdx.x * (long)blockDim.x + threadIdx.x;
-  const long total = (long)T * NB * 64;
+  const long total = (long)T * NQ * 64;
   if (gid >= total) return;
-  const int r = (int)(gid & 63);
-  const long tb = gid >> 6;            // t * NB + b
-  const int b = (int)(tb % NB);
-  const int t = (int)(tb / NB);
-  const int n = t * 64 + r;
+  const int l = (int)(gid & 63);
+  const long tq = gid >> 6;            // t * NQ + q
+  const int q = (int)(tq % NQ);
+  const int t = (int)(tq / NQ);
+  const int n = t * 16 + (l & 15);
+  const int b = q * 4 + (l >> 4);
   uint32_t wd[4] = {0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u};
   uint16_t d16 = 0;
-  if (n < N) {
+  if (n < N && b < NB) {
     float v[32];
     if (DT == 0) {
       const float4* src = reinterpret_cast<const float4*>(static_cast<const float*>(w) + (long)n * K + b * 32);
@@ -85,19 +88,19 @@ __global__ void __launch_bounds__(256) k_q4_pack(const void* __restrict__ w, int
       for (int i = 0; i < 4; i++) wd[i] = acc[i];
     }
   }
-  codes[tb * 64 + r] = (u4v){wd[0], wd[1], wd[2], wd[3]};
-  scales[tb * 64 + r] = d16;
+  codes[tq * 64 + l] = (u4v){wd[0], wd[1], wd[2], wd[3]};
+  scales[tq * 64 + l] = d16;
 }
 
 // One thread per (row, block): device layout -> canonical 18-byte block.
 __global__ void __launch_bounds__(256) k_q4_unpack(const u4v* __restrict__ codes,
                                                    const uint16_t* __restrict__ scales, int N,
                                                    int K, uint8_t* __restrict__ blocks) {
-  const int NB = K >> 5;
+  const int NB = K >> 5, NQ = (NB + 3) >> 2;
   const long gid = blockIdx.x * (long)blockDim.x + threadIdx.x;
   if (gid >= (long)N * NB) return;
   const int n = (int)(gid / NB), b = (int)(gid % NB);
-  const long src = ((long)(n >> 6) * NB + b) * 64 + (n & 63);
+  const long src = ((long)(n >> 4) * NQ + (b >> 2)) * 64 + (b & 3) * 16 + (n & 15);
   const u4v c = codes[src];
   const uint32_t wd[4] = {c.x, c.y, c.z, c.w};
   const uint16_t d16 = scales[src];

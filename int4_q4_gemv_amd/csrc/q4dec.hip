@@ -24,6 +24,8 @@ namespace {
 constexpr int kMaxRows = 4;
 constexpr int kFullSplits = 256;     // decode-step splits of a full layer's positions
 constexpr int kTilePos = 128;        // positions per workgroup pass (4 waves x 32)
+constexpr int kMaxLds = 160 * 1024;
+constexpr int kSplitQuads = 32;      // decode step: longest run of K quads per workgroup
 
 bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 hipStream_t S(void* s) { return reinterpret_cast<hipStream_t>(s); }
@@ -37,32 +39,44 @@ long ceil_div(long a, long b) { return (a + b - 1) / b; }
 
 // ------------------------------------------------------------- GEMV plan ----
 struct GemvPlan {
-  int T = 0, NB = 0, CB = 0, G = 0;
-  size_t partial_floats(int B) const { return (G > 1) ? (size_t)T * G * B * 64 : 0; }
+  int T = 0, NQ = 0, CQ = 0, W = 0, S = 1, NQs = 0;
 };
 
-GemvPlan gemv_plan(int T, int K) {
+// [N x K] product: S runs of K (NQs quads each; S = 1 unless split_quads > 0
+// caps a run), W waves per tile streaming CQ quads each.  CQ is the smallest
+// of 4, 8, 16 that keeps W within max_waves; W = -1 when none does.
+GemvPlan gemv_plan(int N, int K, int max_waves, int split_quads = 0) {
   GemvPlan p;
-  p.T = T;
-  p.NB = K / 32;
-  const long want = (long)p.NB * T / 1024;     // aim for >= ~1024 waves per launch
-  p.CB = want >= 16 ? 16 : (want >= 8 ? 8 : 4);
-  const int C = (int)ceil_div(p.NB, p.CB);
-  p.G = (int)ceil_div(C, 4);
+  p.T = (int)ceil_div(N, 16);
+  p.NQ = (int)ceil_div(K, 128);
+  p.S = split_quads > 0 ? (int)ceil_div(p.NQ, split_quads) : 1;
+  p.NQs = (int)ceil_div(p.NQ, p.S);
+  p.W = -1;
+  for (int cq : {4, 8, 16}) {
+    const int w = (int)ceil_div(p.NQs, cq);
+    if (w <= max_waves) {
+      p.CQ = cq;
+      p.W = w;
+      break;
+    }
+  }
   return p;
 }
 
+size_t gemv_lds(int B, const GemvPlan& p) { return (size_t)B * p.NQs * 128 * 2; }
+
+// grid: (tiles, splits); waves: per workgroup (both halves for EPI_GATEUP)
 template <int B, int EPI>
-void launch_gemv(const GemvArgs& a, int T, hipStream_t st) {
-  const dim3 grid(T * a.G), block(256);
-  if (a.CB == 16) hipLaunchKernelGGL((k_q4_gemv<B, EPI, 16>), grid, block, 0, st, a);
-  else if (a.CB == 8) hipLaunchKernelGGL((k_q4_gemv<B, EPI, 8>), grid, block, 0, st, a);
-  else hipLaunchKernelGGL((k_q4_gemv<B, EPI, 4>), grid, block, 0, st, a);
+void launch_gemv(const GemvArgs& a, const GemvPlan& p, int tiles, int waves, size_t lds, hipStream_t st) {
+  const dim3 g(tiles, p.S), blk(64 * waves);
+  if (p.CQ == 16) hipLaunchKernelGGL((k_q4_gemv<B, EPI, 16>), g, blk, lds, st, a);
+  else if (p.CQ == 8) hipLaunchKernelGGL((k_q4_gemv<B, EPI, 8>), g, blk, lds, st, a);
+  else hipLaunchKernelGGL((k_q4_gemv<B, EPI, 4>), g, blk, lds, st, a);
 }
 
 void fill_seg(GemvSeg& s, const void* packed, int N, int K, int tile0, int out_off) {
-  const int T = (int)ceil_div(N, 64);
-  const size_t code_bytes = (size_t)T * (K / 32) * 64 * 16;
+  const int T = (int)ceil_div(N, 16);
+  const size_t code_bytes = (size_t)T * ceil_div(K, 128) * 64 * 16;
   s.codes = reinterpret_cast<const u4v*>(packed);
   s.scales = reinterpret_cast<const uint16_t*>(static_cast<const uint8_t*>(packed) + code_bytes);
   s.N = N;
@@ -74,48 +88,71 @@ void fill_seg(GemvSeg& s, const void* packed, int N, int K, int tile0, int out_o
 // ---------------------------------------------------------- attention plan ----
 int fd_split_cap(int n_seq, int n_rows) { return std::max(8, 256 / std::max(1, n_seq * n_rows)); }
 
-bool attn_attr_set = false;
+bool attrs_set = false;
 std::mutex g_mu;
 
-q4_status set_attn_attrs() {
+template <typename F>
+hipError_t max_lds(F* fn) {
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
+                             kMaxLds - 8 * 1024);
+}
+
+template <int B>
+hipError_t gemv_attrs() {
+  hipError_t e = hipSuccess;
+  e = e != hipSuccess ? e : max_lds(&k_q4_gemv<B, EPI_STORE, 4>);
+  e = e != hipSuccess ? e : max_lds(&k_q4_gemv<B, EPI_STORE, 8>);
+  e = e != hipSuccess ? e : max_lds(&k_q4_gemv<B, EPI_STORE, 16>);
+  e = e != hipSuccess ? e : max_lds(&k_q4_gemv<B, EPI_GATEUP, 4>);
+  e = e != hipSuccess ? e : max_lds(&k_q4_gemv<B, EPI_GATEUP, 8>);
+  e = e != hipSuccess ? e : max_lds(&k_q4_gemv<B, EPI_GATEUP, 16>);
+  return e;
+}
+
+q4_status set_attrs() {
   std::lock_guard<std::mutex> lk(g_mu);
-  if (attn_attr_set) return Q4_OK;
-  const int sizes[4] = {64, 128, 256, 512};
-  const void* fns[4] = {reinterpret_cast<const void*>(&k_fd_partial<64>),
-                        reinterpret_cast<const void*>(&k_fd_partial<128>),
-                        reinterpret_cast<const void*>(&k_fd_partial<256>),
-                        reinterpret_cast<const void*>(&k_fd_partial<512>)};
-  for (int i = 0; i < 4; i++) {
-    const int bytes = 4 * 32 * (sizes[i] + 2) * 2;
-    if (hipFuncSetAttribute(fns[i], hipFuncAttributeMaxDynamicSharedMemorySize, bytes) != hipSuccess)
-      return Q4_EHIP;
-  }
-  attn_attr_set = true;
+  if (attrs_set) return Q4_OK;
+  hipError_t e = hipSuccess;
+  e = e != hipSuccess ? e : max_lds(&k_fd_partial<64>);
+  e = e != hipSuccess ? e : max_lds(&k_fd_partial<128>);
+  e = e != hipSuccess ? e : max_lds(&k_fd_partial<256>);
+  e = e != hipSuccess ? e : max_lds(&k_fd_partial<512>);
+  e = e != hipSuccess ? e : gemv_attrs<1>();
+  e = e != hipSuccess ? e : gemv_attrs<4>();
+  if (e != hipSuccess) return Q4_EHIP;
+  attrs_set = true;
   return Q4_OK;
 }
 
-size_t attn_lds_bytes(int D) { return (size_t)4 * 32 * (D + 2) * 2; }
+size_t attn_lds_bytes(int D) {
+  switch (D) {
+    case 64: return fd_lds_bytes<64>();
+    case 128: return fd_lds_bytes<128>();
+    case 256: return fd_lds_bytes<256>();
+    default: return fd_lds_bytes<512>();
+  }
+}
 
 void launch_fd(const AttnArgs& a, int D, int n_seq, float* out32, uint16_t* out16, hipStream_t st) {
   const dim3 grid(a.S, a.Hkv, n_seq * a.n_rows);
-  const dim3 cgrid(n_seq * a.n_rows, a.Hq);
+  const dim3 cgrid(n_seq * a.n_rows * a.Hq, D / 64);
   const size_t lds = attn_lds_bytes(D);
   switch (D) {
     case 64:
       hipLaunchKernelGGL(k_fd_partial<64>, grid, dim3(256), lds, st, a);
-      hipLaunchKernelGGL(k_fd_combine<64>, cgrid, dim3(256), 0, st, a, out32, out16);
+      hipLaunchKernelGGL(k_fd_combine<64>, cgrid, dim3(64), 0, st, a, out32, out16);
       break;
     case 128:
       hipLaunchKernelGGL(k_fd_partial<128>, grid, dim3(256), lds, st, a);
-      hipLaunchKernelGGL(k_fd_combine<128>, cgrid, dim3(256), 0, st, a, out32, out16);
+      hipLaunchKernelGGL(k_fd_combine<128>, cgrid, dim3(64), 0, st, a, out32, out16);
       break;
     case 256:
       hipLaunchKernelGGL(k_fd_partial<256>, grid, dim3(256), lds, st, a);
-      hipLaunchKernelGGL(k_fd_combine<256>, cgrid, dim3(256), 0, st, a, out32, out16);
+      hipLaunchKernelGGL(k_fd_combine<256>, cgrid, dim3(64), 0, st, a, out32, out16);
       break;
     default:
       hipLaunchKernelGGL(k_fd_partial<512>, grid, dim3(256), lds, st, a);
-      hipLaunchKernelGGL(k_fd_combine<512>, cgrid, dim3(256), 0, st, a, out32, out16);
+      hipLaunchKernelGGL(k_fd_combine<512>, cgrid, dim3(64), 0, st, a, out32, out16);
       break;
   }
 }
@@ -124,18 +161,19 @@ bool valid_d(int D) { return D == 64 || D == 128 || D == 256 || D == 512; }
 
 // ------------------------------------------------------ decode-step layout ----
 struct StepLayout {
-  size_t sp, cnt, best, h, x, qkv, qh, o, y, gu, a, gpart, apart, total;
-  int ncnt;
+  size_t sp, best, rope, hA, hB, qkv, o, y, a, xf, apart, total;
   int qkv_ld, o_ld;
   int Dmax;
-  GemvPlan plan_qkv_s, plan_qkv_f, plan_o_s, plan_o_f, plan_gu, plan_d;
+  GemvPlan p_qkv_s, p_qkv_f, p_o_s, p_o_f, p_gu, p_d;
+  int ymax;       // largest split count of a product that writes y
   int S_full, S_ring;
+  bool ok;
 };
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 bool model_dims_ok(const q4dec_model* m) {
-  if (m->hidden < 32 || m->hidden % 32 || m->hidden % 8 || m->hidden > 4096) return false;
+  if (m->hidden < 32 || m->hidden % 32 || m->hidden > 4096) return false;
   if (m->inter < 32 || m->inter % 32) return false;
   if (m->n_heads < 1 || m->n_heads > 16 || m->n_layers < 1 || m->vocab < 1) return false;
   if (!valid_d(m->sl_head_dim) || !valid_d(m->full_head_dim)) return false;
@@ -146,46 +184,42 @@ bool model_dims_ok(const q4dec_model* m) {
   return true;
 }
 
-StepLayout step_layout(const q4dec_model* m, int n) {
-  (void)n;
+StepLayout step_layout(const q4dec_model* m) {
   StepLayout L{};
   const int H = m->hidden, I = m->inter, Hq = m->n_heads;
   const int Ds = m->sl_head_dim, Df = m->full_head_dim, Hs = m->sl_kv_heads;
   L.Dmax = std::max(Ds, Df);
   L.qkv_ld = std::max(Hq * Ds + 2 * Hs * Ds, Hq * Df + Df);
   L.o_ld = Hq * L.Dmax;
-  L.plan_qkv_s = gemv_plan((int)(ceil_div(Hq * Ds, 64) + 2 * ceil_div(Hs * Ds, 64)), H);
-  L.plan_qkv_f = gemv_plan((int)(ceil_div(Hq * Df, 64) + ceil_div(Df, 64)), H);
-  L.plan_o_s = gemv_plan((int)ceil_div(H, 64), Hq * Ds);
-  L.plan_o_f = gemv_plan((int)ceil_div(H, 64), Hq * Df);
-  L.plan_gu = gemv_plan((int)(2 * ceil_div(I, 64)), H);
-  L.plan_d = gemv_plan((int)ceil_div(H, 64), I);
+  // Products whose K is long are split so that each has enough workgroups;
+  // gate/up keeps K whole (its epilogue needs both full sums).
+  L.p_qkv_s = gemv_plan(Hq * Ds + 2 * Hs * Ds, H, 8);
+  L.p_qkv_f = gemv_plan(Hq * Df + Df, H, 8);
+  L.p_o_s = gemv_plan(H, Hq * Ds, 8, kSplitQuads);
+  L.p_o_f = gemv_plan(H, Hq * Df, 8, kSplitQuads);
+  L.p_gu = gemv_plan(I, H, 4);
+  L.p_d = gemv_plan(H, I, 8, kSplitQuads);
+  L.ymax = std::max(std::max(L.p_o_s.S, L.p_o_f.S), L.p_d.S);
+  L.ok = true;
+  for (const GemvPlan* p : {&L.p_qkv_s, &L.p_qkv_f, &L.p_o_s, &L.p_o_f, &L.p_gu, &L.p_d})
+    if (p->W < 1 || gemv_lds(kMaxRows, *p) > (size_t)kMaxLds - 8 * 1024) L.ok = false;
+  if (L.p_gu.S != 1 || L.ymax > 4) L.ok = false;
   L.S_full = kFullSplits;
   L.S_ring = (int)std::min<long>(16, std::max<long>(1, ceil_div(m->window, kTilePos)));
-  size_t gpart = 0;
-  for (const GemvPlan* p : {&L.plan_qkv_s, &L.plan_qkv_f, &L.plan_o_s, &L.plan_o_f, &L.plan_gu, &L.plan_d})
-    gpart = std::max(gpart, p->partial_floats(kMaxRows));
-  int maxT = 0;
-  for (const GemvPlan* p : {&L.plan_qkv_s, &L.plan_qkv_f, &L.plan_o_s, &L.plan_o_f, &L.plan_gu, &L.plan_d})
-    maxT = std::max(maxT, p->T);
-  // counters: tile counters, group counters, head counter
-  L.ncnt = maxT + maxT + 8;
   const size_t apart_full = (size_t)kMaxRows * 1 * L.S_full * Hq * (Df + 4);
   const size_t apart_ring = (size_t)kMaxRows * Hs * L.S_ring * (Hq / Hs) * (Ds + 4);
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off = align256(off + bytes); return o; };
   L.sp = take(sizeof(StepParams));
-  L.cnt = take(sizeof(unsigned) * L.ncnt);
   L.best = take(sizeof(unsigned long long) * 4);
-  L.h = take(sizeof(float) * kMaxRows * H);
-  L.x = take(sizeof(uint16_t) * kMaxRows * std::max(H, I));
+  L.rope = take(sizeof(double) * (m->sl_rot_pairs + m->full_rot_pairs + 1));
+  L.hA = take(sizeof(float) * kMaxRows * H);
+  L.hB = take(sizeof(float) * kMaxRows * H);
   L.qkv = take(sizeof(float) * kMaxRows * L.qkv_ld);
-  L.qh = take(sizeof(uint16_t) * kMaxRows * Hq * L.Dmax);
   L.o = take(sizeof(uint16_t) * kMaxRows * L.o_ld);
-  L.y = take(sizeof(float) * kMaxRows * H);
-  L.gu = take(sizeof(float) * kMaxRows * 2 * I);
+  L.y = take(sizeof(float) * L.ymax * kMaxRows * H);
   L.a = take(sizeof(uint16_t) * kMaxRows * I);
-  L.gpart = take(sizeof(float) * std::max<size_t>(gpart, 64));
+  L.xf = take(sizeof(uint16_t) * kMaxRows * H);
   L.apart = take(sizeof(float) * std::max(apart_full, apart_ring));
   L.total = off;
   return L;
@@ -193,47 +227,49 @@ StepLayout step_layout(const q4dec_model* m, int n) {
 
 struct StepPtrs {
   StepParams* sp;
-  unsigned* cnt;
   unsigned long long* best;
-  float *h, *qkv, *y, *gu, *gpart, *apart;
-  uint16_t *x, *qh, *o, *a;
+  double* rope;
+  float *hA, *hB, *qkv, *y, *apart;
+  uint16_t *o, *a, *xf;
 };
 
 StepPtrs step_ptrs(const StepLayout& L, void* ws) {
   uint8_t* b = static_cast<uint8_t*>(ws);
   StepPtrs p;
   p.sp = reinterpret_cast<StepParams*>(b + L.sp);
-  p.cnt = reinterpret_cast<unsigned*>(b + L.cnt);
   p.best = reinterpret_cast<unsigned long long*>(b + L.best);
-  p.h = reinterpret_cast<float*>(b + L.h);
-  p.x = reinterpret_cast<uint16_t*>(b + L.x);
+  p.rope = reinterpret_cast<double*>(b + L.rope);
+  p.hA = reinterpret_cast<float*>(b + L.hA);
+  p.hB = reinterpret_cast<float*>(b + L.hB);
   p.qkv = reinterpret_cast<float*>(b + L.qkv);
-  p.qh = reinterpret_cast<uint16_t*>(b + L.qh);
   p.o = reinterpret_cast<uint16_t*>(b + L.o);
   p.y = reinterpret_cast<float*>(b + L.y);
-  p.gu = reinterpret_cast<float*>(b + L.gu);
   p.a = reinterpret_cast<uint16_t*>(b + L.a);
-  p.gpart = reinterpret_cast<float*>(b + L.gpart);
+  p.xf = reinterpret_cast<uint16_t*>(b + L.xf);
   p.apart = reinterpret_cast<float*>(b + L.apart);
   return p;
 }
 
+// Launch sequence of one step (every kernel reads positions and the row
+// count from the device-side StepParams, so the sequence is position-free):
+// per layer: input RMSNorm of the residual stream (with the previous layer's
+// post-FF residual), q/k/v projections, attention (q/k/v finishing +
+// split-K partials), combine, output projection, post-attention residual and
+// pre-FF norm, gate/up with GELU * up, down projection; then the final norm,
+// the tied head and the argmax read-out.
 template <int B>
 q4_status enqueue_layers(const q4dec_model* m, const StepLayout& L, const StepPtrs& P, int n,
                          float* logits, int32_t* argmax, hipStream_t st) {
   const int H = m->hidden, I = m->inter, Hq = m->n_heads;
-  unsigned* tile_cnt = P.cnt;
-  unsigned* grp_cnt = P.cnt + (L.ncnt - 8) / 2;
-  unsigned* head_cnt = P.cnt + L.ncnt - 1;
   for (int l = 0; l < m->n_layers; l++) {
     const q4dec_layer& ly = m->layers[l];
     const bool full = ly.is_full != 0;
     const int D = full ? m->full_head_dim : m->sl_head_dim;
     const int Hkv = full ? 1 : m->sl_kv_heads;
-    // ---- q/k/v projections; last arrival per head finishes norm, RoPE, cache write
+    // ---- q/k/v projections
     {
       GemvArgs a{};
-      const GemvPlan& pl = full ? L.plan_qkv_f : L.plan_qkv_s;
+      const GemvPlan& pl = full ? L.p_qkv_f : L.p_qkv_s;
       int t0 = 0;
       fill_seg(a.seg[0], ly.wq, Hq * D, H, t0, 0);
       t0 += a.seg[0].T;
@@ -245,84 +281,94 @@ q4_status enqueue_layers(const q4dec_model* m, const StepLayout& L, const StepPt
         t0 += a.seg[2].T;
         a.nseg = 3;
       }
-      a.K = H; a.NB = pl.NB; a.CB = pl.CB; a.G = pl.G;
-      a.x = P.x; a.ldx = H; a.y = P.qkv; a.ldy = L.qkv_ld;
-      a.partial = P.gpart; a.tile_cnt = tile_cnt; a.n_rows = n;
-      EpiArgs& e = a.e;
-      e.sp = P.sp; e.grp_cnt = grp_cnt; e.grp_tiles = D / 64;
-      e.Hq = Hq; e.Hkv = Hkv; e.D = D; e.is_full = full; e.v_norm = ly.v_norm;
-      e.rot_pairs = full ? m->full_rot_pairs : m->sl_rot_pairs;
-      e.R = m->ring; e.theta = full ? m->full_theta : m->sl_theta; e.eps = m->eps;
-      e.q_norm = ly.q_norm; e.k_norm = ly.k_norm; e.q_out = P.qh;
-      e.k_cache = ly.k_cache; e.v_cache = ly.v_cache;
-      launch_gemv<B, EPI_QKV>(a, t0, st);
+      NormIn ni{};
+      if (l == 0) { ni.h_src = P.hA; ni.y = nullptr; ni.w_post = nullptr; ni.scalar = 1.0f; ni.h_dst = nullptr; }
+      else {
+        const q4dec_layer& prev = m->layers[l - 1];
+        ni.h_src = P.hB; ni.y = P.y; ni.w_post = prev.post_ff_norm; ni.scalar = prev.layer_scalar; ni.h_dst = P.hA;
+        ni.ny = L.p_d.S; ni.y_split = (long)n * H;
+      }
+      ni.w_in = ly.attn_norm; ni.H = H; ni.eps = m->eps;
+      hipLaunchKernelGGL(k_norm_rows, dim3(n), dim3(1024), 0, st, ni, P.sp, n, P.xf);
+      a.K = H; a.NQ = pl.NQ; a.W = pl.W; a.NQs = pl.NQs;
+      a.x = P.xf; a.ldx = H;
+      a.y = P.qkv; a.ldy = L.qkv_ld; a.n_rows = n; a.sp = P.sp;
+      launch_gemv<B, EPI_STORE>(a, pl, t0, pl.W, gemv_lds(B, pl), st);
     }
-    // ---- attention
+    // ---- attention: q/k/v finishing, split-K partials, combine
     {
       AttnArgs a{};
-      a.q = P.qh; a.k = ly.k_cache; a.v = ly.v_cache; a.seq_stride = 0;
+      a.q = nullptr; a.k = ly.k_cache; a.v = ly.v_cache; a.seq_stride = 0;
       a.Hq = Hq; a.Hkv = Hkv; a.GQ = Hq / Hkv;
       a.ring = full ? 0 : 1; a.R = m->ring; a.W = m->window;
       a.n_rows = n; a.S = full ? L.S_full : L.S_ring;
       a.scale_log2 = (full ? m->full_scale : m->sl_scale) * 1.4426950408889634f;
       a.sp = P.sp; a.part = P.apart;
+      a.fin_on = 1;
+      a.fin.qkv = P.qkv; a.fin.ldq = L.qkv_ld; a.fin.q_norm = ly.q_norm; a.fin.k_norm = ly.k_norm;
+      a.fin.v_norm = ly.v_norm; a.fin.rot_pairs = full ? m->full_rot_pairs : m->sl_rot_pairs;
+      a.fin.inv_freq = full ? P.rope + m->sl_rot_pairs : P.rope; a.fin.eps = m->eps;
       launch_fd(a, D, 1, nullptr, P.o, st);
     }
-    // ---- output projection + post-attention norm residual + pre-FF norm
+    // ---- output projection
     {
       GemvArgs a{};
-      const GemvPlan& pl = full ? L.plan_o_f : L.plan_o_s;
+      const GemvPlan& pl = full ? L.p_o_f : L.p_o_s;
       fill_seg(a.seg[0], ly.wo, H, Hq * D, 0, 0);
       a.nseg = 1;
-      a.K = Hq * D; a.NB = pl.NB; a.CB = pl.CB; a.G = pl.G;
-      a.x = P.o; a.ldx = Hq * D; a.y = P.y; a.ldy = H;
-      a.partial = P.gpart; a.tile_cnt = tile_cnt; a.n_rows = n;
-      EpiArgs& e = a.e;
-      e.sp = P.sp; e.grp_cnt = grp_cnt; e.H = H; e.h = P.h; e.eps = m->eps;
-      e.w_post = ly.post_attn_norm; e.w_next = ly.pre_ff_norm; e.scalar = 1.0f; e.x_out = P.x;
-      launch_gemv<B, EPI_RESID>(a, a.seg[0].T, st);
+      a.K = Hq * D; a.NQ = pl.NQ; a.W = pl.W; a.NQs = pl.NQs;
+      a.x = P.o; a.ldx = Hq * D;
+      a.y = P.y; a.ldy = H; a.y_split = (long)n * H; a.n_rows = n; a.sp = P.sp;
+      launch_gemv<B, EPI_STORE>(a, pl, a.seg[0].T, pl.W, gemv_lds(B, pl), st);
     }
-    // ---- gate/up with GELU(gate) * up
+    // ---- gate/up with GELU(gate) * up; post-attention residual + pre-FF norm in the prologue
     {
       GemvArgs a{};
-      const GemvPlan& pl = L.plan_gu;
+      const GemvPlan& pl = L.p_gu;
       fill_seg(a.seg[0], ly.wg, I, H, 0, 0);
-      fill_seg(a.seg[1], ly.wu, I, H, a.seg[0].T, I);
+      fill_seg(a.seg[1], ly.wu, I, H, 0, 0);
       a.nseg = 2;
-      a.K = H; a.NB = pl.NB; a.CB = pl.CB; a.G = pl.G;
-      a.x = P.x; a.ldx = H; a.y = P.gu; a.ldy = 2 * I;
-      a.partial = P.gpart; a.tile_cnt = tile_cnt; a.n_rows = n;
-      EpiArgs& e = a.e;
-      e.sp = P.sp; e.grp_cnt = grp_cnt; e.inter = I; e.a_out = P.a;
-      launch_gemv<B, EPI_GATEUP>(a, 2 * a.seg[0].T, st);
+      NormIn ni{};
+      ni.h_src = P.hA; ni.y = P.y; ni.ny = (full ? L.p_o_f : L.p_o_s).S; ni.y_split = (long)n * H;
+      ni.w_post = ly.post_attn_norm; ni.scalar = 1.0f;
+      ni.w_in = ly.pre_ff_norm; ni.h_dst = P.hB; ni.H = H; ni.eps = m->eps;
+      hipLaunchKernelGGL(k_norm_rows, dim3(n), dim3(1024), 0, st, ni, P.sp, n, P.xf);
+      a.K = H; a.NQ = pl.NQ; a.W = pl.W; a.NQs = pl.NQs;
+      a.x = P.xf; a.ldx = H;
+      a.a_out = P.a; a.inter = I; a.n_rows = n; a.sp = P.sp;
+      launch_gemv<B, EPI_GATEUP>(a, pl, a.seg[0].T, 2 * pl.W, gemv_lds(B, pl), st);
     }
-    // ---- down projection + post-FF norm residual, layer scalar, next norm
+    // ---- down projection
     {
       GemvArgs a{};
-      const GemvPlan& pl = L.plan_d;
+      const GemvPlan& pl = L.p_d;
       fill_seg(a.seg[0], ly.wd, H, I, 0, 0);
       a.nseg = 1;
-      a.K = I; a.NB = pl.NB; a.CB = pl.CB; a.G = pl.G;
-      a.x = P.a; a.ldx = I; a.y = P.y; a.ldy = H;
-      a.partial = P.gpart; a.tile_cnt = tile_cnt; a.n_rows = n;
-      EpiArgs& e = a.e;
-      e.sp = P.sp; e.grp_cnt = grp_cnt; e.H = H; e.h = P.h; e.eps = m->eps;
-      e.w_post = ly.post_ff_norm; e.scalar = ly.layer_scalar; e.x_out = P.x;
-      e.w_next = (l + 1 < m->n_layers) ? m->layers[l + 1].attn_norm : m->final_norm;
-      launch_gemv<B, EPI_RESID>(a, a.seg[0].T, st);
+      a.K = I; a.NQ = pl.NQ; a.W = pl.W; a.NQs = pl.NQs;
+      a.x = P.a; a.ldx = I;
+      a.y = P.y; a.ldy = H; a.y_split = (long)n * H; a.n_rows = n; a.sp = P.sp;
+      launch_gemv<B, EPI_STORE>(a, pl, a.seg[0].T, pl.W, gemv_lds(B, pl), st);
     }
   }
-  // ---- tied fp16 head, softcap, argmax
+  // ---- final norm (post-FF residual of the last layer), tied head, argmax
+  {
+    const q4dec_layer& last = m->layers[m->n_layers - 1];
+    NormIn ni{};
+    ni.h_src = P.hB; ni.y = P.y; ni.ny = L.p_d.S; ni.y_split = (long)n * H;
+    ni.w_post = last.post_ff_norm; ni.scalar = last.layer_scalar;
+    ni.w_in = m->final_norm; ni.h_dst = P.hA; ni.H = H; ni.eps = m->eps;
+    hipLaunchKernelGGL(k_norm_rows, dim3(n), dim3(1024), 0, st, ni, P.sp, n, P.xf);
+  }
   {
     HeadArgs a{};
-    a.E = m->embed; a.x = P.x; a.V = m->vocab; a.H = H; a.softcap = m->softcap;
-    a.logits = logits; a.best = P.best; a.cnt = head_cnt; a.argmax = argmax;
-    a.sp = P.sp; a.n_rows = n;
+    a.E = m->embed; a.x = P.xf; a.V = m->vocab; a.H = H; a.softcap = m->softcap;
+    a.logits = logits; a.best = P.best; a.sp = P.sp; a.n_rows = n;
     const int waves = 8192;
     a.rows_per_wave = (int)std::max<long>(2, ceil_div(m->vocab, waves));
     if (a.rows_per_wave & 1) a.rows_per_wave++;
     const int grid = (int)ceil_div(ceil_div(m->vocab, a.rows_per_wave), 4);
     hipLaunchKernelGGL((k_head<B>), dim3(grid), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(k_argmax_out, dim3(1), dim3(64), 0, st, P.best, P.sp, n, argmax);
   }
   return launch_status();
 }
@@ -370,14 +416,16 @@ std::string graph_key(const q4dec_model* m, int n, const void* ws, size_t ws_byt
   return k;
 }
 
-q4_status begin_step(const q4dec_model* m, const StepLayout& L, const StepPtrs& P, const int32_t* tokens,
-                     int n, int pos0, hipStream_t st) {
+q4_status begin_step(const q4dec_model* m, const StepPtrs& P, const int32_t* tokens, int n, int pos0,
+                     hipStream_t st) {
   BeginArgs b{};
   b.sp = P.sp; b.pos0 = pos0; b.n = n;
   for (int i = 0; i < 4; i++) b.tokens[i] = i < n ? tokens[i] : 0;
-  b.cnt = P.cnt; b.ncnt = L.ncnt; b.best = P.best;
+  b.best = P.best;
   b.E = m->embed; b.H = m->hidden; b.emb_scale = (float)std::sqrt((double)m->hidden);
-  b.h = P.h; b.w_norm = m->layers[0].attn_norm; b.eps = m->eps; b.x = P.x;
+  b.h = P.hA;
+  b.inv_freq = P.rope; b.ns = m->sl_rot_pairs; b.nf = m->full_rot_pairs;
+  b.Ds = m->sl_head_dim; b.Df = m->full_head_dim; b.theta_s = m->sl_theta; b.theta_f = m->full_theta;
   hipLaunchKernelGGL(k_step_begin, dim3(n), dim3(256), 0, st, b);
   return launch_status();
 }
@@ -388,13 +436,14 @@ q4_status decode_step_impl(const q4dec_model* m, const int32_t* tokens, int n, i
   if (rc != Q4_OK) return rc;
   if (!ws) return Q4_EINVAL;
   if (!al16(ws) || (logits && !al16(logits))) return Q4_EALIGN;
-  const StepLayout L = step_layout(m, n);
+  const StepLayout L = step_layout(m);
+  if (!L.ok) return Q4_ESHAPE;
   if (ws_bytes < L.total) return Q4_ENOSPACE;
-  rc = set_attn_attrs();
+  rc = set_attrs();
   if (rc != Q4_OK) return rc;
   const StepPtrs P = step_ptrs(L, ws);
   hipStream_t st = S(stream);
-  rc = begin_step(m, L, P, tokens, n, pos0, st);
+  rc = begin_step(m, P, tokens, n, pos0, st);
   if (rc != Q4_OK) return rc;
   if (!use_graph || st == nullptr) {
     return n == 1 ? enqueue_layers<1>(m, L, P, n, logits, argmax, st)
@@ -414,11 +463,11 @@ q4_status decode_step_impl(const q4dec_model* m, const int32_t* tokens, int n, i
     hipGraph_t graph = nullptr;
     hipError_t e = hipStreamEndCapture(st, &graph);
     if (r2 != Q4_OK || e != hipSuccess || !graph) {
-      if (graph) hipGraphDestroy(graph);
+      if (graph) (void)hipGraphDestroy(graph);
       return Q4_EHIP;
     }
     e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
-    hipGraphDestroy(graph);
+    (void)hipGraphDestroy(graph);
     if (e != hipSuccess) return Q4_EHIP;
     std::lock_guard<std::mutex> lk(g_mu);
     g_graphs[key] = exec;
@@ -449,7 +498,7 @@ const char* q4dec_version(void) { return "q4dec 0.1 gfx950"; }
 
 size_t q4_packed_bytes(int N, int K) {
   if (N < 1 || K < 32 || K % 32) return 0;
-  return (size_t)ceil_div(N, 64) * 64 * (K / 32) * 18;
+  return (size_t)ceil_div(N, 16) * 16 * ceil_div(K, 128) * 4 * 18;
 }
 
 q4_status q4_pack(const void* w, int w_dtype, int N, int K, void* packed, size_t packed_bytes,
@@ -459,8 +508,8 @@ q4_status q4_pack(const void* w, int w_dtype, int N, int K, void* packed, size_t
   if (N < 1 || K < 32 || K % 32) return Q4_ESHAPE;
   if (packed_bytes < q4_packed_bytes(N, K)) return Q4_ENOSPACE;
   if (!al16(w) || !al16(packed)) return Q4_EALIGN;
-  const int T = (int)ceil_div(N, 64);
-  const long total = (long)T * (K / 32) * 64;
+  const int T = (int)ceil_div(N, 16);
+  const long total = (long)T * ceil_div(K, 128) * 64;
   const size_t code_bytes = (size_t)total * 16;
   u4v* codes = static_cast<u4v*>(packed);
   uint16_t* scales = reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(packed) + code_bytes);
@@ -476,8 +525,8 @@ q4_status q4_unpack(const void* packed, int N, int K, uint8_t* blocks, void* str
   if (!packed || !blocks) return Q4_EINVAL;
   if (N < 1 || K < 32 || K % 32) return Q4_ESHAPE;
   if (!al16(packed)) return Q4_EALIGN;
-  const int T = (int)ceil_div(N, 64);
-  const size_t code_bytes = (size_t)T * (K / 32) * 64 * 16;
+  const int T = (int)ceil_div(N, 16);
+  const size_t code_bytes = (size_t)T * ceil_div(K, 128) * 64 * 16;
   const u4v* codes = static_cast<const u4v*>(packed);
   const uint16_t* scales = reinterpret_cast<const uint16_t*>(static_cast<const uint8_t*>(packed) + code_bytes);
   const long total = (long)N * (K / 32);
@@ -486,29 +535,21 @@ q4_status q4_unpack(const void* packed, int N, int K, uint8_t* blocks, void* str
   return launch_status();
 }
 
-size_t q4_gemv_workspace_size(int N, int K, int B) {
-  if (N < 1 || K < 32 || K % 32 || B < 1 || B > kMaxRows) return 0;
-  const GemvPlan p = gemv_plan((int)ceil_div(N, 64), K);
-  const size_t cnt = align256(sizeof(unsigned) * p.T);
-  return cnt + align256(sizeof(float) * std::max<size_t>(64, p.partial_floats(B == 1 ? 1 : 4)));
-}
-
-q4_status q4_gemv(const void* packed, int N, int K, const uint16_t* x, int B, float* y, void* ws,
-                  size_t ws_bytes, void* stream) {
-  if (!packed || !x || !y || !ws) return Q4_EINVAL;
+q4_status q4_gemv(const void* packed, int N, int K, const uint16_t* x, int B, float* y, void* stream) {
+  if (!packed || !x || !y) return Q4_EINVAL;
   if (N < 1 || K < 32 || K % 32 || B < 1 || B > kMaxRows) return Q4_ESHAPE;
-  if (ws_bytes < q4_gemv_workspace_size(N, K, B)) return Q4_ENOSPACE;
-  if (!al16(packed) || !al16(x) || !al16(y) || !al16(ws)) return Q4_EALIGN;
-  const GemvPlan p = gemv_plan((int)ceil_div(N, 64), K);
+  const GemvPlan p = gemv_plan(N, K, B == 1 ? 16 : 8);
+  if (p.W < 1 || gemv_lds(B == 1 ? 1 : 4, p) > (size_t)kMaxLds - 8 * 1024) return Q4_ESHAPE;
+  if (!al16(packed) || !al16(x) || !al16(y)) return Q4_EALIGN;
+  q4_status rc = set_attrs();
+  if (rc != Q4_OK) return rc;
   GemvArgs a{};
   fill_seg(a.seg[0], packed, N, K, 0, 0);
   a.nseg = 1;
-  a.K = K; a.NB = p.NB; a.CB = p.CB; a.G = p.G;
-  a.x = x; a.ldx = K; a.y = y; a.ldy = N; a.n_rows = B;
-  a.tile_cnt = static_cast<unsigned*>(ws);
-  a.partial = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + align256(sizeof(unsigned) * p.T));
-  if (B == 1) launch_gemv<1, EPI_STORE>(a, p.T, S(stream));
-  else launch_gemv<4, EPI_STORE>(a, p.T, S(stream));
+  a.K = K; a.NQ = p.NQ; a.W = p.W; a.NQs = p.NQs;
+  a.x = x; a.ldx = K; a.y = y; a.ldy = N; a.n_rows = B; a.sp = nullptr;
+  if (B == 1) launch_gemv<1, EPI_STORE>(a, p, p.T, p.W, gemv_lds(1, p), S(stream));
+  else launch_gemv<4, EPI_STORE>(a, p, p.T, p.W, gemv_lds(4, p), S(stream));
   return launch_status();
 }
 
@@ -541,10 +582,10 @@ q4_status flash_decode_full(const uint16_t* q, const uint16_t* k, const uint16_t
     if (pos0[s] < 0 || (long)pos0[s] + n_rows - 1 >= cap) return Q4_ERANGE;
     maxlen = std::max(maxlen, (long)pos0[s] + n_rows);
   }
-  rc = set_attn_attrs();
+  rc = set_attrs();
   if (rc != Q4_OK) return rc;
   AttnArgs a{};
-  a.q = q; a.k = k; a.v = v; a.seq_stride = seq_stride;
+  a.q = q; a.k = const_cast<uint16_t*>(k); a.v = const_cast<uint16_t*>(v); a.seq_stride = seq_stride;
   a.Hq = Hq; a.Hkv = 1; a.GQ = Hq; a.ring = 0; a.R = cap; a.W = cap;
   a.n_rows = n_rows;
   a.S = (int)std::min<long>(fd_split_cap(n_seq, n_rows), std::max<long>(1, ceil_div(maxlen, kTilePos)));
@@ -565,10 +606,10 @@ q4_status flash_decode_ring(const uint16_t* q, const uint16_t* k_ring, const uin
   if (n_seq > 1 && seq_stride < (int64_t)Hkv * R * D) return Q4_ESHAPE;
   for (int s = 0; s < n_seq; s++)
     if (pos0[s] < 0 || (long)pos0[s] + n_rows - 1 > 0x7FFFFFFFL) return Q4_ERANGE;
-  rc = set_attn_attrs();
+  rc = set_attrs();
   if (rc != Q4_OK) return rc;
   AttnArgs a{};
-  a.q = q; a.k = k_ring; a.v = v_ring; a.seq_stride = seq_stride;
+  a.q = q; a.k = const_cast<uint16_t*>(k_ring); a.v = const_cast<uint16_t*>(v_ring); a.seq_stride = seq_stride;
   a.Hq = Hq; a.Hkv = Hkv; a.GQ = Hq / Hkv; a.ring = 1; a.R = R; a.W = W;
   a.n_rows = n_rows;
   a.S = (int)std::min<long>(fd_split_cap(n_seq, n_rows), std::max<long>(1, ceil_div(W, kTilePos)));
@@ -581,7 +622,20 @@ q4_status flash_decode_ring(const uint16_t* q, const uint16_t* k_ring, const uin
 
 size_t decode_step_workspace_size(const q4dec_model* m, int n) {
   if (!m || n < 1 || n > kMaxRows || !model_dims_ok(m)) return 0;
-  return step_layout(m, n).total;
+  const StepLayout L = step_layout(m);
+  return L.ok ? L.total : 0;
+}
+
+q4_status decode_step_hidden(const q4dec_model* m, const void* ws, size_t ws_bytes, int n, float* h_out,
+                             void* stream) {
+  if (!m || !ws || !h_out) return Q4_EINVAL;
+  if (n < 1 || n > kMaxRows || !model_dims_ok(m)) return Q4_ESHAPE;
+  const StepLayout L = step_layout(m);
+  if (ws_bytes < L.total) return Q4_ENOSPACE;
+  const void* src = static_cast<const uint8_t*>(ws) + L.hA;
+  if (hipMemcpyAsync(h_out, src, sizeof(float) * n * m->hidden, hipMemcpyDeviceToDevice, S(stream)) != hipSuccess)
+    return Q4_EHIP;
+  return Q4_OK;
 }
 
 q4_status decode_step(const q4dec_model* m, const int32_t* tokens, int n, int pos0, float* logits,

@@ -10,22 +10,20 @@ struct BeginArgs {
   StepParams* sp;
   int pos0, n;
   int tokens[4];
-  unsigned* cnt;            // counters to clear
-  int ncnt;
   unsigned long long* best; // [4] argmax slots
   const uint16_t* E;        // [vocab][H] fp16
   int H;
   float emb_scale;          // sqrt(H)
   float* h;                 // [4][H]
-  const float* w_norm;      // first layer's attention-input norm
-  float eps;
-  uint16_t* x;              // [4][H]
+  double* inv_freq;         // [ns + nf]: RoPE inverse frequencies, sliding then full
+  int ns, nf, Ds, Df;
+  double theta_s, theta_f;
 };
 
-// One workgroup per row.  h = fp32(E[token]) * sqrt(H) (reading of the
-// embedding scale), x = fp16(RMSNorm(h) * w).
+// One workgroup per row: h = fp32(E[token]) * sqrt(H) (reading of the
+// embedding scale); workgroup 0 also publishes the step parameters and the
+// RoPE inverse frequencies theta^(-2i/D) in fp64 (one table per layer kind).
 __global__ void __launch_bounds__(256) k_step_begin(BeginArgs a) {
-  __shared__ float red[4];
   const int b = blockIdx.x, tid = threadIdx.x;
   if (b == 0) {
     if (tid == 0) {
@@ -33,21 +31,14 @@ __global__ void __launch_bounds__(256) k_step_begin(BeginArgs a) {
       a.sp->n = a.n;
       for (int i = 0; i < 4; i++) a.sp->tokens[i] = a.tokens[i];
     }
-    for (int i = tid; i < a.ncnt; i += 256) a.cnt[i] = 0u;
     if (tid < 4) a.best[tid] = 0ull;
+    for (int i = tid; i < a.ns + a.nf; i += 256)
+      a.inv_freq[i] = i < a.ns ? pow(a.theta_s, -2.0 * (double)i / (double)a.Ds)
+                               : pow(a.theta_f, -2.0 * (double)(i - a.ns) / (double)a.Df);
   }
-  const int tok = a.tokens[b];
-  const uint16_t* e = a.E + (long)tok * a.H;
+  const uint16_t* e = a.E + (long)a.tokens[b] * a.H;
   float* h = a.h + (long)b * a.H;
-  float ss = 0.f;
-  for (int i = tid; i < a.H; i += 256) {
-    const float v = h2f(e[i]) * a.emb_scale;
-    h[i] = v;
-    ss += v * v;
-  }
-  ss = block_sum<256>(ss, red);
-  const float inv = 1.0f / sqrtf(ss / (float)a.H + a.eps);
-  for (int i = tid; i < a.H; i += 256) a.x[(long)b * a.H + i] = f2h(h[i] * inv * a.w_norm[i]);
+  for (int i = tid; i < a.H; i += 256) h[i] = h2f(e[i]) * a.emb_scale;
 }
 
 }  // namespace q4k

@@ -21,6 +21,29 @@ def assert_close(gpu, ref, atol=ATOL, rtol=RTOL, what=""):
                              f"gpu {g[i]!r} oracle {r[i]!r}")
 
 
+def assert_close_composed(gpu, ref, atol=ATOL, rtol=RTOL, frac=0.995, factor=4.0, what=""):
+    """The bar for outputs of a composition with fp16 rounding points inside
+    it (a whole layer and the 262144-row head): at least ``frac`` of the
+    elements within the fp32 bar, every element within ``factor`` times it,
+    and the RMS error under half the absolute bar.  In scale-1 attention the
+    fp32-vs-fp64 accumulation error of the scores flips fp16 roundings of the
+    attention output, so two correct fp32 implementations already differ by
+    about the bar on a few elements; the kernel-level outputs keep the
+    elementwise bar (assert_close)."""
+    g = gpu.detach().double().cpu().numpy() if torch.is_tensor(gpu) else np.asarray(gpu, np.float64)
+    r = np.asarray(ref, dtype=np.float64)
+    assert g.shape == r.shape, (what, g.shape, r.shape)
+    assert np.isfinite(g).all(), f"{what}: non-finite GPU output"
+    err = np.abs(g - r)
+    bound = atol + rtol * np.abs(r)
+    inside = float((err <= bound).mean())
+    worst = float((err / bound).max())
+    rms = float(np.sqrt((err ** 2).mean()))
+    assert inside >= frac and worst <= factor and rms <= atol / 2, (
+        f"{what}: {inside:.5f} of elements within the bar (need {frac}), worst error/bound {worst:.2f} "
+        f"(need <= {factor}), rms error {rms:.2e} (need <= {atol / 2:.1e})")
+
+
 def f16bits(t):
     return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
 

@@ -37,9 +37,8 @@ def test_status_strings_and_sizes():
     for s in (-1, -2, -3, -4, -5, -6):
         assert L.q4dec_status_str(s).startswith(b"Q4_E")
     assert q4.packed_bytes(3840, 15360) == 33_177_600
-    assert q4.packed_bytes(100, 64) == 128 * 2 * 18        # rows padded to the 64-row tile
+    assert q4.packed_bytes(100, 64) == 112 * 4 * 18         # 16-row tiles, 4-block quads
     assert q4.packed_bytes(10, 48) == 0                     # K not a multiple of 32
-    assert L.q4_gemv_workspace_size(3840, 15360, 5) == 0    # B outside 1..4
     assert L.flash_decode_workspace_size(1, 1, 16, 96) == 0  # unsupported head_dim
 
 
@@ -52,8 +51,11 @@ def test_argument_checks_fail_before_launch():
     assert L.q4_pack(fake, 0, 64, 48, fake, 1 << 20, None, None) == q4.Q4_ESHAPE
     assert L.q4_pack(fake, 0, 64, 64, fake, 10, None, None) == q4.Q4_ENOSPACE
     assert L.q4_pack(odd, 0, 64, 64, fake, 1 << 20, None, None) == q4.Q4_EALIGN
-    assert L.q4_gemv(fake, 64, 64, fake, 5, fake, fake, 1 << 20, None) == q4.Q4_ESHAPE
-    assert L.q4_gemv(fake, 64, 64, fake, 1, fake, fake, 0, None) == q4.Q4_ENOSPACE
+    assert L.q4_gemv(fake, 64, 64, fake, 5, fake, None) == q4.Q4_ESHAPE
+    assert L.q4_gemv(fake, 64, 40, fake, 1, fake, None) == q4.Q4_ESHAPE
+    assert L.q4_gemv(fake, 64, 65536, fake, 1, fake, None) == q4.Q4_ESHAPE
+    assert L.q4_gemv(None, 64, 64, fake, 1, fake, None) == q4.Q4_EINVAL
+    assert L.q4_gemv(odd, 64, 64, fake, 1, fake, None) == q4.Q4_EALIGN
     pos = (C.c_int32 * 1)(100)
     ws = 1 << 30
     # position beyond capacity
@@ -90,5 +92,7 @@ def test_decode_step_checks():
     assert L.decode_step(C.byref(m), tok, 1, 5, f, f, f, C.c_size_t(16), None) == q4.Q4_ENOSPACE
     bad = (C.c_int32 * 1)(cfg.vocab)
     assert L.decode_step(C.byref(m), bad, 1, 5, f, f, f, big, None) == q4.Q4_ERANGE
+    assert L.decode_step_hidden(C.byref(m), f, C.c_size_t(16), 1, f, None) == q4.Q4_ENOSPACE
+    assert L.decode_step_hidden(C.byref(m), f, big, 5, f, None) == q4.Q4_ESHAPE
     m.ring = cfg.window + 2      # a 4-row block needs R >= W + 3
     assert L.decode_step(C.byref(m), tok, 4, 5, f, f, f, big, None) == q4.Q4_ERANGE

@@ -75,7 +75,7 @@ def _grid_weights(N, K, seed, unit=False):
 
 
 @pytest.mark.parametrize("B", [1, 4])
-@pytest.mark.parametrize("N,K", [(64, 64), (200, 512), (130, 4096)])
+@pytest.mark.parametrize("N,K", [(64, 64), (200, 512), (130, 4096), (33, 96), (17, 16384)])
 def test_gemv_one_hot_bit_exact(orc, N, K, B):
     print(f"gemv one-hot N={N} K={K} B={B}", flush=True)
     q, d, w = _grid_weights(N, K, N + K)
@@ -115,15 +115,14 @@ def test_gemv_random_vs_oracle(orc, N, K, B):
     assert_close(y, ref, what=f"q4_gemv N={N} K={K} B={B}")
 
 
-def test_gemv_deterministic_and_workspace_reusable():
+@pytest.mark.parametrize("B", [1, 4])
+def test_gemv_deterministic(B):
     N, K = 3840, 15360
-    w, x = synth.gemv_inputs(N, K, 1, seed_w=1, seed_x=2, device=DEV)
+    w, x = synth.gemv_inputs(N, K, B, seed_w=1, seed_x=2, device=DEV)
     packed = q4.q4_pack(w)
-    g = q4.Gemv(N, K, 1)
-    y1 = g(packed, x).clone()
-    y2 = g(packed, x).clone()
+    y1 = q4.q4_gemv(packed, N, K, x).clone()
+    y2 = q4.q4_gemv(packed, N, K, x).clone()
     assert torch.equal(y1, y2)
-    assert int(g.ws[: 4 * 60].view(torch.int32).abs().sum().item()) == 0   # counters back at zero
 
 
 @pytest.mark.parametrize("B", [1, 4])

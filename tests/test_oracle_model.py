@@ -214,3 +214,24 @@ def test_layerwise_parts_compose_to_the_step(orc):
         h = b.run_layer(l, h, 90)
     parts, am2 = b.run_head(h)
     assert np.array_equal(whole, parts) and np.array_equal(am, am2)
+
+
+def test_deep_random_stack_amplifies_last_bit_changes(orc):
+    """Why the 48-layer step is compared per layer: in the oracle itself, a
+    1-ulp change of one fp16 embedding element moves the logits of a 48-layer
+    toy-width stack (scale-1 attention) by far more than the fp32 parity bar
+    and more than ten times as much as a 2-layer stack."""
+    from dataclasses import replace
+    tol = 2e-3
+    moved = {}
+    for nl in (2, 48):
+        cfg = replace(synth.TOY, n_layers=nl, full_every=6)
+        m = build_oracle_model(orc, cfg, 7, 200)
+        toks = synth.tokens(cfg, 1, 7)
+        a, _ = clone(m).decode_step(toks, 200)
+        b = clone(m)
+        b.embed = b.embed.copy()
+        b.embed[int(toks[0]), 5] ^= 1
+        lb, _ = b.decode_step(toks, 200)
+        moved[nl] = float(np.abs(a - lb).max())
+    assert moved[48] > 10 * moved[2] and moved[48] > 10 * tol, moved
