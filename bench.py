@@ -164,7 +164,7 @@ def main():
             ach = nbytes / avg_s / 1e9
             out["roofline"] = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_GBPS, "unit": "GB/s",
                                "frac": round(ach / PEAK_GBPS, 4), "traffic": None,
-                               "kernel": "k_q4_gemv<1,0,8> (q4_gemv, B=1, 3840->15360, 960 workgroups x 8 waves)",
+                               "kernel": "k_q4_gemv<1,0,4> (q4_gemv, B=1, 3840->15360, 960 workgroups x 8 waves)",
                                "bytes_per_launch": nbytes, "avg_launch_us": round(avg_s * 1e6, 3),
                                "launches": launches}
             log(f"q4_gemv 3840->15360: {avg_s * 1e6:.2f} us/launch, {ach:.0f} GB/s")

@@ -64,35 +64,35 @@ Q4_DEV long attn_rec(const AttnArgs& a, int seq, int row, int kvh, int split, in
   return (((((long)seq * a.n_rows + row) * a.Hkv + kvh) * a.S + split) * a.GQ + col) * (long)(D + 4);
 }
 
+// LDS of k_fd_partial: V rows [4 waves][32][pitch] (pitch D + 2 halves when
+// staged from registers, D when loaded straight into LDS with swizzled
+// chunks), rows of this step newK / newV [4][D], finished queries q16 [16][D].
+template <int D>
+constexpr int fd_vpitch() { return D <= 256 ? D + 2 : D; }
+
 template <int D>
 constexpr size_t fd_lds_bytes() {
-  return (size_t)4 * 32 * (D + 2) * 2 + (size_t)2 * 4 * D * 2;
+  return (size_t)4 * 32 * fd_vpitch<D>() * 2 + (size_t)2 * 4 * D * 2 + (size_t)16 * D * 2;
 }
 
 // Per-head RMSNorm (weight w, or scale-free when w == NULL) and RoPE at
 // position pos on one head vector, done by one wave; src fp32 [D] -> dst
-// fp16 [D].  scratch: D floats of this wave's LDS.
+// fp16 [D] (LDS).  Lane l holds elements l + 64e; the rotated pairs (i,
+// i + D/2) then sit in one lane (D >= 128) or in lanes l and l + 32 (D = 64).
 template <int D>
-Q4_DEV void finish_head(const float* src, const float* w, bool rope, int pos, const AttnFin& f,
-                        float* scratch, uint16_t* dst) {
+Q4_DEV void finish_head(const float* src, const float* w, bool rope, int pos, const AttnFin& f, uint16_t* dst) {
+  constexpr int E = D / 64;
   const int lane = threadIdx.x & 63;
-  float v[D / 64 > 0 ? D / 64 : 1];
+  float v[E];
   float ss = 0.f;
 #pragma unroll
-  for (int e = 0; e < D / 64; e++) { v[e] = src[lane + 64 * e]; ss += v[e] * v[e]; }
+  for (int e = 0; e < E; e++) { v[e] = src[lane + 64 * e]; ss += v[e] * v[e]; }
   ss = wave_sum(ss);
   const float inv = 1.0f / sqrtf(ss / (float)D + f.eps);
 #pragma unroll
-  for (int e = 0; e < D / 64; e++) {
-    const int d = lane + 64 * e;
-    scratch[d] = v[e] * inv * (w ? w[d] : 1.0f);
-  }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-  constexpr int half = D / 2;
-  for (int i = lane; i < half; i += 64) {
-    float x0 = scratch[i], x1 = scratch[i + half];
+  for (int e = 0; e < E; e++) v[e] = v[e] * inv * (w ? w[lane + 64 * e] : 1.0f);
+  // rotate pair i = lane + 64e (first half) with i + D/2
+  auto rot = [&](int i, float& x0, float& x1) {
     if (rope && i < f.rot_pairs) {
       // angle pos * theta^(-2i/D) in fp64, reduced to [-pi, pi] in fp64 by
       // one fma with the double nearest 2 pi (k * 2.5e-16 rad of error, under
@@ -106,8 +106,20 @@ Q4_DEV void finish_head(const float* src, const float* w, bool rope, int pos, co
       const float y1 = x1 * c + x0 * s;
       x0 = y0; x1 = y1;
     }
-    dst[i] = f2h(x0);
-    dst[i + half] = f2h(x1);
+  };
+  if constexpr (E == 1) {
+    float other = __shfl_xor(v[0], 32, 64);
+    float x0 = lane < 32 ? v[0] : other, x1 = lane < 32 ? other : v[0];
+    rot(lane & 31, x0, x1);
+    dst[lane] = f2h(lane < 32 ? x0 : x1);
+  } else {
+#pragma unroll
+    for (int e = 0; e < E / 2; e++) {
+      float x0 = v[e], x1 = v[e + E / 2];
+      rot(lane + 64 * e, x0, x1);
+      dst[lane + 64 * e] = f2h(x0);
+      dst[lane + 64 * e + D / 2] = f2h(x1);
+    }
   }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
   __builtin_amdgcn_wave_barrier();
@@ -116,13 +128,14 @@ Q4_DEV void finish_head(const float* src, const float* w, bool rope, int pos, co
 
 template <int D>
 __global__ void __launch_bounds__(256) k_fd_partial(AttnArgs a) {
-  constexpr int VROW = D + 2;                 // LDS row pitch (halves): 1-dword pad
+  constexpr int VROW = fd_vpitch<D>();        // LDS row pitch of the V rows (halves)
   constexpr int NDS = D / 16;                 // PV dim steps
   constexpr int NKS = D / 32;                 // QK k steps
   extern __shared__ __align__(16) unsigned char smem[];
   uint16_t* vlds = reinterpret_cast<uint16_t*>(smem);
   uint16_t* newK = vlds + 4 * 32 * VROW;      // [4][D] rows of this step (decode step)
   uint16_t* newV = newK + 4 * D;
+  uint16_t* q16 = newV + 4 * D;               // [16][D] finished queries (decode step)
   __shared__ float wm[4][16], wl[4][16];
 
   const int split = blockIdx.x, kvh = blockIdx.y;
@@ -145,49 +158,106 @@ __global__ void __launch_bounds__(256) k_fd_partial(AttnArgs a) {
   uint16_t* kb = a.k + seq * a.seq_stride + (a.ring ? (long)kvh * a.R * D : 0);
   uint16_t* vb = a.v + seq * a.seq_stride + (a.ring ? (long)kvh * a.R * D : 0);
 
+  // ---- K and V of this wave's first tile, issued before anything waits.
+  // MFMA row r of half h <-> tile position 8*(r/4) + 4h + r%4, so lane
+  // (column j, group g) ends up holding positions 8g .. 8g+7 of the tile.
+  // Rows formed in this step (p >= P0new) are not in the cache yet: their
+  // lanes load cache row 0 and are patched from LDS after the prologue.
+  constexpr int VCH = D / 16;                 // 16-byte V chunks per lane per tile
+  constexpr bool HV = D <= 256;               // the tile's K and V are loaded before the
+                                              // prologue, V held in registers and staged
+                                              // to LDS rows of pitch VROW.  D = 512: loaded
+                                              // after it, V straight into LDS rows of
+                                              // pitch D whose 16-byte chunks are swizzled
+                                              // (chunk c of row r at c ^ ((r >> 3) & 3))
+  static_assert(HV || D == 512, "direct V loads assume one 1 KB row per instruction");
+  uint16_t* vl = vlds + wave * 32 * VROW;
+  h8_t KA[NKS], KB[NKS];
+  u4v VV[HV ? VCH : 1];
+  auto cache_row = [&](int p) -> long {
+    return (p < en && p < P0new) ? (long)(a.ring ? p % a.R : p) * D : 0l;
+  };
+  auto load_k = [&](int t0) {
+    const int pa = t0 + 8 * (j >> 2) + (j & 3);
+    const uint16_t* ka = kb + cache_row(pa) + 8 * g;
+    const uint16_t* kc = kb + cache_row(pa + 4) + 8 * g;
+#pragma unroll
+    for (int s = 0; s < NKS; s++) {
+      KA[s] = __builtin_bit_cast(h8_t, __builtin_nontemporal_load(reinterpret_cast<const u4v*>(ka + 32 * s)));
+      KB[s] = __builtin_bit_cast(h8_t, __builtin_nontemporal_load(reinterpret_cast<const u4v*>(kc + 32 * s)));
+    }
+  };
+  auto load_v = [&](int t0) {
+    if constexpr (HV) {
+#pragma unroll
+      for (int i = 0; i < VCH; i++) {
+        const int c = lane + 64 * i, r = c / (D / 8), cc = c - r * (D / 8);
+        VV[i] = __builtin_nontemporal_load(reinterpret_cast<const u4v*>(vb + cache_row(t0 + r) + cc * 8));
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 32; r++) {
+        const int c = lane ^ ((r >> 3) & 3);
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint32_t*>(vb + cache_row(t0 + r) + c * 8),
+                                         reinterpret_cast<uint32_t*>(vl + r * D), 16, 0, 0);
+      }
+    }
+  };
+  // the first tile: V (and for D <= 256 also K) before the prologue; K of
+  // D = 512 (128 registers) waits for the prologue's registers to free up
+  int t0 = st + 32 * wave;
+  if (t0 < en) {
+    load_v(t0);
+    if (HV) load_k(t0);
+  }
+
   // ---- queries of this workgroup's columns as the MFMA B operand
   h8_t qb[NKS];
   if (a.fin_on) {
     const AttnFin& f = a.fin;
-    uint16_t* q16 = vlds;                                   // [16][D], aliases the V rows
-    float* scratch = reinterpret_cast<float*>(vlds + 16 * D) + wave * D;
-    for (int c = wave; c < a.GQ; c += 4) {
-      const int h = kvh * a.GQ + c;
-      finish_head<D>(f.qkv + (long)row * f.ldq + (long)h * D, f.q_norm, true, P, f, scratch, q16 + c * D);
-    }
-    // rows of this step inside [st, en): wave r forms row r (k, then v)
-    if (wave < nlive && wave <= row) {
-      const int p = base + wave;
-      if (p >= st && p < en) {
-        const float* raw = f.qkv + (long)wave * f.ldq;
-        const float* rk = raw + (long)(a.Hq + kvh) * D;
-        finish_head<D>(rk, f.k_norm, true, p, f, scratch, newK + wave * D);
+    // finishing jobs dealt round-robin to the waves: the query heads of this
+    // workgroup's columns, then k and v of each row of this step that lies
+    // in [st, en) and that this row attends (rows r0 .. r1)
+    const int r0 = max(0, st - base), r1 = min(row, en - 1 - base);
+    const int njobs = a.GQ + 2 * max(0, r1 - r0 + 1);
+    for (int jb = wave; jb < njobs; jb += 4) {
+      if (jb < a.GQ) {
+        const int h = kvh * a.GQ + jb;
+        finish_head<D>(f.qkv + (long)row * f.ldq + (long)h * D, f.q_norm, true, P, f, q16 + jb * D);
+        continue;
+      }
+      const int r = r0 + ((jb - a.GQ) >> 1), p = base + r;
+      const float* raw = f.qkv + (long)r * f.ldq;
+      const float* rk = raw + (long)(a.Hq + kvh) * D;
+      if (((jb - a.GQ) & 1) == 0) {
+        finish_head<D>(rk, f.k_norm, true, p, f, newK + r * D);
+      } else {
         const float* rv = a.ring ? raw + (long)(a.Hq + a.Hkv + kvh) * D : rk;  // full: V from raw k
         if (f.v_norm) {
-          finish_head<D>(rv, nullptr, false, p, f, scratch, newV + wave * D);
+          finish_head<D>(rv, nullptr, false, p, f, newV + r * D);
         } else {
-          for (int d = lane; d < D; d += 64) newV[wave * D + d] = f2h(rv[d]);
+          for (int d = lane; d < D; d += 64) newV[r * D + d] = f2h(rv[d]);
           __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
           __builtin_amdgcn_wave_barrier();
           __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
         }
-        if (wave == row) {     // this workgroup owns position p: store the row
-          const long so = (long)(a.ring ? p % a.R : p) * D;
-          for (int d = lane; d < D; d += 64) {
-            kb[so + d] = newK[wave * D + d];
-            vb[so + d] = newV[wave * D + d];
-          }
-        }
       }
     }
     __syncthreads();
+    // the workgroup whose own row lies in its range stores that row
+    if (P >= st && P < en) {
+      const long so = (long)(a.ring ? P % a.R : P) * D;
+      for (int d = threadIdx.x; d < D; d += 256) {
+        kb[so + d] = newK[row * D + d];
+        vb[so + d] = newV[row * D + d];
+      }
+    }
 #pragma unroll
     for (int s = 0; s < NKS; s++) {
       u4v t = *reinterpret_cast<const u4v*>(q16 + (col_ok ? j : 0) * D + 32 * s + 8 * g);
       if (!col_ok) t = (u4v){0u, 0u, 0u, 0u};
       qb[s] = __builtin_bit_cast(h8_t, t);
     }
-    __syncthreads();
   } else {
     const uint16_t* qp = a.q + (((long)seq * a.n_rows + row) * a.Hq + (col_ok ? kvh * a.GQ + j : 0)) * D + 8 * g;
 #pragma unroll
@@ -197,60 +267,57 @@ __global__ void __launch_bounds__(256) k_fd_partial(AttnArgs a) {
       qb[s] = __builtin_bit_cast(h8_t, t);
     }
   }
-  uint16_t* vl = vlds + wave * 32 * VROW;
 
   float m_run = -INFINITY, l_part = 0.f;
   f4_t O[NDS];
 #pragma unroll
   for (int d = 0; d < NDS; d++) O[d] = (f4_t){0.f, 0.f, 0.f, 0.f};
 
-  for (int t0 = st + 32 * wave; t0 < en; t0 += 128) {
-    // MFMA row r of half h <-> tile position 8*(r/4) + 4h + r%4, so lane
-    // (column j, group g) ends up holding positions 8g .. 8g+7 of the tile.
-    const bool fresh = t0 + 31 >= P0new;      // this tile may hold rows of this step
-    const int pa = t0 + 8 * (j >> 2) + (j & 3);
-    const int pb = pa + 4;
-    const int pac = pa < en ? pa : st, pbc = pb < en ? pb : st;
-    const int sa = a.ring ? pac % a.R : pac;
-    const int sb = a.ring ? pbc % a.R : pbc;
-    f4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-    {
-      const uint16_t* ka = (fresh && pac >= P0new) ? newK + (pac - P0new) * D + 8 * g : kb + (long)sa * D + 8 * g;
-      const uint16_t* kc = (fresh && pbc >= P0new) ? newK + (pbc - P0new) * D + 8 * g : kb + (long)sb * D + 8 * g;
-      h8_t KA[NKS], KB[NKS];
-      if (!fresh) {
-#pragma unroll
-        for (int s = 0; s < NKS; s++) {
-          KA[s] = __builtin_bit_cast(h8_t, __builtin_nontemporal_load(reinterpret_cast<const u4v*>(ka + 32 * s)));
-          KB[s] = __builtin_bit_cast(h8_t, __builtin_nontemporal_load(reinterpret_cast<const u4v*>(kc + 32 * s)));
-        }
-      } else {
-#pragma unroll
-        for (int s = 0; s < NKS; s++) {
-          KA[s] = __builtin_bit_cast(h8_t, *reinterpret_cast<const u4v*>(ka + 32 * s));
-          KB[s] = __builtin_bit_cast(h8_t, *reinterpret_cast<const u4v*>(kc + 32 * s));
-        }
-      }
-      // stage the V tile (32 positions) into this wave's LDS rows
-#pragma unroll 4
-      for (int c = lane; c < 32 * (D / 8); c += 64) {
-        const int r = c / (D / 8), cc = c - r * (D / 8);
-        const int p = t0 + r;
-        const int pc = p < en ? p : st;
-        u4v vv;
-        if (fresh && pc >= P0new) vv = *reinterpret_cast<const u4v*>(newV + (pc - P0new) * D + cc * 8);
-        else {
-          const int sl = a.ring ? pc % a.R : pc;
-          vv = __builtin_nontemporal_load(reinterpret_cast<const u4v*>(vb + (long)sl * D + cc * 8));
-        }
-        uint32_t* dst = reinterpret_cast<uint32_t*>(vl + r * VROW + cc * 8);
-        dst[0] = vv.x; dst[1] = vv.y; dst[2] = vv.z; dst[3] = vv.w;
-      }
+  for (bool first = true; t0 < en; t0 += 128, first = false) {
+    if (!first) load_v(t0);
+    if (!first || !HV) load_k(t0);
+    if (t0 + 31 >= P0new) {                   // patch the rows formed in this step
+      const int pa = t0 + 8 * (j >> 2) + (j & 3), pb = pa + 4;
 #pragma unroll
       for (int s = 0; s < NKS; s++) {
-        s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(KA[s], qb[s], s0, 0, 0, 0);
-        s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(KB[s], qb[s], s1, 0, 0, 0);
+        if (pa >= P0new && pa < en) KA[s] = *reinterpret_cast<const h8_t*>(newK + (pa - P0new) * D + 32 * s + 8 * g);
+        if (pb >= P0new && pb < en) KB[s] = *reinterpret_cast<const h8_t*>(newK + (pb - P0new) * D + 32 * s + 8 * g);
       }
+      if constexpr (HV) {
+#pragma unroll
+        for (int i = 0; i < VCH; i++) {
+          const int c = lane + 64 * i, r = c / (D / 8), cc = c - r * (D / 8);
+          const int p = t0 + r;
+          if (p >= P0new && p < en) VV[i] = *reinterpret_cast<const u4v*>(newV + (p - P0new) * D + cc * 8);
+        }
+      }
+    }
+    // stage the V tile (32 positions) into this wave's LDS rows
+    if constexpr (HV) {
+#pragma unroll
+      for (int i = 0; i < VCH; i++) {
+        const int c = lane + 64 * i, r = c / (D / 8), cc = c - r * (D / 8);
+        uint32_t* dst = reinterpret_cast<uint32_t*>(vl + r * VROW + cc * 8);
+        dst[0] = VV[i].x; dst[1] = VV[i].y; dst[2] = VV[i].z; dst[3] = VV[i].w;
+      }
+    } else {
+      // the direct loads have landed; rows of this step overwrite theirs
+      __builtin_amdgcn_s_waitcnt(0);
+      __asm__ __volatile__("" ::: "memory");
+      if (t0 + 31 >= P0new) {
+        for (int r = 0; r < 32; r++) {
+          const int p = t0 + r;
+          if (p >= P0new && p < en)
+            *reinterpret_cast<u4v*>(vl + r * D + lane * 8) =
+                *reinterpret_cast<const u4v*>(newV + (p - P0new) * D + (lane ^ ((r >> 3) & 3)) * 8);
+        }
+      }
+    }
+    f4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < NKS; s++) {
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(KA[s], qb[s], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(KB[s], qb[s], s1, 0, 0, 0);
     }
     // lane (j, g): reg i of s0 -> position t0 + 8g + i; of s1 -> t0 + 8g + 4 + i
     float sv[8];
@@ -292,10 +359,12 @@ __global__ void __launch_bounds__(256) k_fd_partial(AttnArgs a) {
     // O += P V: B operand lane (dim 16d + j, group g) = V[8g .. 8g+7][dim]
 #pragma unroll
     for (int d = 0; d < NDS; d++) {
-      const uint16_t* vc = vl + 8 * g * VROW + 16 * d + j;
+      constexpr int PITCH = HV ? VROW : D;
+      const uint16_t* vc = HV ? vl + 8 * g * VROW + 16 * d + j
+                              : vl + 8 * g * D + ((2 * d + (j >> 3)) ^ g) * 8 + (j & 7);
       h8_t Bv;
 #pragma unroll
-      for (int e = 0; e < 8; e++) Bv[e] = __builtin_bit_cast(_Float16, vc[e * VROW]);
+      for (int e = 0; e < 8; e++) Bv[e] = __builtin_bit_cast(_Float16, vc[e * PITCH]);
       O[d] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ahi, Bv, O[d], 0, 0, 0);
       O[d] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Alo, Bv, O[d], 0, 0, 0);
     }
@@ -337,41 +406,56 @@ __global__ void __launch_bounds__(256) k_fd_partial(AttnArgs a) {
 }
 
 // out[seq][row][h][d] = sum_s O_s 2^(m_s - M) / sum_s l_s 2^(m_s - M).
-// Grid (n_seq * n_rows * Hq, D / 64); one wave per 64 output dims.
-template <int D>
-__global__ void __launch_bounds__(64) k_fd_combine(AttnArgs a, float* out32, uint16_t* out16) {
-  __shared__ float wsp[256];
+// Grid (n_seq * n_rows * Hq, D / 64), 256 threads: lane = output dim, wave w
+// takes splits w, w + 4, ... (S <= MAXS).  Every load of the workgroup is
+// issued before the first use (split indices past S are clamped and their
+// weight is zero), and the four wave sums meet in LDS in a fixed order.
+constexpr int kMaxSplits = 256;
+
+template <int D, int MAXS>
+__global__ void __launch_bounds__(256) k_fd_combine(AttnArgs a, float* out32, uint16_t* out16) {
+  constexpr int PER = MAXS / 4;
+  __shared__ float wsp[MAXS];
+  __shared__ float red[4][64];
+  __shared__ float rm[4], rl[4];
   const int idx = blockIdx.x;
   const int h = idx % a.Hq, sr = idx / a.Hq;
   const int seq = sr / a.n_rows, row = sr - seq * a.n_rows;
-  const int nlive = a.sp ? a.sp->n : a.n_rows;
-  if (row >= nlive) return;
   const int kvh = h / a.GQ, col = h - kvh * a.GQ;
-  const int lane = threadIdx.x;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const long r0 = attn_rec(a, seq, row, kvh, 0, col, D);
   const long rs = (long)a.GQ * (D + 4);                // stride between splits
-  float M = -INFINITY;
-  for (int s = lane; s < a.S; s += 64) M = fmaxf(M, a.part[r0 + s * rs + D]);
-  M = wave_max(M);
-  float L = 0.f;
-  for (int s = lane; s < a.S; s += 64) {
-    const float m = a.part[r0 + s * rs + D];
-    const float w = (m == -INFINITY) ? 0.f : exp2f(m - M);
-    wsp[s] = w;
-    L += w * a.part[r0 + s * rs + D + 1];
-  }
-  L = wave_sum(L);
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
   const int d = blockIdx.y * 64 + lane;
+  const int S = a.S;
+  const bool own = tid < S;
+  const long mo = r0 + (long)min(tid, S - 1) * rs + D;
+  const float m_raw = a.part[mo], l_raw = a.part[mo + 1];
+  float ov[PER];
+#pragma unroll
+  for (int i = 0; i < PER; i++) ov[i] = a.part[r0 + (long)min(wave + 4 * i, S - 1) * rs + d];
+  const float m = own ? m_raw : -INFINITY;
+  float M = wave_max(m);
+  if (lane == 0) rm[wave] = M;
+  __syncthreads();
+  M = fmaxf(fmaxf(rm[0], rm[1]), fmaxf(rm[2], rm[3]));
+  const float w = (own && m != -INFINITY) ? exp2f(m - M) : 0.f;
+  if (tid < MAXS) wsp[tid] = w;
+  float L = wave_sum(w * (own ? l_raw : 0.f));
+  if (lane == 0) rl[wave] = L;
+  __syncthreads();
+  L = ((rl[0] + rl[1]) + rl[2]) + rl[3];
   float o = 0.f;
-#pragma unroll 8
-  for (int s = 0; s < a.S; s++) o += wsp[s] * a.part[r0 + s * rs + d];
-  o *= (L > 0.f) ? 1.0f / L : 0.f;
-  const long oi = (((long)seq * a.n_rows + row) * a.Hq + h) * D + d;
-  if (out32) out32[oi] = o;
-  if (out16) out16[oi] = f2h(o);
+#pragma unroll
+  for (int i = 0; i < PER; i++) o += wsp[wave + 4 * i] * ov[i];
+  red[wave][lane] = o;
+  __syncthreads();
+  if (wave == 0) {
+    o = ((red[0][lane] + red[1][lane]) + red[2][lane]) + red[3][lane];
+    o *= (L > 0.f) ? 1.0f / L : 0.f;
+    const long oi = (((long)seq * a.n_rows + row) * a.Hq + h) * D + d;
+    if (out32) out32[oi] = o;
+    if (out16) out16[oi] = f2h(o);
+  }
 }
 
 }  // namespace q4k

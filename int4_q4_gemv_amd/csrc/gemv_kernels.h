@@ -266,31 +266,34 @@ __global__ void __launch_bounds__(B == 1 ? 1024 : 512) k_q4_gemv(GemvArgs a) {
 // stored to h_dst (when set), and x = fp16(RMSNorm(h_new) * w_in), the input
 // of the next product.  Every global load of the row is issued up front; the
 // two mean squares are block sums in a fixed order.
-__global__ void __launch_bounds__(1024) k_norm_rows(NormIn p, const StepParams* sp, int n_rows, uint16_t* x) {
+__global__ void __launch_bounds__(1024) k_norm_rows(NormIn p, uint16_t* x) {
   constexpr int E = 4;
   __shared__ float nred[16];
-  const int b = blockIdx.x;
-  if (b >= (sp ? sp->n : n_rows)) return;
+  const int b = blockIdx.x;               // grid: the rows of the step
   const int H = p.H, tid = threadIdx.x;
   const float* hs = p.h_src + (long)b * H;
   const float* y = p.y ? p.y + (long)b * H : nullptr;
+  // partial products past ny alias the first one and are dropped below, so
+  // every load is unconditional and all of them are in flight together
+  const float* y0 = y ? y : hs;
+  const float* y1 = p.ny > 1 ? y0 + p.y_split : y0;
+  const float* y2 = p.ny > 2 ? y0 + 2 * p.y_split : y0;
+  const float* y3 = p.ny > 3 ? y0 + 3 * p.y_split : y0;
+  const float* wpp = y ? p.w_post : p.w_in;
   float hv[E], yv[E], wp[E], wi[E];
 #pragma unroll
   for (int e = 0; e < E; e++) {
-    const int k = tid + 1024 * e;
-    const bool ok = k < H;
-    hv[e] = ok ? hs[k] : 0.f;
-    wi[e] = ok ? p.w_in[k] : 0.f;
-    yv[e] = 0.f;
-    wp[e] = 0.f;
-    if (y && ok) {
-      float v = y[k];
-      if (p.ny > 1) v += y[p.y_split + k];
-      if (p.ny > 2) v += y[2 * p.y_split + k];
-      if (p.ny > 3) v += y[3 * p.y_split + k];
-      yv[e] = v;
-      wp[e] = p.w_post[k];
-    }
+    const int k = min(tid + 1024 * e, H - 1);
+    hv[e] = hs[k];
+    wi[e] = p.w_in[k];
+    wp[e] = wpp[k];
+    const float a0 = y0[k], a1 = y1[k], a2 = y2[k], a3 = y3[k];
+    float v = a0;
+    if (p.ny > 1) v += a1;
+    if (p.ny > 2) v += a2;
+    if (p.ny > 3) v += a3;
+    yv[e] = (y && tid + 1024 * e < H) ? v : 0.f;
+    if (tid + 1024 * e >= H) hv[e] = 0.f;
   }
   float inv_y = 0.f;
   if (y) {

@@ -124,36 +124,22 @@ q4_status set_attrs() {
   return Q4_OK;
 }
 
-size_t attn_lds_bytes(int D) {
-  switch (D) {
-    case 64: return fd_lds_bytes<64>();
-    case 128: return fd_lds_bytes<128>();
-    case 256: return fd_lds_bytes<256>();
-    default: return fd_lds_bytes<512>();
-  }
+template <int D>
+void launch_fd_d(const AttnArgs& a, int n_seq, float* out32, uint16_t* out16, hipStream_t st) {
+  const dim3 grid(a.S, a.Hkv, n_seq * a.n_rows);
+  const dim3 cgrid(n_seq * a.n_rows * a.Hq, D / 64);  // 256 threads each
+  hipLaunchKernelGGL(k_fd_partial<D>, grid, dim3(256), fd_lds_bytes<D>(), st, a);
+  if (a.S <= 16) hipLaunchKernelGGL((k_fd_combine<D, 16>), cgrid, dim3(256), 0, st, a, out32, out16);
+  else hipLaunchKernelGGL((k_fd_combine<D, kMaxSplits>), cgrid, dim3(256), 0, st, a, out32, out16);
 }
 
+// Split-K partials then the combine (S <= kMaxSplits).
 void launch_fd(const AttnArgs& a, int D, int n_seq, float* out32, uint16_t* out16, hipStream_t st) {
-  const dim3 grid(a.S, a.Hkv, n_seq * a.n_rows);
-  const dim3 cgrid(n_seq * a.n_rows * a.Hq, D / 64);
-  const size_t lds = attn_lds_bytes(D);
   switch (D) {
-    case 64:
-      hipLaunchKernelGGL(k_fd_partial<64>, grid, dim3(256), lds, st, a);
-      hipLaunchKernelGGL(k_fd_combine<64>, cgrid, dim3(64), 0, st, a, out32, out16);
-      break;
-    case 128:
-      hipLaunchKernelGGL(k_fd_partial<128>, grid, dim3(256), lds, st, a);
-      hipLaunchKernelGGL(k_fd_combine<128>, cgrid, dim3(64), 0, st, a, out32, out16);
-      break;
-    case 256:
-      hipLaunchKernelGGL(k_fd_partial<256>, grid, dim3(256), lds, st, a);
-      hipLaunchKernelGGL(k_fd_combine<256>, cgrid, dim3(64), 0, st, a, out32, out16);
-      break;
-    default:
-      hipLaunchKernelGGL(k_fd_partial<512>, grid, dim3(256), lds, st, a);
-      hipLaunchKernelGGL(k_fd_combine<512>, cgrid, dim3(64), 0, st, a, out32, out16);
-      break;
+    case 64: launch_fd_d<64>(a, n_seq, out32, out16, st); break;
+    case 128: launch_fd_d<128>(a, n_seq, out32, out16, st); break;
+    case 256: launch_fd_d<256>(a, n_seq, out32, out16, st); break;
+    default: launch_fd_d<512>(a, n_seq, out32, out16, st); break;
   }
 }
 
@@ -205,7 +191,7 @@ StepLayout step_layout(const q4dec_model* m) {
     if (p->W < 1 || gemv_lds(kMaxRows, *p) > (size_t)kMaxLds - 8 * 1024) L.ok = false;
   if (L.p_gu.S != 1 || L.ymax > 4) L.ok = false;
   L.S_full = kFullSplits;
-  L.S_ring = (int)std::min<long>(16, std::max<long>(1, ceil_div(m->window, kTilePos)));
+  L.S_ring = (int)std::min<long>(16, std::max<long>(1, ceil_div(m->window, 64)));
   const size_t apart_full = (size_t)kMaxRows * 1 * L.S_full * Hq * (Df + 4);
   const size_t apart_ring = (size_t)kMaxRows * Hs * L.S_ring * (Hq / Hs) * (Ds + 4);
   size_t off = 0;
@@ -289,7 +275,7 @@ q4_status enqueue_layers(const q4dec_model* m, const StepLayout& L, const StepPt
         ni.ny = L.p_d.S; ni.y_split = (long)n * H;
       }
       ni.w_in = ly.attn_norm; ni.H = H; ni.eps = m->eps;
-      hipLaunchKernelGGL(k_norm_rows, dim3(n), dim3(1024), 0, st, ni, P.sp, n, P.xf);
+      hipLaunchKernelGGL(k_norm_rows, dim3(n), dim3(1024), 0, st, ni, P.xf);
       a.K = H; a.NQ = pl.NQ; a.W = pl.W; a.NQs = pl.NQs;
       a.x = P.xf; a.ldx = H;
       a.y = P.qkv; a.ldy = L.qkv_ld; a.n_rows = n; a.sp = P.sp;
@@ -332,7 +318,7 @@ q4_status enqueue_layers(const q4dec_model* m, const StepLayout& L, const StepPt
       ni.h_src = P.hA; ni.y = P.y; ni.ny = (full ? L.p_o_f : L.p_o_s).S; ni.y_split = (long)n * H;
       ni.w_post = ly.post_attn_norm; ni.scalar = 1.0f;
       ni.w_in = ly.pre_ff_norm; ni.h_dst = P.hB; ni.H = H; ni.eps = m->eps;
-      hipLaunchKernelGGL(k_norm_rows, dim3(n), dim3(1024), 0, st, ni, P.sp, n, P.xf);
+      hipLaunchKernelGGL(k_norm_rows, dim3(n), dim3(1024), 0, st, ni, P.xf);
       a.K = H; a.NQ = pl.NQ; a.W = pl.W; a.NQs = pl.NQs;
       a.x = P.xf; a.ldx = H;
       a.a_out = P.a; a.inter = I; a.n_rows = n; a.sp = P.sp;
@@ -357,7 +343,7 @@ q4_status enqueue_layers(const q4dec_model* m, const StepLayout& L, const StepPt
     ni.h_src = P.hB; ni.y = P.y; ni.ny = L.p_d.S; ni.y_split = (long)n * H;
     ni.w_post = last.post_ff_norm; ni.scalar = last.layer_scalar;
     ni.w_in = m->final_norm; ni.h_dst = P.hA; ni.H = H; ni.eps = m->eps;
-    hipLaunchKernelGGL(k_norm_rows, dim3(n), dim3(1024), 0, st, ni, P.sp, n, P.xf);
+    hipLaunchKernelGGL(k_norm_rows, dim3(n), dim3(1024), 0, st, ni, P.xf);
   }
   {
     HeadArgs a{};

@@ -21,15 +21,16 @@ def assert_close(gpu, ref, atol=ATOL, rtol=RTOL, what=""):
                              f"gpu {g[i]!r} oracle {r[i]!r}")
 
 
-def assert_close_composed(gpu, ref, atol=ATOL, rtol=RTOL, frac=0.995, factor=4.0, what=""):
+def assert_close_composed(gpu, ref, atol=ATOL, rtol=RTOL, frac=0.98, factor=4.0, what=""):
     """The bar for outputs of a composition with fp16 rounding points inside
-    it (a whole layer and the 262144-row head): at least ``frac`` of the
-    elements within the fp32 bar, every element within ``factor`` times it,
-    and the RMS error under half the absolute bar.  In scale-1 attention the
-    fp32-vs-fp64 accumulation error of the scores flips fp16 roundings of the
-    attention output, so two correct fp32 implementations already differ by
-    about the bar on a few elements; the kernel-level outputs keep the
-    elementwise bar (assert_close)."""
+    it (a whole layer and the 262144-row head): the RMS error within the
+    relative bar of the reference's RMS plus a quarter of the absolute bar,
+    at least ``frac`` of the elements within the elementwise bar and none
+    beyond ``factor`` times it.  In scale-1 attention the fp32-vs-fp64
+    accumulation error of the scores flips fp16 roundings of the attention
+    output, so two correct fp32 implementations (two summation orders of the
+    same kernels) already differ by about the elementwise bar on a few
+    elements; kernel-level outputs keep the elementwise bar (assert_close)."""
     g = gpu.detach().double().cpu().numpy() if torch.is_tensor(gpu) else np.asarray(gpu, np.float64)
     r = np.asarray(ref, dtype=np.float64)
     assert g.shape == r.shape, (what, g.shape, r.shape)
@@ -39,9 +40,10 @@ def assert_close_composed(gpu, ref, atol=ATOL, rtol=RTOL, frac=0.995, factor=4.0
     inside = float((err <= bound).mean())
     worst = float((err / bound).max())
     rms = float(np.sqrt((err ** 2).mean()))
-    assert inside >= frac and worst <= factor and rms <= atol / 2, (
+    rms_bar = rtol * float(np.sqrt((r ** 2).mean())) + atol / 4
+    assert inside >= frac and worst <= factor and rms <= rms_bar, (
         f"{what}: {inside:.5f} of elements within the bar (need {frac}), worst error/bound {worst:.2f} "
-        f"(need <= {factor}), rms error {rms:.2e} (need <= {atol / 2:.1e})")
+        f"(need <= {factor}), rms error {rms:.2e} (need <= {rms_bar:.2e})")
 
 
 def f16bits(t):
