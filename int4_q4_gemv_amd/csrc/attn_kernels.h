@@ -75,29 +75,29 @@ constexpr size_t fd_lds_bytes() {
   return (size_t)4 * 32 * fd_vpitch<D>() * 2 + (size_t)2 * 4 * D * 2 + (size_t)16 * D * 2;
 }
 
-// Per-head RMSNorm (weight w, or scale-free when w == NULL) and RoPE at
-// position pos on one head vector, done by one wave; src fp32 [D] -> dst
-// fp16 [D] (LDS).  Lane l holds elements l + 64e; the rotated pairs (i,
-// i + D/2) then sit in one lane (D >= 128) or in lanes l and l + 32 (D = 64).
+// Per-head RMSNorm (weights wv, or scale-free) and RoPE at position pos on
+// one head vector held by one wave: lane l holds elements l + 64e (v, wv);
+// fp16 result to dst (LDS).  The rotated pairs (i, i + D/2) sit in one lane
+// (D >= 128) or in lanes l and l + 32 (D = 64); ivf holds the inverse
+// frequencies of this lane's pairs.
 template <int D>
-Q4_DEV void finish_head(const float* src, const float* w, bool rope, int pos, const AttnFin& f, uint16_t* dst) {
+Q4_DEV void finish_vals(float (&v)[D / 64], const float (&wv)[D / 64], bool weighted, bool rope, int pos,
+                        const double (&ivf)[D / 128 > 0 ? D / 128 : 1], int rot_pairs, float eps, uint16_t* dst) {
   constexpr int E = D / 64;
   const int lane = threadIdx.x & 63;
-  float v[E];
   float ss = 0.f;
 #pragma unroll
-  for (int e = 0; e < E; e++) { v[e] = src[lane + 64 * e]; ss += v[e] * v[e]; }
+  for (int e = 0; e < E; e++) ss += v[e] * v[e];
   ss = wave_sum(ss);
-  const float inv = 1.0f / sqrtf(ss / (float)D + f.eps);
+  const float inv = 1.0f / sqrtf(ss / (float)D + eps);
 #pragma unroll
-  for (int e = 0; e < E; e++) v[e] = v[e] * inv * (w ? w[lane + 64 * e] : 1.0f);
-  // rotate pair i = lane + 64e (first half) with i + D/2
-  auto rot = [&](int i, float& x0, float& x1) {
-    if (rope && i < f.rot_pairs) {
+  for (int e = 0; e < E; e++) v[e] = v[e] * inv * (weighted ? wv[e] : 1.0f);
+  auto rot = [&](int i, double fr, float& x0, float& x1) {
+    if (rope && i < rot_pairs) {
       // angle pos * theta^(-2i/D) in fp64, reduced to [-pi, pi] in fp64 by
       // one fma with the double nearest 2 pi (k * 2.5e-16 rad of error, under
       // 1e-10 for positions below 2^20), then cos/sin in fp32
-      const double ang = (double)pos * f.inv_freq[i];
+      const double ang = (double)pos * fr;
       const double k = rint(ang * 0.15915494309189535);
       const float r = (float)fma(-k, 6.283185307179586, ang);
       float s, c;
@@ -108,22 +108,19 @@ Q4_DEV void finish_head(const float* src, const float* w, bool rope, int pos, co
     }
   };
   if constexpr (E == 1) {
-    float other = __shfl_xor(v[0], 32, 64);
+    const float other = __shfl_xor(v[0], 32, 64);
     float x0 = lane < 32 ? v[0] : other, x1 = lane < 32 ? other : v[0];
-    rot(lane & 31, x0, x1);
+    rot(lane & 31, ivf[0], x0, x1);
     dst[lane] = f2h(lane < 32 ? x0 : x1);
   } else {
 #pragma unroll
     for (int e = 0; e < E / 2; e++) {
       float x0 = v[e], x1 = v[e + E / 2];
-      rot(lane + 64 * e, x0, x1);
+      rot(lane + 64 * e, ivf[e], x0, x1);
       dst[lane + 64 * e] = f2h(x0);
       dst[lane + 64 * e + D / 2] = f2h(x1);
     }
   }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 }
 
 template <int D>
@@ -217,30 +214,56 @@ __global__ void __launch_bounds__(256) k_fd_partial(AttnArgs a) {
     const AttnFin& f = a.fin;
     // finishing jobs dealt round-robin to the waves: the query heads of this
     // workgroup's columns, then k and v of each row of this step that lies
-    // in [st, en) and that this row attends (rows r0 .. r1)
+    // in [st, en) and that this row attends (rows r0 .. r1).  Every input of
+    // a wave's jobs (raw rows, norm weights, inverse frequencies) is loaded
+    // in one round before any of them is finished.
+    constexpr int E = D / 64, EH = D / 128 > 0 ? D / 128 : 1;
+    constexpr int MAXJ = (16 + 2 * 4 + 3) / 4;
     const int r0 = max(0, st - base), r1 = min(row, en - 1 - base);
     const int njobs = a.GQ + 2 * max(0, r1 - r0 + 1);
-    for (int jb = wave; jb < njobs; jb += 4) {
+    float raw[MAXJ][E], wq[E], wk[E];
+    double ivf[EH];
+#pragma unroll
+    for (int e = 0; e < E; e++) {
+      wq[e] = f.q_norm[lane + 64 * e];
+      wk[e] = f.k_norm[lane + 64 * e];
+    }
+#pragma unroll
+    for (int e = 0; e < EH; e++) {
+      const int i = E == 1 ? (lane & 31) : lane + 64 * e;
+      ivf[e] = i < f.rot_pairs ? f.inv_freq[i] : 0.0;
+    }
+    auto job_src = [&](int jb) -> const float* {
+      if (jb < a.GQ) return f.qkv + (long)row * f.ldq + (long)(kvh * a.GQ + jb) * D;
+      const int r = r0 + ((jb - a.GQ) >> 1);
+      const float* rr = f.qkv + (long)r * f.ldq;
+      const float* rk = rr + (long)(a.Hq + kvh) * D;
+      if (((jb - a.GQ) & 1) == 0 || !a.ring) return rk;      // full: V from raw k
+      return rr + (long)(a.Hq + a.Hkv + kvh) * D;
+    };
+#pragma unroll
+    for (int k = 0; k < MAXJ; k++) {
+      const int jb = wave + 4 * k;
+      const float* src = job_src(jb < njobs ? jb : 0);
+#pragma unroll
+      for (int e = 0; e < E; e++) raw[k][e] = src[lane + 64 * e];
+    }
+#pragma unroll
+    for (int k = 0; k < MAXJ; k++) {
+      const int jb = wave + 4 * k;
+      if (jb >= njobs) break;
       if (jb < a.GQ) {
-        const int h = kvh * a.GQ + jb;
-        finish_head<D>(f.qkv + (long)row * f.ldq + (long)h * D, f.q_norm, true, P, f, q16 + jb * D);
+        finish_vals<D>(raw[k], wq, true, true, P, ivf, f.rot_pairs, f.eps, q16 + jb * D);
         continue;
       }
       const int r = r0 + ((jb - a.GQ) >> 1), p = base + r;
-      const float* raw = f.qkv + (long)r * f.ldq;
-      const float* rk = raw + (long)(a.Hq + kvh) * D;
       if (((jb - a.GQ) & 1) == 0) {
-        finish_head<D>(rk, f.k_norm, true, p, f, newK + r * D);
+        finish_vals<D>(raw[k], wk, true, true, p, ivf, f.rot_pairs, f.eps, newK + r * D);
+      } else if (f.v_norm) {
+        finish_vals<D>(raw[k], wk, false, false, p, ivf, f.rot_pairs, f.eps, newV + r * D);
       } else {
-        const float* rv = a.ring ? raw + (long)(a.Hq + a.Hkv + kvh) * D : rk;  // full: V from raw k
-        if (f.v_norm) {
-          finish_head<D>(rv, nullptr, false, p, f, newV + r * D);
-        } else {
-          for (int d = lane; d < D; d += 64) newV[r * D + d] = f2h(rv[d]);
-          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-          __builtin_amdgcn_wave_barrier();
-          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-        }
+#pragma unroll
+        for (int e = 0; e < E; e++) newV[r * D + lane + 64 * e] = f2h(raw[k][e]);
       }
     }
     __syncthreads();
@@ -376,32 +399,38 @@ __global__ void __launch_bounds__(256) k_fd_partial(AttnArgs a) {
   float l_tot = l_part + __shfl_xor(l_part, 16, 64);
   l_tot += __shfl_xor(l_tot, 32, 64);
 
-  // ---- merge the 4 waves through LDS (the V rows are free now)
+  // ---- merge the 4 waves (the V rows are free now): per head the wave
+  // maxima meet in LDS, each wave rescales its own O rows in registers, and
+  // the four rescaled slices are added in a fixed order
+  __syncthreads();
+  if (lane < 16) { wm[wave][lane] = m_run; wl[wave][lane] = l_tot; }
   __syncthreads();
   float* ow = reinterpret_cast<float*>(smem);     // [4][16][D]
-  if (lane < 16) { wm[wave][lane] = m_run; wl[wave][lane] = l_tot; }
 #pragma unroll
-  for (int d = 0; d < NDS; d++)
+  for (int i = 0; i < 4; i++) {
+    const int hc = 4 * g + i;
+    const float M = fmaxf(fmaxf(wm[0][hc], wm[1][hc]), fmaxf(wm[2][hc], wm[3][hc]));
+    const float fw = (M == -INFINITY) ? 0.f : exp2f(wm[wave][hc] - M);
 #pragma unroll
-    for (int i = 0; i < 4; i++) ow[(wave * 16 + 4 * g + i) * D + 16 * d + j] = O[d][i];
+    for (int d = 0; d < NDS; d++) ow[(wave * 16 + hc) * D + 16 * d + j] = O[d][i] * fw;
+  }
   __syncthreads();
   for (int idx = threadIdx.x; idx < a.GQ * D; idx += 256) {
     const int col = idx / D, dim = idx - col * D;
-    float M = wm[0][col];
-#pragma unroll
-    for (int w = 1; w < 4; w++) M = fmaxf(M, wm[w][col]);
-    float o = 0.f, l = 0.f;
-    if (M != -INFINITY) {
-#pragma unroll
-      for (int w = 0; w < 4; w++) {
-        const float f = exp2f(wm[w][col] - M);
-        o += f * ow[(w * 16 + col) * D + dim];
-        l += f * wl[w][col];
-      }
-    }
+    const float o = ((ow[col * D + dim] + ow[(16 + col) * D + dim]) + ow[(32 + col) * D + dim]) +
+                    ow[(48 + col) * D + dim];
     float* rec = a.part + attn_rec(a, seq, row, kvh, split, col, D);
     rec[dim] = o;
-    if (dim == 0) { rec[D] = M; rec[D + 1] = l; }
+    if (dim == 0) {
+      const float M = fmaxf(fmaxf(wm[0][col], wm[1][col]), fmaxf(wm[2][col], wm[3][col]));
+      float l = 0.f;
+      if (M != -INFINITY) {
+#pragma unroll
+        for (int w = 0; w < 4; w++) l += exp2f(wm[w][col] - M) * wl[w][col];
+      }
+      rec[D] = M;
+      rec[D + 1] = l;
+    }
   }
 }
 

@@ -130,6 +130,7 @@ void launch_fd_d(const AttnArgs& a, int n_seq, float* out32, uint16_t* out16, hi
   const dim3 cgrid(n_seq * a.n_rows * a.Hq, D / 64);  // 256 threads each
   hipLaunchKernelGGL(k_fd_partial<D>, grid, dim3(256), fd_lds_bytes<D>(), st, a);
   if (a.S <= 16) hipLaunchKernelGGL((k_fd_combine<D, 16>), cgrid, dim3(256), 0, st, a, out32, out16);
+  else if (a.S <= 32) hipLaunchKernelGGL((k_fd_combine<D, 32>), cgrid, dim3(256), 0, st, a, out32, out16);
   else hipLaunchKernelGGL((k_fd_combine<D, kMaxSplits>), cgrid, dim3(256), 0, st, a, out32, out16);
 }
 
@@ -191,7 +192,7 @@ StepLayout step_layout(const q4dec_model* m) {
     if (p->W < 1 || gemv_lds(kMaxRows, *p) > (size_t)kMaxLds - 8 * 1024) L.ok = false;
   if (L.p_gu.S != 1 || L.ymax > 4) L.ok = false;
   L.S_full = kFullSplits;
-  L.S_ring = (int)std::min<long>(16, std::max<long>(1, ceil_div(m->window, 64)));
+  L.S_ring = (int)std::min<long>(32, std::max<long>(1, ceil_div(m->window, 32)));
   const size_t apart_full = (size_t)kMaxRows * 1 * L.S_full * Hq * (Df + 4);
   const size_t apart_ring = (size_t)kMaxRows * Hs * L.S_ring * (Hq / Hs) * (Ds + 4);
   size_t off = 0;
