@@ -28,7 +28,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--mode", default="full", choices=["full", "gemv", "step"])
+    ap.add_argument("--mode", default="full", choices=["full", "gemv", "step", "traffic"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     return ap.parse_args()
 
@@ -66,6 +66,59 @@ def time_gemv(q4, torch, model, reps=3):
     launches = reps * len(mats)
     avg_s = e0.elapsed_time(e1) * 1e-3 / launches
     return avg_s, launches, q4.packed_bytes(N, K)
+
+
+COPY_BYTES = 512 << 20
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "q4_gemv_15360x3840_traffic.txt")
+GEMV_SOURCES = ("int4_q4_gemv_amd/csrc/gemv_kernels.h", "int4_q4_gemv_amd/csrc/device_common.h",
+                "int4_q4_gemv_amd/csrc/q4dec.hip")
+
+
+def gemv_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in GEMV_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_launches(q4, torch, model):
+    """What the two counter runs profile: a plain device copy of COPY_BYTES
+    (its FETCH_SIZE / WRITE_SIZE calibrate the counters to bytes), then the
+    batch-1 q4 GEMV over the 96 gate/up matrices, twice."""
+    src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    cfg = model.cfg
+    g = q4.Gemv(cfg.inter, cfg.hidden, 1)
+    x = torch.randn(1, cfg.hidden, device="cuda").half()
+    y = torch.empty(1, cfg.inter, device="cuda")
+    for _ in range(2):
+        for L in model.layers:
+            g(L["wg"], x, y)
+            g(L["wu"], x, y)
+    torch.cuda.synchronize()
+
+
+def stored_traffic():
+    """Per-launch HBM bytes of the roofline kernel from the committed counter
+    summary, or None when the summary is absent or was taken on other GEMV
+    sources than the ones built now."""
+    try:
+        kv = {}
+        with open(TRAFFIC_FILE) as fh:
+            for line in fh:
+                if ":" in line and not line.startswith("#"):
+                    k, v = line.split(":", 1)
+                    kv[k.strip()] = v.strip()
+        if kv.get("gemv_source_sha256_16") != gemv_source_hash():
+            return None
+        return int(kv["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def time_steps(torch, model, toks, pos, steps, warmup):
@@ -159,11 +212,16 @@ def main():
         log(f"model ready in {time.perf_counter() - t0:.1f} s")
         toks = [[int(t)] for t in synth.tokens(cfg, 64, 5)]
         out = {}
+        if args.mode == "traffic":
+            traffic_launches(q4, torch, model)
+            print(json.dumps({"mode": "traffic", "copy_bytes": COPY_BYTES,
+                              "gemv_source_sha256_16": gemv_source_hash()}))
+            return
         if args.mode in ("full", "gemv"):
             avg_s, launches, nbytes = time_gemv(q4, torch, model)
             ach = nbytes / avg_s / 1e9
             out["roofline"] = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_GBPS, "unit": "GB/s",
-                               "frac": round(ach / PEAK_GBPS, 4), "traffic": None,
+                               "frac": round(ach / PEAK_GBPS, 4), "traffic": stored_traffic(),
                                "kernel": "k_q4_gemv<1,0,4> (q4_gemv, B=1, 3840->15360, 960 workgroups x 8 waves)",
                                "bytes_per_launch": nbytes, "avg_launch_us": round(avg_s * 1e6, 3),
                                "launches": launches}
