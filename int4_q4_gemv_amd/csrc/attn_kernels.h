@@ -137,7 +137,7 @@ __global__ void __launch_bounds__(256) k_fd_partial(AttnArgs a) {
 
   const int split = blockIdx.x, kvh = blockIdx.y;
   const int seq = blockIdx.z / a.n_rows, row = blockIdx.z - seq * a.n_rows;
-  const int nlive = a.sp ? a.sp->n : a.n_rows;
+  const int nlive = a.n_rows;                 // the grid is built per row count
   if (row >= nlive) return;
   const int base = a.sp ? a.sp->pos0 : a.pos0[seq];
   const int P = base + row;

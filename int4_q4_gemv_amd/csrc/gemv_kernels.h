@@ -75,8 +75,7 @@ struct GemvArgs {
   int ldy;
   uint16_t* a_out;        // EPI_GATEUP: fp16 [rows][inter] = GELU(gate) * up
   int inter;
-  int n_rows;             // rows of x (<= B); replaced by sp->n when sp is set
-  const StepParams* sp;
+  int n_rows;             // rows of x (<= B)
 };
 
 Q4_DEV float gelu_tanh(float g) {
@@ -131,13 +130,17 @@ __global__ void __launch_bounds__(B == 1 ? 1024 : 512) k_q4_gemv(GemvArgs a) {
   const int half = (EPI == EPI_GATEUP) ? wave / a.W : 0;
   const int wq = wave - half * a.W;
   const int tile = blockIdx.x, split = blockIdx.y;
-  int s = half, lt = tile;
-  if constexpr (EPI != EPI_GATEUP) {
-    s = 0;
-    if (a.nseg > 1 && tile >= a.seg[1].tile0) s = 1;
-    if (a.nseg > 2 && tile >= a.seg[2].tile0) s = 2;
-    lt = tile - a.seg[s].tile0;
-  }
+  // every segment descriptor is read in one round of scalar loads and the
+  // one this tile needs is selected without a dependent load
+  const GemvSeg sg0 = a.seg[0], sg1 = a.seg[1], sg2 = a.seg[2];
+  int s = half;
+  if constexpr (EPI != EPI_GATEUP)
+    s = (a.nseg > 1 && tile >= sg1.tile0 ? 1 : 0) + (a.nseg > 2 && tile >= sg2.tile0 ? 1 : 0);
+  const u4v* seg_codes = s == 0 ? sg0.codes : (s == 1 ? sg1.codes : sg2.codes);
+  const uint16_t* seg_scales = s == 0 ? sg0.scales : (s == 1 ? sg1.scales : sg2.scales);
+  const int seg_N = s == 0 ? sg0.N : (s == 1 ? sg1.N : sg2.N);
+  const int seg_off = s == 0 ? sg0.out_off : (s == 1 ? sg1.out_off : sg2.out_off);
+  const int lt = (EPI == EPI_GATEUP) ? tile : tile - (s == 0 ? sg0.tile0 : (s == 1 ? sg1.tile0 : sg2.tile0));
   const int qs0 = split * a.NQs;                // first quad of this split
   const int qend = min(a.NQ, qs0 + a.NQs);
   const int q0raw = qs0 + wq * CQ;
@@ -150,10 +153,10 @@ __global__ void __launch_bounds__(B == 1 ? 1024 : 512) k_q4_gemv(GemvArgs a) {
   uint16_t sr[CQ];   // batch 1: this lane's scales
   u2v s4[CQ];        // batch 4: the scales of this lane's 4 MFMA rows
   {
-    const u4v* cp = a.seg[s].codes + tq * 64 + lane;
+    const u4v* cp = seg_codes + tq * 64 + lane;
 #pragma unroll
     for (int i = 0; i < CQ; i++) c[i] = __builtin_nontemporal_load(cp + (long)(i < nq ? i : 0) * 64);
-    const uint16_t* spp = a.seg[s].scales + tq * 64 + (B == 1 ? lane : (lane & ~3));
+    const uint16_t* spp = seg_scales + tq * 64 + (B == 1 ? lane : (lane & ~3));
 #pragma unroll
     for (int i = 0; i < CQ; i++) {
       const long o = (long)(i < nq ? i : 0) * 64;
@@ -162,15 +165,17 @@ __global__ void __launch_bounds__(B == 1 ? 1024 : 512) k_q4_gemv(GemvArgs a) {
     }
   }
   // ---- the activation run into LDS, while the weights are in flight
-  const int nrow = a.sp ? a.sp->n : a.n_rows;
+  const int nrow = a.n_rows;
   {
     const int n8 = ldxs / 8;
-    for (int i = threadIdx.x; i < B * n8; i += blockDim.x) {
-      const int bb = i / n8, k = qs0 * 128 + (i - bb * n8) * 8;
-      u4v v = {0u, 0u, 0u, 0u};
-      if (bb < nrow && k < a.K) v = *reinterpret_cast<const u4v*>(a.x + (long)bb * a.ldx + k);
-      *reinterpret_cast<u4v*>(&xs[bb * ldxs + (i - bb * n8) * 8]) = v;
-    }
+#pragma unroll
+    for (int bb = 0; bb < B; bb++)
+      for (int i = threadIdx.x; i < n8; i += blockDim.x) {
+        const int k = qs0 * 128 + i * 8;
+        u4v v = {0u, 0u, 0u, 0u};
+        if (bb < nrow && k < a.K) v = *reinterpret_cast<const u4v*>(a.x + (long)bb * a.ldx + k);
+        *reinterpret_cast<u4v*>(&xs[bb * ldxs + i * 8]) = v;
+      }
   }
   __syncthreads();
 
@@ -256,7 +261,7 @@ __global__ void __launch_bounds__(B == 1 ? 1024 : 512) k_q4_gemv(GemvArgs a) {
     } else {
       float v = 0.f;
       for (int w = 0; w < a.W; w++) v += red[(w * B + bb) * 16 + rr];
-      if (row < a.seg[s].N && bb < nrow) a.y[split * a.y_split + (long)bb * a.ldy + a.seg[s].out_off + row] = v;
+      if (row < seg_N && bb < nrow) a.y[split * a.y_split + (long)bb * a.ldy + seg_off + row] = v;
     }
   }
 }
@@ -338,7 +343,6 @@ struct HeadArgs {
   float softcap;
   float* logits;           // [n][V] or NULL
   unsigned long long* best;  // [4], zeroed before the kernel
-  const StepParams* sp;
   int n_rows;
   int rows_per_wave;
 };
@@ -347,7 +351,7 @@ template <int B>
 __global__ void __launch_bounds__(256) k_head(HeadArgs a) {
   __shared__ unsigned long long sbest[4][4];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int n = a.sp ? a.sp->n : a.n_rows;
+  const int n = a.n_rows;
   const int nchunk = a.H >> 3;           // 16-byte chunks per row
   const int J = (nchunk + 63) >> 6;      // chunks per lane (<= 8)
   u4v xr[B][8];
@@ -421,8 +425,8 @@ __global__ void __launch_bounds__(256) k_head(HeadArgs a) {
 }
 
 // Reads the argmax slots out and clears them for the next step.
-__global__ void k_argmax_out(unsigned long long* best, const StepParams* sp, int n_rows, int32_t* argmax) {
-  const int n = sp ? sp->n : n_rows;
+__global__ void k_argmax_out(unsigned long long* best, int n_rows, int32_t* argmax) {
+  const int n = n_rows;
   const int i = threadIdx.x;
   if (i < 4) {
     const unsigned long long m = best[i];

@@ -279,7 +279,7 @@ q4_status enqueue_layers(const q4dec_model* m, const StepLayout& L, const StepPt
       hipLaunchKernelGGL(k_norm_rows, dim3(n), dim3(1024), 0, st, ni, P.xf);
       a.K = H; a.NQ = pl.NQ; a.W = pl.W; a.NQs = pl.NQs;
       a.x = P.xf; a.ldx = H;
-      a.y = P.qkv; a.ldy = L.qkv_ld; a.n_rows = n; a.sp = P.sp;
+      a.y = P.qkv; a.ldy = L.qkv_ld; a.n_rows = n;
       launch_gemv<B, EPI_STORE>(a, pl, t0, pl.W, gemv_lds(B, pl), st);
     }
     // ---- attention: q/k/v finishing, split-K partials, combine
@@ -305,7 +305,7 @@ q4_status enqueue_layers(const q4dec_model* m, const StepLayout& L, const StepPt
       a.nseg = 1;
       a.K = Hq * D; a.NQ = pl.NQ; a.W = pl.W; a.NQs = pl.NQs;
       a.x = P.o; a.ldx = Hq * D;
-      a.y = P.y; a.ldy = H; a.y_split = (long)n * H; a.n_rows = n; a.sp = P.sp;
+      a.y = P.y; a.ldy = H; a.y_split = (long)n * H; a.n_rows = n;
       launch_gemv<B, EPI_STORE>(a, pl, a.seg[0].T, pl.W, gemv_lds(B, pl), st);
     }
     // ---- gate/up with GELU(gate) * up; post-attention residual + pre-FF norm in the prologue
@@ -322,7 +322,7 @@ q4_status enqueue_layers(const q4dec_model* m, const StepLayout& L, const StepPt
       hipLaunchKernelGGL(k_norm_rows, dim3(n), dim3(1024), 0, st, ni, P.xf);
       a.K = H; a.NQ = pl.NQ; a.W = pl.W; a.NQs = pl.NQs;
       a.x = P.xf; a.ldx = H;
-      a.a_out = P.a; a.inter = I; a.n_rows = n; a.sp = P.sp;
+      a.a_out = P.a; a.inter = I; a.n_rows = n;
       launch_gemv<B, EPI_GATEUP>(a, pl, a.seg[0].T, 2 * pl.W, gemv_lds(B, pl), st);
     }
     // ---- down projection
@@ -333,7 +333,7 @@ q4_status enqueue_layers(const q4dec_model* m, const StepLayout& L, const StepPt
       a.nseg = 1;
       a.K = I; a.NQ = pl.NQ; a.W = pl.W; a.NQs = pl.NQs;
       a.x = P.a; a.ldx = I;
-      a.y = P.y; a.ldy = H; a.y_split = (long)n * H; a.n_rows = n; a.sp = P.sp;
+      a.y = P.y; a.ldy = H; a.y_split = (long)n * H; a.n_rows = n;
       launch_gemv<B, EPI_STORE>(a, pl, a.seg[0].T, pl.W, gemv_lds(B, pl), st);
     }
   }
@@ -349,13 +349,13 @@ q4_status enqueue_layers(const q4dec_model* m, const StepLayout& L, const StepPt
   {
     HeadArgs a{};
     a.E = m->embed; a.x = P.xf; a.V = m->vocab; a.H = H; a.softcap = m->softcap;
-    a.logits = logits; a.best = P.best; a.sp = P.sp; a.n_rows = n;
+    a.logits = logits; a.best = P.best; a.n_rows = n;
     const int waves = 8192;
     a.rows_per_wave = (int)std::max<long>(2, ceil_div(m->vocab, waves));
     if (a.rows_per_wave & 1) a.rows_per_wave++;
     const int grid = (int)ceil_div(ceil_div(m->vocab, a.rows_per_wave), 4);
     hipLaunchKernelGGL((k_head<B>), dim3(grid), dim3(256), 0, st, a);
-    hipLaunchKernelGGL(k_argmax_out, dim3(1), dim3(64), 0, st, P.best, P.sp, n, argmax);
+    hipLaunchKernelGGL(k_argmax_out, dim3(1), dim3(64), 0, st, P.best, n, argmax);
   }
   return launch_status();
 }
@@ -534,7 +534,7 @@ q4_status q4_gemv(const void* packed, int N, int K, const uint16_t* x, int B, fl
   fill_seg(a.seg[0], packed, N, K, 0, 0);
   a.nseg = 1;
   a.K = K; a.NQ = p.NQ; a.W = p.W; a.NQs = p.NQs;
-  a.x = x; a.ldx = K; a.y = y; a.ldy = N; a.n_rows = B; a.sp = nullptr;
+  a.x = x; a.ldx = K; a.y = y; a.ldy = N; a.n_rows = B;
   if (B == 1) launch_gemv<1, EPI_STORE>(a, p, p.T, p.W, gemv_lds(1, p), S(stream));
   else launch_gemv<4, EPI_STORE>(a, p, p.T, p.W, gemv_lds(4, p), S(stream));
   return launch_status();
