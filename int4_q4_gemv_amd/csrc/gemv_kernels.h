@@ -285,18 +285,26 @@ __global__ void __launch_bounds__(1024) k_norm_rows(NormIn p, uint16_t* x) {
   const float* y2 = p.ny > 2 ? y0 + 2 * p.y_split : y0;
   const float* y3 = p.ny > 3 ? y0 + 3 * p.y_split : y0;
   const float* wpp = y ? p.w_post : p.w_in;
-  float hv[E], yv[E], wp[E], wi[E];
+  const float m1 = p.ny > 1 ? 1.f : 0.f, m2 = p.ny > 2 ? 1.f : 0.f, m3 = p.ny > 3 ? 1.f : 0.f;
+  float hv[E], yv[E], wp[E], wi[E], a1[E], a2[E], a3[E];
 #pragma unroll
   for (int e = 0; e < E; e++) {
     const int k = min(tid + 1024 * e, H - 1);
     hv[e] = hs[k];
     wi[e] = p.w_in[k];
     wp[e] = wpp[k];
-    const float a0 = y0[k], a1 = y1[k], a2 = y2[k], a3 = y3[k];
-    float v = a0;
-    if (p.ny > 1) v += a1;
-    if (p.ny > 2) v += a2;
-    if (p.ny > 3) v += a3;
+    yv[e] = y0[k];
+    a1[e] = y1[k];
+    a2[e] = y2[k];
+    a3[e] = y3[k];
+  }
+  // the sums come after every load has been issued, and are branch-free so
+  // that none of them waits on a single load; same order ((a0 + a1) + a2) +
+  // a3, an absent part adding an exact zero
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int e = 0; e < E; e++) {
+    const float v = ((yv[e] + m1 * a1[e]) + m2 * a2[e]) + m3 * a3[e];
     yv[e] = (y && tid + 1024 * e < H) ? v : 0.f;
     if (tid + 1024 * e >= H) hv[e] = 0.f;
   }
