@@ -148,14 +148,26 @@ __global__ void __launch_bounds__(B == 1 ? 1024 : 512) k_q4_gemv(GemvArgs a) {
   const int q0 = nq > 0 ? q0raw : qs0;          // idle waves load (and ignore) valid quads
   const long tq = (long)lt * a.NQ + q0;
 
-  // ---- every weight load of this wave, first
+  // ---- loads, in the order their data is used: this thread's share of the
+  // activation run, then the scales, then the codes.  Loads return in order,
+  // so the activation reaches LDS as soon as its own load lands and quad i
+  // is worked on as soon as its codes land, while the later quads are still
+  // in flight.  A share beyond one u4v per thread and row (only very long
+  // unsplit runs) is staged after the weights.
+  const int nrow = a.n_rows;
+  const int n8 = ldxs / 8;
+  const int kx = qs0 * 128 + threadIdx.x * 8;
+  u4v xr[B];
+#pragma unroll
+  for (int bb = 0; bb < B; bb++) {
+    const int br = min(bb, nrow - 1);
+    xr[bb] = *reinterpret_cast<const u4v*>(a.x + (long)br * a.ldx + min(kx, a.K - 8));
+  }
+  __builtin_amdgcn_sched_barrier(0);
   u4v c[CQ];
   uint16_t sr[CQ];   // batch 1: this lane's scales
   u2v s4[CQ];        // batch 4: the scales of this lane's 4 MFMA rows
   {
-    const u4v* cp = seg_codes + tq * 64 + lane;
-#pragma unroll
-    for (int i = 0; i < CQ; i++) c[i] = __builtin_nontemporal_load(cp + (long)(i < nq ? i : 0) * 64);
     const uint16_t* spp = seg_scales + tq * 64 + (B == 1 ? lane : (lane & ~3));
 #pragma unroll
     for (int i = 0; i < CQ; i++) {
@@ -163,14 +175,24 @@ __global__ void __launch_bounds__(B == 1 ? 1024 : 512) k_q4_gemv(GemvArgs a) {
       if constexpr (B == 1) sr[i] = spp[o];
       else s4[i] = *reinterpret_cast<const u2v*>(spp + o);
     }
+    const u4v* cp = seg_codes + tq * 64 + lane;
+#pragma unroll
+    for (int i = 0; i < CQ; i++) {
+      c[i] = __builtin_nontemporal_load(cp + (long)(i < nq ? i : 0) * 64);
+      __builtin_amdgcn_sched_barrier(0);   // keep the issue order
+    }
   }
-  // ---- the activation run into LDS, while the weights are in flight
-  const int nrow = a.n_rows;
   {
-    const int n8 = ldxs / 8;
+    const bool in = threadIdx.x < n8;
+    const bool kin = kx < a.K;
+#pragma unroll
+    for (int bb = 0; bb < B; bb++) {
+      const u4v z = {0u, 0u, 0u, 0u};
+      if (in) *reinterpret_cast<u4v*>(&xs[bb * ldxs + threadIdx.x * 8]) = (bb < nrow && kin) ? xr[bb] : z;
+    }
 #pragma unroll
     for (int bb = 0; bb < B; bb++)
-      for (int i = threadIdx.x; i < n8; i += blockDim.x) {
+      for (int i = threadIdx.x + blockDim.x; i < n8; i += blockDim.x) {
         const int k = qs0 * 128 + i * 8;
         u4v v = {0u, 0u, 0u, 0u};
         if (bb < nrow && k < a.K) v = *reinterpret_cast<const u4v*>(a.x + (long)bb * a.ldx + k);
