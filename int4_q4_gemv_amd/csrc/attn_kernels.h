@@ -400,37 +400,62 @@ __global__ void __launch_bounds__(256) k_fd_partial(AttnArgs a) {
   l_tot += __shfl_xor(l_tot, 32, 64);
 
   // ---- merge the 4 waves (the V rows are free now): per head the wave
-  // maxima meet in LDS, each wave rescales its own O rows in registers, and
-  // the four rescaled slices are added in a fixed order
+  // maxima meet in LDS; each wave rescales its own O rows in registers and
+  // stores them as one float4 per (dim step, lane), the 4 heads of that lane
+  // (conflict-free 16-byte LDS writes); then every thread adds the four
+  // waves' float4s of its items in a fixed order and stores them to the
+  // records.  LDS: 4 * NDS * 64 float4 (D = 512: 128 KB, inside the V rows).
   __syncthreads();
   if (lane < 16) { wm[wave][lane] = m_run; wl[wave][lane] = l_tot; }
   __syncthreads();
-  float* ow = reinterpret_cast<float*>(smem);     // [4][16][D]
+  static_assert((size_t)4 * 32 * VROW * 2 >= (size_t)4 * NDS * 64 * 16, "merge buffer inside the V rows");
+  f4_t* ow = reinterpret_cast<f4_t*>(smem);       // [4][NDS][64]
+  {
+    float fw[4];
 #pragma unroll
-  for (int i = 0; i < 4; i++) {
-    const int hc = 4 * g + i;
-    const float M = fmaxf(fmaxf(wm[0][hc], wm[1][hc]), fmaxf(wm[2][hc], wm[3][hc]));
-    const float fw = (M == -INFINITY) ? 0.f : exp2f(wm[wave][hc] - M);
+    for (int i = 0; i < 4; i++) {
+      const int hc = 4 * g + i;
+      const float M = fmaxf(fmaxf(wm[0][hc], wm[1][hc]), fmaxf(wm[2][hc], wm[3][hc]));
+      fw[i] = (M == -INFINITY) ? 0.f : exp2f(wm[wave][hc] - M);
+    }
 #pragma unroll
-    for (int d = 0; d < NDS; d++) ow[(wave * 16 + hc) * D + 16 * d + j] = O[d][i] * fw;
+    for (int d = 0; d < NDS; d++)
+      ow[(wave * NDS + d) * 64 + lane] = (f4_t){O[d][0] * fw[0], O[d][1] * fw[1], O[d][2] * fw[2], O[d][3] * fw[3]};
   }
   __syncthreads();
-  for (int idx = threadIdx.x; idx < a.GQ * D; idx += 256) {
-    const int col = idx / D, dim = idx - col * D;
-    const float o = ((ow[col * D + dim] + ow[(16 + col) * D + dim]) + ow[(32 + col) * D + dim]) +
-                    ow[(48 + col) * D + dim];
-    float* rec = a.part + attn_rec(a, seq, row, kvh, split, col, D);
-    rec[dim] = o;
-    if (dim == 0) {
-      const float M = fmaxf(fmaxf(wm[0][col], wm[1][col]), fmaxf(wm[2][col], wm[3][col]));
-      float l = 0.f;
-      if (M != -INFINITY) {
+  {
+    // items (d, lane) with d = wave + 4k: heads 4g + i at dim 16d + j
+    constexpr int NI = NDS / 4;
+    f4_t acc[NI];
 #pragma unroll
-        for (int w = 0; w < 4; w++) l += exp2f(wm[w][col] - M) * wl[w][col];
-      }
-      rec[D] = M;
-      rec[D + 1] = l;
+    for (int k = 0; k < NI; k++) {
+      const int d = wave + 4 * k;
+      const f4_t v0 = ow[(0 * NDS + d) * 64 + lane], v1 = ow[(1 * NDS + d) * 64 + lane];
+      const f4_t v2 = ow[(2 * NDS + d) * 64 + lane], v3 = ow[(3 * NDS + d) * 64 + lane];
+#pragma unroll
+      for (int i = 0; i < 4; i++) acc[k][i] = ((v0[i] + v1[i]) + v2[i]) + v3[i];
     }
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const int col = 4 * g + i;
+      if (col < a.GQ) {
+        float* rec = a.part + attn_rec(a, seq, row, kvh, split, col, D);
+#pragma unroll
+        for (int k = 0; k < NI; k++) rec[16 * (wave + 4 * k) + j] = acc[k][i];
+      }
+    }
+  }
+  if (threadIdx.x < a.GQ) {
+    const int col = threadIdx.x;
+    const float M = fmaxf(fmaxf(wm[0][col], wm[1][col]), fmaxf(wm[2][col], wm[3][col]));
+    float l = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < 4; w++) l += exp2f(wm[w][col] - M) * wl[w][col];
+    }
+    float* rec = a.part + attn_rec(a, seq, row, kvh, split, col, D);
+    rec[D] = M;
+    rec[D + 1] = l;
   }
 }
 
