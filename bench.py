@@ -37,11 +37,13 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def time_gemv(q4, torch, model, reps=3):
+def time_gemv(q4, torch, model, reps=10, warm=5):
     """Average launch time of the batch-1 q4 GEMV at 12B shapes: the gate and
     up matrices of all 48 layers (3.2 GB, so every launch streams from HBM),
     captured once into a graph and replayed back to back between two HIP
-    events on the current stream (so host launch cost is not timed)."""
+    events on the current stream (so host launch cost is not timed).  `warm`
+    untimed replays first bring the GPU from the model build to a steady
+    clock."""
     cfg = model.cfg
     N, K = cfg.inter, cfg.hidden
     g = q4.Gemv(N, K, 1)
@@ -55,7 +57,8 @@ def time_gemv(q4, torch, model, reps=3):
     with torch.cuda.graph(graph, stream=torch.cuda.current_stream()):
         for m in mats:
             g(m, x, y)
-    graph.replay()
+    for _ in range(warm):
+        graph.replay()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
