@@ -134,7 +134,8 @@ q4_status flash_decode_full(const uint16_t* q, const uint16_t* k, const uint16_t
  * out: device fp32 [n_seq][n_rows][Hq][D].  Hq % Hkv == 0, Hq/Hkv <= 16.
  * Errors: Q4_ERANGE if W < 1, W > R, R < W + n_rows - 1 (the rows of a
  * verify block written after row i must stay outside row i's window) or
- * pos0[s] < 0; Q4_ESHAPE, Q4_EINVAL, Q4_ENOSPACE, Q4_EALIGN, Q4_EHIP. */
+ * pos0[s] < 0; Q4_ESHAPE if R < 32 (a ring holds at least one 32-position
+ * tile), and Q4_ESHAPE, Q4_EINVAL, Q4_ENOSPACE, Q4_EALIGN, Q4_EHIP as above. */
 q4_status flash_decode_ring(const uint16_t* q, const uint16_t* k_ring, const uint16_t* v_ring,
                             int64_t seq_stride, int Hq, int Hkv, int D, int R, int W,
                             const int32_t* pos0, int n_seq, int n_rows, float scale,
@@ -198,8 +199,8 @@ size_t decode_step_workspace_size(const q4dec_model* m, int n);
  * HIP graph of the step; later calls replay it (positions and tokens are read
  * on the device, so one graph serves every position).
  * Errors: Q4_ERANGE (pos0 < 0; pos0 + n - 1 >= full_cap; R < W + n - 1;
- * token outside [0, vocab)); Q4_ESHAPE (n outside 1..4 or unsupported
- * dimensions); Q4_EINVAL; Q4_ENOSPACE; Q4_EALIGN; Q4_EHIP. */
+ * token outside [0, vocab)); Q4_ESHAPE (n outside 1..4, ring < 32 or
+ * unsupported dimensions); Q4_EINVAL; Q4_ENOSPACE; Q4_EALIGN; Q4_EHIP. */
 q4_status decode_step(const q4dec_model* m, const int32_t* tokens, int n, int pos0,
                       float* logits, int32_t* argmax, void* ws, size_t ws_bytes,
                       void* stream);

@@ -39,7 +39,8 @@ struct AttnFin {
   const float* k_norm;
   int v_norm;
   int rot_pairs;
-  const double* inv_freq; // [rot_pairs]: theta^(-2i/D) in fp64
+  const float2* rope_cs;  // [row][cs_ld]: (cos, sin) of pair i at the row's position
+  int cs_ld;
   float eps;
 };
 
@@ -75,14 +76,14 @@ constexpr size_t fd_lds_bytes() {
   return (size_t)4 * 32 * fd_vpitch<D>() * 2 + (size_t)2 * 4 * D * 2 + (size_t)16 * D * 2;
 }
 
-// Per-head RMSNorm (weights wv, or scale-free) and RoPE at position pos on
-// one head vector held by one wave: lane l holds elements l + 64e (v, wv);
-// fp16 result to dst (LDS).  The rotated pairs (i, i + D/2) sit in one lane
-// (D >= 128) or in lanes l and l + 32 (D = 64); ivf holds the inverse
-// frequencies of this lane's pairs.
+// Per-head RMSNorm (weights wv, or scale-free) and RoPE on one head vector
+// held by one wave: lane l holds elements l + 64e (v, wv); fp16 result to dst
+// (LDS).  The rotated pairs (i, i + D/2) sit in one lane (D >= 128) or in
+// lanes l and l + 32 (D = 64); cs holds (cos, sin) of this lane's pairs at
+// the vector's position (pairs past rot_pairs are not rotated).
 template <int D>
-Q4_DEV void finish_vals(float (&v)[D / 64], const float (&wv)[D / 64], bool weighted, bool rope, int pos,
-                        const double (&ivf)[D / 128 > 0 ? D / 128 : 1], int rot_pairs, float eps, uint16_t* dst) {
+Q4_DEV void finish_vals(float (&v)[D / 64], const float (&wv)[D / 64], bool weighted, bool rope,
+                        const float2 (&cs)[D / 128 > 0 ? D / 128 : 1], int rot_pairs, float eps, uint16_t* dst) {
   constexpr int E = D / 64;
   const int lane = threadIdx.x & 63;
   float ss = 0.f;
@@ -92,16 +93,9 @@ Q4_DEV void finish_vals(float (&v)[D / 64], const float (&wv)[D / 64], bool weig
   const float inv = 1.0f / sqrtf(ss / (float)D + eps);
 #pragma unroll
   for (int e = 0; e < E; e++) v[e] = v[e] * inv * (weighted ? wv[e] : 1.0f);
-  auto rot = [&](int i, double fr, float& x0, float& x1) {
+  auto rot = [&](int i, float2 t, float& x0, float& x1) {
     if (rope && i < rot_pairs) {
-      // angle pos * theta^(-2i/D) in fp64, reduced to [-pi, pi] in fp64 by
-      // one fma with the double nearest 2 pi (k * 2.5e-16 rad of error, under
-      // 1e-10 for positions below 2^20), then cos/sin in fp32
-      const double ang = (double)pos * fr;
-      const double k = rint(ang * 0.15915494309189535);
-      const float r = (float)fma(-k, 6.283185307179586, ang);
-      float s, c;
-      sincosf(r, &s, &c);
+      const float c = t.x, s = t.y;
       const float y0 = x0 * c - x1 * s;
       const float y1 = x1 * c + x0 * s;
       x0 = y0; x1 = y1;
@@ -110,13 +104,13 @@ Q4_DEV void finish_vals(float (&v)[D / 64], const float (&wv)[D / 64], bool weig
   if constexpr (E == 1) {
     const float other = __shfl_xor(v[0], 32, 64);
     float x0 = lane < 32 ? v[0] : other, x1 = lane < 32 ? other : v[0];
-    rot(lane & 31, ivf[0], x0, x1);
+    rot(lane & 31, cs[0], x0, x1);
     dst[lane] = f2h(lane < 32 ? x0 : x1);
   } else {
 #pragma unroll
     for (int e = 0; e < E / 2; e++) {
       float x0 = v[e], x1 = v[e + E / 2];
-      rot(lane + 64 * e, ivf[e], x0, x1);
+      rot(lane + 64 * e, cs[e], x0, x1);
       dst[lane + 64 * e] = f2h(x0);
       dst[lane + 64 * e + D / 2] = f2h(x1);
     }
@@ -139,7 +133,55 @@ __global__ void __launch_bounds__(256) k_fd_partial(AttnArgs a) {
   const int seq = blockIdx.z / a.n_rows, row = blockIdx.z - seq * a.n_rows;
   const int nlive = a.n_rows;                 // the grid is built per row count
   if (row >= nlive) return;
-  const int base = a.sp ? a.sp->pos0 : a.pos0[seq];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+
+  // ---- the step's first position, before any other load: a global load
+  // (not a generic one through a pointer that may also point at the
+  // arguments), so waiting for it does not wait for the loads issued after it
+  int base;
+  if (a.sp) base = *(const __attribute__((address_space(1))) int*)(&a.sp->pos0);
+  else base = a.pos0[seq];
+
+  // ---- inputs of the finishing prologue (decode step), issued first: they
+  // do not depend on the position, so they travel while the step
+  // parameters are read.  Jobs are dealt round-robin to the waves: the query
+  // heads of this workgroup's columns, then k and v of every row 0 .. row of
+  // the step (after the position is known, only the rows in this
+  // workgroup's range are finished).
+  constexpr int FE = D / 64, FEH = D / 128 > 0 ? D / 128 : 1;
+  constexpr int MAXJ = (16 + 2 * 4 + 3) / 4;
+  const int njobs = a.fin_on ? a.GQ + 2 * (row + 1) : 0;
+  float raw[MAXJ][FE], wq[FE], wk[FE];
+  float2 fcs[MAXJ][FEH];
+  if (a.fin_on) {
+    const AttnFin& f = a.fin;
+#pragma unroll
+    for (int e = 0; e < FE; e++) {
+      wq[e] = f.q_norm[lane + 64 * e];
+      wk[e] = f.k_norm[lane + 64 * e];
+    }
+#pragma unroll
+    for (int k = 0; k < MAXJ; k++) {
+      const int jb0 = wave + 4 * k;
+      const int jb = jb0 < njobs ? jb0 : 0;
+      const int r = jb < a.GQ ? row : (jb - a.GQ) >> 1;    // row of the step the job belongs to
+      const float* rr = f.qkv + (long)r * f.ldq;
+      const float* src;
+      if (jb < a.GQ) src = rr + (long)(kvh * a.GQ + jb) * D;
+      else if (((jb - a.GQ) & 1) == 0 || !a.ring) src = rr + (long)(a.Hq + kvh) * D;   // k (full: V from raw k)
+      else src = rr + (long)(a.Hq + a.Hkv + kvh) * D;                                   // v
+#pragma unroll
+      for (int e = 0; e < FE; e++) raw[k][e] = src[lane + 64 * e];
+      const float2* cr = f.rope_cs + (long)r * f.cs_ld;
+#pragma unroll
+      for (int e = 0; e < FEH; e++) {
+        const int i = FE == 1 ? (lane & 31) : lane + 64 * e;
+        fcs[k][e] = cr[min(i, max(f.rot_pairs - 1, 0))];
+      }
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
   const int P = base + row;
   const int lo = a.ring ? max(0, P - a.W + 1) : 0;
   const int L = P - lo + 1;
@@ -148,7 +190,6 @@ __global__ void __launch_bounds__(256) k_fd_partial(AttnArgs a) {
   const int en = min(st + chunk, P + 1);
   const int P0new = a.fin_on ? base : 0x7FFFFFFF;   // first position formed in this step
 
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int j = lane & 15, g = lane >> 4;
   const bool col_ok = j < a.GQ;
 
@@ -171,13 +212,28 @@ __global__ void __launch_bounds__(256) k_fd_partial(AttnArgs a) {
   uint16_t* vl = vlds + wave * 32 * VROW;
   h8_t KA[NKS], KB[NKS];
   u4v VV[HV ? VCH : 1];
-  auto cache_row = [&](int p) -> long {
-    return (p < en && p < P0new) ? (long)(a.ring ? p % a.R : p) * D : 0l;
+  // Cache rows of a tile.  Rows [0, nv) of the tile at t0 come from the cache
+  // (the rest are masked out or formed in this step: they read row 0).  On a
+  // ring layer, tile row r lives at slot (t0 + r) mod R; rings hold at least
+  // 32 slots (the host checks), so the 32 rows of a tile wrap at most once: a
+  // lane takes one remainder for its first row and steps from there with one
+  // compare per row, with no division and no branch per row.
+  const bool ringf = a.ring != 0;
+  const int Rr = ringf ? a.R : 1;
+  const int nv_end = min(en, P0new);
+  auto slot_of = [&](int p) -> int { return ringf ? p % Rr : p; };
+  // cache row (in elements) of tile row r0 + d, given s0 = slot of tile row r0
+  auto row_at = [&](int nv, int s0, int r0, int d) -> long {
+    const int sl = ringf && d >= Rr - s0 ? s0 + d - Rr : s0 + d;
+    const long off = (long)sl * D;
+    return r0 + d < nv ? off : 0l;
   };
   auto load_k = [&](int t0) {
-    const int pa = t0 + 8 * (j >> 2) + (j & 3);
-    const uint16_t* ka = kb + cache_row(pa) + 8 * g;
-    const uint16_t* kc = kb + cache_row(pa + 4) + 8 * g;
+    const int nv = nv_end - t0;
+    const int ra = 8 * (j >> 2) + (j & 3);
+    const int s0 = slot_of(t0 + ra);
+    const uint16_t* ka = kb + row_at(nv, s0, ra, 0) + 8 * g;
+    const uint16_t* kc = kb + row_at(nv, s0, ra, 4) + 8 * g;
 #pragma unroll
     for (int s = 0; s < NKS; s++) {
       KA[s] = __builtin_bit_cast(h8_t, __builtin_nontemporal_load(reinterpret_cast<const u4v*>(ka + 32 * s)));
@@ -185,17 +241,21 @@ __global__ void __launch_bounds__(256) k_fd_partial(AttnArgs a) {
     }
   };
   auto load_v = [&](int t0) {
+    const int nv = nv_end - t0;
     if constexpr (HV) {
+      // chunk i of lane l: tile row (l + 64 i) / (D / 8), 16-byte column (l mod D / 8)
+      constexpr int STEP = 512 / D;
+      const int r0 = lane / (D / 8), cc = lane % (D / 8);
+      const int s0 = slot_of(t0 + r0);
 #pragma unroll
-      for (int i = 0; i < VCH; i++) {
-        const int c = lane + 64 * i, r = c / (D / 8), cc = c - r * (D / 8);
-        VV[i] = __builtin_nontemporal_load(reinterpret_cast<const u4v*>(vb + cache_row(t0 + r) + cc * 8));
-      }
+      for (int i = 0; i < VCH; i++)
+        VV[i] = __builtin_nontemporal_load(reinterpret_cast<const u4v*>(vb + row_at(nv, s0, r0, STEP * i) + cc * 8));
     } else {
+      const int s0 = slot_of(t0);
 #pragma unroll
       for (int r = 0; r < 32; r++) {
         const int c = lane ^ ((r >> 3) & 3);
-        __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint32_t*>(vb + cache_row(t0 + r) + c * 8),
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint32_t*>(vb + row_at(nv, s0, 0, r) + c * 8),
                                          reinterpret_cast<uint32_t*>(vl + r * D), 16, 0, 0);
       }
     }
@@ -204,66 +264,34 @@ __global__ void __launch_bounds__(256) k_fd_partial(AttnArgs a) {
   // D = 512 (128 registers) waits for the prologue's registers to free up
   int t0 = st + 32 * wave;
   if (t0 < en) {
-    load_v(t0);
     if (HV) load_k(t0);
+    load_v(t0);
   }
 
   // ---- queries of this workgroup's columns as the MFMA B operand
   h8_t qb[NKS];
   if (a.fin_on) {
     const AttnFin& f = a.fin;
-    // finishing jobs dealt round-robin to the waves: the query heads of this
-    // workgroup's columns, then k and v of each row of this step that lies
-    // in [st, en) and that this row attends (rows r0 .. r1).  Every input of
-    // a wave's jobs (raw rows, norm weights, inverse frequencies) is loaded
-    // in one round before any of them is finished.
-    constexpr int E = D / 64, EH = D / 128 > 0 ? D / 128 : 1;
-    constexpr int MAXJ = (16 + 2 * 4 + 3) / 4;
+    // finish the jobs: every query head, and k and v of the rows of this
+    // step that lie in [st, en) and that this row attends (rows r0 .. r1)
     const int r0 = max(0, st - base), r1 = min(row, en - 1 - base);
-    const int njobs = a.GQ + 2 * max(0, r1 - r0 + 1);
-    float raw[MAXJ][E], wq[E], wk[E];
-    double ivf[EH];
-#pragma unroll
-    for (int e = 0; e < E; e++) {
-      wq[e] = f.q_norm[lane + 64 * e];
-      wk[e] = f.k_norm[lane + 64 * e];
-    }
-#pragma unroll
-    for (int e = 0; e < EH; e++) {
-      const int i = E == 1 ? (lane & 31) : lane + 64 * e;
-      ivf[e] = i < f.rot_pairs ? f.inv_freq[i] : 0.0;
-    }
-    auto job_src = [&](int jb) -> const float* {
-      if (jb < a.GQ) return f.qkv + (long)row * f.ldq + (long)(kvh * a.GQ + jb) * D;
-      const int r = r0 + ((jb - a.GQ) >> 1);
-      const float* rr = f.qkv + (long)r * f.ldq;
-      const float* rk = rr + (long)(a.Hq + kvh) * D;
-      if (((jb - a.GQ) & 1) == 0 || !a.ring) return rk;      // full: V from raw k
-      return rr + (long)(a.Hq + a.Hkv + kvh) * D;
-    };
-#pragma unroll
-    for (int k = 0; k < MAXJ; k++) {
-      const int jb = wave + 4 * k;
-      const float* src = job_src(jb < njobs ? jb : 0);
-#pragma unroll
-      for (int e = 0; e < E; e++) raw[k][e] = src[lane + 64 * e];
-    }
 #pragma unroll
     for (int k = 0; k < MAXJ; k++) {
       const int jb = wave + 4 * k;
       if (jb >= njobs) break;
       if (jb < a.GQ) {
-        finish_vals<D>(raw[k], wq, true, true, P, ivf, f.rot_pairs, f.eps, q16 + jb * D);
+        finish_vals<D>(raw[k], wq, true, true, fcs[k], f.rot_pairs, f.eps, q16 + jb * D);
         continue;
       }
-      const int r = r0 + ((jb - a.GQ) >> 1), p = base + r;
+      const int r = (jb - a.GQ) >> 1;
+      if (r < r0 || r > r1) continue;
       if (((jb - a.GQ) & 1) == 0) {
-        finish_vals<D>(raw[k], wk, true, true, p, ivf, f.rot_pairs, f.eps, newK + r * D);
+        finish_vals<D>(raw[k], wk, true, true, fcs[k], f.rot_pairs, f.eps, newK + r * D);
       } else if (f.v_norm) {
-        finish_vals<D>(raw[k], wk, false, false, p, ivf, f.rot_pairs, f.eps, newV + r * D);
+        finish_vals<D>(raw[k], wk, false, false, fcs[k], f.rot_pairs, f.eps, newV + r * D);
       } else {
 #pragma unroll
-        for (int e = 0; e < E; e++) newV[r * D + lane + 64 * e] = f2h(raw[k][e]);
+        for (int e = 0; e < FE; e++) newV[r * D + lane + 64 * e] = f2h(raw[k][e]);
       }
     }
     __syncthreads();
@@ -297,8 +325,8 @@ __global__ void __launch_bounds__(256) k_fd_partial(AttnArgs a) {
   for (int d = 0; d < NDS; d++) O[d] = (f4_t){0.f, 0.f, 0.f, 0.f};
 
   for (bool first = true; t0 < en; t0 += 128, first = false) {
-    if (!first) load_v(t0);
     if (!first || !HV) load_k(t0);
+    if (!first) load_v(t0);
     if (t0 + 31 >= P0new) {                   // patch the rows formed in this step
       const int pa = t0 + 8 * (j >> 2) + (j & 3), pb = pa + 4;
 #pragma unroll

@@ -168,6 +168,7 @@ bool model_dims_ok(const q4dec_model* m) {
   if (m->n_heads / m->sl_kv_heads > 16) return false;
   if (m->sl_rot_pairs < 0 || m->sl_rot_pairs > m->sl_head_dim / 2) return false;
   if (m->full_rot_pairs < 0 || m->full_rot_pairs > m->full_head_dim / 2) return false;
+  if (m->ring < 32) return false;   // a tile's 32 positions wrap the ring at most once
   return true;
 }
 
@@ -199,7 +200,7 @@ StepLayout step_layout(const q4dec_model* m) {
   auto take = [&](size_t bytes) { size_t o = off; off = align256(off + bytes); return o; };
   L.sp = take(sizeof(StepParams));
   L.best = take(sizeof(unsigned long long) * 4);
-  L.rope = take(sizeof(double) * (m->sl_rot_pairs + m->full_rot_pairs + 1));
+  L.rope = take(sizeof(float2) * kMaxRows * (m->sl_rot_pairs + m->full_rot_pairs + 1));
   L.hA = take(sizeof(float) * kMaxRows * H);
   L.hB = take(sizeof(float) * kMaxRows * H);
   L.qkv = take(sizeof(float) * kMaxRows * L.qkv_ld);
@@ -215,7 +216,7 @@ StepLayout step_layout(const q4dec_model* m) {
 struct StepPtrs {
   StepParams* sp;
   unsigned long long* best;
-  double* rope;
+  float2* rope;
   float *hA, *hB, *qkv, *y, *apart;
   uint16_t *o, *a, *xf;
 };
@@ -225,7 +226,7 @@ StepPtrs step_ptrs(const StepLayout& L, void* ws) {
   StepPtrs p;
   p.sp = reinterpret_cast<StepParams*>(b + L.sp);
   p.best = reinterpret_cast<unsigned long long*>(b + L.best);
-  p.rope = reinterpret_cast<double*>(b + L.rope);
+  p.rope = reinterpret_cast<float2*>(b + L.rope);
   p.hA = reinterpret_cast<float*>(b + L.hA);
   p.hB = reinterpret_cast<float*>(b + L.hB);
   p.qkv = reinterpret_cast<float*>(b + L.qkv);
@@ -294,7 +295,8 @@ q4_status enqueue_layers(const q4dec_model* m, const StepLayout& L, const StepPt
       a.fin_on = 1;
       a.fin.qkv = P.qkv; a.fin.ldq = L.qkv_ld; a.fin.q_norm = ly.q_norm; a.fin.k_norm = ly.k_norm;
       a.fin.v_norm = ly.v_norm; a.fin.rot_pairs = full ? m->full_rot_pairs : m->sl_rot_pairs;
-      a.fin.inv_freq = full ? P.rope + m->sl_rot_pairs : P.rope; a.fin.eps = m->eps;
+      a.fin.rope_cs = full ? P.rope + m->sl_rot_pairs : P.rope;
+      a.fin.cs_ld = m->sl_rot_pairs + m->full_rot_pairs + 1; a.fin.eps = m->eps;
       launch_fd(a, D, 1, nullptr, P.o, st);
     }
     // ---- output projection
@@ -411,7 +413,7 @@ q4_status begin_step(const q4dec_model* m, const StepPtrs& P, const int32_t* tok
   b.best = P.best;
   b.E = m->embed; b.H = m->hidden; b.emb_scale = (float)std::sqrt((double)m->hidden);
   b.h = P.hA;
-  b.inv_freq = P.rope; b.ns = m->sl_rot_pairs; b.nf = m->full_rot_pairs;
+  b.rope_cs = P.rope; b.ns = m->sl_rot_pairs; b.nf = m->full_rot_pairs;
   b.Ds = m->sl_head_dim; b.Df = m->full_head_dim; b.theta_s = m->sl_theta; b.theta_f = m->full_theta;
   hipLaunchKernelGGL(k_step_begin, dim3(n), dim3(256), 0, st, b);
   return launch_status();
@@ -590,6 +592,7 @@ q4_status flash_decode_ring(const uint16_t* q, const uint16_t* k_ring, const uin
   q4_status rc = fd_common(q, k_ring, v_ring, seq_stride, Hq, Hkv, D, pos0, n_seq, n_rows, out, ws, ws_bytes);
   if (rc != Q4_OK) return rc;
   if (W < 1 || R < 1 || W > R || (long)R < (long)W + n_rows - 1) return Q4_ERANGE;
+  if (R < 32) return Q4_ESHAPE;   // a tile's 32 positions wrap the ring at most once
   if (n_seq > 1 && seq_stride < (int64_t)Hkv * R * D) return Q4_ESHAPE;
   for (int s = 0; s < n_seq; s++)
     if (pos0[s] < 0 || (long)pos0[s] + n_rows - 1 > 0x7FFFFFFFL) return Q4_ERANGE;

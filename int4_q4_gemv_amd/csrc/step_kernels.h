@@ -15,14 +15,19 @@ struct BeginArgs {
   int H;
   float emb_scale;          // sqrt(H)
   float* h;                 // [4][H]
-  double* inv_freq;         // [ns + nf]: RoPE inverse frequencies, sliding then full
+  float2* rope_cs;          // [4][ns + nf + 1]: (cos, sin) per row and pair, sliding then full
   int ns, nf, Ds, Df;
   double theta_s, theta_f;
 };
 
 // One workgroup per row: h = fp32(E[token]) * sqrt(H) (reading of the
-// embedding scale); workgroup 0 also publishes the step parameters and the
-// RoPE inverse frequencies theta^(-2i/D) in fp64 (one table per layer kind).
+// embedding scale) and the RoPE rotations of the row's position p: for pair
+// i of a layer kind with head size D and base theta, the angle p * theta^(-2i/D)
+// is formed in fp64 (power and product), reduced to [-pi, pi] in fp64 by one
+// fma with the double nearest 2 pi (k * 2.5e-16 rad of error, under 1e-10 for
+// positions below 2^20), and its cos and sin are taken in fp32.  Every
+// attention workgroup of the step reads them from this table instead of
+// recomputing them.  Workgroup 0 also publishes the step parameters.
 __global__ void __launch_bounds__(256) k_step_begin(BeginArgs a) {
   const int b = blockIdx.x, tid = threadIdx.x;
   if (b == 0) {
@@ -32,9 +37,20 @@ __global__ void __launch_bounds__(256) k_step_begin(BeginArgs a) {
       for (int i = 0; i < 4; i++) a.sp->tokens[i] = a.tokens[i];
     }
     if (tid < 4) a.best[tid] = 0ull;
-    for (int i = tid; i < a.ns + a.nf; i += 256)
-      a.inv_freq[i] = i < a.ns ? pow(a.theta_s, -2.0 * (double)i / (double)a.Ds)
-                               : pow(a.theta_f, -2.0 * (double)(i - a.ns) / (double)a.Df);
+  }
+  const int pos = a.pos0 + b;
+  const int ld = a.ns + a.nf + 1;
+  for (int i = tid; i < a.ns + a.nf; i += 256) {
+    const bool sl = i < a.ns;
+    const int ii = sl ? i : i - a.ns;
+    const double fr = sl ? pow(a.theta_s, -2.0 * (double)ii / (double)a.Ds)
+                         : pow(a.theta_f, -2.0 * (double)ii / (double)a.Df);
+    const double ang = (double)pos * fr;
+    const double k = rint(ang * 0.15915494309189535);
+    const float r = (float)fma(-k, 6.283185307179586, ang);
+    float sn, cn;
+    sincosf(r, &sn, &cn);
+    a.rope_cs[(long)b * ld + i] = make_float2(cn, sn);
   }
   const uint16_t* e = a.E + (long)a.tokens[b] * a.H;
   float* h = a.h + (long)b * a.H;

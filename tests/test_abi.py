@@ -68,6 +68,9 @@ def test_argument_checks_fail_before_launch():
                                C.c_float(1.0), fake, fake, ws, None) == q4.Q4_ERANGE
     assert L.flash_decode_ring(fake, fake, fake, 0, 16, 5, 256, 2048, 1024, pos, 1, 1,
                                C.c_float(1.0), fake, fake, ws, None) == q4.Q4_ESHAPE
+    # a ring holds at least one 32-position tile
+    assert L.flash_decode_ring(fake, fake, fake, 0, 16, 8, 256, 16, 8, pos, 1, 1,
+                               C.c_float(1.0), fake, fake, ws, None) == q4.Q4_ESHAPE
 
 
 def test_decode_step_checks():
@@ -96,3 +99,5 @@ def test_decode_step_checks():
     assert L.decode_step_hidden(C.byref(m), f, big, 5, f, None) == q4.Q4_ESHAPE
     m.ring = cfg.window + 2      # a 4-row block needs R >= W + 3
     assert L.decode_step(C.byref(m), tok, 4, 5, f, f, f, big, None) == q4.Q4_ERANGE
+    m.ring, m.window = 16, 8     # a ring holds at least one 32-position tile
+    assert L.decode_step(C.byref(m), tok, 1, 5, f, f, f, big, None) == q4.Q4_ESHAPE
