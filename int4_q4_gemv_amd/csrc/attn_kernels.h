@@ -427,6 +427,28 @@ __global__ void __launch_bounds__(256) k_fd_partial(AttnArgs a) {
   float l_tot = l_part + __shfl_xor(l_part, 16, 64);
   l_tot += __shfl_xor(l_tot, 32, 64);
 
+  // ---- a split of at most one tile: wave 0 holds the whole record and
+  // stores it from registers (the merge below would give the same values:
+  // the other waves' weights are 0 and wave 0's is 1)
+  if (en - st <= 32) {
+    if (wave != 0) return;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const int col = 4 * g + i;
+      if (col < a.GQ) {
+        float* rec = a.part + attn_rec(a, seq, row, kvh, split, col, D);
+#pragma unroll
+        for (int d = 0; d < NDS; d++) rec[16 * d + j] = O[d][i];
+      }
+    }
+    if (lane < a.GQ) {
+      float* rec = a.part + attn_rec(a, seq, row, kvh, split, lane, D);
+      rec[D] = m_run;
+      rec[D + 1] = l_tot;
+    }
+    return;
+  }
+
   // ---- merge the 4 waves (the V rows are free now): per head the wave
   // maxima meet in LDS; each wave rescales its own O rows in registers and
   // stores them as one float4 per (dim step, lane), the 4 heads of that lane
