@@ -289,73 +289,91 @@ __global__ void __launch_bounds__(B == 1 ? 1024 : 512) k_q4_gemv(GemvArgs a) {
 }
 
 // ------------------------------------------------------------- RMSNorm ----
-// One workgroup of 1024 threads per row (H <= 4096): h_new as in NormIn,
-// stored to h_dst (when set), and x = fp16(RMSNorm(h_new) * w_in), the input
-// of the next product.  Every global load of the row is issued up front; the
+// One workgroup of 512 threads per row (H <= 4096, H % 4 == 0): h_new as in
+// NormIn, stored to h_dst (when set), and x = fp16(RMSNorm(h_new) * w_in),
+// the input of the next product.  Thread t handles elements 4 (t + 512 c) ..
+// +3 through 16-byte loads, and every global load of the row is issued up
+// front (a lone workgroup is bound by its CU's load issue: 16-byte loads
+// move the row in a quarter of the instructions).  Partial products past ny
+// alias the first and are added times 0, so no load waits for another; the
 // two mean squares are block sums in a fixed order.
-__global__ void __launch_bounds__(1024) k_norm_rows(NormIn p, uint16_t* x) {
-  constexpr int E = 4;
+__global__ void __launch_bounds__(512) k_norm_rows(NormIn p, uint16_t* x) {
+  constexpr int NT = 512, C = 4096 / 4 / NT;
   __shared__ float nred[16];
   const int b = blockIdx.x;               // grid: the rows of the step
-  const int H = p.H, tid = threadIdx.x;
-  const float* hs = p.h_src + (long)b * H;
+  const int H = p.H, tid = threadIdx.x, n4 = H / 4;
   const float* y = p.y ? p.y + (long)b * H : nullptr;
-  // partial products past ny alias the first one and are dropped below, so
-  // every load is unconditional and all of them are in flight together
-  const float* y0 = y ? y : hs;
-  const float* y1 = p.ny > 1 ? y0 + p.y_split : y0;
-  const float* y2 = p.ny > 2 ? y0 + 2 * p.y_split : y0;
-  const float* y3 = p.ny > 3 ? y0 + 3 * p.y_split : y0;
-  const float* wpp = y ? p.w_post : p.w_in;
+  const float4* hs = reinterpret_cast<const float4*>(p.h_src + (long)b * H);
+  const float4* y0 = y ? reinterpret_cast<const float4*>(y) : hs;
+  const long ys4 = p.y_split / 4;
+  const float4* y1 = p.ny > 1 ? y0 + ys4 : y0;
+  const float4* y2 = p.ny > 2 ? y0 + 2 * ys4 : y0;
+  const float4* y3 = p.ny > 3 ? y0 + 3 * ys4 : y0;
+  const float4* wp4 = reinterpret_cast<const float4*>(y ? p.w_post : p.w_in);
+  const float4* wi4 = reinterpret_cast<const float4*>(p.w_in);
   const float m1 = p.ny > 1 ? 1.f : 0.f, m2 = p.ny > 2 ? 1.f : 0.f, m3 = p.ny > 3 ? 1.f : 0.f;
-  float hv[E], yv[E], wp[E], wi[E], a1[E], a2[E], a3[E];
+  float4 hv[C], a0[C], a1[C], a2[C], a3[C], wp[C], wi[C];
 #pragma unroll
-  for (int e = 0; e < E; e++) {
-    const int k = min(tid + 1024 * e, H - 1);
-    hv[e] = hs[k];
-    wi[e] = p.w_in[k];
-    wp[e] = wpp[k];
-    yv[e] = y0[k];
-    a1[e] = y1[k];
-    a2[e] = y2[k];
-    a3[e] = y3[k];
+  for (int c = 0; c < C; c++) {
+    const int k = min(tid + NT * c, n4 - 1);
+    hv[c] = hs[k];
+    a0[c] = y0[k];
+    a1[c] = y1[k];
+    a2[c] = y2[k];
+    a3[c] = y3[k];
+    wp[c] = wp4[k];
+    wi[c] = wi4[k];
   }
-  // the sums come after every load has been issued, and are branch-free so
-  // that none of them waits on a single load; same order ((a0 + a1) + a2) +
-  // a3, an absent part adding an exact zero
   __builtin_amdgcn_sched_barrier(0);
+  // partial sums in the order ((a0 + a1) + a2) + a3; out-of-range elements 0
+  float yv[C][4], hh[C][4];
+  float ss = 0.f;
 #pragma unroll
-  for (int e = 0; e < E; e++) {
-    const float v = ((yv[e] + m1 * a1[e]) + m2 * a2[e]) + m3 * a3[e];
-    yv[e] = (y && tid + 1024 * e < H) ? v : 0.f;
-    if (tid + 1024 * e >= H) hv[e] = 0.f;
+  for (int c = 0; c < C; c++) {
+    const bool in = tid + NT * c < n4;
+    const float A0[4] = {a0[c].x, a0[c].y, a0[c].z, a0[c].w}, A1[4] = {a1[c].x, a1[c].y, a1[c].z, a1[c].w};
+    const float A2[4] = {a2[c].x, a2[c].y, a2[c].z, a2[c].w}, A3[4] = {a3[c].x, a3[c].y, a3[c].z, a3[c].w};
+    const float HV[4] = {hv[c].x, hv[c].y, hv[c].z, hv[c].w};
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+      const float v = ((A0[e] + m1 * A1[e]) + m2 * A2[e]) + m3 * A3[e];
+      yv[c][e] = (y && in) ? v : 0.f;
+      hh[c][e] = in ? HV[e] : 0.f;
+      ss += yv[c][e] * yv[c][e];
+    }
   }
   float inv_y = 0.f;
   if (y) {
-    float ss = 0.f;
-#pragma unroll
-    for (int e = 0; e < E; e++) ss += yv[e] * yv[e];
     ss = block_sum_dyn(ss, nred);
     inv_y = 1.0f / sqrtf(ss / (float)H + p.eps);
   }
   float ss2 = 0.f;
 #pragma unroll
-  for (int e = 0; e < E; e++) {
-    float v = hv[e];
-    if (y) v += yv[e] * inv_y * wp[e];
-    v *= p.scalar;
-    hv[e] = v;
-    ss2 += v * v;
+  for (int c = 0; c < C; c++) {
+    const float WP[4] = {wp[c].x, wp[c].y, wp[c].z, wp[c].w};
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+      float v = hh[c][e];
+      if (y) v += yv[c][e] * inv_y * WP[e];
+      v *= p.scalar;
+      hh[c][e] = v;
+      ss2 += v * v;
+    }
   }
   ss2 = block_sum_dyn(ss2, nred);
   const float inv_h = 1.0f / sqrtf(ss2 / (float)H + p.eps);
-  float* hd = p.h_dst ? p.h_dst + (long)b * H : nullptr;
+  float4* hd = p.h_dst ? reinterpret_cast<float4*>(p.h_dst + (long)b * H) : nullptr;
+  uint2* xo = reinterpret_cast<uint2*>(x + (long)b * H);
 #pragma unroll
-  for (int e = 0; e < E; e++) {
-    const int k = tid + 1024 * e;
-    if (k < H) {
-      if (hd) hd[k] = hv[e];
-      x[(long)b * H + k] = f2h(hv[e] * inv_h * wi[e]);
+  for (int c = 0; c < C; c++) {
+    const int k = tid + NT * c;
+    if (k < n4) {
+      const float WI[4] = {wi[c].x, wi[c].y, wi[c].z, wi[c].w};
+      if (hd) hd[k] = make_float4(hh[c][0], hh[c][1], hh[c][2], hh[c][3]);
+      uint2 o;
+      o.x = (uint32_t)f2h(hh[c][0] * inv_h * WI[0]) | ((uint32_t)f2h(hh[c][1] * inv_h * WI[1]) << 16);
+      o.y = (uint32_t)f2h(hh[c][2] * inv_h * WI[2]) | ((uint32_t)f2h(hh[c][3] * inv_h * WI[3]) << 16);
+      xo[k] = o;
     }
   }
 }

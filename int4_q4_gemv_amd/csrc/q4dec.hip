@@ -25,7 +25,8 @@ constexpr int kMaxRows = 4;
 constexpr int kFullSplits = 256;     // decode-step splits of a full layer's positions
 constexpr int kTilePos = 128;        // positions per workgroup pass (4 waves x 32)
 constexpr int kMaxLds = 160 * 1024;
-constexpr int kSplitQuads = 32;      // decode step: longest run of K quads per workgroup
+constexpr int kSplitQuads = 32;      // decode step: longest run of K quads per workgroup (down)
+constexpr int kSplitQuadsO = 16;     // decode step: the same for the output projection
 
 bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 hipStream_t S(void* s) { return reinterpret_cast<hipStream_t>(s); }
@@ -183,8 +184,8 @@ StepLayout step_layout(const q4dec_model* m) {
   // gate/up keeps K whole (its epilogue needs both full sums).
   L.p_qkv_s = gemv_plan(Hq * Ds + 2 * Hs * Ds, H, 8);
   L.p_qkv_f = gemv_plan(Hq * Df + Df, H, 8);
-  L.p_o_s = gemv_plan(H, Hq * Ds, 8, kSplitQuads);
-  L.p_o_f = gemv_plan(H, Hq * Df, 8, kSplitQuads);
+  L.p_o_s = gemv_plan(H, Hq * Ds, 8, kSplitQuadsO);
+  L.p_o_f = gemv_plan(H, Hq * Df, 8, kSplitQuadsO);
   L.p_gu = gemv_plan(I, H, 4);
   L.p_d = gemv_plan(H, I, 8, kSplitQuads);
   L.ymax = std::max(std::max(L.p_o_s.S, L.p_o_f.S), L.p_d.S);
@@ -277,7 +278,7 @@ q4_status enqueue_layers(const q4dec_model* m, const StepLayout& L, const StepPt
         ni.ny = L.p_d.S; ni.y_split = (long)n * H;
       }
       ni.w_in = ly.attn_norm; ni.H = H; ni.eps = m->eps;
-      hipLaunchKernelGGL(k_norm_rows, dim3(n), dim3(1024), 0, st, ni, P.xf);
+      hipLaunchKernelGGL(k_norm_rows, dim3(n), dim3(512), 0, st, ni, P.xf);
       a.K = H; a.NQ = pl.NQ; a.W = pl.W; a.NQs = pl.NQs;
       a.x = P.xf; a.ldx = H;
       a.y = P.qkv; a.ldy = L.qkv_ld; a.n_rows = n;
@@ -321,7 +322,7 @@ q4_status enqueue_layers(const q4dec_model* m, const StepLayout& L, const StepPt
       ni.h_src = P.hA; ni.y = P.y; ni.ny = (full ? L.p_o_f : L.p_o_s).S; ni.y_split = (long)n * H;
       ni.w_post = ly.post_attn_norm; ni.scalar = 1.0f;
       ni.w_in = ly.pre_ff_norm; ni.h_dst = P.hB; ni.H = H; ni.eps = m->eps;
-      hipLaunchKernelGGL(k_norm_rows, dim3(n), dim3(1024), 0, st, ni, P.xf);
+      hipLaunchKernelGGL(k_norm_rows, dim3(n), dim3(512), 0, st, ni, P.xf);
       a.K = H; a.NQ = pl.NQ; a.W = pl.W; a.NQs = pl.NQs;
       a.x = P.xf; a.ldx = H;
       a.a_out = P.a; a.inter = I; a.n_rows = n;
@@ -346,7 +347,7 @@ q4_status enqueue_layers(const q4dec_model* m, const StepLayout& L, const StepPt
     ni.h_src = P.hB; ni.y = P.y; ni.ny = L.p_d.S; ni.y_split = (long)n * H;
     ni.w_post = last.post_ff_norm; ni.scalar = last.layer_scalar;
     ni.w_in = m->final_norm; ni.h_dst = P.hA; ni.H = H; ni.eps = m->eps;
-    hipLaunchKernelGGL(k_norm_rows, dim3(n), dim3(1024), 0, st, ni, P.xf);
+    hipLaunchKernelGGL(k_norm_rows, dim3(n), dim3(512), 0, st, ni, P.xf);
   }
   {
     HeadArgs a{};
