@@ -39,7 +39,7 @@ struct AttnFin {
   const float* k_norm;
   int v_norm;
   int rot_pairs;
-  const float2* rope_cs;  // [row][cs_ld]: (cos, sin) of pair i at the row's position
+  const float2* rope_cs;  // [row][cs_ld]: (cos, sin) of pair i < D/2 at the row's position
   int cs_ld;
   float eps;
 };
@@ -76,14 +76,59 @@ constexpr size_t fd_lds_bytes() {
   return (size_t)4 * 32 * fd_vpitch<D>() * 2 + (size_t)2 * 4 * D * 2 + (size_t)16 * D * 2;
 }
 
-// Per-head RMSNorm (weights wv, or scale-free) and RoPE on one head vector
-// held by one wave: lane l holds elements l + 64e (v, wv); fp16 result to dst
-// (LDS).  The rotated pairs (i, i + D/2) sit in one lane (D >= 128) or in
-// lanes l and l + 32 (D = 64); cs holds (cos, sin) of this lane's pairs at
-// the vector's position (pairs past rot_pairs are not rotated).
+// Layout of a head vector (D elements) spread over one wave for finishing:
+// lane l holds H = D / 128 consecutive elements of each half, l*H .. l*H+H-1
+// and D/2 + l*H .. D/2 + l*H+H-1 (v[0..H) and v[H..2H)), so the rotated pairs
+// (i, i + D/2) sit in one lane and each half is one vector load; D = 64 keeps
+// one element per lane (element l), its pairs in lanes l and l + 32.
+template <int D> constexpr int fin_h() { return D >= 128 ? D / 128 : 1; }
+
+template <int N> struct fvec;            // N consecutive floats as one load
+template <> struct fvec<1> { using t = float; };
+template <> struct fvec<2> { using t = float2; };
+template <> struct fvec<4> { using t = float4; };
+
+// loads the wave's share of a D-float vector in the finishing layout
+template <int D>
+Q4_DEV void fin_load(float (&v)[D / 64], const float* src) {
+  const int lane = threadIdx.x & 63;
+  if constexpr (D == 64) {
+    v[0] = src[lane];
+  } else {
+    constexpr int H = fin_h<D>();
+    using V = typename fvec<H>::t;
+    const V lo = *reinterpret_cast<const V*>(src + lane * H);
+    const V hi = *reinterpret_cast<const V*>(src + D / 2 + lane * H);
+    const float* pl = reinterpret_cast<const float*>(&lo);
+    const float* ph = reinterpret_cast<const float*>(&hi);
+#pragma unroll
+    for (int e = 0; e < H; e++) { v[e] = pl[e]; v[H + e] = ph[e]; }
+  }
+}
+
+// stores the wave's share (finishing layout) as fp16 to dst (LDS)
+template <int D>
+Q4_DEV void fin_store(const float (&v)[D / 64], uint16_t* dst) {
+  const int lane = threadIdx.x & 63;
+  if constexpr (D == 64) {
+    dst[lane] = f2h(v[0]);
+  } else {
+    constexpr int H = fin_h<D>();
+#pragma unroll
+    for (int e = 0; e < H; e++) {
+      dst[lane * H + e] = f2h(v[e]);
+      dst[D / 2 + lane * H + e] = f2h(v[H + e]);
+    }
+  }
+}
+
+// Per-head RMSNorm (weights wv, or scale-free) and RoPE on one head vector in
+// the finishing layout; fp16 result to dst (LDS).  cs holds (cos, sin) of
+// this lane's pairs (l*H + e; D = 64: l mod 32) at the vector's position;
+// pairs past rot_pairs are not rotated.
 template <int D>
 Q4_DEV void finish_vals(float (&v)[D / 64], const float (&wv)[D / 64], bool weighted, bool rope,
-                        const float2 (&cs)[D / 128 > 0 ? D / 128 : 1], int rot_pairs, float eps, uint16_t* dst) {
+                        const float2 (&cs)[fin_h<D>()], int rot_pairs, float eps, uint16_t* dst) {
   constexpr int E = D / 64;
   const int lane = threadIdx.x & 63;
   float ss = 0.f;
@@ -105,16 +150,13 @@ Q4_DEV void finish_vals(float (&v)[D / 64], const float (&wv)[D / 64], bool weig
     const float other = __shfl_xor(v[0], 32, 64);
     float x0 = lane < 32 ? v[0] : other, x1 = lane < 32 ? other : v[0];
     rot(lane & 31, cs[0], x0, x1);
-    dst[lane] = f2h(lane < 32 ? x0 : x1);
+    v[0] = lane < 32 ? x0 : x1;
   } else {
+    constexpr int H = fin_h<D>();
 #pragma unroll
-    for (int e = 0; e < E / 2; e++) {
-      float x0 = v[e], x1 = v[e + E / 2];
-      rot(lane + 64 * e, cs[e], x0, x1);
-      dst[lane + 64 * e] = f2h(x0);
-      dst[lane + 64 * e + D / 2] = f2h(x1);
-    }
+    for (int e = 0; e < H; e++) rot(lane * H + e, cs[e], v[e], v[H + e]);
   }
+  fin_store<D>(v, dst);
 }
 
 template <int D>
@@ -133,7 +175,9 @@ __global__ void __launch_bounds__(256) k_fd_partial(AttnArgs a) {
   const int seq = blockIdx.z / a.n_rows, row = blockIdx.z - seq * a.n_rows;
   const int nlive = a.n_rows;                 // the grid is built per row count
   if (row >= nlive) return;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // the wave index as a scalar: tile origins and cache rows derived from it
+  // are then computed once per wave, not per lane
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
 
   // ---- the step's first position, before any other load: a global load
   // (not a generic one through a pointer that may also point at the
@@ -148,40 +192,43 @@ __global__ void __launch_bounds__(256) k_fd_partial(AttnArgs a) {
   // heads of this workgroup's columns, then k and v of every row 0 .. row of
   // the step (after the position is known, only the rows in this
   // workgroup's range are finished).
-  constexpr int FE = D / 64, FEH = D / 128 > 0 ? D / 128 : 1;
+  constexpr int FE = D / 64, FEH = fin_h<D>();
   constexpr int MAXJ = (16 + 2 * 4 + 3) / 4;
   const int njobs = a.fin_on ? a.GQ + 2 * (row + 1) : 0;
   float raw[MAXJ][FE], wq[FE], wk[FE];
   float2 fcs[MAXJ][FEH];
   if (a.fin_on) {
     const AttnFin& f = a.fin;
-#pragma unroll
-    for (int e = 0; e < FE; e++) {
-      wq[e] = f.q_norm[lane + 64 * e];
-      wk[e] = f.k_norm[lane + 64 * e];
-    }
+    fin_load<D>(wq, f.q_norm);
+    fin_load<D>(wk, f.k_norm);
 #pragma unroll
     for (int k = 0; k < MAXJ; k++) {
-      const int jb0 = wave + 4 * k;
-      const int jb = jb0 < njobs ? jb0 : 0;
+      const int jb = wave + 4 * k;
+      if (jb >= njobs) break;                                // wave-uniform
       const int r = jb < a.GQ ? row : (jb - a.GQ) >> 1;    // row of the step the job belongs to
       const float* rr = f.qkv + (long)r * f.ldq;
       const float* src;
       if (jb < a.GQ) src = rr + (long)(kvh * a.GQ + jb) * D;
       else if (((jb - a.GQ) & 1) == 0 || !a.ring) src = rr + (long)(a.Hq + kvh) * D;   // k (full: V from raw k)
       else src = rr + (long)(a.Hq + a.Hkv + kvh) * D;                                   // v
-#pragma unroll
-      for (int e = 0; e < FE; e++) raw[k][e] = src[lane + 64 * e];
-      const float2* cr = f.rope_cs + (long)r * f.cs_ld;
-#pragma unroll
-      for (int e = 0; e < FEH; e++) {
-        const int i = FE == 1 ? (lane & 31) : lane + 64 * e;
-        fcs[k][e] = cr[min(i, max(f.rot_pairs - 1, 0))];
+      fin_load<D>(raw[k], src);
+      // (cos, sin) of this lane's pairs: the table row holds D / 2 pairs
+      const float2* cr = f.rope_cs + (long)r * f.cs_ld + (D == 64 ? (lane & 31) : lane * FEH);
+      if constexpr (FEH == 4) {
+        const float4 c0 = *reinterpret_cast<const float4*>(cr), c1 = *reinterpret_cast<const float4*>(cr + 2);
+        fcs[k][0] = make_float2(c0.x, c0.y); fcs[k][1] = make_float2(c0.z, c0.w);
+        fcs[k][2] = make_float2(c1.x, c1.y); fcs[k][3] = make_float2(c1.z, c1.w);
+      } else if constexpr (FEH == 2) {
+        const float4 c0 = *reinterpret_cast<const float4*>(cr);
+        fcs[k][0] = make_float2(c0.x, c0.y); fcs[k][1] = make_float2(c0.z, c0.w);
+      } else {
+        fcs[k][0] = *cr;
       }
     }
   }
   __builtin_amdgcn_sched_barrier(0);
 
+  base = __builtin_amdgcn_readfirstlane(base);   // uniform: the split bounds and rows are scalar
   const int P = base + row;
   const int lo = a.ring ? max(0, P - a.W + 1) : 0;
   const int L = P - lo + 1;
@@ -221,19 +268,23 @@ __global__ void __launch_bounds__(256) k_fd_partial(AttnArgs a) {
   const bool ringf = a.ring != 0;
   const int Rr = ringf ? a.R : 1;
   const int nv_end = min(en, P0new);
-  auto slot_of = [&](int p) -> int { return ringf ? p % Rr : p; };
-  // cache row (in elements) of tile row r0 + d, given s0 = slot of tile row r0
-  auto row_at = [&](int nv, int s0, int r0, int d) -> long {
-    const int sl = ringf && d >= Rr - s0 ? s0 + d - Rr : s0 + d;
-    const long off = (long)sl * D;
-    return r0 + d < nv ? off : 0l;
+  // scalar tile geometry: slot of the tile's first position and the number
+  // of tile rows read from the cache
+  auto tile_geom = [&](int t0, int& s0, int& nv) {
+    s0 = __builtin_amdgcn_readfirstlane(ringf ? t0 % Rr : t0);
+    nv = __builtin_amdgcn_readfirstlane(nv_end - t0);
+  };
+  // cache row (in elements) of tile row r (r < 32)
+  auto row_at = [&](int s0, int nv, int r) -> long {
+    const int sl = ringf && r >= Rr - s0 ? s0 + r - Rr : s0 + r;
+    return r < nv ? (long)sl * D : 0l;
   };
   auto load_k = [&](int t0) {
-    const int nv = nv_end - t0;
+    int s0, nv;
+    tile_geom(t0, s0, nv);
     const int ra = 8 * (j >> 2) + (j & 3);
-    const int s0 = slot_of(t0 + ra);
-    const uint16_t* ka = kb + row_at(nv, s0, ra, 0) + 8 * g;
-    const uint16_t* kc = kb + row_at(nv, s0, ra, 4) + 8 * g;
+    const uint16_t* ka = kb + row_at(s0, nv, ra) + 8 * g;
+    const uint16_t* kc = kb + row_at(s0, nv, ra + 4) + 8 * g;
 #pragma unroll
     for (int s = 0; s < NKS; s++) {
       KA[s] = __builtin_bit_cast(h8_t, __builtin_nontemporal_load(reinterpret_cast<const u4v*>(ka + 32 * s)));
@@ -241,27 +292,30 @@ __global__ void __launch_bounds__(256) k_fd_partial(AttnArgs a) {
     }
   };
   auto load_v = [&](int t0) {
-    const int nv = nv_end - t0;
+    int s0, nv;
+    tile_geom(t0, s0, nv);
     if constexpr (HV) {
       // chunk i of lane l: tile row (l + 64 i) / (D / 8), 16-byte column (l mod D / 8)
       constexpr int STEP = 512 / D;
       const int r0 = lane / (D / 8), cc = lane % (D / 8);
-      const int s0 = slot_of(t0 + r0);
 #pragma unroll
       for (int i = 0; i < VCH; i++)
-        VV[i] = __builtin_nontemporal_load(reinterpret_cast<const u4v*>(vb + row_at(nv, s0, r0, STEP * i) + cc * 8));
+        VV[i] = __builtin_nontemporal_load(reinterpret_cast<const u4v*>(vb + row_at(s0, nv, r0 + STEP * i) + cc * 8));
     } else {
-      const int s0 = slot_of(t0);
+      // one 1 KB row per instruction: its address is scalar, plus the lane's
+      // swizzled 16-byte column
 #pragma unroll
       for (int r = 0; r < 32; r++) {
         const int c = lane ^ ((r >> 3) & 3);
-        __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint32_t*>(vb + row_at(nv, s0, 0, r) + c * 8),
+        const uint16_t* rowp = vb + row_at(s0, nv, r);
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint32_t*>(rowp + c * 8),
                                          reinterpret_cast<uint32_t*>(vl + r * D), 16, 0, 0);
       }
     }
   };
-  // the first tile: V (and for D <= 256 also K) before the prologue; K of
-  // D = 512 (128 registers) waits for the prologue's registers to free up
+  // the first tile: V, and for D <= 256 also K, before the prologue (with the
+  // prologue's inputs that stays under the 63 vector loads a wave may have in
+  // flight); K of D = 512 (128 registers) waits for the prologue's registers
   int t0 = st + 32 * wave;
   if (t0 < en) {
     if (HV) load_k(t0);
@@ -290,8 +344,7 @@ __global__ void __launch_bounds__(256) k_fd_partial(AttnArgs a) {
       } else if (f.v_norm) {
         finish_vals<D>(raw[k], wk, false, false, fcs[k], f.rot_pairs, f.eps, newV + r * D);
       } else {
-#pragma unroll
-        for (int e = 0; e < FE; e++) newV[r * D + lane + 64 * e] = f2h(raw[k][e]);
+        fin_store<D>(raw[k], newV + r * D);
       }
     }
     __syncthreads();

@@ -201,7 +201,7 @@ StepLayout step_layout(const q4dec_model* m) {
   auto take = [&](size_t bytes) { size_t o = off; off = align256(off + bytes); return o; };
   L.sp = take(sizeof(StepParams));
   L.best = take(sizeof(unsigned long long) * 4);
-  L.rope = take(sizeof(float2) * kMaxRows * (m->sl_rot_pairs + m->full_rot_pairs + 1));
+  L.rope = take(sizeof(float2) * kMaxRows * (Ds / 2 + Df / 2));
   L.hA = take(sizeof(float) * kMaxRows * H);
   L.hB = take(sizeof(float) * kMaxRows * H);
   L.qkv = take(sizeof(float) * kMaxRows * L.qkv_ld);
@@ -296,8 +296,8 @@ q4_status enqueue_layers(const q4dec_model* m, const StepLayout& L, const StepPt
       a.fin_on = 1;
       a.fin.qkv = P.qkv; a.fin.ldq = L.qkv_ld; a.fin.q_norm = ly.q_norm; a.fin.k_norm = ly.k_norm;
       a.fin.v_norm = ly.v_norm; a.fin.rot_pairs = full ? m->full_rot_pairs : m->sl_rot_pairs;
-      a.fin.rope_cs = full ? P.rope + m->sl_rot_pairs : P.rope;
-      a.fin.cs_ld = m->sl_rot_pairs + m->full_rot_pairs + 1; a.fin.eps = m->eps;
+      a.fin.rope_cs = full ? P.rope + m->sl_head_dim / 2 : P.rope;
+      a.fin.cs_ld = m->sl_head_dim / 2 + m->full_head_dim / 2; a.fin.eps = m->eps;
       launch_fd(a, D, 1, nullptr, P.o, st);
     }
     // ---- output projection

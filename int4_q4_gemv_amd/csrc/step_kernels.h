@@ -15,7 +15,7 @@ struct BeginArgs {
   int H;
   float emb_scale;          // sqrt(H)
   float* h;                 // [4][H]
-  float2* rope_cs;          // [4][ns + nf + 1]: (cos, sin) per row and pair, sliding then full
+  float2* rope_cs;          // [4][Ds/2 + Df/2]: (cos, sin) per row and pair, sliding then full
   int ns, nf, Ds, Df;
   double theta_s, theta_f;
 };
@@ -38,19 +38,25 @@ __global__ void __launch_bounds__(256) k_step_begin(BeginArgs a) {
     }
     if (tid < 4) a.best[tid] = 0ull;
   }
+  // every pair slot of both kinds is written (pairs past rot_pairs, which
+  // are not rotated, get (1, 0)), so readers may load whole runs of it
   const int pos = a.pos0 + b;
-  const int ld = a.ns + a.nf + 1;
-  for (int i = tid; i < a.ns + a.nf; i += 256) {
-    const bool sl = i < a.ns;
-    const int ii = sl ? i : i - a.ns;
-    const double fr = sl ? pow(a.theta_s, -2.0 * (double)ii / (double)a.Ds)
-                         : pow(a.theta_f, -2.0 * (double)ii / (double)a.Df);
-    const double ang = (double)pos * fr;
-    const double k = rint(ang * 0.15915494309189535);
-    const float r = (float)fma(-k, 6.283185307179586, ang);
-    float sn, cn;
-    sincosf(r, &sn, &cn);
-    a.rope_cs[(long)b * ld + i] = make_float2(cn, sn);
+  const int hs = a.Ds / 2, ld = a.Ds / 2 + a.Df / 2;
+  for (int i = tid; i < ld; i += 256) {
+    const bool sl = i < hs;
+    const int ii = sl ? i : i - hs;
+    float2 c = make_float2(1.0f, 0.0f);
+    if (ii < (sl ? a.ns : a.nf)) {
+      const double fr = sl ? pow(a.theta_s, -2.0 * (double)ii / (double)a.Ds)
+                           : pow(a.theta_f, -2.0 * (double)ii / (double)a.Df);
+      const double ang = (double)pos * fr;
+      const double k = rint(ang * 0.15915494309189535);
+      const float r = (float)fma(-k, 6.283185307179586, ang);
+      float sn, cn;
+      sincosf(r, &sn, &cn);
+      c = make_float2(cn, sn);
+    }
+    a.rope_cs[(long)b * ld + i] = c;
   }
   const uint16_t* e = a.E + (long)a.tokens[b] * a.H;
   float* h = a.h + (long)b * a.H;
