@@ -71,6 +71,62 @@ def time_gemv(q4, torch, model, reps=10, warm=5):
     return avg_s, launches, q4.packed_bytes(N, K)
 
 
+def time_graph_calls(torch, fn, reps, replays=5):
+    """Average device time of fn(i), captured reps times into one graph and
+    replayed between two HIP events on the current stream."""
+    fn(0)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=torch.cuda.current_stream()):
+        for i in range(reps):
+            fn(i)
+    graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(replays):
+        graph.replay()
+    e1.record()
+    e1.synchronize()
+    return e0.elapsed_time(e1) * 1e-3 / (reps * replays)
+
+
+def time_attention(q4, torch):
+    """The two attention kernels on their own, on the synthetic inputs of the
+    scope table: full attention (16 q heads over one KV head, D 512, scale 1)
+    at contexts 32768 and 131072 in a 131076-row buffer, rotating 6 buffers
+    so that no call finds its keys in the last-level cache; the ring (8 KV
+    heads, D 256, W 1024, R 2048, position 100000) as one call and as 40
+    independent rings in one call.  Bytes per call: 2048 per full position,
+    1024 per admitted ring position and KV head."""
+    from int4_q4_gemv_amd import synth
+    res = {}
+    cap = 131076
+    bufs = [synth.full_attn_inputs(131072, cap, seed=3 + i, device="cuda") for i in range(6)]
+    ws = q4._fd_ws(1, 1, 16, 512, "cuda")
+    for ctx in (32768, 131072):
+        t = time_graph_calls(torch, lambda i: q4.flash_decode_full(*bufs[i % 6], ctx - 1, 1.0, ws=ws), 24)
+        nb = ctx * 2048
+        res[f"full_attention_ctx{ctx}"] = {"us": round(t * 1e6, 2), "bytes": nb,
+                                          "GBps": round(nb / t / 1e9, 1), "frac": round(nb / t / 1e9 / PEAK_GBPS, 4)}
+    del bufs
+    q, k, v = (t.to("cuda") for t in synth.ring_inputs(100000, n_rows=1, n_rejected=4))
+    ws = q4._fd_ws(1, 1, 16, 256, "cuda")
+    t = time_graph_calls(torch, lambda i: q4.flash_decode_ring(q, k, v, 1024, 100000, 1.0, ws=ws), 40)
+    res["ring_attention_1seq_us"] = round(t * 1e6, 2)
+    rings = [synth.ring_inputs(100000, n_rows=1, n_rejected=4, seed=100 + s, device="cuda") for s in range(40)]
+    qs = torch.stack([r[0] for r in rings]).to("cuda")
+    ks = torch.stack([r[1] for r in rings]).to("cuda")
+    vs = torch.stack([r[2] for r in rings]).to("cuda")
+    del rings
+    ws = q4._fd_ws(40, 1, 16, 256, "cuda")
+    t = time_graph_calls(torch, lambda i: q4.flash_decode_ring(qs, ks, vs, 1024, [100000] * 40, 1.0, ws=ws), 10)
+    nb = 40 * 8 * 1024 * 1024
+    res["ring_attention_40seq"] = {"us": round(t * 1e6, 2), "bytes": nb,
+                                   "GBps": round(nb / t / 1e9, 1), "frac": round(nb / t / 1e9 / PEAK_GBPS, 4)}
+    return res
+
+
 COPY_BYTES = 512 << 20
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "q4_gemv_15360x3840_traffic.txt")
 GEMV_SOURCES = ("int4_q4_gemv_amd/csrc/gemv_kernels.h", "int4_q4_gemv_amd/csrc/device_common.h",
@@ -176,20 +232,28 @@ def cpu_baseline(model, torch):
 
     tok = [1234]
     pos = 32767
-    m_s, m_sf = om([0]), om([0, 5])
-    x = np.zeros((1, cfg.hidden), np.uint16)
-    t = time.perf_counter(); oracle.f16_gemv(emb, x); t_h = time.perf_counter() - t
-    t = time.perf_counter(); m_s.decode_step(tok, pos, want_logits=False); t_c = time.perf_counter() - t
-    t = time.perf_counter(); m_sf.decode_step(tok, pos, want_logits=False); t_a = time.perf_counter() - t
-    t_s = max(t_c - t_h, 1e-9)
-    t_f = max(t_a - t_c, 1e-9)
+    m = om([0, 5])                  # its layer 0 is model layer 0 (sliding), layer 1 is layer 5 (full)
+    h = m.embed_tokens(tok)
+    wall = time.perf_counter()
+
+    def med3(f):
+        ts = []
+        for _ in range(3):
+            t = time.perf_counter()
+            f()
+            ts.append(time.perf_counter() - t)
+        return sorted(ts)[1]
+
+    t_s = med3(lambda: m.run_layer(0, h, pos))
+    t_f = med3(lambda: m.run_layer(1, h, pos))
+    t_h = med3(lambda: m.run_head(h, want_logits=False))
     per_tok = 40 * t_s + 8 * t_f + t_h
     return {"value": 1.0 / per_tok, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": ("one decode step of layer 0 (sliding) and of layers 0+5 (full, ctx 32768) of the "
-                       "same 12B-shape weights plus one vocab-head product; tokens/s = 1/(40 t_sliding + "
-                       "8 t_full + t_head)"),
+            "sample": ("the oracle's layer 0 (sliding) and layer 5 (full, context 32768) of the same "
+                       "12B-shape weights at position 32767, and its vocab head, each timed 3 times "
+                       "(median); tokens/s = 1/(40 t_sliding + 8 t_full + t_head)"),
             "t_sliding_s": t_s, "t_full_s": t_f, "t_head_s": t_h,
-            "wall_s": t_h + t_c + t_a}
+            "wall_s": round(time.perf_counter() - wall, 2)}
 
 
 def main():
@@ -251,6 +315,8 @@ def main():
                                          "rows_per_s": round(4 * k2 / sv, 2),
                                          "achieved_GBps": round(step_bytes * k2 / sv / 1e9, 1)}
             log(f"ctx 131072: {extra['ctx131072']}; verify4: {extra['verify4_ctx32768']}")
+            extra["attention_kernels"] = time_attention(q4, torch)
+            log(f"attention kernels: {extra['attention_kernels']}")
     res = {
         "metric": "decode tokens/s (batch 1, 48 layers) + achieved HBM GB/s as % of peak",
         "value": round(tok_s, 2), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,

@@ -12,6 +12,7 @@ import ctypes as C
 import math
 import os
 import subprocess
+import sys
 
 import torch
 
@@ -314,7 +315,7 @@ def build_decode_model(cfg, seed: int, ctx: int, device="cuda", pack_check=None,
     layers = []
     for l in range(cfg.n_layers):
         if cfg.n_layers > 8 and l % 8 == 0:
-            print(f"  building layer {l}/{cfg.n_layers}", flush=True)
+            print(f"  building layer {l}/{cfg.n_layers}", file=sys.stderr, flush=True)
         lp = synth.layer_params(cfg, l, seed, device=gd)
         L = {"is_full": cfg.is_full(l), "v_norm": cfg.is_full(l) or cfg.sl_v_norm,
              "layer_scalar": lp.layer_scalar}
