@@ -65,11 +65,13 @@ Q4_DEV long attn_rec(const AttnArgs& a, int seq, int row, int kvh, int split, in
   return (((((long)seq * a.n_rows + row) * a.Hkv + kvh) * a.S + split) * a.GQ + col) * (long)(D + 4);
 }
 
-// LDS of k_fd_partial: V rows [4 waves][32][pitch] (pitch D + 2 halves when
-// staged from registers, D when loaded straight into LDS with swizzled
-// chunks), rows of this step newK / newV [4][D], finished queries q16 [16][D].
+// LDS of k_fd_partial: V rows [4 waves][32][D + 16 halves], rows of this step
+// newK / newV [4][D], finished queries q16 [16][D].  The 32-byte pad moves
+// consecutive rows 8 banks apart, so the transposing reads of the PV step (16
+// lanes read 4 rows x 32 bytes) touch 32 distinct banks.  D = 512 needs
+// 159,744 bytes.
 template <int D>
-constexpr int fd_vpitch() { return D <= 256 ? D + 2 : D; }
+constexpr int fd_vpitch() { return D + 16; }
 
 template <int D>
 constexpr size_t fd_lds_bytes() {
@@ -170,6 +172,7 @@ __global__ void __launch_bounds__(256) k_fd_partial(AttnArgs a) {
   uint16_t* newV = newK + 4 * D;
   uint16_t* q16 = newV + 4 * D;               // [16][D] finished queries (decode step)
   __shared__ float wm[4][16], wl[4][16];
+  static_assert(fd_lds_bytes<D>() + sizeof(wm) + sizeof(wl) <= 160 * 1024, "LDS of one workgroup");
 
   const int split = blockIdx.x, kvh = blockIdx.y;
   const int seq = blockIdx.z / a.n_rows, row = blockIdx.z - seq * a.n_rows;
@@ -252,9 +255,7 @@ __global__ void __launch_bounds__(256) k_fd_partial(AttnArgs a) {
   constexpr bool HV = D <= 256;               // the tile's K and V are loaded before the
                                               // prologue, V held in registers and staged
                                               // to LDS rows of pitch VROW.  D = 512: loaded
-                                              // after it, V straight into LDS rows of
-                                              // pitch D whose 16-byte chunks are swizzled
-                                              // (chunk c of row r at c ^ ((r >> 3) & 3))
+                                              // after it, V straight into the LDS rows
   static_assert(HV || D == 512, "direct V loads assume one 1 KB row per instruction");
   uint16_t* vl = vlds + wave * 32 * VROW;
   h8_t KA[NKS], KB[NKS];
@@ -303,13 +304,12 @@ __global__ void __launch_bounds__(256) k_fd_partial(AttnArgs a) {
         VV[i] = __builtin_nontemporal_load(reinterpret_cast<const u4v*>(vb + row_at(s0, nv, r0 + STEP * i) + cc * 8));
     } else {
       // one 1 KB row per instruction: its address is scalar, plus the lane's
-      // swizzled 16-byte column
+      // 16-byte column
 #pragma unroll
       for (int r = 0; r < 32; r++) {
-        const int c = lane ^ ((r >> 3) & 3);
         const uint16_t* rowp = vb + row_at(s0, nv, r);
-        __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint32_t*>(rowp + c * 8),
-                                         reinterpret_cast<uint32_t*>(vl + r * D), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint32_t*>(rowp + lane * 8),
+                                         reinterpret_cast<uint32_t*>(vl + r * VROW), 16, 0, 0);
       }
     }
   };
@@ -401,8 +401,7 @@ __global__ void __launch_bounds__(256) k_fd_partial(AttnArgs a) {
 #pragma unroll
       for (int i = 0; i < VCH; i++) {
         const int c = lane + 64 * i, r = c / (D / 8), cc = c - r * (D / 8);
-        uint32_t* dst = reinterpret_cast<uint32_t*>(vl + r * VROW + cc * 8);
-        dst[0] = VV[i].x; dst[1] = VV[i].y; dst[2] = VV[i].z; dst[3] = VV[i].w;
+        *reinterpret_cast<u4v*>(vl + r * VROW + cc * 8) = VV[i];
       }
     } else {
       // the direct loads have landed; rows of this step overwrite theirs
@@ -412,8 +411,8 @@ __global__ void __launch_bounds__(256) k_fd_partial(AttnArgs a) {
         for (int r = 0; r < 32; r++) {
           const int p = t0 + r;
           if (p >= P0new && p < en)
-            *reinterpret_cast<u4v*>(vl + r * D + lane * 8) =
-                *reinterpret_cast<const u4v*>(newV + (p - P0new) * D + (lane ^ ((r >> 3) & 3)) * 8);
+            *reinterpret_cast<u4v*>(vl + r * VROW + lane * 8) =
+                *reinterpret_cast<const u4v*>(newV + (p - P0new) * D + lane * 8);
         }
       }
     }
@@ -460,15 +459,21 @@ __global__ void __launch_bounds__(256) k_fd_partial(AttnArgs a) {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-    // O += P V: B operand lane (dim 16d + j, group g) = V[8g .. 8g+7][dim]
+    // O += P V: B operand lane (dim 16d + j, group g) = V[8g .. 8g+7][dim].
+    // A transposing 8-byte read gives lane j of a 16-lane group element j % 4
+    // of the 4-half chunks addressed by lanes j / 4 + 4i of the group, as its
+    // element i; so lane j addresses row 8g + 4h + j / 4 at column
+    // 16d + 4 (j % 4), and reads h = 0, 1 return elements 4h .. 4h+3.
+    const uint16_t* vt = vl + (8 * g + (j >> 2)) * VROW + 4 * (j & 3);
 #pragma unroll
     for (int d = 0; d < NDS; d++) {
-      constexpr int PITCH = HV ? VROW : D;
-      const uint16_t* vc = HV ? vl + 8 * g * VROW + 16 * d + j
-                              : vl + 8 * g * D + ((2 * d + (j >> 3)) ^ g) * 8 + (j & 7);
-      h8_t Bv;
-#pragma unroll
-      for (int e = 0; e < 8; e++) Bv[e] = __builtin_bit_cast(_Float16, vc[e * PITCH]);
+      typedef short v4s_t __attribute__((ext_vector_type(4)));
+      typedef __attribute__((address_space(3))) v4s_t lds_v4s;
+      const v4s_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(vt + 16 * d));
+      const v4s_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(vt + 4 * VROW + 16 * d));
+      // joined as one vector: filling Bv element by element from lo and hi
+      // compiled to a wrong operand (the low half of each read repeated)
+      const h8_t Bv = __builtin_bit_cast(h8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       O[d] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ahi, Bv, O[d], 0, 0, 0);
       O[d] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Alo, Bv, O[d], 0, 0, 0);
     }

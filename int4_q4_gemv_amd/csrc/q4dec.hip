@@ -93,9 +93,8 @@ bool attrs_set = false;
 std::mutex g_mu;
 
 template <typename F>
-hipError_t max_lds(F* fn) {
-  return hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
-                             kMaxLds - 8 * 1024);
+hipError_t max_lds(F* fn, int bytes = kMaxLds - 8 * 1024) {
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
 }
 
 template <int B>
@@ -114,10 +113,10 @@ q4_status set_attrs() {
   std::lock_guard<std::mutex> lk(g_mu);
   if (attrs_set) return Q4_OK;
   hipError_t e = hipSuccess;
-  e = e != hipSuccess ? e : max_lds(&k_fd_partial<64>);
-  e = e != hipSuccess ? e : max_lds(&k_fd_partial<128>);
-  e = e != hipSuccess ? e : max_lds(&k_fd_partial<256>);
-  e = e != hipSuccess ? e : max_lds(&k_fd_partial<512>);
+  e = e != hipSuccess ? e : max_lds(&k_fd_partial<64>, (int)fd_lds_bytes<64>());
+  e = e != hipSuccess ? e : max_lds(&k_fd_partial<128>, (int)fd_lds_bytes<128>());
+  e = e != hipSuccess ? e : max_lds(&k_fd_partial<256>, (int)fd_lds_bytes<256>());
+  e = e != hipSuccess ? e : max_lds(&k_fd_partial<512>, (int)fd_lds_bytes<512>());
   e = e != hipSuccess ? e : gemv_attrs<1>();
   e = e != hipSuccess ? e : gemv_attrs<4>();
   if (e != hipSuccess) return Q4_EHIP;
