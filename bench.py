@@ -71,6 +71,25 @@ def time_gemv(q4, torch, model, reps=10, warm=5):
     return avg_s, launches, q4.packed_bytes(N, K)
 
 
+def time_stream_read(q4, torch, nbytes=4 << 30, reps=5):
+    """Achievable read bandwidth on this GPU: the library's plain streaming
+    read (16-byte loads, 8 in flight per thread) over a 4 GiB buffer, two
+    untimed calls, then `reps` calls between two HIP events."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    sink = None
+    for _ in range(2):
+        sink = q4.stream_read(src, sink)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        q4.stream_read(src, sink)
+    e1.record()
+    e1.synchronize()
+    t = e0.elapsed_time(e1) * 1e-3 / reps
+    del src
+    return nbytes / t / 1e9
+
+
 def time_graph_calls(torch, fn, reps, replays=5):
     """Average device time of fn(i), captured reps times into one graph and
     replayed between two HIP events on the current stream."""
@@ -293,6 +312,11 @@ def main():
                                "bytes_per_launch": nbytes, "avg_launch_us": round(avg_s * 1e6, 3),
                                "launches": launches}
             log(f"q4_gemv 3840->15360: {avg_s * 1e6:.2f} us/launch, {ach:.0f} GB/s")
+            peak_meas = time_stream_read(q4, torch)
+            out["roofline"]["achievable"] = {
+                "GBps": round(peak_meas, 1), "kernel": "q4_stream_read over 4 GiB (plain 16-byte streaming read)",
+                "frac_of_peak": round(peak_meas / PEAK_GBPS, 4), "gemv_frac_of_achievable": round(ach / peak_meas, 4)}
+            log(f"plain streaming read, 4 GiB: {peak_meas:.0f} GB/s")
             if args.mode == "gemv":
                 print(json.dumps(out))
                 return

@@ -217,6 +217,45 @@ q4_status decode_step_eager(const q4dec_model* m, const int32_t* tokens, int n, 
                             float* logits, int32_t* argmax, void* ws, size_t ws_bytes,
                             void* stream);
 
+/* ------------------------------------------------------------------------ */
+/* speculative verify: greedy acceptance                                     */
+/* ------------------------------------------------------------------------ */
+/* The host half of one speculative verify block (host only, no device work).
+ * block (host int32 [n]): the tokens fed to decode_step(n) at pos0 -- block[0]
+ * is the last emitted token, block[1..n-1] are draft tokens for positions
+ * pos0+1 .. pos0+n-1.  argmax (host int32 [n]): that step's argmax rows, row i
+ * being the target's greedy token after block[0..i].
+ * The accepted prefix is the longest a <= n-1 with block[i+1] == argmax[i]
+ * for every i < a.  emitted (host int32 [n]) receives block[1..a] followed by
+ * argmax[a], the target's own token after the prefix (a correction, or one more
+ * token when every draft is accepted); *n_emitted = a + 1.  Every emitted
+ * token is therefore one the target chose, so the emitted stream equals plain
+ * greedy decoding by the same target (gemma-4-12b-coreml-iphone-practical-chat
+ * card, speculative assets: the verifier, not the drafter, picks every token;
+ * gemma-4-12b-it-coreml-128k card, Key numbers: identical output with
+ * speculation on and off).
+ * The caller continues with block[0] = emitted[a] at position pos0 + a + 1.
+ * decode_step writes all n rows of the block; with R >= W + n - 1 the rows of
+ * rejected drafts are never admitted by a later query and are overwritten when
+ * their positions are decoded again, so one pass per block suffices
+ * (Gemma-4-12B-CoreAI card, "v5/ -- ring extent R = 2W": single-pass
+ * speculative verify).
+ * Errors: Q4_EINVAL (null pointer), Q4_ESHAPE (n outside 1..4). */
+q4_status q4_spec_accept(const int32_t* block, const int32_t* argmax, int n, int32_t* emitted,
+                         int* n_emitted);
+
+/* ------------------------------------------------------------------------ */
+/* measurement                                                               */
+/* ------------------------------------------------------------------------ */
+/* A plain streaming read, the achievable-bandwidth reference for the
+ * weight-streaming kernels: reads `bytes` (a multiple of 16) from src (device,
+ * 16-byte aligned) with 16-byte loads and writes q4_stream_read_sink_words()
+ * uint32 words to sink (device): word b is the XOR of the 32-bit words that
+ * workgroup b read, so the XOR of all sink words is the XOR of every 32-bit
+ * word of src.  Errors: Q4_EINVAL, Q4_ESHAPE, Q4_EALIGN, Q4_EHIP. */
+int q4_stream_read_sink_words(void);
+q4_status q4_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream);
+
 /* Destroys every captured decode-step graph.  Call before freeing buffers a
  * graph refers to if the same addresses may be reused for a different model. */
 q4_status q4dec_release(void);

@@ -113,12 +113,18 @@ def _declare(L):
     L.q4dec_release.restype = _i
     L.decode_step_hidden.restype = _i
     L.decode_step_hidden.argtypes = [C.POINTER(Model), _p, _sz, _i, _p, _p]
+    L.q4_spec_accept.restype = _i
+    L.q4_spec_accept.argtypes = [_p, _p, _i, _p, _p]
+    L.q4_stream_read_sink_words.restype = _i
+    L.q4_stream_read_sink_words.argtypes = []
+    L.q4_stream_read.restype = _i
+    L.q4_stream_read.argtypes = [_p, _sz, _p, _p]
 
 
 EXPORTS = ["q4dec_status_str", "q4dec_version", "q4_packed_bytes", "q4_pack", "q4_unpack",
            "q4_gemv", "flash_decode_workspace_size", "flash_decode_full", "flash_decode_ring",
            "decode_step_workspace_size", "decode_step", "decode_step_hidden", "decode_step_eager",
-           "q4dec_release"]
+           "q4_spec_accept", "q4_stream_read_sink_words", "q4_stream_read", "q4dec_release"]
 
 
 def _check(fn: str, rc: int):
@@ -303,6 +309,58 @@ DecodeModel.hidden = _hidden
 
 def release():
     _check("q4dec_release", lib().q4dec_release())
+
+
+# ------------------------------------------------------ speculative verify ----
+def spec_accept(block, argmax) -> list[int]:
+    """q4_spec_accept on host lists: the tokens a verify block emits."""
+    n = len(block)
+    if len(argmax) != n:
+        raise ValueError("block and argmax need the same length")
+    b = (C.c_int32 * n)(*[int(t) for t in block])
+    a = (C.c_int32 * n)(*[int(t) for t in argmax])
+    e = (C.c_int32 * n)()
+    ne = C.c_int(0)
+    _check("q4_spec_accept", lib().q4_spec_accept(b, a, n, e, C.byref(ne)))
+    return [int(e[i]) for i in range(ne.value)]
+
+
+def speculative_greedy(model: DecodeModel, token0: int, pos0: int, n_new: int, drafter, width: int = 4):
+    """Greedy decoding with single-pass speculative verify blocks of `width`
+    rows: each block feeds the last emitted token and width - 1 drafts
+    (drafter(pos, token, k) -> k proposed tokens for positions pos+1..pos+k)
+    to decode_step at `pos`, and q4_spec_accept picks the emitted tokens.
+    Returns (the first n_new emitted tokens, the number of blocks run)."""
+    dev = model.embed.device
+    am = torch.empty(width, dtype=torch.int32, device=dev)
+    out: list[int] = []
+    tok, pos, blocks = int(token0), int(pos0), 0
+    while len(out) < n_new:
+        drafts = [int(t) for t in drafter(pos, tok, width - 1)]
+        if len(drafts) != width - 1:
+            raise ValueError("the drafter must propose width - 1 tokens")
+        block = [tok] + drafts
+        model.step(block, pos, argmax=am, want_logits=False)
+        emitted = spec_accept(block, am.cpu().tolist())
+        out.extend(emitted)
+        pos += len(emitted)
+        tok = emitted[-1]
+        blocks += 1
+    return out[:n_new], blocks
+
+
+# ------------------------------------------------------------ measurement ----
+def stream_read(src: torch.Tensor, sink: torch.Tensor | None = None) -> torch.Tensor:
+    """q4_stream_read over a contiguous device tensor; returns the uint32
+    sink (its XOR is the XOR of every 32-bit word of src)."""
+    _need_cuda(src)
+    if not src.is_contiguous():
+        raise ValueError("stream_read needs a contiguous tensor")
+    if sink is None:
+        sink = torch.empty(int(lib().q4_stream_read_sink_words()), dtype=torch.int32, device=src.device)
+    nbytes = src.numel() * src.element_size()
+    _check("q4_stream_read", lib().q4_stream_read(_ptr(src), nbytes, _ptr(sink), _stream()))
+    return sink
 
 
 def build_decode_model(cfg, seed: int, ctx: int, device="cuda", pack_check=None, gen_device=None):

@@ -390,6 +390,35 @@ q4_status check_model(const q4dec_model* m, int n, int pos0, const int32_t* toke
   return Q4_OK;
 }
 
+// ------------------------------------------------------ streaming read ----
+// Reads n16 16-byte words with kStreamGrid x 256 threads: each wave takes 8
+// consecutive 1 KB runs per pass (8 loads in flight per lane), then strides
+// by all waves; workgroup b stores the XOR of the 32-bit words it read to
+// sink[b].
+constexpr int kStreamGrid = 4096;
+
+__global__ void __launch_bounds__(256) k_stream_read(const u4v* p, long n16, uint32_t* sink) {
+  __shared__ uint32_t wx[4];
+  const int lane = threadIdx.x & 63;
+  const long nw = (long)gridDim.x * 4;
+  uint32_t s = 0;
+  for (long w = blockIdx.x * 4L + (threadIdx.x >> 6); w * 512 < n16; w += nw) {
+    u4v c[8];
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+      const long o = (w * 8 + j) * 64 + lane;
+      c[j] = o < n16 ? __builtin_nontemporal_load(p + o) : (u4v){0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int j = 0; j < 8; j++) s ^= c[j].x ^ c[j].y ^ c[j].z ^ c[j].w;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) s ^= (uint32_t)__shfl_xor((int)s, o, 64);
+  if (lane == 0) wx[threadIdx.x >> 6] = s;
+  __syncthreads();
+  if (threadIdx.x == 0) sink[blockIdx.x] = wx[0] ^ wx[1] ^ wx[2] ^ wx[3];
+}
+
 // ----------------------------------------------------------- graph cache ----
 std::map<std::string, hipGraphExec_t> g_graphs;
 
@@ -636,6 +665,31 @@ q4_status decode_step(const q4dec_model* m, const int32_t* tokens, int n, int po
 q4_status decode_step_eager(const q4dec_model* m, const int32_t* tokens, int n, int pos0, float* logits,
                             int32_t* argmax, void* ws, size_t ws_bytes, void* stream) {
   return decode_step_impl(m, tokens, n, pos0, logits, argmax, ws, ws_bytes, stream, false);
+}
+
+q4_status q4_spec_accept(const int32_t* block, const int32_t* argmax, int n, int32_t* emitted,
+                         int* n_emitted) {
+  if (!block || !argmax || !emitted || !n_emitted) return Q4_EINVAL;
+  if (n < 1 || n > kMaxRows) return Q4_ESHAPE;
+  int a = 0;
+  while (a < n - 1 && block[a + 1] == argmax[a]) {
+    emitted[a] = block[a + 1];
+    a++;
+  }
+  emitted[a] = argmax[a];
+  *n_emitted = a + 1;
+  return Q4_OK;
+}
+
+int q4_stream_read_sink_words(void) { return kStreamGrid; }
+
+q4_status q4_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream) {
+  if (!src || !sink) return Q4_EINVAL;
+  if (bytes == 0 || bytes % 16) return Q4_ESHAPE;
+  if (!al16(src) || !al16(sink)) return Q4_EALIGN;
+  hipLaunchKernelGGL(k_stream_read, dim3(kStreamGrid), dim3(256), 0, S(stream),
+                     static_cast<const u4v*>(src), (long)(bytes / 16), sink);
+  return launch_status();
 }
 
 q4_status q4dec_release(void) {

@@ -101,3 +101,38 @@ def test_decode_step_checks():
     assert L.decode_step(C.byref(m), tok, 4, 5, f, f, f, big, None) == q4.Q4_ERANGE
     m.ring, m.window = 16, 8     # a ring holds at least one 32-position tile
     assert L.decode_step(C.byref(m), tok, 1, 5, f, f, f, big, None) == q4.Q4_ESHAPE
+
+
+def test_spec_accept_rule():
+    """The host acceptance rule of a verify block (no device work): drafts are
+    kept while they equal the target's argmax of the previous row; the
+    target's own token at the first mismatch (or after the last draft) ends
+    the emitted run."""
+    acc = q4.spec_accept
+    assert acc([5, 1, 2, 3], [1, 2, 3, 9]) == [1, 2, 3, 9]      # every draft accepted, plus one
+    assert acc([5, 1, 2, 3], [1, 7, 3, 9]) == [1, 7]            # second draft rejected
+    assert acc([5, 1, 2, 3], [4, 2, 3, 9]) == [4]               # first draft rejected
+    assert acc([5, 1, 2, 3], [1, 2, 4, 3]) == [1, 2, 4]         # a later match does not resume
+    assert acc([5], [8]) == [8]                                 # plain greedy step
+    assert acc([0, 0], [0, 0]) == [0, 0]
+    L = q4.lib()
+    b = (C.c_int32 * 4)(1, 2, 3, 4)
+    e = (C.c_int32 * 4)()
+    ne = C.c_int(-1)
+    assert L.q4_spec_accept(b, b, 0, e, C.byref(ne)) == q4.Q4_ESHAPE
+    assert L.q4_spec_accept(b, b, 5, e, C.byref(ne)) == q4.Q4_ESHAPE
+    assert L.q4_spec_accept(None, b, 4, e, C.byref(ne)) == q4.Q4_EINVAL
+    assert L.q4_spec_accept(b, b, 4, e, None) == q4.Q4_EINVAL
+    assert ne.value == -1
+
+
+def test_stream_read_checks():
+    L = q4.lib()
+    fake = C.c_void_p(0x10000)
+    odd = C.c_void_p(0x10008)
+    assert L.q4_stream_read_sink_words() >= 256
+    assert L.q4_stream_read(None, 1024, fake, None) == q4.Q4_EINVAL
+    assert L.q4_stream_read(fake, 1024, None, None) == q4.Q4_EINVAL
+    assert L.q4_stream_read(fake, 0, fake, None) == q4.Q4_ESHAPE
+    assert L.q4_stream_read(fake, 1000, fake, None) == q4.Q4_ESHAPE
+    assert L.q4_stream_read(odd, 1024, fake, None) == q4.Q4_EALIGN

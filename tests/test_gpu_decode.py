@@ -104,6 +104,48 @@ def test_verify_block_rows_equal_sequential_rows(orc, stream):
         assert_close(lb[i], rows[i][0].cpu().double().numpy(), atol=1e-3, rtol=1e-3, what=f"row {i}")
 
 
+def test_speculative_greedy_equals_plain_greedy(stream):
+    """Single-pass width-4 verify blocks (decode_step n = 4 at R = 2W) with
+    the host acceptance rule emit exactly the tokens of plain batch-1 greedy
+    decoding on the same device model; drafts are the greedy stream with an
+    error at every position divisible by 5."""
+    cfg = synth.TOY
+    print("speculative greedy toy", flush=True)
+    ga = q4.build_decode_model(cfg, 6, 200, device=DEV, gen_device="cpu")
+    gb = q4.build_decode_model(cfg, 6, 200, device=DEV, gen_device="cpu")
+    tok0 = int(synth.tokens(cfg, 1, 6)[0])
+    n_new = 40
+    stream_g, tok = [], tok0
+    for p in range(200, 200 + n_new):
+        _, am = ga.step([tok], p, want_logits=False)
+        tok = int(am.cpu()[0])
+        stream_g.append(tok)
+    truth = {201 + i: t for i, t in enumerate(stream_g)}
+
+    def drafter(pos, tok, k):
+        out = []
+        for j in range(1, k + 1):
+            t = truth.get(pos + j, 0)
+            out.append((t + 1) % cfg.vocab if (pos + j) % 5 == 0 else t)
+        return out
+
+    out, blocks = q4.speculative_greedy(gb, tok0, 200, n_new, drafter)
+    assert out == stream_g
+    assert blocks < n_new
+
+
+def test_stream_read_xor(stream):
+    print("stream read", flush=True)
+    g = torch.Generator(device="cpu").manual_seed(11)
+    for nbytes in (16, 1 << 20, (5 << 20) + 48):
+        src = torch.randint(-2**31, 2**31 - 1, (nbytes // 4,), generator=g, dtype=torch.int32)
+        sink = q4.stream_read(src.to(DEV))
+        torch.cuda.synchronize()
+        got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
+        want = np.bitwise_xor.reduce(src.numpy().view(np.uint32))
+        assert got == want, nbytes
+
+
 def sub_model(gm, layer_ids, cfg=None, scalars=None):
     """A device model over a subset of gm's layers (shared tensors)."""
     import dataclasses

@@ -235,3 +235,44 @@ def test_deep_random_stack_amplifies_last_bit_changes(orc):
         lb, _ = b.decode_step(toks, 200)
         moved[nl] = float(np.abs(a - lb).max())
     assert moved[48] > 10 * moved[2] and moved[48] > 10 * tol, moved
+
+
+def test_single_pass_speculative_verify_is_lossless(orc):
+    """Gemma-4-12B-CoreAI card, "v5/ -- ring extent R = 2W": with R >= W + n - 1
+    the host commits every row of a verify block and continues from the
+    accepted prefix, one pass per block.  On the oracle, width-4 blocks fed
+    the greedy stream with injected draft errors, accepted by the library's
+    host rule, emit exactly the plain greedy stream (toy: W 64, R 128)."""
+    import int4_q4_gemv_amd as q4
+    cfg = synth.TOY
+    assert cfg.ring >= cfg.window + 3
+    m = build_oracle_model(orc, cfg, 6, 200)
+    tok0 = int(synth.tokens(cfg, 1, 6)[0])
+    n_new = 20
+    g = clone(m)
+    stream, tok = [], tok0
+    for p in range(200, 200 + n_new):
+        _, am = g.decode_step([tok], p)
+        tok = int(am[0])
+        stream.append(tok)                       # the token at position p + 1
+    truth = {201 + i: t for i, t in enumerate(stream)}
+
+    def drafter(pos, k):                         # wrong at every position divisible by 5
+        out = []
+        for j in range(1, k + 1):
+            t = truth.get(pos + j, 0)
+            out.append((t + 1) % cfg.vocab if (pos + j) % 5 == 0 else t)
+        return out
+
+    s = clone(m)
+    out, tok, pos, sizes = [], tok0, 200, []
+    while len(out) < n_new:
+        block = [tok] + drafter(pos, 3)
+        _, am = s.decode_step(block, pos)
+        emitted = q4.spec_accept(block, [int(a) for a in am])
+        out += emitted
+        sizes.append(len(emitted))
+        pos += len(emitted)
+        tok = emitted[-1]
+    assert out[:n_new] == stream
+    assert 4 in sizes and min(sizes) < 4 and len(sizes) < n_new
