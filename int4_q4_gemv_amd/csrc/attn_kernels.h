@@ -65,13 +65,24 @@ Q4_DEV long attn_rec(const AttnArgs& a, int seq, int row, int kvh, int split, in
   return (((((long)seq * a.n_rows + row) * a.Hkv + kvh) * a.S + split) * a.GQ + col) * (long)(D + 4);
 }
 
-// LDS of k_fd_partial: V rows [4 waves][32][D + 16 halves], rows of this step
-// newK / newV [4][D], finished queries q16 [16][D].  The 32-byte pad moves
-// consecutive rows 8 banks apart, so the transposing reads of the PV step (16
-// lanes read 4 rows x 32 bytes) touch 32 distinct banks.  D = 512 needs
-// 159,744 bytes.
+// LDS of k_fd_partial: V rows [4 waves][32][pitch], rows of this step newK /
+// newV [4][D], finished queries q16 [16][D].  The V rows are written by direct
+// global-to-LDS loads of 1 KB per instruction.  Each 16-lane group of the PV
+// step's transposing reads touches 4 rows x 32 bytes, which must fall in
+// distinct banks.  D <= 256: several rows per instruction, so the rows are
+// unpadded and the 16-byte chunk c of tile row r sits at chunk c ^ 2 vswz(r)
+// (which also separates the two groups of a 32-lane half).  D = 512: one row
+// per instruction, padded by 32 bytes (rows 8 banks apart), unswizzled;
+// 159,744 bytes in all.
 template <int D>
-constexpr int fd_vpitch() { return D + 16; }
+constexpr int fd_vpitch() { return D == 512 ? D + 16 : D; }
+
+// swizzle of tile row r, in units of two 16-byte chunks (< D / 16)
+template <int D>
+Q4_DEV int vswz(int r) { return D == 512 ? 0 : ((r & 3) | (((r >> 3) & 1) << 2)) & (D / 16 - 1); }
+
+template <int D>
+constexpr size_t fd_lds_vbytes() { return (size_t)4 * 32 * fd_vpitch<D>() * 2; }
 
 template <int D>
 constexpr size_t fd_lds_bytes() {
@@ -161,8 +172,10 @@ Q4_DEV void finish_vals(float (&v)[D / 64], const float (&wv)[D / 64], bool weig
   fin_store<D>(v, dst);
 }
 
+// D <= 256 fits two waves per SIMD (<= 256 registers), so two workgroups
+// share a CU when the grid is larger than the chip (many sequences).
 template <int D>
-__global__ void __launch_bounds__(256) k_fd_partial(AttnArgs a) {
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D <= 256 ? 2 : 1))) k_fd_partial(AttnArgs a) {
   constexpr int VROW = fd_vpitch<D>();        // LDS row pitch of the V rows (halves)
   constexpr int NDS = D / 16;                 // PV dim steps
   constexpr int NKS = D / 32;                 // QK k steps
@@ -251,15 +264,12 @@ __global__ void __launch_bounds__(256) k_fd_partial(AttnArgs a) {
   // (column j, group g) ends up holding positions 8g .. 8g+7 of the tile.
   // Rows formed in this step (p >= P0new) are not in the cache yet: their
   // lanes load cache row 0 and are patched from LDS after the prologue.
-  constexpr int VCH = D / 16;                 // 16-byte V chunks per lane per tile
-  constexpr bool HV = D <= 256;               // the tile's K and V are loaded before the
-                                              // prologue, V held in registers and staged
-                                              // to LDS rows of pitch VROW.  D = 512: loaded
-                                              // after it, V straight into the LDS rows
-  static_assert(HV || D == 512, "direct V loads assume one 1 KB row per instruction");
+  constexpr bool EK = D <= 256;               // K of the first tile is loaded before the
+                                              // prologue (D = 512: its 128 registers wait
+                                              // for the prologue's); V always goes
+                                              // straight into this wave's LDS rows
   uint16_t* vl = vlds + wave * 32 * VROW;
   h8_t KA[NKS], KB[NKS];
-  u4v VV[HV ? VCH : 1];
   // Cache rows of a tile.  Rows [0, nv) of the tile at t0 come from the cache
   // (the rest are masked out or formed in this step: they read row 0).  On a
   // ring layer, tile row r lives at slot (t0 + r) mod R; rings hold at least
@@ -292,25 +302,21 @@ __global__ void __launch_bounds__(256) k_fd_partial(AttnArgs a) {
       KB[s] = __builtin_bit_cast(h8_t, __builtin_nontemporal_load(reinterpret_cast<const u4v*>(kc + 32 * s)));
     }
   };
+  // V: each instruction fills 1 KB of LDS, RPI = 512 / D consecutive tile
+  // rows; lane l writes chunk position l mod (D / 8) of row l / (D / 8) and
+  // so loads the global chunk that the swizzle puts there (D = 512: one row
+  // per instruction, its address scalar)
   auto load_v = [&](int t0) {
     int s0, nv;
     tile_geom(t0, s0, nv);
-    if constexpr (HV) {
-      // chunk i of lane l: tile row (l + 64 i) / (D / 8), 16-byte column (l mod D / 8)
-      constexpr int STEP = 512 / D;
-      const int r0 = lane / (D / 8), cc = lane % (D / 8);
+    constexpr int CPR = D / 8, RPI = 64 / CPR;
+    const int rl = lane / CPR, pc = lane % CPR;
 #pragma unroll
-      for (int i = 0; i < VCH; i++)
-        VV[i] = __builtin_nontemporal_load(reinterpret_cast<const u4v*>(vb + row_at(s0, nv, r0 + STEP * i) + cc * 8));
-    } else {
-      // one 1 KB row per instruction: its address is scalar, plus the lane's
-      // 16-byte column
-#pragma unroll
-      for (int r = 0; r < 32; r++) {
-        const uint16_t* rowp = vb + row_at(s0, nv, r);
-        __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint32_t*>(rowp + lane * 8),
-                                         reinterpret_cast<uint32_t*>(vl + r * VROW), 16, 0, 0);
-      }
+    for (int i = 0; i < 32 / RPI; i++) {
+      const int r = RPI * i + rl;
+      const int c = pc ^ (2 * vswz<D>(r));
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint32_t*>(vb + row_at(s0, nv, r) + c * 8),
+                                       reinterpret_cast<uint32_t*>(vl + RPI * i * VROW), 16, 0, 0);
     }
   };
   // the first tile: V, and for D <= 256 also K, before the prologue (with the
@@ -318,7 +324,7 @@ __global__ void __launch_bounds__(256) k_fd_partial(AttnArgs a) {
   // flight); K of D = 512 (128 registers) waits for the prologue's registers
   int t0 = st + 32 * wave;
   if (t0 < en) {
-    if (HV) load_k(t0);
+    if (EK) load_k(t0);
     load_v(t0);
   }
 
@@ -378,7 +384,7 @@ __global__ void __launch_bounds__(256) k_fd_partial(AttnArgs a) {
   for (int d = 0; d < NDS; d++) O[d] = (f4_t){0.f, 0.f, 0.f, 0.f};
 
   for (bool first = true; t0 < en; t0 += 128, first = false) {
-    if (!first || !HV) load_k(t0);
+    if (!first || !EK) load_k(t0);
     if (!first) load_v(t0);
     if (t0 + 31 >= P0new) {                   // patch the rows formed in this step
       const int pa = t0 + 8 * (j >> 2) + (j & 3), pb = pa + 4;
@@ -386,34 +392,6 @@ __global__ void __launch_bounds__(256) k_fd_partial(AttnArgs a) {
       for (int s = 0; s < NKS; s++) {
         if (pa >= P0new && pa < en) KA[s] = *reinterpret_cast<const h8_t*>(newK + (pa - P0new) * D + 32 * s + 8 * g);
         if (pb >= P0new && pb < en) KB[s] = *reinterpret_cast<const h8_t*>(newK + (pb - P0new) * D + 32 * s + 8 * g);
-      }
-      if constexpr (HV) {
-#pragma unroll
-        for (int i = 0; i < VCH; i++) {
-          const int c = lane + 64 * i, r = c / (D / 8), cc = c - r * (D / 8);
-          const int p = t0 + r;
-          if (p >= P0new && p < en) VV[i] = *reinterpret_cast<const u4v*>(newV + (p - P0new) * D + cc * 8);
-        }
-      }
-    }
-    // stage the V tile (32 positions) into this wave's LDS rows
-    if constexpr (HV) {
-#pragma unroll
-      for (int i = 0; i < VCH; i++) {
-        const int c = lane + 64 * i, r = c / (D / 8), cc = c - r * (D / 8);
-        *reinterpret_cast<u4v*>(vl + r * VROW + cc * 8) = VV[i];
-      }
-    } else {
-      // the direct loads have landed; rows of this step overwrite theirs
-      __builtin_amdgcn_s_waitcnt(0);
-      __asm__ __volatile__("" ::: "memory");
-      if (t0 + 31 >= P0new) {
-        for (int r = 0; r < 32; r++) {
-          const int p = t0 + r;
-          if (p >= P0new && p < en)
-            *reinterpret_cast<u4v*>(vl + r * VROW + lane * 8) =
-                *reinterpret_cast<const u4v*>(newV + (p - P0new) * D + lane * 8);
-        }
       }
     }
     f4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
@@ -456,6 +434,19 @@ __global__ void __launch_bounds__(256) k_fd_partial(AttnArgs a) {
       Ahi[i] = hi;
       Alo[i] = (_Float16)(p[i] - (float)hi);
     }
+    // the tile's direct V loads have landed (waiting for them here, not
+    // before QK, lets the scores go ahead as soon as K is in); rows formed in
+    // this step overwrite theirs
+    __builtin_amdgcn_s_waitcnt(0);
+    __asm__ __volatile__("" ::: "memory");
+    if (t0 + 31 >= P0new) {
+      for (int r = 0; r < 32; r++) {
+        const int pr = t0 + r;
+        if (pr >= P0new && pr < en && lane < D / 8)
+          *reinterpret_cast<u4v*>(vl + r * VROW + (lane ^ (2 * vswz<D>(r))) * 8) =
+              *reinterpret_cast<const u4v*>(newV + (pr - P0new) * D + lane * 8);
+      }
+    }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
@@ -463,14 +454,18 @@ __global__ void __launch_bounds__(256) k_fd_partial(AttnArgs a) {
     // A transposing 8-byte read gives lane j of a 16-lane group element j % 4
     // of the 4-half chunks addressed by lanes j / 4 + 4i of the group, as its
     // element i; so lane j addresses row 8g + 4h + j / 4 at column
-    // 16d + 4 (j % 4), and reads h = 0, 1 return elements 4h .. 4h+3.
+    // 16d + 4 (j % 4) (16-byte chunk 2d + (j % 4) / 2, stored at chunk
+    // position 2 (d ^ vswz) + (j % 4) / 2 of the row), and reads h = 0, 1
+    // return elements 4h .. 4h+3.  Both rows share the swizzle.
+    const int sw = vswz<D>(8 * g + (j >> 2));
     const uint16_t* vt = vl + (8 * g + (j >> 2)) * VROW + 4 * (j & 3);
 #pragma unroll
     for (int d = 0; d < NDS; d++) {
       typedef short v4s_t __attribute__((ext_vector_type(4)));
       typedef __attribute__((address_space(3))) v4s_t lds_v4s;
-      const v4s_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(vt + 16 * d));
-      const v4s_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(vt + 4 * VROW + 16 * d));
+      const int cd = 16 * (d ^ sw);
+      const v4s_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(vt + cd));
+      const v4s_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(vt + 4 * VROW + cd));
       // joined as one vector: filling Bv element by element from lo and hi
       // compiled to a wrong operand (the low half of each read repeated)
       const h8_t Bv = __builtin_bit_cast(h8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));

@@ -128,7 +128,9 @@ template <int D>
 void launch_fd_d(const AttnArgs& a, int n_seq, float* out32, uint16_t* out16, hipStream_t st) {
   const dim3 grid(a.S, a.Hkv, n_seq * a.n_rows);
   const dim3 cgrid(n_seq * a.n_rows * a.Hq, D / 64);  // 256 threads each
-  hipLaunchKernelGGL(k_fd_partial<D>, grid, dim3(256), fd_lds_bytes<D>(), st, a);
+  // without the finishing prologue only the V rows (which also hold the
+  // merge buffer) are used: a smaller allocation lets more workgroups share a CU
+  hipLaunchKernelGGL(k_fd_partial<D>, grid, dim3(256), a.fin_on ? fd_lds_bytes<D>() : fd_lds_vbytes<D>(), st, a);
   if (a.S <= 16) hipLaunchKernelGGL((k_fd_combine<D, 16>), cgrid, dim3(256), 0, st, a, out32, out16);
   else if (a.S <= 32) hipLaunchKernelGGL((k_fd_combine<D, 32>), cgrid, dim3(256), 0, st, a, out32, out16);
   else hipLaunchKernelGGL((k_fd_combine<D, kMaxSplits>), cgrid, dim3(256), 0, st, a, out32, out16);
