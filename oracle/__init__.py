@@ -65,6 +65,9 @@ def _declare(L):
     L.orc_q4_dequant.argtypes = [_p, _i64, _i64, _p]
     L.orc_q4_gemv.argtypes = [_p, _i64, _i64, _p, _i, _p]
     L.orc_f16_gemv.argtypes = [_p, _i64, _i64, _p, _i, _p]
+    L.orc_q8_pack.argtypes = [_p, _i64, _i64, _p]
+    L.orc_q8_dequant.argtypes = [_p, _i64, _i64, _p]
+    L.orc_q8_gemv.argtypes = [_p, _i64, _i64, _p, _i, _p]
     L.orc_ring_admit.argtypes = [_i64, _i64, _i64, _p]
     L.orc_attend.argtypes = [_p, _i, _i, _i, _p, _p, _i64, _p, _i64, _d, _p]
     L.orc_flash_full.argtypes = [_p, _p, _p, _i64, _i, _i, _i64, _i, _d, _p]
@@ -136,6 +139,35 @@ def q4_gemv(blocks: np.ndarray, N: int, K: int, x16: np.ndarray) -> np.ndarray:
     assert x16.shape[1] == K
     y = np.empty((B, N), dtype=np.float64)
     lib().orc_q4_gemv(_ptr(blocks), N, K, _ptr(x16), B, _ptr(y))
+    return y
+
+
+# ------------------------------------------------------------ q8 int8lin ----
+def q8_pack(w: np.ndarray) -> np.ndarray:
+    """fp32 [N, K] -> canonical q8 blocks uint8 [N, K/32, 34]."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    N, K = w.shape
+    assert K % 32 == 0
+    out = np.empty((N, K // 32, 34), dtype=np.uint8)
+    lib().orc_q8_pack(_ptr(w), N, K, _ptr(out))
+    return out
+
+
+def q8_dequant(blocks: np.ndarray, N: int, K: int) -> np.ndarray:
+    blocks = np.ascontiguousarray(blocks, dtype=np.uint8)
+    out = np.empty((N, K), dtype=np.float64)
+    lib().orc_q8_dequant(_ptr(blocks), N, K, _ptr(out))
+    return out
+
+
+def q8_gemv(blocks: np.ndarray, N: int, K: int, x16: np.ndarray) -> np.ndarray:
+    """x16: uint16 fp16 bits [B, K] -> y float64 [B, N]."""
+    blocks = np.ascontiguousarray(blocks, dtype=np.uint8)
+    x16 = np.ascontiguousarray(np.atleast_2d(x16), dtype=np.uint16)
+    B = x16.shape[0]
+    assert x16.shape[1] == K
+    y = np.empty((B, N), dtype=np.float64)
+    lib().orc_q8_gemv(_ptr(blocks), N, K, _ptr(x16), B, _ptr(y))
     return y
 
 

@@ -156,6 +156,82 @@ void orc_q4_gemv(const uint8_t* blocks, int64_t N, int64_t K,
   free(xd);
 }
 
+/* ------------------------------------------------------------------------ */
+/* q8 ("int8lin") packing and the int8 matrix-vector product                 */
+/* ------------------------------------------------------------------------ */
+/* [zoo] intro and Throughput table: the int8lin ship is the verified-clean
+ * variant beside the faster int4linsym.  Reading (the pages give no block
+ * size for it): the int4 rule with the int8 grid, per block of 32 weights
+ * d = fp16(absmax/127) and q = clamp(round_half_away(w / d), -127, 127) with
+ * w / d an IEEE fp32 quotient against the stored fp16 scale; a zero or
+ * underflowing scale gives zero codes; a block holding a non-finite weight,
+ * or whose scale overflows fp16, is stored as a zero block. */
+void orc_q8_pack(const float* w, int64_t N, int64_t K, uint8_t* blocks) {
+  const int64_t nb = K / 32;
+#pragma omp parallel for schedule(static)
+  for (int64_t n = 0; n < N; n++) {
+    for (int64_t b = 0; b < nb; b++) {
+      const float* src = w + n * K + b * 32;
+      uint8_t* blk = blocks + (n * nb + b) * 34;
+      float amax = 0.0f;
+      int finite = 1;
+      for (int i = 0; i < 32; i++) {
+        if (!isfinite(src[i])) finite = 0;
+        float a = fabsf(src[i]);
+        if (a > amax) amax = a;
+      }
+      uint16_t d16 = finite ? orc_f32_to_f16(amax / 127.0f) : 0;
+      float d = (float)orc_f16_to_f64(d16);
+      if (!isfinite(d)) { d16 = 0; d = 0.0f; }
+      blk[0] = (uint8_t)(d16 & 0xFF);
+      blk[1] = (uint8_t)(d16 >> 8);
+      for (int i = 0; i < 32; i++) {
+        int qi = 0;
+        if (d != 0.0f) {
+          float rr = roundf(src[i] / d);      /* fp32 quotient, half away from zero */
+          qi = (rr > 127.0f) ? 127 : (rr < -127.0f ? -127 : (int)rr);
+        }
+        blk[2 + i] = (uint8_t)(int8_t)qi;
+      }
+    }
+  }
+}
+
+static inline double q8_scale(const uint8_t* blk) {
+  return orc_f16_to_f64((uint16_t)(blk[0] | (blk[1] << 8)));
+}
+
+void orc_q8_dequant(const uint8_t* blocks, int64_t N, int64_t K, double* w_hat) {
+  const int64_t nb = K / 32;
+  for (int64_t n = 0; n < N; n++)
+    for (int64_t b = 0; b < nb; b++) {
+      const uint8_t* blk = blocks + (n * nb + b) * 34;
+      double d = q8_scale(blk);
+      for (int i = 0; i < 32; i++) w_hat[n * K + b * 32 + i] = d * (double)(int8_t)blk[2 + i];
+    }
+}
+
+void orc_q8_gemv(const uint8_t* blocks, int64_t N, int64_t K,
+                 const uint16_t* x, int B, double* y) {
+  const int64_t nb = K / 32;
+  double* xd = (double*)malloc(sizeof(double) * (size_t)(B * K));
+  for (int64_t i = 0; i < (int64_t)B * K; i++) xd[i] = orc_f16_to_f64(x[i]);
+#pragma omp parallel for schedule(static)
+  for (int64_t n = 0; n < N; n++) {
+    for (int b = 0; b < B; b++) {
+      const double* xb = xd + (int64_t)b * K;
+      double acc = 0.0;
+      for (int64_t blkI = 0; blkI < nb; blkI++) {
+        const uint8_t* blk = blocks + (n * nb + blkI) * 34;
+        double d = q8_scale(blk);
+        for (int i = 0; i < 32; i++) acc += d * (double)(int8_t)blk[2 + i] * xb[blkI * 32 + i];
+      }
+      y[(int64_t)b * N + n] = acc;
+    }
+  }
+  free(xd);
+}
+
 void orc_f16_gemv(const uint16_t* W, int64_t N, int64_t K,
                   const uint16_t* x, int B, double* y) {
   double* xd = (double*)malloc(sizeof(double) * (size_t)(B * K));

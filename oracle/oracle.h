@@ -45,6 +45,15 @@ void orc_q4_dequant(const uint8_t* blocks, int64_t N, int64_t K, double* w_hat);
 /* y[b][n] = sum_k w_hat[n][k] * x[b][k], x given as fp16 bits [B][K] */
 void orc_q4_gemv(const uint8_t* blocks, int64_t N, int64_t K,
                  const uint16_t* x, int B, double* y);
+/* ---- q8 "int8lin" weights (gemma4-12b card: the int8lin ship beside int4linsym;
+ *      reading: per-block-32 absmax symmetric int8, grid [-127, 127]) ----
+ * Canonical block = 34 bytes: bytes 0..1 fp16 scale d = fp16(absmax/127)
+ * (little endian), bytes 2..33 the codes q as int8 (two's complement), element
+ * i in byte 2+i.  Blocks are row-major [N][K/32]. */
+void orc_q8_pack(const float* w, int64_t N, int64_t K, uint8_t* blocks);
+void orc_q8_dequant(const uint8_t* blocks, int64_t N, int64_t K, double* w_hat);
+void orc_q8_gemv(const uint8_t* blocks, int64_t N, int64_t K,
+                 const uint16_t* x, int B, double* y);
 /* same for an fp16 matrix W [N][K] (the tied vocab table) */
 void orc_f16_gemv(const uint16_t* W, int64_t N, int64_t K,
                   const uint16_t* x, int B, double* y);
