@@ -146,6 +146,25 @@ def time_attention(q4, torch):
     return res
 
 
+def time_q8_gemv(q4, torch, N=15360, K=3840, copies=16, launches=96, reps=10, warm=5):
+    """The int8 (int8lin) product at the gate/up shape, batch 1: one random
+    N(0, 0.02) matrix packed into `copies` separate buffers (1 GB, above the
+    last-level cache), launches rotating over them captured into a graph and
+    replayed between two HIP events.  Bytes per launch: 1.0625 B per weight."""
+    gen = torch.Generator(device="cuda").manual_seed(21)
+    w = torch.randn(N, K, device="cuda", generator=gen) * 0.02
+    mats = [q4.q8_pack(w) for _ in range(copies)]
+    del w
+    x = torch.randn(1, K, device="cuda", generator=gen).half()
+    y = torch.empty(1, N, device="cuda")
+    avg = time_graph_calls(torch, lambda i: q4.q8_gemv(mats[i % copies], N, K, x, y), launches,
+                           replays=reps)
+    nb = q4.q8_packed_bytes(N, K)
+    del mats
+    return {"us": round(avg * 1e6, 3), "bytes": nb, "GBps": round(nb / avg / 1e9, 1),
+            "frac": round(nb / avg / 1e9 / PEAK_GBPS, 4), "shape": f"{N}x{K}, batch 1"}
+
+
 COPY_BYTES = 512 << 20
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "q4_gemv_15360x3840_traffic.txt")
 GEMV_SOURCES = ("int4_q4_gemv_amd/csrc/gemv_kernels.h", "int4_q4_gemv_amd/csrc/device_common.h",
@@ -341,6 +360,8 @@ def main():
             log(f"ctx 131072: {extra['ctx131072']}; verify4: {extra['verify4_ctx32768']}")
             extra["attention_kernels"] = time_attention(q4, torch)
             log(f"attention kernels: {extra['attention_kernels']}")
+            extra["q8_gemv"] = time_q8_gemv(q4, torch)
+            log(f"q8 (int8lin) gemv: {extra['q8_gemv']}")
     res = {
         "metric": "decode tokens/s (batch 1, 48 layers) + achieved HBM GB/s as % of peak",
         "value": round(tok_s, 2), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,

@@ -102,6 +102,46 @@ q4_status q4_gemv(const void* packed, int N, int K, const uint16_t* x, int B,
                   float* y, void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* int8 ("int8lin") weights                                                  */
+/* ------------------------------------------------------------------------ */
+/* The verified-clean weight variant (gemma4-12b card, intro and Throughput
+ * table: the int8lin ship beside int4linsym).  The pages give no block format
+ * for it; the reading is the q4_0 rule on the int8 grid: for each row and
+ * block of 32 weights, d = fp16_rne(absmax / 127) and
+ * q = clamp(round_half_away(w / d), -127, 127), w / d an IEEE fp32 quotient
+ * against the stored fp16 scale (d == 0 gives q = 0); 1.0625 B per weight.
+ *
+ * Bytes of the packed form of an [N, K] matrix:
+ * ceil(N/16) * ceil(K/64) * 1088 (= N*K/32*34 when N is a multiple of 16 and K
+ * of 64).  Returns 0 when K is not a positive multiple of 32 or N < 1. */
+size_t q8_packed_bytes(int N, int K);
+
+/* Quantises W (device, row-major [N, K], fp32 or bf16) onto the int8 grid.
+ * `packed` (device, packed_bytes >= q8_packed_bytes(N, K)) receives the
+ * device layout: "pairs" of 16 rows x 2 blocks (64 columns), one 1 KB
+ * wave-wide load each; codes [N/16][K/64][64 lanes][16 B] (lane l: row l % 16,
+ * columns 16 (l / 16) .. +15 of the pair, byte j = q + 128 of column j of
+ * those 16) followed by scales [N/16][K/64][2 blocks][16 rows] fp16; padding
+ * rows and blocks have zero scale.  `nonfinite` as for q4_pack.
+ * Errors: Q4_EINVAL, Q4_ESHAPE (N < 1, K % 32), Q4_ENOSPACE, Q4_EALIGN, Q4_EHIP. */
+q4_status q8_pack(const void* w, int w_dtype, int N, int K, void* packed,
+                  size_t packed_bytes, int32_t* nonfinite, void* stream);
+
+/* Exports the packed matrix as canonical 34-byte blocks (device `blocks`,
+ * row-major [N][K/32]): the fp16 scale (little endian) followed by the 32
+ * codes as int8, element i in byte 2 + i. */
+q4_status q8_unpack(const void* packed, int N, int K, uint8_t* blocks, void* stream);
+
+/* y[b][n] = sum_k (d * q)[n][k] * x[b][k] for b < B, fp32 accumulation.
+ * packed: device, from q8_pack(N, K).  x: device fp16 [B][K].  y: device fp32
+ * [B][N].  B in 1..4 (B > 1 runs on MFMA).  K <= 16384.  No workspace;
+ * each 16-row tile is finished by one workgroup, so results are deterministic.
+ * Errors: Q4_EINVAL, Q4_ESHAPE (K % 32, K too large, B outside 1..4),
+ * Q4_EALIGN, Q4_EHIP. */
+q4_status q8_gemv(const void* packed, int N, int K, const uint16_t* x, int B,
+                  float* y, void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* flash-decode attention                                                    */
 /* ------------------------------------------------------------------------ */
 /* Workspace bytes for flash_decode_full / flash_decode_ring. */

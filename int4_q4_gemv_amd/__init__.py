@@ -99,6 +99,14 @@ def _declare(L):
     L.q4_unpack.argtypes = [_p, _i, _i, _p, _p]
     L.q4_gemv.restype = _i
     L.q4_gemv.argtypes = [_p, _i, _i, _p, _i, _p, _p]
+    L.q8_packed_bytes.restype = _sz
+    L.q8_packed_bytes.argtypes = [_i, _i]
+    L.q8_pack.restype = _i
+    L.q8_pack.argtypes = [_p, _i, _i, _i, _p, _sz, _p, _p]
+    L.q8_unpack.restype = _i
+    L.q8_unpack.argtypes = [_p, _i, _i, _p, _p]
+    L.q8_gemv.restype = _i
+    L.q8_gemv.argtypes = [_p, _i, _i, _p, _i, _p, _p]
     L.flash_decode_workspace_size.restype = _sz
     L.flash_decode_workspace_size.argtypes = [_i, _i, _i, _i]
     L.flash_decode_full.restype = _i
@@ -122,7 +130,7 @@ def _declare(L):
 
 
 EXPORTS = ["q4dec_status_str", "q4dec_version", "q4_packed_bytes", "q4_pack", "q4_unpack",
-           "q4_gemv", "flash_decode_workspace_size", "flash_decode_full", "flash_decode_ring",
+           "q4_gemv", "q8_packed_bytes", "q8_pack", "q8_unpack", "q8_gemv", "flash_decode_workspace_size", "flash_decode_full", "flash_decode_ring",
            "decode_step_workspace_size", "decode_step", "decode_step_hidden", "decode_step_eager",
            "q4_spec_accept", "q4_stream_read_sink_words", "q4_stream_read", "q4dec_release"]
 
@@ -194,6 +202,45 @@ def q4_gemv(packed, N: int, K: int, x: torch.Tensor) -> torch.Tensor:
     """y[b, n] = sum_k W[n, k] x[b, k] for fp16 x [B, K]; fp32 y [B, N]."""
     x2 = x.reshape(-1, K)
     return Gemv(N, K, x2.shape[0], device=x.device)(packed, x2)
+
+
+# ----------------------------------------------------------- q8 int8lin ----
+def q8_packed_bytes(N: int, K: int) -> int:
+    return int(lib().q8_packed_bytes(N, K))
+
+
+def q8_pack(w: torch.Tensor, nonfinite: torch.Tensor | None = None) -> torch.Tensor:
+    """Quantise fp32/bf16 [N, K] (device) to the packed int8 layout (uint8)."""
+    _need_cuda(w)
+    w = w.contiguous()
+    N, K = w.shape
+    dt = {torch.float32: Q4_F32, torch.bfloat16: Q4_BF16}.get(w.dtype)
+    if dt is None:
+        raise ValueError("q8_pack takes fp32 or bf16 weights")
+    nbytes = q8_packed_bytes(N, K)
+    if nbytes == 0:
+        raise Q4Error("q8_pack", Q4_ESHAPE)
+    out = torch.empty(nbytes, dtype=torch.uint8, device=w.device)
+    _check("q8_pack", lib().q8_pack(_ptr(w), dt, N, K, _ptr(out), nbytes, _ptr(nonfinite), _stream()))
+    return out
+
+
+def q8_unpack(packed: torch.Tensor, N: int, K: int) -> torch.Tensor:
+    """Canonical int8 blocks [N, K/32, 34] (uint8) of a packed matrix."""
+    out = torch.empty((N, K // 32, 34), dtype=torch.uint8, device=packed.device)
+    _check("q8_unpack", lib().q8_unpack(_ptr(packed), N, K, _ptr(out), _stream()))
+    return out
+
+
+def q8_gemv(packed, N: int, K: int, x: torch.Tensor, y: torch.Tensor | None = None) -> torch.Tensor:
+    """y[b, n] = sum_k W[n, k] x[b, k] for int8 weights and fp16 x [B, K]; fp32 y [B, N]."""
+    _need_cuda(packed, x)
+    x2 = x.reshape(-1, K).contiguous()
+    B = x2.shape[0]
+    if y is None:
+        y = torch.empty((B, N), dtype=torch.float32, device=x.device)
+    _check("q8_gemv", lib().q8_gemv(_ptr(packed), N, K, _ptr(x2), B, _ptr(y), _stream()))
+    return y
 
 
 # ------------------------------------------------------------- attention ----

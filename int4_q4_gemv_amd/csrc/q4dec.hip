@@ -15,6 +15,7 @@
 #include "attn_kernels.h"
 #include "gemv_kernels.h"
 #include "pack_kernels.h"
+#include "q8_kernels.h"
 #include "step_kernels.h"
 
 using namespace q4k;
@@ -65,6 +66,33 @@ GemvPlan gemv_plan(int N, int K, int max_waves, int split_quads = 0) {
 }
 
 size_t gemv_lds(int B, const GemvPlan& p) { return (size_t)B * p.NQs * 128 * 2; }
+
+// q8 product: T 16-row tiles of NP 64-column pairs, W waves of CQ pairs each;
+// CQ is the smallest of 4, 8, 16 that keeps W within 8 (so the grid of a 12B
+// shape is resident at once: 15360 x 3840 in 12.0 us against 12.4-12.8 us with
+// 15 waves of 4 pairs), else within 16; W = -1 when none does.
+struct Q8Plan {
+  int T = 0, NP = 0, CQ = 0, W = -1;
+};
+
+Q8Plan q8_plan(int N, int K) {
+  Q8Plan p;
+  p.T = (int)ceil_div(N, 16);
+  p.NP = (int)ceil_div(K, 64);
+  for (int lim : {8, 16}) {
+    for (int cq : {4, 8, 16}) {
+      const int w = (int)ceil_div(p.NP, cq);
+      if (w <= lim) {
+        p.CQ = cq;
+        p.W = w;
+        return p;
+      }
+    }
+  }
+  return p;
+}
+
+size_t q8_lds(int B, const Q8Plan& p) { return (size_t)B * p.NP * 64 * 2; }
 
 // grid: (tiles, splits); waves: per workgroup (both halves for EPI_GATEUP)
 template <int B, int EPI>
@@ -119,6 +147,12 @@ q4_status set_attrs() {
   e = e != hipSuccess ? e : max_lds(&k_fd_partial<512>, (int)fd_lds_bytes<512>());
   e = e != hipSuccess ? e : gemv_attrs<1>();
   e = e != hipSuccess ? e : gemv_attrs<4>();
+  e = e != hipSuccess ? e : max_lds(&k_q8_gemv<1, 4>);
+  e = e != hipSuccess ? e : max_lds(&k_q8_gemv<1, 8>);
+  e = e != hipSuccess ? e : max_lds(&k_q8_gemv<1, 16>);
+  e = e != hipSuccess ? e : max_lds(&k_q8_gemv<4, 4>);
+  e = e != hipSuccess ? e : max_lds(&k_q8_gemv<4, 8>);
+  e = e != hipSuccess ? e : max_lds(&k_q8_gemv<4, 16>);
   if (e != hipSuccess) return Q4_EHIP;
   attrs_set = true;
   return Q4_OK;
@@ -570,6 +604,73 @@ q4_status q4_gemv(const void* packed, int N, int K, const uint16_t* x, int B, fl
   a.x = x; a.ldx = K; a.y = y; a.ldy = N; a.n_rows = B;
   if (B == 1) launch_gemv<1, EPI_STORE>(a, p, p.T, p.W, gemv_lds(1, p), S(stream));
   else launch_gemv<4, EPI_STORE>(a, p, p.T, p.W, gemv_lds(4, p), S(stream));
+  return launch_status();
+}
+
+size_t q8_packed_bytes(int N, int K) {
+  if (N < 1 || K < 32 || K % 32) return 0;
+  return (size_t)ceil_div(N, 16) * ceil_div(K, 64) * (64 * 16 + 32 * 2);
+}
+
+q4_status q8_pack(const void* w, int w_dtype, int N, int K, void* packed, size_t packed_bytes,
+                  int32_t* nonfinite, void* stream) {
+  if (!w || !packed) return Q4_EINVAL;
+  if (w_dtype != Q4_F32 && w_dtype != Q4_BF16) return Q4_EINVAL;
+  if (N < 1 || K < 32 || K % 32) return Q4_ESHAPE;
+  if (packed_bytes < q8_packed_bytes(N, K)) return Q4_ENOSPACE;
+  if (!al16(w) || !al16(packed)) return Q4_EALIGN;
+  const int T = (int)ceil_div(N, 16);
+  const long pairs = (long)T * ceil_div(K, 64);
+  u4v* codes = static_cast<u4v*>(packed);
+  uint16_t* scales = reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(packed) + (size_t)pairs * 64 * 16);
+  const dim3 grid((unsigned)ceil_div(pairs * 32, 256));
+  if (w_dtype == Q4_F32)
+    hipLaunchKernelGGL(k_q8_pack<0>, grid, dim3(256), 0, S(stream), w, N, K, codes, scales, T, nonfinite);
+  else
+    hipLaunchKernelGGL(k_q8_pack<1>, grid, dim3(256), 0, S(stream), w, N, K, codes, scales, T, nonfinite);
+  return launch_status();
+}
+
+q4_status q8_unpack(const void* packed, int N, int K, uint8_t* blocks, void* stream) {
+  if (!packed || !blocks) return Q4_EINVAL;
+  if (N < 1 || K < 32 || K % 32) return Q4_ESHAPE;
+  if (!al16(packed)) return Q4_EALIGN;
+  const long pairs = (long)ceil_div(N, 16) * ceil_div(K, 64);
+  const u4v* codes = static_cast<const u4v*>(packed);
+  const uint16_t* scales = reinterpret_cast<const uint16_t*>(static_cast<const uint8_t*>(packed) + (size_t)pairs * 64 * 16);
+  const long total = (long)N * (K / 32);
+  hipLaunchKernelGGL(k_q8_unpack, dim3((unsigned)ceil_div(total, 256)), dim3(256), 0, S(stream), codes,
+                     scales, N, K, blocks);
+  return launch_status();
+}
+
+q4_status q8_gemv(const void* packed, int N, int K, const uint16_t* x, int B, float* y, void* stream) {
+  if (!packed || !x || !y) return Q4_EINVAL;
+  if (N < 1 || K < 32 || K % 32 || B < 1 || B > kMaxRows) return Q4_ESHAPE;
+  const Q8Plan p = q8_plan(N, K);
+  const int Bk = B == 1 ? 1 : 4;
+  if (p.W < 1 || q8_lds(Bk, p) > (size_t)kMaxLds - 8 * 1024) return Q4_ESHAPE;
+  if (!al16(packed) || !al16(x) || !al16(y)) return Q4_EALIGN;
+  q4_status rc = set_attrs();
+  if (rc != Q4_OK) return rc;
+  Q8Args a{};
+  a.codes = static_cast<const u4v*>(packed);
+  a.scales = reinterpret_cast<const uint16_t*>(static_cast<const uint8_t*>(packed) +
+                                               (size_t)p.T * p.NP * 64 * 16);
+  a.N = N; a.K = K; a.NP = p.NP; a.W = p.W;
+  a.x = x; a.ldx = K; a.y = y; a.ldy = N; a.n_rows = B;
+  const dim3 g(p.T), blk(64 * p.W);
+  const size_t lds = q8_lds(Bk, p);
+  hipStream_t st = S(stream);
+  if (B == 1) {
+    if (p.CQ == 16) hipLaunchKernelGGL((k_q8_gemv<1, 16>), g, blk, lds, st, a);
+    else if (p.CQ == 8) hipLaunchKernelGGL((k_q8_gemv<1, 8>), g, blk, lds, st, a);
+    else hipLaunchKernelGGL((k_q8_gemv<1, 4>), g, blk, lds, st, a);
+  } else {
+    if (p.CQ == 16) hipLaunchKernelGGL((k_q8_gemv<4, 16>), g, blk, lds, st, a);
+    else if (p.CQ == 8) hipLaunchKernelGGL((k_q8_gemv<4, 8>), g, blk, lds, st, a);
+    else hipLaunchKernelGGL((k_q8_gemv<4, 4>), g, blk, lds, st, a);
+  }
   return launch_status();
 }
 
