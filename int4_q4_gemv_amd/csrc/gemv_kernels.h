@@ -76,6 +76,14 @@ struct GemvArgs {
   uint16_t* a_out;        // EPI_GATEUP: fp16 [rows][inter] = GELU(gate) * up
   int inter;
   int n_rows;             // rows of x (<= B)
+  // Read-ahead for the one-workgroup launch that follows (the RMSNorm rows):
+  // two fp32 arrays of ra_n float4 (its norm weights) are read by workgroups
+  // 0, 8, 16, .. so that they sit in the L2 of the XCD that runs workgroup 0
+  // of every launch (workgroups go round-robin over the 8 XCDs, and L2
+  // contents outlive a launch).  Performance only; NULL: none.
+  const float4* ra0;
+  const float4* ra1;
+  int ra_n;
 };
 
 Q4_DEV float gelu_tanh(float g) {
@@ -182,6 +190,15 @@ __global__ void __launch_bounds__(B == 1 ? 1024 : 512) k_q4_gemv(GemvArgs a) {
       __builtin_amdgcn_sched_barrier(0);   // keep the issue order
     }
   }
+  // read-ahead, issued after this wave's own loads: one 64-byte line per lane
+  // of wave 0 of workgroups 0, 8, 16, ..
+  float rav = 0.f;
+  {
+    const int id = blockIdx.y * gridDim.x + blockIdx.x;
+    const int line = (id >> 3) * 64 + lane;
+    if (a.ra0 && (id & 7) == 0 && threadIdx.x < 64 && line * 4 < a.ra_n)
+      rav = a.ra0[line * 4].x + a.ra1[line * 4].x;
+  }
   {
     const bool in = threadIdx.x < n8;
     const bool kin = kx < a.K;
@@ -267,6 +284,7 @@ __global__ void __launch_bounds__(B == 1 ? 1024 : 512) k_q4_gemv(GemvArgs a) {
         if (bb < B) red[(wave * B + bb) * 16 + (lane & ~3) + r] = acc[r];
     }
   }
+  __asm__ __volatile__("" :: "v"(rav));   // keeps the read-ahead loads
   __syncthreads();
   // ---- sum the waves in fixed order, then the epilogue
   const int t = threadIdx.x;

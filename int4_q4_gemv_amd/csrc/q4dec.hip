@@ -344,6 +344,9 @@ q4_status enqueue_layers(const q4dec_model* m, const StepLayout& L, const StepPt
       a.K = Hq * D; a.NQ = pl.NQ; a.W = pl.W; a.NQs = pl.NQs;
       a.x = P.o; a.ldx = Hq * D;
       a.y = P.y; a.ldy = H; a.y_split = (long)n * H; a.n_rows = n;
+      a.ra0 = reinterpret_cast<const float4*>(ly.post_attn_norm);   // read by the next norm
+      a.ra1 = reinterpret_cast<const float4*>(ly.pre_ff_norm);
+      a.ra_n = H / 4;
       launch_gemv<B, EPI_STORE>(a, pl, a.seg[0].T, pl.W, gemv_lds(B, pl), st);
     }
     // ---- gate/up with GELU(gate) * up; post-attention residual + pre-FF norm in the prologue
@@ -372,6 +375,9 @@ q4_status enqueue_layers(const q4dec_model* m, const StepLayout& L, const StepPt
       a.K = I; a.NQ = pl.NQ; a.W = pl.W; a.NQs = pl.NQs;
       a.x = P.a; a.ldx = I;
       a.y = P.y; a.ldy = H; a.y_split = (long)n * H; a.n_rows = n;
+      a.ra0 = reinterpret_cast<const float4*>(ly.post_ff_norm);      // read by the next norm
+      a.ra1 = reinterpret_cast<const float4*>(l + 1 < m->n_layers ? m->layers[l + 1].attn_norm : m->final_norm);
+      a.ra_n = H / 4;
       launch_gemv<B, EPI_STORE>(a, pl, a.seg[0].T, pl.W, gemv_lds(B, pl), st);
     }
   }
