@@ -165,6 +165,23 @@ def time_q8_gemv(q4, torch, N=15360, K=3840, copies=16, launches=96, reps=10, wa
             "frac": round(nb / avg / 1e9 / PEAK_GBPS, 4), "shape": f"{N}x{K}, batch 1"}
 
 
+def time_int8_step(q4, torch, bytemodel, synth, toks, steps):
+    """The same 48-layer step over int8 (int8lin) weights, batch 1 at context
+    32768: a second model from the same synthetic weights packed with q8_pack,
+    timed like the main figure.  Bytes: the int4 byte model with 34 instead of
+    18 bytes per 32-weight block."""
+    from dataclasses import replace
+    cfg = replace(synth.FULL48, full_cap=32768 + 8)
+    m8 = q4.build_decode_model(cfg, 5, 32767, device="cuda", gen_device="cuda", weights="q8")
+    torch.cuda.synchronize()
+    secs = time_steps(torch, m8, toks, 32767, steps, 2)
+    nb = bytemodel.step_bytes(cfg, 32767) + bytemodel.weight_bytes(cfg) * 16 // 18
+    del m8
+    torch.cuda.empty_cache()
+    return {"ms_per_step": round(secs * 1e3 / steps, 4), "tokens_per_s": round(steps / secs, 2),
+            "algorithmic_bytes": nb, "achieved_GBps": round(nb * steps / secs / 1e9, 1)}
+
+
 COPY_BYTES = 512 << 20
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "q4_gemv_15360x3840_traffic.txt")
 GEMV_SOURCES = ("int4_q4_gemv_amd/csrc/gemv_kernels.h", "int4_q4_gemv_amd/csrc/device_common.h",
@@ -362,6 +379,8 @@ def main():
             log(f"attention kernels: {extra['attention_kernels']}")
             extra["q8_gemv"] = time_q8_gemv(q4, torch)
             log(f"q8 (int8lin) gemv: {extra['q8_gemv']}")
+            extra["int8_ctx32768"] = time_int8_step(q4, torch, bytemodel, synth, toks, k2)
+            log(f"int8 (int8lin) step: {extra['int8_ctx32768']}")
     res = {
         "metric": "decode tokens/s (batch 1, 48 layers) + achieved HBM GB/s as % of peak",
         "value": round(tok_s, 2), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,

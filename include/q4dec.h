@@ -219,6 +219,7 @@ typedef struct q4dec_model {
   const uint16_t* embed;                 /* device fp16 [vocab][hidden], tied head      */
   const float* final_norm;               /* device fp32 [hidden]                        */
   const q4dec_layer* layers;             /* host array [n_layers]                       */
+  int32_t weight_format;                 /* 0: wq..wd packed by q4_pack; 1: by q8_pack   */
 } q4dec_model;
 
 /* Workspace bytes decode_step needs for `m` and n rows. */

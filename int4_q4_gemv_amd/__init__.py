@@ -84,7 +84,8 @@ class Model(C.Structure):
                 ("sl_rot_pairs", C.c_int32), ("full_rot_pairs", C.c_int32),
                 ("sl_theta", C.c_double), ("full_theta", C.c_double),
                 ("sl_scale", C.c_float), ("full_scale", C.c_float), ("eps", C.c_float),
-                ("softcap", C.c_float), ("embed", _p), ("final_norm", _p), ("layers", C.POINTER(Layer))]
+                ("softcap", C.c_float), ("embed", _p), ("final_norm", _p), ("layers", C.POINTER(Layer)),
+                ("weight_format", C.c_int32)]
 
 
 def _declare(L):
@@ -294,8 +295,9 @@ class DecodeModel:
     fp16 tied table and fp16 KV caches, all torch CUDA tensors kept alive
     here, plus the ctypes descriptor the library reads."""
 
-    def __init__(self, cfg, layers, embed, final_norm):
+    def __init__(self, cfg, layers, embed, final_norm, weight_format: int = 0):
         self.cfg = cfg
+        self.weight_format = weight_format   # 0: q4_0 packs, 1: int8 packs
         self.layers = layers          # list of dicts of device tensors
         self.embed = embed
         self.final_norm = final_norm
@@ -315,7 +317,7 @@ class DecodeModel:
                           c.sl_kv_heads, c.sl_head_dim, c.full_head_dim,
                           c.window, c.ring, c.full_cap, c.sl_rot_pairs, c.full_rot_pairs,
                           c.sl_theta, c.full_theta, c.sl_scale, c.full_scale, c.eps, c.softcap,
-                          embed.data_ptr(), final_norm.data_ptr(), arr)
+                          embed.data_ptr(), final_norm.data_ptr(), arr, int(weight_format))
         self._ws = {}
 
     def workspace(self, n: int):
@@ -410,11 +412,16 @@ def stream_read(src: torch.Tensor, sink: torch.Tensor | None = None) -> torch.Te
     return sink
 
 
-def build_decode_model(cfg, seed: int, ctx: int, device="cuda", pack_check=None, gen_device=None):
+def build_decode_model(cfg, seed: int, ctx: int, device="cuda", pack_check=None, gen_device=None,
+                       weights: str = "q4"):
     """Draws the synthetic model of ``synth`` on the GPU, packs every matrix
-    with q4_pack and prefills the caches for a decode at position ``ctx``.
-    ``pack_check(name, l, w_fp32_device, packed)`` is called per matrix when
-    given (the tests use it to compare against the oracle)."""
+    with q4_pack (``weights="q4"``) or q8_pack (``"q8"``) and prefills the
+    caches for a decode at position ``ctx``.  ``pack_check(name, l,
+    w_fp32_device, packed)`` is called per matrix when given (the tests use it
+    to compare against the oracle)."""
+    if weights not in ("q4", "q8"):
+        raise ValueError("weights is 'q4' or 'q8'")
+    pack = q4_pack if weights == "q4" else q8_pack
     from . import synth
     gd = gen_device or device
     layers = []
@@ -426,7 +433,7 @@ def build_decode_model(cfg, seed: int, ctx: int, device="cuda", pack_check=None,
              "layer_scalar": lp.layer_scalar}
         for name, w in lp.mats.items():
             wd = w.to(device)
-            L[name] = q4_pack(wd)
+            L[name] = pack(wd)
             if pack_check is not None:
                 pack_check(name, l, wd, L[name])
             del wd
@@ -438,4 +445,4 @@ def build_decode_model(cfg, seed: int, ctx: int, device="cuda", pack_check=None,
         layers.append(L)
     embed = synth.embed_table(cfg, seed, device=gd).to(device).contiguous()
     fnorm = synth.final_norm(cfg, seed, device=gd).to(device).contiguous()
-    return DecodeModel(cfg, layers, embed, fnorm)
+    return DecodeModel(cfg, layers, embed, fnorm, weight_format=0 if weights == "q4" else 1)

@@ -121,14 +121,25 @@ Q4_DEV float block_sum_dyn(float v, float* red) {
   return s;
 }
 
+// fp16 pair (1024 + u_a, 1024 + u_b) of two code bytes of an int8 code word
+Q4_DEV h2_t q8_pair(uint32_t w, uint32_t sel) { return as_h2(__builtin_amdgcn_perm(0x64646464u, w, sel)); }
+
 // ------------------------------------------------------------ the kernel ----
 // Grid: (tiles, S).  Block: 64 * W threads (EPI_GATEUP: 64 * 2W, the first W
 // waves on the gate tile, the rest on the up tile; S = 1).  Dynamic LDS:
-// B * NQs * 128 halves of activation.
-template <int B, int EPI, int CQ>
-__global__ void __launch_bounds__(B == 1 ? 1024 : 512) k_q4_gemv(GemvArgs a) {
+// B * NQs * UC halves of activation.
+// FMT 0: q4 weights, a unit is a quad (16 rows x 4 blocks, UC = 128 columns),
+// lane l holds row l & 15 and block l >> 4.  FMT 1: int8 weights
+// (q8_kernels.h), a unit is a pair (16 rows x 2 blocks, UC = 64 columns), lane
+// l holds row l & 15 and columns 16 (l >> 4) .. +15; its scales are laid out
+// [unit][block][row].  NQ / NQs / CQ count units.
+// (int8 at batch 4 allows 16 waves: a standalone product with K up to 16384
+// needs them at 16 units per wave)
+template <int B, int EPI, int CQ, int FMT>
+__global__ void __launch_bounds__((B == 1 || FMT == 1) ? 1024 : 512) k_q4_gemv(GemvArgs a) {
+  constexpr int UC = FMT == 0 ? 128 : 64;       // columns per unit
   extern __shared__ __align__(16) unsigned char smem_g[];
-  const int ldxs = a.NQs * 128;                 // staged activation row (halves)
+  const int ldxs = a.NQs * UC;                  // staged activation row (halves)
   uint16_t* xs = reinterpret_cast<uint16_t*>(smem_g);
   __shared__ float red[16 * B * 16];
 
@@ -164,7 +175,7 @@ __global__ void __launch_bounds__(B == 1 ? 1024 : 512) k_q4_gemv(GemvArgs a) {
   // unsplit runs) is staged after the weights.
   const int nrow = a.n_rows;
   const int n8 = ldxs / 8;
-  const int kx = qs0 * 128 + threadIdx.x * 8;
+  const int kx = qs0 * UC + threadIdx.x * 8;
   u4v xr[B];
 #pragma unroll
   for (int bb = 0; bb < B; bb++) {
@@ -176,10 +187,12 @@ __global__ void __launch_bounds__(B == 1 ? 1024 : 512) k_q4_gemv(GemvArgs a) {
   uint16_t sr[CQ];   // batch 1: this lane's scales
   u2v s4[CQ];        // batch 4: the scales of this lane's 4 MFMA rows
   {
-    const uint16_t* spp = seg_scales + tq * 64 + (B == 1 ? lane : (lane & ~3));
+    constexpr int SU = FMT == 0 ? 64 : 32;      // scales per unit
+    const uint16_t* spp = FMT == 0 ? seg_scales + tq * 64 + (B == 1 ? lane : (lane & ~3))
+                                   : seg_scales + tq * 32 + (g >> 1) * 16 + (B == 1 ? (lane & 15) : (lane & 12));
 #pragma unroll
     for (int i = 0; i < CQ; i++) {
-      const long o = (long)(i < nq ? i : 0) * 64;
+      const long o = (long)(i < nq ? i : 0) * SU;
       if constexpr (B == 1) sr[i] = spp[o];
       else s4[i] = *reinterpret_cast<const u2v*>(spp + o);
     }
@@ -210,7 +223,7 @@ __global__ void __launch_bounds__(B == 1 ? 1024 : 512) k_q4_gemv(GemvArgs a) {
 #pragma unroll
     for (int bb = 0; bb < B; bb++)
       for (int i = threadIdx.x + blockDim.x; i < n8; i += blockDim.x) {
-        const int k = qs0 * 128 + i * 8;
+        const int k = qs0 * UC + i * 8;
         u4v v = {0u, 0u, 0u, 0u};
         if (bb < nrow && k < a.K) v = *reinterpret_cast<const u4v*>(a.x + (long)bb * a.ldx + k);
         *reinterpret_cast<u4v*>(&xs[bb * ldxs + i * 8]) = v;
@@ -218,29 +231,43 @@ __global__ void __launch_bounds__(B == 1 ? 1024 : 512) k_q4_gemv(GemvArgs a) {
   }
   __syncthreads();
 
-  const int qx = q0 - qs0;                      // quad index inside the staged run
+  const int qx = q0 - qs0;                      // unit index inside the staged run
+  const h2_t b8 = {(_Float16)1152.0f, (_Float16)1152.0f};   // int8: 1024 + 128
   if constexpr (B == 1) {
     float acc = 0.f;
 #pragma unroll
     for (int i = 0; i < CQ; i++) {
       const int ii = i < nq ? i : 0;
-      const u4v* xv = reinterpret_cast<const u4v*>(xs + ((qx + ii) * 4 + g) * 32);
       const uint32_t qw[4] = {c[i].x, c[i].y, c[i].z, c[i].w};
       float bs = 0.f;
+      if constexpr (FMT == 0) {
+        const u4v* xv = reinterpret_cast<const u4v*>(xs + ((qx + ii) * 4 + g) * 32);
 #pragma unroll
-      for (int w = 0; w < 4; w++) {
-        const u4v xx = xv[w];
-        h2_t v0, v1, v2, v3;
-        dq_word(qw[w], v0, v1, v2, v3);
-        bs = __builtin_amdgcn_fdot2(v0, as_h2(xx.x), bs, false);
-        bs = __builtin_amdgcn_fdot2(v1, as_h2(xx.y), bs, false);
-        bs = __builtin_amdgcn_fdot2(v2, as_h2(xx.z), bs, false);
-        bs = __builtin_amdgcn_fdot2(v3, as_h2(xx.w), bs, false);
+        for (int w = 0; w < 4; w++) {
+          const u4v xx = xv[w];
+          h2_t v0, v1, v2, v3;
+          dq_word(qw[w], v0, v1, v2, v3);
+          bs = __builtin_amdgcn_fdot2(v0, as_h2(xx.x), bs, false);
+          bs = __builtin_amdgcn_fdot2(v1, as_h2(xx.y), bs, false);
+          bs = __builtin_amdgcn_fdot2(v2, as_h2(xx.z), bs, false);
+          bs = __builtin_amdgcn_fdot2(v3, as_h2(xx.w), bs, false);
+        }
+      } else {
+        const u4v* xv = reinterpret_cast<const u4v*>(xs + (qx + ii) * 64 + g * 16);
+        const u4v x0 = xv[0], x1 = xv[1];
+        const uint32_t xw[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+        for (int w = 0; w < 4; w++) {
+          const h2_t lo = q8_pair(qw[w], 0x04010400u) - b8;
+          const h2_t hi = q8_pair(qw[w], 0x04030402u) - b8;
+          bs = __builtin_amdgcn_fdot2(lo, as_h2(xw[2 * w]), bs, false);
+          bs = __builtin_amdgcn_fdot2(hi, as_h2(xw[2 * w + 1]), bs, false);
+        }
       }
       const float d = i < nq ? h2f(sr[i]) : 0.f;
       acc = fmaf(d, bs, acc);
     }
-    // the 4 lane groups hold the same 16 rows over different blocks
+    // the 4 lane groups hold the same 16 rows over different columns
     acc += __shfl_xor(acc, 16, 64);
     acc += __shfl_xor(acc, 32, 64);
     if (lane < 16) red[wave * 16 + lane] = acc;
@@ -251,19 +278,31 @@ __global__ void __launch_bounds__(B == 1 ? 1024 : 512) k_q4_gemv(GemvArgs a) {
 #pragma unroll
     for (int i = 0; i < CQ; i++) {
       const int ii = i < nq ? i : 0;
-      const uint16_t* xb = xl + ((qx + ii) * 4 + g) * 32;
       const uint32_t qw[4] = {c[i].x, c[i].y, c[i].z, c[i].w};
       f4_t cb = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (FMT == 0) {
+        const uint16_t* xb = xl + ((qx + ii) * 4 + g) * 32;
 #pragma unroll
-      for (int w = 0; w < 4; w++) {
-        h2_t v0, v1, v2, v3;
-        dq_word(qw[w], v0, v1, v2, v3);
-        const u2v xa = *reinterpret_cast<const u2v*>(xb + 8 * w);
-        const u2v xc = *reinterpret_cast<const u2v*>(xb + 8 * w + 4);
-        const h4_t A0 = {v0.x, v0.y, v1.x, v1.y};
-        const h4_t A1 = {v2.x, v2.y, v3.x, v3.y};
-        cb = __builtin_amdgcn_mfma_f32_4x4x4f16(A0, __builtin_bit_cast(h4_t, xa), cb, 0, 0, 0);
-        cb = __builtin_amdgcn_mfma_f32_4x4x4f16(A1, __builtin_bit_cast(h4_t, xc), cb, 0, 0, 0);
+        for (int w = 0; w < 4; w++) {
+          h2_t v0, v1, v2, v3;
+          dq_word(qw[w], v0, v1, v2, v3);
+          const u2v xa = *reinterpret_cast<const u2v*>(xb + 8 * w);
+          const u2v xc = *reinterpret_cast<const u2v*>(xb + 8 * w + 4);
+          const h4_t A0 = {v0.x, v0.y, v1.x, v1.y};
+          const h4_t A1 = {v2.x, v2.y, v3.x, v3.y};
+          cb = __builtin_amdgcn_mfma_f32_4x4x4f16(A0, __builtin_bit_cast(h4_t, xa), cb, 0, 0, 0);
+          cb = __builtin_amdgcn_mfma_f32_4x4x4f16(A1, __builtin_bit_cast(h4_t, xc), cb, 0, 0, 0);
+        }
+      } else {
+        const uint16_t* xb = xl + (qx + ii) * 64 + g * 16;
+#pragma unroll
+        for (int w = 0; w < 4; w++) {
+          const h2_t lo = q8_pair(qw[w], 0x04010400u) - b8;
+          const h2_t hi = q8_pair(qw[w], 0x04030402u) - b8;
+          const h4_t A = {lo.x, lo.y, hi.x, hi.y};
+          const u2v xa = *reinterpret_cast<const u2v*>(xb + 4 * w);
+          cb = __builtin_amdgcn_mfma_f32_4x4x4f16(A, __builtin_bit_cast(h4_t, xa), cb, 0, 0, 0);
+        }
       }
       const bool ok = i < nq;
       const uint32_t s01 = s4[i].x, s23 = s4[i].y;

@@ -26,8 +26,8 @@ constexpr int kMaxRows = 4;
 constexpr int kFullSplits = 256;     // decode-step splits of a full layer's positions
 constexpr int kTilePos = 128;        // positions per workgroup pass (4 waves x 32)
 constexpr int kMaxLds = 160 * 1024;
-constexpr int kSplitQuads = 32;      // decode step: longest run of K quads per workgroup (down)
-constexpr int kSplitQuadsO = 16;     // decode step: the same for the output projection
+constexpr int kSplitCols = 4096;     // decode step: longest run of K columns per workgroup (down)
+constexpr int kSplitColsO = 2048;    // decode step: the same for the output projection
 
 bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 hipStream_t S(void* s) { return reinterpret_cast<hipStream_t>(s); }
@@ -40,18 +40,23 @@ q4_status launch_status() {
 long ceil_div(long a, long b) { return (a + b - 1) / b; }
 
 // ------------------------------------------------------------- GEMV plan ----
+// Weight formats: 0 = q4 (units of 16 rows x 128 columns), 1 = int8 (units of
+// 16 rows x 64 columns); one unit is one 1 KB wave-wide load of codes.
+constexpr int unit_cols(int fmt) { return fmt == 0 ? 128 : 64; }
+
 struct GemvPlan {
-  int T = 0, NQ = 0, CQ = 0, W = 0, S = 1, NQs = 0;
+  int T = 0, NQ = 0, CQ = 0, W = 0, S = 1, NQs = 0, fmt = 0;
 };
 
-// [N x K] product: S runs of K (NQs quads each; S = 1 unless split_quads > 0
-// caps a run), W waves per tile streaming CQ quads each.  CQ is the smallest
+// [N x K] product: S runs of K (NQs units each; S = 1 unless split_cols > 0
+// caps a run), W waves per tile streaming CQ units each.  CQ is the smallest
 // of 4, 8, 16 that keeps W within max_waves; W = -1 when none does.
-GemvPlan gemv_plan(int N, int K, int max_waves, int split_quads = 0) {
+GemvPlan gemv_plan(int N, int K, int max_waves, int split_cols = 0, int fmt = 0) {
   GemvPlan p;
+  p.fmt = fmt;
   p.T = (int)ceil_div(N, 16);
-  p.NQ = (int)ceil_div(K, 128);
-  p.S = split_quads > 0 ? (int)ceil_div(p.NQ, split_quads) : 1;
+  p.NQ = (int)ceil_div(K, unit_cols(fmt));
+  p.S = split_cols > 0 ? (int)ceil_div(p.NQ, split_cols / unit_cols(fmt)) : 1;
   p.NQs = (int)ceil_div(p.NQ, p.S);
   p.W = -1;
   for (int cq : {4, 8, 16}) {
@@ -65,47 +70,26 @@ GemvPlan gemv_plan(int N, int K, int max_waves, int split_quads = 0) {
   return p;
 }
 
-size_t gemv_lds(int B, const GemvPlan& p) { return (size_t)B * p.NQs * 128 * 2; }
-
-// q8 product: T 16-row tiles of NP 64-column pairs, W waves of CQ pairs each;
-// CQ is the smallest of 4, 8, 16 that keeps W within 8 (so the grid of a 12B
-// shape is resident at once: 15360 x 3840 in 12.0 us against 12.4-12.8 us with
-// 15 waves of 4 pairs), else within 16; W = -1 when none does.
-struct Q8Plan {
-  int T = 0, NP = 0, CQ = 0, W = -1;
-};
-
-Q8Plan q8_plan(int N, int K) {
-  Q8Plan p;
-  p.T = (int)ceil_div(N, 16);
-  p.NP = (int)ceil_div(K, 64);
-  for (int lim : {8, 16}) {
-    for (int cq : {4, 8, 16}) {
-      const int w = (int)ceil_div(p.NP, cq);
-      if (w <= lim) {
-        p.CQ = cq;
-        p.W = w;
-        return p;
-      }
-    }
-  }
-  return p;
-}
-
-size_t q8_lds(int B, const Q8Plan& p) { return (size_t)B * p.NP * 64 * 2; }
+size_t gemv_lds(int B, const GemvPlan& p) { return (size_t)B * p.NQs * unit_cols(p.fmt) * 2; }
 
 // grid: (tiles, splits); waves: per workgroup (both halves for EPI_GATEUP)
-template <int B, int EPI>
-void launch_gemv(const GemvArgs& a, const GemvPlan& p, int tiles, int waves, size_t lds, hipStream_t st) {
+template <int B, int EPI, int FMT>
+void launch_gemv_f(const GemvArgs& a, const GemvPlan& p, int tiles, int waves, size_t lds, hipStream_t st) {
   const dim3 g(tiles, p.S), blk(64 * waves);
-  if (p.CQ == 16) hipLaunchKernelGGL((k_q4_gemv<B, EPI, 16>), g, blk, lds, st, a);
-  else if (p.CQ == 8) hipLaunchKernelGGL((k_q4_gemv<B, EPI, 8>), g, blk, lds, st, a);
-  else hipLaunchKernelGGL((k_q4_gemv<B, EPI, 4>), g, blk, lds, st, a);
+  if (p.CQ == 16) hipLaunchKernelGGL((k_q4_gemv<B, EPI, 16, FMT>), g, blk, lds, st, a);
+  else if (p.CQ == 8) hipLaunchKernelGGL((k_q4_gemv<B, EPI, 8, FMT>), g, blk, lds, st, a);
+  else hipLaunchKernelGGL((k_q4_gemv<B, EPI, 4, FMT>), g, blk, lds, st, a);
 }
 
-void fill_seg(GemvSeg& s, const void* packed, int N, int K, int tile0, int out_off) {
+template <int B, int EPI>
+void launch_gemv(const GemvArgs& a, const GemvPlan& p, int tiles, int waves, size_t lds, hipStream_t st) {
+  if (p.fmt == 0) launch_gemv_f<B, EPI, 0>(a, p, tiles, waves, lds, st);
+  else launch_gemv_f<B, EPI, 1>(a, p, tiles, waves, lds, st);
+}
+
+void fill_seg(GemvSeg& s, const void* packed, int N, int K, int tile0, int out_off, int fmt = 0) {
   const int T = (int)ceil_div(N, 16);
-  const size_t code_bytes = (size_t)T * ceil_div(K, 128) * 64 * 16;
+  const size_t code_bytes = (size_t)T * ceil_div(K, unit_cols(fmt)) * 64 * 16;
   s.codes = reinterpret_cast<const u4v*>(packed);
   s.scales = reinterpret_cast<const uint16_t*>(static_cast<const uint8_t*>(packed) + code_bytes);
   s.N = N;
@@ -125,15 +109,15 @@ hipError_t max_lds(F* fn, int bytes = kMaxLds - 8 * 1024) {
   return hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
 }
 
-template <int B>
+template <int B, int FMT>
 hipError_t gemv_attrs() {
   hipError_t e = hipSuccess;
-  e = e != hipSuccess ? e : max_lds(&k_q4_gemv<B, EPI_STORE, 4>);
-  e = e != hipSuccess ? e : max_lds(&k_q4_gemv<B, EPI_STORE, 8>);
-  e = e != hipSuccess ? e : max_lds(&k_q4_gemv<B, EPI_STORE, 16>);
-  e = e != hipSuccess ? e : max_lds(&k_q4_gemv<B, EPI_GATEUP, 4>);
-  e = e != hipSuccess ? e : max_lds(&k_q4_gemv<B, EPI_GATEUP, 8>);
-  e = e != hipSuccess ? e : max_lds(&k_q4_gemv<B, EPI_GATEUP, 16>);
+  e = e != hipSuccess ? e : max_lds(&k_q4_gemv<B, EPI_STORE, 4, FMT>);
+  e = e != hipSuccess ? e : max_lds(&k_q4_gemv<B, EPI_STORE, 8, FMT>);
+  e = e != hipSuccess ? e : max_lds(&k_q4_gemv<B, EPI_STORE, 16, FMT>);
+  e = e != hipSuccess ? e : max_lds(&k_q4_gemv<B, EPI_GATEUP, 4, FMT>);
+  e = e != hipSuccess ? e : max_lds(&k_q4_gemv<B, EPI_GATEUP, 8, FMT>);
+  e = e != hipSuccess ? e : max_lds(&k_q4_gemv<B, EPI_GATEUP, 16, FMT>);
   return e;
 }
 
@@ -145,14 +129,10 @@ q4_status set_attrs() {
   e = e != hipSuccess ? e : max_lds(&k_fd_partial<128>, (int)fd_lds_bytes<128>());
   e = e != hipSuccess ? e : max_lds(&k_fd_partial<256>, (int)fd_lds_bytes<256>());
   e = e != hipSuccess ? e : max_lds(&k_fd_partial<512>, (int)fd_lds_bytes<512>());
-  e = e != hipSuccess ? e : gemv_attrs<1>();
-  e = e != hipSuccess ? e : gemv_attrs<4>();
-  e = e != hipSuccess ? e : max_lds(&k_q8_gemv<1, 4>);
-  e = e != hipSuccess ? e : max_lds(&k_q8_gemv<1, 8>);
-  e = e != hipSuccess ? e : max_lds(&k_q8_gemv<1, 16>);
-  e = e != hipSuccess ? e : max_lds(&k_q8_gemv<4, 4>);
-  e = e != hipSuccess ? e : max_lds(&k_q8_gemv<4, 8>);
-  e = e != hipSuccess ? e : max_lds(&k_q8_gemv<4, 16>);
+  e = e != hipSuccess ? e : gemv_attrs<1, 0>();
+  e = e != hipSuccess ? e : gemv_attrs<4, 0>();
+  e = e != hipSuccess ? e : gemv_attrs<1, 1>();
+  e = e != hipSuccess ? e : gemv_attrs<4, 1>();
   if (e != hipSuccess) return Q4_EHIP;
   attrs_set = true;
   return Q4_OK;
@@ -205,6 +185,7 @@ bool model_dims_ok(const q4dec_model* m) {
   if (m->sl_rot_pairs < 0 || m->sl_rot_pairs > m->sl_head_dim / 2) return false;
   if (m->full_rot_pairs < 0 || m->full_rot_pairs > m->full_head_dim / 2) return false;
   if (m->ring < 32) return false;   // a tile's 32 positions wrap the ring at most once
+  if (m->weight_format != 0 && m->weight_format != 1) return false;
   return true;
 }
 
@@ -217,12 +198,13 @@ StepLayout step_layout(const q4dec_model* m) {
   L.o_ld = Hq * L.Dmax;
   // Products whose K is long are split so that each has enough workgroups;
   // gate/up keeps K whole (its epilogue needs both full sums).
-  L.p_qkv_s = gemv_plan(Hq * Ds + 2 * Hs * Ds, H, 8);
-  L.p_qkv_f = gemv_plan(Hq * Df + Df, H, 8);
-  L.p_o_s = gemv_plan(H, Hq * Ds, 8, kSplitQuadsO);
-  L.p_o_f = gemv_plan(H, Hq * Df, 8, kSplitQuadsO);
-  L.p_gu = gemv_plan(I, H, 4);
-  L.p_d = gemv_plan(H, I, 8, kSplitQuads);
+  const int fmt = m->weight_format;
+  L.p_qkv_s = gemv_plan(Hq * Ds + 2 * Hs * Ds, H, 8, 0, fmt);
+  L.p_qkv_f = gemv_plan(Hq * Df + Df, H, 8, 0, fmt);
+  L.p_o_s = gemv_plan(H, Hq * Ds, 8, kSplitColsO, fmt);
+  L.p_o_f = gemv_plan(H, Hq * Df, 8, kSplitColsO, fmt);
+  L.p_gu = gemv_plan(I, H, 4, 0, fmt);
+  L.p_d = gemv_plan(H, I, 8, kSplitCols, fmt);
   L.ymax = std::max(std::max(L.p_o_s.S, L.p_o_f.S), L.p_d.S);
   L.ok = true;
   for (const GemvPlan* p : {&L.p_qkv_s, &L.p_qkv_f, &L.p_o_s, &L.p_o_f, &L.p_gu, &L.p_d})
@@ -285,6 +267,7 @@ template <int B>
 q4_status enqueue_layers(const q4dec_model* m, const StepLayout& L, const StepPtrs& P, int n,
                          float* logits, int32_t* argmax, hipStream_t st) {
   const int H = m->hidden, I = m->inter, Hq = m->n_heads;
+  const int fmt = m->weight_format;
   for (int l = 0; l < m->n_layers; l++) {
     const q4dec_layer& ly = m->layers[l];
     const bool full = ly.is_full != 0;
@@ -295,13 +278,13 @@ q4_status enqueue_layers(const q4dec_model* m, const StepLayout& L, const StepPt
       GemvArgs a{};
       const GemvPlan& pl = full ? L.p_qkv_f : L.p_qkv_s;
       int t0 = 0;
-      fill_seg(a.seg[0], ly.wq, Hq * D, H, t0, 0);
+      fill_seg(a.seg[0], ly.wq, Hq * D, H, t0, 0, fmt);
       t0 += a.seg[0].T;
-      fill_seg(a.seg[1], ly.wk, Hkv * D, H, t0, Hq * D);
+      fill_seg(a.seg[1], ly.wk, Hkv * D, H, t0, Hq * D, fmt);
       t0 += a.seg[1].T;
       a.nseg = 2;
       if (!full) {
-        fill_seg(a.seg[2], ly.wv, Hkv * D, H, t0, (Hq + Hkv) * D);
+        fill_seg(a.seg[2], ly.wv, Hkv * D, H, t0, (Hq + Hkv) * D, fmt);
         t0 += a.seg[2].T;
         a.nseg = 3;
       }
@@ -339,7 +322,7 @@ q4_status enqueue_layers(const q4dec_model* m, const StepLayout& L, const StepPt
     {
       GemvArgs a{};
       const GemvPlan& pl = full ? L.p_o_f : L.p_o_s;
-      fill_seg(a.seg[0], ly.wo, H, Hq * D, 0, 0);
+      fill_seg(a.seg[0], ly.wo, H, Hq * D, 0, 0, fmt);
       a.nseg = 1;
       a.K = Hq * D; a.NQ = pl.NQ; a.W = pl.W; a.NQs = pl.NQs;
       a.x = P.o; a.ldx = Hq * D;
@@ -353,8 +336,8 @@ q4_status enqueue_layers(const q4dec_model* m, const StepLayout& L, const StepPt
     {
       GemvArgs a{};
       const GemvPlan& pl = L.p_gu;
-      fill_seg(a.seg[0], ly.wg, I, H, 0, 0);
-      fill_seg(a.seg[1], ly.wu, I, H, 0, 0);
+      fill_seg(a.seg[0], ly.wg, I, H, 0, 0, fmt);
+      fill_seg(a.seg[1], ly.wu, I, H, 0, 0, fmt);
       a.nseg = 2;
       NormIn ni{};
       ni.h_src = P.hA; ni.y = P.y; ni.ny = (full ? L.p_o_f : L.p_o_s).S; ni.y_split = (long)n * H;
@@ -370,7 +353,7 @@ q4_status enqueue_layers(const q4dec_model* m, const StepLayout& L, const StepPt
     {
       GemvArgs a{};
       const GemvPlan& pl = L.p_d;
-      fill_seg(a.seg[0], ly.wd, H, I, 0, 0);
+      fill_seg(a.seg[0], ly.wd, H, I, 0, 0, fmt);
       a.nseg = 1;
       a.K = I; a.NQ = pl.NQ; a.W = pl.W; a.NQs = pl.NQs;
       a.x = P.a; a.ldx = I;
@@ -653,30 +636,22 @@ q4_status q8_unpack(const void* packed, int N, int K, uint8_t* blocks, void* str
 q4_status q8_gemv(const void* packed, int N, int K, const uint16_t* x, int B, float* y, void* stream) {
   if (!packed || !x || !y) return Q4_EINVAL;
   if (N < 1 || K < 32 || K % 32 || B < 1 || B > kMaxRows) return Q4_ESHAPE;
-  const Q8Plan p = q8_plan(N, K);
-  const int Bk = B == 1 ? 1 : 4;
-  if (p.W < 1 || q8_lds(Bk, p) > (size_t)kMaxLds - 8 * 1024) return Q4_ESHAPE;
+  // the smallest CQ that keeps W within 8 (the grid of a 12B shape is then
+  // resident at once: 15360 x 3840 in 12.0 us against 12.4-12.8 us with 15
+  // waves of 4 pairs), else within 16
+  GemvPlan p = gemv_plan(N, K, 8, 0, 1);
+  if (p.W < 1) p = gemv_plan(N, K, 16, 0, 1);
+  if (p.W < 1 || gemv_lds(B == 1 ? 1 : 4, p) > (size_t)kMaxLds - 8 * 1024) return Q4_ESHAPE;
   if (!al16(packed) || !al16(x) || !al16(y)) return Q4_EALIGN;
   q4_status rc = set_attrs();
   if (rc != Q4_OK) return rc;
-  Q8Args a{};
-  a.codes = static_cast<const u4v*>(packed);
-  a.scales = reinterpret_cast<const uint16_t*>(static_cast<const uint8_t*>(packed) +
-                                               (size_t)p.T * p.NP * 64 * 16);
-  a.N = N; a.K = K; a.NP = p.NP; a.W = p.W;
+  GemvArgs a{};
+  fill_seg(a.seg[0], packed, N, K, 0, 0, 1);
+  a.nseg = 1;
+  a.K = K; a.NQ = p.NQ; a.W = p.W; a.NQs = p.NQs;
   a.x = x; a.ldx = K; a.y = y; a.ldy = N; a.n_rows = B;
-  const dim3 g(p.T), blk(64 * p.W);
-  const size_t lds = q8_lds(Bk, p);
-  hipStream_t st = S(stream);
-  if (B == 1) {
-    if (p.CQ == 16) hipLaunchKernelGGL((k_q8_gemv<1, 16>), g, blk, lds, st, a);
-    else if (p.CQ == 8) hipLaunchKernelGGL((k_q8_gemv<1, 8>), g, blk, lds, st, a);
-    else hipLaunchKernelGGL((k_q8_gemv<1, 4>), g, blk, lds, st, a);
-  } else {
-    if (p.CQ == 16) hipLaunchKernelGGL((k_q8_gemv<4, 16>), g, blk, lds, st, a);
-    else if (p.CQ == 8) hipLaunchKernelGGL((k_q8_gemv<4, 8>), g, blk, lds, st, a);
-    else hipLaunchKernelGGL((k_q8_gemv<4, 4>), g, blk, lds, st, a);
-  }
+  if (B == 1) launch_gemv<1, EPI_STORE>(a, p, p.T, p.W, gemv_lds(1, p), S(stream));
+  else launch_gemv<4, EPI_STORE>(a, p, p.T, p.W, gemv_lds(4, p), S(stream));
   return launch_status();
 }
 

@@ -270,14 +270,15 @@ class _Model(C.Structure):
                 ("sl_theta", _d), ("full_theta", _d),
                 ("sl_rot_pairs", _i), ("full_rot_pairs", _i),
                 ("sl_scale", _d), ("full_scale", _d), ("eps", _d), ("softcap", _d),
-                ("embed", _p), ("final_norm", _p), ("layers", C.POINTER(_Layer))]
+                ("embed", _p), ("final_norm", _p), ("layers", C.POINTER(_Layer)),
+                ("weight_format", _i)]
 
 
 @dataclass
 class OracleLayer:
     is_full: bool
     v_norm: bool
-    wq: np.ndarray  # canonical q4_0 blocks
+    wq: np.ndarray  # canonical q4_0 (or int8) blocks
     wk: np.ndarray
     wv: np.ndarray | None
     wo: np.ndarray
@@ -319,6 +320,7 @@ class OracleModel:
     embed: np.ndarray        # uint16 [vocab, hidden]
     final_norm: np.ndarray   # float32 [hidden]
     layers: list = field(default_factory=list)
+    weight_format: int = 0   # 0: layer matrices are q4_0 blocks, 1: int8 (q8) blocks
 
     def _struct(self):
         arr = (_Layer * len(self.layers))()
@@ -346,7 +348,7 @@ class OracleModel:
                    self.window, self.ring, self.full_cap,
                    self.sl_theta, self.full_theta, self.sl_rot_pairs, self.full_rot_pairs,
                    self.sl_scale, self.full_scale, self.eps, self.softcap,
-                   emb.ctypes.data, fn.ctypes.data, arr)
+                   emb.ctypes.data, fn.ctypes.data, arr, int(self.weight_format))
         return m, keep
 
     def embed_tokens(self, tokens) -> np.ndarray:

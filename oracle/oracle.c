@@ -393,6 +393,13 @@ int orc_embed(const orc_model* m, const int32_t* tokens, int n, double* h) {
 /* One decoder layer on the residual stream h [n][hidden] (updated in place);
  * row i sits at position pos0 + i; the layer's cache receives every row's
  * K/V before any row attends. */
+/* the product of a layer matrix in the model's weight format */
+static void wgemv(const orc_model* m, const uint8_t* blocks, int64_t N, int64_t K,
+                  const uint16_t* x, int B, double* y) {
+  if (m->weight_format == 1) orc_q8_gemv(blocks, N, K, x, B, y);
+  else orc_q4_gemv(blocks, N, K, x, B, y);
+}
+
 int orc_run_layer(const orc_model* m, int l, double* h, int n, int64_t pos0) {
   if (check_rows(m, l, n, pos0)) return -1;
   const int H = m->hidden, Hq = m->n_heads, I = m->inter;
@@ -426,10 +433,10 @@ int orc_run_layer(const orc_model* m, int l, double* h, int n, int64_t pos0) {
     orc_rmsnorm(h + (int64_t)i * H, L->attn_norm, H, m->eps, t0);
     to_f16(t0, H, x16 + (int64_t)i * H);
   }
-  orc_q4_gemv(L->wq, (int64_t)Hq * D, H, x16, n, qv);
-  orc_q4_gemv(L->wk, (int64_t)Hkv * D, H, x16, n, kv);
+  wgemv(m, L->wq, (int64_t)Hq * D, H, x16, n, qv);
+  wgemv(m, L->wk, (int64_t)Hkv * D, H, x16, n, kv);
   if (full) memcpy(vv, kv, sizeof(double) * (size_t)n * Hkv * D); /* attention_k_eq_v: raw k_proj */
-  else orc_q4_gemv(L->wv, (int64_t)Hkv * D, H, x16, n, vv);
+  else wgemv(m, L->wv, (int64_t)Hkv * D, H, x16, n, vv);
 
   for (int i = 0; i < n; i++) {
     const int64_t P = pos0 + i;
@@ -461,7 +468,7 @@ int orc_run_layer(const orc_model* m, int l, double* h, int n, int64_t pos0) {
 
   /* output projection, post-attention norm, residual */
   to_f16(att, (int64_t)n * Hq * D, q16);
-  orc_q4_gemv(L->wo, H, (int64_t)Hq * D, q16, n, y);
+  wgemv(m, L->wo, H, (int64_t)Hq * D, q16, n, y);
   for (int i = 0; i < n; i++) {
     orc_rmsnorm(y + (int64_t)i * H, L->post_attn_norm, H, m->eps, t0);
     for (int c = 0; c < H; c++) h[(int64_t)i * H + c] += t0[c];
@@ -471,11 +478,11 @@ int orc_run_layer(const orc_model* m, int l, double* h, int n, int64_t pos0) {
     orc_rmsnorm(h + (int64_t)i * H, L->pre_ff_norm, H, m->eps, t0);
     to_f16(t0, H, x16 + (int64_t)i * H);
   }
-  orc_q4_gemv(L->wg, I, H, x16, n, g);
-  orc_q4_gemv(L->wu, I, H, x16, n, u);
+  wgemv(m, L->wg, I, H, x16, n, g);
+  wgemv(m, L->wu, I, H, x16, n, u);
   for (int64_t e = 0; e < (int64_t)n * I; e++) g[e] = orc_gelu_tanh(g[e]) * u[e];
   to_f16(g, (int64_t)n * I, x16);
-  orc_q4_gemv(L->wd, H, I, x16, n, y);
+  wgemv(m, L->wd, H, I, x16, n, y);
   for (int i = 0; i < n; i++) {
     orc_rmsnorm(y + (int64_t)i * H, L->post_ff_norm, H, m->eps, t0);
     for (int c = 0; c < H; c++) {

@@ -95,7 +95,8 @@ double orc_softcap(double z, double c);
 typedef struct {
   int is_full;            /* 1: full attention layer, 0: sliding ring layer  */
   int v_norm;             /* apply the scale-free RMSNorm to V               */
-  const uint8_t *wq, *wk, *wv, *wo, *wg, *wu, *wd; /* canonical q4_0 blocks; wv unused on full layers */
+  const uint8_t *wq, *wk, *wv, *wo, *wg, *wu, *wd; /* canonical blocks (q4_0 or int8, per the model's
+                                                      weight_format); wv unused on full layers */
   const float *attn_norm, *q_norm, *k_norm, *post_attn_norm, *pre_ff_norm, *post_ff_norm;
   float layer_scalar;
   uint16_t *k_cache, *v_cache; /* sliding: [Hkv][R][D]; full: [cap][D] */
@@ -111,6 +112,7 @@ typedef struct {
   const uint16_t* embed;      /* fp16 [vocab][hidden], tied with the head */
   const float* final_norm;    /* [hidden] */
   orc_layer* layers;          /* [n_layers] */
+  int weight_format;          /* 0: the layers' matrices are canonical q4_0 blocks; 1: int8 (q8) blocks */
 } orc_model;
 
 /* The step in three parts (used alone for teacher-forced checks):

@@ -52,8 +52,9 @@ def f16bits(t):
 
 def oracle_model_from_device(orc, cfg, gm, blocks):
     """Oracle model over the same inputs as the GPU model ``gm``: the oracle's
-    own q4_0 blocks (``blocks[l][name]``, packed by the oracle from the fp32
-    weights), host copies of the norms, table and caches."""
+    own blocks (``blocks[l][name]``, q4_0 or int8 as ``gm``'s weight format,
+    packed by the oracle from the fp32 weights), host copies of the norms,
+    table and caches."""
     layers = []
     for l, L in enumerate(gm.layers):
         layers.append(orc.OracleLayer(
@@ -72,7 +73,8 @@ def oracle_model_from_device(orc, cfg, gm, blocks):
         sl_theta=cfg.sl_theta, full_theta=cfg.full_theta,
         sl_rot_pairs=cfg.sl_rot_pairs, full_rot_pairs=cfg.full_rot_pairs,
         sl_scale=cfg.sl_scale, full_scale=cfg.full_scale, eps=cfg.eps, softcap=cfg.softcap,
-        embed=f16bits(gm.embed), final_norm=gm.final_norm.cpu().numpy(), layers=layers)
+        embed=f16bits(gm.embed), final_norm=gm.final_norm.cpu().numpy(), layers=layers,
+        weight_format=int(getattr(gm, "weight_format", 0)))
 
 
 def check_argmax(gpu_logits, gpu_argmax, ref_logits, tol_margin):

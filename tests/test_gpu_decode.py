@@ -13,17 +13,19 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda"
 
 
-def build_pair(orc, cfg, seed, ctx, gen_device="cpu"):
+def build_pair(orc, cfg, seed, ctx, gen_device="cpu", weights="q4"):
     blocks = {}
+    opack, unpack = (orc.q4_pack, q4.q4_unpack) if weights == "q4" else (orc.q8_pack, q4.q8_unpack)
 
     def check(name, l, w, packed):
-        ref = orc.q4_pack(w.float().cpu().numpy())
+        ref = opack(w.float().cpu().numpy())
         N, K = w.shape
-        got = q4.q4_unpack(packed, N, K).cpu().numpy()
+        got = unpack(packed, N, K).cpu().numpy()
         assert np.array_equal(got, ref), (name, l)
         blocks.setdefault(l, {})[name] = ref
 
-    gm = q4.build_decode_model(cfg, seed, ctx, device=DEV, pack_check=check, gen_device=gen_device)
+    gm = q4.build_decode_model(cfg, seed, ctx, device=DEV, pack_check=check, gen_device=gen_device,
+                               weights=weights)
     om = oracle_model_from_device(orc, cfg, gm, blocks)
     return gm, om
 
@@ -53,6 +55,27 @@ def test_toy_step_vs_oracle(orc, stream, n, graph):
             g = L[nm].float().cpu().numpy()
             r = getattr(om.layers[l], nm).view(np.float16).astype(np.float32)
             assert_close(g, r, atol=2e-3, rtol=2e-3, what=f"layer {l} {nm}")
+
+
+@pytest.mark.parametrize("n", [1, 4])
+def test_toy_int8_step_vs_oracle(orc, stream, n):
+    """The step over int8 (int8lin) weights: packs bit-exact, logits and the
+    K/V rows written against the oracle's int8 step."""
+    print(f"toy int8 step n={n}", flush=True)
+    cfg = synth.TOY
+    gm, om = build_pair(orc, cfg, 8, 200, weights="q8")
+    assert gm.weight_format == 1 and om.weight_format == 1
+    toks = synth.tokens(cfg, n, 8)
+    logits, am = gm.step(toks, 200)
+    torch.cuda.synchronize()
+    ref, _ = om.decode_step(toks, 200)
+    assert_close(logits, ref, what=f"toy int8 logits n={n}")
+    check_argmax(logits, am, ref, 4e-3)
+    for l, L in enumerate(gm.layers):
+        for nm in ("k_cache", "v_cache"):
+            g = L[nm].float().cpu().numpy()
+            r = getattr(om.layers[l], nm).view(np.float16).astype(np.float32)
+            assert_close(g, r, atol=2e-3, rtol=2e-3, what=f"int8 layer {l} {nm}")
 
 
 def test_toy_graph_replay_matches_eager(orc, stream):
@@ -156,7 +179,7 @@ def sub_model(gm, layer_ids, cfg=None, scalars=None):
         if scalars is not None:
             L["layer_scalar"] = scalars[i]
         layers.append(L)
-    return q4.DecodeModel(cfg, layers, gm.embed, gm.final_norm)
+    return q4.DecodeModel(cfg, layers, gm.embed, gm.final_norm, gm.weight_format)
 
 
 def sub_oracle(om, layer_ids, scalars=None):
@@ -257,6 +280,36 @@ def test_48_layer_each_layer_vs_oracle(orc, full48, stream, n):
             assert_close(g, r, atol=2e-3, rtol=2e-3, what=f"layer {l} {nm} rows")
         if l % 8 == 0:
             print(f"  layer {l} ok", flush=True)
+
+
+@pytest.mark.parametrize("n", [1, 4])
+def test_12b_int8_layers_vs_oracle(orc, stream, n):
+    """The int8 step at the 12B shapes and context 32768, in the benchmark's
+    launch configuration: a sliding and a full layer (layers 0 and 5 of a
+    6-layer model), each run as a one-layer step from the token embedding,
+    against the oracle's int8 step under the composed-output bar."""
+    import dataclasses
+    print(f"12B int8 layers n={n}", flush=True)
+    cfg = dataclasses.replace(synth.FULL48, n_layers=6, full_cap=32768 + 8)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        gm, om = build_pair(orc, cfg, 5, 32768 - 4, gen_device=DEV, weights="q8")
+    torch.cuda.synchronize()
+    pos = 32768 - n
+    toks = synth.tokens(cfg, n, 5)
+    for l in (0, 5):
+        g1 = sub_model(gm, [l])
+        o1 = sub_oracle(om, [l])
+        logits, am = g1.step(toks, pos, graph=False)
+        h = g1.hidden(n)
+        torch.cuda.synchronize()
+        ref_h = o1.run_layer(0, o1.embed_tokens(toks), pos)
+        ref_logits, _ = o1.run_head(ref_h)
+        assert_close_composed(logits, ref_logits, what=f"int8 layer {l} alone: logits (n={n})")
+        assert_close_composed(h, ref_h, what=f"int8 layer {l} alone: residual (n={n})")
+        check_argmax(logits, am, ref_logits, 1.6e-2)
+    del gm
+    torch.cuda.empty_cache()
 
 
 @pytest.mark.timeout(900)

@@ -276,3 +276,40 @@ def test_single_pass_speculative_verify_is_lossless(orc):
         tok = emitted[-1]
     assert out[:n_new] == stream
     assert 4 in sizes and min(sizes) < 4 and len(sizes) < n_new
+
+
+def q4_to_q8_blocks(b4):
+    """Canonical q4_0 blocks [N, nb, 18] -> int8 blocks [N, nb, 34] holding the
+    same scale and the same codes, so that both dequantise to the same weights."""
+    b4 = np.asarray(b4)
+    lo = (b4[..., 2:] & 15).astype(np.int16) - 8        # elements 0..15
+    hi = (b4[..., 2:] >> 4).astype(np.int16) - 8        # elements 16..31
+    q = np.concatenate([lo, hi], axis=-1).astype(np.int8)
+    out = np.empty(b4.shape[:-1] + (34,), dtype=np.uint8)
+    out[..., :2] = b4[..., :2]
+    out[..., 2:] = q.view(np.uint8)
+    return out
+
+
+def test_int8_weight_format_selects_the_int8_product(orc):
+    """The int8 step (weight_format 1) on int8 blocks that hold exactly the q4
+    blocks' scales and codes reproduces the q4 step bit for bit; on blocks that
+    differ (a zeroed down projection in one layer) it does not."""
+    cfg = synth.TOY
+    m4 = build_oracle_model(orc, cfg, 7, 150)
+    assert np.array_equal(orc.q8_dequant(q4_to_q8_blocks(m4.layers[0].wq), cfg.n_heads * cfg.sl_head_dim,
+                                         cfg.hidden),
+                          orc.q4_dequant(m4.layers[0].wq, cfg.n_heads * cfg.sl_head_dim, cfg.hidden))
+    m8 = clone(m4)
+    m8.weight_format = 1
+    for L in m8.layers:
+        for nm in ("wq", "wk", "wv", "wo", "wg", "wu", "wd"):
+            if getattr(L, nm) is not None:
+                setattr(L, nm, q4_to_q8_blocks(getattr(L, nm)))
+    toks = synth.tokens(cfg, 2, 7)
+    l4, a4 = clone(m4).decode_step(toks, 150)
+    l8, a8 = clone(m8).decode_step(toks, 150)
+    assert np.array_equal(l4, l8) and np.array_equal(a4, a8)
+    m8.layers[1].wd = np.zeros_like(m8.layers[1].wd)
+    l8z, _ = clone(m8).decode_step(toks, 150)
+    assert not np.allclose(l8z, l4)
