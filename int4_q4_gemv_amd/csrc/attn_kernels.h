@@ -57,6 +57,8 @@ struct AttnArgs {
   const StepParams* sp;   // decode step: positions on the device
   float* part;            // records [n_seq][n_rows][Hkv][S][GQ][D + 4]
   int fin_on;
+  int kvh_major;          // grids enumerate KV heads fastest (the splits of one KV head, and
+                          // the combine of its query heads, then share an XCD when Hkv = 8)
   AttnFin fin;
   int pos0[64];
 };
@@ -187,7 +189,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D <= 2
   __shared__ float wm[4][16], wl[4][16];
   static_assert(fd_lds_bytes<D>() + sizeof(wm) + sizeof(wl) <= 160 * 1024, "LDS of one workgroup");
 
-  const int split = blockIdx.x, kvh = blockIdx.y;
+  const int split = a.kvh_major ? blockIdx.y : blockIdx.x, kvh = a.kvh_major ? blockIdx.x : blockIdx.y;
   const int seq = blockIdx.z / a.n_rows, row = blockIdx.z - seq * a.n_rows;
   const int nlive = a.n_rows;                 // the grid is built per row count
   if (row >= nlive) return;
@@ -576,7 +578,7 @@ __global__ void __launch_bounds__(256) k_fd_combine(AttnArgs a, float* out32, ui
   __shared__ float red[4][64];
   __shared__ float rm[4], rl[4];
   const int idx = blockIdx.x;
-  const int h = idx % a.Hq, sr = idx / a.Hq;
+  const int h = a.kvh_major ? (idx % a.Hkv) * a.GQ + (idx / a.Hkv) % a.GQ : idx % a.Hq, sr = idx / a.Hq;
   const int seq = sr / a.n_rows, row = sr - seq * a.n_rows;
   const int kvh = h / a.GQ, col = h - kvh * a.GQ;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;

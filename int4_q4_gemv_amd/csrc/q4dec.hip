@@ -140,7 +140,7 @@ q4_status set_attrs() {
 
 template <int D>
 void launch_fd_d(const AttnArgs& a, int n_seq, float* out32, uint16_t* out16, hipStream_t st) {
-  const dim3 grid(a.S, a.Hkv, n_seq * a.n_rows);
+  const dim3 grid(a.kvh_major ? a.Hkv : a.S, a.kvh_major ? a.S : a.Hkv, n_seq * a.n_rows);
   const dim3 cgrid(n_seq * a.n_rows * a.Hq, D / 64);  // 256 threads each
   // without the finishing prologue only the V rows (which also hold the
   // merge buffer) are used: a smaller allocation lets more workgroups share a CU
@@ -312,6 +312,7 @@ q4_status enqueue_layers(const q4dec_model* m, const StepLayout& L, const StepPt
       a.scale_log2 = (full ? m->full_scale : m->sl_scale) * 1.4426950408889634f;
       a.sp = P.sp; a.part = P.apart;
       a.fin_on = 1;
+      a.kvh_major = full ? 0 : 1;
       a.fin.qkv = P.qkv; a.fin.ldq = L.qkv_ld; a.fin.q_norm = ly.q_norm; a.fin.k_norm = ly.k_norm;
       a.fin.v_norm = ly.v_norm; a.fin.rot_pairs = full ? m->full_rot_pairs : m->sl_rot_pairs;
       a.fin.rope_cs = full ? P.rope + m->sl_head_dim / 2 : P.rope;
