@@ -71,6 +71,7 @@ def _declare(L):
     L.orc_ring_admit.argtypes = [_i64, _i64, _i64, _p]
     L.orc_attend.argtypes = [_p, _i, _i, _i, _p, _p, _i64, _p, _i64, _d, _p]
     L.orc_flash_full.argtypes = [_p, _p, _p, _i64, _i, _i, _i64, _i, _d, _p]
+    L.orc_flash_full_vrow.argtypes = [_p, _p, _i64, _i, _i, _i64, _i, _p, _d, _i, _d, _p]
     L.orc_flash_ring.argtypes = [_p, _p, _p, _i, _i, _i, _i64, _i64, _i64, _i, _d, _p]
     L.orc_rmsnorm.argtypes = [_p, _p, _i64, _d, _p]
     L.orc_rope.argtypes = [_p, _i, _i64, _d, _i]
@@ -215,6 +216,22 @@ def flash_full(q16, k16, v16, pos0: int, scale: float) -> np.ndarray:
     return out
 
 
+def flash_full_vrow(q16, vrow16, kw, theta: float, rot_pairs: int, pos0: int,
+                    scale: float) -> np.ndarray:
+    """Full layer caching one row per position: q16 [n, Hq, D]; vrow16 [cap, D]
+    (the V rows); kw [D] the k_norm multiplier; key t = RoPE_t(kw * v_t)."""
+    q16 = np.ascontiguousarray(q16, dtype=np.uint16)
+    vrow16 = np.ascontiguousarray(vrow16, dtype=np.uint16)
+    kw = np.ascontiguousarray(kw, dtype=np.float32)
+    n, Hq, D = q16.shape
+    cap = vrow16.shape[0]
+    assert pos0 + n - 1 < cap and kw.shape == (D,)
+    out = np.empty((n, Hq, D), dtype=np.float64)
+    lib().orc_flash_full_vrow(_ptr(q16), _ptr(vrow16), cap, Hq, D, pos0, n, _ptr(kw),
+                              theta, rot_pairs, scale, _ptr(out))
+    return out
+
+
 def flash_ring(q16, k16, v16, W: int, pos0: int, scale: float) -> np.ndarray:
     """q16 [n, Hq, D]; k16, v16 [Hkv, R, D]; row i sits at position pos0+i."""
     q16 = np.ascontiguousarray(q16, dtype=np.uint16)
@@ -271,7 +288,7 @@ class _Model(C.Structure):
                 ("sl_rot_pairs", _i), ("full_rot_pairs", _i),
                 ("sl_scale", _d), ("full_scale", _d), ("eps", _d), ("softcap", _d),
                 ("embed", _p), ("final_norm", _p), ("layers", C.POINTER(_Layer)),
-                ("weight_format", _i)]
+                ("weight_format", _i), ("kv_format", _i)]
 
 
 @dataclass
@@ -292,7 +309,8 @@ class OracleLayer:
     pre_ff_norm: np.ndarray
     post_ff_norm: np.ndarray
     layer_scalar: float
-    k_cache: np.ndarray  # uint16 fp16 bits; sliding [Hkv, R, D], full [cap, D]
+    k_cache: np.ndarray | None  # uint16 fp16 bits; sliding [Hkv, R, D], full [cap, D]
+                                # (None on full layers of a kv_format 1 model)
     v_cache: np.ndarray
 
 
@@ -321,6 +339,7 @@ class OracleModel:
     final_norm: np.ndarray   # float32 [hidden]
     layers: list = field(default_factory=list)
     weight_format: int = 0   # 0: layer matrices are q4_0 blocks, 1: int8 (q8) blocks
+    kv_format: int = 0       # 0: full layers cache K and V; 1: only the V row (key rebuilt)
 
     def _struct(self):
         arr = (_Layer * len(self.layers))()
@@ -333,12 +352,14 @@ class OracleModel:
                 keep.append(a)
                 return a.ctypes.data
             for nm in ("k_cache", "v_cache"):
-                assert getattr(L, nm).flags["C_CONTIGUOUS"] and getattr(L, nm).dtype == np.uint16
+                c = getattr(L, nm)
+                assert c is None or (c.flags["C_CONTIGUOUS"] and c.dtype == np.uint16)
+            assert L.v_cache is not None and (L.k_cache is not None or (L.is_full and self.kv_format == 1))
             arr[i] = _Layer(int(L.is_full), int(L.v_norm),
                             P(L.wq), P(L.wk), P(L.wv), P(L.wo), P(L.wg), P(L.wu), P(L.wd),
                             P(L.attn_norm), P(L.q_norm), P(L.k_norm), P(L.post_attn_norm),
                             P(L.pre_ff_norm), P(L.post_ff_norm), float(L.layer_scalar),
-                            L.k_cache.ctypes.data, L.v_cache.ctypes.data)
+                            None if L.k_cache is None else L.k_cache.ctypes.data, L.v_cache.ctypes.data)
         keep.append(arr)
         emb = np.ascontiguousarray(self.embed, dtype=np.uint16)
         fn = np.ascontiguousarray(self.final_norm, dtype=np.float32)
@@ -348,7 +369,7 @@ class OracleModel:
                    self.window, self.ring, self.full_cap,
                    self.sl_theta, self.full_theta, self.sl_rot_pairs, self.full_rot_pairs,
                    self.sl_scale, self.full_scale, self.eps, self.softcap,
-                   emb.ctypes.data, fn.ctypes.data, arr, int(self.weight_format))
+                   emb.ctypes.data, fn.ctypes.data, arr, int(self.weight_format), int(self.kv_format))
         return m, keep
 
     def embed_tokens(self, tokens) -> np.ndarray:

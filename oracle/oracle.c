@@ -328,6 +328,59 @@ void orc_flash_ring(const uint16_t* q, const uint16_t* k, const uint16_t* v,
   free(admit);
 }
 
+/* Full layer whose cache keeps ONE fp16 row per position ("vrow").  [12b]
+ * "The per-tier cost": the full-layer pair costs 2 x 512 fp16 per position and
+ * layer, the one KV term that grows with the context, and cutting it is named
+ * as an open lever.  [zoo] architecture notes: on a full layer V is the
+ * scale-free RMSNorm of the raw k projection and K is the k_norm-weighted
+ * RMSNorm of the same row, rotated.  With one eps for both norms, K = RoPE(w .*
+ * V) exactly, so the row v_t alone determines both.  Reading: the stored row is
+ * fp16(v_t); the key is formed from that stored row at full precision,
+ * k_t = RoPE_t(w .* v_t) (never rounded), and v_t is used as stored.
+ * kw: the layer's k_norm multiplier [D]; the rotation is orc_rope's. */
+void orc_flash_full_vrow(const uint16_t* q, const uint16_t* vrow, int64_t cap, int Hq, int D,
+                         int64_t pos0, int n_rows, const float* kw, double theta, int rot_pairs,
+                         double scale, double* out) {
+  const int64_t npos = pos0 + n_rows;
+  if (npos > cap || D > 1024) return;
+  double* kd = (double*)malloc(sizeof(double) * (size_t)(npos > 0 ? npos : 1) * (size_t)D);
+#pragma omp parallel for schedule(static)
+  for (int64_t t = 0; t < npos; t++) {
+    double* kt = kd + t * D;
+    for (int d = 0; d < D; d++) kt[d] = (double)kw[d] * orc_f16_to_f64(vrow[t * D + d]);
+    orc_rope(kt, D, t, theta, rot_pairs);
+  }
+  for (int i = 0; i < n_rows; i++) {
+    const int64_t P = pos0 + i;
+    const uint16_t* qi = q + (int64_t)i * Hq * D;
+    double* oi = out + (int64_t)i * Hq * D;
+#pragma omp parallel for schedule(static)
+    for (int h = 0; h < Hq; h++) {
+      double* s = (double*)malloc(sizeof(double) * (size_t)(P + 1));
+      double qd[1024];
+      for (int d = 0; d < D; d++) qd[d] = orc_f16_to_f64(qi[(int64_t)h * D + d]);
+      double m = -INFINITY;
+      for (int64_t t = 0; t <= P; t++) {
+        double dot = 0.0;
+        for (int d = 0; d < D; d++) dot += qd[d] * kd[t * D + d];
+        s[t] = scale * dot;
+        if (s[t] > m) m = s[t];
+      }
+      double den = 0.0;
+      double* o = oi + (int64_t)h * D;
+      for (int d = 0; d < D; d++) o[d] = 0.0;
+      for (int64_t t = 0; t <= P; t++) {
+        double e = exp(s[t] - m);
+        den += e;
+        for (int d = 0; d < D; d++) o[d] += e * orc_f16_to_f64(vrow[t * D + d]);
+      }
+      for (int d = 0; d < D; d++) o[d] /= den;
+      free(s);
+    }
+  }
+  free(kd);
+}
+
 /* ------------------------------------------------------------------------ */
 /* elementwise pieces                                                        */
 /* ------------------------------------------------------------------------ */
@@ -375,6 +428,8 @@ static int check_rows(const orc_model* m, int l, int n, int64_t pos0) {
   if (!m || n < 1 || pos0 < 0 || l < 0 || l >= m->n_layers) return -1;
   if (m->window > m->ring || m->ring < m->window + n - 1) return -1;
   if (m->layers[l].is_full && pos0 + n - 1 >= m->full_cap) return -1;
+  if (m->kv_format != 0 && m->kv_format != 1) return -1;
+  if (m->kv_format == 1 && m->layers[l].is_full && !m->layers[l].v_norm) return -1;
   return 0;
 }
 
@@ -452,18 +507,21 @@ int orc_run_layer(const orc_model* m, int l, double* h, int n, int64_t pos0) {
       orc_rmsnorm(kh, L->k_norm, D, m->eps, tmp);
       orc_rope(tmp, D, P, theta, rot);
       uint16_t* kdst; uint16_t* vdst;
-      if (full) { kdst = L->k_cache + P * D; vdst = L->v_cache + P * D; }
+      if (full && m->kv_format == 1) { kdst = NULL; vdst = L->v_cache + P * D; }   /* vrow: V only */
+      else if (full) { kdst = L->k_cache + P * D; vdst = L->v_cache + P * D; }
       else {
         int64_t slot = P % R;
         kdst = L->k_cache + ((int64_t)gg * R + slot) * D;
         vdst = L->v_cache + ((int64_t)gg * R + slot) * D;
       }
-      to_f16(tmp, D, kdst);
+      if (kdst) to_f16(tmp, D, kdst);
       if (L->v_norm) { orc_rmsnorm(vh, NULL, D, m->eps, tmp); to_f16(tmp, D, vdst); }
       else to_f16(vh, D, vdst);
     }
   }
-  if (full) orc_flash_full(q16, L->k_cache, L->v_cache, m->full_cap, Hq, D, pos0, n, scale, att);
+  if (full && m->kv_format == 1)
+    orc_flash_full_vrow(q16, L->v_cache, m->full_cap, Hq, D, pos0, n, L->k_norm, theta, rot, scale, att);
+  else if (full) orc_flash_full(q16, L->k_cache, L->v_cache, m->full_cap, Hq, D, pos0, n, scale, att);
   else orc_flash_ring(q16, L->k_cache, L->v_cache, Hq, Hkv, D, R, W, pos0, n, scale, att);
 
   /* output projection, post-attention norm, residual */

@@ -77,6 +77,13 @@ void orc_attend(const uint16_t* q, int Hq, int Hkv, int D,
 void orc_flash_full(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                     int64_t cap, int Hq, int D, int64_t pos0, int n_rows,
                     double scale, double* out);
+/* full layer caching one fp16 row per position ("vrow": the scale-free normed
+ * raw k, which is V): the key of position t is RoPE_t(kw .* v_t), formed at
+ * full precision from the stored row; q, v and the row rule as orc_flash_full.
+ * vrow [cap][D]; kw [D] the layer's k_norm multiplier. */
+void orc_flash_full_vrow(const uint16_t* q, const uint16_t* vrow, int64_t cap, int Hq, int D,
+                         int64_t pos0, int n_rows, const float* kw, double theta, int rot_pairs,
+                         double scale, double* out);
 /* sliding-window layer ring [Hkv][R][D]; row i sits at position pos0+i. */
 void orc_flash_ring(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                     int Hq, int Hkv, int D, int64_t R, int64_t W,
@@ -99,7 +106,8 @@ typedef struct {
                                                       weight_format); wv unused on full layers */
   const float *attn_norm, *q_norm, *k_norm, *post_attn_norm, *pre_ff_norm, *post_ff_norm;
   float layer_scalar;
-  uint16_t *k_cache, *v_cache; /* sliding: [Hkv][R][D]; full: [cap][D] */
+  uint16_t *k_cache, *v_cache; /* sliding: [Hkv][R][D]; full: [cap][D] (k_cache unused
+                                  when the model's kv_format is 1) */
 } orc_layer;
 
 typedef struct {
@@ -113,6 +121,8 @@ typedef struct {
   const float* final_norm;    /* [hidden] */
   orc_layer* layers;          /* [n_layers] */
   int weight_format;          /* 0: the layers' matrices are canonical q4_0 blocks; 1: int8 (q8) blocks */
+  int kv_format;              /* 0: full layers cache K and V rows; 1: they cache only the V row
+                                 (orc_flash_full_vrow; needs v_norm on full layers) */
 } orc_model;
 
 /* The step in three parts (used alone for teacher-forced checks):
