@@ -163,6 +163,27 @@ q4_status flash_decode_full(const uint16_t* q, const uint16_t* k, const uint16_t
                             const int32_t* pos0, int n_seq, int n_rows, float scale,
                             float* out, void* ws, size_t ws_bytes, void* stream);
 
+/* Full-attention flash decode over a cache that keeps ONE fp16 row per
+ * position (Gemma-4-12B-CoreAI card, "The per-tier cost": the full-layer K/V
+ * pair is the KV term that grows with the context; gemma4-12b card,
+ * architecture notes: a full layer's V is the scale-free RMSNorm of the raw k
+ * projection and its K the k_norm-weighted norm of the same row, rotated, so
+ * K = RoPE(kw * V)).  The row is V; the key of row t is formed from it at full
+ * precision in the kernel:
+ *   k_t = RoPE_t(kw * v_t), pair (i, i + D/2) turned by t * theta^(-2i/D) for
+ *   i < rot_pairs, never rounded to fp16;
+ *   out[s][i][h] = sum_t softmax_t(scale * q[s][i][h] . k_t) v_t, t in [0, pos0[s] + i].
+ * Half the bytes per position of flash_decode_full.  vrow: device fp16,
+ * sequence s at vrow + s*seq_stride, rows [cap][D].  kw: device fp32 [D],
+ * 16-byte aligned.  D in {128, 512}; rot_pairs in 0..64; theta > 0; the rest
+ * as flash_decode_full (same workspace size).
+ * Errors: Q4_ESHAPE (D, rot_pairs, theta), Q4_ERANGE, Q4_EINVAL, Q4_ENOSPACE,
+ * Q4_EALIGN, Q4_EHIP. */
+q4_status flash_decode_full_vrow(const uint16_t* q, const uint16_t* vrow, int64_t seq_stride, int cap,
+                                 int Hq, int D, const float* kw, double theta, int rot_pairs,
+                                 const int32_t* pos0, int n_seq, int n_rows, float scale,
+                                 float* out, void* ws, size_t ws_bytes, void* stream);
+
 /* Sliding-window flash decode over a ring (Gemma-4-12B-CoreAI card, "v5/ --
  * ring extent R = 2W"; gemma-4-E4B-CoreAI card, ring/: written, causal,
  * in-window slots).  Row i of sequence s sits at position P = pos0[s] + i and
@@ -220,6 +241,11 @@ typedef struct q4dec_model {
   const float* final_norm;               /* device fp32 [hidden]                        */
   const q4dec_layer* layers;             /* host array [n_layers]                       */
   int32_t weight_format;                 /* 0: wq..wd packed by q4_pack; 1: by q8_pack   */
+  int32_t kv_format;                     /* 0: full layers cache K and V rows; 1: only the V
+                                            row (see flash_decode_full_vrow): k_cache of a
+                                            full layer is then unused and may be NULL;
+                                            needs v_norm on full layers, full_head_dim 128
+                                            or 512 and full_rot_pairs <= 64               */
 } q4dec_model;
 
 /* Workspace bytes decode_step needs for `m` and n rows. */

@@ -85,7 +85,7 @@ class Model(C.Structure):
                 ("sl_theta", C.c_double), ("full_theta", C.c_double),
                 ("sl_scale", C.c_float), ("full_scale", C.c_float), ("eps", C.c_float),
                 ("softcap", C.c_float), ("embed", _p), ("final_norm", _p), ("layers", C.POINTER(Layer)),
-                ("weight_format", C.c_int32)]
+                ("weight_format", C.c_int32), ("kv_format", C.c_int32)]
 
 
 def _declare(L):
@@ -112,6 +112,9 @@ def _declare(L):
     L.flash_decode_workspace_size.argtypes = [_i, _i, _i, _i]
     L.flash_decode_full.restype = _i
     L.flash_decode_full.argtypes = [_p, _p, _p, _i64, _i, _i, _i, _p, _i, _i, _f, _p, _p, _sz, _p]
+    L.flash_decode_full_vrow.restype = _i
+    L.flash_decode_full_vrow.argtypes = [_p, _p, _i64, _i, _i, _i, _p, C.c_double, _i, _p, _i, _i, _f, _p,
+                                         _p, _sz, _p]
     L.flash_decode_ring.restype = _i
     L.flash_decode_ring.argtypes = [_p, _p, _p, _i64, _i, _i, _i, _i, _i, _p, _i, _i, _f, _p, _p, _sz, _p]
     L.decode_step_workspace_size.restype = _sz
@@ -131,7 +134,8 @@ def _declare(L):
 
 
 EXPORTS = ["q4dec_status_str", "q4dec_version", "q4_packed_bytes", "q4_pack", "q4_unpack",
-           "q4_gemv", "q8_packed_bytes", "q8_pack", "q8_unpack", "q8_gemv", "flash_decode_workspace_size", "flash_decode_full", "flash_decode_ring",
+           "q4_gemv", "q8_packed_bytes", "q8_pack", "q8_unpack", "q8_gemv", "flash_decode_workspace_size", "flash_decode_full",
+           "flash_decode_full_vrow", "flash_decode_ring",
            "decode_step_workspace_size", "decode_step", "decode_step_hidden", "decode_step_eager",
            "q4_spec_accept", "q4_stream_read_sink_words", "q4_stream_read", "q4dec_release"]
 
@@ -271,6 +275,27 @@ def flash_decode_full(q, k, v, pos0, scale: float = 1.0, ws=None):
     return out
 
 
+def flash_decode_full_vrow(q, vrow, kw, theta: float, rot_pairs: int, pos0, scale: float = 1.0, ws=None):
+    """Full layer caching one row per position: q fp16 [n_seq, n_rows, Hq, D];
+    vrow fp16 [n_seq, cap, D] (or [cap, D]), the V rows; kw fp32 [D], the
+    k_norm multiplier; the key of row t is RoPE_t(kw * v_t).  D in {128, 512}."""
+    _need_cuda(q, vrow, kw)
+    if vrow.dim() == 2:
+        vrow = vrow.unsqueeze(0)
+    if q.dim() == 3:
+        q = q.unsqueeze(0)
+    n_seq, n_rows, Hq, D = q.shape
+    cap = vrow.shape[1]
+    pos = (C.c_int32 * n_seq)(*([int(pos0)] * n_seq if isinstance(pos0, int) else [int(p) for p in pos0]))
+    out = torch.empty((n_seq, n_rows, Hq, D), dtype=torch.float32, device=q.device)
+    ws = ws if ws is not None else _fd_ws(n_seq, n_rows, Hq, D, q.device)
+    kw = kw.contiguous()
+    _check("flash_decode_full_vrow", lib().flash_decode_full_vrow(
+        _ptr(q.contiguous()), _ptr(vrow), vrow.stride(0), cap, Hq, D, _ptr(kw), float(theta), int(rot_pairs),
+        pos, n_seq, n_rows, float(scale), _ptr(out), _ptr(ws), ws.numel(), _stream()))
+    return out
+
+
 def flash_decode_ring(q, k, v, W: int, pos0, scale: float = 1.0, ws=None):
     """q fp16 [n_seq, n_rows, Hq, D]; k, v fp16 [n_seq, Hkv, R, D] (or [Hkv, R, D])."""
     _need_cuda(q, k, v)
@@ -295,9 +320,10 @@ class DecodeModel:
     fp16 tied table and fp16 KV caches, all torch CUDA tensors kept alive
     here, plus the ctypes descriptor the library reads."""
 
-    def __init__(self, cfg, layers, embed, final_norm, weight_format: int = 0):
+    def __init__(self, cfg, layers, embed, final_norm, weight_format: int = 0, kv_format: int = 0):
         self.cfg = cfg
         self.weight_format = weight_format   # 0: q4_0 packs, 1: int8 packs
+        self.kv_format = kv_format           # 0: full layers cache K and V, 1: only the V row
         self.layers = layers          # list of dicts of device tensors
         self.embed = embed
         self.final_norm = final_norm
@@ -310,14 +336,15 @@ class DecodeModel:
                            L["attn_norm"].data_ptr(), L["q_norm"].data_ptr(), L["k_norm"].data_ptr(),
                            L["post_attn_norm"].data_ptr(), L["pre_ff_norm"].data_ptr(),
                            L["post_ff_norm"].data_ptr(), float(L["layer_scalar"]),
-                           L["k_cache"].data_ptr(), L["v_cache"].data_ptr())
+                           L["k_cache"].data_ptr() if L.get("k_cache") is not None else None,
+                           L["v_cache"].data_ptr())
         self._arr = arr
         c = cfg
         self.desc = Model(c.hidden, c.n_heads, c.inter, c.vocab, len(layers),
                           c.sl_kv_heads, c.sl_head_dim, c.full_head_dim,
                           c.window, c.ring, c.full_cap, c.sl_rot_pairs, c.full_rot_pairs,
                           c.sl_theta, c.full_theta, c.sl_scale, c.full_scale, c.eps, c.softcap,
-                          embed.data_ptr(), final_norm.data_ptr(), arr, int(weight_format))
+                          embed.data_ptr(), final_norm.data_ptr(), arr, int(weight_format), int(kv_format))
         self._ws = {}
 
     def workspace(self, n: int):
@@ -413,14 +440,17 @@ def stream_read(src: torch.Tensor, sink: torch.Tensor | None = None) -> torch.Te
 
 
 def build_decode_model(cfg, seed: int, ctx: int, device="cuda", pack_check=None, gen_device=None,
-                       weights: str = "q4"):
+                       weights: str = "q4", kv: str = "pair"):
     """Draws the synthetic model of ``synth`` on the GPU, packs every matrix
     with q4_pack (``weights="q4"``) or q8_pack (``"q8"``) and prefills the
-    caches for a decode at position ``ctx``.  ``pack_check(name, l,
-    w_fp32_device, packed)`` is called per matrix when given (the tests use it
-    to compare against the oracle)."""
+    caches for a decode at position ``ctx``.  ``kv="vrow"`` keeps only the V
+    row of the full layers (no K cache is allocated for them).
+    ``pack_check(name, l, w_fp32_device, packed)`` is called per matrix when
+    given (the tests use it to compare against the oracle)."""
     if weights not in ("q4", "q8"):
         raise ValueError("weights is 'q4' or 'q8'")
+    if kv not in ("pair", "vrow"):
+        raise ValueError("kv is 'pair' or 'vrow'")
     pack = q4_pack if weights == "q4" else q8_pack
     from . import synth
     gd = gen_device or device
@@ -441,8 +471,13 @@ def build_decode_model(cfg, seed: int, ctx: int, device="cuda", pack_check=None,
         for name, t in lp.norms.items():
             L[name] = t.to(device).contiguous()
         k, v = synth.layer_cache(cfg, l, seed, ctx, device=gd)
-        L["k_cache"], L["v_cache"] = k.to(device).contiguous(), v.to(device).contiguous()
+        if kv == "vrow" and L["is_full"]:
+            L["k_cache"], L["v_cache"] = None, v.to(device).contiguous()
+        else:
+            L["k_cache"], L["v_cache"] = k.to(device).contiguous(), v.to(device).contiguous()
+        del k, v
         layers.append(L)
     embed = synth.embed_table(cfg, seed, device=gd).to(device).contiguous()
     fnorm = synth.final_norm(cfg, seed, device=gd).to(device).contiguous()
-    return DecodeModel(cfg, layers, embed, fnorm, weight_format=0 if weights == "q4" else 1)
+    return DecodeModel(cfg, layers, embed, fnorm, weight_format=0 if weights == "q4" else 1,
+                       kv_format=0 if kv == "pair" else 1)

@@ -60,8 +60,25 @@ struct AttnArgs {
   int kvh_major;          // grids enumerate KV heads fastest (the splits of one KV head, and
                           // the combine of its query heads, then share an XCD when Hkv = 8)
   AttnFin fin;
+  // Full layers that cache one row per position (kernel template VR): the
+  // key of cached row t is RoPE_t(kw * v_t), formed in registers from the V
+  // row (gemma4-12b card, architecture notes: V is the scale-free norm of the
+  // raw k projection and K its k_norm-weighted norm, rotated, so K = RoPE(kw *
+  // V); Gemma-4-12B-CoreAI card, "The per-tier cost": the full-layer pair is
+  // the KV term that grows with the context).  a.k is then unused.
+  int vrow;               // host-side dispatch flag for VR
+  const float* kw;        // [D] the layer's k_norm multiplier (16-byte aligned)
+  double theta;           // RoPE base of the layer kind
+  int krot;               // rotated pairs, at most vr_max_rot<D>()
   int pos0[64];
 };
+
+// Pairs (i, i + D/2) that a VR kernel can rotate: those of its first
+// min(2, D/64) k steps (64 pairs for D >= 128).
+template <int D>
+constexpr int vr_rsteps() { return D / 64 < 2 ? D / 64 : 2; }
+template <int D>
+constexpr int vr_max_rot() { return 32 * vr_rsteps<D>(); }
 
 Q4_DEV long attn_rec(const AttnArgs& a, int seq, int row, int kvh, int split, int col, int D) {
   return (((((long)seq * a.n_rows + row) * a.Hkv + kvh) * a.S + split) * a.GQ + col) * (long)(D + 4);
@@ -176,18 +193,40 @@ Q4_DEV void finish_vals(float (&v)[D / 64], const float (&wv)[D / 64], bool weig
 
 // D <= 256 fits two waves per SIMD (<= 256 registers), so two workgroups
 // share a CU when the grid is larger than the chip (many sequences).
-template <int D>
+//
+// VR (one cached row per position): the V row of a tile is loaded twice, into
+// registers as the QK operand and into LDS for PV (the second read is served
+// by the L2), so HBM carries 1 KB per position at D = 512.  In k steps whose
+// dims rotate (pairs below vr_max_rot: steps s < RS and their partners
+// s + D/64), the lane rebuilds its key elements k = RoPE_t(kw * v) in fp32 and
+// splits them into fp16 hi + lo; in the other steps the key is kw * v, so kw
+// is folded into the query (q * kw split into fp16 hi + lo).  Either way the
+// scores carry about 22 significant bits of the key, which is never rounded
+// to fp16.  The angle t * theta^(-2i/D) is formed in fp64 revolutions and
+// reduced to [0, 1) before the hardware sine and cosine; the row 4 positions
+// on is turned by the precomputed (cos, sin) of 4 * theta^(-2i/D).
+template <int D, bool VR = false>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D <= 256 ? 2 : 1))) k_fd_partial(AttnArgs a) {
   constexpr int VROW = fd_vpitch<D>();        // LDS row pitch of the V rows (halves)
   constexpr int NDS = D / 16;                 // PV dim steps
   constexpr int NKS = D / 32;                 // QK k steps
+  constexpr int HS = D / 64;                  // k steps per half head: step s pairs with s + HS
+  constexpr int RS = vr_rsteps<D>();          // VR: rotating k steps of the first half
+  constexpr int NR = VR ? 32 * RS : 1;        // VR: rotatable pairs
   extern __shared__ __align__(16) unsigned char smem[];
   uint16_t* vlds = reinterpret_cast<uint16_t*>(smem);
   uint16_t* newK = vlds + 4 * 32 * VROW;      // [4][D] rows of this step (decode step)
   uint16_t* newV = newK + 4 * D;
   uint16_t* q16 = newV + 4 * D;               // [16][D] finished queries (decode step)
   __shared__ float wm[4][16], wl[4][16];
-  static_assert(fd_lds_bytes<D>() + sizeof(wm) + sizeof(wl) <= 160 * 1024, "LDS of one workgroup");
+  // VR tables of the rotatable pairs i: revolutions per position of pair i
+  // (0 past krot), (cos, sin) of 4 positions' turn, kw at dims i and i + D/2
+  __shared__ double vr_f[NR];
+  __shared__ float2 vr_c4[NR];
+  __shared__ float vr_w[2 * NR];
+  static_assert(fd_lds_bytes<D>() + sizeof(wm) + sizeof(wl) + sizeof(vr_f) + sizeof(vr_c4) + sizeof(vr_w) <=
+                    160 * 1024, "LDS of one workgroup");
+  auto rebuilt = [](int s) { return VR && (s < RS || (s >= HS && s < HS + RS)); };
 
   const int split = a.kvh_major ? blockIdx.y : blockIdx.x, kvh = a.kvh_major ? blockIdx.x : blockIdx.y;
   const int seq = blockIdx.z / a.n_rows, row = blockIdx.z - seq * a.n_rows;
@@ -258,8 +297,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D <= 2
   const int j = lane & 15, g = lane >> 4;
   const bool col_ok = j < a.GQ;
 
-  uint16_t* kb = a.k + seq * a.seq_stride + (a.ring ? (long)kvh * a.R * D : 0);
   uint16_t* vb = a.v + seq * a.seq_stride + (a.ring ? (long)kvh * a.R * D : 0);
+  uint16_t* kb = VR ? vb : a.k + seq * a.seq_stride + (a.ring ? (long)kvh * a.R * D : 0);
 
   // ---- K and V of this wave's first tile, issued before anything waits.
   // MFMA row r of half h <-> tile position 8*(r/4) + 4h + r%4, so lane
@@ -272,6 +311,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D <= 2
                                               // straight into this wave's LDS rows
   uint16_t* vl = vlds + wave * 32 * VROW;
   h8_t KA[NKS], KB[NKS];
+  h8_t KAl[NKS], KBl[NKS];                    // VR: fp16 lo parts of the rebuilt key elements
   // Cache rows of a tile.  Rows [0, nv) of the tile at t0 come from the cache
   // (the rest are masked out or formed in this step: they read row 0).  On a
   // ring layer, tile row r lives at slot (t0 + r) mod R; rings hold at least
@@ -300,8 +340,11 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D <= 2
     const uint16_t* kc = kb + row_at(s0, nv, ra + 4) + 8 * g;
 #pragma unroll
     for (int s = 0; s < NKS; s++) {
-      KA[s] = __builtin_bit_cast(h8_t, __builtin_nontemporal_load(reinterpret_cast<const u4v*>(ka + 32 * s)));
-      KB[s] = __builtin_bit_cast(h8_t, __builtin_nontemporal_load(reinterpret_cast<const u4v*>(kc + 32 * s)));
+      // VR: plain loads, so that the lines stay in the L2 for the V read
+      const u4v* pa_ = reinterpret_cast<const u4v*>(ka + 32 * s);
+      const u4v* pb_ = reinterpret_cast<const u4v*>(kc + 32 * s);
+      KA[s] = __builtin_bit_cast(h8_t, VR ? *pa_ : __builtin_nontemporal_load(pa_));
+      KB[s] = __builtin_bit_cast(h8_t, VR ? *pb_ : __builtin_nontemporal_load(pb_));
     }
   };
   // V: each instruction fills 1 KB of LDS, RPI = 512 / D consecutive tile
@@ -329,9 +372,42 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D <= 2
     if (EK) load_k(t0);
     load_v(t0);
   }
+  if constexpr (VR) {
+    const int i = threadIdx.x;
+    if (i < NR) {
+      const double f = i < a.krot ? pow(a.theta, -2.0 * (double)i / (double)D) : 0.0;
+      const double r4 = 4.0 * f;
+      vr_f[i] = f * 0.15915494309189535;                       // revolutions per position
+      vr_c4[i] = make_float2((float)cos(r4), (float)sin(r4));
+      vr_w[i] = a.kw[i];
+      vr_w[NR + i] = a.kw[D / 2 + i];
+    }
+  }
 
-  // ---- queries of this workgroup's columns as the MFMA B operand
-  h8_t qb[NKS];
+  // ---- queries of this workgroup's columns as the MFMA B operand (VR: in
+  // the steps whose key is kw * v, q * kw as fp16 hi in qb; the lo parts are
+  // parked in LDS over the finished queries, qlo [NKS][64 lanes][8])
+  h8_t qb[NKS], qlo[NKS];
+  uint16_t* qlo_l = q16;
+  auto set_q = [&](int s, u4v t) {
+    if (VR && !rebuilt(s)) {
+      const float4 w0 = *reinterpret_cast<const float4*>(a.kw + 32 * s + 8 * g);
+      const float4 w1 = *reinterpret_cast<const float4*>(a.kw + 32 * s + 8 * g + 4);
+      const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+      const h8_t qh = __builtin_bit_cast(h8_t, t);
+      h8_t hi, lo;
+#pragma unroll
+      for (int e = 0; e < 8; e++) {
+        const float x = (float)qh[e] * wv[e];
+        hi[e] = (_Float16)x;
+        lo[e] = (_Float16)(x - (float)hi[e]);
+      }
+      qb[s] = hi;
+      qlo[s] = lo;
+    } else {
+      qb[s] = __builtin_bit_cast(h8_t, t);
+    }
+  };
   if (a.fin_on) {
     const AttnFin& f = a.fin;
     // finish the jobs: every query head, and k and v of the rows of this
@@ -348,7 +424,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D <= 2
       const int r = (jb - a.GQ) >> 1;
       if (r < r0 || r > r1) continue;
       if (((jb - a.GQ) & 1) == 0) {
-        finish_vals<D>(raw[k], wk, true, true, fcs[k], f.rot_pairs, f.eps, newK + r * D);
+        if (!VR) finish_vals<D>(raw[k], wk, true, true, fcs[k], f.rot_pairs, f.eps, newK + r * D);
       } else if (f.v_norm) {
         finish_vals<D>(raw[k], wk, false, false, fcs[k], f.rot_pairs, f.eps, newV + r * D);
       } else {
@@ -360,7 +436,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D <= 2
     if (P >= st && P < en) {
       const long so = (long)(a.ring ? P % a.R : P) * D;
       for (int d = threadIdx.x; d < D; d += 256) {
-        kb[so + d] = newK[row * D + d];
+        if (!VR) kb[so + d] = newK[row * D + d];
         vb[so + d] = newV[row * D + d];
       }
     }
@@ -368,7 +444,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D <= 2
     for (int s = 0; s < NKS; s++) {
       u4v t = *reinterpret_cast<const u4v*>(q16 + (col_ok ? j : 0) * D + 32 * s + 8 * g);
       if (!col_ok) t = (u4v){0u, 0u, 0u, 0u};
-      qb[s] = __builtin_bit_cast(h8_t, t);
+      set_q(s, t);
     }
   } else {
     const uint16_t* qp = a.q + (((long)seq * a.n_rows + row) * a.Hq + (col_ok ? kvh * a.GQ + j : 0)) * D + 8 * g;
@@ -376,8 +452,17 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D <= 2
     for (int s = 0; s < NKS; s++) {
       u4v t = *reinterpret_cast<const u4v*>(qp + 32 * s);
       if (!col_ok) t = (u4v){0u, 0u, 0u, 0u};
-      qb[s] = __builtin_bit_cast(h8_t, t);
+      set_q(s, t);
     }
+  }
+  if constexpr (VR) {
+    __syncthreads();                          // every wave has read q16; the VR tables are in
+    if (wave == 0) {
+#pragma unroll
+      for (int s = 0; s < NKS; s++)
+        if (!rebuilt(s)) *reinterpret_cast<h8_t*>(qlo_l + (s * 64 + lane) * 8) = qlo[s];
+    }
+    __syncthreads();
   }
 
   float m_run = -INFINITY, l_part = 0.f;
@@ -390,10 +475,39 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D <= 2
     if (!first) load_v(t0);
     if (t0 + 31 >= P0new) {                   // patch the rows formed in this step
       const int pa = t0 + 8 * (j >> 2) + (j & 3), pb = pa + 4;
+      const uint16_t* nk = VR ? newV : newK;  // VR: the key is formed from the V row
 #pragma unroll
       for (int s = 0; s < NKS; s++) {
-        if (pa >= P0new && pa < en) KA[s] = *reinterpret_cast<const h8_t*>(newK + (pa - P0new) * D + 32 * s + 8 * g);
-        if (pb >= P0new && pb < en) KB[s] = *reinterpret_cast<const h8_t*>(newK + (pb - P0new) * D + 32 * s + 8 * g);
+        if (pa >= P0new && pa < en) KA[s] = *reinterpret_cast<const h8_t*>(nk + (pa - P0new) * D + 32 * s + 8 * g);
+        if (pb >= P0new && pb < en) KB[s] = *reinterpret_cast<const h8_t*>(nk + (pb - P0new) * D + 32 * s + 8 * g);
+      }
+    }
+    if constexpr (VR) {
+      // key elements of the rotating steps: lane (j, g) holds positions
+      // pa (KA) and pa + 4 (KB) at dims 32 s + 8 g + e and that + D/2
+      const int pa = t0 + 8 * (j >> 2) + (j & 3);
+#pragma unroll
+      for (int s = 0; s < RS; s++) {
+#pragma unroll
+        for (int e = 0; e < 8; e++) {
+          const int i = 32 * s + 8 * g + e;
+          double r = (double)pa * vr_f[i];
+          r -= floor(r);
+          const float rv = (float)r;
+          const float ca = __builtin_amdgcn_cosf(rv), sa = __builtin_amdgcn_sinf(rv);
+          const float2 c4 = vr_c4[i];
+          const float cb = ca * c4.x - sa * c4.y, sb = sa * c4.x + ca * c4.y;
+          const float w0 = vr_w[i], w1 = vr_w[NR + i];
+          auto form = [&](h8_t& X0, h8_t& X1, h8_t& L0, h8_t& L1, float c, float sn) {
+            const float u0 = w0 * (float)X0[e], u1 = w1 * (float)X1[e];
+            const float k0 = c * u0 - sn * u1, k1 = sn * u0 + c * u1;
+            const _Float16 h0 = (_Float16)k0, h1 = (_Float16)k1;
+            X0[e] = h0; L0[e] = (_Float16)(k0 - (float)h0);
+            X1[e] = h1; L1[e] = (_Float16)(k1 - (float)h1);
+          };
+          form(KA[s], KA[s + HS], KAl[s], KAl[s + HS], ca, sa);
+          form(KB[s], KB[s + HS], KBl[s], KBl[s + HS], cb, sb);
+        }
       }
     }
     f4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
@@ -401,6 +515,14 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D <= 2
     for (int s = 0; s < NKS; s++) {
       s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(KA[s], qb[s], s0, 0, 0, 0);
       s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(KB[s], qb[s], s1, 0, 0, 0);
+      if (VR && rebuilt(s)) {
+        s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(KAl[s], qb[s], s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(KBl[s], qb[s], s1, 0, 0, 0);
+      } else if (VR) {
+        const h8_t ql = *reinterpret_cast<const h8_t*>(qlo_l + (s * 64 + lane) * 8);
+        s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(KA[s], ql, s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(KB[s], ql, s1, 0, 0, 0);
+      }
     }
     // lane (j, g): reg i of s0 -> position t0 + 8g + i; of s1 -> t0 + 8g + 4 + i
     float sv[8];

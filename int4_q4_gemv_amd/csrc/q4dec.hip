@@ -129,6 +129,8 @@ q4_status set_attrs() {
   e = e != hipSuccess ? e : max_lds(&k_fd_partial<128>, (int)fd_lds_bytes<128>());
   e = e != hipSuccess ? e : max_lds(&k_fd_partial<256>, (int)fd_lds_bytes<256>());
   e = e != hipSuccess ? e : max_lds(&k_fd_partial<512>, (int)fd_lds_bytes<512>());
+  e = e != hipSuccess ? e : max_lds(&k_fd_partial<128, true>, (int)fd_lds_bytes<128>());
+  e = e != hipSuccess ? e : max_lds(&k_fd_partial<512, true>, (int)fd_lds_bytes<512>());
   e = e != hipSuccess ? e : gemv_attrs<1, 0>();
   e = e != hipSuccess ? e : gemv_attrs<4, 0>();
   e = e != hipSuccess ? e : gemv_attrs<1, 1>();
@@ -144,7 +146,13 @@ void launch_fd_d(const AttnArgs& a, int n_seq, float* out32, uint16_t* out16, hi
   const dim3 cgrid(n_seq * a.n_rows * a.Hq, D / 64);  // 256 threads each
   // without the finishing prologue only the V rows (which also hold the
   // merge buffer) are used: a smaller allocation lets more workgroups share a CU
-  hipLaunchKernelGGL(k_fd_partial<D>, grid, dim3(256), a.fin_on ? fd_lds_bytes<D>() : fd_lds_vbytes<D>(), st, a);
+  const size_t lds = (a.fin_on || a.vrow) ? fd_lds_bytes<D>() : fd_lds_vbytes<D>();   // VR parks q lo parts
+  if constexpr (D == 128 || D == 512) {
+    if (a.vrow) hipLaunchKernelGGL((k_fd_partial<D, true>), grid, dim3(256), lds, st, a);
+    else hipLaunchKernelGGL((k_fd_partial<D, false>), grid, dim3(256), lds, st, a);
+  } else {
+    hipLaunchKernelGGL((k_fd_partial<D, false>), grid, dim3(256), lds, st, a);
+  }
   if (a.S <= 16) hipLaunchKernelGGL((k_fd_combine<D, 16>), cgrid, dim3(256), 0, st, a, out32, out16);
   else if (a.S <= 32) hipLaunchKernelGGL((k_fd_combine<D, 32>), cgrid, dim3(256), 0, st, a, out32, out16);
   else hipLaunchKernelGGL((k_fd_combine<D, kMaxSplits>), cgrid, dim3(256), 0, st, a, out32, out16);
@@ -175,6 +183,13 @@ struct StepLayout {
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
+// head sizes and rotations a one-row-per-position full layer supports
+bool vrow_dims_ok(int D, int rot_pairs) {
+  if (D == 128) return rot_pairs >= 0 && rot_pairs <= vr_max_rot<128>();
+  if (D == 512) return rot_pairs >= 0 && rot_pairs <= vr_max_rot<512>();
+  return false;
+}
+
 bool model_dims_ok(const q4dec_model* m) {
   if (m->hidden < 32 || m->hidden % 32 || m->hidden > 4096) return false;
   if (m->inter < 32 || m->inter % 32) return false;
@@ -186,6 +201,8 @@ bool model_dims_ok(const q4dec_model* m) {
   if (m->full_rot_pairs < 0 || m->full_rot_pairs > m->full_head_dim / 2) return false;
   if (m->ring < 32) return false;   // a tile's 32 positions wrap the ring at most once
   if (m->weight_format != 0 && m->weight_format != 1) return false;
+  if (m->kv_format != 0 && m->kv_format != 1) return false;
+  if (m->kv_format == 1 && !vrow_dims_ok(m->full_head_dim, m->full_rot_pairs)) return false;
   return true;
 }
 
@@ -313,6 +330,9 @@ q4_status enqueue_layers(const q4dec_model* m, const StepLayout& L, const StepPt
       a.sp = P.sp; a.part = P.apart;
       a.fin_on = 1;
       a.kvh_major = full ? 0 : 1;
+      if (full && m->kv_format == 1) {
+        a.vrow = 1; a.k = ly.v_cache; a.kw = ly.k_norm; a.theta = m->full_theta; a.krot = m->full_rot_pairs;
+      }
       a.fin.qkv = P.qkv; a.fin.ldq = L.qkv_ld; a.fin.q_norm = ly.q_norm; a.fin.k_norm = ly.k_norm;
       a.fin.v_norm = ly.v_norm; a.fin.rot_pairs = full ? m->full_rot_pairs : m->sl_rot_pairs;
       a.fin.rope_cs = full ? P.rope + m->sl_head_dim / 2 : P.rope;
@@ -401,11 +421,14 @@ q4_status check_model(const q4dec_model* m, int n, int pos0, const int32_t* toke
     const bool full = ly.is_full != 0;
     any_full |= full;
     if (!ly.wq || !ly.wk || !ly.wo || !ly.wg || !ly.wu || !ly.wd || (!full && !ly.wv)) return Q4_EINVAL;
+    const bool vrow = full && m->kv_format == 1;   // the K cache is not used
     if (!ly.attn_norm || !ly.q_norm || !ly.k_norm || !ly.post_attn_norm || !ly.pre_ff_norm ||
-        !ly.post_ff_norm || !ly.k_cache || !ly.v_cache)
+        !ly.post_ff_norm || (!ly.k_cache && !vrow) || !ly.v_cache)
       return Q4_EINVAL;
+    if (vrow && !ly.v_norm) return Q4_EINVAL;         // K = RoPE(k_norm * V) needs the normed V
     const void* ps[] = {ly.wq, ly.wk, ly.wo, ly.wg, ly.wu, ly.wd, ly.attn_norm, ly.q_norm, ly.k_norm,
-                        ly.post_attn_norm, ly.pre_ff_norm, ly.post_ff_norm, ly.k_cache, ly.v_cache};
+                        ly.post_attn_norm, ly.pre_ff_norm, ly.post_ff_norm, vrow ? ly.v_cache : ly.k_cache,
+                        ly.v_cache};
     for (const void* p : ps)
       if (!al16(p)) return Q4_EALIGN;
     if (!full && !al16(ly.wv)) return Q4_EALIGN;
@@ -694,6 +717,36 @@ q4_status flash_decode_full(const uint16_t* q, const uint16_t* k, const uint16_t
   a.S = (int)std::min<long>(fd_split_cap(n_seq, n_rows), std::max<long>(1, ceil_div(maxlen, kTilePos)));
   a.scale_log2 = scale * 1.4426950408889634f;
   a.sp = nullptr; a.part = static_cast<float*>(ws);
+  for (int s = 0; s < n_seq; s++) a.pos0[s] = pos0[s];
+  launch_fd(a, D, n_seq, out, nullptr, S(stream));
+  return launch_status();
+}
+
+q4_status flash_decode_full_vrow(const uint16_t* q, const uint16_t* vrow, int64_t seq_stride, int cap, int Hq,
+                                 int D, const float* kw, double theta, int rot_pairs, const int32_t* pos0,
+                                 int n_seq, int n_rows, float scale, float* out, void* ws, size_t ws_bytes,
+                                 void* stream) {
+  q4_status rc = fd_common(q, vrow, vrow, seq_stride, Hq, 1, D, pos0, n_seq, n_rows, out, ws, ws_bytes);
+  if (rc != Q4_OK) return rc;
+  if (!kw) return Q4_EINVAL;
+  if (!vrow_dims_ok(D, rot_pairs) || !(theta > 0.0) || cap < 1) return Q4_ESHAPE;
+  if (!al16(kw)) return Q4_EALIGN;
+  if (n_seq > 1 && seq_stride < (int64_t)cap * D) return Q4_ESHAPE;
+  long maxlen = 1;
+  for (int s = 0; s < n_seq; s++) {
+    if (pos0[s] < 0 || (long)pos0[s] + n_rows - 1 >= cap) return Q4_ERANGE;
+    maxlen = std::max(maxlen, (long)pos0[s] + n_rows);
+  }
+  rc = set_attrs();
+  if (rc != Q4_OK) return rc;
+  AttnArgs a{};
+  a.q = q; a.k = const_cast<uint16_t*>(vrow); a.v = const_cast<uint16_t*>(vrow); a.seq_stride = seq_stride;
+  a.Hq = Hq; a.Hkv = 1; a.GQ = Hq; a.ring = 0; a.R = cap; a.W = cap;
+  a.n_rows = n_rows;
+  a.S = (int)std::min<long>(fd_split_cap(n_seq, n_rows), std::max<long>(1, ceil_div(maxlen, kTilePos)));
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.sp = nullptr; a.part = static_cast<float*>(ws);
+  a.vrow = 1; a.kw = kw; a.theta = theta; a.krot = rot_pairs;
   for (int s = 0; s < n_seq; s++) a.pos0[s] = pos0[s];
   launch_fd(a, D, n_seq, out, nullptr, S(stream));
   return launch_status();

@@ -65,7 +65,8 @@ def oracle_model_from_device(orc, cfg, gm, blocks):
             k_norm=L["k_norm"].cpu().numpy(), post_attn_norm=L["post_attn_norm"].cpu().numpy(),
             pre_ff_norm=L["pre_ff_norm"].cpu().numpy(), post_ff_norm=L["post_ff_norm"].cpu().numpy(),
             layer_scalar=float(L["layer_scalar"]),
-            k_cache=f16bits(L["k_cache"]).copy(), v_cache=f16bits(L["v_cache"]).copy()))
+            k_cache=None if L.get("k_cache") is None else f16bits(L["k_cache"]).copy(),
+            v_cache=f16bits(L["v_cache"]).copy()))
     return orc.OracleModel(
         hidden=cfg.hidden, n_heads=cfg.n_heads, inter=cfg.inter, vocab=cfg.vocab,
         sl_kv_heads=cfg.sl_kv_heads, sl_head_dim=cfg.sl_head_dim, full_head_dim=cfg.full_head_dim,
@@ -74,7 +75,7 @@ def oracle_model_from_device(orc, cfg, gm, blocks):
         sl_rot_pairs=cfg.sl_rot_pairs, full_rot_pairs=cfg.full_rot_pairs,
         sl_scale=cfg.sl_scale, full_scale=cfg.full_scale, eps=cfg.eps, softcap=cfg.softcap,
         embed=f16bits(gm.embed), final_norm=gm.final_norm.cpu().numpy(), layers=layers,
-        weight_format=int(getattr(gm, "weight_format", 0)))
+        weight_format=int(getattr(gm, "weight_format", 0)), kv_format=int(getattr(gm, "kv_format", 0)))
 
 
 def check_argmax(gpu_logits, gpu_argmax, ref_logits, tol_margin):

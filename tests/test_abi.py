@@ -71,6 +71,20 @@ def test_argument_checks_fail_before_launch():
     # a ring holds at least one 32-position tile
     assert L.flash_decode_ring(fake, fake, fake, 0, 16, 8, 256, 16, 8, pos, 1, 1,
                                C.c_float(1.0), fake, fake, ws, None) == q4.Q4_ESHAPE
+    # one-row full layers: D in {128, 512}, at most 64 rotated pairs, theta > 0, kw given and aligned
+    fv = L.flash_decode_full_vrow
+    ok = (fake, fake, 0, 200, 16, 512, fake, C.c_double(1e6), 64, pos, 1, 1, C.c_float(1.0), fake, fake, ws, None)
+    def call(**kw):
+        a = list(ok)
+        for k, v in kw.items():
+            a[{"D": 5, "kw": 6, "theta": 7, "rot": 8, "cap": 3}[k]] = v
+        return fv(*a)
+    assert call(D=256) == q4.Q4_ESHAPE
+    assert call(rot=65) == q4.Q4_ESHAPE
+    assert call(theta=C.c_double(0.0)) == q4.Q4_ESHAPE
+    assert call(kw=None) == q4.Q4_EINVAL
+    assert call(kw=odd) == q4.Q4_EALIGN
+    assert call(cap=100) == q4.Q4_ERANGE
 
 
 def test_decode_step_checks():
@@ -97,6 +111,18 @@ def test_decode_step_checks():
     assert L.decode_step(C.byref(m), bad, 1, 5, f, f, f, big, None) == q4.Q4_ERANGE
     assert L.decode_step_hidden(C.byref(m), f, C.c_size_t(16), 1, f, None) == q4.Q4_ENOSPACE
     assert L.decode_step_hidden(C.byref(m), f, big, 5, f, None) == q4.Q4_ESHAPE
+    # kv_format: 0 or 1; the one-row layout needs the V norm on full layers and
+    # does not need their K cache
+    m.kv_format = 2
+    assert L.decode_step(C.byref(m), tok, 1, 5, f, f, f, big, None) == q4.Q4_ESHAPE
+    m.kv_format = 1
+    lay[1].k_cache = None
+    assert L.decode_step(C.byref(m), bad, 1, 5, f, f, f, big, None) == q4.Q4_ERANGE   # passes the layer checks
+    lay[1].v_norm = 0
+    assert L.decode_step(C.byref(m), tok, 1, 5, f, f, f, big, None) == q4.Q4_EINVAL
+    m.kv_format = 0
+    assert L.decode_step(C.byref(m), tok, 1, 5, f, f, f, big, None) == q4.Q4_EINVAL  # K cache missing
+    lay[1].v_norm, lay[1].k_cache = 1, fake
     m.ring = cfg.window + 2      # a 4-row block needs R >= W + 3
     assert L.decode_step(C.byref(m), tok, 4, 5, f, f, f, big, None) == q4.Q4_ERANGE
     m.ring, m.window = 16, 8     # a ring holds at least one 32-position tile

@@ -13,7 +13,7 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda"
 
 
-def build_pair(orc, cfg, seed, ctx, gen_device="cpu", weights="q4"):
+def build_pair(orc, cfg, seed, ctx, gen_device="cpu", weights="q4", kv="pair"):
     blocks = {}
     opack, unpack = (orc.q4_pack, q4.q4_unpack) if weights == "q4" else (orc.q8_pack, q4.q8_unpack)
 
@@ -25,7 +25,7 @@ def build_pair(orc, cfg, seed, ctx, gen_device="cpu", weights="q4"):
         blocks.setdefault(l, {})[name] = ref
 
     gm = q4.build_decode_model(cfg, seed, ctx, device=DEV, pack_check=check, gen_device=gen_device,
-                               weights=weights)
+                               weights=weights, kv=kv)
     om = oracle_model_from_device(orc, cfg, gm, blocks)
     return gm, om
 
@@ -179,7 +179,7 @@ def sub_model(gm, layer_ids, cfg=None, scalars=None):
         if scalars is not None:
             L["layer_scalar"] = scalars[i]
         layers.append(L)
-    return q4.DecodeModel(cfg, layers, gm.embed, gm.final_norm, gm.weight_format)
+    return q4.DecodeModel(cfg, layers, gm.embed, gm.final_norm, gm.weight_format, gm.kv_format)
 
 
 def sub_oracle(om, layer_ids, scalars=None):
@@ -188,7 +188,7 @@ def sub_oracle(om, layer_ids, scalars=None):
     m.layers = []
     for i, l in enumerate(layer_ids):
         L = copy.copy(om.layers[l])
-        L.k_cache = L.k_cache.copy()
+        L.k_cache = None if L.k_cache is None else L.k_cache.copy()
         L.v_cache = L.v_cache.copy()
         if scalars is not None:
             L.layer_scalar = scalars[i]
