@@ -128,6 +128,15 @@ def time_attention(q4, torch):
         nb = ctx * 2048
         res[f"full_attention_ctx{ctx}"] = {"us": round(t * 1e6, 2), "bytes": nb,
                                           "GBps": round(nb / t / 1e9, 1), "frac": round(nb / t / 1e9 / PEAK_GBPS, 4)}
+    # the one-row layout over the same V rows: 1024 bytes per position
+    kw = synth.normal((512,), 0.1, synth.gen(3), mean=1.0).to("cuda")
+    for ctx in (32768, 131072):
+        t = time_graph_calls(torch, lambda i: q4.flash_decode_full_vrow(bufs[i % 6][0], bufs[i % 6][2], kw, 1e6,
+                                                                        64, ctx - 1, 1.0, ws=ws), 24)
+        nb = ctx * 1024
+        res[f"full_attention_vrow_ctx{ctx}"] = {"us": round(t * 1e6, 2), "bytes": nb,
+                                               "GBps": round(nb / t / 1e9, 1),
+                                               "frac": round(nb / t / 1e9 / PEAK_GBPS, 4)}
     del bufs
     q, k, v = (t.to("cuda") for t in synth.ring_inputs(100000, n_rows=1, n_rejected=4))
     ws = q4._fd_ws(1, 1, 16, 256, "cuda")
@@ -180,6 +189,21 @@ def time_int8_step(q4, torch, bytemodel, synth, toks, steps):
     torch.cuda.empty_cache()
     return {"ms_per_step": round(secs * 1e3 / steps, 4), "tokens_per_s": round(steps / secs, 2),
             "algorithmic_bytes": nb, "achieved_GBps": round(nb * steps / secs / 1e9, 1)}
+
+
+def time_vrow_steps(q4, torch, bytemodel, model, toks, steps, ctx_hi):
+    """The same step with the full layers caching only the V row (the key
+    formed from it): the bench model's layers and V caches, kv_format 1, at
+    positions 32767 and ctx_hi - 1."""
+    layers = [dict(L, k_cache=None) if L["is_full"] else L for L in model.layers]
+    mv = q4.DecodeModel(model.cfg, layers, model.embed, model.final_norm, 0, 1)
+    res = {}
+    for pos in (32767, ctx_hi - 1):
+        secs = time_steps(torch, mv, toks, pos, steps, 2)
+        nb = bytemodel.step_bytes(model.cfg, pos, kv_format=1)
+        res[f"ctx{pos + 1}"] = {"ms_per_step": round(secs * 1e3 / steps, 4), "tokens_per_s": round(steps / secs, 2),
+                                "algorithmic_bytes": nb, "achieved_GBps": round(nb * steps / secs / 1e9, 1)}
+    return res
 
 
 COPY_BYTES = 512 << 20
@@ -377,6 +401,8 @@ def main():
             log(f"ctx 131072: {extra['ctx131072']}; verify4: {extra['verify4_ctx32768']}")
             extra["attention_kernels"] = time_attention(q4, torch)
             log(f"attention kernels: {extra['attention_kernels']}")
+            extra["vrow_kv"] = time_vrow_steps(q4, torch, bytemodel, model, toks, k2, ctx_hi)
+            log(f"one-row full-layer KV: {extra['vrow_kv']}")
             extra["q8_gemv"] = time_q8_gemv(q4, torch)
             log(f"q8 (int8lin) gemv: {extra['q8_gemv']}")
             extra["int8_ctx32768"] = time_int8_step(q4, torch, bytemodel, synth, toks, k2)

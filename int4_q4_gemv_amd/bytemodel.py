@@ -7,7 +7,8 @@ Per unit:
     vocab path, tied head [262144, 3840]);
   * full-attention position: K and V rows of head_dim fp16 values, 2*2*D B
     (2,048 B at D = 512; Gemma-4-12B-CoreAI card, per-tier cost: a global pair
-    [8,1,1,C,512] is 16,384 B per token over 8 layers);
+    [8,1,1,C,512] is 16,384 B per token over 8 layers), or 2*D B when the
+    layer caches only the V row and forms the key from it;
   * sliding-window position: 2*2*D B per KV head, W positions per KV head.
 Activations, norm vectors and split-K partials are not counted (they are
 kilobytes and stay in L2/MALL).
@@ -34,8 +35,10 @@ def head_bytes(cfg: ModelConfig) -> int:
     return cfg.vocab * cfg.hidden * 2
 
 
-def full_pos_bytes(cfg: ModelConfig) -> int:
-    return 2 * 2 * cfg.full_head_dim
+def full_pos_bytes(cfg: ModelConfig, kv_format: int = 0) -> int:
+    """Bytes per full-attention position: the K and V rows, or only the V
+    row when the layer caches one row per position (kv_format 1)."""
+    return (2 if kv_format == 0 else 1) * 2 * cfg.full_head_dim
 
 
 def ring_call_bytes(cfg: ModelConfig, q_pos: int) -> int:
@@ -48,13 +51,13 @@ def n_full(cfg: ModelConfig) -> int:
     return sum(1 for l in range(cfg.n_layers) if cfg.is_full(l))
 
 
-def step_bytes(cfg: ModelConfig, pos: int, n_rows: int = 1) -> int:
+def step_bytes(cfg: ModelConfig, pos: int, n_rows: int = 1, kv_format: int = 0) -> int:
     """Algorithmic bytes of one decode step whose last row sits at ``pos``.
 
     Weights, head and KV are streamed once for all rows of a verify block."""
     nf = n_full(cfg)
     ns = cfg.n_layers - nf
-    return (weight_bytes(cfg) + head_bytes(cfg) + nf * (pos + 1) * full_pos_bytes(cfg)
+    return (weight_bytes(cfg) + head_bytes(cfg) + nf * (pos + 1) * full_pos_bytes(cfg, kv_format)
             + ns * ring_call_bytes(cfg, pos))
 
 
