@@ -285,6 +285,41 @@ q4_status decode_step_eager(const q4dec_model* m, const int32_t* tokens, int n, 
                             void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* prefill chunk                                                             */
+/* ------------------------------------------------------------------------ */
+/* Y[b][n] = sum_k (d * q)[n][k] * x[b][k] for the n <= 64 rows of a chunk, the
+ * product of the prefill path, on MFMA (the q4 layout as q4_gemv takes it;
+ * the scale enters the operand as an exact fp16 hi + lo split, sums are fp32).
+ * packed: device, from q4_pack(N, K).  x: device fp16 [n][K].  y: device fp32
+ * [n][N].  Requires |d * q| < 65504 (block absmax below 65504).
+ * Errors: Q4_EINVAL, Q4_ESHAPE (K % 32, n outside 1..64), Q4_EALIGN (pointers,
+ * K % 8), Q4_EHIP. */
+q4_status q4_gemm(const void* packed, int N, int K, const uint16_t* x, int n, float* y,
+                  void* stream);
+
+/* Workspace bytes for prefill_chunk (any n <= 64); 0 for an unsupported model. */
+size_t prefill_chunk_workspace_size(const q4dec_model* m);
+
+/* One prefill chunk: n <= 64 tokens at positions pos0 .. pos0 + n - 1 through
+ * the whole model in one pass (gemma-4-E4B-CoreAI card, Provenance and ring/:
+ * a second entry point beside the S = 1 decode takes 64-token prefill chunks,
+ * and the sliding ring holds the window plus one chunk; Gemma-4-12B-CoreAI
+ * card, "v5/ -- ring extent R = 2W": the slot rule stays causal for a block of
+ * rows while R >= W + rows - 1).  Every layer writes the K/V rows of all n
+ * rows into the caller's caches, then each row attends its causal, in-window
+ * positions as a decode row would; the products run on q4_gemm's kernel.
+ * Same model descriptor as decode_step (weight_format 0; kv_format 0 or 1).
+ * tokens: host int32 [n].  logits: device fp32 [vocab] of the LAST row, or
+ * NULL.  argmax: device int32 [1] (greedy id of the last row), or NULL.
+ * h_out: device fp32 [n][hidden], the residual stream of every row after the
+ * last layer, or NULL.  No alignment of pos0 is needed (every row's ring slot
+ * is written on its own).
+ * Errors: as decode_step with n in 1..64; Q4_ESHAPE for weight_format != 0. */
+q4_status prefill_chunk(const q4dec_model* m, const int32_t* tokens, int n, int pos0,
+                        float* logits, int32_t* argmax, float* h_out, void* ws,
+                        size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* speculative verify: greedy acceptance                                     */
 /* ------------------------------------------------------------------------ */
 /* The host half of one speculative verify block (host only, no device work).

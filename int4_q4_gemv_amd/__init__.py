@@ -125,6 +125,12 @@ def _declare(L):
     L.q4dec_release.restype = _i
     L.decode_step_hidden.restype = _i
     L.decode_step_hidden.argtypes = [C.POINTER(Model), _p, _sz, _i, _p, _p]
+    L.q4_gemm.restype = _i
+    L.q4_gemm.argtypes = [_p, _i, _i, _p, _i, _p, _p]
+    L.prefill_chunk_workspace_size.restype = _sz
+    L.prefill_chunk_workspace_size.argtypes = [C.POINTER(Model)]
+    L.prefill_chunk.restype = _i
+    L.prefill_chunk.argtypes = [C.POINTER(Model), _p, _i, _i, _p, _p, _p, _p, _sz, _p]
     L.q4_spec_accept.restype = _i
     L.q4_spec_accept.argtypes = [_p, _p, _i, _p, _p]
     L.q4_stream_read_sink_words.restype = _i
@@ -137,6 +143,7 @@ EXPORTS = ["q4dec_status_str", "q4dec_version", "q4_packed_bytes", "q4_pack", "q
            "q4_gemv", "q8_packed_bytes", "q8_pack", "q8_unpack", "q8_gemv", "flash_decode_workspace_size", "flash_decode_full",
            "flash_decode_full_vrow", "flash_decode_ring",
            "decode_step_workspace_size", "decode_step", "decode_step_hidden", "decode_step_eager",
+           "q4_gemm", "prefill_chunk_workspace_size", "prefill_chunk",
            "q4_spec_accept", "q4_stream_read_sink_words", "q4_stream_read", "q4dec_release"]
 
 
@@ -207,6 +214,18 @@ def q4_gemv(packed, N: int, K: int, x: torch.Tensor) -> torch.Tensor:
     """y[b, n] = sum_k W[n, k] x[b, k] for fp16 x [B, K]; fp32 y [B, N]."""
     x2 = x.reshape(-1, K)
     return Gemv(N, K, x2.shape[0], device=x.device)(packed, x2)
+
+
+def q4_gemm(packed, N: int, K: int, x: torch.Tensor, y: torch.Tensor | None = None) -> torch.Tensor:
+    """The prefill product: y[b, n] = sum_k W[n, k] x[b, k] for fp16 x [n <= 64, K]
+    on MFMA; fp32 y [n, N]."""
+    _need_cuda(packed, x)
+    x = x.reshape(-1, K).contiguous()
+    n = x.shape[0]
+    if y is None:
+        y = torch.empty((n, N), dtype=torch.float32, device=x.device)
+    _check("q4_gemm", lib().q4_gemm(_ptr(packed), N, K, _ptr(x), n, _ptr(y), _stream()))
+    return y
 
 
 # ----------------------------------------------------------- q8 int8lin ----
@@ -370,6 +389,34 @@ class DecodeModel:
         _check("decode_step", fn(C.byref(self.desc), tk, n, int(pos0), _ptr(logits), _ptr(argmax),
                                  _ptr(ws), ws.numel(), _stream()))
         return logits, argmax
+
+
+def _prefill(self, tokens, pos0: int, logits: torch.Tensor | None = None, argmax: torch.Tensor | None = None,
+             want_logits: bool = True, want_hidden: bool = False):
+    """One prefill chunk of len(tokens) <= 64 rows at positions pos0 ..:
+    returns (logits of the last row [vocab] or None, argmax [1], residual
+    stream of every row [n, hidden] or None)."""
+    toks = [int(t) for t in tokens]
+    n = len(toks)
+    dev = self.embed.device
+    if logits is None and want_logits:
+        logits = torch.empty(self.cfg.vocab, dtype=torch.float32, device=dev)
+    if argmax is None:
+        argmax = torch.empty(1, dtype=torch.int32, device=dev)
+    h = torch.empty((n, self.cfg.hidden), dtype=torch.float32, device=dev) if want_hidden else None
+    if getattr(self, "_chunk_ws", None) is None:
+        nb = int(lib().prefill_chunk_workspace_size(C.byref(self.desc)))
+        if nb == 0:
+            raise Q4Error("prefill_chunk_workspace_size", Q4_ESHAPE)
+        self._chunk_ws = torch.zeros(nb, dtype=torch.uint8, device=dev)
+    ws = self._chunk_ws
+    tk = (C.c_int32 * n)(*toks)
+    _check("prefill_chunk", lib().prefill_chunk(C.byref(self.desc), tk, n, int(pos0), _ptr(logits), _ptr(argmax),
+                                                _ptr(h), _ptr(ws), ws.numel(), _stream()))
+    return logits, argmax, h
+
+
+DecodeModel.prefill = _prefill
 
 
 def _hidden(self, n: int) -> torch.Tensor:

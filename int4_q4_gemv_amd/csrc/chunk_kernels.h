@@ -1,0 +1,305 @@
+// chunk_kernels.h -- the kernels of a prefill chunk: up to 64 rows (tokens at
+// consecutive positions) through the decoder in one pass (Gemma-4-12B-CoreAI
+// card, "v5/ -- ring extent R = 2W": a block of rows is written into the ring
+// before it is read, and the slot rule keeps it causal while R >= W + rows - 1;
+// gemma-4-E4B-CoreAI card, ring/: only written, causal, in-window slots are
+// attended).
+//
+// k_q4_gemm: Y[b][n] = sum_k x[b][k] * (d * q)[n][k] for the rows b < 64 of a
+// chunk, on v_mfma_f32_16x16x32_f16.  The weights stay in the q4 device layout
+// of pack_kernels.h: lane l of a wave-wide load holds row l & 15 and block
+// l >> 4 of a quad (16 rows x 4 blocks).  The MFMA's k index is permuted so
+// that every lane multiplies its own data: MFMA w of a quad takes, in lane
+// group g, elements 8w .. 8w+7 of block g (the A operand of lane (r, g) is
+// word w of its own 16 bytes), and the x operand of lane (c, g) is read at
+// the same columns, 128 q + 32 g + 8 w.  One MFMA thus spans four blocks with
+// four scales, so the scale goes into the operand: d * q is split exactly into
+// fp16 hi + lo (d has 11 significant bits and |q| <= 8, so d * q has at most 15
+// and its lowest bit is at least 2^-24; packed fp16 multiply and fma), and each
+// product is two MFMAs.  Sums are fp32 in the MFMA accumulators.  The chunk's
+// x rows are staged in LDS 512 columns at a time (direct global-to-LDS loads,
+// one 1 KB row per instruction, rows padded by 16 bytes).
+//
+// A workgroup is 4 waves; each wave owns 2 row tiles (32 rows) and all 64
+// chunk rows (4 column groups of 16), accumulating 2 x 4 MFMA tiles.  STORE:
+// the 4 waves take 128 consecutive rows, and blockIdx.y picks one of S runs of
+// K, written as S partial products side by side (the next kernel adds them in
+// order).  GATEUP: waves 0, 1 take 32 gate rows each and waves 2, 3 the same
+// rows of up; the epilogue writes fp16(gelu_tanh(gate) * up).
+//
+// Limits: the dequantised weights d * q must be finite in fp16 (block absmax
+// below 65504); the decode path, which scales in fp32, has no such limit.
+#pragma once
+#include "device_common.h"
+#include "gemv_kernels.h"
+#include "attn_kernels.h"
+
+namespace q4k {
+
+constexpr int kChunkRows = 64;                 // rows of a chunk
+constexpr int kGemmCQ = 4;                     // quads per staged x run (512 columns)
+constexpr int kGemmPitch = kGemmCQ * 128 + 8;  // halves per staged x row
+constexpr size_t kGemmLds = (size_t)kChunkRows * kGemmPitch * 2;
+
+// One matrix of a launch.  STORE launches may hold up to 3 (the q, k and v
+// projections), laid out along blockIdx.x from workgroup wg0 on; GATEUP holds
+// gate (seg[0]) and up (seg[1]) over the same rows.
+struct GemmSeg {
+  const u4v* codes;        // q4 device layout
+  const uint16_t* scales;
+  int N, T;                // rows, 16-row tiles
+  int wg0;                 // first workgroup (STORE)
+  int out_off;             // first output column (STORE)
+};
+
+struct GemmArgs {
+  GemmSeg seg[3];
+  int nseg;
+  int K, NQ;               // columns, quads per row
+  int NQs;                 // quads per run of K (blockIdx.y = run)
+  const uint16_t* x;       // fp16 [n][ldx], ldx >= K >= 8
+  int ldx, n;
+  float* y;                // STORE: run s at y + s * y_split: fp32 [n][ldy], columns out_off ..
+  int ldy;
+  long y_split;
+  uint16_t* a_out;         // GATEUP: fp16 [n][ld_a]
+  int ld_a;
+};
+
+template <int EPI>
+__global__ void __launch_bounds__(256) k_q4_gemm(GemmArgs a) {
+  extern __shared__ __align__(16) unsigned char smem_c[];
+  uint16_t* xs = reinterpret_cast<uint16_t*>(smem_c);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int r = lane & 15, g = lane >> 4;
+  const bool up = EPI == EPI_GATEUP && wave >= 2;
+  // the segment of this workgroup, selected without a dependent load
+  const GemmSeg s0 = a.seg[0], s1 = a.seg[1], s2 = a.seg[2];
+  int si = up ? 1 : 0;
+  if constexpr (EPI != EPI_GATEUP)
+    si = (a.nseg > 1 && (int)blockIdx.x >= s1.wg0 ? 1 : 0) + (a.nseg > 2 && (int)blockIdx.x >= s2.wg0 ? 1 : 0);
+  const GemmSeg sg = si == 0 ? s0 : (si == 1 ? s1 : s2);
+  const int bx = EPI == EPI_GATEUP ? (int)blockIdx.x : (int)blockIdx.x - sg.wg0;
+  const int tile0 = EPI == EPI_GATEUP ? bx * 4 + 2 * (wave & 1) : bx * 8 + 2 * wave;
+  const u4v* codes = sg.codes;
+  const uint16_t* scales = sg.scales;
+  // tiles past the matrix read tile 0 and are not stored
+  const int tA = tile0 < sg.T ? tile0 : 0, tB = tile0 + 1 < sg.T ? tile0 + 1 : 0;
+  const int q_begin = blockIdx.y * a.NQs, q_end = min(a.NQ, q_begin + a.NQs);
+
+  f4_t acc[2][4];
+#pragma unroll
+  for (int t = 0; t < 2; t++)
+#pragma unroll
+    for (int c = 0; c < 4; c++) acc[t][c] = (f4_t){0.f, 0.f, 0.f, 0.f};
+
+  for (int qc = q_begin; qc < q_end; qc += kGemmCQ) {
+    const int nq = min(kGemmCQ, q_end - qc);
+    // weights of this run: 2 tiles x nq quads, one 16-byte load and one
+    // scale per lane each
+    u4v cw[2][kGemmCQ];
+    uint16_t sw[2][kGemmCQ];
+#pragma unroll
+    for (int i = 0; i < kGemmCQ; i++) {
+      const int qi = qc + (i < nq ? i : 0);
+      const long oa = ((long)tA * a.NQ + qi) * 64 + lane, ob = ((long)tB * a.NQ + qi) * 64 + lane;
+      cw[0][i] = __builtin_nontemporal_load(codes + oa);
+      cw[1][i] = __builtin_nontemporal_load(codes + ob);
+      sw[0][i] = scales[oa];
+      sw[1][i] = scales[ob];
+    }
+    // x rows 16 wave .. +15, columns 128 qc + 8 lane (clamped into the row;
+    // columns past the run are never used; rows past n repeat row n - 1 and
+    // are not stored)
+    __syncthreads();                              // the previous run's reads are done
+#pragma unroll
+    for (int i = 0; i < 16; i++) {
+      const int b = 16 * wave + i;
+      const int bs = min(b, a.n - 1);
+      const int col = min(qc * 128 + lane * 8, a.K - 8);
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint32_t*>(a.x + (long)bs * a.ldx + col),
+                                       reinterpret_cast<uint32_t*>(xs + b * kGemmPitch), 16, 0, 0);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kGemmCQ; i++) {
+      if (i >= nq) break;                         // uniform
+#pragma unroll
+      for (int t = 0; t < 2; t++) {
+        const _Float16 d = __builtin_bit_cast(_Float16, sw[t][i]);
+        const h2_t d2 = {d, d};
+        const uint32_t qw[4] = {cw[t][i].x, cw[t][i].y, cw[t][i].z, cw[t][i].w};
+#pragma unroll
+        for (int w = 0; w < 4; w++) {
+          h2_t v0, v1, v2, v3;
+          dq_word(qw[w], v0, v1, v2, v3);
+          const h2_t h0 = v0 * d2, h1 = v1 * d2, h2 = v2 * d2, h3 = v3 * d2;
+          const h2_t l0 = __builtin_elementwise_fma(v0, d2, -h0), l1 = __builtin_elementwise_fma(v1, d2, -h1);
+          const h2_t l2 = __builtin_elementwise_fma(v2, d2, -h2), l3 = __builtin_elementwise_fma(v3, d2, -h3);
+          const h8_t hi = __builtin_shufflevector(__builtin_shufflevector(h0, h1, 0, 1, 2, 3),
+                                                  __builtin_shufflevector(h2, h3, 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
+          const h8_t lo = __builtin_shufflevector(__builtin_shufflevector(l0, l1, 0, 1, 2, 3),
+                                                  __builtin_shufflevector(l2, l3, 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+          for (int c = 0; c < 4; c++) {
+            const h8_t xb = *reinterpret_cast<const h8_t*>(xs + (16 * c + r) * kGemmPitch + i * 128 + 32 * g + 8 * w);
+            acc[t][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(hi, xb, acc[t][c], 0, 0, 0);
+            acc[t][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(lo, xb, acc[t][c], 0, 0, 0);
+          }
+        }
+      }
+    }
+  }
+  // lane (c, g) of tile t, column group cg holds rows 16 tile + 4 g + i of
+  // chunk row 16 cg + c
+  if constexpr (EPI == EPI_GATEUP) {
+    __syncthreads();                              // x reads done: reuse the LDS
+    f4_t* ex = reinterpret_cast<f4_t*>(smem_c);   // [2 waves][2 tiles][4 groups][64 lanes]
+    if (up) {
+#pragma unroll
+      for (int t = 0; t < 2; t++)
+#pragma unroll
+        for (int c = 0; c < 4; c++) ex[(((wave - 2) * 2 + t) * 4 + c) * 64 + lane] = acc[t][c];
+    }
+    __syncthreads();
+    if (!up) {
+#pragma unroll
+      for (int t = 0; t < 2; t++) {
+        const int tile = tile0 + t;
+        if (tile >= sg.T) continue;
+#pragma unroll
+        for (int c = 0; c < 4; c++) {
+          const int b = 16 * c + r;
+          const f4_t u = ex[((wave * 2 + t) * 4 + c) * 64 + lane];
+          if (b < a.n) {
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+              const int row = tile * 16 + 4 * g + i;
+              if (row < sg.N) a.a_out[(long)b * a.ld_a + row] = f2h(gelu_tanh(acc[t][c][i]) * u[i]);
+            }
+          }
+        }
+      }
+    }
+  } else {
+    float* yb = a.y + blockIdx.y * a.y_split + sg.out_off;
+#pragma unroll
+    for (int t = 0; t < 2; t++) {
+      const int tile = tile0 + t;
+      if (tile >= sg.T) continue;
+#pragma unroll
+      for (int c = 0; c < 4; c++) {
+        const int b = 16 * c + r;
+        if (b >= a.n) continue;
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          const int row = tile * 16 + 4 * g + i;
+          if (row < sg.N) yb[(long)b * a.ldy + row] = acc[t][c][i];
+        }
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------ embedding ----
+struct ChunkEmbedArgs {
+  const uint16_t* E;       // [vocab][H] fp16
+  int H;
+  float emb_scale;         // sqrt(H)
+  float* h;                // [n][H]
+  unsigned long long* best;  // [4] argmax slots of the head
+  int tokens[kChunkRows];
+};
+
+// One workgroup per row: h = fp32(E[token]) * sqrt(H); workgroup 0 also
+// clears the head's argmax slots.
+__global__ void __launch_bounds__(256) k_chunk_embed(ChunkEmbedArgs a) {
+  const int b = blockIdx.x;
+  if (b == 0 && threadIdx.x < 4) a.best[threadIdx.x] = 0ull;
+  const uint16_t* e = a.E + (long)a.tokens[b] * a.H;
+  float* h = a.h + (long)b * a.H;
+  for (int i = threadIdx.x; i < a.H; i += 256) h[i] = h2f(e[i]) * a.emb_scale;
+}
+
+// ------------------------------------------------------------ finishing ----
+// (cos, sin) of the RoPE angle pos * theta^(-2i/D) for pair i (i < rot_pairs;
+// (1, 0) beyond): the angle in fp64, reduced mod 2 pi in fp64, then fp32
+// sincos, as k_step_begin forms its table.
+Q4_DEV float2 rope_cs(int pos, int i, int D, double theta, int rot_pairs) {
+  if (i >= rot_pairs) return make_float2(1.0f, 0.0f);
+  const double ang = (double)pos * pow(theta, -2.0 * (double)i / (double)D);
+  const double k = rint(ang * 0.15915494309189535);
+  const float rr = (float)fma(-k, 6.283185307179586, ang);
+  float sn, cn;
+  sincosf(rr, &sn, &cn);
+  return make_float2(cn, sn);
+}
+
+struct ChunkFinArgs {
+  const float* qkv;        // [n][ldq]: q (Hq*D) | k (Hkv*D) | v (Hkv*D, sliding), ny runs y_split apart
+  int ldq, ny;
+  long y_split;
+  int Hq, Hkv;
+  int ring, R;             // ring layer: slot p mod R of KV head h at (h * R + slot) * D
+  int v_norm, vrow;        // vrow: a full layer keeps only the V row
+  const float* q_norm;
+  const float* k_norm;
+  double theta;
+  int rot_pairs;
+  float eps;
+  int pos0;
+  uint16_t* q16;           // [n][Hq][D]
+  uint16_t* kc;
+  uint16_t* vc;
+};
+
+// Grid (rows, Hq + 2 Hkv jobs), one wave each: query head j (per-head
+// RMSNorm with q_norm, RoPE) to q16; then for KV head h, job Hq + 2h the key
+// (k_norm, RoPE) and job Hq + 2h + 1 the value (the scale-free norm of V, or
+// of the raw k on a full layer, or V as it is), written to the caches at the
+// row's position.  The products' S runs are added in order first.
+template <int D>
+__global__ void __launch_bounds__(64) k_chunk_finish(ChunkFinArgs a) {
+  constexpr int FE = D / 64, FEH = fin_h<D>();
+  const int row = blockIdx.x, job = blockIdx.y;
+  const int lane = threadIdx.x;
+  const int pos = a.pos0 + row;
+  int kind, head;                                 // 0 q, 1 k, 2 v
+  if (job < a.Hq) { kind = 0; head = job; }
+  else { kind = 1 + ((job - a.Hq) & 1); head = (job - a.Hq) >> 1; }
+  if (kind == 1 && a.vrow) return;
+  const float* rr = a.qkv + (long)row * a.ldq;
+  long off;
+  if (kind == 0) off = (long)head * D;
+  else if (kind == 1 || !a.ring) off = (long)(a.Hq + head) * D;     // full: V from the raw k
+  else off = (long)(a.Hq + a.Hkv + head) * D;
+  float v[FE], t[FE];
+  fin_load<D>(v, rr + off);
+  for (int s = 1; s < a.ny; s++) {
+    fin_load<D>(t, rr + s * a.y_split + off);
+#pragma unroll
+    for (int e = 0; e < FE; e++) v[e] += t[e];
+  }
+  float wv[FE];
+#pragma unroll
+  for (int e = 0; e < FE; e++) wv[e] = 1.0f;
+  float2 cs[FEH];
+#pragma unroll
+  for (int e = 0; e < FEH; e++)
+    cs[e] = rope_cs(pos, D == 64 ? (lane & 31) : lane * FEH + e, D, a.theta, kind == 2 ? 0 : a.rot_pairs);
+  const long slot = a.ring ? ((long)head * a.R + pos % a.R) * D : (long)pos * D;
+  if (kind == 0) {
+    fin_load<D>(wv, a.q_norm);
+    finish_vals<D>(v, wv, true, true, cs, a.rot_pairs, a.eps, a.q16 + ((long)row * a.Hq + head) * D);
+  } else if (kind == 1) {
+    fin_load<D>(wv, a.k_norm);
+    finish_vals<D>(v, wv, true, true, cs, a.rot_pairs, a.eps, a.kc + slot);
+  } else if (a.v_norm) {
+    finish_vals<D>(v, wv, false, false, cs, a.rot_pairs, a.eps, a.vc + slot);
+  } else {
+    fin_store<D>(v, a.vc + slot);
+  }
+}
+
+}  // namespace q4k

@@ -13,6 +13,7 @@
 
 #include "../../include/q4dec.h"
 #include "attn_kernels.h"
+#include "chunk_kernels.h"
 #include "gemv_kernels.h"
 #include "pack_kernels.h"
 #include "q8_kernels.h"
@@ -131,6 +132,8 @@ q4_status set_attrs() {
   e = e != hipSuccess ? e : max_lds(&k_fd_partial<512>, (int)fd_lds_bytes<512>());
   e = e != hipSuccess ? e : max_lds(&k_fd_partial<128, true>, (int)fd_lds_bytes<128>());
   e = e != hipSuccess ? e : max_lds(&k_fd_partial<512, true>, (int)fd_lds_bytes<512>());
+  e = e != hipSuccess ? e : max_lds(&k_q4_gemm<EPI_STORE>, (int)kGemmLds);
+  e = e != hipSuccess ? e : max_lds(&k_q4_gemm<EPI_GATEUP>, (int)kGemmLds);
   e = e != hipSuccess ? e : gemv_attrs<1, 0>();
   e = e != hipSuccess ? e : gemv_attrs<4, 0>();
   e = e != hipSuccess ? e : gemv_attrs<1, 1>();
@@ -408,9 +411,9 @@ q4_status enqueue_layers(const q4dec_model* m, const StepLayout& L, const StepPt
   return launch_status();
 }
 
-q4_status check_model(const q4dec_model* m, int n, int pos0, const int32_t* tokens) {
+q4_status check_model(const q4dec_model* m, int n, int pos0, const int32_t* tokens, int max_rows = kMaxRows) {
   if (!m || !m->layers || !m->embed || !m->final_norm || !tokens) return Q4_EINVAL;
-  if (n < 1 || n > kMaxRows) return Q4_ESHAPE;
+  if (n < 1 || n > max_rows) return Q4_ESHAPE;
   if (!model_dims_ok(m)) return Q4_ESHAPE;
   if (!al16(m->embed) || !al16(m->final_norm)) return Q4_EALIGN;
   if (pos0 < 0) return Q4_ERANGE;
@@ -494,6 +497,235 @@ q4_status begin_step(const q4dec_model* m, const StepPtrs& P, const int32_t* tok
   b.rope_cs = P.rope; b.ns = m->sl_rot_pairs; b.nf = m->full_rot_pairs;
   b.Ds = m->sl_head_dim; b.Df = m->full_head_dim; b.theta_s = m->sl_theta; b.theta_f = m->full_theta;
   hipLaunchKernelGGL(k_step_begin, dim3(n), dim3(256), 0, st, b);
+  return launch_status();
+}
+
+
+// ------------------------------------------------------- prefill chunk ----
+constexpr int kChunkSplits = 8;       // attention splits per (row, KV head) of a chunk
+
+// A matrix product of a chunk: S runs of K (S <= 4: the partial products are
+// added by the norm or finishing kernel that reads them) chosen so that a
+// launch has about 256 workgroups.
+struct ChunkPlan {
+  int NQ, NQs, S;
+};
+
+ChunkPlan chunk_plan(int N, int K, int wgs_other = 0) {
+  ChunkPlan p{};
+  p.NQ = (int)ceil_div(K, 128);
+  const int wgs = (int)ceil_div(ceil_div(N, 16), 8) + wgs_other;
+  const int s = std::max(1, std::min(4, (int)ceil_div(256, wgs)));
+  p.NQs = (int)ceil_div(p.NQ, s);
+  p.S = (int)ceil_div(p.NQ, p.NQs);
+  return p;
+}
+
+struct ChunkLayout {
+  int qkv_ld, S_qkv_s, S_qkv_f, S_o_s, S_o_f, S_d, ymax;
+  size_t hA, hB, qkv, q16, o, y, a, xf, apart, best, total;
+};
+
+ChunkLayout chunk_layout(const q4dec_model* m) {
+  ChunkLayout L{};
+  const int H = m->hidden, I = m->inter, Hq = m->n_heads;
+  const int Ds = m->sl_head_dim, Df = m->full_head_dim, Hs = m->sl_kv_heads;
+  const int Dmax = std::max(Ds, Df);
+  const int R = kChunkRows;
+  L.qkv_ld = std::max(Hq * Ds + 2 * Hs * Ds, Hq * Df + Df);
+  // the q, k and v products share one launch: plan on their joint workgroups
+  L.S_qkv_s = chunk_plan(Hq * Ds + 2 * Hs * Ds, H).S;
+  L.S_qkv_f = chunk_plan(Hq * Df + Df, H).S;
+  L.S_o_s = chunk_plan(H, Hq * Ds).S;
+  L.S_o_f = chunk_plan(H, Hq * Df).S;
+  L.S_d = chunk_plan(H, I).S;
+  L.ymax = std::max(std::max(L.S_o_s, L.S_o_f), L.S_d);
+  const int Sq = std::max(L.S_qkv_s, L.S_qkv_f);
+  size_t off = 0;
+  auto take = [&](size_t bytes) { const size_t o = off; off = align256(off + bytes); return o; };
+  L.best = take(sizeof(unsigned long long) * 4);
+  L.hA = take(sizeof(float) * R * H);
+  L.hB = take(sizeof(float) * R * H);
+  L.qkv = take(sizeof(float) * Sq * R * L.qkv_ld);
+  L.q16 = take(sizeof(uint16_t) * R * Hq * Dmax);
+  L.o = take(sizeof(uint16_t) * R * Hq * Dmax);
+  L.y = take(sizeof(float) * L.ymax * R * H);
+  L.a = take(sizeof(uint16_t) * R * I);
+  L.xf = take(sizeof(uint16_t) * R * H);
+  const size_t apart_full = (size_t)R * kChunkSplits * Hq * (Df + 4);
+  const size_t apart_ring = (size_t)R * Hs * kChunkSplits * (Hq / Hs) * (Ds + 4);
+  L.apart = take(sizeof(float) * std::max(apart_full, apart_ring));
+  L.total = off;
+  return L;
+}
+
+void fill_gseg(GemmSeg& s, const void* packed, int N, int K, int wg0, int out_off) {
+  const int T = (int)ceil_div(N, 16), NQ = (int)ceil_div(K, 128);
+  s.codes = static_cast<const u4v*>(packed);
+  s.scales = reinterpret_cast<const uint16_t*>(static_cast<const uint8_t*>(packed) + (size_t)T * NQ * 64 * 16);
+  s.N = N; s.T = T; s.wg0 = wg0; s.out_off = out_off;
+}
+
+int gseg_wgs(const GemmSeg& s) { return (int)ceil_div(s.T, 8); }
+
+// One chunk of n rows at positions pos0 .. pos0 + n - 1 through the whole
+// model, launched eagerly: embedding; per layer the input norm, the q/k/v
+// products (one launch), q/k/v finishing with the cache writes of every row,
+// split-K attention and combine (the rows read the caches only), the output
+// product, the post-attention residual and pre-FF norm, gate/up with GELU * up,
+// the down product; then the final norm of every row and the head of the last.
+q4_status enqueue_chunk(const q4dec_model* m, const ChunkLayout& L, void* ws, const int32_t* tokens, int n,
+                        int pos0, float* logits, int32_t* argmax, hipStream_t st) {
+  uint8_t* wb = static_cast<uint8_t*>(ws);
+  float* hA = reinterpret_cast<float*>(wb + L.hA);
+  float* hB = reinterpret_cast<float*>(wb + L.hB);
+  float* qkv = reinterpret_cast<float*>(wb + L.qkv);
+  uint16_t* q16 = reinterpret_cast<uint16_t*>(wb + L.q16);
+  uint16_t* o16 = reinterpret_cast<uint16_t*>(wb + L.o);
+  float* y = reinterpret_cast<float*>(wb + L.y);
+  uint16_t* a16 = reinterpret_cast<uint16_t*>(wb + L.a);
+  uint16_t* xf = reinterpret_cast<uint16_t*>(wb + L.xf);
+  float* apart = reinterpret_cast<float*>(wb + L.apart);
+  unsigned long long* best = reinterpret_cast<unsigned long long*>(wb + L.best);
+  const int H = m->hidden, I = m->inter, Hq = m->n_heads;
+  {
+    ChunkEmbedArgs e{};
+    e.E = m->embed; e.H = H; e.emb_scale = std::sqrt((float)H); e.h = hA; e.best = best;
+    for (int i = 0; i < n; i++) e.tokens[i] = tokens[i];
+    hipLaunchKernelGGL(k_chunk_embed, dim3(n), dim3(256), 0, st, e);
+  }
+  auto gemm = [&](GemmArgs& g, int wgs, int S, bool gateup) {
+    if (gateup) hipLaunchKernelGGL(k_q4_gemm<EPI_GATEUP>, dim3(wgs, 1), dim3(256), kGemmLds, st, g);
+    else hipLaunchKernelGGL(k_q4_gemm<EPI_STORE>, dim3(wgs, S), dim3(256), kGemmLds, st, g);
+  };
+  for (int l = 0; l < m->n_layers; l++) {
+    const q4dec_layer& ly = m->layers[l];
+    const bool full = ly.is_full != 0;
+    const int D = full ? m->full_head_dim : m->sl_head_dim;
+    const int Hkv = full ? 1 : m->sl_kv_heads;
+    const int Sq = full ? L.S_qkv_f : L.S_qkv_s;
+    // ---- input norm (with the previous layer's post-FF residual), q/k/v products
+    {
+      NormIn ni{};
+      if (l == 0) { ni.h_src = hA; ni.y = nullptr; ni.w_post = nullptr; ni.scalar = 1.0f; ni.h_dst = nullptr; }
+      else {
+        const q4dec_layer& prev = m->layers[l - 1];
+        ni.h_src = hB; ni.y = y; ni.w_post = prev.post_ff_norm; ni.scalar = prev.layer_scalar; ni.h_dst = hA;
+        ni.ny = L.S_d; ni.y_split = (long)n * H;
+      }
+      ni.w_in = ly.attn_norm; ni.H = H; ni.eps = m->eps;
+      hipLaunchKernelGGL(k_norm_rows, dim3(n), dim3(512), 0, st, ni, xf);
+      GemmArgs g{};
+      int wg = 0;
+      fill_gseg(g.seg[0], ly.wq, Hq * D, H, wg, 0);
+      wg += gseg_wgs(g.seg[0]);
+      fill_gseg(g.seg[1], ly.wk, Hkv * D, H, wg, Hq * D);
+      wg += gseg_wgs(g.seg[1]);
+      g.nseg = 2;
+      if (!full) {
+        fill_gseg(g.seg[2], ly.wv, Hkv * D, H, wg, (Hq + Hkv) * D);
+        wg += gseg_wgs(g.seg[2]);
+        g.nseg = 3;
+      }
+      g.K = H; g.NQ = (int)ceil_div(H, 128); g.NQs = (int)ceil_div(g.NQ, Sq);
+      g.x = xf; g.ldx = H; g.n = n;
+      g.y = qkv; g.ldy = L.qkv_ld; g.y_split = (long)n * L.qkv_ld;
+      gemm(g, wg, Sq, false);
+    }
+    // ---- finishing: q to q16, K/V rows of every row into the caches
+    {
+      ChunkFinArgs f{};
+      f.qkv = qkv; f.ldq = L.qkv_ld; f.ny = Sq; f.y_split = (long)n * L.qkv_ld;
+      f.Hq = Hq; f.Hkv = Hkv; f.ring = full ? 0 : 1; f.R = m->ring;
+      f.v_norm = ly.v_norm; f.vrow = (full && m->kv_format == 1) ? 1 : 0;
+      f.q_norm = ly.q_norm; f.k_norm = ly.k_norm;
+      f.theta = full ? m->full_theta : m->sl_theta;
+      f.rot_pairs = full ? m->full_rot_pairs : m->sl_rot_pairs;
+      f.eps = m->eps; f.pos0 = pos0;
+      f.q16 = q16; f.kc = ly.k_cache; f.vc = ly.v_cache;
+      const dim3 grid(n, Hq + 2 * Hkv);
+      switch (D) {
+        case 64: hipLaunchKernelGGL(k_chunk_finish<64>, grid, dim3(64), 0, st, f); break;
+        case 128: hipLaunchKernelGGL(k_chunk_finish<128>, grid, dim3(64), 0, st, f); break;
+        case 256: hipLaunchKernelGGL(k_chunk_finish<256>, grid, dim3(64), 0, st, f); break;
+        default: hipLaunchKernelGGL(k_chunk_finish<512>, grid, dim3(64), 0, st, f); break;
+      }
+    }
+    // ---- attention over the caches (every row of the chunk is in them)
+    {
+      AttnArgs a{};
+      a.q = q16; a.k = ly.k_cache; a.v = ly.v_cache; a.seq_stride = 0;
+      a.Hq = Hq; a.Hkv = Hkv; a.GQ = Hq / Hkv;
+      a.ring = full ? 0 : 1; a.R = m->ring; a.W = m->window;
+      a.n_rows = n; a.S = kChunkSplits;
+      a.scale_log2 = (full ? m->full_scale : m->sl_scale) * 1.4426950408889634f;
+      a.sp = nullptr; a.part = apart;
+      a.fin_on = 0;
+      a.kvh_major = full ? 0 : 1;
+      if (full && m->kv_format == 1) {
+        a.vrow = 1; a.k = ly.v_cache; a.kw = ly.k_norm; a.theta = m->full_theta; a.krot = m->full_rot_pairs;
+      }
+      a.pos0[0] = pos0;
+      launch_fd(a, D, 1, nullptr, o16, st);
+    }
+    // ---- output projection
+    const int So = full ? L.S_o_f : L.S_o_s;
+    {
+      GemmArgs g{};
+      fill_gseg(g.seg[0], ly.wo, H, Hq * D, 0, 0);
+      g.nseg = 1;
+      g.K = Hq * D; g.NQ = (int)ceil_div(Hq * D, 128); g.NQs = (int)ceil_div(g.NQ, So);
+      g.x = o16; g.ldx = Hq * D; g.n = n;
+      g.y = y; g.ldy = H; g.y_split = (long)n * H;
+      gemm(g, gseg_wgs(g.seg[0]), So, false);
+    }
+    // ---- post-attention residual + pre-FF norm, gate/up with GELU * up
+    {
+      NormIn ni{};
+      ni.h_src = hA; ni.y = y; ni.ny = So; ni.y_split = (long)n * H;
+      ni.w_post = ly.post_attn_norm; ni.scalar = 1.0f;
+      ni.w_in = ly.pre_ff_norm; ni.h_dst = hB; ni.H = H; ni.eps = m->eps;
+      hipLaunchKernelGGL(k_norm_rows, dim3(n), dim3(512), 0, st, ni, xf);
+      GemmArgs g{};
+      fill_gseg(g.seg[0], ly.wg, I, H, 0, 0);
+      fill_gseg(g.seg[1], ly.wu, I, H, 0, 0);
+      g.nseg = 2;
+      g.K = H; g.NQ = (int)ceil_div(H, 128); g.NQs = g.NQ;
+      g.x = xf; g.ldx = H; g.n = n;
+      g.a_out = a16; g.ld_a = I;
+      gemm(g, (int)ceil_div(g.seg[0].T, 4), 1, true);
+    }
+    // ---- down projection
+    {
+      GemmArgs g{};
+      fill_gseg(g.seg[0], ly.wd, H, I, 0, 0);
+      g.nseg = 1;
+      g.K = I; g.NQ = (int)ceil_div(I, 128); g.NQs = (int)ceil_div(g.NQ, L.S_d);
+      g.x = a16; g.ldx = I; g.n = n;
+      g.y = y; g.ldy = H; g.y_split = (long)n * H;
+      gemm(g, gseg_wgs(g.seg[0]), L.S_d, false);
+    }
+  }
+  // ---- final norm of every row (the residual stream lands in hA), head of the last
+  {
+    const q4dec_layer& last = m->layers[m->n_layers - 1];
+    NormIn ni{};
+    ni.h_src = hB; ni.y = y; ni.ny = L.S_d; ni.y_split = (long)n * H;
+    ni.w_post = last.post_ff_norm; ni.scalar = last.layer_scalar;
+    ni.w_in = m->final_norm; ni.h_dst = hA; ni.H = H; ni.eps = m->eps;
+    hipLaunchKernelGGL(k_norm_rows, dim3(n), dim3(512), 0, st, ni, xf);
+  }
+  {
+    HeadArgs a{};
+    a.E = m->embed; a.x = xf + (size_t)(n - 1) * H; a.V = m->vocab; a.H = H; a.softcap = m->softcap;
+    a.logits = logits; a.best = best; a.n_rows = 1;
+    const int waves = 8192;
+    a.rows_per_wave = (int)std::max<long>(2, ceil_div(m->vocab, waves));
+    if (a.rows_per_wave & 1) a.rows_per_wave++;
+    const int grid = (int)ceil_div(ceil_div(m->vocab, a.rows_per_wave), 4);
+    hipLaunchKernelGGL((k_head<1>), dim3(grid), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(k_argmax_out, dim3(1), dim3(64), 0, st, best, 1, argmax);
+  }
   return launch_status();
 }
 
@@ -803,6 +1035,49 @@ q4_status decode_step(const q4dec_model* m, const int32_t* tokens, int n, int po
 q4_status decode_step_eager(const q4dec_model* m, const int32_t* tokens, int n, int pos0, float* logits,
                             int32_t* argmax, void* ws, size_t ws_bytes, void* stream) {
   return decode_step_impl(m, tokens, n, pos0, logits, argmax, ws, ws_bytes, stream, false);
+}
+
+q4_status q4_gemm(const void* packed, int N, int K, const uint16_t* x, int n, float* y, void* stream) {
+  if (!packed || !x || !y) return Q4_EINVAL;
+  if (N < 1 || K < 32 || K % 32 || n < 1 || n > kChunkRows) return Q4_ESHAPE;
+  if (!al16(packed) || !al16(x) || !al16(y) || K % 8) return Q4_EALIGN;
+  q4_status rc = set_attrs();
+  if (rc != Q4_OK) return rc;
+  GemmArgs g{};
+  fill_gseg(g.seg[0], packed, N, K, 0, 0);
+  g.nseg = 1;
+  g.K = K; g.NQ = (int)ceil_div(K, 128); g.NQs = g.NQ;
+  g.x = x; g.ldx = K; g.n = n;
+  g.y = y; g.ldy = N; g.y_split = 0;
+  hipLaunchKernelGGL(k_q4_gemm<EPI_STORE>, dim3(gseg_wgs(g.seg[0]), 1), dim3(256), kGemmLds, S(stream), g);
+  return launch_status();
+}
+
+size_t prefill_chunk_workspace_size(const q4dec_model* m) {
+  if (!m || !model_dims_ok(m)) return 0;
+  return chunk_layout(m).total;
+}
+
+q4_status prefill_chunk(const q4dec_model* m, const int32_t* tokens, int n, int pos0, float* logits,
+                        int32_t* argmax, float* h_out, void* ws, size_t ws_bytes, void* stream) {
+  q4_status rc = check_model(m, n, pos0, tokens, kChunkRows);
+  if (rc != Q4_OK) return rc;
+  if (m->weight_format != 0) return Q4_ESHAPE;          // the chunk products take q4 weights
+  if (!ws) return Q4_EINVAL;
+  if (!al16(ws) || (logits && !al16(logits))) return Q4_EALIGN;
+  const ChunkLayout L = chunk_layout(m);
+  if (ws_bytes < L.total) return Q4_ENOSPACE;
+  rc = set_attrs();
+  if (rc != Q4_OK) return rc;
+  hipStream_t st = S(stream);
+  rc = enqueue_chunk(m, L, ws, tokens, n, pos0, logits, argmax, st);
+  if (rc != Q4_OK) return rc;
+  if (h_out) {
+    const void* src = static_cast<const uint8_t*>(ws) + L.hA;
+    if (hipMemcpyAsync(h_out, src, sizeof(float) * n * m->hidden, hipMemcpyDeviceToDevice, st) != hipSuccess)
+      return Q4_EHIP;
+  }
+  return Q4_OK;
 }
 
 q4_status q4_spec_accept(const int32_t* block, const int32_t* argmax, int n, int32_t* emitted,
