@@ -9,7 +9,7 @@ at 12B shapes, timed live with HIP events on its stream), context-131072 and
 width-4 verify figures, and the CPU oracle timed on the host cores on a
 bounded sample.
 
-  python bench.py [--gpus 1] [--steps K] [--warmup W] [--mode full|gemv|step]
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--mode full|gemv|step|traffic|prefill]
 """
 import argparse
 import json
@@ -28,7 +28,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--mode", default="full", choices=["full", "gemv", "step", "traffic"])
+    ap.add_argument("--mode", default="full", choices=["full", "gemv", "step", "traffic", "prefill"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     return ap.parse_args()
 
@@ -206,6 +206,51 @@ def time_vrow_steps(q4, torch, bytemodel, model, toks, steps, ctx_hi):
     return res
 
 
+def time_prefill(q4, torch, bytemodel, model, reps=3):
+    """Prefill chunks of 64 tokens on the bench model (the caches are those
+    of the decode figures): a chunk at positions 0 .. 63 and one ending at
+    position 32767 (every row attends up to 32K positions on the full
+    layers), each timed over `reps` eager calls between HIP events.  Bytes:
+    the weights once per chunk plus each row's attended KV."""
+    from int4_q4_gemv_amd import synth
+    cfg = model.cfg
+    toks = [int(t) for t in synth.tokens(cfg, 64, 9)]
+    res = {}
+    for name, pos0 in (("pos0", 0), ("ctx32768", 32768 - 64)):
+        model.prefill(toks, pos0, want_logits=False)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            model.prefill(toks, pos0, want_logits=False)
+        e1.record()
+        e1.synchronize()
+        secs = e0.elapsed_time(e1) * 1e-3 / reps
+        kv = sum(bytemodel.step_bytes(cfg, pos0 + i) - bytemodel.weight_bytes(cfg) - bytemodel.head_bytes(cfg)
+                 for i in range(64))
+        nb = bytemodel.weight_bytes(cfg) + bytemodel.head_bytes(cfg) + kv
+        res[name] = {"ms_per_chunk": round(secs * 1e3, 3), "tokens_per_s": round(64 / secs, 1),
+                     "algorithmic_bytes": nb, "achieved_GBps": round(nb / secs / 1e9, 1)}
+    return res
+
+
+def time_gemm(q4, torch, N=15360, K=3840, n=64, copies=16, launches=48):
+    """The chunk product alone at the gate/up shape with 64 rows (16 packed
+    copies rotated, above the last-level cache), as q4_gemm launches it (one
+    run of K).  Work: 2 n N K flops; bytes: the q4 weights."""
+    gen = torch.Generator(device="cuda").manual_seed(31)
+    w = torch.randn(N, K, device="cuda", generator=gen) * 0.02
+    mats = [q4.q4_pack(w) for _ in range(copies)]
+    del w
+    x = torch.randn(n, K, device="cuda", generator=gen).half()
+    y = torch.empty(n, N, device="cuda")
+    avg = time_graph_calls(torch, lambda i: q4.q4_gemm(mats[i % copies], N, K, x, y), launches)
+    del mats
+    nb = N * K // 32 * 18
+    return {"us": round(avg * 1e6, 2), "TFLOPs": round(2 * n * N * K / avg / 1e12, 1),
+            "GBps": round(nb / avg / 1e9, 1), "shape": f"{N}x{K}, {n} rows"}
+
+
 COPY_BYTES = 512 << 20
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "q4_gemv_15360x3840_traffic.txt")
 GEMV_SOURCES = ("int4_q4_gemv_amd/csrc/gemv_kernels.h", "int4_q4_gemv_amd/csrc/device_common.h",
@@ -363,6 +408,9 @@ def main():
             print(json.dumps({"mode": "traffic", "copy_bytes": COPY_BYTES,
                               "gemv_source_sha256_16": gemv_source_hash()}))
             return
+        if args.mode == "prefill":
+            print(json.dumps({"mode": "prefill", "prefill64": time_prefill(q4, torch, bytemodel, model)}))
+            return
         if args.mode in ("full", "gemv"):
             avg_s, launches, nbytes = time_gemv(q4, torch, model)
             ach = nbytes / avg_s / 1e9
@@ -403,6 +451,10 @@ def main():
             log(f"attention kernels: {extra['attention_kernels']}")
             extra["vrow_kv"] = time_vrow_steps(q4, torch, bytemodel, model, toks, k2, ctx_hi)
             log(f"one-row full-layer KV: {extra['vrow_kv']}")
+            extra["prefill64"] = time_prefill(q4, torch, bytemodel, model)
+            log(f"prefill chunks: {extra['prefill64']}")
+            extra["chunk_gemm"] = time_gemm(q4, torch)
+            log(f"chunk product: {extra['chunk_gemm']}")
             extra["q8_gemv"] = time_q8_gemv(q4, torch)
             log(f"q8 (int8lin) gemv: {extra['q8_gemv']}")
             extra["int8_ctx32768"] = time_int8_step(q4, torch, bytemodel, synth, toks, k2)

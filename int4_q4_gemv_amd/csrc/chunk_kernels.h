@@ -20,12 +20,12 @@
 // x rows are staged in LDS 512 columns at a time (direct global-to-LDS loads,
 // one 1 KB row per instruction, rows padded by 16 bytes).
 //
-// A workgroup is 4 waves; each wave owns 2 row tiles (32 rows) and all 64
-// chunk rows (4 column groups of 16), accumulating 2 x 4 MFMA tiles.  STORE:
-// the 4 waves take 128 consecutive rows, and blockIdx.y picks one of S runs of
+// A workgroup is 4 waves; each wave owns TPW row tiles and all 64 chunk rows
+// (4 column groups of 16), accumulating TPW x 4 MFMA tiles.  STORE: the 4
+// waves take 64 TPW consecutive rows, and blockIdx.y picks one of S runs of
 // K, written as S partial products side by side (the next kernel adds them in
-// order).  GATEUP: waves 0, 1 take 32 gate rows each and waves 2, 3 the same
-// rows of up; the epilogue writes fp16(gelu_tanh(gate) * up).
+// order).  GATEUP: waves 0, 1 take 16 TPW gate rows each and waves 2, 3 the
+// same rows of up; the epilogue writes fp16(gelu_tanh(gate) * up).
 //
 // Limits: the dequantised weights d * q must be finite in fp16 (block absmax
 // below 65504); the decode path, which scales in fp32, has no such limit.
@@ -66,8 +66,16 @@ struct GemmArgs {
   int ld_a;
 };
 
-template <int EPI>
+// TPW: 16-row tiles per wave (STORE: 4 TPW x 16 rows per workgroup; GATEUP:
+// the gate waves 0, 1 and the up waves 2, 3 on the same 32 TPW rows).  The K
+// loop is pipelined over runs of kGemmCQ quads: the weights and x rows of run
+// r + 1 are loaded into registers while run r is computed from LDS, and the
+// x rows are written to LDS after it.  (Global-to-LDS loads of the next run
+// would make the compiler wait for them before every LDS read of the
+// current one, as it cannot tell the two apart.)
+template <int EPI, int TPW>
 __global__ void __launch_bounds__(256) k_q4_gemm(GemmArgs a) {
+  constexpr int CQ = kGemmCQ;
   extern __shared__ __align__(16) unsigned char smem_c[];
   uint16_t* xs = reinterpret_cast<uint16_t*>(smem_c);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -80,53 +88,64 @@ __global__ void __launch_bounds__(256) k_q4_gemm(GemmArgs a) {
     si = (a.nseg > 1 && (int)blockIdx.x >= s1.wg0 ? 1 : 0) + (a.nseg > 2 && (int)blockIdx.x >= s2.wg0 ? 1 : 0);
   const GemmSeg sg = si == 0 ? s0 : (si == 1 ? s1 : s2);
   const int bx = EPI == EPI_GATEUP ? (int)blockIdx.x : (int)blockIdx.x - sg.wg0;
-  const int tile0 = EPI == EPI_GATEUP ? bx * 4 + 2 * (wave & 1) : bx * 8 + 2 * wave;
+  const int tile0 = EPI == EPI_GATEUP ? (bx * 2 + (wave & 1)) * TPW : (bx * 4 + wave) * TPW;
   const u4v* codes = sg.codes;
   const uint16_t* scales = sg.scales;
   // tiles past the matrix read tile 0 and are not stored
-  const int tA = tile0 < sg.T ? tile0 : 0, tB = tile0 + 1 < sg.T ? tile0 + 1 : 0;
+  int tl[TPW];
+#pragma unroll
+  for (int t = 0; t < TPW; t++) tl[t] = tile0 + t < sg.T ? tile0 + t : 0;
   const int q_begin = blockIdx.y * a.NQs, q_end = min(a.NQ, q_begin + a.NQs);
 
-  f4_t acc[2][4];
+  f4_t acc[TPW][4];
 #pragma unroll
-  for (int t = 0; t < 2; t++)
+  for (int t = 0; t < TPW; t++)
 #pragma unroll
     for (int c = 0; c < 4; c++) acc[t][c] = (f4_t){0.f, 0.f, 0.f, 0.f};
 
-  for (int qc = q_begin; qc < q_end; qc += kGemmCQ) {
-    const int nq = min(kGemmCQ, q_end - qc);
-    // weights of this run: 2 tiles x nq quads, one 16-byte load and one
-    // scale per lane each
-    u4v cw[2][kGemmCQ];
-    uint16_t sw[2][kGemmCQ];
+  // one run: the weights (TPW tiles x CQ quads, a 16-byte load and a scale
+  // per lane each; quads past the run reload the run's first) and the x rows
+  // 16 wave .. +15 at columns 128 qc + 8 lane (clamped into the row; rows
+  // past n repeat row n - 1; neither is used)
+  auto load_run = [&](int qc, u4v (&cw)[TPW][CQ], uint16_t (&sw)[TPW][CQ], u4v (&xr)[16]) {
+    const int nq = min(CQ, q_end - qc);
 #pragma unroll
-    for (int i = 0; i < kGemmCQ; i++) {
+    for (int i = 0; i < CQ; i++) {
       const int qi = qc + (i < nq ? i : 0);
-      const long oa = ((long)tA * a.NQ + qi) * 64 + lane, ob = ((long)tB * a.NQ + qi) * 64 + lane;
-      cw[0][i] = __builtin_nontemporal_load(codes + oa);
-      cw[1][i] = __builtin_nontemporal_load(codes + ob);
-      sw[0][i] = scales[oa];
-      sw[1][i] = scales[ob];
+#pragma unroll
+      for (int t = 0; t < TPW; t++) {
+        const long o = ((long)tl[t] * a.NQ + qi) * 64 + lane;
+        cw[t][i] = __builtin_nontemporal_load(codes + o);
+        sw[t][i] = scales[o];
+      }
     }
-    // x rows 16 wave .. +15, columns 128 qc + 8 lane (clamped into the row;
-    // columns past the run are never used; rows past n repeat row n - 1 and
-    // are not stored)
-    __syncthreads();                              // the previous run's reads are done
+    const int col = min(qc * 128 + lane * 8, a.K - 8);
 #pragma unroll
     for (int i = 0; i < 16; i++) {
-      const int b = 16 * wave + i;
-      const int bs = min(b, a.n - 1);
-      const int col = min(qc * 128 + lane * 8, a.K - 8);
-      __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint32_t*>(a.x + (long)bs * a.ldx + col),
-                                       reinterpret_cast<uint32_t*>(xs + b * kGemmPitch), 16, 0, 0);
+      const int bs = min(16 * wave + i, a.n - 1);
+      xr[i] = *reinterpret_cast<const u4v*>(a.x + (long)bs * a.ldx + col);
     }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+  };
+  auto store_x = [&](const u4v (&xr)[16]) {
 #pragma unroll
-    for (int i = 0; i < kGemmCQ; i++) {
-      if (i >= nq) break;                         // uniform
+    for (int i = 0; i < 16; i++) *reinterpret_cast<u4v*>(xs + (16 * wave + i) * kGemmPitch + lane * 8) = xr[i];
+  };
+  u4v cw[TPW][CQ], cn[TPW][CQ], xr[16];
+  uint16_t sw[TPW][CQ], sn[TPW][CQ];
+  if (q_begin < q_end) {
+    load_run(q_begin, cw, sw, xr);
+    store_x(xr);
+  }
+  __syncthreads();
+  for (int qc = q_begin; qc < q_end; qc += CQ) {
+    const int nq = min(CQ, q_end - qc);
+    const bool more = qc + CQ < q_end;             // uniform
+    if (more) load_run(qc + CQ, cn, sn, xr);
 #pragma unroll
-      for (int t = 0; t < 2; t++) {
+    for (int i = 0; i < CQ; i++) {
+      if (i >= nq) break;                          // uniform
+#pragma unroll
+      for (int t = 0; t < TPW; t++) {
         const _Float16 d = __builtin_bit_cast(_Float16, sw[t][i]);
         const h2_t d2 = {d, d};
         const uint32_t qw[4] = {cw[t][i].x, cw[t][i].y, cw[t][i].z, cw[t][i].w};
@@ -141,37 +160,49 @@ __global__ void __launch_bounds__(256) k_q4_gemm(GemmArgs a) {
                                                   __builtin_shufflevector(h2, h3, 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
           const h8_t lo = __builtin_shufflevector(__builtin_shufflevector(l0, l1, 0, 1, 2, 3),
                                                   __builtin_shufflevector(l2, l3, 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
+          h8_t xb[4];
 #pragma unroll
-          for (int c = 0; c < 4; c++) {
-            const h8_t xb = *reinterpret_cast<const h8_t*>(xs + (16 * c + r) * kGemmPitch + i * 128 + 32 * g + 8 * w);
-            acc[t][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(hi, xb, acc[t][c], 0, 0, 0);
-            acc[t][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(lo, xb, acc[t][c], 0, 0, 0);
-          }
+          for (int c = 0; c < 4; c++)
+            xb[c] = *reinterpret_cast<const h8_t*>(xs + (16 * c + r) * kGemmPitch + i * 128 + 32 * g + 8 * w);
+          // the hi products of the 4 column groups, then the lo ones: no
+          // MFMA waits for the one just issued
+#pragma unroll
+          for (int c = 0; c < 4; c++) acc[t][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(hi, xb[c], acc[t][c], 0, 0, 0);
+#pragma unroll
+          for (int c = 0; c < 4; c++) acc[t][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(lo, xb[c], acc[t][c], 0, 0, 0);
         }
       }
     }
+    __syncthreads();                               // every wave is done with this run's x
+    if (more) {
+      store_x(xr);
+#pragma unroll
+      for (int t = 0; t < TPW; t++)
+#pragma unroll
+        for (int i = 0; i < CQ; i++) { cw[t][i] = cn[t][i]; sw[t][i] = sn[t][i]; }
+    }
+    __syncthreads();
   }
   // lane (c, g) of tile t, column group cg holds rows 16 tile + 4 g + i of
   // chunk row 16 cg + c
   if constexpr (EPI == EPI_GATEUP) {
-    __syncthreads();                              // x reads done: reuse the LDS
-    f4_t* ex = reinterpret_cast<f4_t*>(smem_c);   // [2 waves][2 tiles][4 groups][64 lanes]
+    f4_t* ex = reinterpret_cast<f4_t*>(smem_c);   // [2 waves][TPW tiles][4 groups][64 lanes]
     if (up) {
 #pragma unroll
-      for (int t = 0; t < 2; t++)
+      for (int t = 0; t < TPW; t++)
 #pragma unroll
-        for (int c = 0; c < 4; c++) ex[(((wave - 2) * 2 + t) * 4 + c) * 64 + lane] = acc[t][c];
+        for (int c = 0; c < 4; c++) ex[(((wave - 2) * TPW + t) * 4 + c) * 64 + lane] = acc[t][c];
     }
     __syncthreads();
     if (!up) {
 #pragma unroll
-      for (int t = 0; t < 2; t++) {
+      for (int t = 0; t < TPW; t++) {
         const int tile = tile0 + t;
         if (tile >= sg.T) continue;
 #pragma unroll
         for (int c = 0; c < 4; c++) {
           const int b = 16 * c + r;
-          const f4_t u = ex[((wave * 2 + t) * 4 + c) * 64 + lane];
+          const f4_t u = ex[((wave * TPW + t) * 4 + c) * 64 + lane];
           if (b < a.n) {
 #pragma unroll
             for (int i = 0; i < 4; i++) {
@@ -185,7 +216,7 @@ __global__ void __launch_bounds__(256) k_q4_gemm(GemmArgs a) {
   } else {
     float* yb = a.y + blockIdx.y * a.y_split + sg.out_off;
 #pragma unroll
-    for (int t = 0; t < 2; t++) {
+    for (int t = 0; t < TPW; t++) {
       const int tile = tile0 + t;
       if (tile >= sg.T) continue;
 #pragma unroll

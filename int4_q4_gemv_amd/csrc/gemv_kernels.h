@@ -47,7 +47,8 @@ struct GemvSeg {
 
 // x = fp16(RMSNorm(h_new) * w_in), h_new = (h_src + RMSNorm(y) * w_post) * scalar
 // (y == NULL: h_new = h_src * scalar), where y is the sum, in order, of ny
-// (<= 4) partial products laid y_split floats apart.  h_new goes to h_dst.
+// (<= MAXY of the kernel) partial products laid y_split floats apart.  h_new
+// goes to h_dst.
 struct NormIn {
   const float* h_src;
   const float* y;
@@ -354,6 +355,7 @@ __global__ void __launch_bounds__((B == 1 || FMT == 1) ? 1024 : 512) k_q4_gemv(G
 // move the row in a quarter of the instructions).  Partial products past ny
 // alias the first and are added times 0, so no load waits for another; the
 // two mean squares are block sums in a fixed order.
+template <int MAXY>
 __global__ void __launch_bounds__(512) k_norm_rows(NormIn p, uint16_t* x) {
   constexpr int NT = 512, C = 4096 / 4 / NT;
   __shared__ float nred[16];
@@ -363,37 +365,38 @@ __global__ void __launch_bounds__(512) k_norm_rows(NormIn p, uint16_t* x) {
   const float4* hs = reinterpret_cast<const float4*>(p.h_src + (long)b * H);
   const float4* y0 = y ? reinterpret_cast<const float4*>(y) : hs;
   const long ys4 = p.y_split / 4;
-  const float4* y1 = p.ny > 1 ? y0 + ys4 : y0;
-  const float4* y2 = p.ny > 2 ? y0 + 2 * ys4 : y0;
-  const float4* y3 = p.ny > 3 ? y0 + 3 * ys4 : y0;
+  const float4* yp[MAXY];
+  float mj[MAXY];
+#pragma unroll
+  for (int j = 0; j < MAXY; j++) {
+    yp[j] = p.ny > j ? y0 + j * ys4 : y0;
+    mj[j] = p.ny > j ? 1.f : 0.f;
+  }
   const float4* wp4 = reinterpret_cast<const float4*>(y ? p.w_post : p.w_in);
   const float4* wi4 = reinterpret_cast<const float4*>(p.w_in);
-  const float m1 = p.ny > 1 ? 1.f : 0.f, m2 = p.ny > 2 ? 1.f : 0.f, m3 = p.ny > 3 ? 1.f : 0.f;
-  float4 hv[C], a0[C], a1[C], a2[C], a3[C], wp[C], wi[C];
+  float4 hv[C], ay[MAXY][C], wp[C], wi[C];
 #pragma unroll
   for (int c = 0; c < C; c++) {
     const int k = min(tid + NT * c, n4 - 1);
     hv[c] = hs[k];
-    a0[c] = y0[k];
-    a1[c] = y1[k];
-    a2[c] = y2[k];
-    a3[c] = y3[k];
+#pragma unroll
+    for (int j = 0; j < MAXY; j++) ay[j][c] = yp[j][k];
     wp[c] = wp4[k];
     wi[c] = wi4[k];
   }
   __builtin_amdgcn_sched_barrier(0);
-  // partial sums in the order ((a0 + a1) + a2) + a3; out-of-range elements 0
+  // partial sums in the order ((a0 + a1) + a2) + ..; out-of-range elements 0
   float yv[C][4], hh[C][4];
   float ss = 0.f;
 #pragma unroll
   for (int c = 0; c < C; c++) {
     const bool in = tid + NT * c < n4;
-    const float A0[4] = {a0[c].x, a0[c].y, a0[c].z, a0[c].w}, A1[4] = {a1[c].x, a1[c].y, a1[c].z, a1[c].w};
-    const float A2[4] = {a2[c].x, a2[c].y, a2[c].z, a2[c].w}, A3[4] = {a3[c].x, a3[c].y, a3[c].z, a3[c].w};
     const float HV[4] = {hv[c].x, hv[c].y, hv[c].z, hv[c].w};
 #pragma unroll
     for (int e = 0; e < 4; e++) {
-      const float v = ((A0[e] + m1 * A1[e]) + m2 * A2[e]) + m3 * A3[e];
+      float v = ay[0][c][e];
+#pragma unroll
+      for (int j = 1; j < MAXY; j++) v = v + mj[j] * ay[j][c][e];
       yv[c][e] = (y && in) ? v : 0.f;
       hh[c][e] = in ? HV[e] : 0.f;
       ss += yv[c][e] * yv[c][e];

@@ -132,8 +132,9 @@ q4_status set_attrs() {
   e = e != hipSuccess ? e : max_lds(&k_fd_partial<512>, (int)fd_lds_bytes<512>());
   e = e != hipSuccess ? e : max_lds(&k_fd_partial<128, true>, (int)fd_lds_bytes<128>());
   e = e != hipSuccess ? e : max_lds(&k_fd_partial<512, true>, (int)fd_lds_bytes<512>());
-  e = e != hipSuccess ? e : max_lds(&k_q4_gemm<EPI_STORE>, (int)kGemmLds);
-  e = e != hipSuccess ? e : max_lds(&k_q4_gemm<EPI_GATEUP>, (int)kGemmLds);
+  e = e != hipSuccess ? e : max_lds(&k_q4_gemm<EPI_STORE, 1>, (int)kGemmLds);
+  e = e != hipSuccess ? e : max_lds(&k_q4_gemm<EPI_STORE, 2>, (int)kGemmLds);
+  e = e != hipSuccess ? e : max_lds(&k_q4_gemm<EPI_GATEUP, 1>, (int)kGemmLds);
   e = e != hipSuccess ? e : gemv_attrs<1, 0>();
   e = e != hipSuccess ? e : gemv_attrs<4, 0>();
   e = e != hipSuccess ? e : gemv_attrs<1, 1>();
@@ -316,7 +317,7 @@ q4_status enqueue_layers(const q4dec_model* m, const StepLayout& L, const StepPt
         ni.ny = L.p_d.S; ni.y_split = (long)n * H;
       }
       ni.w_in = ly.attn_norm; ni.H = H; ni.eps = m->eps;
-      hipLaunchKernelGGL(k_norm_rows, dim3(n), dim3(512), 0, st, ni, P.xf);
+      hipLaunchKernelGGL(k_norm_rows<4>, dim3(n), dim3(512), 0, st, ni, P.xf);
       a.K = H; a.NQ = pl.NQ; a.W = pl.W; a.NQs = pl.NQs;
       a.x = P.xf; a.ldx = H;
       a.y = P.qkv; a.ldy = L.qkv_ld; a.n_rows = n;
@@ -367,7 +368,7 @@ q4_status enqueue_layers(const q4dec_model* m, const StepLayout& L, const StepPt
       ni.h_src = P.hA; ni.y = P.y; ni.ny = (full ? L.p_o_f : L.p_o_s).S; ni.y_split = (long)n * H;
       ni.w_post = ly.post_attn_norm; ni.scalar = 1.0f;
       ni.w_in = ly.pre_ff_norm; ni.h_dst = P.hB; ni.H = H; ni.eps = m->eps;
-      hipLaunchKernelGGL(k_norm_rows, dim3(n), dim3(512), 0, st, ni, P.xf);
+      hipLaunchKernelGGL(k_norm_rows<4>, dim3(n), dim3(512), 0, st, ni, P.xf);
       a.K = H; a.NQ = pl.NQ; a.W = pl.W; a.NQs = pl.NQs;
       a.x = P.xf; a.ldx = H;
       a.a_out = P.a; a.inter = I; a.n_rows = n;
@@ -395,7 +396,7 @@ q4_status enqueue_layers(const q4dec_model* m, const StepLayout& L, const StepPt
     ni.h_src = P.hB; ni.y = P.y; ni.ny = L.p_d.S; ni.y_split = (long)n * H;
     ni.w_post = last.post_ff_norm; ni.scalar = last.layer_scalar;
     ni.w_in = m->final_norm; ni.h_dst = P.hA; ni.H = H; ni.eps = m->eps;
-    hipLaunchKernelGGL(k_norm_rows, dim3(n), dim3(512), 0, st, ni, P.xf);
+    hipLaunchKernelGGL(k_norm_rows<4>, dim3(n), dim3(512), 0, st, ni, P.xf);
   }
   {
     HeadArgs a{};
@@ -504,25 +505,29 @@ q4_status begin_step(const q4dec_model* m, const StepPtrs& P, const int32_t* tok
 // ------------------------------------------------------- prefill chunk ----
 constexpr int kChunkSplits = 8;       // attention splits per (row, KV head) of a chunk
 
-// A matrix product of a chunk: S runs of K (S <= 4: the partial products are
-// added by the norm or finishing kernel that reads them) chosen so that a
-// launch has about 256 workgroups.
+// A matrix product of a chunk: one 16-row tile per wave and S runs of K
+// (S <= max_s; S > 1 writes partial products that the norm or finishing
+// kernel reading them adds), chosen so that a launch has about 512
+// workgroups: two per CU (x run in LDS 66.5 KB, 152 VGPRs), so that one
+// workgroup's MFMAs run while the other waits for its next run.
 struct ChunkPlan {
-  int NQ, NQs, S;
+  int NQ, NQs, S, tpw;
 };
 
-ChunkPlan chunk_plan(int N, int K, int wgs_other = 0) {
+ChunkPlan chunk_plan(int N, int K, int max_s = 8) {
   ChunkPlan p{};
   p.NQ = (int)ceil_div(K, 128);
-  const int wgs = (int)ceil_div(ceil_div(N, 16), 8) + wgs_other;
-  const int s = std::max(1, std::min(4, (int)ceil_div(256, wgs)));
+  p.tpw = 1;
+  const int base = (int)ceil_div(ceil_div(N, 16), 4);
+  const int s = std::max(1, std::min(std::min(max_s, p.NQ), (int)ceil_div(512, base)));
   p.NQs = (int)ceil_div(p.NQ, s);
   p.S = (int)ceil_div(p.NQ, p.NQs);
   return p;
 }
 
 struct ChunkLayout {
-  int qkv_ld, S_qkv_s, S_qkv_f, S_o_s, S_o_f, S_d, ymax;
+  int qkv_ld, ymax;
+  ChunkPlan p_qkv_s, p_qkv_f, p_o_s, p_o_f, p_d;
   size_t hA, hB, qkv, q16, o, y, a, xf, apart, best, total;
 };
 
@@ -534,13 +539,13 @@ ChunkLayout chunk_layout(const q4dec_model* m) {
   const int R = kChunkRows;
   L.qkv_ld = std::max(Hq * Ds + 2 * Hs * Ds, Hq * Df + Df);
   // the q, k and v products share one launch: plan on their joint workgroups
-  L.S_qkv_s = chunk_plan(Hq * Ds + 2 * Hs * Ds, H).S;
-  L.S_qkv_f = chunk_plan(Hq * Df + Df, H).S;
-  L.S_o_s = chunk_plan(H, Hq * Ds).S;
-  L.S_o_f = chunk_plan(H, Hq * Df).S;
-  L.S_d = chunk_plan(H, I).S;
-  L.ymax = std::max(std::max(L.S_o_s, L.S_o_f), L.S_d);
-  const int Sq = std::max(L.S_qkv_s, L.S_qkv_f);
+  L.p_qkv_s = chunk_plan(Hq * Ds + 2 * Hs * Ds, H);
+  L.p_qkv_f = chunk_plan(Hq * Df + Df, H);
+  L.p_o_s = chunk_plan(H, Hq * Ds);
+  L.p_o_f = chunk_plan(H, Hq * Df);
+  L.p_d = chunk_plan(H, I);
+  L.ymax = std::max(std::max(L.p_o_s.S, L.p_o_f.S), L.p_d.S);
+  const int Sq = std::max(L.p_qkv_s.S, L.p_qkv_f.S);
   size_t off = 0;
   auto take = [&](size_t bytes) { const size_t o = off; off = align256(off + bytes); return o; };
   L.best = take(sizeof(unsigned long long) * 4);
@@ -566,7 +571,7 @@ void fill_gseg(GemmSeg& s, const void* packed, int N, int K, int wg0, int out_of
   s.N = N; s.T = T; s.wg0 = wg0; s.out_off = out_off;
 }
 
-int gseg_wgs(const GemmSeg& s) { return (int)ceil_div(s.T, 8); }
+int gseg_wgs(const GemmSeg& s, int tpw) { return (int)ceil_div(s.T, 4 * tpw); }
 
 // One chunk of n rows at positions pos0 .. pos0 + n - 1 through the whole
 // model, launched eagerly: embedding; per layer the input norm, the q/k/v
@@ -594,16 +599,18 @@ q4_status enqueue_chunk(const q4dec_model* m, const ChunkLayout& L, void* ws, co
     for (int i = 0; i < n; i++) e.tokens[i] = tokens[i];
     hipLaunchKernelGGL(k_chunk_embed, dim3(n), dim3(256), 0, st, e);
   }
-  auto gemm = [&](GemmArgs& g, int wgs, int S, bool gateup) {
-    if (gateup) hipLaunchKernelGGL(k_q4_gemm<EPI_GATEUP>, dim3(wgs, 1), dim3(256), kGemmLds, st, g);
-    else hipLaunchKernelGGL(k_q4_gemm<EPI_STORE>, dim3(wgs, S), dim3(256), kGemmLds, st, g);
+  auto gemm = [&](GemmArgs& g, int wgs, const ChunkPlan& p) {
+    g.NQ = p.NQ; g.NQs = p.NQs;
+    if (p.tpw == 2) hipLaunchKernelGGL((k_q4_gemm<EPI_STORE, 2>), dim3(wgs, p.S), dim3(256), kGemmLds, st, g);
+    else hipLaunchKernelGGL((k_q4_gemm<EPI_STORE, 1>), dim3(wgs, p.S), dim3(256), kGemmLds, st, g);
   };
   for (int l = 0; l < m->n_layers; l++) {
     const q4dec_layer& ly = m->layers[l];
     const bool full = ly.is_full != 0;
     const int D = full ? m->full_head_dim : m->sl_head_dim;
     const int Hkv = full ? 1 : m->sl_kv_heads;
-    const int Sq = full ? L.S_qkv_f : L.S_qkv_s;
+    const ChunkPlan& pq = full ? L.p_qkv_f : L.p_qkv_s;
+    const int Sq = pq.S;
     // ---- input norm (with the previous layer's post-FF residual), q/k/v products
     {
       NormIn ni{};
@@ -611,26 +618,26 @@ q4_status enqueue_chunk(const q4dec_model* m, const ChunkLayout& L, void* ws, co
       else {
         const q4dec_layer& prev = m->layers[l - 1];
         ni.h_src = hB; ni.y = y; ni.w_post = prev.post_ff_norm; ni.scalar = prev.layer_scalar; ni.h_dst = hA;
-        ni.ny = L.S_d; ni.y_split = (long)n * H;
+        ni.ny = L.p_d.S; ni.y_split = (long)n * H;
       }
       ni.w_in = ly.attn_norm; ni.H = H; ni.eps = m->eps;
-      hipLaunchKernelGGL(k_norm_rows, dim3(n), dim3(512), 0, st, ni, xf);
+      hipLaunchKernelGGL(k_norm_rows<8>, dim3(n), dim3(512), 0, st, ni, xf);
       GemmArgs g{};
       int wg = 0;
       fill_gseg(g.seg[0], ly.wq, Hq * D, H, wg, 0);
-      wg += gseg_wgs(g.seg[0]);
+      wg += gseg_wgs(g.seg[0], pq.tpw);
       fill_gseg(g.seg[1], ly.wk, Hkv * D, H, wg, Hq * D);
-      wg += gseg_wgs(g.seg[1]);
+      wg += gseg_wgs(g.seg[1], pq.tpw);
       g.nseg = 2;
       if (!full) {
         fill_gseg(g.seg[2], ly.wv, Hkv * D, H, wg, (Hq + Hkv) * D);
-        wg += gseg_wgs(g.seg[2]);
+        wg += gseg_wgs(g.seg[2], pq.tpw);
         g.nseg = 3;
       }
-      g.K = H; g.NQ = (int)ceil_div(H, 128); g.NQs = (int)ceil_div(g.NQ, Sq);
+      g.K = H;
       g.x = xf; g.ldx = H; g.n = n;
       g.y = qkv; g.ldy = L.qkv_ld; g.y_split = (long)n * L.qkv_ld;
-      gemm(g, wg, Sq, false);
+      gemm(g, wg, pq);
     }
     // ---- finishing: q to q16, K/V rows of every row into the caches
     {
@@ -669,15 +676,16 @@ q4_status enqueue_chunk(const q4dec_model* m, const ChunkLayout& L, void* ws, co
       launch_fd(a, D, 1, nullptr, o16, st);
     }
     // ---- output projection
-    const int So = full ? L.S_o_f : L.S_o_s;
+    const ChunkPlan& po = full ? L.p_o_f : L.p_o_s;
+    const int So = po.S;
     {
       GemmArgs g{};
       fill_gseg(g.seg[0], ly.wo, H, Hq * D, 0, 0);
       g.nseg = 1;
-      g.K = Hq * D; g.NQ = (int)ceil_div(Hq * D, 128); g.NQs = (int)ceil_div(g.NQ, So);
+      g.K = Hq * D;
       g.x = o16; g.ldx = Hq * D; g.n = n;
       g.y = y; g.ldy = H; g.y_split = (long)n * H;
-      gemm(g, gseg_wgs(g.seg[0]), So, false);
+      gemm(g, gseg_wgs(g.seg[0], po.tpw), po);
     }
     // ---- post-attention residual + pre-FF norm, gate/up with GELU * up
     {
@@ -685,7 +693,7 @@ q4_status enqueue_chunk(const q4dec_model* m, const ChunkLayout& L, void* ws, co
       ni.h_src = hA; ni.y = y; ni.ny = So; ni.y_split = (long)n * H;
       ni.w_post = ly.post_attn_norm; ni.scalar = 1.0f;
       ni.w_in = ly.pre_ff_norm; ni.h_dst = hB; ni.H = H; ni.eps = m->eps;
-      hipLaunchKernelGGL(k_norm_rows, dim3(n), dim3(512), 0, st, ni, xf);
+      hipLaunchKernelGGL(k_norm_rows<8>, dim3(n), dim3(512), 0, st, ni, xf);
       GemmArgs g{};
       fill_gseg(g.seg[0], ly.wg, I, H, 0, 0);
       fill_gseg(g.seg[1], ly.wu, I, H, 0, 0);
@@ -693,27 +701,27 @@ q4_status enqueue_chunk(const q4dec_model* m, const ChunkLayout& L, void* ws, co
       g.K = H; g.NQ = (int)ceil_div(H, 128); g.NQs = g.NQ;
       g.x = xf; g.ldx = H; g.n = n;
       g.a_out = a16; g.ld_a = I;
-      gemm(g, (int)ceil_div(g.seg[0].T, 4), 1, true);
+      hipLaunchKernelGGL((k_q4_gemm<EPI_GATEUP, 1>), dim3(ceil_div(g.seg[0].T, 2), 1), dim3(256), kGemmLds, st, g);
     }
     // ---- down projection
     {
       GemmArgs g{};
       fill_gseg(g.seg[0], ly.wd, H, I, 0, 0);
       g.nseg = 1;
-      g.K = I; g.NQ = (int)ceil_div(I, 128); g.NQs = (int)ceil_div(g.NQ, L.S_d);
+      g.K = I;
       g.x = a16; g.ldx = I; g.n = n;
       g.y = y; g.ldy = H; g.y_split = (long)n * H;
-      gemm(g, gseg_wgs(g.seg[0]), L.S_d, false);
+      gemm(g, gseg_wgs(g.seg[0], L.p_d.tpw), L.p_d);
     }
   }
   // ---- final norm of every row (the residual stream lands in hA), head of the last
   {
     const q4dec_layer& last = m->layers[m->n_layers - 1];
     NormIn ni{};
-    ni.h_src = hB; ni.y = y; ni.ny = L.S_d; ni.y_split = (long)n * H;
+    ni.h_src = hB; ni.y = y; ni.ny = L.p_d.S; ni.y_split = (long)n * H;
     ni.w_post = last.post_ff_norm; ni.scalar = last.layer_scalar;
     ni.w_in = m->final_norm; ni.h_dst = hA; ni.H = H; ni.eps = m->eps;
-    hipLaunchKernelGGL(k_norm_rows, dim3(n), dim3(512), 0, st, ni, xf);
+    hipLaunchKernelGGL(k_norm_rows<8>, dim3(n), dim3(512), 0, st, ni, xf);
   }
   {
     HeadArgs a{};
@@ -1046,10 +1054,13 @@ q4_status q4_gemm(const void* packed, int N, int K, const uint16_t* x, int n, fl
   GemmArgs g{};
   fill_gseg(g.seg[0], packed, N, K, 0, 0);
   g.nseg = 1;
-  g.K = K; g.NQ = (int)ceil_div(K, 128); g.NQs = g.NQ;
+  const ChunkPlan p = chunk_plan(N, K, 1);       // one run of K: y is the whole product
+  g.K = K; g.NQ = p.NQ; g.NQs = p.NQs;
   g.x = x; g.ldx = K; g.n = n;
   g.y = y; g.ldy = N; g.y_split = 0;
-  hipLaunchKernelGGL(k_q4_gemm<EPI_STORE>, dim3(gseg_wgs(g.seg[0]), 1), dim3(256), kGemmLds, S(stream), g);
+  const dim3 grid(gseg_wgs(g.seg[0], p.tpw), 1);
+  if (p.tpw == 2) hipLaunchKernelGGL((k_q4_gemm<EPI_STORE, 2>), grid, dim3(256), kGemmLds, S(stream), g);
+  else hipLaunchKernelGGL((k_q4_gemm<EPI_STORE, 1>), grid, dim3(256), kGemmLds, S(stream), g);
   return launch_status();
 }
 
