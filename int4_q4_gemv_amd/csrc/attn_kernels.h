@@ -59,6 +59,9 @@ struct AttnArgs {
   int fin_on;
   int kvh_major;          // grids enumerate KV heads fastest (the splits of one KV head, and
                           // the combine of its query heads, then share an XCD when Hkv = 8)
+  int rpw;                // rows per workgroup (fin_on == 0 only; 0 or 1: one): the MFMA
+                          // columns are (row, query head) pairs, GQ * rpw <= 16, so a K/V
+                          // tile is read once for rpw rows (a prefill chunk's ring layers)
   AttnFin fin;
   // Full layers that cache one row per position (kernel template VR): the
   // key of cached row t is RoPE_t(kw * v_t), formed in registers from the V
@@ -205,7 +208,11 @@ Q4_DEV void finish_vals(float (&v)[D / 64], const float (&wv)[D / 64], bool weig
 // to fp16.  The angle t * theta^(-2i/D) is formed in fp64 revolutions and
 // reduced to [0, 1) before the hardware sine and cosine; the row 4 positions
 // on is turned by the precomputed (cos, sin) of 4 * theta^(-2i/D).
-template <int D, bool VR = false>
+//
+// MR (several rows per workgroup, a.rpw; without the finishing prologue): the
+// MFMA columns are (row, query head) pairs, each masked to its own row's
+// window, and the splits divide the union of the rows' ranges.
+template <int D, bool VR = false, bool MR = false>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D <= 256 ? 2 : 1))) k_fd_partial(AttnArgs a) {
   constexpr int VROW = fd_vpitch<D>();        // LDS row pitch of the V rows (halves)
   constexpr int NDS = D / 16;                 // PV dim steps
@@ -229,9 +236,19 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D <= 2
   auto rebuilt = [](int s) { return VR && (s < RS || (s >= HS && s < HS + RS)); };
 
   const int split = a.kvh_major ? blockIdx.y : blockIdx.x, kvh = a.kvh_major ? blockIdx.x : blockIdx.y;
-  const int seq = blockIdx.z / a.n_rows, row = blockIdx.z - seq * a.n_rows;
-  const int nlive = a.n_rows;                 // the grid is built per row count
-  if (row >= nlive) return;
+  // rows of this workgroup: row .. rlast (one unless MR)
+  const int rpw = MR && a.rpw > 1 ? a.rpw : 1;
+  int seq, row;
+  if constexpr (MR) {
+    const int nrg = (a.n_rows + rpw - 1) / rpw;
+    seq = blockIdx.z / nrg;
+    row = (blockIdx.z - seq * nrg) * rpw;
+  } else {
+    seq = blockIdx.z / a.n_rows;
+    row = blockIdx.z - seq * a.n_rows;
+  }
+  if (row >= a.n_rows) return;
+  const int rlast = MR ? min(a.n_rows, row + rpw) - 1 : row;
   // the wave index as a scalar: tile origins and cache rows derived from it
   // are then computed once per wave, not per lane
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -288,14 +305,19 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D <= 2
   base = __builtin_amdgcn_readfirstlane(base);   // uniform: the split bounds and rows are scalar
   const int P = base + row;
   const int lo = a.ring ? max(0, P - a.W + 1) : 0;
-  const int L = P - lo + 1;
+  const int Pl = MR ? base + rlast : P;               // MR: the union of the rows' ranges
+  const int L = Pl - lo + 1;
   const int chunk = (L + a.S - 1) / a.S;
   const int st = lo + split * chunk;
-  const int en = min(st + chunk, P + 1);
+  const int en = min(st + chunk, Pl + 1);
   const int P0new = a.fin_on ? base : 0x7FFFFFFF;   // first position formed in this step
 
   const int j = lane & 15, g = lane >> 4;
-  const bool col_ok = j < a.GQ;
+  // column j: row row + jr, query head jh of this KV head; it admits
+  // positions lo_j .. P_j (its own window and causal bound)
+  const int jr = MR ? j / a.GQ : 0, jh = MR ? j - jr * a.GQ : j;
+  const bool col_ok = MR ? (j < a.GQ * rpw && row + jr <= rlast) : j < a.GQ;
+  const int Pj = P + jr, loj = a.ring ? Pj - a.W + 1 : 0;
 
   uint16_t* vb = a.v + seq * a.seq_stride + (a.ring ? (long)kvh * a.R * D : 0);
   uint16_t* kb = VR ? vb : a.k + seq * a.seq_stride + (a.ring ? (long)kvh * a.R * D : 0);
@@ -447,7 +469,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D <= 2
       set_q(s, t);
     }
   } else {
-    const uint16_t* qp = a.q + (((long)seq * a.n_rows + row) * a.Hq + (col_ok ? kvh * a.GQ + j : 0)) * D + 8 * g;
+    const uint16_t* qp = MR ? a.q + (((long)seq * a.n_rows + row + (col_ok ? jr : 0)) * a.Hq +
+                                     (col_ok ? kvh * a.GQ + jh : 0)) * D + 8 * g
+                            : a.q + (((long)seq * a.n_rows + row) * a.Hq + (col_ok ? kvh * a.GQ + j : 0)) * D + 8 * g;
 #pragma unroll
     for (int s = 0; s < NKS; s++) {
       u4v t = *reinterpret_cast<const u4v*>(qp + 32 * s);
@@ -528,8 +552,14 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D <= 2
     float sv[8];
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-      sv[i] = (t0 + 8 * g + i < en) ? s0[i] * a.scale_log2 : -INFINITY;
-      sv[4 + i] = (t0 + 8 * g + 4 + i < en) ? s1[i] * a.scale_log2 : -INFINITY;
+      if constexpr (MR) {
+        const int pa = t0 + 8 * g + i, pb = pa + 4;
+        sv[i] = (pa < en && pa <= Pj && pa >= loj) ? s0[i] * a.scale_log2 : -INFINITY;
+        sv[4 + i] = (pb < en && pb <= Pj && pb >= loj) ? s1[i] * a.scale_log2 : -INFINITY;
+      } else {
+        sv[i] = (t0 + 8 * g + i < en) ? s0[i] * a.scale_log2 : -INFINITY;
+        sv[4 + i] = (t0 + 8 * g + 4 + i < en) ? s1[i] * a.scale_log2 : -INFINITY;
+      }
     }
     float mt = sv[0];
 #pragma unroll
@@ -537,11 +567,17 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D <= 2
     mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
     mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
     const float m_new = fmaxf(m_run, mt);
-    const float alpha = exp2f(m_run - m_new);
+    // a column none of whose positions so far is admitted keeps m = -inf
+    // and weights 0 (its rows' windows may start past this tile)
+    const bool none = MR && m_new == -INFINITY;
+    const float alpha = MR ? (none ? 1.f : exp2f(m_run - m_new)) : exp2f(m_run - m_new);
     m_run = m_new;
     float p[8], ps = 0.f;
 #pragma unroll
-    for (int i = 0; i < 8; i++) { p[i] = exp2f(sv[i] - m_new); ps += p[i]; }
+    for (int i = 0; i < 8; i++) {
+      p[i] = MR ? (none ? 0.f : exp2f(sv[i] - m_new)) : exp2f(sv[i] - m_new);
+      ps += p[i];
+    }
     l_part = l_part * alpha + ps;
     // rescale O rows (heads 4g+i): their alpha lives in lane 4g+i
     float al[4];
@@ -604,6 +640,18 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D <= 2
   float l_tot = l_part + __shfl_xor(l_part, 16, 64);
   l_tot += __shfl_xor(l_tot, 32, 64);
 
+  // record of column col, or NULL for columns without a row and head
+  auto rec_of = [&](int col) -> float* {
+    int rr = row, hh = col;
+    if (MR) {
+      rr = row + col / a.GQ;
+      hh = col - (col / a.GQ) * a.GQ;
+      if (col >= a.GQ * rpw || rr > rlast) return nullptr;
+    } else if (col >= a.GQ) {
+      return nullptr;
+    }
+    return a.part + attn_rec(a, seq, rr, kvh, split, hh, D);
+  };
   // ---- a split of at most one tile: wave 0 holds the whole record and
   // stores it from registers (the merge below would give the same values:
   // the other waves' weights are 0 and wave 0's is 1)
@@ -611,17 +659,19 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D <= 2
     if (wave != 0) return;
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-      const int col = 4 * g + i;
-      if (col < a.GQ) {
-        float* rec = a.part + attn_rec(a, seq, row, kvh, split, col, D);
+      float* rec = MR ? rec_of(4 * g + i)
+                      : (4 * g + i < a.GQ ? a.part + attn_rec(a, seq, row, kvh, split, 4 * g + i, D) : nullptr);
+      if (rec) {
 #pragma unroll
         for (int d = 0; d < NDS; d++) rec[16 * d + j] = O[d][i];
       }
     }
-    if (lane < a.GQ) {
-      float* rec = a.part + attn_rec(a, seq, row, kvh, split, lane, D);
-      rec[D] = m_run;
-      rec[D + 1] = l_tot;
+    if (lane < (MR ? 16 : a.GQ)) {
+      float* rec = MR ? rec_of(lane) : a.part + attn_rec(a, seq, row, kvh, split, lane, D);
+      if (rec) {
+        rec[D] = m_run;
+        rec[D + 1] = l_tot;
+      }
     }
     return;
   }
@@ -664,15 +714,15 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D <= 2
     }
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-      const int col = 4 * g + i;
-      if (col < a.GQ) {
-        float* rec = a.part + attn_rec(a, seq, row, kvh, split, col, D);
+      float* rec = MR ? rec_of(4 * g + i)
+                      : (4 * g + i < a.GQ ? a.part + attn_rec(a, seq, row, kvh, split, 4 * g + i, D) : nullptr);
+      if (rec) {
 #pragma unroll
         for (int k = 0; k < NI; k++) rec[16 * (wave + 4 * k) + j] = acc[k][i];
       }
     }
   }
-  if (threadIdx.x < a.GQ) {
+  if (MR ? (threadIdx.x < 16 && rec_of(threadIdx.x)) : threadIdx.x < a.GQ) {
     const int col = threadIdx.x;
     const float M = fmaxf(fmaxf(wm[0][col], wm[1][col]), fmaxf(wm[2][col], wm[3][col]));
     float l = 0.f;
@@ -680,7 +730,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D <= 2
 #pragma unroll
       for (int w = 0; w < 4; w++) l += exp2f(wm[w][col] - M) * wl[w][col];
     }
-    float* rec = a.part + attn_rec(a, seq, row, kvh, split, col, D);
+    float* rec = MR ? rec_of(col) : a.part + attn_rec(a, seq, row, kvh, split, col, D);
     rec[D] = M;
     rec[D + 1] = l;
   }

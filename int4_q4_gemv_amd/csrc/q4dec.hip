@@ -132,6 +132,12 @@ q4_status set_attrs() {
   e = e != hipSuccess ? e : max_lds(&k_fd_partial<512>, (int)fd_lds_bytes<512>());
   e = e != hipSuccess ? e : max_lds(&k_fd_partial<128, true>, (int)fd_lds_bytes<128>());
   e = e != hipSuccess ? e : max_lds(&k_fd_partial<512, true>, (int)fd_lds_bytes<512>());
+  e = e != hipSuccess ? e : max_lds(&k_fd_partial<64, false, true>, (int)fd_lds_bytes<64>());
+  e = e != hipSuccess ? e : max_lds(&k_fd_partial<128, false, true>, (int)fd_lds_bytes<128>());
+  e = e != hipSuccess ? e : max_lds(&k_fd_partial<256, false, true>, (int)fd_lds_bytes<256>());
+  e = e != hipSuccess ? e : max_lds(&k_fd_partial<512, false, true>, (int)fd_lds_bytes<512>());
+  e = e != hipSuccess ? e : max_lds(&k_fd_partial<128, true, true>, (int)fd_lds_bytes<128>());
+  e = e != hipSuccess ? e : max_lds(&k_fd_partial<512, true, true>, (int)fd_lds_bytes<512>());
   e = e != hipSuccess ? e : max_lds(&k_q4_gemm<EPI_STORE, 1>, (int)kGemmLds);
   e = e != hipSuccess ? e : max_lds(&k_q4_gemm<EPI_STORE, 2>, (int)kGemmLds);
   e = e != hipSuccess ? e : max_lds(&k_q4_gemm<EPI_GATEUP, 1>, (int)kGemmLds);
@@ -146,16 +152,21 @@ q4_status set_attrs() {
 
 template <int D>
 void launch_fd_d(const AttnArgs& a, int n_seq, float* out32, uint16_t* out16, hipStream_t st) {
-  const dim3 grid(a.kvh_major ? a.Hkv : a.S, a.kvh_major ? a.S : a.Hkv, n_seq * a.n_rows);
+  const int rpw = a.rpw > 1 ? a.rpw : 1;
+  const dim3 grid(a.kvh_major ? a.Hkv : a.S, a.kvh_major ? a.S : a.Hkv, n_seq * (int)ceil_div(a.n_rows, rpw));
   const dim3 cgrid(n_seq * a.n_rows * a.Hq, D / 64);  // 256 threads each
   // without the finishing prologue only the V rows (which also hold the
   // merge buffer) are used: a smaller allocation lets more workgroups share a CU
   const size_t lds = (a.fin_on || a.vrow) ? fd_lds_bytes<D>() : fd_lds_vbytes<D>();   // VR parks q lo parts
+  const bool mr = rpw > 1;
   if constexpr (D == 128 || D == 512) {
-    if (a.vrow) hipLaunchKernelGGL((k_fd_partial<D, true>), grid, dim3(256), lds, st, a);
+    if (a.vrow && mr) hipLaunchKernelGGL((k_fd_partial<D, true, true>), grid, dim3(256), lds, st, a);
+    else if (a.vrow) hipLaunchKernelGGL((k_fd_partial<D, true>), grid, dim3(256), lds, st, a);
+    else if (mr) hipLaunchKernelGGL((k_fd_partial<D, false, true>), grid, dim3(256), lds, st, a);
     else hipLaunchKernelGGL((k_fd_partial<D, false>), grid, dim3(256), lds, st, a);
   } else {
-    hipLaunchKernelGGL((k_fd_partial<D, false>), grid, dim3(256), lds, st, a);
+    if (mr) hipLaunchKernelGGL((k_fd_partial<D, false, true>), grid, dim3(256), lds, st, a);
+    else hipLaunchKernelGGL((k_fd_partial<D, false>), grid, dim3(256), lds, st, a);
   }
   if (a.S <= 16) hipLaunchKernelGGL((k_fd_combine<D, 16>), cgrid, dim3(256), 0, st, a, out32, out16);
   else if (a.S <= 32) hipLaunchKernelGGL((k_fd_combine<D, 32>), cgrid, dim3(256), 0, st, a, out32, out16);
@@ -669,6 +680,9 @@ q4_status enqueue_chunk(const q4dec_model* m, const ChunkLayout& L, void* ws, co
       a.sp = nullptr; a.part = apart;
       a.fin_on = 0;
       a.kvh_major = full ? 0 : 1;
+      // the rows of the chunk share K/V tiles: as many rows per workgroup as
+      // their query heads fill the 16 MFMA columns (8 on a ring layer)
+      a.rpw = 16 % a.GQ == 0 ? 16 / a.GQ : 1;
       if (full && m->kv_format == 1) {
         a.vrow = 1; a.k = ly.v_cache; a.kw = ly.k_norm; a.theta = m->full_theta; a.krot = m->full_rot_pairs;
       }
