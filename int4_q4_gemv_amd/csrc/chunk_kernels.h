@@ -233,6 +233,180 @@ __global__ void __launch_bounds__(256) k_q4_gemm(GemmArgs a) {
   }
 }
 
+// ------------------------------------------------------- chunk attention ----
+// Rows of a chunk over shared K/V tiles (layers whose query heads already fill
+// the 16 MFMA columns, so rows cannot share a tile as columns): a workgroup's
+// 4 waves take 4 consecutive rows, and every 32-position tile of its split is
+// staged once in LDS for all four -- K rows at pitch D with 16-byte chunk c of
+// row r at c ^ kswz(r) (the 16 rows one 16-lane group reads fall in distinct
+// banks), V rows in the layout of k_fd_partial's transposing PV reads.  Each
+// wave runs the online softmax of its own row over the union of the 4 rows'
+// ranges (positions outside its row's range are masked) and writes its row's
+// (O, m, l) records; the combine is k_fd_combine's.  One tile at a time: two
+// workgroups share a CU (66 KB of LDS at D = 512), so one's loads overlap the
+// other's arithmetic.
+Q4_DEV int kswz(int r) { return (r & 3) | (((r >> 3) & 3) << 2); }
+
+template <int D>
+constexpr size_t rows4_lds_bytes() { return (size_t)32 * D * 2 + (size_t)32 * fd_vpitch<D>() * 2; }
+
+template <int D>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) k_fd_rows4(AttnArgs a) {
+  static_assert(D >= 128, "a K row holds at least 16 chunks");
+  constexpr int VROW = fd_vpitch<D>();
+  constexpr int NDS = D / 16, NKS = D / 32;
+  constexpr int CPR = D / 8, RPI = 64 / CPR;      // 16-byte chunks per row, rows per 1 KB load
+  extern __shared__ __align__(16) unsigned char smem_r[];
+  uint16_t* kt = reinterpret_cast<uint16_t*>(smem_r);   // [32][D]
+  uint16_t* vt = kt + 32 * D;                           // [32][VROW]
+  const int split = blockIdx.x, kvh = blockIdx.y;
+  const int ngrp = (a.n_rows + 3) / 4;
+  const int seq = blockIdx.z / ngrp, row0 = (blockIdx.z - seq * ngrp) * 4;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int rlast = min(a.n_rows, row0 + 4) - 1;
+  const bool live = row0 + wave <= rlast;              // wave-uniform
+  const int row = live ? row0 + wave : rlast;
+  const int base = a.pos0[seq];
+  const int P = base + row;
+  const int lo = a.ring ? max(0, base + row0 - a.W + 1) : 0;
+  const int Pl = base + rlast;
+  const int L = Pl - lo + 1;
+  const int chunk = (L + a.S - 1) / a.S;
+  const int st = lo + split * chunk;
+  const int en = min(st + chunk, Pl + 1);
+  const int loj = a.ring ? P - a.W + 1 : 0;
+  const int j = lane & 15, g = lane >> 4;
+  const bool col_ok = live && j < a.GQ;
+
+  const uint16_t* kb = a.k + seq * a.seq_stride + (a.ring ? (long)kvh * a.R * D : 0);
+  const uint16_t* vb = a.v + seq * a.seq_stride + (a.ring ? (long)kvh * a.R * D : 0);
+  const bool ringf = a.ring != 0;
+  const int Rr = ringf ? a.R : 1;
+
+  h8_t qb[NKS];
+  {
+    const uint16_t* qp = a.q + (((long)seq * a.n_rows + row) * a.Hq + (col_ok ? kvh * a.GQ + j : 0)) * D + 8 * g;
+#pragma unroll
+    for (int s = 0; s < NKS; s++) {
+      u4v t = *reinterpret_cast<const u4v*>(qp + 32 * s);
+      if (!col_ok) t = (u4v){0u, 0u, 0u, 0u};
+      qb[s] = __builtin_bit_cast(h8_t, t);
+    }
+  }
+  float m_run = -INFINITY, l_part = 0.f;
+  f4_t O[NDS];
+#pragma unroll
+  for (int d = 0; d < NDS; d++) O[d] = (f4_t){0.f, 0.f, 0.f, 0.f};
+
+  for (int t0 = st; t0 < en; t0 += 32) {
+    // cache rows of the tile: tile row r at slot (t0 + r) mod R (rings hold
+    // at least 32 slots), rows past en read row 0 and are masked
+    const int s0 = __builtin_amdgcn_readfirstlane(ringf ? t0 % Rr : t0);
+    const int nv = __builtin_amdgcn_readfirstlane(en - t0);
+    auto row_at = [&](int r) -> long {
+      const int sl = ringf && r >= Rr - s0 ? s0 + r - Rr : s0 + r;
+      return r < nv ? (long)sl * D : 0l;
+    };
+    __syncthreads();                               // the previous tile's reads are done
+    // wave w stages tile rows 8w .. 8w+7 of K and of V, 1 KB per instruction
+    {
+      const int rl = lane / CPR, pc = lane % CPR;
+#pragma unroll
+      for (int i = 0; i < 8 / RPI; i++) {
+        const int r = 8 * wave + RPI * i + rl;
+        const int ck = pc ^ kswz(r);
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint32_t*>(kb + row_at(r) + ck * 8),
+                                         reinterpret_cast<uint32_t*>(kt + (8 * wave + RPI * i) * D), 16, 0, 0);
+        const int cv = pc ^ (2 * vswz<D>(r));
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint32_t*>(vb + row_at(r) + cv * 8),
+                                         reinterpret_cast<uint32_t*>(vt + (8 * wave + RPI * i) * VROW), 16, 0, 0);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (!live) continue;                           // wave-uniform; it still joins every barrier
+    // S^T = K Q^T: MFMA row r of half h <-> tile position 8 (r / 4) + 4h + r % 4
+    const int ra = 8 * (j >> 2) + (j & 3);
+    f4_t s0v = {0.f, 0.f, 0.f, 0.f}, s1v = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < NKS; s++) {
+      const int cc = 4 * s + g;                    // 16-byte chunk of dims 32 s + 8 g
+      const h8_t KA = *reinterpret_cast<const h8_t*>(kt + ra * D + (cc ^ kswz(ra)) * 8);
+      const h8_t KB = *reinterpret_cast<const h8_t*>(kt + (ra + 4) * D + (cc ^ kswz(ra + 4)) * 8);
+      s0v = __builtin_amdgcn_mfma_f32_16x16x32_f16(KA, qb[s], s0v, 0, 0, 0);
+      s1v = __builtin_amdgcn_mfma_f32_16x16x32_f16(KB, qb[s], s1v, 0, 0, 0);
+    }
+    float sv[8];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const int pa = t0 + 8 * g + i, pb = pa + 4;
+      sv[i] = (pa < en && pa <= P && pa >= loj) ? s0v[i] * a.scale_log2 : -INFINITY;
+      sv[4 + i] = (pb < en && pb <= P && pb >= loj) ? s1v[i] * a.scale_log2 : -INFINITY;
+    }
+    float mt = sv[0];
+#pragma unroll
+    for (int i = 1; i < 8; i++) mt = fmaxf(mt, sv[i]);
+    mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+    const float m_new = fmaxf(m_run, mt);
+    const bool none = m_new == -INFINITY;          // nothing of this row admitted yet
+    const float alpha = none ? 1.f : exp2f(m_run - m_new);
+    m_run = m_new;
+    float p[8], ps = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      p[i] = none ? 0.f : exp2f(sv[i] - m_new);
+      ps += p[i];
+    }
+    l_part = l_part * alpha + ps;
+    float al[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) al[i] = __shfl(alpha, 4 * g + i, 64);
+#pragma unroll
+    for (int d = 0; d < NDS; d++)
+#pragma unroll
+      for (int i = 0; i < 4; i++) O[d][i] *= al[i];
+    h8_t Ahi, Alo;
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      const _Float16 hi = (_Float16)p[i];
+      Ahi[i] = hi;
+      Alo[i] = (_Float16)(p[i] - (float)hi);
+    }
+    // O += P V with the transposing reads of k_fd_partial
+    const int sw = vswz<D>(8 * g + (j >> 2));
+    const uint16_t* vp = vt + (8 * g + (j >> 2)) * VROW + 4 * (j & 3);
+#pragma unroll
+    for (int d = 0; d < NDS; d++) {
+      typedef short v4s_t __attribute__((ext_vector_type(4)));
+      typedef __attribute__((address_space(3))) v4s_t lds_v4s;
+      const int cd = 16 * (d ^ sw);
+      const v4s_t vlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(vp + cd));
+      const v4s_t vhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(vp + 4 * VROW + cd));
+      const h8_t Bv = __builtin_bit_cast(h8_t, __builtin_shufflevector(vlo, vhi, 0, 1, 2, 3, 4, 5, 6, 7));
+      O[d] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ahi, Bv, O[d], 0, 0, 0);
+      O[d] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Alo, Bv, O[d], 0, 0, 0);
+    }
+  }
+  if (!live) return;
+  float l_tot = l_part + __shfl_xor(l_part, 16, 64);
+  l_tot += __shfl_xor(l_tot, 32, 64);
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const int col = 4 * g + i;
+    if (col < a.GQ) {
+      float* rec = a.part + attn_rec(a, seq, row, kvh, split, col, D);
+#pragma unroll
+      for (int d = 0; d < NDS; d++) rec[16 * d + j] = O[d][i];
+    }
+  }
+  if (lane < a.GQ) {
+    float* rec = a.part + attn_rec(a, seq, row, kvh, split, lane, D);
+    rec[D] = m_run;
+    rec[D + 1] = l_tot;
+  }
+}
+
 // ------------------------------------------------------------ embedding ----
 struct ChunkEmbedArgs {
   const uint16_t* E;       // [vocab][H] fp16

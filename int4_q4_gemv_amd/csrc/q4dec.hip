@@ -138,6 +138,8 @@ q4_status set_attrs() {
   e = e != hipSuccess ? e : max_lds(&k_fd_partial<512, false, true>, (int)fd_lds_bytes<512>());
   e = e != hipSuccess ? e : max_lds(&k_fd_partial<128, true, true>, (int)fd_lds_bytes<128>());
   e = e != hipSuccess ? e : max_lds(&k_fd_partial<512, true, true>, (int)fd_lds_bytes<512>());
+  e = e != hipSuccess ? e : max_lds(&k_fd_rows4<256>, (int)rows4_lds_bytes<256>());
+  e = e != hipSuccess ? e : max_lds(&k_fd_rows4<512>, (int)rows4_lds_bytes<512>());
   e = e != hipSuccess ? e : max_lds(&k_q4_gemm<EPI_STORE, 1>, (int)kGemmLds);
   e = e != hipSuccess ? e : max_lds(&k_q4_gemm<EPI_STORE, 2>, (int)kGemmLds);
   e = e != hipSuccess ? e : max_lds(&k_q4_gemm<EPI_GATEUP, 1>, (int)kGemmLds);
@@ -151,10 +153,17 @@ q4_status set_attrs() {
 }
 
 template <int D>
+void launch_combine(const AttnArgs& a, int n_seq, float* out32, uint16_t* out16, hipStream_t st) {
+  const dim3 cgrid(n_seq * a.n_rows * a.Hq, D / 64);  // 256 threads each
+  if (a.S <= 16) hipLaunchKernelGGL((k_fd_combine<D, 16>), cgrid, dim3(256), 0, st, a, out32, out16);
+  else if (a.S <= 32) hipLaunchKernelGGL((k_fd_combine<D, 32>), cgrid, dim3(256), 0, st, a, out32, out16);
+  else hipLaunchKernelGGL((k_fd_combine<D, kMaxSplits>), cgrid, dim3(256), 0, st, a, out32, out16);
+}
+
+template <int D>
 void launch_fd_d(const AttnArgs& a, int n_seq, float* out32, uint16_t* out16, hipStream_t st) {
   const int rpw = a.rpw > 1 ? a.rpw : 1;
   const dim3 grid(a.kvh_major ? a.Hkv : a.S, a.kvh_major ? a.S : a.Hkv, n_seq * (int)ceil_div(a.n_rows, rpw));
-  const dim3 cgrid(n_seq * a.n_rows * a.Hq, D / 64);  // 256 threads each
   // without the finishing prologue only the V rows (which also hold the
   // merge buffer) are used: a smaller allocation lets more workgroups share a CU
   const size_t lds = (a.fin_on || a.vrow) ? fd_lds_bytes<D>() : fd_lds_vbytes<D>();   // VR parks q lo parts
@@ -168,9 +177,16 @@ void launch_fd_d(const AttnArgs& a, int n_seq, float* out32, uint16_t* out16, hi
     if (mr) hipLaunchKernelGGL((k_fd_partial<D, false, true>), grid, dim3(256), lds, st, a);
     else hipLaunchKernelGGL((k_fd_partial<D, false>), grid, dim3(256), lds, st, a);
   }
-  if (a.S <= 16) hipLaunchKernelGGL((k_fd_combine<D, 16>), cgrid, dim3(256), 0, st, a, out32, out16);
-  else if (a.S <= 32) hipLaunchKernelGGL((k_fd_combine<D, 32>), cgrid, dim3(256), 0, st, a, out32, out16);
-  else hipLaunchKernelGGL((k_fd_combine<D, kMaxSplits>), cgrid, dim3(256), 0, st, a, out32, out16);
+  launch_combine<D>(a, n_seq, out32, out16, st);
+}
+
+// The chunk's full layers: 4 rows per workgroup over shared K/V tiles, then
+// the combine.
+template <int D>
+void launch_rows4_d(const AttnArgs& a, int n_seq, uint16_t* out16, hipStream_t st) {
+  const dim3 grid(a.S, a.Hkv, n_seq * (int)ceil_div(a.n_rows, 4));
+  hipLaunchKernelGGL(k_fd_rows4<D>, grid, dim3(256), rows4_lds_bytes<D>(), st, a);
+  launch_combine<D>(a, n_seq, nullptr, out16, st);
 }
 
 // Split-K partials then the combine (S <= kMaxSplits).
@@ -515,6 +531,7 @@ q4_status begin_step(const q4dec_model* m, const StepPtrs& P, const int32_t* tok
 
 // ------------------------------------------------------- prefill chunk ----
 constexpr int kChunkSplits = 8;       // attention splits per (row, KV head) of a chunk
+constexpr int kRows4Splits = 16;      // the same for the 4-row kernel of the full layers
 
 // A matrix product of a chunk: one 16-row tile per wave and S runs of K
 // (S <= max_s; S > 1 writes partial products that the norm or finishing
@@ -568,7 +585,7 @@ ChunkLayout chunk_layout(const q4dec_model* m) {
   L.y = take(sizeof(float) * L.ymax * R * H);
   L.a = take(sizeof(uint16_t) * R * I);
   L.xf = take(sizeof(uint16_t) * R * H);
-  const size_t apart_full = (size_t)R * kChunkSplits * Hq * (Df + 4);
+  const size_t apart_full = (size_t)R * std::max(kChunkSplits, kRows4Splits) * Hq * (Df + 4);
   const size_t apart_ring = (size_t)R * Hs * kChunkSplits * (Hq / Hs) * (Ds + 4);
   L.apart = take(sizeof(float) * std::max(apart_full, apart_ring));
   L.total = off;
@@ -687,7 +704,14 @@ q4_status enqueue_chunk(const q4dec_model* m, const ChunkLayout& L, void* ws, co
         a.vrow = 1; a.k = ly.v_cache; a.kw = ly.k_norm; a.theta = m->full_theta; a.krot = m->full_rot_pairs;
       }
       a.pos0[0] = pos0;
-      launch_fd(a, D, 1, nullptr, o16, st);
+      if (a.rpw <= 1 && !a.vrow && (D == 256 || D == 512)) {
+        // 16 query heads fill the columns: 4 rows share each K/V tile instead
+        a.S = kRows4Splits;
+        if (D == 256) launch_rows4_d<256>(a, 1, o16, st);
+        else launch_rows4_d<512>(a, 1, o16, st);
+      } else {
+        launch_fd(a, D, 1, nullptr, o16, st);
+      }
     }
     // ---- output projection
     const ChunkPlan& po = full ? L.p_o_f : L.p_o_s;
