@@ -220,3 +220,21 @@ def test_12b_prefill_layers_vs_oracle(orc, stream, n):
         print(f"  layer {l} ok", flush=True)
     del gm
     torch.cuda.empty_cache()
+
+
+def test_prefill_full_layer_rows4_d256(orc, stream):
+    """A model whose full layer has 16 query heads of 256 dims (one KV head):
+    the chunk's full-layer attention then takes the 4-rows-per-workgroup
+    kernel at D = 256 (the 12B layers use D = 512); 64 and 29 rows."""
+    cfg = dataclasses.replace(synth.TOY, n_heads=16, sl_kv_heads=8, full_head_dim=256)
+    for n, pos0 in ((64, 100), (29, 3)):
+        print(f"rows4 D=256 n={n} pos0={pos0}", flush=True)
+        gm, om = build_pair(orc, cfg, 24, pos0)
+        toks = synth.tokens(cfg, n, 24)
+        logits, am, h = gm.prefill(toks, pos0, want_hidden=True)
+        torch.cuda.synchronize()
+        ref, _ = om.decode_step(toks, pos0)
+        assert_close(logits, ref[-1], what=f"rows4 D=256 logits n={n}")
+        check_cache_rows(cfg, gm, om, pos0, n, f"rows4 D=256 n={n}")
+        gm, om = build_pair(orc, cfg, 24, pos0)
+        check_layers_alone(gm, om, toks, pos0, f"rows4 D=256 n={n}")
