@@ -17,8 +17,9 @@
 // fp16 hi + lo (d has 11 significant bits and |q| <= 8, so d * q has at most 15
 // and its lowest bit is at least 2^-24; packed fp16 multiply and fma), and each
 // product is two MFMAs.  Sums are fp32 in the MFMA accumulators.  The chunk's
-// x rows are staged in LDS 512 columns at a time (direct global-to-LDS loads,
-// one 1 KB row per instruction, rows padded by 16 bytes).
+// x rows are staged in LDS 256 columns at a time (direct global-to-LDS loads,
+// two rows per instruction; 16-byte chunk p of row b at position p ^ (b & 15),
+// so the 16 rows a 16-lane group reads fall in distinct banks).
 //
 // A workgroup is 4 waves; each wave owns TPW row tiles and all 64 chunk rows
 // (4 column groups of 16), accumulating TPW x 4 MFMA tiles.  STORE: the 4
@@ -37,9 +38,8 @@
 namespace q4k {
 
 constexpr int kChunkRows = 64;                 // rows of a chunk
-constexpr int kGemmCQ = 4;                     // quads per staged x run (512 columns)
-constexpr int kGemmPitch = kGemmCQ * 128 + 8;  // halves per staged x row
-constexpr size_t kGemmLds = (size_t)kChunkRows * kGemmPitch * 2;
+constexpr int kGemmCQ = 2;                     // quads per staged x run (256 columns)
+constexpr size_t kGemmLds = 0;                 // the x runs live in two static LDS arrays
 
 // One matrix of a launch.  STORE launches may hold up to 3 (the q, k and v
 // projections), laid out along blockIdx.x from workgroup wg0 on; GATEUP holds
@@ -68,16 +68,16 @@ struct GemmArgs {
 
 // TPW: 16-row tiles per wave (STORE: 4 TPW x 16 rows per workgroup; GATEUP:
 // the gate waves 0, 1 and the up waves 2, 3 on the same 32 TPW rows).  The K
-// loop is pipelined over runs of kGemmCQ quads: the weights and x rows of run
-// r + 1 are loaded into registers while run r is computed from LDS, and the
-// x rows are written to LDS after it.  (Global-to-LDS loads of the next run
-// would make the compiler wait for them before every LDS read of the
-// current one, as it cannot tell the two apart.)
+// loop is pipelined over runs of kGemmCQ quads: while run r is computed from
+// one LDS array, the weights of run r + 1 are loaded into registers and its x
+// rows straight into the other array (two distinct arrays, so that the
+// compiler can tell the next run's global-to-LDS writes from this run's LDS
+// reads and does not wait for them first).  The scales are kept one per
+// 32-bit register (packing two into one made the compiler wait for the load
+// in flight).
 template <int EPI, int TPW>
 __global__ void __launch_bounds__(256) k_q4_gemm(GemmArgs a) {
   constexpr int CQ = kGemmCQ;
-  extern __shared__ __align__(16) unsigned char smem_c[];
-  uint16_t* xs = reinterpret_cast<uint16_t*>(smem_c);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int r = lane & 15, g = lane >> 4;
   const bool up = EPI == EPI_GATEUP && wave >= 2;
@@ -107,46 +107,43 @@ __global__ void __launch_bounds__(256) k_q4_gemm(GemmArgs a) {
   // per lane each; quads past the run reload the run's first) and the x rows
   // 16 wave .. +15 at columns 128 qc + 8 lane (clamped into the row; rows
   // past n repeat row n - 1; neither is used)
-  auto load_run = [&](int qc, u4v (&cw)[TPW][CQ], uint16_t (&sw)[TPW][CQ], u4v (&xr)[16]) {
-    const int nq = min(CQ, q_end - qc);
+  // double-buffered x runs of 2 quads in two distinct LDS arrays, filled by
+  // global-to-LDS loads; row b at pitch 256 columns, 16-byte chunk p of row b
+  // at position p ^ (b & 15)
+  constexpr int DQ = 2;
+  __shared__ __align__(16) uint16_t xa[64 * 256];
+  __shared__ __align__(16) uint16_t xb2[64 * 256];
+  auto load_w = [&](int qc, u4v (&cw)[TPW][CQ], uint32_t (&sw)[TPW][CQ]) {
+    const int nq = min(DQ, q_end - qc);
 #pragma unroll
-    for (int i = 0; i < CQ; i++) {
+    for (int i = 0; i < DQ; i++) {
       const int qi = qc + (i < nq ? i : 0);
 #pragma unroll
       for (int t = 0; t < TPW; t++) {
         const long o = ((long)tl[t] * a.NQ + qi) * 64 + lane;
         cw[t][i] = __builtin_nontemporal_load(codes + o);
-        sw[t][i] = scales[o];
+        sw[t][i] = (uint32_t)scales[o];
       }
     }
-    const int col = min(qc * 128 + lane * 8, a.K - 8);
+  };
+  auto load_x = [&](int qc, uint16_t* buf) {
 #pragma unroll
-    for (int i = 0; i < 16; i++) {
-      const int bs = min(16 * wave + i, a.n - 1);
-      xr[i] = *reinterpret_cast<const u4v*>(a.x + (long)bs * a.ldx + col);
+    for (int i = 0; i < 8; i++) {
+      const int b = 16 * wave + 2 * i + (lane >> 5);
+      const int bs = min(b, a.n - 1);
+      const int p = lane & 31;
+      const int col = min(qc * 128 + (p ^ (b & 15)) * 8, a.K - 8);
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint32_t*>(a.x + (long)bs * a.ldx + col),
+                                       reinterpret_cast<uint32_t*>(buf + (16 * wave + 2 * i) * 256), 16, 0, 0);
     }
   };
-  auto store_x = [&](const u4v (&xr)[16]) {
+  auto compute = [&](const uint16_t* buf, const u4v (&cw)[TPW][CQ], const uint32_t (&sw)[TPW][CQ], int nq) {
 #pragma unroll
-    for (int i = 0; i < 16; i++) *reinterpret_cast<u4v*>(xs + (16 * wave + i) * kGemmPitch + lane * 8) = xr[i];
-  };
-  u4v cw[TPW][CQ], cn[TPW][CQ], xr[16];
-  uint16_t sw[TPW][CQ], sn[TPW][CQ];
-  if (q_begin < q_end) {
-    load_run(q_begin, cw, sw, xr);
-    store_x(xr);
-  }
-  __syncthreads();
-  for (int qc = q_begin; qc < q_end; qc += CQ) {
-    const int nq = min(CQ, q_end - qc);
-    const bool more = qc + CQ < q_end;             // uniform
-    if (more) load_run(qc + CQ, cn, sn, xr);
-#pragma unroll
-    for (int i = 0; i < CQ; i++) {
-      if (i >= nq) break;                          // uniform
+    for (int i = 0; i < DQ; i++) {
+      if (i >= nq) break;
 #pragma unroll
       for (int t = 0; t < TPW; t++) {
-        const _Float16 d = __builtin_bit_cast(_Float16, sw[t][i]);
+        const _Float16 d = __builtin_bit_cast(_Float16, (uint16_t)sw[t][i]);
         const h2_t d2 = {d, d};
         const uint32_t qw[4] = {cw[t][i].x, cw[t][i].y, cw[t][i].z, cw[t][i].w};
 #pragma unroll
@@ -160,33 +157,60 @@ __global__ void __launch_bounds__(256) k_q4_gemm(GemmArgs a) {
                                                   __builtin_shufflevector(h2, h3, 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
           const h8_t lo = __builtin_shufflevector(__builtin_shufflevector(l0, l1, 0, 1, 2, 3),
                                                   __builtin_shufflevector(l2, l3, 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
-          h8_t xb[4];
+          h8_t xv[4];
 #pragma unroll
-          for (int c = 0; c < 4; c++)
-            xb[c] = *reinterpret_cast<const h8_t*>(xs + (16 * c + r) * kGemmPitch + i * 128 + 32 * g + 8 * w);
-          // the hi products of the 4 column groups, then the lo ones: no
-          // MFMA waits for the one just issued
+          for (int c = 0; c < 4; c++) {
+            const int b = 16 * c + r;
+            const int p = (16 * i + 4 * g + w) ^ (b & 15);
+            xv[c] = *reinterpret_cast<const h8_t*>(buf + b * 256 + p * 8);
+          }
 #pragma unroll
-          for (int c = 0; c < 4; c++) acc[t][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(hi, xb[c], acc[t][c], 0, 0, 0);
+          for (int c = 0; c < 4; c++) acc[t][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(hi, xv[c], acc[t][c], 0, 0, 0);
 #pragma unroll
-          for (int c = 0; c < 4; c++) acc[t][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(lo, xb[c], acc[t][c], 0, 0, 0);
+          for (int c = 0; c < 4; c++) acc[t][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(lo, xv[c], acc[t][c], 0, 0, 0);
         }
       }
     }
-    __syncthreads();                               // every wave is done with this run's x
-    if (more) {
-      store_x(xr);
+  };
+  u4v cw[TPW][CQ], cn[TPW][CQ];
+  uint32_t sw[TPW][CQ], sn[TPW][CQ];
+  if (q_begin < q_end) {
+    load_w(q_begin, cw, sw);
+    load_x(q_begin, xa);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int qc = q_begin; qc < q_end; qc += 2 * DQ) {
+    {
+      const bool more = qc + DQ < q_end;
+      if (more) { load_w(qc + DQ, cn, sn); load_x(qc + DQ, xb2); }
+      compute(xa, cw, sw, min(DQ, q_end - qc));
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (!more) break;
 #pragma unroll
       for (int t = 0; t < TPW; t++)
 #pragma unroll
         for (int i = 0; i < CQ; i++) { cw[t][i] = cn[t][i]; sw[t][i] = sn[t][i]; }
     }
-    __syncthreads();
+    {
+      const int q1 = qc + DQ;
+      const bool more = q1 + DQ < q_end;
+      if (more) { load_w(q1 + DQ, cn, sn); load_x(q1 + DQ, xa); }
+      compute(xb2, cw, sw, min(DQ, q_end - q1));
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (!more) break;
+#pragma unroll
+      for (int t = 0; t < TPW; t++)
+#pragma unroll
+        for (int i = 0; i < CQ; i++) { cw[t][i] = cn[t][i]; sw[t][i] = sn[t][i]; }
+    }
   }
   // lane (c, g) of tile t, column group cg holds rows 16 tile + 4 g + i of
   // chunk row 16 cg + c
   if constexpr (EPI == EPI_GATEUP) {
-    f4_t* ex = reinterpret_cast<f4_t*>(smem_c);   // [2 waves][TPW tiles][4 groups][64 lanes]
+    f4_t* ex = reinterpret_cast<f4_t*>(xa);   // [2 waves][TPW tiles][4 groups][64 lanes]
     if (up) {
 #pragma unroll
       for (int t = 0; t < TPW; t++)
