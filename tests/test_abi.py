@@ -129,6 +129,40 @@ def test_decode_step_checks():
     assert L.decode_step(C.byref(m), tok, 1, 5, f, f, f, big, None) == q4.Q4_ESHAPE
 
 
+def test_chunk_entry_points_check_their_arguments():
+    """q4_gemm and prefill_chunk reject bad calls on the host, before any launch."""
+    from int4_q4_gemv_amd import synth
+    L = q4.lib()
+    fake = C.c_void_p(0x10000)
+    odd = C.c_void_p(0x10008)
+    assert L.q4_gemm(None, 64, 128, fake, 4, fake, None) == q4.Q4_EINVAL
+    assert L.q4_gemm(fake, 64, 128, fake, 0, fake, None) == q4.Q4_ESHAPE       # no rows
+    assert L.q4_gemm(fake, 64, 128, fake, 65, fake, None) == q4.Q4_ESHAPE      # more than a chunk
+    assert L.q4_gemm(fake, 64, 100, fake, 4, fake, None) == q4.Q4_ESHAPE      # K % 32
+    assert L.q4_gemm(fake, 64, 128, odd, 4, fake, None) == q4.Q4_EALIGN
+    cfg = synth.TOY
+    lay = (q4.Layer * 2)()
+    for i in range(2):
+        lay[i] = q4.Layer(int(cfg.is_full(i)), 1, *([0x10000] * 13), 1.0, 0x10000, 0x10000)
+    m = q4.Model(cfg.hidden, cfg.n_heads, cfg.inter, cfg.vocab, 2, cfg.sl_kv_heads, cfg.sl_head_dim,
+                 cfg.full_head_dim, cfg.window, cfg.ring, cfg.full_cap, cfg.sl_rot_pairs,
+                 cfg.full_rot_pairs, cfg.sl_theta, cfg.full_theta, 1.0, 1.0, 1e-6, 30.0, 0x10000, 0x10000, lay)
+    need = L.prefill_chunk_workspace_size(C.byref(m))
+    assert need > 0
+    big = C.c_size_t(need * 2)
+    toks = (C.c_int32 * 65)(*range(65))
+    f = fake
+    assert L.prefill_chunk(C.byref(m), toks, 65, 0, f, f, None, f, big, None) == q4.Q4_ESHAPE   # > 64 rows
+    assert L.prefill_chunk(C.byref(m), toks, 64, -1, f, f, None, f, big, None) == q4.Q4_ERANGE
+    assert L.prefill_chunk(C.byref(m), toks, 64, cfg.full_cap - 10, f, f, None, f, big, None) == q4.Q4_ERANGE
+    assert L.prefill_chunk(C.byref(m), toks, 64, 0, f, f, None, f, C.c_size_t(64), None) == q4.Q4_ENOSPACE
+    m.weight_format = 1                      # the chunk products take q4 weights only
+    assert L.prefill_chunk(C.byref(m), toks, 64, 0, f, f, None, f, big, None) == q4.Q4_ESHAPE
+    m.weight_format = 0
+    m.ring = cfg.window + 62                 # R >= W + n - 1 fails for 64 rows
+    assert L.prefill_chunk(C.byref(m), toks, 64, 0, f, f, None, f, big, None) == q4.Q4_ERANGE
+
+
 def test_spec_accept_rule():
     """The host acceptance rule of a verify block (no device work): drafts are
     kept while they equal the target's argmax of the previous row; the
