@@ -180,6 +180,8 @@ __global__ void __launch_bounds__(256) k_q4_gemm(GemmArgs a) {
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  // two phases per iteration with swapped roles (no register copies: a copy
+  // of a load in flight would wait for it)
   for (int qc = q_begin; qc < q_end; qc += 2 * DQ) {
     {
       const bool more = qc + DQ < q_end;
@@ -188,23 +190,15 @@ __global__ void __launch_bounds__(256) k_q4_gemm(GemmArgs a) {
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
       if (!more) break;
-#pragma unroll
-      for (int t = 0; t < TPW; t++)
-#pragma unroll
-        for (int i = 0; i < CQ; i++) { cw[t][i] = cn[t][i]; sw[t][i] = sn[t][i]; }
     }
     {
       const int q1 = qc + DQ;
       const bool more = q1 + DQ < q_end;
-      if (more) { load_w(q1 + DQ, cn, sn); load_x(q1 + DQ, xa); }
-      compute(xb2, cw, sw, min(DQ, q_end - q1));
+      if (more) { load_w(q1 + DQ, cw, sw); load_x(q1 + DQ, xa); }
+      compute(xb2, cn, sn, min(DQ, q_end - q1));
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
       if (!more) break;
-#pragma unroll
-      for (int t = 0; t < TPW; t++)
-#pragma unroll
-        for (int i = 0; i < CQ; i++) { cw[t][i] = cn[t][i]; sw[t][i] = sn[t][i]; }
     }
   }
   // lane (c, g) of tile t, column group cg holds rows 16 tile + 4 g + i of
