@@ -17,7 +17,7 @@
 // fp16 hi + lo (d has 11 significant bits and |q| <= 8, so d * q has at most 15
 // and its lowest bit is at least 2^-24; packed fp16 multiply and fma), and each
 // product is two MFMAs.  Sums are fp32 in the MFMA accumulators.  The chunk's
-// x rows are staged in LDS 256 columns at a time (direct global-to-LDS loads,
+// x rows are staged in LDS 128 or 256 columns at a time (direct global-to-LDS loads,
 // two rows per instruction; 16-byte chunk p of row b at position p ^ (b & 15),
 // so the 16 rows a 16-lane group reads fall in distinct banks).
 //
@@ -38,7 +38,8 @@
 namespace q4k {
 
 constexpr int kChunkRows = 64;                 // rows of a chunk
-constexpr int kGemmCQ = 2;                     // quads per staged x run (256 columns)
+constexpr int kChunkRunQ = 1;                  // quads per staged x run in the chunk's products
+constexpr int kGemmRunQ = 2;                   // ... in q4_gemm (one workgroup per CU: longer runs)
 constexpr size_t kGemmLds = 0;                 // the x runs live in two static LDS arrays
 
 // One matrix of a launch.  STORE launches may hold up to 3 (the q, k and v
@@ -68,16 +69,15 @@ struct GemmArgs {
 
 // TPW: 16-row tiles per wave (STORE: 4 TPW x 16 rows per workgroup; GATEUP:
 // the gate waves 0, 1 and the up waves 2, 3 on the same 32 TPW rows).  The K
-// loop is pipelined over runs of kGemmCQ quads: while run r is computed from
+// loop is pipelined over runs of CQ quads (128 CQ columns): while run r is computed from
 // one LDS array, the weights of run r + 1 are loaded into registers and its x
 // rows straight into the other array (two distinct arrays, so that the
 // compiler can tell the next run's global-to-LDS writes from this run's LDS
 // reads and does not wait for them first).  The scales are kept one per
 // 32-bit register (packing two into one made the compiler wait for the load
 // in flight).
-template <int EPI, int TPW>
+template <int EPI, int TPW, int CQ>
 __global__ void __launch_bounds__(256) k_q4_gemm(GemmArgs a) {
-  constexpr int CQ = kGemmCQ;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int r = lane & 15, g = lane >> 4;
   const bool up = EPI == EPI_GATEUP && wave >= 2;
@@ -107,12 +107,14 @@ __global__ void __launch_bounds__(256) k_q4_gemm(GemmArgs a) {
   // per lane each; quads past the run reload the run's first) and the x rows
   // 16 wave .. +15 at columns 128 qc + 8 lane (clamped into the row; rows
   // past n repeat row n - 1; neither is used)
-  // double-buffered x runs of 2 quads in two distinct LDS arrays, filled by
-  // global-to-LDS loads; row b at pitch 256 columns, 16-byte chunk p of row b
-  // at position p ^ (b & 15)
-  constexpr int DQ = 2;
-  __shared__ __align__(16) uint16_t xa[64 * 256];
-  __shared__ __align__(16) uint16_t xb2[64 * 256];
+  // double-buffered x runs of CQ quads in two distinct LDS arrays, filled by
+  // global-to-LDS loads; row b at pitch 128 CQ columns, 16-byte chunk p of
+  // row b at position p ^ (b & 15)
+  constexpr int DQ = CQ;
+  constexpr int RW = 128 * DQ, CPR = 16 * DQ, RPI = 64 / CPR;   // halves and chunks per row, rows per load
+  __shared__ __align__(16) uint16_t xa[64 * RW];
+  __shared__ __align__(16) uint16_t xb2[64 * RW];
+  static_assert(EPI != EPI_GATEUP || 2 * TPW * 4 * 64 * 16 <= 64 * RW * 2, "exchange fits in xa");
   auto load_w = [&](int qc, u4v (&cw)[TPW][CQ], uint32_t (&sw)[TPW][CQ]) {
     const int nq = min(DQ, q_end - qc);
 #pragma unroll
@@ -128,13 +130,13 @@ __global__ void __launch_bounds__(256) k_q4_gemm(GemmArgs a) {
   };
   auto load_x = [&](int qc, uint16_t* buf) {
 #pragma unroll
-    for (int i = 0; i < 8; i++) {
-      const int b = 16 * wave + 2 * i + (lane >> 5);
+    for (int i = 0; i < 16 / RPI; i++) {
+      const int b = 16 * wave + RPI * i + lane / CPR;
       const int bs = min(b, a.n - 1);
-      const int p = lane & 31;
+      const int p = lane % CPR;
       const int col = min(qc * 128 + (p ^ (b & 15)) * 8, a.K - 8);
       __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint32_t*>(a.x + (long)bs * a.ldx + col),
-                                       reinterpret_cast<uint32_t*>(buf + (16 * wave + 2 * i) * 256), 16, 0, 0);
+                                       reinterpret_cast<uint32_t*>(buf + (16 * wave + RPI * i) * RW), 16, 0, 0);
     }
   };
   auto compute = [&](const uint16_t* buf, const u4v (&cw)[TPW][CQ], const uint32_t (&sw)[TPW][CQ], int nq) {
@@ -162,7 +164,7 @@ __global__ void __launch_bounds__(256) k_q4_gemm(GemmArgs a) {
           for (int c = 0; c < 4; c++) {
             const int b = 16 * c + r;
             const int p = (16 * i + 4 * g + w) ^ (b & 15);
-            xv[c] = *reinterpret_cast<const h8_t*>(buf + b * 256 + p * 8);
+            xv[c] = *reinterpret_cast<const h8_t*>(buf + b * RW + p * 8);
           }
 #pragma unroll
           for (int c = 0; c < 4; c++) acc[t][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(hi, xv[c], acc[t][c], 0, 0, 0);

@@ -140,9 +140,11 @@ q4_status set_attrs() {
   e = e != hipSuccess ? e : max_lds(&k_fd_partial<512, true, true>, (int)fd_lds_bytes<512>());
   e = e != hipSuccess ? e : max_lds(&k_fd_rows4<256>, (int)rows4_lds_bytes<256>());
   e = e != hipSuccess ? e : max_lds(&k_fd_rows4<512>, (int)rows4_lds_bytes<512>());
-  e = e != hipSuccess ? e : max_lds(&k_q4_gemm<EPI_STORE, 1>, (int)kGemmLds);
-  e = e != hipSuccess ? e : max_lds(&k_q4_gemm<EPI_STORE, 2>, (int)kGemmLds);
-  e = e != hipSuccess ? e : max_lds(&k_q4_gemm<EPI_GATEUP, 1>, (int)kGemmLds);
+  e = e != hipSuccess ? e : max_lds(&k_q4_gemm<EPI_STORE, 1, kChunkRunQ>, (int)kGemmLds);
+  e = e != hipSuccess ? e : max_lds(&k_q4_gemm<EPI_STORE, 2, kChunkRunQ>, (int)kGemmLds);
+  e = e != hipSuccess ? e : max_lds(&k_q4_gemm<EPI_GATEUP, 1, kChunkRunQ>, (int)kGemmLds);
+  e = e != hipSuccess ? e : max_lds(&k_q4_gemm<EPI_STORE, 1, kGemmRunQ>, (int)kGemmLds);
+  e = e != hipSuccess ? e : max_lds(&k_q4_gemm<EPI_STORE, 2, kGemmRunQ>, (int)kGemmLds);
   e = e != hipSuccess ? e : gemv_attrs<1, 0>();
   e = e != hipSuccess ? e : gemv_attrs<4, 0>();
   e = e != hipSuccess ? e : gemv_attrs<1, 1>();
@@ -629,8 +631,8 @@ q4_status enqueue_chunk(const q4dec_model* m, const ChunkLayout& L, void* ws, co
   }
   auto gemm = [&](GemmArgs& g, int wgs, const ChunkPlan& p) {
     g.NQ = p.NQ; g.NQs = p.NQs;
-    if (p.tpw == 2) hipLaunchKernelGGL((k_q4_gemm<EPI_STORE, 2>), dim3(wgs, p.S), dim3(256), kGemmLds, st, g);
-    else hipLaunchKernelGGL((k_q4_gemm<EPI_STORE, 1>), dim3(wgs, p.S), dim3(256), kGemmLds, st, g);
+    if (p.tpw == 2) hipLaunchKernelGGL((k_q4_gemm<EPI_STORE, 2, kChunkRunQ>), dim3(wgs, p.S), dim3(256), kGemmLds, st, g);
+    else hipLaunchKernelGGL((k_q4_gemm<EPI_STORE, 1, kChunkRunQ>), dim3(wgs, p.S), dim3(256), kGemmLds, st, g);
   };
   for (int l = 0; l < m->n_layers; l++) {
     const q4dec_layer& ly = m->layers[l];
@@ -739,7 +741,7 @@ q4_status enqueue_chunk(const q4dec_model* m, const ChunkLayout& L, void* ws, co
       g.K = H; g.NQ = (int)ceil_div(H, 128); g.NQs = g.NQ;
       g.x = xf; g.ldx = H; g.n = n;
       g.a_out = a16; g.ld_a = I;
-      hipLaunchKernelGGL((k_q4_gemm<EPI_GATEUP, 1>), dim3(ceil_div(g.seg[0].T, 2), 1), dim3(256), kGemmLds, st, g);
+      hipLaunchKernelGGL((k_q4_gemm<EPI_GATEUP, 1, kChunkRunQ>), dim3(ceil_div(g.seg[0].T, 2), 1), dim3(256), kGemmLds, st, g);
     }
     // ---- down projection
     {
@@ -1097,8 +1099,8 @@ q4_status q4_gemm(const void* packed, int N, int K, const uint16_t* x, int n, fl
   g.x = x; g.ldx = K; g.n = n;
   g.y = y; g.ldy = N; g.y_split = 0;
   const dim3 grid(gseg_wgs(g.seg[0], p.tpw), 1);
-  if (p.tpw == 2) hipLaunchKernelGGL((k_q4_gemm<EPI_STORE, 2>), grid, dim3(256), kGemmLds, S(stream), g);
-  else hipLaunchKernelGGL((k_q4_gemm<EPI_STORE, 1>), grid, dim3(256), kGemmLds, S(stream), g);
+  if (p.tpw == 2) hipLaunchKernelGGL((k_q4_gemm<EPI_STORE, 2, kGemmRunQ>), grid, dim3(256), kGemmLds, S(stream), g);
+  else hipLaunchKernelGGL((k_q4_gemm<EPI_STORE, 1, kGemmRunQ>), grid, dim3(256), kGemmLds, S(stream), g);
   return launch_status();
 }
 
