@@ -105,8 +105,9 @@ __global__ void __launch_bounds__(256) k_q4_gemm(GemmArgs a) {
 
   // one run: the weights (TPW tiles x CQ quads, a 16-byte load and a scale
   // per lane each; quads past the run reload the run's first) and the x rows
-  // 16 wave .. +15 at columns 128 qc + 8 lane (clamped into the row; rows
-  // past n repeat row n - 1; neither is used)
+  // 16 wave .. +15 from column 128 qc, 16 CQ chunks of 8 columns per row, one
+  // chunk per lane and 64 / (16 CQ) rows per load (chunks are clamped into
+  // the row and rows past n repeat row n - 1; neither is used)
   // double-buffered x runs of CQ quads in two distinct LDS arrays, filled by
   // global-to-LDS loads; row b at pitch 128 CQ columns, 16-byte chunk p of
   // row b at position p ^ (b & 15)
