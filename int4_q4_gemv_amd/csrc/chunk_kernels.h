@@ -18,7 +18,7 @@
 // and its lowest bit is at least 2^-24; packed fp16 multiply and fma), and each
 // product is two MFMAs.  Sums are fp32 in the MFMA accumulators.  The chunk's
 // x rows are staged in LDS 128 or 256 columns at a time (direct global-to-LDS loads,
-// two rows per instruction; 16-byte chunk p of row b at position p ^ (b & 15),
+// 2 or 4 rows per instruction; 16-byte chunk p of row b at position p ^ (b & 15),
 // so the 16 rows a 16-lane group reads fall in distinct banks).
 //
 // A workgroup is 4 waves; each wave owns TPW row tiles and all 64 chunk rows
