@@ -533,7 +533,9 @@ q4_status begin_step(const q4dec_model* m, const StepPtrs& P, const int32_t* tok
 
 // ------------------------------------------------------- prefill chunk ----
 constexpr int kChunkSplits = 8;       // attention splits per (row, KV head) of a chunk
-constexpr int kRows4Splits = 16;      // the same for the 4-row kernel of the full layers
+constexpr int kRows4Splits = 16;      // the same for the 4-row kernel of the full layers, and
+constexpr int kRows4SplitsLong = 32;  // ... when the rows attend kRows4Long positions or more
+constexpr int kRows4Long = 4096;
 
 // A matrix product of a chunk: one 16-row tile per wave and S runs of K
 // (S <= max_s; S > 1 writes partial products that the norm or finishing
@@ -587,7 +589,7 @@ ChunkLayout chunk_layout(const q4dec_model* m) {
   L.y = take(sizeof(float) * L.ymax * R * H);
   L.a = take(sizeof(uint16_t) * R * I);
   L.xf = take(sizeof(uint16_t) * R * H);
-  const size_t apart_full = (size_t)R * std::max(kChunkSplits, kRows4Splits) * Hq * (Df + 4);
+  const size_t apart_full = (size_t)R * std::max(kChunkSplits, kRows4SplitsLong) * Hq * (Df + 4);
   const size_t apart_ring = (size_t)R * Hs * kChunkSplits * (Hq / Hs) * (Ds + 4);
   L.apart = take(sizeof(float) * std::max(apart_full, apart_ring));
   L.total = off;
@@ -708,7 +710,7 @@ q4_status enqueue_chunk(const q4dec_model* m, const ChunkLayout& L, void* ws, co
       a.pos0[0] = pos0;
       if (a.rpw <= 1 && !a.vrow && (D == 256 || D == 512)) {
         // 16 query heads fill the columns: 4 rows share each K/V tile instead
-        a.S = kRows4Splits;
+        a.S = pos0 + n >= kRows4Long ? kRows4SplitsLong : kRows4Splits;
         if (D == 256) launch_rows4_d<256>(a, 1, o16, st);
         else launch_rows4_d<512>(a, 1, o16, st);
       } else {

@@ -194,14 +194,14 @@ def test_prefill_argument_checks(stream):
         gm.prefill(list(range(8)), cfg.full_cap - 4)
 
 
-@pytest.mark.parametrize("n", [64, 23])
-def test_12b_prefill_layers_vs_oracle(orc, stream, n):
+@pytest.mark.parametrize("n, pos0", [(64, 2048), (23, 2048), (64, 6000)])
+def test_12b_prefill_layers_vs_oracle(orc, stream, n, pos0):
     """A 12B-shape sliding and full layer (layers 0 and 5 of a 6-layer model)
-    each run as a one-layer chunk of n rows at positions 2048 .. (the ring
-    wraps), against the oracle under the composed-output bar."""
-    print(f"12B prefill layers n={n}", flush=True)
-    cfg = dataclasses.replace(synth.FULL48, n_layers=6, full_cap=4096)
-    pos0 = 2048
+    each run as a one-layer chunk of n rows at positions pos0 .. (the ring
+    wraps), against the oracle under the composed-output bar.  From 4096
+    positions on, the full layer's 4-row kernel takes 32 splits instead of 16."""
+    print(f"12B prefill layers n={n} pos0={pos0}", flush=True)
+    cfg = dataclasses.replace(synth.FULL48, n_layers=6, full_cap=8192)
     s = torch.cuda.Stream()
     with torch.cuda.stream(s):
         gm, om = build_pair(orc, cfg, 5, pos0, gen_device=DEV)
@@ -214,8 +214,8 @@ def test_12b_prefill_layers_vs_oracle(orc, stream, n):
         torch.cuda.synchronize()
         ref_h = o1.run_layer(0, o1.embed_tokens(toks), pos0)
         ref_logits, _ = o1.run_head(ref_h[-1:])
-        assert_close_composed(h, ref_h, what=f"12B prefill layer {l}: residual (n={n})")
-        assert_close_composed(logits[None], ref_logits, what=f"12B prefill layer {l}: logits (n={n})")
+        assert_close_composed(h, ref_h, what=f"12B prefill layer {l}: residual (n={n}, pos0={pos0})")
+        assert_close_composed(logits[None], ref_logits, what=f"12B prefill layer {l}: logits (n={n}, pos0={pos0})")
         check_argmax(logits[None], am, ref_logits, 1.6e-2)
         print(f"  layer {l} ok", flush=True)
     del gm
