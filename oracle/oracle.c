@@ -82,7 +82,10 @@ int orc_num_threads(void) {
  * (a positive scale); the codes are taken against the stored fp16 scale;
  * q = clamp(round_half_away(w / d), -8, 7) with w / d an IEEE fp32 quotient,
  * so +absmax maps to 8 and is clipped to 7; a zero (or underflowing) scale
- * gives all-zero codes. */
+ * gives all-zero codes.  A block with a non-finite weight, or whose scale
+ * absmax/8 overflows fp16 (above 65504 after rounding), has no q4_0 encoding:
+ * it is stored as the zero block (scale 0, every code 0), the same rule as
+ * the int8 format below. */
 void orc_q4_pack(const float* w, int64_t N, int64_t K, uint8_t* blocks) {
   const int64_t nb = K / 32;
 #pragma omp parallel for schedule(static)
@@ -91,19 +94,20 @@ void orc_q4_pack(const float* w, int64_t N, int64_t K, uint8_t* blocks) {
       const float* src = w + n * K + b * 32;
       uint8_t* blk = blocks + (n * nb + b) * 18;
       float amax = 0.0f;
+      int finite = 1;
       for (int i = 0; i < 32; i++) {
+        if (!isfinite(src[i])) finite = 0;
         float a = fabsf(src[i]);
         if (a > amax) amax = a;
       }
-      uint16_t d16 = orc_f32_to_f16(amax / 8.0f);
+      uint16_t d16 = finite ? orc_f32_to_f16(amax / 8.0f) : 0;
       float d = (float)orc_f16_to_f64(d16);
+      if (!isfinite(d)) { d16 = 0; d = 0.0f; }
       int q[32];
       for (int i = 0; i < 32; i++) {
-        if (d == 0.0f || !isfinite(d)) { q[i] = 0; continue; }
-        float r = src[i] / d;               /* IEEE fp32 division */
-        float rr = roundf(r);               /* half away from zero */
-        int qi = (rr > 7.0f) ? 7 : (rr < -8.0f ? -8 : (int)rr);
-        q[i] = qi;
+        if (d == 0.0f) { q[i] = 0; continue; }
+        float rr = roundf(src[i] / d);      /* IEEE fp32 quotient, half away from zero */
+        q[i] = (rr > 7.0f) ? 7 : (rr < -8.0f ? -8 : (int)rr);
       }
       blk[0] = (uint8_t)(d16 & 0xFF);
       blk[1] = (uint8_t)(d16 >> 8);

@@ -63,6 +63,31 @@ def test_pack_counts_nonfinite_blocks():
     assert blk[3, 0, 0] == 0 and blk[3, 0, 1] == 0 and (blk[3, 0, 2:] == 0x88).all()
 
 
+def test_pack_degenerate_blocks_match_oracle(orc):
+    # non-finite weights and scales that overflow fp16 give the zero block on
+    # both sides, and the GPU counts each such block once
+    rng = np.random.default_rng(1)
+    w = rng.normal(0, 0.02, (48, 256)).astype(np.float32)
+    w[0, 3] = np.inf
+    w[1, 40] = -np.inf
+    w[2, 70] = np.nan
+    w[3, 96:128] = 1e6                               # absmax/8 far past 65504
+    w[4, 128:160] = 8 * 65520.0 / 3; w[4, 130] = -8 * 65520.0   # rounds to inf
+    w[5, :32] = 0.0; w[5, 5] = -8 * 65504.0          # the largest finite scale: kept
+    w[6, 224:256] = np.nan                           # a whole block
+    w[7, 0] = np.nan; w[7, 1] = np.inf               # two in one block: counted once
+    cnt = torch.zeros(1, dtype=torch.int32, device=DEV)
+    packed = q4.q4_pack(torch.from_numpy(w).to(DEV), nonfinite=cnt)
+    gb = q4.q4_unpack(packed, 48, 256).cpu().numpy()
+    rb = orc.q4_pack(w)
+    assert np.array_equal(gb, rb)
+    assert int(cnt.item()) == 7
+    zero = np.array([0, 0] + [0x88] * 16, dtype=np.uint8)
+    for n, b in [(0, 0), (1, 1), (2, 2), (3, 3), (4, 4), (6, 7), (7, 0)]:
+        assert np.array_equal(rb[n, b], zero), (n, b)
+    assert rb[5, 0, 0] == 0xFF and rb[5, 0, 1] == 0x7B
+
+
 def _grid_weights(N, K, seed, unit=False):
     rng = np.random.default_rng(seed)
     q = rng.integers(-8, 8, size=(N, K))

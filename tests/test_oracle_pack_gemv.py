@@ -98,6 +98,46 @@ def test_codes_use_the_stored_fp16_scale(orc):
     assert s == f16bits(0.125) and codes == canon_bytes(q)
 
 
+@pytest.mark.parametrize("bad", [float("inf"), float("-inf"), float("nan")])
+def test_nonfinite_weight_gives_zero_block(orc, bad):
+    # a block holding a non-finite weight has no q4_0 encoding: the zero block
+    # (scale 0, every code 0), whatever its other weights
+    w = np.linspace(-0.05, 0.05, 32)
+    w[11] = bad
+    s, codes = pack1(orc, w)
+    assert s == 0 and codes == [0x88] * 16
+
+
+def test_overflowing_scale_gives_zero_block(orc):
+    # absmax/8 must be representable in fp16: 8 * 65504 keeps the largest
+    # finite scale; 8 * 65520 rounds (ties to even) to inf, and 1e6 is far past
+    w = np.zeros(32)
+    w[0] = -8 * 65504.0
+    w[1] = 4 * 65504.0
+    s, codes = pack1(orc, w)
+    q = np.zeros(32, dtype=int); q[0] = -8; q[1] = 4
+    assert s == 0x7BFF and codes == canon_bytes(q)
+    for amax in (8 * 65520.0, 1e6):
+        w = np.full(32, amax / 3)
+        w[7] = -amax
+        s, codes = pack1(orc, w)
+        assert s == 0 and codes == [0x88] * 16
+
+
+def test_degenerate_block_leaves_its_neighbours(orc):
+    # only the block that holds the bad value is zeroed
+    rng = np.random.default_rng(3)
+    w = rng.normal(0, 0.02, (3, 128)).astype(np.float32)
+    ref = orc.q4_pack(w.copy())
+    w[1, 40] = np.nan
+    w[2, 100] = 1e6
+    blk = orc.q4_pack(w)
+    zero = np.array([0, 0] + [0x88] * 16, dtype=np.uint8)
+    assert np.array_equal(blk[1, 1], zero) and np.array_equal(blk[2, 3], zero)
+    keep = np.ones((3, 4), bool); keep[1, 1] = False; keep[2, 3] = False
+    assert np.array_equal(blk[keep], ref[keep])
+
+
 def _grid_matrix(N, K, seed, unit_scale=False):
     """Codes in [-8,7] with one -8 per block (so the block's absmax is 8d and
     packing must reproduce the codes exactly), fp16 scales."""
