@@ -88,6 +88,22 @@ def _declare(L):
     L.orc_run_layer.argtypes = [_p, _i, _p, _i, _i64]
     L.orc_head.restype = _i
     L.orc_head.argtypes = [_p, _p, _i, _p, _p]
+    L.orc_stage_qkv.restype = _i
+    L.orc_stage_qkv.argtypes = [_p, _i, _p, _i, _p, _p, _p, _p]
+    L.orc_stage_finish.restype = _i
+    L.orc_stage_finish.argtypes = [_p, _i, _p, _p, _p, _i, _i64, _p]
+    L.orc_stage_attend.restype = _i
+    L.orc_stage_attend.argtypes = [_p, _i, _p, _i, _i64, _p]
+    L.orc_stage_oproj.restype = _i
+    L.orc_stage_oproj.argtypes = [_p, _i, _p, _i, _p]
+    L.orc_stage_gateup.restype = _i
+    L.orc_stage_gateup.argtypes = [_p, _i, _p, _i, _p, _p]
+    L.orc_stage_down.restype = _i
+    L.orc_stage_down.argtypes = [_p, _i, _p, _i, _p]
+    L.orc_head_input.restype = _i
+    L.orc_head_input.argtypes = [_p, _p, _i, _p]
+    L.orc_head_logits.restype = _i
+    L.orc_head_logits.argtypes = [_p, _p, _i, _p, _p]
 
 
 def _ptr(a: np.ndarray):
@@ -396,6 +412,103 @@ class OracleModel:
         am = np.empty(n, dtype=np.int32)
         if lib().orc_head(C.byref(m), _ptr(h), n, _ptr(logits) if logits is not None else None, _ptr(am)) != 0:
             raise ValueError("oracle head rejected its arguments")
+        return logits, am
+
+    # ---- the layer's six stages and the head's two (orc_run_layer and
+    # orc_head compose them); each takes the previous stage's storage values,
+    # so a stage can be fed another implementation's rounding points
+    def _dims(self, l: int):
+        L = self.layers[l]
+        D = self.full_head_dim if L.is_full else self.sl_head_dim
+        Hkv = 1 if L.is_full else self.sl_kv_heads
+        return D, Hkv
+
+    def stage_qkv(self, l: int, h):
+        """-> (x16 uint16 [n, hidden], q [n, Hq*D], k [n, Hkv*D], v [n, Hkv*D])"""
+        h = np.ascontiguousarray(np.atleast_2d(h), dtype=np.float64)
+        n = h.shape[0]
+        D, Hkv = self._dims(l)
+        x16 = np.empty((n, self.hidden), dtype=np.uint16)
+        q = np.empty((n, self.n_heads * D)); k = np.empty((n, Hkv * D)); v = np.empty((n, Hkv * D))
+        m, keep = self._struct()
+        if lib().orc_stage_qkv(C.byref(m), l, _ptr(h), n, _ptr(x16), _ptr(q), _ptr(k), _ptr(v)) != 0:
+            raise ValueError("oracle stage_qkv rejected its arguments")
+        return x16, q, k, v
+
+    def stage_finish(self, l: int, q, k, v, pos0: int):
+        """Writes the rows' K/V into layer l's cache; -> q16 uint16 [n, Hq, D]."""
+        q = np.ascontiguousarray(np.atleast_2d(q), dtype=np.float64)
+        k = np.ascontiguousarray(np.atleast_2d(k), dtype=np.float64)
+        v = np.ascontiguousarray(np.atleast_2d(v), dtype=np.float64)
+        n = q.shape[0]
+        D, _ = self._dims(l)
+        q16 = np.empty((n, self.n_heads, D), dtype=np.uint16)
+        m, keep = self._struct()
+        if lib().orc_stage_finish(C.byref(m), l, _ptr(q), _ptr(k), _ptr(v), n, pos0, _ptr(q16)) != 0:
+            raise ValueError("oracle stage_finish rejected its arguments")
+        return q16
+
+    def stage_attend(self, l: int, q16, pos0: int):
+        """-> att float64 [n, Hq, D] over layer l's cache."""
+        q16 = np.ascontiguousarray(q16, dtype=np.uint16)
+        D, _ = self._dims(l)
+        q16 = q16.reshape(-1, self.n_heads, D)
+        n = q16.shape[0]
+        att = np.empty((n, self.n_heads, D))
+        m, keep = self._struct()
+        if lib().orc_stage_attend(C.byref(m), l, _ptr(q16), n, pos0, _ptr(att)) != 0:
+            raise ValueError("oracle stage_attend rejected its arguments")
+        return att
+
+    def stage_oproj(self, l: int, o16, h):
+        """-> h + RMSNorm(Wo o16, post_attn_norm)"""
+        D, _ = self._dims(l)
+        o16 = np.ascontiguousarray(o16, dtype=np.uint16).reshape(-1, self.n_heads * D)
+        h = np.array(np.atleast_2d(h), dtype=np.float64, copy=True, order="C")
+        m, keep = self._struct()
+        if lib().orc_stage_oproj(C.byref(m), l, _ptr(o16), h.shape[0], _ptr(h)) != 0:
+            raise ValueError("oracle stage_oproj rejected its arguments")
+        return h
+
+    def stage_gateup(self, l: int, h):
+        """-> (x16 uint16 [n, hidden], a16 uint16 [n, inter])"""
+        h = np.ascontiguousarray(np.atleast_2d(h), dtype=np.float64)
+        n = h.shape[0]
+        x16 = np.empty((n, self.hidden), dtype=np.uint16)
+        a16 = np.empty((n, self.inter), dtype=np.uint16)
+        m, keep = self._struct()
+        if lib().orc_stage_gateup(C.byref(m), l, _ptr(h), n, _ptr(x16), _ptr(a16)) != 0:
+            raise ValueError("oracle stage_gateup rejected its arguments")
+        return x16, a16
+
+    def stage_down(self, l: int, a16, h):
+        """-> (h + RMSNorm(Wd a16, post_ff_norm)) * layer_scalar"""
+        a16 = np.ascontiguousarray(a16, dtype=np.uint16).reshape(-1, self.inter)
+        h = np.array(np.atleast_2d(h), dtype=np.float64, copy=True, order="C")
+        m, keep = self._struct()
+        if lib().orc_stage_down(C.byref(m), l, _ptr(a16), h.shape[0], _ptr(h)) != 0:
+            raise ValueError("oracle stage_down rejected its arguments")
+        return h
+
+    def head_input(self, h):
+        """-> x16 = fp16(RMSNorm(h, final_norm)) uint16 [n, hidden]"""
+        h = np.ascontiguousarray(np.atleast_2d(h), dtype=np.float64)
+        x16 = np.empty((h.shape[0], self.hidden), dtype=np.uint16)
+        m, keep = self._struct()
+        if lib().orc_head_input(C.byref(m), _ptr(h), h.shape[0], _ptr(x16)) != 0:
+            raise ValueError("oracle head_input rejected its arguments")
+        return x16
+
+    def head_logits(self, x16, want_logits: bool = True):
+        """-> (softcapped logits float64 [n, vocab] or None, argmax int32 [n])"""
+        x16 = np.ascontiguousarray(np.atleast_2d(x16), dtype=np.uint16)
+        n = x16.shape[0]
+        logits = np.empty((n, self.vocab), dtype=np.float64) if want_logits else None
+        am = np.empty(n, dtype=np.int32)
+        m, keep = self._struct()
+        if lib().orc_head_logits(C.byref(m), _ptr(x16), n, _ptr(logits) if logits is not None else None,
+                                 _ptr(am)) != 0:
+            raise ValueError("oracle head_logits rejected its arguments")
         return logits, am
 
     def decode_step(self, tokens, pos0: int, want_logits: bool = True):

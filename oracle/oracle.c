@@ -449,9 +449,6 @@ int orc_embed(const orc_model* m, const int32_t* tokens, int n, double* h) {
   return 0;
 }
 
-/* One decoder layer on the residual stream h [n][hidden] (updated in place);
- * row i sits at position pos0 + i; the layer's cache receives every row's
- * K/V before any row attends. */
 /* the product of a layer matrix in the model's weight format */
 static void wgemv(const orc_model* m, const uint8_t* blocks, int64_t N, int64_t K,
                   const uint16_t* x, int B, double* y) {
@@ -459,55 +456,67 @@ static void wgemv(const orc_model* m, const uint8_t* blocks, int64_t N, int64_t 
   else orc_q4_gemv(blocks, N, K, x, B, y);
 }
 
-int orc_run_layer(const orc_model* m, int l, double* h, int n, int64_t pos0) {
-  if (check_rows(m, l, n, pos0)) return -1;
-  const int H = m->hidden, Hq = m->n_heads, I = m->inter;
-  const int Hs = m->sl_kv_heads, Ds = m->sl_head_dim, Df = m->full_head_dim;
-  const int64_t R = m->ring, W = m->window;
-  const int Dmax = Ds > Df ? Ds : Df;
-  const int64_t qdim = (int64_t)Hq * Dmax;
-  const int HI = H > I ? H : I;
-  double* t0 = (double*)malloc(sizeof(double) * (size_t)HI);
-  uint16_t* x16 = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)n * HI);
-  double* qv = (double*)malloc(sizeof(double) * (size_t)n * qdim);
-  double* kv = (double*)malloc(sizeof(double) * (size_t)n * Hs * Dmax);
-  double* vv = (double*)malloc(sizeof(double) * (size_t)n * Hs * Dmax);
-  uint16_t* q16 = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)n * qdim);
-  double* att = (double*)malloc(sizeof(double) * (size_t)n * qdim);
-  double* y = (double*)malloc(sizeof(double) * (size_t)n * HI);
-  double* g = (double*)malloc(sizeof(double) * (size_t)n * I);
-  double* u = (double*)malloc(sizeof(double) * (size_t)n * I);
-  double* tmp = (double*)malloc(sizeof(double) * (size_t)(Dmax > H ? Dmax : H));
+static int layer_ok(const orc_model* m, int l, int n) {
+  return m && n >= 1 && l >= 0 && l < m->n_layers;
+}
 
+/* One decoder layer ([zoo] architecture notes: gemma3_text-like pre/post
+ * norms, attention_k_eq_v on full layers, dual RoPE, layer_scalar), as six
+ * stages that orc_run_layer composes; each stage starts from the storage
+ * values of the previous one (the fp16 rounding points), so a stage can also
+ * be run on another implementation's values.  Row i sits at position pos0+i.
+ *
+ * Stage 1: x16 = fp16(RMSNorm(h, attn_norm)); raw projections q = Wq x16,
+ * k = Wk x16, and v = Wv x16 on sliding layers or the raw k itself on full
+ * layers (attention_k_eq_v).  q [n][Hq*D], k and v [n][Hkv*D]. */
+int orc_stage_qkv(const orc_model* m, int l, const double* h, int n, uint16_t* x16,
+                  double* q, double* k, double* v) {
+  if (!layer_ok(m, l, n)) return -1;
+  const int H = m->hidden, Hq = m->n_heads;
   const orc_layer* L = &m->layers[l];
   const int full = L->is_full;
-  const int D = full ? Df : Ds;
-  const int Hkv = full ? 1 : Hs;
-  const double theta = full ? m->full_theta : m->sl_theta;
-  const int rot = full ? m->full_rot_pairs : m->sl_rot_pairs;
-  const double scale = full ? m->full_scale : m->sl_scale;
-
-  /* attention input norm, fp16 activations into the projections */
+  const int D = full ? m->full_head_dim : m->sl_head_dim;
+  const int Hkv = full ? 1 : m->sl_kv_heads;
+  double* t0 = (double*)malloc(sizeof(double) * (size_t)H);
   for (int i = 0; i < n; i++) {
     orc_rmsnorm(h + (int64_t)i * H, L->attn_norm, H, m->eps, t0);
     to_f16(t0, H, x16 + (int64_t)i * H);
   }
-  wgemv(m, L->wq, (int64_t)Hq * D, H, x16, n, qv);
-  wgemv(m, L->wk, (int64_t)Hkv * D, H, x16, n, kv);
-  if (full) memcpy(vv, kv, sizeof(double) * (size_t)n * Hkv * D); /* attention_k_eq_v: raw k_proj */
-  else wgemv(m, L->wv, (int64_t)Hkv * D, H, x16, n, vv);
+  wgemv(m, L->wq, (int64_t)Hq * D, H, x16, n, q);
+  wgemv(m, L->wk, (int64_t)Hkv * D, H, x16, n, k);
+  if (full) memcpy(v, k, sizeof(double) * (size_t)n * Hkv * D);
+  else wgemv(m, L->wv, (int64_t)Hkv * D, H, x16, n, v);
+  free(t0);
+  return 0;
+}
 
+/* Stage 2: per head, q16 = fp16(RoPE(RMSNorm(q, q_norm))); the key
+ * RoPE(RMSNorm(k, k_norm)) and the value (scale-free RMSNorm of v when the
+ * layer normalises V, else v) are rounded to fp16 and written into the
+ * layer's cache at position pos0 + i (ring slot p mod R, full row p; a
+ * kv_format 1 model keeps only the V row of a full layer). */
+int orc_stage_finish(const orc_model* m, int l, const double* q, const double* k, const double* v,
+                     int n, int64_t pos0, uint16_t* q16) {
+  if (check_rows(m, l, n, pos0)) return -1;
+  const int Hq = m->n_heads;
+  const orc_layer* L = &m->layers[l];
+  const int full = L->is_full;
+  const int D = full ? m->full_head_dim : m->sl_head_dim;
+  const int Hkv = full ? 1 : m->sl_kv_heads;
+  const int64_t R = m->ring;
+  const double theta = full ? m->full_theta : m->sl_theta;
+  const int rot = full ? m->full_rot_pairs : m->sl_rot_pairs;
+  double* tmp = (double*)malloc(sizeof(double) * (size_t)D);
   for (int i = 0; i < n; i++) {
     const int64_t P = pos0 + i;
     for (int hh = 0; hh < Hq; hh++) {
-      double* qh = qv + (int64_t)i * Hq * D + (int64_t)hh * D;
-      orc_rmsnorm(qh, L->q_norm, D, m->eps, tmp);
+      orc_rmsnorm(q + (int64_t)i * Hq * D + (int64_t)hh * D, L->q_norm, D, m->eps, tmp);
       orc_rope(tmp, D, P, theta, rot);
       to_f16(tmp, D, q16 + (int64_t)i * Hq * D + (int64_t)hh * D);
     }
     for (int gg = 0; gg < Hkv; gg++) {
-      double* kh = kv + (int64_t)i * Hkv * D + (int64_t)gg * D;
-      double* vh = vv + (int64_t)i * Hkv * D + (int64_t)gg * D;
+      const double* kh = k + (int64_t)i * Hkv * D + (int64_t)gg * D;
+      const double* vh = v + (int64_t)i * Hkv * D + (int64_t)gg * D;
       orc_rmsnorm(kh, L->k_norm, D, m->eps, tmp);
       orc_rope(tmp, D, P, theta, rot);
       uint16_t* kdst; uint16_t* vdst;
@@ -523,19 +532,55 @@ int orc_run_layer(const orc_model* m, int l, double* h, int n, int64_t pos0) {
       else to_f16(vh, D, vdst);
     }
   }
-  if (full && m->kv_format == 1)
-    orc_flash_full_vrow(q16, L->v_cache, m->full_cap, Hq, D, pos0, n, L->k_norm, theta, rot, scale, att);
-  else if (full) orc_flash_full(q16, L->k_cache, L->v_cache, m->full_cap, Hq, D, pos0, n, scale, att);
-  else orc_flash_ring(q16, L->k_cache, L->v_cache, Hq, Hkv, D, R, W, pos0, n, scale, att);
+  free(tmp);
+  return 0;
+}
 
-  /* output projection, post-attention norm, residual */
-  to_f16(att, (int64_t)n * Hq * D, q16);
-  wgemv(m, L->wo, H, (int64_t)Hq * D, q16, n, y);
+/* Stage 3: attention of the rows' fp16 queries q16 [n][Hq][D] over the
+ * layer's cache (every row of the block already written), att [n][Hq][D]. */
+int orc_stage_attend(const orc_model* m, int l, const uint16_t* q16, int n, int64_t pos0, double* att) {
+  if (check_rows(m, l, n, pos0)) return -1;
+  const orc_layer* L = &m->layers[l];
+  const int full = L->is_full;
+  const int D = full ? m->full_head_dim : m->sl_head_dim;
+  const int Hkv = full ? 1 : m->sl_kv_heads;
+  const double theta = full ? m->full_theta : m->sl_theta;
+  const int rot = full ? m->full_rot_pairs : m->sl_rot_pairs;
+  const double scale = full ? m->full_scale : m->sl_scale;
+  if (full && m->kv_format == 1)
+    orc_flash_full_vrow(q16, L->v_cache, m->full_cap, m->n_heads, D, pos0, n, L->k_norm, theta, rot, scale, att);
+  else if (full) orc_flash_full(q16, L->k_cache, L->v_cache, m->full_cap, m->n_heads, D, pos0, n, scale, att);
+  else orc_flash_ring(q16, L->k_cache, L->v_cache, m->n_heads, Hkv, D, m->ring, m->window, pos0, n, scale, att);
+  return 0;
+}
+
+/* Stage 4: output projection of the fp16 attention output o16 [n][Hq*D],
+ * post-attention RMSNorm, residual: h += RMSNorm(Wo o16, post_attn_norm). */
+int orc_stage_oproj(const orc_model* m, int l, const uint16_t* o16, int n, double* h) {
+  if (!layer_ok(m, l, n)) return -1;
+  const int H = m->hidden;
+  const orc_layer* L = &m->layers[l];
+  const int D = L->is_full ? m->full_head_dim : m->sl_head_dim;
+  double* y = (double*)malloc(sizeof(double) * (size_t)n * H);
+  double* t0 = (double*)malloc(sizeof(double) * (size_t)H);
+  wgemv(m, L->wo, H, (int64_t)m->n_heads * D, o16, n, y);
   for (int i = 0; i < n; i++) {
     orc_rmsnorm(y + (int64_t)i * H, L->post_attn_norm, H, m->eps, t0);
     for (int c = 0; c < H; c++) h[(int64_t)i * H + c] += t0[c];
   }
-  /* gated MLP */
+  free(y); free(t0);
+  return 0;
+}
+
+/* Stage 5: gated MLP input: x16 = fp16(RMSNorm(h, pre_ff_norm)),
+ * a16 = fp16(gelu_tanh(Wg x16) * (Wu x16)), a16 [n][inter]. */
+int orc_stage_gateup(const orc_model* m, int l, const double* h, int n, uint16_t* x16, uint16_t* a16) {
+  if (!layer_ok(m, l, n)) return -1;
+  const int H = m->hidden, I = m->inter;
+  const orc_layer* L = &m->layers[l];
+  double* t0 = (double*)malloc(sizeof(double) * (size_t)H);
+  double* g = (double*)malloc(sizeof(double) * (size_t)n * I);
+  double* u = (double*)malloc(sizeof(double) * (size_t)n * I);
   for (int i = 0; i < n; i++) {
     orc_rmsnorm(h + (int64_t)i * H, L->pre_ff_norm, H, m->eps, t0);
     to_f16(t0, H, x16 + (int64_t)i * H);
@@ -543,8 +588,20 @@ int orc_run_layer(const orc_model* m, int l, double* h, int n, int64_t pos0) {
   wgemv(m, L->wg, I, H, x16, n, g);
   wgemv(m, L->wu, I, H, x16, n, u);
   for (int64_t e = 0; e < (int64_t)n * I; e++) g[e] = orc_gelu_tanh(g[e]) * u[e];
-  to_f16(g, (int64_t)n * I, x16);
-  wgemv(m, L->wd, H, I, x16, n, y);
+  to_f16(g, (int64_t)n * I, a16);
+  free(t0); free(g); free(u);
+  return 0;
+}
+
+/* Stage 6: down projection, post-FF RMSNorm, residual, layer scalar:
+ * h = (h + RMSNorm(Wd a16, post_ff_norm)) * layer_scalar. */
+int orc_stage_down(const orc_model* m, int l, const uint16_t* a16, int n, double* h) {
+  if (!layer_ok(m, l, n)) return -1;
+  const int H = m->hidden;
+  const orc_layer* L = &m->layers[l];
+  double* y = (double*)malloc(sizeof(double) * (size_t)n * H);
+  double* t0 = (double*)malloc(sizeof(double) * (size_t)H);
+  wgemv(m, L->wd, H, m->inter, a16, n, y);
   for (int i = 0; i < n; i++) {
     orc_rmsnorm(y + (int64_t)i * H, L->post_ff_norm, H, m->eps, t0);
     for (int c = 0; c < H; c++) {
@@ -552,20 +609,60 @@ int orc_run_layer(const orc_model* m, int l, double* h, int n, int64_t pos0) {
       *hc = (*hc + t0[c]) * (double)L->layer_scalar;
     }
   }
-  free(t0); free(x16); free(qv); free(kv); free(vv); free(q16); free(att); free(y); free(g); free(u); free(tmp);
+  free(y); free(t0);
   return 0;
 }
 
-/* final norm, tied fp16 head, softcap, greedy argmax (lowest index on ties) */
-int orc_head(const orc_model* m, const double* h, int n, double* logits, int32_t* argmax) {
-  if (!m || n < 1) return -1;
-  const int H = m->hidden, V = m->vocab;
-  double* t0 = (double*)malloc(sizeof(double) * (size_t)H);
+/* One decoder layer on the residual stream h [n][hidden] (updated in place):
+ * the six stages in order; the layer's cache receives every row's K/V before
+ * any row attends. */
+int orc_run_layer(const orc_model* m, int l, double* h, int n, int64_t pos0) {
+  if (check_rows(m, l, n, pos0)) return -1;
+  const int H = m->hidden, Hq = m->n_heads, I = m->inter;
+  const int Hs = m->sl_kv_heads, Ds = m->sl_head_dim, Df = m->full_head_dim;
+  const int Dmax = Ds > Df ? Ds : Df;
+  const int64_t qdim = (int64_t)Hq * Dmax;
+  const int64_t kvdim = (int64_t)(Hs > 1 ? Hs : 1) * Dmax;
   uint16_t* x16 = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)n * H);
+  uint16_t* a16 = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)n * I);
+  double* qv = (double*)malloc(sizeof(double) * (size_t)n * qdim);
+  double* kv = (double*)malloc(sizeof(double) * (size_t)n * kvdim);
+  double* vv = (double*)malloc(sizeof(double) * (size_t)n * kvdim);
+  uint16_t* q16 = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)n * qdim);
+  double* att = (double*)malloc(sizeof(double) * (size_t)n * qdim);
+  const int D = m->layers[l].is_full ? Df : Ds;
+  int rc = orc_stage_qkv(m, l, h, n, x16, qv, kv, vv);
+  if (rc == 0) rc = orc_stage_finish(m, l, qv, kv, vv, n, pos0, q16);
+  if (rc == 0) rc = orc_stage_attend(m, l, q16, n, pos0, att);
+  if (rc == 0) {
+    to_f16(att, (int64_t)n * Hq * D, q16);             /* o16: the output projection's input */
+    rc = orc_stage_oproj(m, l, q16, n, h);
+  }
+  if (rc == 0) rc = orc_stage_gateup(m, l, h, n, x16, a16);
+  if (rc == 0) rc = orc_stage_down(m, l, a16, n, h);
+  free(x16); free(a16); free(qv); free(kv); free(vv); free(q16); free(att);
+  return rc;
+}
+
+/* final norm, tied fp16 head, softcap, greedy argmax (lowest index on ties)
+ * ([zoo] architecture notes: tied embeddings, final softcap; [128k]: the head
+ * emits the greedy id).  orc_head_input: x16 = fp16(RMSNorm(h, final_norm));
+ * orc_head_logits: logits = c * tanh(E x16 / c) and the argmax. */
+int orc_head_input(const orc_model* m, const double* h, int n, uint16_t* x16) {
+  if (!m || n < 1) return -1;
+  const int H = m->hidden;
+  double* t0 = (double*)malloc(sizeof(double) * (size_t)H);
   for (int i = 0; i < n; i++) {
     orc_rmsnorm(h + (int64_t)i * H, m->final_norm, H, m->eps, t0);
     to_f16(t0, H, x16 + (int64_t)i * H);
   }
+  free(t0);
+  return 0;
+}
+
+int orc_head_logits(const orc_model* m, const uint16_t* x16, int n, double* logits, int32_t* argmax) {
+  if (!m || n < 1) return -1;
+  const int H = m->hidden, V = m->vocab;
   double* z = (double*)malloc(sizeof(double) * (size_t)n * V);
   orc_f16_gemv(m->embed, V, H, x16, n, z);
   for (int i = 0; i < n; i++) {
@@ -578,8 +675,17 @@ int orc_head(const orc_model* m, const double* h, int n, double* logits, int32_t
     if (argmax) argmax[i] = best;
   }
   if (logits) memcpy(logits, z, sizeof(double) * (size_t)n * V);
-  free(z); free(t0); free(x16);
+  free(z);
   return 0;
+}
+
+int orc_head(const orc_model* m, const double* h, int n, double* logits, int32_t* argmax) {
+  if (!m || n < 1) return -1;
+  uint16_t* x16 = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)n * m->hidden);
+  int rc = orc_head_input(m, h, n, x16);
+  if (rc == 0) rc = orc_head_logits(m, x16, n, logits, argmax);
+  free(x16);
+  return rc;
 }
 
 int orc_decode_step(const orc_model* m, const int32_t* tokens, int n, int64_t pos0,

@@ -216,6 +216,36 @@ def test_layerwise_parts_compose_to_the_step(orc):
     assert np.array_equal(whole, parts) and np.array_equal(am, am2)
 
 
+@pytest.mark.parametrize("n", [1, 4])
+def test_stages_compose_to_the_layer(orc, n):
+    """The six layer stages and the two head stages, chained through their
+    storage values (x16, q16, o16 = fp16 of the attention, a16), give run_layer
+    and run_head bit for bit, and write the same cache rows (the GPU's stages
+    are compared against these one at a time)."""
+    cfg = synth.TOY
+    m = build_oracle_model(orc, cfg, 6, 125)     # rows 125..128 wrap the 128-slot ring
+    toks = synth.tokens(cfg, n, 6)
+    a = clone(m)
+    b = clone(m)
+    ha = a.embed_tokens(toks)
+    hb = ha.copy()
+    for l in range(cfg.n_layers):
+        ha = a.run_layer(l, ha, 125)
+        x16, q, k, v = b.stage_qkv(l, hb)
+        q16 = b.stage_finish(l, q, k, v, 125)
+        att = b.stage_attend(l, q16, 125)
+        o16 = orc.f64_to_f16(att.ravel()).reshape(att.shape)
+        hm = b.stage_oproj(l, o16, hb)
+        x2, a16 = b.stage_gateup(l, hm)
+        hb = b.stage_down(l, a16, hm)
+        assert np.array_equal(ha, hb), l
+    for La, Lb in zip(a.layers, b.layers):
+        assert np.array_equal(La.k_cache, Lb.k_cache) and np.array_equal(La.v_cache, Lb.v_cache)
+    la, ama = a.run_head(ha)
+    lb, amb = b.head_logits(b.head_input(hb))
+    assert np.array_equal(la, lb) and np.array_equal(ama, amb)
+
+
 def test_deep_random_stack_amplifies_last_bit_changes(orc):
     """Why the 48-layer step is compared per layer: in the oracle itself, a
     1-ulp change of one fp16 embedding element moves the logits of a 48-layer
