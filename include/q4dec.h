@@ -47,7 +47,9 @@ typedef int q4_status;
 
 /* Human-readable name of a status code (static string). */
 const char* q4dec_status_str(q4_status s);
-/* Library version string (static). */
+/* Library version string (static): "q4dec <version> gfx950 src <hash>", where
+ * <hash> is the first 16 hex digits of the SHA-256 of the library's sources
+ * (the binding refuses a library whose hash differs from its tree's). */
 const char* q4dec_version(void);
 
 /* ------------------------------------------------------------------------ */
@@ -262,9 +264,15 @@ size_t decode_step_workspace_size(const q4dec_model* m, int n);
  * tokens: host int32 [n].  logits: device fp32 [n][vocab] or NULL.
  * argmax: device int32 [n] or NULL (greedy id, lowest index on ties).
  * ws: device workspace of decode_step_workspace_size(m, n) bytes.
- * The first call for a given (model, caches, n, ws, outputs, stream) captures a
- * HIP graph of the step; later calls replay it (positions and tokens are read
- * on the device, so one graph serves every position).
+ * The first call for a given (model descriptor and layer table, n, ws)
+ * captures a HIP graph of the step; later calls replay it on any stream.
+ * Positions, tokens and the logits/argmax pointers are written to the
+ * workspace by a kernel launched before the graph and read on the device,
+ * so one graph serves every position and every pair of output buffers.  At
+ * most 16 graphs are kept: capturing a 17th first destroys the least
+ * recently used one, after synchronising the stream it last ran on.
+ * A width-4 block finishes all rows first, then its rows share every K/V
+ * tile they read (one pass over each layer's cache per block).
  * Errors: Q4_ERANGE (pos0 < 0; pos0 + n - 1 >= full_cap; R < W + n - 1;
  * token outside [0, vocab)); Q4_ESHAPE (n outside 1..4, ring < 32 or
  * unsupported dimensions); Q4_EINVAL; Q4_ENOSPACE; Q4_EALIGN; Q4_EHIP. */
@@ -278,6 +286,34 @@ q4_status decode_step(const q4dec_model* m, const int32_t* tokens, int n, int po
  * layer of the step.  Errors: Q4_EINVAL, Q4_ESHAPE, Q4_ENOSPACE, Q4_EHIP. */
 q4_status decode_step_hidden(const q4dec_model* m, const void* ws, size_t ws_bytes, int n,
                              float* h_out, void* stream);
+
+/* Stages of the last layer of the most recent step run with workspace `ws`
+ * (rows 0 .. n-1; the tests compare each with the oracle fed the same inputs;
+ * gemma4-12b card, architecture notes, for the layer they belong to):
+ *   Q4_STAGE_H_OUT   fp32 [n][hidden]  residual stream after the layer
+ *   Q4_STAGE_H_MID   fp32 [n][hidden]  residual after attention (+ post-attn norm)
+ *   Q4_STAGE_X_ATTN  fp16 [n][hidden]  attention input (RMSNorm, attn_norm)
+ *   Q4_STAGE_QKV     fp32 [n][ld]      raw q | k | v projections (v on sliding
+ *                                      layers only); ld = the widest layer's row
+ *   Q4_STAGE_Q16     fp16 [n][Hq][D]   queries after q_norm and RoPE
+ *   Q4_STAGE_O16     fp16 [n][Hq][D]   attention output, input of the o-proj
+ *   Q4_STAGE_X_MLP   fp16 [n][hidden]  MLP input (RMSNorm, pre_ff_norm)
+ *   Q4_STAGE_A16     fp16 [n][inter]   gelu_tanh(gate) * up
+ *   Q4_STAGE_X_HEAD  fp16 [n][hidden]  head input (final RMSNorm)
+ * decode_step_stage_bytes gives the size (0 for a bad argument); D is the
+ * last layer's head size.  decode_step_stage copies that many bytes to dst
+ * (device).  Errors: Q4_EINVAL (null pointer, unknown stage), Q4_ESHAPE,
+ * Q4_ENOSPACE (ws or dst too small), Q4_EHIP. */
+enum {
+  Q4_STAGE_H_OUT = 0, Q4_STAGE_H_MID = 1, Q4_STAGE_X_ATTN = 2, Q4_STAGE_QKV = 3, Q4_STAGE_Q16 = 4,
+  Q4_STAGE_O16 = 5, Q4_STAGE_X_MLP = 6, Q4_STAGE_A16 = 7, Q4_STAGE_X_HEAD = 8
+};
+size_t decode_step_stage_bytes(const q4dec_model* m, int n, int stage);
+q4_status decode_step_stage(const q4dec_model* m, const void* ws, size_t ws_bytes, int n, int stage,
+                            void* dst, size_t dst_bytes, void* stream);
+
+/* Number of captured decode-step graphs the library holds (at most 16). */
+int q4dec_graph_count(void);
 
 /* Same step without graph capture (every kernel launched directly). */
 q4_status decode_step_eager(const q4dec_model* m, const int32_t* tokens, int n, int pos0,

@@ -9,6 +9,8 @@ the built library every entry point raises.
 from __future__ import annotations
 
 import ctypes as C
+import glob
+import hashlib
 import math
 import os
 import subprocess
@@ -29,11 +31,25 @@ Q4_OK, Q4_EINVAL, Q4_ESHAPE, Q4_EALIGN, Q4_ERANGE, Q4_ENOSPACE, Q4_EHIP = 0, -1,
 Q4_F32, Q4_BF16 = 0, 1
 
 
+def source_hash() -> str:
+    """First 16 hex digits of the SHA-256 over the library's sources (csrc/
+    and include/q4dec.h, in name order): compiled into the library and
+    reported by q4dec_version()."""
+    files = sorted(glob.glob(os.path.join(_HERE, "csrc", "*.h")) + glob.glob(os.path.join(_HERE, "csrc", "*.hip")))
+    files.append(os.path.join(_ROOT, "include", "q4dec.h"))
+    h = hashlib.sha256()
+    for f in files:
+        h.update(os.path.basename(f).encode() + b"\0")
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
 def build(verbose: bool = False) -> str:
     """Compile csrc/ for gfx950 into libq4dec.so (always recompiles)."""
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
     tmp = LIB_PATH + ".tmp"
-    cmd = [hipcc, *HIPCC_FLAGS, "-o", tmp, SRC]
+    cmd = [hipcc, *HIPCC_FLAGS, f'-DQ4DEC_SRC_HASH="{source_hash()}"', "-o", tmp, SRC]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed:\n" + r.stdout + r.stderr)
@@ -58,8 +74,13 @@ def _lib_raw():
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is not built; run int4_q4_gemv_amd.build() "
                                "(or __graft_entry__.build()) first")
-        _lib = C.CDLL(LIB_PATH)
-        _declare(_lib)
+        L = C.CDLL(LIB_PATH)
+        _declare(L)
+        built = L.q4dec_version().decode().rsplit(" ", 1)[-1]
+        if built != source_hash():
+            raise RuntimeError(f"{LIB_PATH} was built from other sources (library {built}, tree "
+                               f"{source_hash()}); rebuild it with int4_q4_gemv_amd.build()")
+        _lib = L
     return _lib
 
 
@@ -123,6 +144,12 @@ def _declare(L):
         fn.restype = _i
         fn.argtypes = [C.POINTER(Model), _p, _i, _i, _p, _p, _p, _sz, _p]
     L.q4dec_release.restype = _i
+    L.q4dec_graph_count.restype = _i
+    L.q4dec_graph_count.argtypes = []
+    L.decode_step_stage_bytes.restype = _sz
+    L.decode_step_stage_bytes.argtypes = [C.POINTER(Model), _i, _i]
+    L.decode_step_stage.restype = _i
+    L.decode_step_stage.argtypes = [C.POINTER(Model), _p, _sz, _i, _i, _p, _sz, _p]
     L.decode_step_hidden.restype = _i
     L.decode_step_hidden.argtypes = [C.POINTER(Model), _p, _sz, _i, _p, _p]
     L.q4_gemm.restype = _i
@@ -143,6 +170,7 @@ EXPORTS = ["q4dec_status_str", "q4dec_version", "q4_packed_bytes", "q4_pack", "q
            "q4_gemv", "q8_packed_bytes", "q8_pack", "q8_unpack", "q8_gemv", "flash_decode_workspace_size", "flash_decode_full",
            "flash_decode_full_vrow", "flash_decode_ring",
            "decode_step_workspace_size", "decode_step", "decode_step_hidden", "decode_step_eager",
+           "decode_step_stage_bytes", "decode_step_stage", "q4dec_graph_count",
            "q4_gemm", "prefill_chunk_workspace_size", "prefill_chunk",
            "q4_spec_accept", "q4_stream_read_sink_words", "q4_stream_read", "q4dec_release"]
 
@@ -365,6 +393,7 @@ class DecodeModel:
                           c.sl_theta, c.full_theta, c.sl_scale, c.full_scale, c.eps, c.softcap,
                           embed.data_ptr(), final_norm.data_ptr(), arr, int(weight_format), int(kv_format))
         self._ws = {}
+        self._argmax = {}
 
     def workspace(self, n: int):
         if n not in self._ws:
@@ -376,13 +405,20 @@ class DecodeModel:
 
     def step(self, tokens, pos0: int, logits: torch.Tensor | None = None,
              argmax: torch.Tensor | None = None, graph: bool = True, want_logits: bool = True):
+        """One decode step of len(tokens) rows at positions pos0 ..; returns
+        (logits [n, vocab] or None, argmax [n]).  Without an ``argmax`` the
+        model's own buffer for n rows is used and returned: the next step of
+        the same width overwrites it (clone it to keep it).  Fresh ``logits``
+        are allocated unless given."""
         toks = [int(t) for t in tokens]
         n = len(toks)
         dev = self.embed.device
         if logits is None and want_logits:
             logits = torch.empty((n, self.cfg.vocab), dtype=torch.float32, device=dev)
         if argmax is None:
-            argmax = torch.empty(n, dtype=torch.int32, device=dev)
+            if n not in self._argmax:
+                self._argmax[n] = torch.zeros(n, dtype=torch.int32, device=dev)
+            argmax = self._argmax[n]
         ws = self.workspace(n)
         tk = (C.c_int32 * n)(*toks)
         fn = lib().decode_step if graph else lib().decode_step_eager
@@ -428,6 +464,31 @@ def _hidden(self, n: int) -> torch.Tensor:
 
 
 DecodeModel.hidden = _hidden
+
+STAGE_H_OUT, STAGE_H_MID, STAGE_X_ATTN, STAGE_QKV, STAGE_Q16, STAGE_O16, STAGE_X_MLP, STAGE_A16, STAGE_X_HEAD = range(9)
+_STAGE_DTYPE = {STAGE_H_OUT: torch.float32, STAGE_H_MID: torch.float32, STAGE_QKV: torch.float32}
+
+
+def _stage(self, n: int, stage: int) -> torch.Tensor:
+    """A stage of the last layer of the most recent step of width n
+    (decode_step_stage): [n, ...] fp32 or fp16 as the header lists."""
+    ws = self.workspace(n)
+    nb = int(lib().decode_step_stage_bytes(C.byref(self.desc), n, stage))
+    if nb == 0:
+        raise Q4Error("decode_step_stage_bytes", Q4_EINVAL)
+    dt = _STAGE_DTYPE.get(stage, torch.float16)
+    out = torch.empty(nb // (4 if dt == torch.float32 else 2), dtype=dt, device=self.embed.device)
+    _check("decode_step_stage", lib().decode_step_stage(C.byref(self.desc), _ptr(ws), ws.numel(), n, stage,
+                                                        _ptr(out), nb, _stream()))
+    return out.view(n, -1)
+
+
+DecodeModel.stage = _stage
+
+
+def graph_count() -> int:
+    """Captured decode-step graphs the library holds."""
+    return int(lib().q4dec_graph_count())
 
 
 def release():

@@ -42,6 +42,8 @@ struct AttnFin {
   const float2* rope_cs;  // [row][cs_ld]: (cos, sin) of pair i < D/2 at the row's position
   int cs_ld;
   float eps;
+  uint16_t* q_out;        // [rows][Hq][D] or NULL: split 0 also stores its finished queries
+                          // (the step's stage export reads them)
 };
 
 struct AttnArgs {
@@ -454,6 +456,14 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D <= 2
       }
     }
     __syncthreads();
+    if (f.q_out && split == 0) {
+      constexpr int CH = D / 8;               // 16-byte chunks per head
+      for (int i = threadIdx.x; i < a.GQ * CH; i += 256) {
+        const int jq = i / CH, c = i - jq * CH;
+        *reinterpret_cast<u4v*>(f.q_out + ((long)row * a.Hq + kvh * a.GQ + jq) * D + c * 8) =
+            *reinterpret_cast<const u4v*>(q16 + jq * D + c * 8);
+      }
+    }
     // the workgroup whose own row lies in its range stores that row
     if (P >= st && P < en) {
       const long so = (long)(a.ring ? P % a.R : P) * D;

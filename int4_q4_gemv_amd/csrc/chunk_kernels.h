@@ -287,7 +287,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) k
   const int rlast = min(a.n_rows, row0 + 4) - 1;
   const bool live = row0 + wave <= rlast;              // wave-uniform
   const int row = live ? row0 + wave : rlast;
-  const int base = a.pos0[seq];
+  // first position: from the decode step's parameters on the device, else the host's
+  const int base = __builtin_amdgcn_readfirstlane(
+      a.sp ? *(const __attribute__((address_space(1))) int*)(&a.sp->pos0) : a.pos0[seq]);
   const int P = base + row;
   const int lo = a.ring ? max(0, base + row0 - a.W + 1) : 0;
   const int Pl = base + rlast;
@@ -475,6 +477,9 @@ struct ChunkFinArgs {
   int rot_pairs;
   float eps;
   int pos0;
+  const StepParams* sp;    // decode step: the first position is read here instead of pos0
+  const float2* rope_cs;   // decode step: (cos, sin) per row and pair [row][cs_ld] (k_step_begin's
+  int cs_ld;               // table, the same values rope_cs() forms); NULL: formed here
   uint16_t* q16;           // [n][Hq][D]
   uint16_t* kc;
   uint16_t* vc;
@@ -490,7 +495,7 @@ __global__ void __launch_bounds__(64) k_chunk_finish(ChunkFinArgs a) {
   constexpr int FE = D / 64, FEH = fin_h<D>();
   const int row = blockIdx.x, job = blockIdx.y;
   const int lane = threadIdx.x;
-  const int pos = a.pos0 + row;
+  const int pos = (a.sp ? a.sp->pos0 : a.pos0) + row;
   int kind, head;                                 // 0 q, 1 k, 2 v
   if (job < a.Hq) { kind = 0; head = job; }
   else { kind = 1 + ((job - a.Hq) & 1); head = (job - a.Hq) >> 1; }
@@ -512,8 +517,10 @@ __global__ void __launch_bounds__(64) k_chunk_finish(ChunkFinArgs a) {
   for (int e = 0; e < FE; e++) wv[e] = 1.0f;
   float2 cs[FEH];
 #pragma unroll
-  for (int e = 0; e < FEH; e++)
-    cs[e] = rope_cs(pos, D == 64 ? (lane & 31) : lane * FEH + e, D, a.theta, kind == 2 ? 0 : a.rot_pairs);
+  for (int e = 0; e < FEH; e++) {
+    const int pr = D == 64 ? (lane & 31) : lane * FEH + e;
+    cs[e] = a.rope_cs ? a.rope_cs[(long)row * a.cs_ld + pr] : rope_cs(pos, pr, D, a.theta, kind == 2 ? 0 : a.rot_pairs);
+  }
   const long slot = a.ring ? ((long)head * a.R + pos % a.R) * D : (long)pos * D;
   if (kind == 0) {
     fin_load<D>(wv, a.q_norm);

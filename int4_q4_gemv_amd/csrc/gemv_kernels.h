@@ -34,6 +34,8 @@ struct StepParams {       // written on the device at the start of every step
   int pos0;
   int n;
   int tokens[4];
+  float* logits;          // this step's outputs (logits may be NULL): the captured
+  int32_t* argmax;        // step graph reads them here, so it is output-independent
 };
 
 struct GemvSeg {
@@ -449,7 +451,8 @@ struct HeadArgs {
   const uint16_t* x;       // [4][H]
   int V, H;
   float softcap;
-  float* logits;           // [n][V] or NULL
+  float* logits;           // [n][V] or NULL (when sp is NULL)
+  const StepParams* sp;    // decode step: the logits pointer is read from here
   unsigned long long* best;  // [4], zeroed before the kernel
   int n_rows;
   int rows_per_wave;
@@ -460,6 +463,7 @@ __global__ void __launch_bounds__(256) k_head(HeadArgs a) {
   __shared__ unsigned long long sbest[4][4];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int n = a.n_rows;
+  float* const logits = a.sp ? a.sp->logits : a.logits;
   const int nchunk = a.H >> 3;           // 16-byte chunks per row
   const int J = (nchunk + 63) >> 6;      // chunks per lane (<= 8)
   u4v xr[B][8];
@@ -508,9 +512,9 @@ __global__ void __launch_bounds__(256) k_head(HeadArgs a) {
       if (bb < n) {
         const float la = a.softcap * tanhf(za / a.softcap);
         const float lb = a.softcap * tanhf(zb / a.softcap);
-        if (lane == 0 && a.logits) {
-          a.logits[(long)bb * a.V + ra] = la;
-          if (hasb) a.logits[(long)bb * a.V + rb] = lb;
+        if (lane == 0 && logits) {
+          logits[(long)bb * a.V + ra] = la;
+          if (hasb) logits[(long)bb * a.V + rb] = lb;
         }
         unsigned long long ka = ((unsigned long long)f32_order_key(la) << 32) | (0xFFFFFFFFu - (uint32_t)ra);
         best[bb] = ka > best[bb] ? ka : best[bb];
@@ -532,10 +536,12 @@ __global__ void __launch_bounds__(256) k_head(HeadArgs a) {
   }
 }
 
-// Reads the argmax slots out and clears them for the next step.
-__global__ void k_argmax_out(unsigned long long* best, int n_rows, int32_t* argmax) {
+// Reads the argmax slots out and clears them for the next step (the output
+// from sp when it is set, else argmax).
+__global__ void k_argmax_out(unsigned long long* best, int n_rows, int32_t* argmax, const StepParams* sp) {
   const int n = n_rows;
   const int i = threadIdx.x;
+  if (sp) argmax = sp->argmax;
   if (i < 4) {
     const unsigned long long m = best[i];
     best[i] = 0ull;

@@ -138,6 +138,7 @@ q4_status set_attrs() {
   e = e != hipSuccess ? e : max_lds(&k_fd_partial<512, false, true>, (int)fd_lds_bytes<512>());
   e = e != hipSuccess ? e : max_lds(&k_fd_partial<128, true, true>, (int)fd_lds_bytes<128>());
   e = e != hipSuccess ? e : max_lds(&k_fd_partial<512, true, true>, (int)fd_lds_bytes<512>());
+  e = e != hipSuccess ? e : max_lds(&k_fd_rows4<128>, (int)rows4_lds_bytes<128>());
   e = e != hipSuccess ? e : max_lds(&k_fd_rows4<256>, (int)rows4_lds_bytes<256>());
   e = e != hipSuccess ? e : max_lds(&k_fd_rows4<512>, (int)rows4_lds_bytes<512>());
   e = e != hipSuccess ? e : max_lds(&k_q4_gemm<EPI_STORE, 1, kChunkRunQ>, (int)kGemmLds);
@@ -159,6 +160,7 @@ void launch_combine(const AttnArgs& a, int n_seq, float* out32, uint16_t* out16,
   const dim3 cgrid(n_seq * a.n_rows * a.Hq, D / 64);  // 256 threads each
   if (a.S <= 16) hipLaunchKernelGGL((k_fd_combine<D, 16>), cgrid, dim3(256), 0, st, a, out32, out16);
   else if (a.S <= 32) hipLaunchKernelGGL((k_fd_combine<D, 32>), cgrid, dim3(256), 0, st, a, out32, out16);
+  else if (a.S <= 64) hipLaunchKernelGGL((k_fd_combine<D, 64>), cgrid, dim3(256), 0, st, a, out32, out16);
   else hipLaunchKernelGGL((k_fd_combine<D, kMaxSplits>), cgrid, dim3(256), 0, st, a, out32, out16);
 }
 
@@ -191,6 +193,14 @@ void launch_rows4_d(const AttnArgs& a, int n_seq, uint16_t* out16, hipStream_t s
   launch_combine<D>(a, n_seq, nullptr, out16, st);
 }
 
+void launch_rows4(const AttnArgs& a, int D, int n_seq, uint16_t* out16, hipStream_t st) {
+  switch (D) {
+    case 128: launch_rows4_d<128>(a, n_seq, out16, st); break;
+    case 256: launch_rows4_d<256>(a, n_seq, out16, st); break;
+    default: launch_rows4_d<512>(a, n_seq, out16, st); break;
+  }
+}
+
 // Split-K partials then the combine (S <= kMaxSplits).
 void launch_fd(const AttnArgs& a, int D, int n_seq, float* out32, uint16_t* out16, hipStream_t st) {
   switch (D) {
@@ -205,12 +215,13 @@ bool valid_d(int D) { return D == 64 || D == 128 || D == 256 || D == 512; }
 
 // ------------------------------------------------------ decode-step layout ----
 struct StepLayout {
-  size_t sp, best, rope, hA, hB, qkv, o, y, a, xf, apart, total;
+  size_t sp, best, rope, hA, hB, qkv, q16, o, y, a, xf, xf2, xh, apart, total;
   int qkv_ld, o_ld;
   int Dmax;
   GemvPlan p_qkv_s, p_qkv_f, p_o_s, p_o_f, p_gu, p_d;
   int ymax;       // largest split count of a product that writes y
   int S_full, S_ring;
+  int S_ring4;    // ring splits of a 4-row verify block (one 32-position tile each)
   bool ok;
 };
 
@@ -262,8 +273,9 @@ StepLayout step_layout(const q4dec_model* m) {
   if (L.p_gu.S != 1 || L.ymax > 4) L.ok = false;
   L.S_full = kFullSplits;
   L.S_ring = (int)std::min<long>(32, std::max<long>(1, ceil_div(m->window, 32)));
+  L.S_ring4 = (int)std::min<long>(64, std::max<long>(1, ceil_div(m->window + kMaxRows - 1, 32)));
   const size_t apart_full = (size_t)kMaxRows * 1 * L.S_full * Hq * (Df + 4);
-  const size_t apart_ring = (size_t)kMaxRows * Hs * L.S_ring * (Hq / Hs) * (Ds + 4);
+  const size_t apart_ring = (size_t)kMaxRows * Hs * std::max(L.S_ring, L.S_ring4) * (Hq / Hs) * (Ds + 4);
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off = align256(off + bytes); return o; };
   L.sp = take(sizeof(StepParams));
@@ -272,10 +284,13 @@ StepLayout step_layout(const q4dec_model* m) {
   L.hA = take(sizeof(float) * kMaxRows * H);
   L.hB = take(sizeof(float) * kMaxRows * H);
   L.qkv = take(sizeof(float) * kMaxRows * L.qkv_ld);
+  L.q16 = take(sizeof(uint16_t) * kMaxRows * L.o_ld);
   L.o = take(sizeof(uint16_t) * kMaxRows * L.o_ld);
   L.y = take(sizeof(float) * L.ymax * kMaxRows * H);
   L.a = take(sizeof(uint16_t) * kMaxRows * I);
   L.xf = take(sizeof(uint16_t) * kMaxRows * H);
+  L.xf2 = take(sizeof(uint16_t) * kMaxRows * H);
+  L.xh = take(sizeof(uint16_t) * kMaxRows * H);
   L.apart = take(sizeof(float) * std::max(apart_full, apart_ring));
   L.total = off;
   return L;
@@ -286,7 +301,7 @@ struct StepPtrs {
   unsigned long long* best;
   float2* rope;
   float *hA, *hB, *qkv, *y, *apart;
-  uint16_t *o, *a, *xf;
+  uint16_t *q16, *o, *a, *xf, *xf2, *xh;
 };
 
 StepPtrs step_ptrs(const StepLayout& L, void* ws) {
@@ -298,24 +313,36 @@ StepPtrs step_ptrs(const StepLayout& L, void* ws) {
   p.hA = reinterpret_cast<float*>(b + L.hA);
   p.hB = reinterpret_cast<float*>(b + L.hB);
   p.qkv = reinterpret_cast<float*>(b + L.qkv);
+  p.q16 = reinterpret_cast<uint16_t*>(b + L.q16);
   p.o = reinterpret_cast<uint16_t*>(b + L.o);
   p.y = reinterpret_cast<float*>(b + L.y);
   p.a = reinterpret_cast<uint16_t*>(b + L.a);
   p.xf = reinterpret_cast<uint16_t*>(b + L.xf);
+  p.xf2 = reinterpret_cast<uint16_t*>(b + L.xf2);
+  p.xh = reinterpret_cast<uint16_t*>(b + L.xh);
   p.apart = reinterpret_cast<float*>(b + L.apart);
   return p;
 }
 
-// Launch sequence of one step (every kernel reads positions and the row
-// count from the device-side StepParams, so the sequence is position-free):
+// Launch sequence of one step (every kernel reads positions, the row count
+// and the output pointers from the device-side StepParams, so the sequence is
+// position- and output-free):
 // per layer: input RMSNorm of the residual stream (with the previous layer's
-// post-FF residual), q/k/v projections, attention (q/k/v finishing +
-// split-K partials), combine, output projection, post-attention residual and
-// pre-FF norm, gate/up with GELU * up, down projection; then the final norm,
-// the tied head and the argmax read-out.
+// post-FF residual), q/k/v projections, attention, combine, output
+// projection, post-attention residual and pre-FF norm, gate/up with GELU *
+// up, down projection; then the final norm, the tied head and the argmax
+// read-out.  Attention of one row finishes q/k/v in the partial kernel's
+// prologue.  A width-4 verify block first finishes every row in its own
+// launch (queries to q16, K/V rows into the caches), then its rows share
+// each K/V tile: on a ring layer as MFMA columns of one workgroup ((row,
+// query head) pairs), on a full layer through the 4-row kernel (one wave per
+// row over tiles staged once in LDS), so the block reads each cached
+// position once (Gemma-4-12B-CoreAI card, "v5/ -- ring extent R = 2W": one
+// pass per block; gemma-4-E4B-CoreAI card, ring3/: the GQA fold).
+// Buffers: x of attention (xf), of the MLP (xf2) and of the head (xh) are
+// kept apart, so after a step the workspace holds the last layer's stages.
 template <int B>
-q4_status enqueue_layers(const q4dec_model* m, const StepLayout& L, const StepPtrs& P, int n,
-                         float* logits, int32_t* argmax, hipStream_t st) {
+q4_status enqueue_layers(const q4dec_model* m, const StepLayout& L, const StepPtrs& P, int n, hipStream_t st) {
   const int H = m->hidden, I = m->inter, Hq = m->n_heads;
   const int fmt = m->weight_format;
   for (int l = 0; l < m->n_layers; l++) {
@@ -353,7 +380,10 @@ q4_status enqueue_layers(const q4dec_model* m, const StepLayout& L, const StepPt
       launch_gemv<B, EPI_STORE>(a, pl, t0, pl.W, gemv_lds(B, pl), st);
     }
     // ---- attention: q/k/v finishing, split-K partials, combine
-    {
+    const bool vrow = full && m->kv_format == 1;
+    const float2* rope_l = full ? P.rope + m->sl_head_dim / 2 : P.rope;
+    const int cs_ld = m->sl_head_dim / 2 + m->full_head_dim / 2;
+    if (B == 1) {
       AttnArgs a{};
       a.q = nullptr; a.k = ly.k_cache; a.v = ly.v_cache; a.seq_stride = 0;
       a.Hq = Hq; a.Hkv = Hkv; a.GQ = Hq / Hkv;
@@ -363,14 +393,50 @@ q4_status enqueue_layers(const q4dec_model* m, const StepLayout& L, const StepPt
       a.sp = P.sp; a.part = P.apart;
       a.fin_on = 1;
       a.kvh_major = full ? 0 : 1;
-      if (full && m->kv_format == 1) {
+      if (vrow) {
         a.vrow = 1; a.k = ly.v_cache; a.kw = ly.k_norm; a.theta = m->full_theta; a.krot = m->full_rot_pairs;
       }
       a.fin.qkv = P.qkv; a.fin.ldq = L.qkv_ld; a.fin.q_norm = ly.q_norm; a.fin.k_norm = ly.k_norm;
       a.fin.v_norm = ly.v_norm; a.fin.rot_pairs = full ? m->full_rot_pairs : m->sl_rot_pairs;
-      a.fin.rope_cs = full ? P.rope + m->sl_head_dim / 2 : P.rope;
-      a.fin.cs_ld = m->sl_head_dim / 2 + m->full_head_dim / 2; a.fin.eps = m->eps;
+      a.fin.rope_cs = rope_l; a.fin.cs_ld = cs_ld; a.fin.eps = m->eps;
+      a.fin.q_out = P.q16;
       launch_fd(a, D, 1, nullptr, P.o, st);
+    } else {
+      // every row finished first: queries to q16, K/V rows into the caches
+      {
+        ChunkFinArgs f{};
+        f.qkv = P.qkv; f.ldq = L.qkv_ld; f.ny = 1; f.y_split = 0;
+        f.Hq = Hq; f.Hkv = Hkv; f.ring = full ? 0 : 1; f.R = m->ring;
+        f.v_norm = ly.v_norm; f.vrow = vrow ? 1 : 0;
+        f.q_norm = ly.q_norm; f.k_norm = ly.k_norm;
+        f.theta = full ? m->full_theta : m->sl_theta;
+        f.rot_pairs = full ? m->full_rot_pairs : m->sl_rot_pairs;
+        f.eps = m->eps; f.pos0 = 0; f.sp = P.sp; f.rope_cs = rope_l; f.cs_ld = cs_ld;
+        f.q16 = P.q16; f.kc = ly.k_cache; f.vc = ly.v_cache;
+        const dim3 grid(n, Hq + 2 * Hkv);
+        switch (D) {
+          case 64: hipLaunchKernelGGL(k_chunk_finish<64>, grid, dim3(64), 0, st, f); break;
+          case 128: hipLaunchKernelGGL(k_chunk_finish<128>, grid, dim3(64), 0, st, f); break;
+          case 256: hipLaunchKernelGGL(k_chunk_finish<256>, grid, dim3(64), 0, st, f); break;
+          default: hipLaunchKernelGGL(k_chunk_finish<512>, grid, dim3(64), 0, st, f); break;
+        }
+      }
+      // then the rows' attention over the caches, sharing K/V tiles
+      AttnArgs a{};
+      a.q = P.q16; a.k = ly.k_cache; a.v = ly.v_cache; a.seq_stride = 0;
+      a.Hq = Hq; a.Hkv = Hkv; a.GQ = Hq / Hkv;
+      a.ring = full ? 0 : 1; a.R = m->ring; a.W = m->window;
+      a.n_rows = n; a.S = full ? L.S_full : L.S_ring4;
+      a.scale_log2 = (full ? m->full_scale : m->sl_scale) * 1.4426950408889634f;
+      a.sp = P.sp; a.part = P.apart;
+      a.fin_on = 0;
+      a.kvh_major = full ? 0 : 1;
+      if (vrow) {
+        a.vrow = 1; a.k = ly.v_cache; a.kw = ly.k_norm; a.theta = m->full_theta; a.krot = m->full_rot_pairs;
+      }
+      a.rpw = 16 % a.GQ == 0 ? 16 / a.GQ : 1;
+      if (a.rpw <= 1 && !vrow && full && D >= 128) launch_rows4(a, D, 1, P.o, st);
+      else launch_fd(a, D, 1, nullptr, P.o, st);
     }
     // ---- output projection
     {
@@ -397,9 +463,9 @@ q4_status enqueue_layers(const q4dec_model* m, const StepLayout& L, const StepPt
       ni.h_src = P.hA; ni.y = P.y; ni.ny = (full ? L.p_o_f : L.p_o_s).S; ni.y_split = (long)n * H;
       ni.w_post = ly.post_attn_norm; ni.scalar = 1.0f;
       ni.w_in = ly.pre_ff_norm; ni.h_dst = P.hB; ni.H = H; ni.eps = m->eps;
-      hipLaunchKernelGGL(k_norm_rows<4>, dim3(n), dim3(512), 0, st, ni, P.xf);
+      hipLaunchKernelGGL(k_norm_rows<4>, dim3(n), dim3(512), 0, st, ni, P.xf2);
       a.K = H; a.NQ = pl.NQ; a.W = pl.W; a.NQs = pl.NQs;
-      a.x = P.xf; a.ldx = H;
+      a.x = P.xf2; a.ldx = H;
       a.a_out = P.a; a.inter = I; a.n_rows = n;
       launch_gemv<B, EPI_GATEUP>(a, pl, a.seg[0].T, 2 * pl.W, gemv_lds(B, pl), st);
     }
@@ -425,18 +491,18 @@ q4_status enqueue_layers(const q4dec_model* m, const StepLayout& L, const StepPt
     ni.h_src = P.hB; ni.y = P.y; ni.ny = L.p_d.S; ni.y_split = (long)n * H;
     ni.w_post = last.post_ff_norm; ni.scalar = last.layer_scalar;
     ni.w_in = m->final_norm; ni.h_dst = P.hA; ni.H = H; ni.eps = m->eps;
-    hipLaunchKernelGGL(k_norm_rows<4>, dim3(n), dim3(512), 0, st, ni, P.xf);
+    hipLaunchKernelGGL(k_norm_rows<4>, dim3(n), dim3(512), 0, st, ni, P.xh);
   }
   {
     HeadArgs a{};
-    a.E = m->embed; a.x = P.xf; a.V = m->vocab; a.H = H; a.softcap = m->softcap;
-    a.logits = logits; a.best = P.best; a.n_rows = n;
+    a.E = m->embed; a.x = P.xh; a.V = m->vocab; a.H = H; a.softcap = m->softcap;
+    a.sp = P.sp; a.best = P.best; a.n_rows = n;
     const int waves = 8192;
     a.rows_per_wave = (int)std::max<long>(2, ceil_div(m->vocab, waves));
     if (a.rows_per_wave & 1) a.rows_per_wave++;
     const int grid = (int)ceil_div(ceil_div(m->vocab, a.rows_per_wave), 4);
     hipLaunchKernelGGL((k_head<B>), dim3(grid), dim3(256), 0, st, a);
-    hipLaunchKernelGGL(k_argmax_out, dim3(1), dim3(64), 0, st, P.best, n, argmax);
+    hipLaunchKernelGGL(k_argmax_out, dim3(1), dim3(64), 0, st, P.best, n, nullptr, P.sp);
   }
   return launch_status();
 }
@@ -502,24 +568,50 @@ __global__ void __launch_bounds__(256) k_stream_read(const u4v* p, long n16, uin
 }
 
 // ----------------------------------------------------------- graph cache ----
-std::map<std::string, hipGraphExec_t> g_graphs;
+// Captured step graphs, keyed by everything their kernel arguments hold: the
+// model descriptor and layer table (weights, caches), the row count and the
+// workspace.  Outputs and positions reach the graph through StepParams, so
+// neither is part of the key.  At most kMaxGraphs are kept; the least recently
+// used one is destroyed (after the stream it last ran on has finished it).
+constexpr size_t kMaxGraphs = 16;
 
-std::string graph_key(const q4dec_model* m, int n, const void* ws, size_t ws_bytes, const float* logits,
-                      const int32_t* argmax, hipStream_t st) {
+struct CachedGraph {
+  hipGraphExec_t exec;
+  hipStream_t last_stream;
+  unsigned long long last_use;
+};
+std::map<std::string, CachedGraph> g_graphs;
+unsigned long long g_use_clock = 0;
+
+std::string graph_key(const q4dec_model* m, int n, const void* ws, size_t ws_bytes) {
   std::string k;
   k.append(reinterpret_cast<const char*>(m), sizeof(q4dec_model));
   k.append(reinterpret_cast<const char*>(m->layers), sizeof(q4dec_layer) * m->n_layers);
-  const void* extra[] = {ws, logits, argmax, st};
-  k.append(reinterpret_cast<const char*>(extra), sizeof(extra));
+  k.append(reinterpret_cast<const char*>(&ws), sizeof(ws));
   k.append(reinterpret_cast<const char*>(&n), sizeof(n));
   k.append(reinterpret_cast<const char*>(&ws_bytes), sizeof(ws_bytes));
   return k;
 }
 
+// under g_mu: drop the least recently used graphs until one more fits
+q4_status evict_graphs_locked() {
+  q4_status rc = Q4_OK;
+  while (g_graphs.size() >= kMaxGraphs) {
+    auto victim = g_graphs.begin();
+    for (auto it = g_graphs.begin(); it != g_graphs.end(); ++it)
+      if (it->second.last_use < victim->second.last_use) victim = it;
+    if (hipStreamSynchronize(victim->second.last_stream) != hipSuccess) rc = Q4_EHIP;
+    if (hipGraphExecDestroy(victim->second.exec) != hipSuccess) rc = Q4_EHIP;
+    g_graphs.erase(victim);
+  }
+  return rc;
+}
+
 q4_status begin_step(const q4dec_model* m, const StepPtrs& P, const int32_t* tokens, int n, int pos0,
-                     hipStream_t st) {
+                     float* logits, int32_t* argmax, hipStream_t st) {
   BeginArgs b{};
   b.sp = P.sp; b.pos0 = pos0; b.n = n;
+  b.logits = logits; b.argmax = argmax;
   for (int i = 0; i < 4; i++) b.tokens[i] = i < n ? tokens[i] : 0;
   b.best = P.best;
   b.E = m->embed; b.H = m->hidden; b.emb_scale = (float)std::sqrt((double)m->hidden);
@@ -708,7 +800,7 @@ q4_status enqueue_chunk(const q4dec_model* m, const ChunkLayout& L, void* ws, co
         a.vrow = 1; a.k = ly.v_cache; a.kw = ly.k_norm; a.theta = m->full_theta; a.krot = m->full_rot_pairs;
       }
       a.pos0[0] = pos0;
-      if (a.rpw <= 1 && !a.vrow && (D == 256 || D == 512)) {
+      if (full && a.rpw <= 1 && !a.vrow && (D == 256 || D == 512)) {
         // 16 query heads fill the columns: 4 rows share each K/V tile instead
         a.S = pos0 + n >= kRows4Long ? kRows4SplitsLong : kRows4Splits;
         if (D == 256) launch_rows4_d<256>(a, 1, o16, st);
@@ -774,7 +866,7 @@ q4_status enqueue_chunk(const q4dec_model* m, const ChunkLayout& L, void* ws, co
     if (a.rows_per_wave & 1) a.rows_per_wave++;
     const int grid = (int)ceil_div(ceil_div(m->vocab, a.rows_per_wave), 4);
     hipLaunchKernelGGL((k_head<1>), dim3(grid), dim3(256), 0, st, a);
-    hipLaunchKernelGGL(k_argmax_out, dim3(1), dim3(64), 0, st, best, 1, argmax);
+    hipLaunchKernelGGL(k_argmax_out, dim3(1), dim3(64), 0, st, best, 1, argmax, nullptr);
   }
   return launch_status();
 }
@@ -792,23 +884,25 @@ q4_status decode_step_impl(const q4dec_model* m, const int32_t* tokens, int n, i
   if (rc != Q4_OK) return rc;
   const StepPtrs P = step_ptrs(L, ws);
   hipStream_t st = S(stream);
-  rc = begin_step(m, P, tokens, n, pos0, st);
+  rc = begin_step(m, P, tokens, n, pos0, logits, argmax, st);
   if (rc != Q4_OK) return rc;
   if (!use_graph || st == nullptr) {
-    return n == 1 ? enqueue_layers<1>(m, L, P, n, logits, argmax, st)
-                  : enqueue_layers<4>(m, L, P, n, logits, argmax, st);
+    return n == 1 ? enqueue_layers<1>(m, L, P, n, st) : enqueue_layers<4>(m, L, P, n, st);
   }
-  const std::string key = graph_key(m, n, ws, ws_bytes, logits, argmax, st);
+  const std::string key = graph_key(m, n, ws, ws_bytes);
   hipGraphExec_t exec = nullptr;
   {
     std::lock_guard<std::mutex> lk(g_mu);
     auto it = g_graphs.find(key);
-    if (it != g_graphs.end()) exec = it->second;
+    if (it != g_graphs.end()) {
+      exec = it->second.exec;
+      it->second.last_stream = st;
+      it->second.last_use = ++g_use_clock;
+    }
   }
   if (!exec) {
     if (hipStreamBeginCapture(st, hipStreamCaptureModeThreadLocal) != hipSuccess) return Q4_EHIP;
-    q4_status r2 = n == 1 ? enqueue_layers<1>(m, L, P, n, logits, argmax, st)
-                          : enqueue_layers<4>(m, L, P, n, logits, argmax, st);
+    q4_status r2 = n == 1 ? enqueue_layers<1>(m, L, P, n, st) : enqueue_layers<4>(m, L, P, n, st);
     hipGraph_t graph = nullptr;
     hipError_t e = hipStreamEndCapture(st, &graph);
     if (r2 != Q4_OK || e != hipSuccess || !graph) {
@@ -819,10 +913,38 @@ q4_status decode_step_impl(const q4dec_model* m, const int32_t* tokens, int n, i
     (void)hipGraphDestroy(graph);
     if (e != hipSuccess) return Q4_EHIP;
     std::lock_guard<std::mutex> lk(g_mu);
-    g_graphs[key] = exec;
+    if (evict_graphs_locked() != Q4_OK) {
+      (void)hipGraphExecDestroy(exec);
+      return Q4_EHIP;
+    }
+    g_graphs[key] = CachedGraph{exec, st, ++g_use_clock};
   }
   if (hipGraphLaunch(exec, st) != hipSuccess) return Q4_EHIP;
   return Q4_OK;
+}
+
+// ------------------------------------------------------- stage export ----
+// Buffer and size of a stage of the last layer a step ran (rows 0 .. n-1).
+struct StageView {
+  size_t off, bytes;
+};
+
+bool stage_view(const q4dec_model* m, const StepLayout& L, int n, int stage, StageView& v) {
+  const int H = m->hidden;
+  const bool full = m->layers[m->n_layers - 1].is_full != 0;
+  const int D = full ? m->full_head_dim : m->sl_head_dim;
+  switch (stage) {
+    case Q4_STAGE_H_OUT: v = {L.hA, sizeof(float) * n * H}; return true;
+    case Q4_STAGE_H_MID: v = {L.hB, sizeof(float) * n * H}; return true;
+    case Q4_STAGE_X_ATTN: v = {L.xf, sizeof(uint16_t) * n * H}; return true;
+    case Q4_STAGE_QKV: v = {L.qkv, sizeof(float) * n * L.qkv_ld}; return true;
+    case Q4_STAGE_Q16: v = {L.q16, sizeof(uint16_t) * n * m->n_heads * D}; return true;
+    case Q4_STAGE_O16: v = {L.o, sizeof(uint16_t) * n * m->n_heads * D}; return true;
+    case Q4_STAGE_X_MLP: v = {L.xf2, sizeof(uint16_t) * n * H}; return true;
+    case Q4_STAGE_A16: v = {L.a, sizeof(uint16_t) * n * m->inter}; return true;
+    case Q4_STAGE_X_HEAD: v = {L.xh, sizeof(uint16_t) * n * H}; return true;
+    default: return false;
+  }
 }
 
 }  // namespace
@@ -843,7 +965,10 @@ const char* q4dec_status_str(q4_status s) {
   }
 }
 
-const char* q4dec_version(void) { return "q4dec 0.1 gfx950"; }
+#ifndef Q4DEC_SRC_HASH
+#define Q4DEC_SRC_HASH "unknown"
+#endif
+const char* q4dec_version(void) { return "q4dec 0.2 gfx950 src " Q4DEC_SRC_HASH; }
 
 size_t q4_packed_bytes(int N, int K) {
   if (N < 1 || K < 32 || K % 32) return 0;
@@ -1077,6 +1202,33 @@ q4_status decode_step_hidden(const q4dec_model* m, const void* ws, size_t ws_byt
   return Q4_OK;
 }
 
+size_t decode_step_stage_bytes(const q4dec_model* m, int n, int stage) {
+  if (!m || n < 1 || n > kMaxRows || !model_dims_ok(m)) return 0;
+  const StepLayout L = step_layout(m);
+  StageView v{};
+  if (!L.ok || !stage_view(m, L, n, stage, v)) return 0;
+  return v.bytes;
+}
+
+q4_status decode_step_stage(const q4dec_model* m, const void* ws, size_t ws_bytes, int n, int stage, void* dst,
+                            size_t dst_bytes, void* stream) {
+  if (!m || !m->layers || !ws || !dst) return Q4_EINVAL;
+  if (n < 1 || n > kMaxRows || !model_dims_ok(m)) return Q4_ESHAPE;
+  const StepLayout L = step_layout(m);
+  StageView v{};
+  if (!L.ok) return Q4_ESHAPE;
+  if (!stage_view(m, L, n, stage, v)) return Q4_EINVAL;
+  if (ws_bytes < L.total || dst_bytes < v.bytes) return Q4_ENOSPACE;
+  const void* src = static_cast<const uint8_t*>(ws) + v.off;
+  if (hipMemcpyAsync(dst, src, v.bytes, hipMemcpyDeviceToDevice, S(stream)) != hipSuccess) return Q4_EHIP;
+  return Q4_OK;
+}
+
+int q4dec_graph_count(void) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  return (int)g_graphs.size();
+}
+
 q4_status decode_step(const q4dec_model* m, const int32_t* tokens, int n, int pos0, float* logits,
                       int32_t* argmax, void* ws, size_t ws_bytes, void* stream) {
   return decode_step_impl(m, tokens, n, pos0, logits, argmax, ws, ws_bytes, stream, true);
@@ -1161,8 +1313,10 @@ q4_status q4_stream_read(const void* src, size_t bytes, uint32_t* sink, void* st
 q4_status q4dec_release(void) {
   std::lock_guard<std::mutex> lk(g_mu);
   q4_status rc = Q4_OK;
-  for (auto& kv : g_graphs)
-    if (hipGraphExecDestroy(kv.second) != hipSuccess) rc = Q4_EHIP;
+  for (auto& kv : g_graphs) {
+    if (hipStreamSynchronize(kv.second.last_stream) != hipSuccess) rc = Q4_EHIP;
+    if (hipGraphExecDestroy(kv.second.exec) != hipSuccess) rc = Q4_EHIP;
+  }
   g_graphs.clear();
   return rc;
 }

@@ -10,6 +10,8 @@ struct BeginArgs {
   StepParams* sp;
   int pos0, n;
   int tokens[4];
+  float* logits;            // the step's outputs, published in sp
+  int32_t* argmax;
   unsigned long long* best; // [4] argmax slots
   const uint16_t* E;        // [vocab][H] fp16
   int H;
@@ -35,6 +37,8 @@ __global__ void __launch_bounds__(256) k_step_begin(BeginArgs a) {
       a.sp->pos0 = a.pos0;
       a.sp->n = a.n;
       for (int i = 0; i < 4; i++) a.sp->tokens[i] = a.tokens[i];
+      a.sp->logits = a.logits;
+      a.sp->argmax = a.argmax;
     }
     if (tid < 4) a.best[tid] = 0ull;
   }

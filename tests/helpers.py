@@ -44,6 +44,7 @@ def assert_close_composed(gpu, ref, atol=ATOL, rtol=RTOL, frac=0.98, factor=4.0,
     assert inside >= frac and worst <= factor and rms <= rms_bar, (
         f"{what}: {inside:.5f} of elements within the bar (need {frac}), worst error/bound {worst:.2f} "
         f"(need <= {factor}), rms error {rms:.2e} (need <= {rms_bar:.2e})")
+    return inside
 
 
 def f16bits(t):
@@ -92,3 +93,70 @@ def check_argmax(gpu_logits, gpu_argmax, ref_logits, tol_margin):
             assert ga[i] == int(np.argmax(r)), (i, ga[i], int(np.argmax(r)))
         else:
             assert r[ga[i]] >= top[1] - tol_margin
+
+
+def _f16(bits):
+    return np.asarray(bits, dtype=np.uint16).view(np.float16).astype(np.float64)
+
+
+def check_layer_stages(orc, gm, om, l, h_in, pos0, n, logits, what=""):
+    """Every stage of the last layer of the step ``gm`` just ran (width n at
+    pos0, its last layer being the oracle's layer ``l``; ``h_in`` the residual
+    stream entering it), each against the oracle's stage fed the GPU's own
+    values at the stage's input, so every comparison is elementwise:
+    attention input, raw q/k/v projections, finished queries, the K/V rows
+    written, attention (over the GPU's own caches), o-proj residual, MLP
+    input, GELU * up, down residual, head input and logits.  Writes the
+    GPU's K/V rows into the oracle layer's cache."""
+    import int4_q4_gemv_amd as q4
+    L = om.layers[l]
+    D, Hkv = om._dims(l)
+    Hq = om.n_heads
+    st = lambda s: gm.stage(n, s)
+    h_in = np.asarray(h_in, dtype=np.float64).reshape(n, -1)
+
+    xa = f16bits(st(q4.STAGE_X_ATTN))
+    assert_close(_f16(xa), _f16(om.stage_attn_in(l, h_in)), what=f"{what} attention input")
+    qkv = st(q4.STAGE_QKV).double().cpu().numpy()
+    q_r, k_r, v_r = om.stage_qkv(l, xa)
+    qg, kg = qkv[:, :Hq * D], qkv[:, Hq * D:(Hq + Hkv) * D]
+    vg = kg if L.is_full else qkv[:, (Hq + Hkv) * D:(Hq + 2 * Hkv) * D]
+    assert_close(qg, q_r, what=f"{what} q projection")
+    assert_close(kg, k_r, what=f"{what} k projection")
+    if not L.is_full:
+        assert_close(vg, v_r, what=f"{what} v projection")
+
+    # finishing from the GPU's raw projections (writes the oracle's cache rows)
+    q16_ref = om.stage_finish(l, qg, kg, vg, pos0)
+    q16 = f16bits(st(q4.STAGE_Q16)).reshape(n, Hq, D)
+    assert_close(_f16(q16), _f16(q16_ref), what=f"{what} finished queries")
+    gl = gm.layers[-1]
+    for nm in ("k_cache", "v_cache"):
+        oc = getattr(L, nm)
+        if oc is None or gl.get(nm) is None:
+            continue
+        gc = f16bits(gl[nm])
+        if L.is_full:
+            sel = (slice(pos0, pos0 + n),)
+        else:
+            sel = (slice(None), [(pos0 + i) % om.ring for i in range(n)])
+        assert_close(_f16(gc[sel]), _f16(oc[sel]), what=f"{what} {nm} rows written")
+        oc[sel] = gc[sel]                                 # attention over the GPU's own caches
+    att_ref = om.stage_attend(l, q16, pos0)
+    o16 = f16bits(st(q4.STAGE_O16)).reshape(n, Hq, D)
+    assert_close(_f16(o16), att_ref, what=f"{what} attention output")
+
+    hm = st(q4.STAGE_H_MID).double().cpu().numpy()
+    assert_close(hm, om.stage_oproj(l, o16, h_in), what=f"{what} residual after attention")
+    xm = f16bits(st(q4.STAGE_X_MLP))
+    assert_close(_f16(xm), _f16(om.stage_mlp_in(l, hm)), what=f"{what} MLP input")
+    a16 = f16bits(st(q4.STAGE_A16))
+    assert_close(_f16(a16), _f16(om.stage_gateup(l, xm)), what=f"{what} gelu(gate) * up")
+    ho = st(q4.STAGE_H_OUT).double().cpu().numpy()
+    assert_close(ho, om.stage_down(l, a16, hm), what=f"{what} residual after the layer")
+    xh = f16bits(st(q4.STAGE_X_HEAD))
+    assert_close(_f16(xh), _f16(om.head_input(ho)), what=f"{what} head input")
+    if logits is not None:
+        ref, _ = om.head_logits(xh)
+        assert_close(logits, ref, what=f"{what} logits")
+    return ho

@@ -129,6 +129,43 @@ def test_decode_step_checks():
     assert L.decode_step(C.byref(m), tok, 1, 5, f, f, f, big, None) == q4.Q4_ESHAPE
 
 
+def test_stage_export_sizes_and_checks():
+    from int4_q4_gemv_amd import synth
+    cfg = synth.TOY
+    L = q4.lib()
+    fake = 0x10000
+    lay = (q4.Layer * 2)()
+    for i in range(2):
+        lay[i] = q4.Layer(int(cfg.is_full(i)), 1, *([fake] * 13), 1.0, fake, fake)
+    m = q4.Model(cfg.hidden, cfg.n_heads, cfg.inter, cfg.vocab, 2, cfg.sl_kv_heads, cfg.sl_head_dim,
+                 cfg.full_head_dim, cfg.window, cfg.ring, cfg.full_cap, cfg.sl_rot_pairs,
+                 cfg.full_rot_pairs, cfg.sl_theta, cfg.full_theta, 1.0, 1.0, 1e-6, 30.0, fake, fake, lay)
+    H, I, Hq = cfg.hidden, cfg.inter, cfg.n_heads
+    D = cfg.full_head_dim if cfg.is_full(1) else cfg.sl_head_dim       # the last layer's head size
+    ld = max(Hq * cfg.sl_head_dim + 2 * cfg.sl_kv_heads * cfg.sl_head_dim, Hq * cfg.full_head_dim + cfg.full_head_dim)
+    want = {q4.STAGE_H_OUT: 4 * H, q4.STAGE_H_MID: 4 * H, q4.STAGE_X_ATTN: 2 * H, q4.STAGE_QKV: 4 * ld,
+            q4.STAGE_Q16: 2 * Hq * D, q4.STAGE_O16: 2 * Hq * D, q4.STAGE_X_MLP: 2 * H,
+            q4.STAGE_A16: 2 * I, q4.STAGE_X_HEAD: 2 * H}
+    for n in (1, 4):
+        for st, b in want.items():
+            assert L.decode_step_stage_bytes(C.byref(m), n, st) == n * b, (n, st)
+    assert L.decode_step_stage_bytes(C.byref(m), 1, 9) == 0
+    assert L.decode_step_stage_bytes(C.byref(m), 5, 0) == 0
+    need = L.decode_step_workspace_size(C.byref(m), 1)
+    f = C.c_void_p(fake)
+    big = C.c_size_t(need)
+    assert L.decode_step_stage(C.byref(m), f, big, 1, 9, f, C.c_size_t(1 << 20), None) == q4.Q4_EINVAL
+    assert L.decode_step_stage(C.byref(m), f, big, 1, 0, f, C.c_size_t(4 * H - 1), None) == q4.Q4_ENOSPACE
+    assert L.decode_step_stage(C.byref(m), f, C.c_size_t(need - 1), 1, 0, f, C.c_size_t(4 * H), None) == q4.Q4_ENOSPACE
+    assert L.decode_step_stage(C.byref(m), None, big, 1, 0, f, C.c_size_t(4 * H), None) == q4.Q4_EINVAL
+    assert L.q4dec_graph_count() == 0
+
+
+def test_version_carries_the_source_hash():
+    v = q4.lib().q4dec_version().decode()
+    assert v.startswith("q4dec ") and v.endswith(" src " + q4.source_hash())
+
+
 def test_chunk_entry_points_check_their_arguments():
     """q4_gemm and prefill_chunk reject bad calls on the host, before any launch."""
     from int4_q4_gemv_amd import synth

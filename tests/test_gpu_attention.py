@@ -104,6 +104,16 @@ def test_ring_verify_rows(orc, n_rows):
     assert_close(out[0], ref, what=f"ring rows={n_rows}")
 
 
+@pytest.mark.parametrize("P", [2045, 2046, 2047, 4094, 100350])
+def test_ring_verify_rows_across_the_ring_end(orc, P):
+    """4 rows whose slots wrap from R-1 to 0 (P mod 2048 in 2045 .. 2047)."""
+    print(f"ring rows across the end P={P}", flush=True)
+    q, k, v = synth.ring_inputs(P, n_rows=4, n_rejected=0)
+    out = q4.flash_decode_ring(q.to(DEV), k.to(DEV), v.to(DEV), 1024, P, 1.0)
+    ref = orc.flash_ring(f16bits(q), f16bits(k), f16bits(v), 1024, P, 1.0)
+    assert_close(out[0], ref, what=f"ring 4 rows at P={P}")
+
+
 def test_ring_small_window_shapes(orc):
     # toy sliding layer: 4 heads over 2 KV heads, D 64, W 64, R 128
     q, k, v = synth.ring_inputs(200, n_rows=3, n_rejected=0, Hq=4, Hkv=2, D=64, R=128, seed=8)

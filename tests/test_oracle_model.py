@@ -218,7 +218,7 @@ def test_layerwise_parts_compose_to_the_step(orc):
 
 @pytest.mark.parametrize("n", [1, 4])
 def test_stages_compose_to_the_layer(orc, n):
-    """The six layer stages and the two head stages, chained through their
+    """The layer's stages and the two head stages, chained through their
     storage values (x16, q16, o16 = fp16 of the attention, a16), give run_layer
     and run_head bit for bit, and write the same cache rows (the GPU's stages
     are compared against these one at a time)."""
@@ -231,12 +231,12 @@ def test_stages_compose_to_the_layer(orc, n):
     hb = ha.copy()
     for l in range(cfg.n_layers):
         ha = a.run_layer(l, ha, 125)
-        x16, q, k, v = b.stage_qkv(l, hb)
+        q, k, v = b.stage_qkv(l, b.stage_attn_in(l, hb))
         q16 = b.stage_finish(l, q, k, v, 125)
         att = b.stage_attend(l, q16, 125)
         o16 = orc.f64_to_f16(att.ravel()).reshape(att.shape)
         hm = b.stage_oproj(l, o16, hb)
-        x2, a16 = b.stage_gateup(l, hm)
+        a16 = b.stage_gateup(l, b.stage_mlp_in(l, hm))
         hb = b.stage_down(l, a16, hm)
         assert np.array_equal(ha, hb), l
     for La, Lb in zip(a.layers, b.layers):
