@@ -165,6 +165,23 @@ q4_status flash_decode_full(const uint16_t* q, const uint16_t* k, const uint16_t
                             const int32_t* pos0, int n_seq, int n_rows, float scale,
                             float* out, void* ws, size_t ws_bytes, void* stream);
 
+/* flash_decode_full for callers that cannot allocate (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * computation, with the split records in the library's own static device
+ * array of flash_decode_noalloc_max_bytes() = 8,454,144 bytes per GPU
+ * (enough for every call with n_seq * n_rows <= 32 and Hq <= 16, D <= 512)
+ * instead of a workspace argument.  It calls no allocating routine.  Every
+ * call on one GPU shares that array: calls that overlap on one GPU (on
+ * different streams, or from different threads) race and must be ordered
+ * by the caller.  Nothing in the array needs clearing (every record is
+ * written before it is read).  Arguments and results as flash_decode_full;
+ * Q4_ENOSPACE when flash_decode_workspace_size(n_seq, n_rows, Hq, D) exceeds
+ * the array; Q4_EHIP if the array's device address cannot be obtained. */
+size_t flash_decode_noalloc_max_bytes(void);
+q4_status flash_decode_full_noalloc(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t seq_stride,
+                                    int cap, int Hq, int D, const int32_t* pos0, int n_seq, int n_rows,
+                                    float scale, float* out, void* stream);
+
 /* Full-attention flash decode over a cache that keeps ONE fp16 row per
  * position (Gemma-4-12B-CoreAI card, "The per-tier cost": the full-layer K/V
  * pair is the KV term that grows with the context; gemma4-12b card,

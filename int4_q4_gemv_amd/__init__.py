@@ -133,6 +133,10 @@ def _declare(L):
     L.flash_decode_workspace_size.argtypes = [_i, _i, _i, _i]
     L.flash_decode_full.restype = _i
     L.flash_decode_full.argtypes = [_p, _p, _p, _i64, _i, _i, _i, _p, _i, _i, _f, _p, _p, _sz, _p]
+    L.flash_decode_noalloc_max_bytes.restype = _sz
+    L.flash_decode_noalloc_max_bytes.argtypes = []
+    L.flash_decode_full_noalloc.restype = _i
+    L.flash_decode_full_noalloc.argtypes = [_p, _p, _p, _i64, _i, _i, _i, _p, _i, _i, _f, _p, _p]
     L.flash_decode_full_vrow.restype = _i
     L.flash_decode_full_vrow.argtypes = [_p, _p, _i64, _i, _i, _i, _p, C.c_double, _i, _p, _i, _i, _f, _p,
                                          _p, _sz, _p]
@@ -168,7 +172,8 @@ def _declare(L):
 
 EXPORTS = ["q4dec_status_str", "q4dec_version", "q4_packed_bytes", "q4_pack", "q4_unpack",
            "q4_gemv", "q8_packed_bytes", "q8_pack", "q8_unpack", "q8_gemv", "flash_decode_workspace_size", "flash_decode_full",
-           "flash_decode_full_vrow", "flash_decode_ring",
+           "flash_decode_full_vrow", "flash_decode_ring", "flash_decode_noalloc_max_bytes",
+           "flash_decode_full_noalloc",
            "decode_step_workspace_size", "decode_step", "decode_step_hidden", "decode_step_eager",
            "decode_step_stage_bytes", "decode_step_stage", "q4dec_graph_count",
            "q4_gemm", "prefill_chunk_workspace_size", "prefill_chunk",
@@ -319,6 +324,26 @@ def flash_decode_full(q, k, v, pos0, scale: float = 1.0, ws=None):
     _check("flash_decode_full", lib().flash_decode_full(
         _ptr(q.contiguous()), _ptr(k), _ptr(v), k.stride(0), cap, Hq, D, pos, n_seq, n_rows,
         float(scale), _ptr(out), _ptr(ws), ws.numel(), _stream()))
+    return out
+
+
+def flash_decode_full_noalloc(q, k, v, pos0, scale: float = 1.0, out=None):
+    """flash_decode_full with the library's static scratch instead of a
+    workspace (no allocation inside the call; ``out`` may be given so that
+    none happens here either).  Calls overlapping on one GPU race."""
+    _need_cuda(q, k, v)
+    if k.dim() == 2:
+        k, v = k.unsqueeze(0), v.unsqueeze(0)
+    if q.dim() == 3:
+        q = q.unsqueeze(0)
+    n_seq, n_rows, Hq, D = q.shape
+    cap = k.shape[1]
+    pos = (C.c_int32 * n_seq)(*([int(pos0)] * n_seq if isinstance(pos0, int) else [int(p) for p in pos0]))
+    if out is None:
+        out = torch.empty((n_seq, n_rows, Hq, D), dtype=torch.float32, device=q.device)
+    _check("flash_decode_full_noalloc", lib().flash_decode_full_noalloc(
+        _ptr(q.contiguous()), _ptr(k), _ptr(v), k.stride(0), cap, Hq, D, pos, n_seq, n_rows,
+        float(scale), _ptr(out), _stream()))
     return out
 
 

@@ -947,6 +947,34 @@ bool stage_view(const q4dec_model* m, const StepLayout& L, int n, int stage, Sta
   }
 }
 
+// ------------------------------------------------------ static scratch ----
+// The split records of flash_decode_full_noalloc live in one file-scope device
+// array instead of a caller's workspace: kNoAllocScratchBytes covers up to
+// 256 splits of 16 query heads at D = 512 (every call with n_seq * n_rows <= 32,
+// Hq <= 16).  Each GPU the library runs on holds its own copy until the
+// process ends.  Host code never passes the array's name to a kernel (on the
+// host it is a stand-in, not a device address): the device address is taken
+// once per device with hipGetSymbolAddress, with that device current, and
+// kept in g_scratch.
+constexpr size_t kNoAllocScratchBytes = (size_t)256 * 16 * (512 + 4) * sizeof(float);
+__device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+void* g_scratch[kMaxDevices] = {};
+
+// the current device's scratch address (NULL on failure)
+void* scratch_ptr() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lk(g_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    g_scratch[dev] = p;
+  }
+  return g_scratch[dev];
+}
+
 }  // namespace
 
 // =================================================================== C ABI ==
@@ -1103,19 +1131,26 @@ static q4_status fd_common(const uint16_t* q, const uint16_t* k, const uint16_t*
   return Q4_OK;
 }
 
-q4_status flash_decode_full(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t seq_stride,
-                            int cap, int Hq, int D, const int32_t* pos0, int n_seq, int n_rows, float scale,
-                            float* out, void* ws, size_t ws_bytes, void* stream) {
-  q4_status rc = fd_common(q, k, v, seq_stride, Hq, 1, D, pos0, n_seq, n_rows, out, ws, ws_bytes);
-  if (rc != Q4_OK) return rc;
-  if (cap < 1) return Q4_ESHAPE;
-  if (n_seq > 1 && seq_stride < (int64_t)cap * D) return Q4_ESHAPE;
-  long maxlen = 1;
+// host-only checks of a full-attention call (everything but the workspace)
+static q4_status full_args(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t seq_stride, int cap,
+                           int Hq, int D, const int32_t* pos0, int n_seq, int n_rows, float* out, long& maxlen) {
+  if (!q || !k || !v || !pos0 || !out) return Q4_EINVAL;
+  if (n_seq < 1 || n_seq > 64 || n_rows < 1 || n_rows > kMaxRows) return Q4_ESHAPE;
+  if (Hq < 1 || Hq > 16 || !valid_d(D) || seq_stride < 0 || cap < 1) return Q4_ESHAPE;
+  if (n_seq > 1 && (seq_stride == 0 || seq_stride < (int64_t)cap * D)) return Q4_ESHAPE;
+  if (!al16(q) || !al16(k) || !al16(v) || !al16(out) || (seq_stride * 2) % 16) return Q4_EALIGN;
+  maxlen = 1;
   for (int s = 0; s < n_seq; s++) {
     if (pos0[s] < 0 || (long)pos0[s] + n_rows - 1 >= cap) return Q4_ERANGE;
     maxlen = std::max(maxlen, (long)pos0[s] + n_rows);
   }
-  rc = set_attrs();
+  return Q4_OK;
+}
+
+static q4_status full_run(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t seq_stride, int cap,
+                          int Hq, int D, const int32_t* pos0, int n_seq, int n_rows, float scale, float* out,
+                          void* ws, long maxlen, void* stream) {
+  q4_status rc = set_attrs();
   if (rc != Q4_OK) return rc;
   AttnArgs a{};
   a.q = q; a.k = const_cast<uint16_t*>(k); a.v = const_cast<uint16_t*>(v); a.seq_stride = seq_stride;
@@ -1127,6 +1162,33 @@ q4_status flash_decode_full(const uint16_t* q, const uint16_t* k, const uint16_t
   for (int s = 0; s < n_seq; s++) a.pos0[s] = pos0[s];
   launch_fd(a, D, n_seq, out, nullptr, S(stream));
   return launch_status();
+}
+
+q4_status flash_decode_full(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t seq_stride,
+                            int cap, int Hq, int D, const int32_t* pos0, int n_seq, int n_rows, float scale,
+                            float* out, void* ws, size_t ws_bytes, void* stream) {
+  long maxlen = 1;
+  q4_status rc = full_args(q, k, v, seq_stride, cap, Hq, D, pos0, n_seq, n_rows, out, maxlen);
+  if (rc != Q4_OK) return rc;
+  if (!ws) return Q4_EINVAL;
+  if (ws_bytes < flash_decode_workspace_size(n_seq, n_rows, Hq, D)) return Q4_ENOSPACE;
+  if (!al16(ws)) return Q4_EALIGN;
+  return full_run(q, k, v, seq_stride, cap, Hq, D, pos0, n_seq, n_rows, scale, out, ws, maxlen, stream);
+}
+
+size_t flash_decode_noalloc_max_bytes(void) { return kNoAllocScratchBytes; }
+
+q4_status flash_decode_full_noalloc(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t seq_stride,
+                                    int cap, int Hq, int D, const int32_t* pos0, int n_seq, int n_rows,
+                                    float scale, float* out, void* stream) {
+  long maxlen = 1;
+  q4_status rc = full_args(q, k, v, seq_stride, cap, Hq, D, pos0, n_seq, n_rows, out, maxlen);
+  if (rc != Q4_OK) return rc;
+  if (flash_decode_workspace_size(n_seq, n_rows, Hq, D) > kNoAllocScratchBytes) return Q4_ENOSPACE;
+  // the first call on a device (with it current) records its scratch address
+  void* ws = scratch_ptr();
+  if (!ws) return Q4_EHIP;
+  return full_run(q, k, v, seq_stride, cap, Hq, D, pos0, n_seq, n_rows, scale, out, ws, maxlen, stream);
 }
 
 q4_status flash_decode_full_vrow(const uint16_t* q, const uint16_t* vrow, int64_t seq_stride, int cap, int Hq,
