@@ -88,8 +88,12 @@ def _declare(L):
     L.orc_run_layer.argtypes = [_p, _i, _p, _i, _i64]
     L.orc_head.restype = _i
     L.orc_head.argtypes = [_p, _p, _i, _p, _p]
+    L.orc_stage_attn_in.restype = _i
+    L.orc_stage_attn_in.argtypes = [_p, _i, _p, _i, _p]
     L.orc_stage_qkv.restype = _i
-    L.orc_stage_qkv.argtypes = [_p, _i, _p, _i, _p, _p, _p, _p]
+    L.orc_stage_qkv.argtypes = [_p, _i, _p, _i, _p, _p, _p]
+    L.orc_stage_mlp_in.restype = _i
+    L.orc_stage_mlp_in.argtypes = [_p, _i, _p, _i, _p]
     L.orc_stage_finish.restype = _i
     L.orc_stage_finish.argtypes = [_p, _i, _p, _p, _p, _i, _i64, _p]
     L.orc_stage_attend.restype = _i
@@ -97,7 +101,7 @@ def _declare(L):
     L.orc_stage_oproj.restype = _i
     L.orc_stage_oproj.argtypes = [_p, _i, _p, _i, _p]
     L.orc_stage_gateup.restype = _i
-    L.orc_stage_gateup.argtypes = [_p, _i, _p, _i, _p, _p]
+    L.orc_stage_gateup.argtypes = [_p, _i, _p, _i, _p]
     L.orc_stage_down.restype = _i
     L.orc_stage_down.argtypes = [_p, _i, _p, _i, _p]
     L.orc_head_input.restype = _i
@@ -414,7 +418,7 @@ class OracleModel:
             raise ValueError("oracle head rejected its arguments")
         return logits, am
 
-    # ---- the layer's six stages and the head's two (orc_run_layer and
+    # ---- the layer's stages and the head's two (orc_run_layer and
     # orc_head compose them); each takes the previous stage's storage values,
     # so a stage can be fed another implementation's rounding points
     def _dims(self, l: int):
@@ -423,17 +427,25 @@ class OracleModel:
         Hkv = 1 if L.is_full else self.sl_kv_heads
         return D, Hkv
 
-    def stage_qkv(self, l: int, h):
-        """-> (x16 uint16 [n, hidden], q [n, Hq*D], k [n, Hkv*D], v [n, Hkv*D])"""
+    def stage_attn_in(self, l: int, h):
+        """-> x16 = fp16(RMSNorm(h, attn_norm)) uint16 [n, hidden]"""
         h = np.ascontiguousarray(np.atleast_2d(h), dtype=np.float64)
-        n = h.shape[0]
+        x16 = np.empty((h.shape[0], self.hidden), dtype=np.uint16)
+        m, keep = self._struct()
+        if lib().orc_stage_attn_in(C.byref(m), l, _ptr(h), h.shape[0], _ptr(x16)) != 0:
+            raise ValueError("oracle stage_attn_in rejected its arguments")
+        return x16
+
+    def stage_qkv(self, l: int, x16):
+        """-> (q [n, Hq*D], k [n, Hkv*D], v [n, Hkv*D]) projections of x16"""
+        x16 = np.ascontiguousarray(np.atleast_2d(x16), dtype=np.uint16)
+        n = x16.shape[0]
         D, Hkv = self._dims(l)
-        x16 = np.empty((n, self.hidden), dtype=np.uint16)
         q = np.empty((n, self.n_heads * D)); k = np.empty((n, Hkv * D)); v = np.empty((n, Hkv * D))
         m, keep = self._struct()
-        if lib().orc_stage_qkv(C.byref(m), l, _ptr(h), n, _ptr(x16), _ptr(q), _ptr(k), _ptr(v)) != 0:
+        if lib().orc_stage_qkv(C.byref(m), l, _ptr(x16), n, _ptr(q), _ptr(k), _ptr(v)) != 0:
             raise ValueError("oracle stage_qkv rejected its arguments")
-        return x16, q, k, v
+        return q, k, v
 
     def stage_finish(self, l: int, q, k, v, pos0: int):
         """Writes the rows' K/V into layer l's cache; -> q16 uint16 [n, Hq, D]."""
@@ -470,16 +482,24 @@ class OracleModel:
             raise ValueError("oracle stage_oproj rejected its arguments")
         return h
 
-    def stage_gateup(self, l: int, h):
-        """-> (x16 uint16 [n, hidden], a16 uint16 [n, inter])"""
+    def stage_mlp_in(self, l: int, h):
+        """-> x16 = fp16(RMSNorm(h, pre_ff_norm)) uint16 [n, hidden]"""
         h = np.ascontiguousarray(np.atleast_2d(h), dtype=np.float64)
-        n = h.shape[0]
-        x16 = np.empty((n, self.hidden), dtype=np.uint16)
+        x16 = np.empty((h.shape[0], self.hidden), dtype=np.uint16)
+        m, keep = self._struct()
+        if lib().orc_stage_mlp_in(C.byref(m), l, _ptr(h), h.shape[0], _ptr(x16)) != 0:
+            raise ValueError("oracle stage_mlp_in rejected its arguments")
+        return x16
+
+    def stage_gateup(self, l: int, x16):
+        """-> a16 = fp16(gelu_tanh(Wg x16) * Wu x16) uint16 [n, inter]"""
+        x16 = np.ascontiguousarray(np.atleast_2d(x16), dtype=np.uint16)
+        n = x16.shape[0]
         a16 = np.empty((n, self.inter), dtype=np.uint16)
         m, keep = self._struct()
-        if lib().orc_stage_gateup(C.byref(m), l, _ptr(h), n, _ptr(x16), _ptr(a16)) != 0:
+        if lib().orc_stage_gateup(C.byref(m), l, _ptr(x16), n, _ptr(a16)) != 0:
             raise ValueError("oracle stage_gateup rejected its arguments")
-        return x16, a16
+        return a16
 
     def stage_down(self, l: int, a16, h):
         """-> (h + RMSNorm(Wd a16, post_ff_norm)) * layer_scalar"""

@@ -461,32 +461,39 @@ static int layer_ok(const orc_model* m, int l, int n) {
 }
 
 /* One decoder layer ([zoo] architecture notes: gemma3_text-like pre/post
- * norms, attention_k_eq_v on full layers, dual RoPE, layer_scalar), as six
+ * norms, attention_k_eq_v on full layers, dual RoPE, layer_scalar), as the
  * stages that orc_run_layer composes; each stage starts from the storage
  * values of the previous one (the fp16 rounding points), so a stage can also
  * be run on another implementation's values.  Row i sits at position pos0+i.
- *
- * Stage 1: x16 = fp16(RMSNorm(h, attn_norm)); raw projections q = Wq x16,
- * k = Wk x16, and v = Wv x16 on sliding layers or the raw k itself on full
- * layers (attention_k_eq_v).  q [n][Hq*D], k and v [n][Hkv*D]. */
-int orc_stage_qkv(const orc_model* m, int l, const double* h, int n, uint16_t* x16,
-                  double* q, double* k, double* v) {
+ */
+
+/* Stage 1a: x16 = fp16(RMSNorm(h, attn_norm)), the projections' input. */
+int orc_stage_attn_in(const orc_model* m, int l, const double* h, int n, uint16_t* x16) {
+  if (!layer_ok(m, l, n)) return -1;
+  const int H = m->hidden;
+  double* t0 = (double*)malloc(sizeof(double) * (size_t)H);
+  for (int i = 0; i < n; i++) {
+    orc_rmsnorm(h + (int64_t)i * H, m->layers[l].attn_norm, H, m->eps, t0);
+    to_f16(t0, H, x16 + (int64_t)i * H);
+  }
+  free(t0);
+  return 0;
+}
+
+/* Stage 1b: raw projections q = Wq x16, k = Wk x16, and v = Wv x16 on
+ * sliding layers or the raw k itself on full layers (attention_k_eq_v).
+ * q [n][Hq*D], k and v [n][Hkv*D]. */
+int orc_stage_qkv(const orc_model* m, int l, const uint16_t* x16, int n, double* q, double* k, double* v) {
   if (!layer_ok(m, l, n)) return -1;
   const int H = m->hidden, Hq = m->n_heads;
   const orc_layer* L = &m->layers[l];
   const int full = L->is_full;
   const int D = full ? m->full_head_dim : m->sl_head_dim;
   const int Hkv = full ? 1 : m->sl_kv_heads;
-  double* t0 = (double*)malloc(sizeof(double) * (size_t)H);
-  for (int i = 0; i < n; i++) {
-    orc_rmsnorm(h + (int64_t)i * H, L->attn_norm, H, m->eps, t0);
-    to_f16(t0, H, x16 + (int64_t)i * H);
-  }
   wgemv(m, L->wq, (int64_t)Hq * D, H, x16, n, q);
   wgemv(m, L->wk, (int64_t)Hkv * D, H, x16, n, k);
   if (full) memcpy(v, k, sizeof(double) * (size_t)n * Hkv * D);
   else wgemv(m, L->wv, (int64_t)Hkv * D, H, x16, n, v);
-  free(t0);
   return 0;
 }
 
@@ -572,24 +579,31 @@ int orc_stage_oproj(const orc_model* m, int l, const uint16_t* o16, int n, doubl
   return 0;
 }
 
-/* Stage 5: gated MLP input: x16 = fp16(RMSNorm(h, pre_ff_norm)),
- * a16 = fp16(gelu_tanh(Wg x16) * (Wu x16)), a16 [n][inter]. */
-int orc_stage_gateup(const orc_model* m, int l, const double* h, int n, uint16_t* x16, uint16_t* a16) {
+/* Stage 5a: x16 = fp16(RMSNorm(h, pre_ff_norm)), the gated MLP's input. */
+int orc_stage_mlp_in(const orc_model* m, int l, const double* h, int n, uint16_t* x16) {
+  if (!layer_ok(m, l, n)) return -1;
+  const int H = m->hidden;
+  double* t0 = (double*)malloc(sizeof(double) * (size_t)H);
+  for (int i = 0; i < n; i++) {
+    orc_rmsnorm(h + (int64_t)i * H, m->layers[l].pre_ff_norm, H, m->eps, t0);
+    to_f16(t0, H, x16 + (int64_t)i * H);
+  }
+  free(t0);
+  return 0;
+}
+
+/* Stage 5b: a16 = fp16(gelu_tanh(Wg x16) * (Wu x16)), a16 [n][inter]. */
+int orc_stage_gateup(const orc_model* m, int l, const uint16_t* x16, int n, uint16_t* a16) {
   if (!layer_ok(m, l, n)) return -1;
   const int H = m->hidden, I = m->inter;
   const orc_layer* L = &m->layers[l];
-  double* t0 = (double*)malloc(sizeof(double) * (size_t)H);
   double* g = (double*)malloc(sizeof(double) * (size_t)n * I);
   double* u = (double*)malloc(sizeof(double) * (size_t)n * I);
-  for (int i = 0; i < n; i++) {
-    orc_rmsnorm(h + (int64_t)i * H, L->pre_ff_norm, H, m->eps, t0);
-    to_f16(t0, H, x16 + (int64_t)i * H);
-  }
   wgemv(m, L->wg, I, H, x16, n, g);
   wgemv(m, L->wu, I, H, x16, n, u);
   for (int64_t e = 0; e < (int64_t)n * I; e++) g[e] = orc_gelu_tanh(g[e]) * u[e];
   to_f16(g, (int64_t)n * I, a16);
-  free(t0); free(g); free(u);
+  free(g); free(u);
   return 0;
 }
 
@@ -614,7 +628,7 @@ int orc_stage_down(const orc_model* m, int l, const uint16_t* a16, int n, double
 }
 
 /* One decoder layer on the residual stream h [n][hidden] (updated in place):
- * the six stages in order; the layer's cache receives every row's K/V before
+ * the stages in order; the layer's cache receives every row's K/V before
  * any row attends. */
 int orc_run_layer(const orc_model* m, int l, double* h, int n, int64_t pos0) {
   if (check_rows(m, l, n, pos0)) return -1;
@@ -631,14 +645,16 @@ int orc_run_layer(const orc_model* m, int l, double* h, int n, int64_t pos0) {
   uint16_t* q16 = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)n * qdim);
   double* att = (double*)malloc(sizeof(double) * (size_t)n * qdim);
   const int D = m->layers[l].is_full ? Df : Ds;
-  int rc = orc_stage_qkv(m, l, h, n, x16, qv, kv, vv);
+  int rc = orc_stage_attn_in(m, l, h, n, x16);
+  if (rc == 0) rc = orc_stage_qkv(m, l, x16, n, qv, kv, vv);
   if (rc == 0) rc = orc_stage_finish(m, l, qv, kv, vv, n, pos0, q16);
   if (rc == 0) rc = orc_stage_attend(m, l, q16, n, pos0, att);
   if (rc == 0) {
     to_f16(att, (int64_t)n * Hq * D, q16);             /* o16: the output projection's input */
     rc = orc_stage_oproj(m, l, q16, n, h);
   }
-  if (rc == 0) rc = orc_stage_gateup(m, l, h, n, x16, a16);
+  if (rc == 0) rc = orc_stage_mlp_in(m, l, h, n, x16);
+  if (rc == 0) rc = orc_stage_gateup(m, l, x16, n, a16);
   if (rc == 0) rc = orc_stage_down(m, l, a16, n, h);
   free(x16); free(a16); free(qv); free(kv); free(vv); free(q16); free(att);
   return rc;

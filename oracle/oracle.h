@@ -133,23 +133,26 @@ int orc_embed(const orc_model* m, const int32_t* tokens, int n, double* h);
 int orc_run_layer(const orc_model* m, int l, double* h, int n, int64_t pos0);
 int orc_head(const orc_model* m, const double* h, int n, double* logits, int32_t* argmax);
 
-/* The layer as the six stages orc_run_layer composes (each from the storage
+/* The layer as the stages orc_run_layer composes (each from the storage
  * values of the previous one; q, k, v raw fp64 projections, x16 / q16 / o16 /
  * a16 fp16 bits; h is updated in place by stages 4 and 6), and the head as
  * its input norm and its product:
- *   1 orc_stage_qkv:    x16 = fp16(RMSNorm(h, attn_norm)); q, k, v projections
- *   2 orc_stage_finish: q16 = fp16(RoPE(RMSNorm(q))); K/V rows into the cache
- *   3 orc_stage_attend: att = attention of q16 over the cache
- *   4 orc_stage_oproj:  h += RMSNorm(Wo o16, post_attn_norm)
- *   5 orc_stage_gateup: x16 = fp16(RMSNorm(h, pre_ff_norm)); a16 = fp16(gelu(Wg x16) Wu x16)
- *   6 orc_stage_down:   h = (h + RMSNorm(Wd a16, post_ff_norm)) * layer_scalar */
-int orc_stage_qkv(const orc_model* m, int l, const double* h, int n, uint16_t* x16,
-                  double* q, double* k, double* v);
+ *   1a orc_stage_attn_in: x16 = fp16(RMSNorm(h, attn_norm))
+ *   1b orc_stage_qkv:     q, k, v projections of x16 (v = k on full layers)
+ *   2  orc_stage_finish:  q16 = fp16(RoPE(RMSNorm(q))); K/V rows into the cache
+ *   3  orc_stage_attend:  att = attention of q16 over the cache
+ *   4  orc_stage_oproj:   h += RMSNorm(Wo o16, post_attn_norm)
+ *   5a orc_stage_mlp_in:  x16 = fp16(RMSNorm(h, pre_ff_norm))
+ *   5b orc_stage_gateup:  a16 = fp16(gelu_tanh(Wg x16) * Wu x16)
+ *   6  orc_stage_down:    h = (h + RMSNorm(Wd a16, post_ff_norm)) * layer_scalar */
+int orc_stage_attn_in(const orc_model* m, int l, const double* h, int n, uint16_t* x16);
+int orc_stage_qkv(const orc_model* m, int l, const uint16_t* x16, int n, double* q, double* k, double* v);
 int orc_stage_finish(const orc_model* m, int l, const double* q, const double* k, const double* v,
                      int n, int64_t pos0, uint16_t* q16);
 int orc_stage_attend(const orc_model* m, int l, const uint16_t* q16, int n, int64_t pos0, double* att);
 int orc_stage_oproj(const orc_model* m, int l, const uint16_t* o16, int n, double* h);
-int orc_stage_gateup(const orc_model* m, int l, const double* h, int n, uint16_t* x16, uint16_t* a16);
+int orc_stage_mlp_in(const orc_model* m, int l, const double* h, int n, uint16_t* x16);
+int orc_stage_gateup(const orc_model* m, int l, const uint16_t* x16, int n, uint16_t* a16);
 int orc_stage_down(const orc_model* m, int l, const uint16_t* a16, int n, double* h);
 int orc_head_input(const orc_model* m, const double* h, int n, uint16_t* x16);
 int orc_head_logits(const orc_model* m, const uint16_t* x16, int n, double* logits, int32_t* argmax);
