@@ -4,10 +4,12 @@ fp16 KV) at context 32768 on one MI355X.
 
 Prints ONE JSON line.  `value` = decode tokens/s (one token per step, inputs
 resident in HBM).  Extra fields: whole-step achieved HBM bandwidth from the
-algorithmic byte model, the dominant kernel's roofline (the batch-1 q4 GEMV
-at 12B shapes, timed live with HIP events on its stream), context-131072 and
-width-4 verify figures, and the CPU oracle timed on the host cores on a
-bounded sample.
+algorithmic byte model, the dominant kernel's roofline (k_q4_gemv<1,0,4,0>,
+the step's q/k/v, output and down products in the step's own launch
+configuration, timed live with HIP events on its stream), the q4 GEMV alone
+at three shapes, context-131072 and width-4 verify figures, the attention
+kernels alone, and the CPU oracle timed on the host cores on a bounded
+sample.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--mode full|gemv|step|traffic|prefill]
 """
@@ -37,26 +39,28 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def time_gemv(q4, torch, model, reps=10, warm=5):
-    """Average launch time of the batch-1 q4 GEMV at 12B shapes: the gate and
-    up matrices of all 48 layers (3.2 GB, so every launch streams from HBM),
-    captured once into a graph and replayed back to back between two HIP
-    events on the current stream (so host launch cost is not timed).  `warm`
-    untimed replays first bring the GPU from the model build to a steady
-    clock."""
+def step_gemv_bytes(cfg):
+    """Algorithmic bytes of the step's q/k/v, output and down products (the
+    launches decode_step_gemvs makes: three per layer)."""
+    from int4_q4_gemv_amd import bytemodel
+    return sum(bytemodel.q4_matrix_bytes(N, K) for l in range(cfg.n_layers)
+               for nm, N, K in cfg.layer_shapes(l) if nm in ("wq", "wk", "wv", "wo", "wd"))
+
+
+def time_step_gemvs(q4, torch, model, reps=10, warm=5):
+    """The step's most launched kernel, k_q4_gemv<1,0,4,0>, in the step's own
+    launch configuration: decode_step_gemvs enqueues the q/k/v, output and
+    down products of all 48 layers (144 launches, 2.95 GB: every launch
+    streams from HBM), captured once into a graph and replayed back to back
+    between two HIP events on the launch stream after `warm` untimed replays.
+    Returns (average seconds per launch, launches timed, average algorithmic
+    bytes per launch)."""
     cfg = model.cfg
-    N, K = cfg.inter, cfg.hidden
-    g = q4.Gemv(N, K, 1)
-    x = torch.randn(1, K, device="cuda", generator=torch.Generator("cuda").manual_seed(7)).half()
-    y = torch.empty(1, N, device="cuda")
-    mats = [L[nm] for L in model.layers for nm in ("wg", "wu")]
-    for m in mats[:8]:
-        g(m, x, y)
+    model.step([1], 32767, want_logits=False)          # the workspace holds a step's activations
     torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph, stream=torch.cuda.current_stream()):
-        for m in mats:
-            g(m, x, y)
+        model.step_gemvs(1)
     for _ in range(warm):
         graph.replay()
     torch.cuda.synchronize()
@@ -66,9 +70,29 @@ def time_gemv(q4, torch, model, reps=10, warm=5):
         graph.replay()
     e1.record()
     e1.synchronize()
-    launches = reps * len(mats)
-    avg_s = e0.elapsed_time(e1) * 1e-3 / launches
-    return avg_s, launches, q4.packed_bytes(N, K)
+    per_step = 3 * cfg.n_layers
+    launches = reps * per_step
+    return e0.elapsed_time(e1) * 1e-3 / launches, launches, step_gemv_bytes(cfg) / per_step
+
+
+def time_gemv_shapes(q4, torch, model):
+    """q4_gemv on its own: 3840 -> 15360 (gate/up shape) at batch 1 and 4,
+    15360 -> 3840 (down shape) at batch 1, each over the 48 layers' matrices
+    of that shape (no launch finds its weights in the last-level cache)."""
+    cfg = model.cfg
+    res = {}
+    for name, nm, B in (("gate_3840x15360_b1", ("wg", "wu"), 1), ("gate_3840x15360_b4", ("wg", "wu"), 4),
+                        ("down_15360x3840_b1", ("wd",), 1)):
+        N, K = (cfg.inter, cfg.hidden) if nm[0] != "wd" else (cfg.hidden, cfg.inter)
+        mats = [L[k] for L in model.layers for k in nm]
+        x = torch.randn(B, K, device="cuda", generator=torch.Generator("cuda").manual_seed(7)).half()
+        y = torch.empty(B, N, device="cuda")
+        g = q4.Gemv(N, K, B)
+        t = time_graph_calls(torch, lambda i: g(mats[i % len(mats)], x, y), len(mats), replays=10)
+        nb = q4.packed_bytes(N, K)
+        res[name] = {"us": round(t * 1e6, 3), "bytes": nb, "GBps": round(nb / t / 1e9, 1),
+                     "frac": round(nb / t / 1e9 / PEAK_GBPS, 4)}
+    return res
 
 
 def time_stream_read(q4, torch, nbytes=4 << 30, reps=5):
@@ -142,13 +166,16 @@ def time_attention(q4, torch):
     ws = q4._fd_ws(1, 1, 16, 256, "cuda")
     t = time_graph_calls(torch, lambda i: q4.flash_decode_ring(q, k, v, 1024, 100000, 1.0, ws=ws), 40)
     res["ring_attention_1seq_us"] = round(t * 1e6, 2)
-    rings = [synth.ring_inputs(100000, n_rows=1, n_rejected=4, seed=100 + s, device="cuda") for s in range(40)]
-    qs = torch.stack([r[0] for r in rings]).to("cuda")
-    ks = torch.stack([r[1] for r in rings]).to("cuda")
-    vs = torch.stack([r[2] for r in rings]).to("cuda")
-    del rings
+    # two sets of 40 rings (2 x 671 MB of K/V, above the last-level cache), alternated
+    sets = []
+    for k in range(2):
+        rings = [synth.ring_inputs(100000, n_rows=1, n_rejected=4, seed=100 + 40 * k + s, device="cuda")
+                 for s in range(40)]
+        sets.append(tuple(torch.stack([r[j] for r in rings]).to("cuda") for j in range(3)))
+        del rings
     ws = q4._fd_ws(40, 1, 16, 256, "cuda")
-    t = time_graph_calls(torch, lambda i: q4.flash_decode_ring(qs, ks, vs, 1024, [100000] * 40, 1.0, ws=ws), 10)
+    t = time_graph_calls(torch, lambda i: q4.flash_decode_ring(*sets[i % 2], 1024, [100000] * 40, 1.0, ws=ws), 10)
+    del sets
     nb = 40 * 8 * 1024 * 1024
     res["ring_attention_40seq"] = {"us": round(t * 1e6, 2), "bytes": nb,
                                    "GBps": round(nb / t / 1e9, 1), "frac": round(nb / t / 1e9 / PEAK_GBPS, 4)}
@@ -211,7 +238,8 @@ def time_prefill(q4, torch, bytemodel, model, reps=3):
     of the decode figures): a chunk at positions 0 .. 63 and one ending at
     position 32767 (every row attends up to 32K positions on the full
     layers), each timed over `reps` eager calls between HIP events.  Bytes:
-    the weights once per chunk plus each row's attended KV."""
+    the weights and head once per chunk, and every cached position the
+    chunk's rows attend once (they share each K/V tile)."""
     from int4_q4_gemv_amd import synth
     cfg = model.cfg
     toks = [int(t) for t in synth.tokens(cfg, 64, 9)]
@@ -226,9 +254,7 @@ def time_prefill(q4, torch, bytemodel, model, reps=3):
         e1.record()
         e1.synchronize()
         secs = e0.elapsed_time(e1) * 1e-3 / reps
-        kv = sum(bytemodel.step_bytes(cfg, pos0 + i) - bytemodel.weight_bytes(cfg) - bytemodel.head_bytes(cfg)
-                 for i in range(64))
-        nb = bytemodel.weight_bytes(cfg) + bytemodel.head_bytes(cfg) + kv
+        nb = bytemodel.chunk_bytes(cfg, pos0, 64)
         res[name] = {"ms_per_chunk": round(secs * 1e3, 3), "tokens_per_s": round(64 / secs, 1),
                      "algorithmic_bytes": nb, "achieved_GBps": round(nb / secs / 1e9, 1)}
     return res
@@ -252,7 +278,7 @@ def time_gemm(q4, torch, N=15360, K=3840, n=64, copies=16, launches=48):
 
 
 COPY_BYTES = 512 << 20
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "q4_gemv_15360x3840_traffic.txt")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "q4_gemv_step_launches_traffic.txt")
 GEMV_SOURCES = ("int4_q4_gemv_amd/csrc/gemv_kernels.h", "int4_q4_gemv_amd/csrc/device_common.h",
                 "int4_q4_gemv_amd/csrc/q4dec.hip")
 
@@ -269,20 +295,15 @@ def gemv_source_hash():
 def traffic_launches(q4, torch, model):
     """What the two counter runs profile: a plain device copy of COPY_BYTES
     (its FETCH_SIZE / WRITE_SIZE calibrate the counters to bytes), then the
-    batch-1 q4 GEMV over the 96 gate/up matrices, twice."""
+    step's q/k/v, output and down products (decode_step_gemvs), twice."""
     src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
     dst = torch.empty_like(src)
     for _ in range(3):
         dst.copy_(src)
     torch.cuda.synchronize()
-    cfg = model.cfg
-    g = q4.Gemv(cfg.inter, cfg.hidden, 1)
-    x = torch.randn(1, cfg.hidden, device="cuda").half()
-    y = torch.empty(1, cfg.inter, device="cuda")
+    model.step([1], 32767, want_logits=False)
     for _ in range(2):
-        for L in model.layers:
-            g(L["wg"], x, y)
-            g(L["wu"], x, y)
+        model.step_gemvs(1)
     torch.cuda.synchronize()
 
 
@@ -360,23 +381,41 @@ def cpu_baseline(model, torch):
     h = m.embed_tokens(tok)
     wall = time.perf_counter()
 
-    def med3(f):
+    def med(f, k):
         ts = []
-        for _ in range(3):
+        for _ in range(k):
             t = time.perf_counter()
             f()
             ts.append(time.perf_counter() - t)
-        return sorted(ts)[1]
+        return sorted(ts)[k // 2]
 
-    t_s = med3(lambda: m.run_layer(0, h, pos))
-    t_f = med3(lambda: m.run_layer(1, h, pos))
-    t_h = med3(lambda: m.run_head(h, want_logits=False))
+    def parts(k):
+        return (med(lambda: m.run_layer(0, h, pos), k), med(lambda: m.run_layer(1, h, pos), k),
+                med(lambda: m.run_head(h, want_logits=False), k))
+
+    cores = oracle.num_threads()
+    t_s, t_f, t_h = parts(5)
+    oracle.set_num_threads(1)
+    t1_s, t1_f, t1_h = parts(1)
+    oracle.set_num_threads(cores)
     per_tok = 40 * t_s + 8 * t_f + t_h
-    return {"value": 1.0 / per_tok, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+    per_tok1 = 40 * t1_s + 8 * t1_f + t1_h
+    cpu = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    cpu = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"value": 1.0 / per_tok, "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": ("the oracle's layer 0 (sliding) and layer 5 (full, context 32768) of the same "
-                       "12B-shape weights at position 32767, and its vocab head, each timed 3 times "
-                       "(median); tokens/s = 1/(40 t_sliding + 8 t_full + t_head)"),
-            "t_sliding_s": t_s, "t_full_s": t_f, "t_head_s": t_h,
+                       "12B-shape weights at position 32767, and its vocab head, each timed 5 times "
+                       "(median) on all threads and once on one thread; tokens/s = "
+                       "1/(40 t_sliding + 8 t_full + t_head)"),
+            "cpu_model": cpu, "t_sliding_s": t_s, "t_full_s": t_f, "t_head_s": t_h,
+            "one_thread": {"value": 1.0 / per_tok1, "t_sliding_s": t1_s, "t_full_s": t1_f, "t_head_s": t1_h},
             "wall_s": round(time.perf_counter() - wall, 2)}
 
 
@@ -412,14 +451,17 @@ def main():
             print(json.dumps({"mode": "prefill", "prefill64": time_prefill(q4, torch, bytemodel, model)}))
             return
         if args.mode in ("full", "gemv"):
-            avg_s, launches, nbytes = time_gemv(q4, torch, model)
+            avg_s, launches, nbytes = time_step_gemvs(q4, torch, model)
             ach = nbytes / avg_s / 1e9
             out["roofline"] = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_GBPS, "unit": "GB/s",
                                "frac": round(ach / PEAK_GBPS, 4), "traffic": stored_traffic(),
-                               "kernel": "k_q4_gemv<1,0,4> (q4_gemv, B=1, 3840->15360, 960 workgroups x 8 waves)",
-                               "bytes_per_launch": nbytes, "avg_launch_us": round(avg_s * 1e6, 3),
+                               "kernel": "k_q4_gemv<1,0,4,0>: the step's q/k/v, output and down products in the "
+                                         "step's launch configuration (decode_step_gemvs, 144 launches per step)",
+                               "bytes_per_launch": round(nbytes), "avg_launch_us": round(avg_s * 1e6, 3),
                                "launches": launches}
-            log(f"q4_gemv 3840->15360: {avg_s * 1e6:.2f} us/launch, {ach:.0f} GB/s")
+            log(f"step q/k/v, o, down products: {avg_s * 1e6:.2f} us/launch, {ach:.0f} GB/s")
+            out["gemv_standalone"] = time_gemv_shapes(q4, torch, model)
+            log(f"q4_gemv alone: {out['gemv_standalone']}")
             peak_meas = time_stream_read(q4, torch)
             out["roofline"]["achievable"] = {
                 "GBps": round(peak_meas, 1), "kernel": "q4_stream_read over 4 GiB (plain 16-byte streaming read)",

@@ -329,6 +329,16 @@ size_t decode_step_stage_bytes(const q4dec_model* m, int n, int stage);
 q4_status decode_step_stage(const q4dec_model* m, const void* ws, size_t ws_bytes, int n, int stage,
                             void* dst, size_t dst_bytes, void* stream);
 
+/* Measurement: enqueues only the q/k/v, output-projection and down products
+ * of every layer of a step of width n (3 launches per layer of the step's
+ * most launched kernel, with exactly the step's launch configuration),
+ * reading the activations the workspace holds and writing its partial
+ * products; no other kernel of the step.  Used to time that kernel in its
+ * step configuration (gemma4-12b card, Throughput: decode is bound by the
+ * weight stream).  Errors: Q4_EINVAL, Q4_ESHAPE, Q4_ENOSPACE, Q4_EALIGN,
+ * Q4_EHIP. */
+q4_status decode_step_gemvs(const q4dec_model* m, int n, void* ws, size_t ws_bytes, void* stream);
+
 /* Number of captured decode-step graphs the library holds (at most 16). */
 int q4dec_graph_count(void);
 

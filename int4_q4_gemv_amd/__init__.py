@@ -148,6 +148,8 @@ def _declare(L):
         fn.restype = _i
         fn.argtypes = [C.POINTER(Model), _p, _i, _i, _p, _p, _p, _sz, _p]
     L.q4dec_release.restype = _i
+    L.decode_step_gemvs.restype = _i
+    L.decode_step_gemvs.argtypes = [C.POINTER(Model), _i, _p, _sz, _p]
     L.q4dec_graph_count.restype = _i
     L.q4dec_graph_count.argtypes = []
     L.decode_step_stage_bytes.restype = _sz
@@ -175,7 +177,7 @@ EXPORTS = ["q4dec_status_str", "q4dec_version", "q4_packed_bytes", "q4_pack", "q
            "flash_decode_full_vrow", "flash_decode_ring", "flash_decode_noalloc_max_bytes",
            "flash_decode_full_noalloc",
            "decode_step_workspace_size", "decode_step", "decode_step_hidden", "decode_step_eager",
-           "decode_step_stage_bytes", "decode_step_stage", "q4dec_graph_count",
+           "decode_step_stage_bytes", "decode_step_stage", "q4dec_graph_count", "decode_step_gemvs",
            "q4_gemm", "prefill_chunk_workspace_size", "prefill_chunk",
            "q4_spec_accept", "q4_stream_read_sink_words", "q4_stream_read", "q4dec_release"]
 
@@ -509,6 +511,16 @@ def _stage(self, n: int, stage: int) -> torch.Tensor:
 
 
 DecodeModel.stage = _stage
+
+
+def _step_gemvs(self, n: int = 1):
+    """decode_step_gemvs: the step's q/k/v, output and down products only
+    (measurement of that kernel in its step launch configuration)."""
+    ws = self.workspace(n)
+    _check("decode_step_gemvs", lib().decode_step_gemvs(C.byref(self.desc), n, _ptr(ws), ws.numel(), _stream()))
+
+
+DecodeModel.step_gemvs = _step_gemvs
 
 
 def graph_count() -> int:

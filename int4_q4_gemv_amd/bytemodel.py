@@ -67,3 +67,17 @@ def cache_bytes(*dims: int, elem: int = 2, pair: bool = True) -> int:
     for d in dims:
         n *= d
     return n * (2 if pair else 1)
+
+
+def chunk_bytes(cfg: ModelConfig, pos0: int, n: int) -> int:
+    """Algorithmic bytes of a prefill chunk of n rows at positions pos0 ..
+    pos0 + n - 1: the weights and the head once (the head for the last row),
+    and every cached position the rows attend read once for the whole chunk
+    (the rows share their K/V tiles): on a full layer positions 0 .. pos0+n-1,
+    on a sliding layer the union of the rows' windows."""
+    nf = n_full(cfg)
+    ns = cfg.n_layers - nf
+    last = pos0 + n - 1
+    ring_pos = min(cfg.window + n - 1, last + 1)
+    return (weight_bytes(cfg) + head_bytes(cfg) + nf * (last + 1) * full_pos_bytes(cfg)
+            + ns * cfg.sl_kv_heads * ring_pos * 2 * 2 * cfg.sl_head_dim)

@@ -341,8 +341,11 @@ StepPtrs step_ptrs(const StepLayout& L, void* ws) {
 // pass per block; gemma-4-E4B-CoreAI card, ring3/: the GQA fold).
 // Buffers: x of attention (xf), of the MLP (xf2) and of the head (xh) are
 // kept apart, so after a step the workspace holds the last layer's stages.
+// gemvs_only: only the q/k/v, output and down products (the step's most
+// launched kernel in its step launch configuration, for measurement).
 template <int B>
-q4_status enqueue_layers(const q4dec_model* m, const StepLayout& L, const StepPtrs& P, int n, hipStream_t st) {
+q4_status enqueue_layers(const q4dec_model* m, const StepLayout& L, const StepPtrs& P, int n, hipStream_t st,
+                         bool gemvs_only = false) {
   const int H = m->hidden, I = m->inter, Hq = m->n_heads;
   const int fmt = m->weight_format;
   for (int l = 0; l < m->n_layers; l++) {
@@ -373,7 +376,7 @@ q4_status enqueue_layers(const q4dec_model* m, const StepLayout& L, const StepPt
         ni.ny = L.p_d.S; ni.y_split = (long)n * H;
       }
       ni.w_in = ly.attn_norm; ni.H = H; ni.eps = m->eps;
-      hipLaunchKernelGGL(k_norm_rows<4>, dim3(n), dim3(512), 0, st, ni, P.xf);
+      if (!gemvs_only) hipLaunchKernelGGL(k_norm_rows<4>, dim3(n), dim3(512), 0, st, ni, P.xf);
       a.K = H; a.NQ = pl.NQ; a.W = pl.W; a.NQs = pl.NQs;
       a.x = P.xf; a.ldx = H;
       a.y = P.qkv; a.ldy = L.qkv_ld; a.n_rows = n;
@@ -383,7 +386,9 @@ q4_status enqueue_layers(const q4dec_model* m, const StepLayout& L, const StepPt
     const bool vrow = full && m->kv_format == 1;
     const float2* rope_l = full ? P.rope + m->sl_head_dim / 2 : P.rope;
     const int cs_ld = m->sl_head_dim / 2 + m->full_head_dim / 2;
-    if (B == 1) {
+    if (gemvs_only) {
+      // attention skipped
+    } else if (B == 1) {
       AttnArgs a{};
       a.q = nullptr; a.k = ly.k_cache; a.v = ly.v_cache; a.seq_stride = 0;
       a.Hq = Hq; a.Hkv = Hkv; a.GQ = Hq / Hkv;
@@ -453,7 +458,7 @@ q4_status enqueue_layers(const q4dec_model* m, const StepLayout& L, const StepPt
       launch_gemv<B, EPI_STORE>(a, pl, a.seg[0].T, pl.W, gemv_lds(B, pl), st);
     }
     // ---- gate/up with GELU(gate) * up; post-attention residual + pre-FF norm in the prologue
-    {
+    if (!gemvs_only) {
       GemvArgs a{};
       const GemvPlan& pl = L.p_gu;
       fill_seg(a.seg[0], ly.wg, I, H, 0, 0, fmt);
@@ -484,6 +489,7 @@ q4_status enqueue_layers(const q4dec_model* m, const StepLayout& L, const StepPt
       launch_gemv<B, EPI_STORE>(a, pl, a.seg[0].T, pl.W, gemv_lds(B, pl), st);
     }
   }
+  if (gemvs_only) return launch_status();
   // ---- final norm (post-FF residual of the last layer), tied head, argmax
   {
     const q4dec_layer& last = m->layers[m->n_layers - 1];
@@ -1284,6 +1290,19 @@ q4_status decode_step_stage(const q4dec_model* m, const void* ws, size_t ws_byte
   const void* src = static_cast<const uint8_t*>(ws) + v.off;
   if (hipMemcpyAsync(dst, src, v.bytes, hipMemcpyDeviceToDevice, S(stream)) != hipSuccess) return Q4_EHIP;
   return Q4_OK;
+}
+
+q4_status decode_step_gemvs(const q4dec_model* m, int n, void* ws, size_t ws_bytes, void* stream) {
+  if (!m || !m->layers || !ws) return Q4_EINVAL;
+  if (n < 1 || n > kMaxRows || !model_dims_ok(m)) return Q4_ESHAPE;
+  const StepLayout L = step_layout(m);
+  if (!L.ok) return Q4_ESHAPE;
+  if (ws_bytes < L.total) return Q4_ENOSPACE;
+  if (!al16(ws)) return Q4_EALIGN;
+  q4_status rc = set_attrs();
+  if (rc != Q4_OK) return rc;
+  const StepPtrs P = step_ptrs(L, ws);
+  return n == 1 ? enqueue_layers<1>(m, L, P, n, S(stream), true) : enqueue_layers<4>(m, L, P, n, S(stream), true);
 }
 
 int q4dec_graph_count(void) {

@@ -82,6 +82,8 @@ def _declare(L):
     L.orc_decode_step.restype = _i
     L.orc_decode_step.argtypes = [_p, _p, _i, _i64, _p, _p]
     L.orc_num_threads.restype = _i
+    L.orc_set_num_threads.restype = None
+    L.orc_set_num_threads.argtypes = [_i]
     L.orc_embed.restype = _i
     L.orc_embed.argtypes = [_p, _p, _i, _p]
     L.orc_run_layer.restype = _i
@@ -117,6 +119,10 @@ def _ptr(a: np.ndarray):
 
 def num_threads() -> int:
     return int(lib().orc_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    lib().orc_set_num_threads(int(n))
 
 
 # ---------------------------------------------------------------- fp16 ----

@@ -165,6 +165,7 @@ int orc_decode_step(const orc_model* m, const int32_t* tokens, int n, int64_t po
                     double* logits, int32_t* argmax);
 
 int orc_num_threads(void);
+void orc_set_num_threads(int n);   /* OpenMP threads of the later calls (n > 0) */
 
 #ifdef __cplusplus
 }
