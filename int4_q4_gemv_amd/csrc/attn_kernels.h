@@ -746,6 +746,726 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D <= 2
   }
 }
 
+// Ring layers whose splits hold at most one 32-position tile (S * 32 >= W).
+// With one tile per workgroup, k_fd_partial streams it from one wave while
+// the other three wait; here the head dimension is dealt to the 4 waves
+// instead.  Wave w loads the keys' dims [w D/4, (w+1) D/4) of all 32
+// positions (its D/128 QK k steps) and V rows 8w .. 8w+7 of the tile into
+// one shared LDS tile; the waves' partial scores meet in LDS and are added
+// in a fixed order, every wave runs the same softmax on the sums, and wave w
+// forms O for its own D/4 dims over the 32 rows.  A wave then has a quarter
+// of the tile in flight (8 KB at D = 256) rather than one wave holding all of
+// it, and that is what keeps the memory pipeline full when a CU holds one
+// workgroup.  Splits, masking, the finishing prologue, the records and the
+// combine are those of k_fd_partial (one tile, no merge of waves).
+template <int D>
+constexpr size_t ds_lds_bytes() {
+  return (size_t)32 * fd_vpitch<D>() * 2 + (size_t)2 * 4 * D * 2 + (size_t)16 * D * 2 + (size_t)4 * 2 * 64 * 16;
+}
+
+template <int D>
+__global__ void __launch_bounds__(256) k_fd_ring_ds(AttnArgs a) {
+  static_assert(D >= 128 && D <= 512, "a wave takes whole QK k steps");
+  constexpr int VROW = fd_vpitch<D>();
+  constexpr int KS = D / 128;                 // QK k steps of a wave
+  constexpr int DS = D / 64;                  // PV dim steps of a wave
+  constexpr int DW = D / 4;                   // dims of a wave
+  extern __shared__ __align__(16) unsigned char smem[];
+  uint16_t* vl = reinterpret_cast<uint16_t*>(smem);   // [32][VROW] the tile's V rows
+  uint16_t* newK = vl + 32 * VROW;                     // [4][D] rows of this step
+  uint16_t* newV = newK + 4 * D;
+  uint16_t* q16 = newV + 4 * D;                        // [16][D] finished queries
+  f4_t* sx = reinterpret_cast<f4_t*>(q16 + 16 * D);    // [4 waves][2][64] partial scores
+  static_assert(ds_lds_bytes<D>() <= 160 * 1024, "LDS of one workgroup");
+
+  const int split = a.kvh_major ? blockIdx.y : blockIdx.x, kvh = a.kvh_major ? blockIdx.x : blockIdx.y;
+  const int seq = blockIdx.z / a.n_rows, row = blockIdx.z - seq * a.n_rows;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+
+  // ---- the step's first position (a global load, issued first)
+  int base;
+  if (a.sp) base = *(const __attribute__((address_space(1))) int*)(&a.sp->pos0);
+  else base = a.pos0[seq];
+
+  // ---- inputs of the finishing prologue: jobs dealt round-robin to the
+  // waves (this workgroup's query heads, then k and v of rows 0 .. row)
+  constexpr int FE = D / 64, FEH = fin_h<D>();
+  constexpr int MAXJ = (16 + 2 * 4 + 3) / 4;
+  const int njobs = a.fin_on ? a.GQ + 2 * (row + 1) : 0;
+  float raw[MAXJ][FE], wq[FE], wk[FE];
+  float2 fcs[MAXJ][FEH];
+  if (a.fin_on) {
+    const AttnFin& f = a.fin;
+    fin_load<D>(wq, f.q_norm);
+    fin_load<D>(wk, f.k_norm);
+#pragma unroll
+    for (int k = 0; k < MAXJ; k++) {
+      const int jb = wave + 4 * k;
+      if (jb >= njobs) break;
+      const int r = jb < a.GQ ? row : (jb - a.GQ) >> 1;
+      const float* rr = f.qkv + (long)r * f.ldq;
+      const float* src;
+      if (jb < a.GQ) src = rr + (long)(kvh * a.GQ + jb) * D;
+      else if (((jb - a.GQ) & 1) == 0) src = rr + (long)(a.Hq + kvh) * D;
+      else src = rr + (long)(a.Hq + a.Hkv + kvh) * D;
+      fin_load<D>(raw[k], src);
+      const float2* cr = f.rope_cs + (long)r * f.cs_ld + lane * FEH;
+      if constexpr (FEH == 4) {
+        const float4 c0 = *reinterpret_cast<const float4*>(cr), c1 = *reinterpret_cast<const float4*>(cr + 2);
+        fcs[k][0] = make_float2(c0.x, c0.y); fcs[k][1] = make_float2(c0.z, c0.w);
+        fcs[k][2] = make_float2(c1.x, c1.y); fcs[k][3] = make_float2(c1.z, c1.w);
+      } else if constexpr (FEH == 2) {
+        const float4 c0 = *reinterpret_cast<const float4*>(cr);
+        fcs[k][0] = make_float2(c0.x, c0.y); fcs[k][1] = make_float2(c0.z, c0.w);
+      } else {
+        fcs[k][0] = *cr;
+      }
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  base = __builtin_amdgcn_readfirstlane(base);
+  const int P = base + row;
+  const int lo = max(0, P - a.W + 1);
+  const int L = P - lo + 1;
+  const int chunk = (L + a.S - 1) / a.S;      // <= 32: the host launches this kernel only then
+  const int st = lo + split * chunk;
+  const int en = min(st + chunk, P + 1);
+  const bool has = st < en;                   // workgroup-uniform
+  const int P0new = a.fin_on ? base : 0x7FFFFFFF;
+
+  const int j = lane & 15, g = lane >> 4;
+  const bool col_ok = j < a.GQ;
+  uint16_t* vb = a.v + seq * a.seq_stride + (long)kvh * a.R * D;
+  uint16_t* kb = a.k + seq * a.seq_stride + (long)kvh * a.R * D;
+  // tile row r lives at slot (st + r) mod R (R >= 32: one wrap at most);
+  // rows past nv are masked or formed in this step and read slot 0
+  const int s0 = __builtin_amdgcn_readfirstlane(st % a.R);
+  const int nv = __builtin_amdgcn_readfirstlane(min(en, P0new) - st);
+  auto row_at = [&](int r) -> long {
+    const int sl = r >= a.R - s0 ? s0 + r - a.R : s0 + r;
+    return r < nv ? (long)sl * D : 0l;
+  };
+
+  // ---- this wave's K elements and V rows, issued before anything waits.
+  // Lane (column j, group g) holds positions 8g .. 8g+7 of the tile (MFMA
+  // row r of half h <-> tile position 8 (r / 4) + 4h + r % 4).
+  h8_t KA[KS], KB[KS];
+  if (has) {
+    const int ra = 8 * (j >> 2) + (j & 3);
+    const uint16_t* ka = kb + row_at(ra) + DW * wave + 8 * g;
+    const uint16_t* kc = kb + row_at(ra + 4) + DW * wave + 8 * g;
+#pragma unroll
+    for (int s = 0; s < KS; s++) {
+      KA[s] = __builtin_bit_cast(h8_t, __builtin_nontemporal_load(reinterpret_cast<const u4v*>(ka + 32 * s)));
+      KB[s] = __builtin_bit_cast(h8_t, __builtin_nontemporal_load(reinterpret_cast<const u4v*>(kc + 32 * s)));
+    }
+    constexpr int CPR = D / 8, RPI = 64 / CPR;   // 16-byte chunks per row, rows per instruction
+    const int rl = lane / CPR, pc = lane % CPR;
+#pragma unroll
+    for (int i = 0; i < 8 / RPI; i++) {
+      const int r0 = 8 * wave + RPI * i, r = r0 + rl;
+      const int c = pc ^ (2 * vswz<D>(r));
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint32_t*>(vb + row_at(r) + c * 8),
+                                       reinterpret_cast<uint32_t*>(vl + r0 * VROW), 16, 0, 0);
+    }
+  }
+
+  // ---- queries (as the MFMA B operand, this wave's k steps)
+  h8_t qb[KS];
+  if (a.fin_on) {
+    const AttnFin& f = a.fin;
+    const int r0 = max(0, st - base), r1 = min(row, en - 1 - base);
+#pragma unroll
+    for (int k = 0; k < MAXJ; k++) {
+      const int jb = wave + 4 * k;
+      if (jb >= njobs) break;
+      if (jb < a.GQ) {
+        finish_vals<D>(raw[k], wq, true, true, fcs[k], f.rot_pairs, f.eps, q16 + jb * D);
+        continue;
+      }
+      const int r = (jb - a.GQ) >> 1;
+      if (r < r0 || r > r1) continue;
+      if (((jb - a.GQ) & 1) == 0) finish_vals<D>(raw[k], wk, true, true, fcs[k], f.rot_pairs, f.eps, newK + r * D);
+      else if (f.v_norm) finish_vals<D>(raw[k], wk, false, false, fcs[k], f.rot_pairs, f.eps, newV + r * D);
+      else fin_store<D>(raw[k], newV + r * D);
+    }
+    __syncthreads();
+    if (f.q_out && split == 0) {
+      constexpr int CH = D / 8;
+      for (int i = threadIdx.x; i < a.GQ * CH; i += 256) {
+        const int jq = i / CH, c = i - jq * CH;
+        *reinterpret_cast<u4v*>(f.q_out + ((long)row * a.Hq + kvh * a.GQ + jq) * D + c * 8) =
+            *reinterpret_cast<const u4v*>(q16 + jq * D + c * 8);
+      }
+    }
+    if (P >= st && P < en) {
+      const long so = (long)(P % a.R) * D;
+      for (int d = threadIdx.x; d < D; d += 256) {
+        kb[so + d] = newK[row * D + d];
+        vb[so + d] = newV[row * D + d];
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < KS; s++) {
+      u4v t = *reinterpret_cast<const u4v*>(q16 + (col_ok ? j : 0) * D + DW * wave + 32 * s + 8 * g);
+      if (!col_ok) t = (u4v){0u, 0u, 0u, 0u};
+      qb[s] = __builtin_bit_cast(h8_t, t);
+    }
+  } else {
+    const uint16_t* qp = a.q + (((long)seq * a.n_rows + row) * a.Hq + (col_ok ? kvh * a.GQ + j : 0)) * D +
+                         DW * wave + 8 * g;
+#pragma unroll
+    for (int s = 0; s < KS; s++) {
+      u4v t = *reinterpret_cast<const u4v*>(qp + 32 * s);
+      if (!col_ok) t = (u4v){0u, 0u, 0u, 0u};
+      qb[s] = __builtin_bit_cast(h8_t, t);
+    }
+  }
+
+  f4_t O[DS];
+#pragma unroll
+  for (int d = 0; d < DS; d++) O[d] = (f4_t){0.f, 0.f, 0.f, 0.f};
+  float m = -INFINITY, l_tot = 0.f;
+  if (has) {
+    // keys of the rows formed in this step come from LDS
+    if (st + 31 >= P0new) {
+      const int pa = st + 8 * (j >> 2) + (j & 3), pb = pa + 4;
+#pragma unroll
+      for (int s = 0; s < KS; s++) {
+        const int off = DW * wave + 32 * s + 8 * g;
+        if (pa >= P0new && pa < en) KA[s] = *reinterpret_cast<const h8_t*>(newK + (pa - P0new) * D + off);
+        if (pb >= P0new && pb < en) KB[s] = *reinterpret_cast<const h8_t*>(newK + (pb - P0new) * D + off);
+      }
+    }
+    f4_t p0 = {0.f, 0.f, 0.f, 0.f}, p1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < KS; s++) {
+      p0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(KA[s], qb[s], p0, 0, 0, 0);
+      p1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(KB[s], qb[s], p1, 0, 0, 0);
+    }
+    sx[(2 * wave) * 64 + lane] = p0;
+    sx[(2 * wave + 1) * 64 + lane] = p1;
+    // this wave's V rows have landed; rows formed in this step overwrite theirs
+    __builtin_amdgcn_s_waitcnt(0);
+    __asm__ __volatile__("" ::: "memory");
+    if (st + 31 >= P0new) {
+#pragma unroll
+      for (int r = 8 * wave; r < 8 * wave + 8; r++) {
+        const int pr = st + r;
+        if (pr >= P0new && pr < en && lane < D / 8)
+          *reinterpret_cast<u4v*>(vl + r * VROW + (lane ^ (2 * vswz<D>(r))) * 8) =
+              *reinterpret_cast<const u4v*>(newV + (pr - P0new) * D + lane * 8);
+      }
+    }
+  }
+  __syncthreads();
+  if (has) {
+    // full scores: the 4 waves' parts added in a fixed order
+    f4_t c0 = sx[0 * 64 + lane], c1 = sx[1 * 64 + lane];
+#pragma unroll
+    for (int w = 1; w < 4; w++) {
+      const f4_t e0 = sx[(2 * w) * 64 + lane], e1 = sx[(2 * w + 1) * 64 + lane];
+#pragma unroll
+      for (int i = 0; i < 4; i++) { c0[i] += e0[i]; c1[i] += e1[i]; }
+    }
+    // lane (j, g): reg i of c0 -> position st + 8g + i; of c1 -> st + 8g + 4 + i
+    float sv[8];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      sv[i] = (st + 8 * g + i < en) ? c0[i] * a.scale_log2 : -INFINITY;
+      sv[4 + i] = (st + 8 * g + 4 + i < en) ? c1[i] * a.scale_log2 : -INFINITY;
+    }
+    float mt = sv[0];
+#pragma unroll
+    for (int i = 1; i < 8; i++) mt = fmaxf(mt, sv[i]);
+    mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+    m = mt;                                   // finite: position st is admitted
+    float p[8], ps = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      p[i] = exp2f(sv[i] - m);
+      ps += p[i];
+    }
+    l_tot = ps + __shfl_xor(ps, 16, 64);
+    l_tot += __shfl_xor(l_tot, 32, 64);
+    h8_t Ahi, Alo;
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      const _Float16 hi = (_Float16)p[i];
+      Ahi[i] = hi;
+      Alo[i] = (_Float16)(p[i] - (float)hi);
+    }
+    // O += P V over this wave's dims (the transposing reads of k_fd_partial)
+    const int sw = vswz<D>(8 * g + (j >> 2));
+    const uint16_t* vt = vl + (8 * g + (j >> 2)) * VROW + 4 * (j & 3);
+#pragma unroll
+    for (int dd = 0; dd < DS; dd++) {
+      typedef short v4s_t __attribute__((ext_vector_type(4)));
+      typedef __attribute__((address_space(3))) v4s_t lds_v4s;
+      const int cd = 16 * ((DS * wave + dd) ^ sw);
+      const v4s_t vlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(vt + cd));
+      const v4s_t vhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(vt + 4 * VROW + cd));
+      const h8_t Bv = __builtin_bit_cast(h8_t, __builtin_shufflevector(vlo, vhi, 0, 1, 2, 3, 4, 5, 6, 7));
+      O[dd] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ahi, Bv, O[dd], 0, 0, 0);
+      O[dd] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Alo, Bv, O[dd], 0, 0, 0);
+    }
+  }
+  // ---- records: wave w stores its dims of every head; wave 0 also m and l
+  // (an empty split stores O = 0, m = -inf, l = 0)
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    if (4 * g + i < a.GQ) {
+      float* rec = a.part + attn_rec(a, seq, row, kvh, split, 4 * g + i, D);
+#pragma unroll
+      for (int dd = 0; dd < DS; dd++) rec[16 * (DS * wave + dd) + j] = O[dd][i];
+    }
+  }
+  if (wave == 0 && lane < a.GQ) {
+    float* rec = a.part + attn_rec(a, seq, row, kvh, split, lane, D);
+    rec[D] = m;
+    rec[D + 1] = l_tot;
+  }
+}
+
+// Full layers (positions 0 .. P, one KV head per cache): 8 waves as 2 groups
+// of 4.  The 32-position tiles covering 0 .. P are dealt to the S splits
+// round-robin (split s: tiles s, s + S, s + 2S, ...), so in each round the
+// workgroups together read one contiguous stretch of the cache.  In round r
+// group c takes the split's tile 2r + c, and inside a group the head dimension is dealt to the waves as in k_fd_ring_ds, but by
+// QK k step round-robin (wave w: steps w, w + 4, ...): the RoPE partner of a
+// dim lies D/64 k steps on, a multiple of 4, so with one cached row per
+// position (VR) a wave rebuilds its keys from its own V elements.  The
+// partial scores meet in LDS, every wave of a group runs the group's online
+// softmax on the sums and forms O for its own D/4 dims.  The next round's V
+// rows are loaded into registers when a round starts and its K elements as
+// soon as the round's scores are formed, so both are in flight while the
+// round is processed; the V rows go to the group's LDS tile once the round's
+// PV is done.  (Global-to-LDS loads would leave the next round's rows in
+// flight across LDS accesses the compiler cannot tell apart from them, and it
+// then waits for all of them before each.)  At the end group 1 hands its
+// rescaled O to group 0 through LDS, which writes the split's records.
+//
+// V rows in LDS are unpadded: the 16-byte chunk c of tile row r sits at chunk
+// position c ^ 2 fds_swz(r), the swizzle k_fd_partial uses for D <= 256 (the
+// transposing reads of a 16-lane group then touch distinct banks for any row
+// pitch that is a multiple of 512 bytes).
+Q4_DEV int fds_swz(int r) { return (r & 3) | (((r >> 3) & 1) << 2); }
+
+// A workgroup barrier that orders LDS only: this wave's LDS operations
+// have completed (lgkmcnt 0) before it arrives.  __syncthreads' release fence
+// would also wait for every global load in flight, the next round's
+// prefetch included.
+Q4_DEV void lds_barrier() {
+  __asm__ __volatile__("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);         // vmcnt 63, expcnt 7, lgkmcnt 0
+  __builtin_amdgcn_s_barrier();
+  __asm__ __volatile__("" ::: "memory");
+}
+
+// queries [16][D], reused for the partial scores [2 groups][4 waves][2][64] float4
+template <int D>
+constexpr size_t fds_qx_bytes() { return (size_t)16 * D * 2 > 16384 ? (size_t)16 * D * 2 : 16384; }
+
+// V rows [2 groups][32][D], rows of this step [2][4][D], queries / scores
+template <int D>
+constexpr size_t fds_lds_bytes() { return (size_t)2 * 32 * D * 2 + (size_t)2 * 4 * D * 2 + fds_qx_bytes<D>(); }
+
+template <int D, bool VR>
+__global__ void __launch_bounds__(512) k_fd_full_ds(AttnArgs a) {
+  static_assert(D == 256 || D == 512, "a wave's k steps pair with their RoPE partners");
+  constexpr int G = 2;                        // wave groups
+  constexpr int KS = D / 128;                 // QK k steps of a wave (global step w + 4k)
+  constexpr int DS = D / 64;                  // PV dim steps of a wave (global DS w + dd)
+  constexpr int HS = D / 64;                  // k steps per half head
+  constexpr int RS = vr_rsteps<D>();          // VR: rotating k steps of the first half
+  constexpr int NR = VR ? 32 * RS : 1;
+  constexpr int CPR = D / 8, RPI = 64 / CPR;  // V: 16-byte chunks per row, rows per instruction
+  constexpr int NVS = 8 / RPI;                // V loads of a wave per tile (its 8 rows)
+  extern __shared__ __align__(16) unsigned char smem[];
+  uint16_t* vbuf = reinterpret_cast<uint16_t*>(smem);  // [G][32][D]
+  uint16_t* newK = vbuf + G * 32 * D;                  // [4][D] rows of this step
+  uint16_t* newV = newK + 4 * D;
+  uint16_t* q16 = newV + 4 * D;                        // [16][D] finished queries, then
+  f4_t* sx = reinterpret_cast<f4_t*>(q16);             // [G][4 waves][2][64] partial scores
+  __shared__ float wm[G][16], wl[G][16];
+  __shared__ double vr_f[NR];
+  __shared__ float2 vr_c4[NR];
+  __shared__ float vr_w[2 * NR];
+  static_assert(fds_lds_bytes<D>() + sizeof(wm) + sizeof(wl) + sizeof(vr_f) + sizeof(vr_c4) + sizeof(vr_w) <=
+                    160 * 1024, "LDS of one workgroup");
+  static_assert((size_t)G * 32 * D * 2 >= (size_t)4 * DS * 64 * 16, "merge buffer inside the V rows");
+  auto rebuilt = [](int s) { return VR && (s < RS || (s >= HS && s < HS + RS)); };
+
+  const int split = blockIdx.x, kvh = blockIdx.y;
+  const int seq = blockIdx.z / a.n_rows, row = blockIdx.z - seq * a.n_rows;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int grp = wave >> 2, w = wave & 3;
+
+  int base;
+  if (a.sp) base = *(const __attribute__((address_space(1))) int*)(&a.sp->pos0);
+  else base = a.pos0[seq];
+
+  // ---- finishing inputs, dealt round-robin to the 8 waves: this
+  // workgroup's query heads, then k and v of rows 0 .. row (both from the
+  // raw k projection on a full layer)
+  constexpr int FE = D / 64, FEH = fin_h<D>();
+  constexpr int MAXJ = (16 + 2 * 4 + 7) / 8;
+  const int njobs = a.fin_on ? a.GQ + 2 * (row + 1) : 0;
+  float raw[MAXJ][FE], wq[FE], wk[FE];
+  float2 fcs[MAXJ][FEH];
+  if (a.fin_on) {
+    const AttnFin& f = a.fin;
+    fin_load<D>(wq, f.q_norm);
+    fin_load<D>(wk, f.k_norm);
+#pragma unroll
+    for (int k = 0; k < MAXJ; k++) {
+      const int jb = wave + 8 * k;
+      if (jb >= njobs) break;
+      const int r = jb < a.GQ ? row : (jb - a.GQ) >> 1;
+      const float* rr = f.qkv + (long)r * f.ldq;
+      const float* src = jb < a.GQ ? rr + (long)(kvh * a.GQ + jb) * D : rr + (long)(a.Hq + kvh) * D;
+      fin_load<D>(raw[k], src);
+      const float2* cr = f.rope_cs + (long)r * f.cs_ld + lane * FEH;
+      if constexpr (FEH == 4) {
+        const float4 c0 = *reinterpret_cast<const float4*>(cr), c1 = *reinterpret_cast<const float4*>(cr + 2);
+        fcs[k][0] = make_float2(c0.x, c0.y); fcs[k][1] = make_float2(c0.z, c0.w);
+        fcs[k][2] = make_float2(c1.x, c1.y); fcs[k][3] = make_float2(c1.z, c1.w);
+      } else {
+        const float4 c0 = *reinterpret_cast<const float4*>(cr);
+        fcs[k][0] = make_float2(c0.x, c0.y); fcs[k][1] = make_float2(c0.z, c0.w);
+      }
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  base = __builtin_amdgcn_readfirstlane(base);
+  const int P = base + row;
+  // this split's tiles: split, split + S, ... of the 32-position tiles
+  // covering 0 .. P (positions past P are masked)
+  const int en = P + 1;
+  const int ntile = split <= (P >> 5) ? ((P >> 5) - split) / a.S + 1 : 0;
+  const int nround = (ntile + G - 1) / G;
+  auto tile0 = [&](int i) { return 32 * (split + a.S * i); };
+  auto owns = [&](int p) { return p <= P && (p >> 5) % a.S == split; };
+  const int P0new = a.fin_on ? base : 0x7FFFFFFF;
+  const int nv_end = min(en, P0new);
+
+  const int j = lane & 15, g = lane >> 4;
+  const bool col_ok = j < a.GQ;
+  uint16_t* vb = a.v + seq * a.seq_stride;
+  uint16_t* kb = VR ? vb : a.k + seq * a.seq_stride;
+  // cache row (elements) of tile row r; rows past nv_end are masked or
+  // formed in this step and read row 0
+  auto row_at = [&](int t0, int r) -> long { return t0 + r < nv_end ? (long)(t0 + r) * D : 0l; };
+  uint16_t* vl = vbuf + grp * 32 * D;
+
+  h8_t KA[KS], KB[KS], KAl[KS], KBl[KS];
+  u4v VS[NVS];                                // this wave's V rows of the next tile
+  // Every round issues the same loads whether or not the group has a next
+  // tile (without one, all lanes read row 0: one line per instruction), so
+  // the compiler's count of loads in flight is the same on every path and its
+  // waits for this round's registers leave the next round's loads in flight.
+  auto load_k = [&](int t0, bool real) {
+    const int ra = 8 * (j >> 2) + (j & 3);
+    const uint16_t* ka = real ? kb + row_at(t0, ra) + 8 * g : kb;
+    const uint16_t* kc = real ? kb + row_at(t0, ra + 4) + 8 * g : kb;
+#pragma unroll
+    for (int k = 0; k < KS; k++) {
+      const int s = w + 4 * k;
+      const u4v* pa_ = reinterpret_cast<const u4v*>(ka + 32 * s);
+      const u4v* pb_ = reinterpret_cast<const u4v*>(kc + 32 * s);
+      // VR: plain loads (the rows' other read is served by the L2)
+      KA[k] = __builtin_bit_cast(h8_t, VR ? *pa_ : __builtin_nontemporal_load(pa_));
+      KB[k] = __builtin_bit_cast(h8_t, VR ? *pb_ : __builtin_nontemporal_load(pb_));
+    }
+  };
+  // lane l takes chunk position l % CPR of tile row 8w + RPI i + l / CPR, so
+  // loads the chunk that the swizzle puts there
+  auto load_v = [&](int t0, bool real) {
+    const int rl = lane / CPR, pc = lane % CPR;
+#pragma unroll
+    for (int i = 0; i < NVS; i++) {
+      const int r = 8 * w + RPI * i + rl;
+      const u4v* src = reinterpret_cast<const u4v*>(real ? vb + row_at(t0, r) + (pc ^ (2 * fds_swz(r))) * 8 : vb);
+      VS[i] = VR ? *src : __builtin_nontemporal_load(src);
+    }
+  };
+  auto store_v = [&]() {
+#pragma unroll
+    for (int i = 0; i < NVS; i++) *reinterpret_cast<u4v*>(vl + (8 * w + RPI * i) * D + lane * 8) = VS[i];
+  };
+  load_k(tile0(grp), grp < ntile);
+  load_v(tile0(grp), grp < ntile);
+  if constexpr (VR) {
+    const int i = threadIdx.x;
+    if (i < NR) {
+      const double f = i < a.krot ? pow(a.theta, -2.0 * (double)i / (double)D) : 0.0;
+      const double r4 = 4.0 * f;
+      vr_f[i] = f * 0.15915494309189535;                       // revolutions per position
+      vr_c4[i] = make_float2((float)cos(r4), (float)sin(r4));
+      vr_w[i] = a.kw[i];
+      vr_w[NR + i] = a.kw[D / 2 + i];
+    }
+  }
+
+  if (a.fin_on) {
+    const AttnFin& f = a.fin;
+#pragma unroll
+    for (int k = 0; k < MAXJ; k++) {
+      const int jb = wave + 8 * k;
+      if (jb >= njobs) break;
+      if (jb < a.GQ) {
+        finish_vals<D>(raw[k], wq, true, true, fcs[k], f.rot_pairs, f.eps, q16 + jb * D);
+        continue;
+      }
+      const int r = (jb - a.GQ) >> 1;        // rows this workgroup attends and holds
+      if (r > row || !owns(base + r)) continue;
+      if (((jb - a.GQ) & 1) == 0) {
+        if (!VR) finish_vals<D>(raw[k], wk, true, true, fcs[k], f.rot_pairs, f.eps, newK + r * D);
+      } else if (f.v_norm) {
+        finish_vals<D>(raw[k], wk, false, false, fcs[k], f.rot_pairs, f.eps, newV + r * D);
+      } else {
+        fin_store<D>(raw[k], newV + r * D);
+      }
+    }
+  }
+  __syncthreads();                            // finished rows and the VR tables are in
+  if (a.fin_on) {
+    const AttnFin& f = a.fin;
+    if (f.q_out && split == 0) {
+      constexpr int CH = D / 8;
+      for (int i = threadIdx.x; i < a.GQ * CH; i += 512) {
+        const int jq = i / CH, c = i - jq * CH;
+        *reinterpret_cast<u4v*>(f.q_out + ((long)row * a.Hq + kvh * a.GQ + jq) * D + c * 8) =
+            *reinterpret_cast<const u4v*>(q16 + jq * D + c * 8);
+      }
+    }
+    if (owns(P)) {                            // the row's own position goes to the cache
+      const long so = (long)P * D;
+      for (int d = threadIdx.x; d < D; d += 512) {
+        if (!VR) kb[so + d] = newK[row * D + d];
+        vb[so + d] = newV[row * D + d];
+      }
+    }
+  }
+  // ---- queries of this wave's k steps as the MFMA B operand (VR: in the
+  // steps whose key is kw * v, q * kw split into fp16 hi and lo)
+  h8_t qb[KS], qlo[KS];
+  {
+    const uint16_t* qp = a.fin_on ? q16 + (col_ok ? j : 0) * D + 8 * g
+                                  : a.q + (((long)seq * a.n_rows + row) * a.Hq + (col_ok ? kvh * a.GQ + j : 0)) * D +
+                                        8 * g;
+#pragma unroll
+    for (int k = 0; k < KS; k++) {
+      const int s = w + 4 * k;
+      u4v t = *reinterpret_cast<const u4v*>(qp + 32 * s);
+      if (!col_ok) t = (u4v){0u, 0u, 0u, 0u};
+      if (VR && !rebuilt(s)) {
+        const float4 w0 = *reinterpret_cast<const float4*>(a.kw + 32 * s + 8 * g);
+        const float4 w1 = *reinterpret_cast<const float4*>(a.kw + 32 * s + 8 * g + 4);
+        const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+        const h8_t qh = __builtin_bit_cast(h8_t, t);
+        h8_t hi, lo;
+#pragma unroll
+        for (int e = 0; e < 8; e++) {
+          const float x = (float)qh[e] * wv[e];
+          hi[e] = (_Float16)x;
+          lo[e] = (_Float16)(x - (float)hi[e]);
+        }
+        qb[k] = hi;
+        qlo[k] = lo;
+      } else {
+        qb[k] = __builtin_bit_cast(h8_t, t);
+      }
+    }
+  }
+  if (a.fin_on) __syncthreads();              // every wave has its queries: the scores take their place
+  store_v();                                  // the first tile's V rows (visible after the first barrier)
+
+  float m_run = -INFINITY, l_part = 0.f;
+  f4_t O[DS];
+#pragma unroll
+  for (int d = 0; d < DS; d++) O[d] = (f4_t){0.f, 0.f, 0.f, 0.f};
+  f4_t* sxw = sx + (grp * 4 + w) * 2 * 64;
+  const f4_t* sxg = sx + grp * 4 * 2 * 64;
+
+  for (int rd = 0; rd < nround; rd++) {
+    const int ti = G * rd + grp;
+    const bool act = ti < ntile;              // group-uniform
+    const bool act1 = ti + G < ntile;         // the group's next round
+    const int t0 = tile0(ti);
+    load_v(tile0(ti + G), act1);
+    if (act) {
+      if (t0 + 31 >= P0new) {                 // rows formed in this step: keys, then V rows
+        const int pa = t0 + 8 * (j >> 2) + (j & 3), pb = pa + 4;
+        const uint16_t* nk = VR ? newV : newK;
+#pragma unroll
+        for (int k = 0; k < KS; k++) {
+          const int off = 32 * (w + 4 * k) + 8 * g;
+          if (pa >= P0new && pa < en) KA[k] = *reinterpret_cast<const h8_t*>(nk + (pa - P0new) * D + off);
+          if (pb >= P0new && pb < en) KB[k] = *reinterpret_cast<const h8_t*>(nk + (pb - P0new) * D + off);
+        }
+#pragma unroll
+        for (int r = 8 * w; r < 8 * w + 8; r++) {
+          const int pr = t0 + r;
+          if (pr >= P0new && pr < en && lane < D / 8)
+            *reinterpret_cast<u4v*>(vl + r * D + (lane ^ (2 * fds_swz(r))) * 8) =
+                *reinterpret_cast<const u4v*>(newV + (pr - P0new) * D + lane * 8);
+        }
+      }
+      if (VR && w < RS) {
+        // keys of the rotating steps w and w + HS (local 0 and HS / 4):
+        // lane (j, g) holds positions pa (KA) and pa + 4 (KB)
+        const int pa = t0 + 8 * (j >> 2) + (j & 3);
+#pragma unroll
+        for (int e = 0; e < 8; e++) {
+          const int i = 32 * w + 8 * g + e;
+          double r = (double)pa * vr_f[i];
+          r -= floor(r);
+          const float rv = (float)r;
+          const float ca = __builtin_amdgcn_cosf(rv), sa = __builtin_amdgcn_sinf(rv);
+          const float2 c4 = vr_c4[i];
+          const float cb = ca * c4.x - sa * c4.y, sb = sa * c4.x + ca * c4.y;
+          const float w0 = vr_w[i], w1 = vr_w[NR + i];
+          auto form = [&](h8_t& X0, h8_t& X1, h8_t& L0, h8_t& L1, float c, float sn) {
+            const float u0 = w0 * (float)X0[e], u1 = w1 * (float)X1[e];
+            const float k0 = c * u0 - sn * u1, k1 = sn * u0 + c * u1;
+            const _Float16 h0 = (_Float16)k0, h1 = (_Float16)k1;
+            X0[e] = h0; L0[e] = (_Float16)(k0 - (float)h0);
+            X1[e] = h1; L1[e] = (_Float16)(k1 - (float)h1);
+          };
+          form(KA[0], KA[HS / 4], KAl[0], KAl[HS / 4], ca, sa);
+          form(KB[0], KB[HS / 4], KBl[0], KBl[HS / 4], cb, sb);
+        }
+      }
+      f4_t p0 = {0.f, 0.f, 0.f, 0.f}, p1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k = 0; k < KS; k++) {
+        const int s = w + 4 * k;
+        p0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(KA[k], qb[k], p0, 0, 0, 0);
+        p1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(KB[k], qb[k], p1, 0, 0, 0);
+        if (VR && rebuilt(s)) {
+          p0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(KAl[k], qb[k], p0, 0, 0, 0);
+          p1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(KBl[k], qb[k], p1, 0, 0, 0);
+        } else if (VR) {
+          p0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(KA[k], qlo[k], p0, 0, 0, 0);
+          p1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(KB[k], qlo[k], p1, 0, 0, 0);
+        }
+      }
+      sxw[lane] = p0;
+      sxw[64 + lane] = p1;
+    }
+    load_k(tile0(ti + G), act1);              // the registers are free once the scores are formed
+    lds_barrier();
+    if (act) {
+      // full scores: the group's 4 parts added in a fixed order
+      f4_t c0 = sxg[lane], c1 = sxg[64 + lane];
+#pragma unroll
+      for (int u = 1; u < 4; u++) {
+        const f4_t e0 = sxg[u * 128 + lane], e1 = sxg[u * 128 + 64 + lane];
+#pragma unroll
+        for (int i = 0; i < 4; i++) { c0[i] += e0[i]; c1[i] += e1[i]; }
+      }
+      float sv[8];
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        sv[i] = (t0 + 8 * g + i < en) ? c0[i] * a.scale_log2 : -INFINITY;
+        sv[4 + i] = (t0 + 8 * g + 4 + i < en) ? c1[i] * a.scale_log2 : -INFINITY;
+      }
+      float mt = sv[0];
+#pragma unroll
+      for (int i = 1; i < 8; i++) mt = fmaxf(mt, sv[i]);
+      mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+      const float m_new = fmaxf(m_run, mt);   // finite: position t0 is admitted
+      const float alpha = exp2f(m_run - m_new);
+      m_run = m_new;
+      float p[8], ps = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; i++) {
+        p[i] = exp2f(sv[i] - m_new);
+        ps += p[i];
+      }
+      l_part = l_part * alpha + ps;
+      float al[4];
+#pragma unroll
+      for (int i = 0; i < 4; i++) al[i] = __shfl(alpha, 4 * g + i, 64);
+#pragma unroll
+      for (int d = 0; d < DS; d++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) O[d][i] *= al[i];
+      h8_t Ahi, Alo;
+#pragma unroll
+      for (int i = 0; i < 8; i++) {
+        const _Float16 hi = (_Float16)p[i];
+        Ahi[i] = hi;
+        Alo[i] = (_Float16)(p[i] - (float)hi);
+      }
+      // O += P V over this wave's dims (lane (j, g) addresses row 8g + j/4
+      // (and + 4) at dims 16d + 4 (j % 4), as in k_fd_partial)
+      const int sw = fds_swz(8 * g + (j >> 2));
+      const uint16_t* vt = vl + (8 * g + (j >> 2)) * D + 4 * (j & 3);
+#pragma unroll
+      for (int dd = 0; dd < DS; dd++) {
+        typedef short v4s_t __attribute__((ext_vector_type(4)));
+        typedef __attribute__((address_space(3))) v4s_t lds_v4s;
+        const int cd = 16 * ((DS * w + dd) ^ sw);
+        const v4s_t vlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(vt + cd));
+        const v4s_t vhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(vt + 4 * D + cd));
+        const h8_t Bv = __builtin_bit_cast(h8_t, __builtin_shufflevector(vlo, vhi, 0, 1, 2, 3, 4, 5, 6, 7));
+        O[dd] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ahi, Bv, O[dd], 0, 0, 0);
+        O[dd] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Alo, Bv, O[dd], 0, 0, 0);
+      }
+    }
+    lds_barrier();                            // the V rows and the scores are free again
+    store_v();                                // the next tile's V rows (visible after its first barrier)
+  }
+
+  // ---- merge the two groups: maxima and sums per head meet in LDS; group 1
+  // stores its rescaled O (one float4 of 4 heads per dim step and lane) into
+  // the V rows, group 0 adds it to its own in a fixed order and writes the
+  // records
+  float l_tot = l_part + __shfl_xor(l_part, 16, 64);
+  l_tot += __shfl_xor(l_tot, 32, 64);
+  if (w == 0 && lane < 16) { wm[grp][lane] = m_run; wl[grp][lane] = l_tot; }
+  __syncthreads();
+  float fw[4];
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const int hc = 4 * g + i;
+    const float M = fmaxf(wm[0][hc], wm[1][hc]);
+    fw[i] = wm[grp][hc] == -INFINITY ? 0.f : exp2f(wm[grp][hc] - M);
+  }
+  f4_t* ob = reinterpret_cast<f4_t*>(smem);   // [4 waves][DS][64]
+  if (grp == 1) {
+#pragma unroll
+    for (int dd = 0; dd < DS; dd++)
+      ob[(w * DS + dd) * 64 + lane] = (f4_t){O[dd][0] * fw[0], O[dd][1] * fw[1], O[dd][2] * fw[2], O[dd][3] * fw[3]};
+  }
+  __syncthreads();
+  if (grp == 0) {
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      if (4 * g + i < a.GQ) {
+        float* rec = a.part + attn_rec(a, seq, row, kvh, split, 4 * g + i, D);
+#pragma unroll
+        for (int dd = 0; dd < DS; dd++)
+          rec[16 * (DS * w + dd) + j] = O[dd][i] * fw[i] + ob[(w * DS + dd) * 64 + lane][i];
+      }
+    }
+    if (w == 0 && lane < a.GQ) {
+      const float M = fmaxf(wm[0][lane], wm[1][lane]);
+      float l = 0.f;
+      if (M != -INFINITY) l = exp2f(wm[0][lane] - M) * wl[0][lane] + exp2f(wm[1][lane] - M) * wl[1][lane];
+      float* rec = a.part + attn_rec(a, seq, row, kvh, split, lane, D);
+      rec[D] = M;
+      rec[D + 1] = l;
+    }
+  }
+}
+
 // out[seq][row][h][d] = sum_s O_s 2^(m_s - M) / sum_s l_s 2^(m_s - M).
 // Grid (n_seq * n_rows * Hq, D / 64), 256 threads: lane = output dim, wave w
 // takes splits w, w + 4, ... (S <= MAXS).  Every load of the workgroup is

@@ -138,6 +138,13 @@ q4_status set_attrs() {
   e = e != hipSuccess ? e : max_lds(&k_fd_partial<512, false, true>, (int)fd_lds_bytes<512>());
   e = e != hipSuccess ? e : max_lds(&k_fd_partial<128, true, true>, (int)fd_lds_bytes<128>());
   e = e != hipSuccess ? e : max_lds(&k_fd_partial<512, true, true>, (int)fd_lds_bytes<512>());
+  e = e != hipSuccess ? e : max_lds(&k_fd_ring_ds<128>, (int)ds_lds_bytes<128>());
+  e = e != hipSuccess ? e : max_lds(&k_fd_ring_ds<256>, (int)ds_lds_bytes<256>());
+  e = e != hipSuccess ? e : max_lds(&k_fd_ring_ds<512>, (int)ds_lds_bytes<512>());
+  e = e != hipSuccess ? e : max_lds(&k_fd_full_ds<256, false>, (int)fds_lds_bytes<256>());
+  e = e != hipSuccess ? e : max_lds(&k_fd_full_ds<256, true>, (int)fds_lds_bytes<256>());
+  e = e != hipSuccess ? e : max_lds(&k_fd_full_ds<512, false>, (int)fds_lds_bytes<512>());
+  e = e != hipSuccess ? e : max_lds(&k_fd_full_ds<512, true>, (int)fds_lds_bytes<512>());
   e = e != hipSuccess ? e : max_lds(&k_fd_rows4<128>, (int)rows4_lds_bytes<128>());
   e = e != hipSuccess ? e : max_lds(&k_fd_rows4<256>, (int)rows4_lds_bytes<256>());
   e = e != hipSuccess ? e : max_lds(&k_fd_rows4<512>, (int)rows4_lds_bytes<512>());
@@ -201,8 +208,46 @@ void launch_rows4(const AttnArgs& a, int D, int n_seq, uint16_t* out16, hipStrea
   }
 }
 
+// Ring layers whose splits hold at most one tile, one row per workgroup:
+// the head dimension dealt to the 4 waves of a workgroup.
+template <int D>
+void launch_ring_ds_d(const AttnArgs& a, int n_seq, float* out32, uint16_t* out16, hipStream_t st) {
+  const dim3 grid(a.kvh_major ? a.Hkv : a.S, a.kvh_major ? a.S : a.Hkv, n_seq * a.n_rows);
+  hipLaunchKernelGGL(k_fd_ring_ds<D>, grid, dim3(256), ds_lds_bytes<D>(), st, a);
+  launch_combine<D>(a, n_seq, out32, out16, st);
+}
+
+bool ring_ds_ok(const AttnArgs& a, int D) {
+  return a.ring && D >= 128 && (long)a.S * 32 >= a.W && a.rpw <= 1 && !a.vrow;
+}
+
+// Full layers, one row per workgroup: 8 waves, the head dimension dealt
+// to the waves of each 4-wave group.
+template <int D>
+void launch_full_ds_d(const AttnArgs& a, int n_seq, float* out32, uint16_t* out16, hipStream_t st) {
+  const dim3 grid(a.S, a.Hkv, n_seq * a.n_rows);
+  if (a.vrow) hipLaunchKernelGGL((k_fd_full_ds<D, true>), grid, dim3(512), fds_lds_bytes<D>(), st, a);
+  else hipLaunchKernelGGL((k_fd_full_ds<D, false>), grid, dim3(512), fds_lds_bytes<D>(), st, a);
+  launch_combine<D>(a, n_seq, out32, out16, st);
+}
+
+bool full_ds_ok(const AttnArgs& a, int D) { return !a.ring && (D == 256 || D == 512) && a.rpw <= 1; }
+
 // Split-K partials then the combine (S <= kMaxSplits).
 void launch_fd(const AttnArgs& a, int D, int n_seq, float* out32, uint16_t* out16, hipStream_t st) {
+  if (full_ds_ok(a, D)) {
+    if (D == 256) launch_full_ds_d<256>(a, n_seq, out32, out16, st);
+    else launch_full_ds_d<512>(a, n_seq, out32, out16, st);
+    return;
+  }
+  if (ring_ds_ok(a, D)) {
+    switch (D) {
+      case 128: launch_ring_ds_d<128>(a, n_seq, out32, out16, st); break;
+      case 256: launch_ring_ds_d<256>(a, n_seq, out32, out16, st); break;
+      default: launch_ring_ds_d<512>(a, n_seq, out32, out16, st); break;
+    }
+    return;
+  }
   switch (D) {
     case 64: launch_fd_d<64>(a, n_seq, out32, out16, st); break;
     case 128: launch_fd_d<128>(a, n_seq, out32, out16, st); break;
@@ -1244,7 +1289,11 @@ q4_status flash_decode_ring(const uint16_t* q, const uint16_t* k_ring, const uin
   a.q = q; a.k = const_cast<uint16_t*>(k_ring); a.v = const_cast<uint16_t*>(v_ring); a.seq_stride = seq_stride;
   a.Hq = Hq; a.Hkv = Hkv; a.GQ = Hq / Hkv; a.ring = 1; a.R = R; a.W = W;
   a.n_rows = n_rows;
-  a.S = (int)std::min<long>(fd_split_cap(n_seq, n_rows), std::max<long>(1, ceil_div(W, kTilePos)));
+  // one 32-position tile per split when the split cap allows it (the waves
+  // then share each tile's head dimension), else 4 tiles per split
+  const long cap_s = fd_split_cap(n_seq, n_rows);
+  a.S = (int)std::min<long>(cap_s, std::max<long>(1, ceil_div(W, kTilePos)));
+  if (D >= 128 && ceil_div(W, 32) <= cap_s) a.S = (int)ceil_div(W, 32);
   a.scale_log2 = scale * 1.4426950408889634f;
   a.sp = nullptr; a.part = static_cast<float*>(ws);
   for (int s = 0; s < n_seq; s++) a.pos0[s] = pos0[s];

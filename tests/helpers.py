@@ -31,6 +31,16 @@ def assert_close_composed(gpu, ref, atol=ATOL, rtol=RTOL, frac=0.98, factor=4.0,
     output, so two correct fp32 implementations (two summation orders of the
     same kernels) already differ by about the elementwise bar on a few
     elements; kernel-level outputs keep the elementwise bar (assert_close)."""
+    inside, worst, rms, rms_bar = composed_stats(gpu, ref, atol, rtol, what)
+    assert inside >= frac and worst <= factor and rms <= rms_bar, (
+        f"{what}: {inside:.5f} of elements within the bar (need {frac}), worst error/bound {worst:.2f} "
+        f"(need <= {factor}), rms error {rms:.2e} (need <= {rms_bar:.2e})")
+    return inside
+
+
+def composed_stats(gpu, ref, atol=ATOL, rtol=RTOL, what=""):
+    """(fraction of elements within the elementwise bar, worst error / bar,
+    RMS error, the composed RMS bar: rtol * RMS(ref) + atol / 4)."""
     g = gpu.detach().double().cpu().numpy() if torch.is_tensor(gpu) else np.asarray(gpu, np.float64)
     r = np.asarray(ref, dtype=np.float64)
     assert g.shape == r.shape, (what, g.shape, r.shape)
@@ -41,10 +51,7 @@ def assert_close_composed(gpu, ref, atol=ATOL, rtol=RTOL, frac=0.98, factor=4.0,
     worst = float((err / bound).max())
     rms = float(np.sqrt((err ** 2).mean()))
     rms_bar = rtol * float(np.sqrt((r ** 2).mean())) + atol / 4
-    assert inside >= frac and worst <= factor and rms <= rms_bar, (
-        f"{what}: {inside:.5f} of elements within the bar (need {frac}), worst error/bound {worst:.2f} "
-        f"(need <= {factor}), rms error {rms:.2e} (need <= {rms_bar:.2e})")
-    return inside
+    return inside, worst, rms, rms_bar
 
 
 def f16bits(t):
