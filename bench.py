@@ -11,7 +11,7 @@ at three shapes, context-131072 and width-4 verify figures, the attention
 kernels alone, and the CPU oracle timed on the host cores on a bounded
 sample.
 
-  python bench.py [--gpus 1] [--steps K] [--warmup W] [--mode full|gemv|step|traffic|prefill]
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--mode full|gemv|step|traffic|prefill|attn_traffic]
 """
 import argparse
 import json
@@ -30,7 +30,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--mode", default="full", choices=["full", "gemv", "step", "traffic", "prefill"])
+    ap.add_argument("--mode", default="full", choices=["full", "gemv", "step", "traffic", "prefill", "attn_traffic"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     return ap.parse_args()
 
@@ -307,6 +307,41 @@ def traffic_launches(q4, torch, model):
     torch.cuda.synchronize()
 
 
+def attention_traffic_launches(q4, torch):
+    """What the attention counter runs profile, eagerly (one dispatch per
+    kernel): a plain device copy of COPY_BYTES (calibration), then twice each
+    full attention at context 32768 (16 q heads, D 512; the K/V pair layout
+    and the one-row layout, in buffers larger than the last-level cache), the
+    ring (8 KV heads, D 256, W 1024, R 2048) for one sequence, and 40 rings
+    in one call."""
+    from int4_q4_gemv_amd import synth
+    src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    del src, dst
+    cap = 131076
+    bufs = [synth.full_attn_inputs(131072, cap, seed=3 + i, device="cuda") for i in range(4)]
+    kw = synth.normal((512,), 0.1, synth.gen(3), mean=1.0).to("cuda")
+    ws = q4._fd_ws(1, 1, 16, 512, "cuda")
+    for i in range(2):
+        q4.flash_decode_full(*bufs[i], 32767, 1.0, ws=ws)
+    for i in range(2):
+        q4.flash_decode_full_vrow(bufs[2 + i][0], bufs[2 + i][2], kw, 1e6, 64, 32767, 1.0, ws=ws)
+    torch.cuda.synchronize()
+    del bufs
+    q, k, v = (t.to("cuda") for t in synth.ring_inputs(100000, n_rows=1, n_rejected=4))
+    ws = q4._fd_ws(1, 1, 16, 256, "cuda")
+    for _ in range(2):
+        q4.flash_decode_ring(q, k, v, 1024, 100000, 1.0, ws=ws)
+    rings = [synth.ring_inputs(100000, n_rows=1, n_rejected=4, seed=100 + s, device="cuda") for s in range(40)]
+    qs, ks, vs = (torch.stack([r[j] for r in rings]).to("cuda") for j in range(3))
+    del rings
+    ws = q4._fd_ws(40, 1, 16, 256, "cuda")
+    q4.flash_decode_ring(qs, ks, vs, 1024, [100000] * 40, 1.0, ws=ws)
+    torch.cuda.synchronize()
+
+
 def stored_traffic():
     """Per-launch HBM bytes of the roofline kernel from the committed counter
     summary, or None when the summary is absent or was taken on other GEMV
@@ -431,6 +466,12 @@ def main():
     from dataclasses import replace
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.mode == "attn_traffic":
+        stream = torch.cuda.Stream()
+        with torch.cuda.stream(stream):
+            attention_traffic_launches(q4, torch)
+        print(json.dumps({"mode": "attn_traffic", "copy_bytes": COPY_BYTES}))
+        return
     ctx_hi = 131072
     cfg = replace(synth.FULL48, full_cap=ctx_hi + 8)
     stream = torch.cuda.Stream()

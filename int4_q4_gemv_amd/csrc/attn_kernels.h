@@ -1033,19 +1033,28 @@ __global__ void __launch_bounds__(256) k_fd_ring_ds(AttnArgs a) {
 // of 4.  The 32-position tiles covering 0 .. P are dealt to the S splits
 // round-robin (split s: tiles s, s + S, s + 2S, ...), so in each round the
 // workgroups together read one contiguous stretch of the cache.  In round r
-// group c takes the split's tile 2r + c, and inside a group the head dimension is dealt to the waves as in k_fd_ring_ds, but by
-// QK k step round-robin (wave w: steps w, w + 4, ...): the RoPE partner of a
-// dim lies D/64 k steps on, a multiple of 4, so with one cached row per
-// position (VR) a wave rebuilds its keys from its own V elements.  The
-// partial scores meet in LDS, every wave of a group runs the group's online
-// softmax on the sums and forms O for its own D/4 dims.  The next round's V
-// rows are loaded into registers when a round starts and its K elements as
-// soon as the round's scores are formed, so both are in flight while the
-// round is processed; the V rows go to the group's LDS tile once the round's
-// PV is done.  (Global-to-LDS loads would leave the next round's rows in
-// flight across LDS accesses the compiler cannot tell apart from them, and it
-// then waits for all of them before each.)  At the end group 1 hands its
-// rescaled O to group 0 through LDS, which writes the split's records.
+// group c takes the split's tile 2r + c.  Inside a group the head dimension
+// is dealt to the waves as in k_fd_ring_ds, but by QK k step round-robin
+// (wave w: steps w, w + 4, ...): the RoPE partner of a dim lies D/64 k steps
+// on, a multiple of 4, so with one cached row per position (VR) a wave
+// rebuilds its keys from its own V elements.  The partial scores meet in
+// LDS, every wave of a group runs the group's online softmax on the sums and
+// forms O for its own D/4 dims.  At the end group 1 hands its rescaled O to
+// group 0 through LDS, which writes the split's records.
+//
+// Loads in flight: V rows go straight to LDS two rounds ahead (the even
+// rounds' tiles in one array, the odd rounds' in another, each refilled once
+// the round reading it has passed its last barrier), K elements to registers
+// one round ahead (issued as soon as the round's scores are formed).  With
+// one row per position the keys are read from the tile's V rows in LDS once
+// every wave's rows have landed, so the cache is read once and no key load
+// is on the round's path.  The V
+// arrays are LDS objects of their own: the compiler then knows that the LDS
+// accesses to the scores, the queries and the step's rows do not touch the
+// rows still arriving, and waits for those only where they are read.  Every
+// round issues the same loads whether or not the group has such a tile
+// (without one, all lanes read row 0: one line per instruction), so the
+// count of loads in flight, and with it each wait, is the same on every path.
 //
 // V rows in LDS are unpadded: the 16-byte chunk c of tile row r sits at chunk
 // position c ^ 2 fds_swz(r), the swizzle k_fd_partial uses for D <= 256 (the
@@ -1055,8 +1064,7 @@ Q4_DEV int fds_swz(int r) { return (r & 3) | (((r >> 3) & 1) << 2); }
 
 // A workgroup barrier that orders LDS only: this wave's LDS operations
 // have completed (lgkmcnt 0) before it arrives.  __syncthreads' release fence
-// would also wait for every global load in flight, the next round's
-// prefetch included.
+// would also wait for every global load in flight, the prefetches included.
 Q4_DEV void lds_barrier() {
   __asm__ __volatile__("" ::: "memory");
   __builtin_amdgcn_s_waitcnt(0xC07F);         // vmcnt 63, expcnt 7, lgkmcnt 0
@@ -1064,13 +1072,19 @@ Q4_DEV void lds_barrier() {
   __asm__ __volatile__("" ::: "memory");
 }
 
+// waits until at most N vector memory instructions of this wave are in flight
+template <int N>
+Q4_DEV void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+  __asm__ __volatile__("" ::: "memory");
+}
+
+template <int N> struct fds_ic { static constexpr int v = N; };
+
 // queries [16][D], reused for the partial scores [2 groups][4 waves][2][64] float4
 template <int D>
-constexpr size_t fds_qx_bytes() { return (size_t)16 * D * 2 > 16384 ? (size_t)16 * D * 2 : 16384; }
-
-// V rows [2 groups][32][D], rows of this step [2][4][D], queries / scores
-template <int D>
-constexpr size_t fds_lds_bytes() { return (size_t)2 * 32 * D * 2 + (size_t)2 * 4 * D * 2 + fds_qx_bytes<D>(); }
+constexpr int fds_qx_halves() { return 16 * D > 8192 ? 16 * D : 8192; }
 
 template <int D, bool VR>
 __global__ void __launch_bounds__(512) k_fd_full_ds(AttnArgs a) {
@@ -1083,30 +1097,41 @@ __global__ void __launch_bounds__(512) k_fd_full_ds(AttnArgs a) {
   constexpr int NR = VR ? 32 * RS : 1;
   constexpr int CPR = D / 8, RPI = 64 / CPR;  // V: 16-byte chunks per row, rows per instruction
   constexpr int NVS = 8 / RPI;                // V loads of a wave per tile (its 8 rows)
-  extern __shared__ __align__(16) unsigned char smem[];
-  uint16_t* vbuf = reinterpret_cast<uint16_t*>(smem);  // [G][32][D]
-  uint16_t* newK = vbuf + G * 32 * D;                  // [4][D] rows of this step
-  uint16_t* newV = newK + 4 * D;
-  uint16_t* q16 = newV + 4 * D;                        // [16][D] finished queries, then
-  f4_t* sx = reinterpret_cast<f4_t*>(q16);             // [G][4 waves][2][64] partial scores
+  __shared__ __align__(16) uint16_t vA[G * 32 * D];   // V rows of the even rounds' tiles [G][32][D]
+  __shared__ __align__(16) uint16_t vB[G * 32 * D];   // ... of the odd rounds' tiles
+  __shared__ __align__(16) uint16_t qx[fds_qx_halves<D>()];
+  __shared__ __align__(16) uint16_t nkv[2 * 4 * D];   // rows of this step: K [4][D], V [4][D]
   __shared__ float wm[G][16], wl[G][16];
   __shared__ double vr_f[NR];
   __shared__ float2 vr_c4[NR];
   __shared__ float vr_w[2 * NR];
-  static_assert(fds_lds_bytes<D>() + sizeof(wm) + sizeof(wl) + sizeof(vr_f) + sizeof(vr_c4) + sizeof(vr_w) <=
-                    160 * 1024, "LDS of one workgroup");
   static_assert((size_t)G * 32 * D * 2 >= (size_t)4 * DS * 64 * 16, "merge buffer inside the V rows");
+  uint16_t* newK = nkv;
+  uint16_t* newV = nkv + 4 * D;
+  uint16_t* q16 = qx;                         // [16][D] finished queries, then
+  f4_t* sx = reinterpret_cast<f4_t*>(qx);     // [G][4 waves][2][64] partial scores
   auto rebuilt = [](int s) { return VR && (s < RS || (s >= HS && s < HS + RS)); };
 
   const int split = blockIdx.x, kvh = blockIdx.y;
   const int seq = blockIdx.z / a.n_rows, row = blockIdx.z - seq * a.n_rows;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int grp = wave >> 2, w = wave & 3;
+  const int j = lane & 15, g = lane >> 4;
+  const bool col_ok = j < a.GQ;
 
   int base;
   if (a.sp) base = *(const __attribute__((address_space(1))) int*)(&a.sp->pos0);
   else base = a.pos0[seq];
 
+  // ---- queries of a call without the finishing prologue: issued first, so
+  // that no K/V load is ahead of them
+  u4v qraw[KS];
+  if (!a.fin_on) {
+    const uint16_t* qp =
+        a.q + (((long)seq * a.n_rows + row) * a.Hq + (col_ok ? kvh * a.GQ + j : 0)) * D + 8 * g;
+#pragma unroll
+    for (int k = 0; k < KS; k++) qraw[k] = *reinterpret_cast<const u4v*>(qp + 32 * (w + 4 * k));
+  }
   // ---- finishing inputs, dealt round-robin to the 8 waves: this
   // workgroup's query heads, then k and v of rows 0 .. row (both from the
   // raw k projection on a full layer)
@@ -1152,22 +1177,16 @@ __global__ void __launch_bounds__(512) k_fd_full_ds(AttnArgs a) {
   const int P0new = a.fin_on ? base : 0x7FFFFFFF;
   const int nv_end = min(en, P0new);
 
-  const int j = lane & 15, g = lane >> 4;
-  const bool col_ok = j < a.GQ;
   uint16_t* vb = a.v + seq * a.seq_stride;
   uint16_t* kb = VR ? vb : a.k + seq * a.seq_stride;
   // cache row (elements) of tile row r; rows past nv_end are masked or
   // formed in this step and read row 0
   auto row_at = [&](int t0, int r) -> long { return t0 + r < nv_end ? (long)(t0 + r) * D : 0l; };
-  uint16_t* vl = vbuf + grp * 32 * D;
 
   h8_t KA[KS], KB[KS], KAl[KS], KBl[KS];
-  u4v VS[NVS];                                // this wave's V rows of the next tile
-  // Every round issues the same loads whether or not the group has a next
-  // tile (without one, all lanes read row 0: one line per instruction), so
-  // the compiler's count of loads in flight is the same on every path and its
-  // waits for this round's registers leave the next round's loads in flight.
+  // K elements of this wave's k steps from global memory (the K/V pair layout)
   auto load_k = [&](int t0, bool real) {
+    if constexpr (VR) return;
     const int ra = 8 * (j >> 2) + (j & 3);
     const uint16_t* ka = real ? kb + row_at(t0, ra) + 8 * g : kb;
     const uint16_t* kc = real ? kb + row_at(t0, ra + 4) + 8 * g : kb;
@@ -1176,28 +1195,39 @@ __global__ void __launch_bounds__(512) k_fd_full_ds(AttnArgs a) {
       const int s = w + 4 * k;
       const u4v* pa_ = reinterpret_cast<const u4v*>(ka + 32 * s);
       const u4v* pb_ = reinterpret_cast<const u4v*>(kc + 32 * s);
-      // VR: plain loads (the rows' other read is served by the L2)
-      KA[k] = __builtin_bit_cast(h8_t, VR ? *pa_ : __builtin_nontemporal_load(pa_));
-      KB[k] = __builtin_bit_cast(h8_t, VR ? *pb_ : __builtin_nontemporal_load(pb_));
+      KA[k] = __builtin_bit_cast(h8_t, __builtin_nontemporal_load(pa_));
+      KB[k] = __builtin_bit_cast(h8_t, __builtin_nontemporal_load(pb_));
     }
   };
-  // lane l takes chunk position l % CPR of tile row 8w + RPI i + l / CPR, so
-  // loads the chunk that the swizzle puts there
-  auto load_v = [&](int t0, bool real) {
+  // VR: the same elements from the group's V rows of the tile in LDS (lane
+  // (j, g) reads rows 8 (j / 4) + j % 4 and that + 4 at dims 32 s + 8 g ..
+  // + 7, chunk 4 s + g of the row, stored at position (4 s + g) ^ 2 fds_swz)
+  auto lds_k = [&](const uint16_t* vl) {
+    const int ra = 8 * (j >> 2) + (j & 3);
+#pragma unroll
+    for (int k = 0; k < KS; k++) {
+      const int c = 4 * (w + 4 * k) + g;
+      KA[k] = *reinterpret_cast<const h8_t*>(vl + ra * D + (c ^ (2 * fds_swz(ra))) * 8);
+      KB[k] = *reinterpret_cast<const h8_t*>(vl + (ra + 4) * D + (c ^ (2 * fds_swz(ra + 4))) * 8);
+    }
+  };
+  // this wave's 8 V rows of a tile into its group's rows of X: lane l writes
+  // chunk position l % CPR of row 8w + RPI i + l / CPR, so loads the chunk
+  // that the swizzle puts there
+  auto load_v = [&](uint16_t* X, int t0, bool real) {
+    uint16_t* vl = X + grp * 32 * D;
     const int rl = lane / CPR, pc = lane % CPR;
 #pragma unroll
     for (int i = 0; i < NVS; i++) {
-      const int r = 8 * w + RPI * i + rl;
-      const u4v* src = reinterpret_cast<const u4v*>(real ? vb + row_at(t0, r) + (pc ^ (2 * fds_swz(r))) * 8 : vb);
-      VS[i] = VR ? *src : __builtin_nontemporal_load(src);
+      const int r0 = 8 * w + RPI * i, r = r0 + rl;
+      const uint16_t* src = real ? vb + row_at(t0, r) + (pc ^ (2 * fds_swz(r))) * 8 : vb;
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint32_t*>(src),
+                                       reinterpret_cast<uint32_t*>(vl + r0 * D), 16, 0, 0);
     }
   };
-  auto store_v = [&]() {
-#pragma unroll
-    for (int i = 0; i < NVS; i++) *reinterpret_cast<u4v*>(vl + (8 * w + RPI * i) * D + lane * 8) = VS[i];
-  };
   load_k(tile0(grp), grp < ntile);
-  load_v(tile0(grp), grp < ntile);
+  load_v(vA, tile0(grp), grp < ntile);
+  load_v(vB, tile0(grp + G), grp + G < ntile);
   if constexpr (VR) {
     const int i = threadIdx.x;
     if (i < NR) {
@@ -1231,7 +1261,7 @@ __global__ void __launch_bounds__(512) k_fd_full_ds(AttnArgs a) {
       }
     }
   }
-  __syncthreads();                            // finished rows and the VR tables are in
+  lds_barrier();                              // finished rows and the VR tables are in
   if (a.fin_on) {
     const AttnFin& f = a.fin;
     if (f.q_out && split == 0) {
@@ -1253,36 +1283,30 @@ __global__ void __launch_bounds__(512) k_fd_full_ds(AttnArgs a) {
   // ---- queries of this wave's k steps as the MFMA B operand (VR: in the
   // steps whose key is kw * v, q * kw split into fp16 hi and lo)
   h8_t qb[KS], qlo[KS];
-  {
-    const uint16_t* qp = a.fin_on ? q16 + (col_ok ? j : 0) * D + 8 * g
-                                  : a.q + (((long)seq * a.n_rows + row) * a.Hq + (col_ok ? kvh * a.GQ + j : 0)) * D +
-                                        8 * g;
 #pragma unroll
-    for (int k = 0; k < KS; k++) {
-      const int s = w + 4 * k;
-      u4v t = *reinterpret_cast<const u4v*>(qp + 32 * s);
-      if (!col_ok) t = (u4v){0u, 0u, 0u, 0u};
-      if (VR && !rebuilt(s)) {
-        const float4 w0 = *reinterpret_cast<const float4*>(a.kw + 32 * s + 8 * g);
-        const float4 w1 = *reinterpret_cast<const float4*>(a.kw + 32 * s + 8 * g + 4);
-        const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-        const h8_t qh = __builtin_bit_cast(h8_t, t);
-        h8_t hi, lo;
+  for (int k = 0; k < KS; k++) {
+    const int s = w + 4 * k;
+    u4v t = a.fin_on ? *reinterpret_cast<const u4v*>(q16 + (col_ok ? j : 0) * D + 32 * s + 8 * g) : qraw[k];
+    if (!col_ok) t = (u4v){0u, 0u, 0u, 0u};
+    if (VR && !rebuilt(s)) {
+      const float4 w0 = *reinterpret_cast<const float4*>(a.kw + 32 * s + 8 * g);
+      const float4 w1 = *reinterpret_cast<const float4*>(a.kw + 32 * s + 8 * g + 4);
+      const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+      const h8_t qh = __builtin_bit_cast(h8_t, t);
+      h8_t hi, lo;
 #pragma unroll
-        for (int e = 0; e < 8; e++) {
-          const float x = (float)qh[e] * wv[e];
-          hi[e] = (_Float16)x;
-          lo[e] = (_Float16)(x - (float)hi[e]);
-        }
-        qb[k] = hi;
-        qlo[k] = lo;
-      } else {
-        qb[k] = __builtin_bit_cast(h8_t, t);
+      for (int e = 0; e < 8; e++) {
+        const float x = (float)qh[e] * wv[e];
+        hi[e] = (_Float16)x;
+        lo[e] = (_Float16)(x - (float)hi[e]);
       }
+      qb[k] = hi;
+      qlo[k] = lo;
+    } else {
+      qb[k] = __builtin_bit_cast(h8_t, t);
     }
   }
-  if (a.fin_on) __syncthreads();              // every wave has its queries: the scores take their place
-  store_v();                                  // the first tile's V rows (visible after the first barrier)
+  if (a.fin_on) lds_barrier();                // every wave has its queries: the scores take their place
 
   float m_run = -INFINITY, l_part = 0.f;
   f4_t O[DS];
@@ -1291,12 +1315,20 @@ __global__ void __launch_bounds__(512) k_fd_full_ds(AttnArgs a) {
   f4_t* sxw = sx + (grp * 4 + w) * 2 * 64;
   const f4_t* sxg = sx + grp * 4 * 2 * 64;
 
-  for (int rd = 0; rd < nround; rd++) {
+  auto body = [&](auto bc, int rd) {
+    constexpr int b = decltype(bc)::v;
+    uint16_t* X = b ? vB : vA;
+    uint16_t* vl = X + grp * 32 * D;
     const int ti = G * rd + grp;
     const bool act = ti < ntile;              // group-uniform
-    const bool act1 = ti + G < ntile;         // the group's next round
     const int t0 = tile0(ti);
-    load_v(tile0(ti + G), act1);
+    // this round's K and V rows have landed; the next round's V rows (the
+    // youngest loads) may stay in flight
+    wait_vm<NVS>();
+    if constexpr (VR) {
+      lds_barrier();                          // every wave's V rows of the tile are in
+      if (act) lds_k(vl);
+    }
     if (act) {
       if (t0 + 31 >= P0new) {                 // rows formed in this step: keys, then V rows
         const int pa = t0 + 8 * (j >> 2) + (j & 3), pb = pa + 4;
@@ -1357,7 +1389,7 @@ __global__ void __launch_bounds__(512) k_fd_full_ds(AttnArgs a) {
       sxw[lane] = p0;
       sxw[64 + lane] = p1;
     }
-    load_k(tile0(ti + G), act1);              // the registers are free once the scores are formed
+    load_k(tile0(ti + G), ti + G < ntile);    // the registers are free once the scores are formed
     lds_barrier();
     if (act) {
       // full scores: the group's 4 parts added in a fixed order
@@ -1419,14 +1451,18 @@ __global__ void __launch_bounds__(512) k_fd_full_ds(AttnArgs a) {
         O[dd] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Alo, Bv, O[dd], 0, 0, 0);
       }
     }
-    lds_barrier();                            // the V rows and the scores are free again
-    store_v();                                // the next tile's V rows (visible after its first barrier)
+    lds_barrier();                            // these V rows and the scores are free again
+    load_v(X, tile0(ti + 2 * G), ti + 2 * G < ntile);
+  };
+  for (int rd = 0; rd < nround; rd += 2) {
+    body(fds_ic<0>{}, rd);
+    if (rd + 1 < nround) body(fds_ic<1>{}, rd + 1);
   }
 
   // ---- merge the two groups: maxima and sums per head meet in LDS; group 1
   // stores its rescaled O (one float4 of 4 heads per dim step and lane) into
-  // the V rows, group 0 adds it to its own in a fixed order and writes the
-  // records
+  // the even rounds' V rows, group 0 adds it to its own in a fixed order and
+  // writes the records
   float l_tot = l_part + __shfl_xor(l_part, 16, 64);
   l_tot += __shfl_xor(l_tot, 32, 64);
   if (w == 0 && lane < 16) { wm[grp][lane] = m_run; wl[grp][lane] = l_tot; }
@@ -1438,7 +1474,7 @@ __global__ void __launch_bounds__(512) k_fd_full_ds(AttnArgs a) {
     const float M = fmaxf(wm[0][hc], wm[1][hc]);
     fw[i] = wm[grp][hc] == -INFINITY ? 0.f : exp2f(wm[grp][hc] - M);
   }
-  f4_t* ob = reinterpret_cast<f4_t*>(smem);   // [4 waves][DS][64]
+  f4_t* ob = reinterpret_cast<f4_t*>(vA);     // [4 waves][DS][64]
   if (grp == 1) {
 #pragma unroll
     for (int dd = 0; dd < DS; dd++)

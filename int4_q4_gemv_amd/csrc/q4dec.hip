@@ -141,10 +141,6 @@ q4_status set_attrs() {
   e = e != hipSuccess ? e : max_lds(&k_fd_ring_ds<128>, (int)ds_lds_bytes<128>());
   e = e != hipSuccess ? e : max_lds(&k_fd_ring_ds<256>, (int)ds_lds_bytes<256>());
   e = e != hipSuccess ? e : max_lds(&k_fd_ring_ds<512>, (int)ds_lds_bytes<512>());
-  e = e != hipSuccess ? e : max_lds(&k_fd_full_ds<256, false>, (int)fds_lds_bytes<256>());
-  e = e != hipSuccess ? e : max_lds(&k_fd_full_ds<256, true>, (int)fds_lds_bytes<256>());
-  e = e != hipSuccess ? e : max_lds(&k_fd_full_ds<512, false>, (int)fds_lds_bytes<512>());
-  e = e != hipSuccess ? e : max_lds(&k_fd_full_ds<512, true>, (int)fds_lds_bytes<512>());
   e = e != hipSuccess ? e : max_lds(&k_fd_rows4<128>, (int)rows4_lds_bytes<128>());
   e = e != hipSuccess ? e : max_lds(&k_fd_rows4<256>, (int)rows4_lds_bytes<256>());
   e = e != hipSuccess ? e : max_lds(&k_fd_rows4<512>, (int)rows4_lds_bytes<512>());
@@ -226,8 +222,8 @@ bool ring_ds_ok(const AttnArgs& a, int D) {
 template <int D>
 void launch_full_ds_d(const AttnArgs& a, int n_seq, float* out32, uint16_t* out16, hipStream_t st) {
   const dim3 grid(a.S, a.Hkv, n_seq * a.n_rows);
-  if (a.vrow) hipLaunchKernelGGL((k_fd_full_ds<D, true>), grid, dim3(512), fds_lds_bytes<D>(), st, a);
-  else hipLaunchKernelGGL((k_fd_full_ds<D, false>), grid, dim3(512), fds_lds_bytes<D>(), st, a);
+  if (a.vrow) hipLaunchKernelGGL((k_fd_full_ds<D, true>), grid, dim3(512), 0, st, a);
+  else hipLaunchKernelGGL((k_fd_full_ds<D, false>), grid, dim3(512), 0, st, a);
   launch_combine<D>(a, n_seq, out32, out16, st);
 }
 
