@@ -17,16 +17,32 @@ Q4_DEV uint16_t f2h(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f);
 Q4_DEV h2_t as_h2(uint32_t u) { return __builtin_bit_cast(h2_t, u); }
 Q4_DEV uint32_t as_u32(h2_t h) { return __builtin_bit_cast(uint32_t, h); }
 
-// Sum over the 64 lanes of a wave (every lane gets the result).
+// Reductions over the 64 lanes of a wave (every lane gets the result).  Each
+// 16-lane row folds its lanes with four DPP shifts on the VALU (row_shr 1,
+// 2, 4, 8: the row's total lands in its last lane; a lane whose source lies
+// outside the row takes the identity), then the four row results are read
+// as scalars and combined in order.  Butterfly shuffles through
+// ds_bpermute cost an LDS round trip per step.  The wave must be fully
+// active: every caller runs in wave-uniform control flow.
+template <int CTRL>
+Q4_DEV float dpp_row_shr(float v, float identity) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, identity),
+                                                               __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+Q4_DEV float lane_f(float v, int l) { return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l)); }
 Q4_DEV float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+  v += dpp_row_shr<0x111>(v, 0.f);
+  v += dpp_row_shr<0x112>(v, 0.f);
+  v += dpp_row_shr<0x114>(v, 0.f);
+  v += dpp_row_shr<0x118>(v, 0.f);
+  return ((lane_f(v, 15) + lane_f(v, 31)) + lane_f(v, 47)) + lane_f(v, 63);
 }
 Q4_DEV float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
+  v = fmaxf(v, dpp_row_shr<0x111>(v, -INFINITY));
+  v = fmaxf(v, dpp_row_shr<0x112>(v, -INFINITY));
+  v = fmaxf(v, dpp_row_shr<0x114>(v, -INFINITY));
+  v = fmaxf(v, dpp_row_shr<0x118>(v, -INFINITY));
+  return fmaxf(fmaxf(lane_f(v, 15), lane_f(v, 31)), fmaxf(lane_f(v, 47), lane_f(v, 63)));
 }
 
 // Block-wide sum for blockDim.x == NT (multiple of 64); `red` holds NT/64 floats.
