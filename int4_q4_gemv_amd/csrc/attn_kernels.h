@@ -574,8 +574,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D <= 2
     float mt = sv[0];
 #pragma unroll
     for (int i = 1; i < 8; i++) mt = fmaxf(mt, sv[i]);
-    mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+    mt = rows_max(mt);
     const float m_new = fmaxf(m_run, mt);
     // a column none of whose positions so far is admitted keeps m = -inf
     // and weights 0 (its rows' windows may start past this tile)
@@ -647,8 +646,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D <= 2
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
   }
   // column totals of l over the 4 lane groups
-  float l_tot = l_part + __shfl_xor(l_part, 16, 64);
-  l_tot += __shfl_xor(l_tot, 32, 64);
+  float l_tot = rows_sum(l_part);
 
   // record of column col, or NULL for columns without a row and head
   auto rec_of = [&](int col) -> float* {
@@ -979,8 +977,7 @@ __global__ void __launch_bounds__(256) k_fd_ring_ds(AttnArgs a) {
     float mt = sv[0];
 #pragma unroll
     for (int i = 1; i < 8; i++) mt = fmaxf(mt, sv[i]);
-    mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+    mt = rows_max(mt);
     m = mt;                                   // finite: position st is admitted
     float p[8], ps = 0.f;
 #pragma unroll
@@ -988,8 +985,7 @@ __global__ void __launch_bounds__(256) k_fd_ring_ds(AttnArgs a) {
       p[i] = exp2f(sv[i] - m);
       ps += p[i];
     }
-    l_tot = ps + __shfl_xor(ps, 16, 64);
-    l_tot += __shfl_xor(l_tot, 32, 64);
+    l_tot = rows_sum(ps);
     h8_t Ahi, Alo;
 #pragma unroll
     for (int i = 0; i < 8; i++) {
@@ -1409,8 +1405,7 @@ __global__ void __launch_bounds__(512) k_fd_full_ds(AttnArgs a) {
       float mt = sv[0];
 #pragma unroll
       for (int i = 1; i < 8; i++) mt = fmaxf(mt, sv[i]);
-      mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+      mt = rows_max(mt);
       const float m_new = fmaxf(m_run, mt);   // finite: position t0 is admitted
       const float alpha = exp2f(m_run - m_new);
       m_run = m_new;
@@ -1463,8 +1458,7 @@ __global__ void __launch_bounds__(512) k_fd_full_ds(AttnArgs a) {
   // stores its rescaled O (one float4 of 4 heads per dim step and lane) into
   // the even rounds' V rows, group 0 adds it to its own in a fixed order and
   // writes the records
-  float l_tot = l_part + __shfl_xor(l_part, 16, 64);
-  l_tot += __shfl_xor(l_tot, 32, 64);
+  float l_tot = rows_sum(l_part);
   if (w == 0 && lane < 16) { wm[grp][lane] = m_run; wl[grp][lane] = l_tot; }
   __syncthreads();
   float fw[4];

@@ -369,8 +369,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) k
     float mt = sv[0];
 #pragma unroll
     for (int i = 1; i < 8; i++) mt = fmaxf(mt, sv[i]);
-    mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+    mt = rows_max(mt);
     const float m_new = fmaxf(m_run, mt);
     const bool none = m_new == -INFINITY;          // nothing of this row admitted yet
     const float alpha = none ? 1.f : exp2f(m_run - m_new);
@@ -412,8 +411,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) k
     }
   }
   if (!live) return;
-  float l_tot = l_part + __shfl_xor(l_part, 16, 64);
-  l_tot += __shfl_xor(l_tot, 32, 64);
+  float l_tot = rows_sum(l_part);
 #pragma unroll
   for (int i = 0; i < 4; i++) {
     const int col = 4 * g + i;

@@ -37,6 +37,30 @@ Q4_DEV float wave_sum(float v) {
   v += dpp_row_shr<0x118>(v, 0.f);
   return ((lane_f(v, 15) + lane_f(v, 31)) + lane_f(v, 47)) + lane_f(v, 63);
 }
+// Sum / maximum over the four 16-lane rows of a wave, per column (lane mod
+// 16), returned in every lane: v_permlane16_swap with both operands v gives
+// rows (0, 0, 2, 2) and (1, 1, 3, 3), so their sum is each row pair's sum in
+// both rows; v_permlane32_swap then does the same for the two halves.  The
+// same values a butterfly over lanes l ^ 16 and l ^ 32 gives, on the VALU
+// instead of through LDS.  The wave must be fully active.  The two results
+// are copied out as unsigned before the bit cast: a bit cast straight from
+// the returned vector's second element compiled to a second read of the
+// first (a wrong sum, caught by the parity tests).
+template <bool MAX>
+Q4_DEV float rows_fold(float v) {
+  const unsigned u = __builtin_bit_cast(unsigned, v);
+  const auto p = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const unsigned p0 = p[0], p1 = p[1];
+  const float a = __builtin_bit_cast(float, p0), b = __builtin_bit_cast(float, p1);
+  v = MAX ? fmaxf(a, b) : a + b;
+  const unsigned w = __builtin_bit_cast(unsigned, v);
+  const auto q = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+  const unsigned q0 = q[0], q1 = q[1];
+  const float c = __builtin_bit_cast(float, q0), d = __builtin_bit_cast(float, q1);
+  return MAX ? fmaxf(c, d) : c + d;
+}
+Q4_DEV float rows_sum(float v) { return rows_fold<false>(v); }
+Q4_DEV float rows_max(float v) { return rows_fold<true>(v); }
 Q4_DEV float wave_max(float v) {
   v = fmaxf(v, dpp_row_shr<0x111>(v, -INFINITY));
   v = fmaxf(v, dpp_row_shr<0x112>(v, -INFINITY));

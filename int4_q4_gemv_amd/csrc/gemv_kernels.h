@@ -271,8 +271,7 @@ __global__ void __launch_bounds__((B == 1 || FMT == 1) ? 1024 : 512) k_q4_gemv(G
       acc = fmaf(d, bs, acc);
     }
     // the 4 lane groups hold the same 16 rows over different columns
-    acc += __shfl_xor(acc, 16, 64);
-    acc += __shfl_xor(acc, 32, 64);
+    acc = rows_sum(acc);
     if (lane < 16) red[wave * 16 + lane] = acc;
   } else {
     // MFMA block m = lane / 4 holds rows 4m..4m+3 (mod 16) of lane group m / 4
@@ -316,8 +315,7 @@ __global__ void __launch_bounds__((B == 1 || FMT == 1) ? 1024 : 512) k_q4_gemv(G
     }
 #pragma unroll
     for (int r = 0; r < 4; r++) {
-      acc[r] += __shfl_xor(acc[r], 16, 64);
-      acc[r] += __shfl_xor(acc[r], 32, 64);
+      acc[r] = rows_sum(acc[r]);
     }
     if (lane < 16) {
       const int bb = lane & 3;
