@@ -11,7 +11,7 @@ at three shapes, context-131072 and width-4 verify figures, the attention
 kernels alone, and the CPU oracle timed on the host cores on a bounded
 sample.
 
-  python bench.py [--gpus 1] [--steps K] [--warmup W] [--mode full|gemv|step|traffic|prefill|attn_traffic]
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--mode full|gemv|step|verify|traffic|prefill|attn_traffic]
 """
 import argparse
 import json
@@ -30,7 +30,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--mode", default="full", choices=["full", "gemv", "step", "traffic", "prefill", "attn_traffic"])
+    ap.add_argument("--mode", default="full", choices=["full", "gemv", "step", "verify", "traffic", "prefill", "attn_traffic"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     return ap.parse_args()
 
@@ -511,6 +511,11 @@ def main():
             if args.mode == "gemv":
                 print(json.dumps(out))
                 return
+        if args.mode == "verify":
+            blocks = [[int(t) for t in synth.tokens(cfg, 4, 50 + i)] for i in range(8)]
+            sv = time_steps(torch, model, blocks, 32764, args.steps, args.warmup)
+            print(json.dumps({"mode": "verify", "verify4_ctx32768_ms_per_block": round(sv * 1e3 / args.steps, 4)}))
+            return
         pos = 32767
         secs = time_steps(torch, model, toks, pos, args.steps, args.warmup)
         ms = secs * 1e3 / args.steps
