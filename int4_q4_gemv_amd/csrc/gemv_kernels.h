@@ -130,7 +130,8 @@ Q4_DEV h2_t q8_pair(uint32_t w, uint32_t sel) { return as_h2(__builtin_amdgcn_pe
 // ------------------------------------------------------------ the kernel ----
 // Grid: (tiles, S).  Block: 64 * W threads (EPI_GATEUP: 64 * 2W, the first W
 // waves on the gate tile, the rest on the up tile; S = 1).  Dynamic LDS:
-// B * NQs * UC halves of activation.
+// B rows of NQs * UC halves of activation (plus 8 halves of padding per row
+// when B > 1).
 // FMT 0: q4 weights, a unit is a quad (16 rows x 4 blocks, UC = 128 columns),
 // lane l holds row l & 15 and block l >> 4.  FMT 1: int8 weights
 // (q8_kernels.h), a unit is a pair (16 rows x 2 blocks, UC = 64 columns), lane
@@ -143,6 +144,9 @@ __global__ void __launch_bounds__((B == 1 || FMT == 1) ? 1024 : 512) k_q4_gemv(G
   constexpr int UC = FMT == 0 ? 128 : 64;       // columns per unit
   extern __shared__ __align__(16) unsigned char smem_g[];
   const int ldxs = a.NQs * UC;                  // staged activation row (halves)
+  // row pitch: batch rows start 16 B apart modulo the 256-byte bank period,
+  // so the 4 rows one MFMA read spans fall in different LDS banks
+  const int ldxp = ldxs + (B > 1 ? 8 : 0);
   uint16_t* xs = reinterpret_cast<uint16_t*>(smem_g);
   __shared__ float red[16 * B * 16];
 
@@ -221,7 +225,7 @@ __global__ void __launch_bounds__((B == 1 || FMT == 1) ? 1024 : 512) k_q4_gemv(G
 #pragma unroll
     for (int bb = 0; bb < B; bb++) {
       const u4v z = {0u, 0u, 0u, 0u};
-      if (in) *reinterpret_cast<u4v*>(&xs[bb * ldxs + threadIdx.x * 8]) = (bb < nrow && kin) ? xr[bb] : z;
+      if (in) *reinterpret_cast<u4v*>(&xs[bb * ldxp + threadIdx.x * 8]) = (bb < nrow && kin) ? xr[bb] : z;
     }
 #pragma unroll
     for (int bb = 0; bb < B; bb++)
@@ -229,7 +233,7 @@ __global__ void __launch_bounds__((B == 1 || FMT == 1) ? 1024 : 512) k_q4_gemv(G
         const int k = qs0 * UC + i * 8;
         u4v v = {0u, 0u, 0u, 0u};
         if (bb < nrow && k < a.K) v = *reinterpret_cast<const u4v*>(a.x + (long)bb * a.ldx + k);
-        *reinterpret_cast<u4v*>(&xs[bb * ldxs + i * 8]) = v;
+        *reinterpret_cast<u4v*>(&xs[bb * ldxp + i * 8]) = v;
       }
   }
   __syncthreads();
@@ -276,7 +280,7 @@ __global__ void __launch_bounds__((B == 1 || FMT == 1) ? 1024 : 512) k_q4_gemv(G
   } else {
     // MFMA block m = lane / 4 holds rows 4m..4m+3 (mod 16) of lane group m / 4
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
-    const uint16_t* xl = xs + (lane & 3) * ldxs;
+    const uint16_t* xl = xs + (lane & 3) * ldxp;
 #pragma unroll
     for (int i = 0; i < CQ; i++) {
       const int ii = i < nq ? i : 0;

@@ -71,7 +71,7 @@ GemvPlan gemv_plan(int N, int K, int max_waves, int split_cols = 0, int fmt = 0)
   return p;
 }
 
-size_t gemv_lds(int B, const GemvPlan& p) { return (size_t)B * p.NQs * unit_cols(p.fmt) * 2; }
+size_t gemv_lds(int B, const GemvPlan& p) { return (size_t)B * (p.NQs * unit_cols(p.fmt) + (B > 1 ? 8 : 0)) * 2; }
 
 // grid: (tiles, splits); waves: per workgroup (both halves for EPI_GATEUP)
 template <int B, int EPI, int FMT>
