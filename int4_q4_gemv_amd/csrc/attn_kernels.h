@@ -756,55 +756,109 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D <= 2
 // it, and that is what keeps the memory pipeline full when a CU holds one
 // workgroup.  Splits, masking, the finishing prologue, the records and the
 // combine are those of k_fd_partial (one tile, no merge of waves).
+//
+// MR (a.rpw rows per workgroup, with the finishing prologue): as in
+// k_fd_partial, the MFMA columns are (row, query head) pairs masked to their
+// own row's window.  The splits divide the first row's window (S * 32 >=
+// W); a later row's own positions past it (formed in this step, at most
+// rpw - 1) are added by the combine (k_fd_combine, TAIL) from the cache.  The
+// workgroup forms the queries of all its columns and the K/V rows of the
+// step in its range; the split holding the first row's position finishes and
+// stores all the workgroup's rows: a block of rows then needs no launch of
+// its own to finish them.
+// A workgroup barrier that orders LDS only: this wave's LDS operations
+// have completed (lgkmcnt 0) before it arrives.  __syncthreads' release fence
+// would also wait for every global load in flight, the prefetches included.
+Q4_DEV void lds_barrier() {
+  __asm__ __volatile__("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);         // vmcnt 63, expcnt 7, lgkmcnt 0
+  __builtin_amdgcn_s_barrier();
+  __asm__ __volatile__("" ::: "memory");
+}
+
+// The step's first position, read in two parts: pos_issue loads the word
+// that holds it with the step parameters on the device (else any valid word:
+// the records), by a vector load through an address the compiler cannot prove
+// uniform, and pos_take picks the value where it is first used.  A scalar
+// load would be waited for together with the kernel's argument loads, before
+// the loads that do not need the position are issued; a vector load is waited
+// for only where the position is used, by a count that leaves the loads
+// issued after it in flight.
+Q4_DEV int pos_issue(const AttnArgs& a) {
+  int z = 0;
+  __asm__ __volatile__("" : "+v"(z));   // an opaque zero
+  const int* w = a.sp ? &a.sp->pos0 : reinterpret_cast<const int*>(a.part);
+  return ((const __attribute__((address_space(1))) int*)w)[z];
+}
+Q4_DEV int pos_take(const AttnArgs& a, int loaded, int seq) {
+  return __builtin_amdgcn_readfirstlane(a.sp ? loaded : a.pos0[seq]);
+}
+
 template <int D>
 constexpr size_t ds_lds_bytes() {
   return (size_t)32 * fd_vpitch<D>() * 2 + (size_t)2 * 4 * D * 2 + (size_t)16 * D * 2 + (size_t)4 * 2 * 64 * 16;
 }
 
-template <int D>
+template <int D, bool MR = false, bool FIN = false>
 __global__ void __launch_bounds__(256) k_fd_ring_ds(AttnArgs a) {
   static_assert(D >= 128 && D <= 512, "a wave takes whole QK k steps");
   constexpr int VROW = fd_vpitch<D>();
   constexpr int KS = D / 128;                 // QK k steps of a wave
   constexpr int DS = D / 64;                  // PV dim steps of a wave
   constexpr int DW = D / 4;                   // dims of a wave
-  extern __shared__ __align__(16) unsigned char smem[];
-  uint16_t* vl = reinterpret_cast<uint16_t*>(smem);   // [32][VROW] the tile's V rows
-  uint16_t* newK = vl + 32 * VROW;                     // [4][D] rows of this step
-  uint16_t* newV = newK + 4 * D;
-  uint16_t* q16 = newV + 4 * D;                        // [16][D] finished queries
-  f4_t* sx = reinterpret_cast<f4_t*>(q16 + 16 * D);    // [4 waves][2][64] partial scores
+  // LDS objects of their own: the compiler then knows that the accesses to
+  // the step's rows, the queries and the scores do not touch the V rows still
+  // arriving, and waits for those only where they are read
+  __shared__ __align__(16) uint16_t vl[32 * VROW];     // the tile's V rows
+  __shared__ __align__(16) uint16_t nkv[2 * 4 * D];    // rows of this step: K [4][D], V [4][D]
+  __shared__ __align__(16) uint16_t q16[16 * D];       // finished queries
+  __shared__ f4_t sx[4 * 2 * 64];                      // [4 waves][2][64] partial scores
+  uint16_t* newK = nkv;
+  uint16_t* newV = nkv + 4 * D;
   static_assert(ds_lds_bytes<D>() <= 160 * 1024, "LDS of one workgroup");
 
   const int split = a.kvh_major ? blockIdx.y : blockIdx.x, kvh = a.kvh_major ? blockIdx.x : blockIdx.y;
-  const int seq = blockIdx.z / a.n_rows, row = blockIdx.z - seq * a.n_rows;
+  // rows of this workgroup: row .. rlast (one unless MR); its columns
+  const int rpw = MR && a.rpw > 1 ? a.rpw : 1;
+  int seq, row;
+  if constexpr (MR) {
+    const int nrg = (a.n_rows + rpw - 1) / rpw;
+    seq = blockIdx.z / nrg;
+    row = (blockIdx.z - seq * nrg) * rpw;
+  } else {
+    seq = blockIdx.z / a.n_rows;
+    row = blockIdx.z - seq * a.n_rows;
+  }
+  if (row >= a.n_rows) return;
+  const int rlast = MR ? min(a.n_rows, row + rpw) - 1 : row;
+  const int ncols = a.GQ * (rlast - row + 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
 
-  // ---- the step's first position (a global load, issued first)
-  int base;
-  if (a.sp) base = *(const __attribute__((address_space(1))) int*)(&a.sp->pos0);
-  else base = a.pos0[seq];
+  // ---- the step's first position, issued first
+  const int pos_w = pos_issue(a);
 
-  // ---- inputs of the finishing prologue: jobs dealt round-robin to the
-  // waves (this workgroup's query heads, then k and v of rows 0 .. row)
+  // ---- inputs of the finishing prologue (FIN): jobs dealt round-robin to
+  // the waves (this workgroup's columns, then k and v of rows 0 .. rlast).
+  // Every wave loads MAXJ jobs' inputs, those past the last job repeating
+  // job 0's, so the count of loads is the same on every path.
   constexpr int FE = D / 64, FEH = fin_h<D>();
   constexpr int MAXJ = (16 + 2 * 4 + 3) / 4;
-  const int njobs = a.fin_on ? a.GQ + 2 * (row + 1) : 0;
+  const int njobs = FIN ? ncols + 2 * (rlast + 1) : 0;
   float raw[MAXJ][FE], wq[FE], wk[FE];
   float2 fcs[MAXJ][FEH];
-  if (a.fin_on) {
+  if constexpr (FIN) {
     const AttnFin& f = a.fin;
     fin_load<D>(wq, f.q_norm);
     fin_load<D>(wk, f.k_norm);
 #pragma unroll
     for (int k = 0; k < MAXJ; k++) {
-      const int jb = wave + 4 * k;
-      if (jb >= njobs) break;
-      const int r = jb < a.GQ ? row : (jb - a.GQ) >> 1;
+      const int jb = wave + 4 * k < njobs ? wave + 4 * k : 0;
+      const int jq = MR ? jb / a.GQ : 0;      // a column's row offset
+      const int r = jb < ncols ? row + jq : (jb - ncols) >> 1;
       const float* rr = f.qkv + (long)r * f.ldq;
       const float* src;
-      if (jb < a.GQ) src = rr + (long)(kvh * a.GQ + jb) * D;
-      else if (((jb - a.GQ) & 1) == 0) src = rr + (long)(a.Hq + kvh) * D;
+      if (jb < ncols) src = rr + (long)(kvh * a.GQ + jb - jq * a.GQ) * D;
+      else if (((jb - ncols) & 1) == 0) src = rr + (long)(a.Hq + kvh) * D;
       else src = rr + (long)(a.Hq + a.Hkv + kvh) * D;
       fin_load<D>(raw[k], src);
       const float2* cr = f.rope_cs + (long)r * f.cs_ld + lane * FEH;
@@ -822,34 +876,50 @@ __global__ void __launch_bounds__(256) k_fd_ring_ds(AttnArgs a) {
   }
   __builtin_amdgcn_sched_barrier(0);
 
-  base = __builtin_amdgcn_readfirstlane(base);
+  const int base = pos_take(a, pos_w, seq);
   const int P = base + row;
   const int lo = max(0, P - a.W + 1);
-  const int L = P - lo + 1;
-  const int chunk = (L + a.S - 1) / a.S;      // <= 32: the host launches this kernel only then
+  const int Pl = base + rlast;                // MR: the union of the rows' ranges
+  // splits of chunk positions over the first row's window (chunk <= 32: the
+  // host launches this kernel only then).  MR: the later rows' positions past
+  // it (P + 1 .. Pl, formed in this step) are left to the combine; the split
+  // holding P finishes and stores those rows.
+  const int chunk = (P - lo + a.S) / a.S;
   const int st = lo + split * chunk;
   const int en = min(st + chunk, P + 1);
   const bool has = st < en;                   // workgroup-uniform
-  const int P0new = a.fin_on ? base : 0x7FFFFFFF;
+  const bool holds_p = P >= st && P < en;
+  const int P0new = FIN ? base : 0x7FFFFFFF;
 
   const int j = lane & 15, g = lane >> 4;
-  const bool col_ok = j < a.GQ;
+  // column j: row row + jr, query head jh; it admits positions loj .. Pj
+  const int jr = MR ? j / a.GQ : 0, jh = j - jr * a.GQ;
+  const bool col_ok = j < ncols;
+  const int Pj = P + jr, loj = Pj - a.W + 1;
   uint16_t* vb = a.v + seq * a.seq_stride + (long)kvh * a.R * D;
   uint16_t* kb = a.k + seq * a.seq_stride + (long)kvh * a.R * D;
-  // tile row r lives at slot (st + r) mod R (R >= 32: one wrap at most);
-  // rows past nv are masked or formed in this step and read slot 0
-  const int s0 = __builtin_amdgcn_readfirstlane(st % a.R);
-  const int nv = __builtin_amdgcn_readfirstlane(min(en, P0new) - st);
-  auto row_at = [&](int r) -> long {
-    const int sl = r >= a.R - s0 ? s0 + r - a.R : s0 + r;
-    return r < nv ? (long)sl * D : 0l;
-  };
 
-  // ---- this wave's K elements and V rows, issued before anything waits.
-  // Lane (column j, group g) holds positions 8g .. 8g+7 of the tile (MFMA
-  // row r of half h <-> tile position 8 (r / 4) + 4h + r % 4).
+  // ---- a tile's K elements and V rows.  Row r of the tile at t0 lives at
+  // slot (t0 + r) mod R (R >= 32: one wrap at most); rows past nv are masked
+  // or formed in this step and read slot 0.  Lane (column j, group g) holds
+  // positions 8g .. 8g+7 of the tile (MFMA row r of half h <-> tile position
+  // 8 (r / 4) + 4h + r % 4).  The V rows travel through registers (RPI rows
+  // per instruction, lane l holding 16-byte chunk l mod CPR of its row, the
+  // one the swizzle puts there) and are written to LDS once the scores are
+  // formed: with loads into registers only, and the same loads on every path
+  // (an empty split loads row 0), the compiler's waits are counts, so the
+  // prologue's finishing and the scores wait for their own inputs, not for
+  // the whole tile.
+  constexpr int CPR = D / 8, RPI = 64 / CPR;   // 16-byte chunks per row, rows per instruction
   h8_t KA[KS], KB[KS];
-  if (has) {
+  u4v vr[8 / RPI];
+  auto load_tile = [&](int t0) {
+    const int s0 = __builtin_amdgcn_readfirstlane(t0 % a.R);
+    const int nv = __builtin_amdgcn_readfirstlane(min(en, P0new) - t0);
+    auto row_at = [&](int r) -> long {
+      const int sl = r >= a.R - s0 ? s0 + r - a.R : s0 + r;
+      return r < nv ? (long)sl * D : 0l;
+    };
     const int ra = 8 * (j >> 2) + (j & 3);
     const uint16_t* ka = kb + row_at(ra) + DW * wave + 8 * g;
     const uint16_t* kc = kb + row_at(ra + 4) + DW * wave + 8 * g;
@@ -858,50 +928,42 @@ __global__ void __launch_bounds__(256) k_fd_ring_ds(AttnArgs a) {
       KA[s] = __builtin_bit_cast(h8_t, __builtin_nontemporal_load(reinterpret_cast<const u4v*>(ka + 32 * s)));
       KB[s] = __builtin_bit_cast(h8_t, __builtin_nontemporal_load(reinterpret_cast<const u4v*>(kc + 32 * s)));
     }
-    constexpr int CPR = D / 8, RPI = 64 / CPR;   // 16-byte chunks per row, rows per instruction
     const int rl = lane / CPR, pc = lane % CPR;
 #pragma unroll
     for (int i = 0; i < 8 / RPI; i++) {
-      const int r0 = 8 * wave + RPI * i, r = r0 + rl;
+      const int r = 8 * wave + RPI * i + rl;
       const int c = pc ^ (2 * vswz<D>(r));
-      __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint32_t*>(vb + row_at(r) + c * 8),
-                                       reinterpret_cast<uint32_t*>(vl + r0 * VROW), 16, 0, 0);
+      vr[i] = __builtin_nontemporal_load(reinterpret_cast<const u4v*>(vb + row_at(r) + c * 8));
     }
-  }
+  };
+  load_tile(st);                              // issued before anything waits
 
   // ---- queries (as the MFMA B operand, this wave's k steps)
   h8_t qb[KS];
-  if (a.fin_on) {
+  if constexpr (FIN) {
     const AttnFin& f = a.fin;
-    const int r0 = max(0, st - base), r1 = min(row, en - 1 - base);
+    const int r0 = max(0, st - base), r1 = holds_p ? rlast : min(rlast, en - 1 - base);
 #pragma unroll
     for (int k = 0; k < MAXJ; k++) {
       const int jb = wave + 4 * k;
       if (jb >= njobs) break;
-      if (jb < a.GQ) {
+      if (jb < ncols) {
         finish_vals<D>(raw[k], wq, true, true, fcs[k], f.rot_pairs, f.eps, q16 + jb * D);
         continue;
       }
-      const int r = (jb - a.GQ) >> 1;
+      const int r = (jb - ncols) >> 1;
       if (r < r0 || r > r1) continue;
-      if (((jb - a.GQ) & 1) == 0) finish_vals<D>(raw[k], wk, true, true, fcs[k], f.rot_pairs, f.eps, newK + r * D);
+      if (((jb - ncols) & 1) == 0) finish_vals<D>(raw[k], wk, true, true, fcs[k], f.rot_pairs, f.eps, newK + r * D);
       else if (f.v_norm) finish_vals<D>(raw[k], wk, false, false, fcs[k], f.rot_pairs, f.eps, newV + r * D);
       else fin_store<D>(raw[k], newV + r * D);
     }
-    __syncthreads();
+    lds_barrier();
     if (f.q_out && split == 0) {
       constexpr int CH = D / 8;
-      for (int i = threadIdx.x; i < a.GQ * CH; i += 256) {
-        const int jq = i / CH, c = i - jq * CH;
-        *reinterpret_cast<u4v*>(f.q_out + ((long)row * a.Hq + kvh * a.GQ + jq) * D + c * 8) =
+      for (int i = threadIdx.x; i < ncols * CH; i += 256) {
+        const int jq = i / CH, c = i - jq * CH, qr = jq / a.GQ;
+        *reinterpret_cast<u4v*>(f.q_out + ((long)(row + qr) * a.Hq + kvh * a.GQ + jq - qr * a.GQ) * D + c * 8) =
             *reinterpret_cast<const u4v*>(q16 + jq * D + c * 8);
-      }
-    }
-    if (P >= st && P < en) {
-      const long so = (long)(P % a.R) * D;
-      for (int d = threadIdx.x; d < D; d += 256) {
-        kb[so + d] = newK[row * D + d];
-        vb[so + d] = newV[row * D + d];
       }
     }
 #pragma unroll
@@ -911,8 +973,8 @@ __global__ void __launch_bounds__(256) k_fd_ring_ds(AttnArgs a) {
       qb[s] = __builtin_bit_cast(h8_t, t);
     }
   } else {
-    const uint16_t* qp = a.q + (((long)seq * a.n_rows + row) * a.Hq + (col_ok ? kvh * a.GQ + j : 0)) * D +
-                         DW * wave + 8 * g;
+    const uint16_t* qp = a.q + (((long)seq * a.n_rows + row + (col_ok ? jr : 0)) * a.Hq +
+                                (col_ok ? kvh * a.GQ + jh : 0)) * D + DW * wave + 8 * g;
 #pragma unroll
     for (int s = 0; s < KS; s++) {
       u4v t = *reinterpret_cast<const u4v*>(qp + 32 * s);
@@ -921,6 +983,7 @@ __global__ void __launch_bounds__(256) k_fd_ring_ds(AttnArgs a) {
     }
   }
 
+  // ---- the split's tile: scores, softmax, O += P V
   f4_t O[DS];
 #pragma unroll
   for (int d = 0; d < DS; d++) O[d] = (f4_t){0.f, 0.f, 0.f, 0.f};
@@ -944,9 +1007,11 @@ __global__ void __launch_bounds__(256) k_fd_ring_ds(AttnArgs a) {
     }
     sx[(2 * wave) * 64 + lane] = p0;
     sx[(2 * wave + 1) * 64 + lane] = p1;
-    // this wave's V rows have landed; rows formed in this step overwrite theirs
-    __builtin_amdgcn_s_waitcnt(0);
-    __asm__ __volatile__("" ::: "memory");
+    // this wave's V rows to LDS (lane l: bytes 16 l .. of RPI rows from row
+    // 8 wave + RPI i); rows formed in this step overwrite theirs
+#pragma unroll
+    for (int i = 0; i < 8 / RPI; i++)
+      *reinterpret_cast<u4v*>(vl + (8 * wave + RPI * i) * VROW + lane * 8) = vr[i];
     if (st + 31 >= P0new) {
 #pragma unroll
       for (int r = 8 * wave; r < 8 * wave + 8; r++) {
@@ -957,7 +1022,7 @@ __global__ void __launch_bounds__(256) k_fd_ring_ds(AttnArgs a) {
       }
     }
   }
-  __syncthreads();
+  lds_barrier();
   if (has) {
     // full scores: the 4 waves' parts added in a fixed order
     f4_t c0 = sx[0 * 64 + lane], c1 = sx[1 * 64 + lane];
@@ -971,18 +1036,22 @@ __global__ void __launch_bounds__(256) k_fd_ring_ds(AttnArgs a) {
     float sv[8];
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-      sv[i] = (st + 8 * g + i < en) ? c0[i] * a.scale_log2 : -INFINITY;
-      sv[4 + i] = (st + 8 * g + 4 + i < en) ? c1[i] * a.scale_log2 : -INFINITY;
+      const int pa = st + 8 * g + i, pb = pa + 4;
+      sv[i] = (pa < en && (!MR || pa >= loj)) ? c0[i] * a.scale_log2 : -INFINITY;
+      sv[4 + i] = (pb < en && (!MR || pb >= loj)) ? c1[i] * a.scale_log2 : -INFINITY;
     }
     float mt = sv[0];
 #pragma unroll
     for (int i = 1; i < 8; i++) mt = fmaxf(mt, sv[i]);
     mt = rows_max(mt);
-    m = mt;                                   // finite: position st is admitted
+    m = mt;                                   // one row: finite, position st is admitted
+    // MR: a column that admits none of the tile's positions (its row's
+    // window starts past it) keeps m = -inf, l = 0 and O = 0
+    const bool none = MR && m == -INFINITY;
     float p[8], ps = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; i++) {
-      p[i] = exp2f(sv[i] - m);
+      p[i] = none ? 0.f : exp2f(sv[i] - m);
       ps += p[i];
     }
     l_tot = rows_sum(ps);
@@ -1008,20 +1077,44 @@ __global__ void __launch_bounds__(256) k_fd_ring_ds(AttnArgs a) {
       O[dd] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Alo, Bv, O[dd], 0, 0, 0);
     }
   }
-  // ---- records: wave w stores its dims of every head; wave 0 also m and l
-  // (an empty split stores O = 0, m = -inf, l = 0)
+  // ---- records: wave w stores its dims of every column; wave 0 also m and
+  // l (an empty split stores O = 0, m = -inf, l = 0).  Column c's record lies
+  // c / GQ rows and c mod GQ heads past the workgroup's first: lane c holds
+  // that offset (32 bits, from the column split above), the other lanes
+  // fetch it, and one scalar base serves every store.  With one wave per
+  // SIMD the wave issues every instruction itself, and 64-bit index
+  // arithmetic per record would take longer than the stores.
+  // All four offsets are formed before the first store, so no register of
+  // a store in flight is reused (which would wait for the store).
+  float* rbase = a.part + attn_rec(a, seq, row, kvh, split, 0, D);
+  const unsigned my_off = (unsigned)(jr * (a.Hkv * a.S * a.GQ * (D + 4)) + jh * (D + 4));
+  unsigned offs[4];
+#pragma unroll
+  for (int i = 0; i < 4; i++) offs[i] = (unsigned)__shfl((int)my_off, 4 * g + i, 64) + 16 * DS * wave + j;
 #pragma unroll
   for (int i = 0; i < 4; i++) {
-    if (4 * g + i < a.GQ) {
-      float* rec = a.part + attn_rec(a, seq, row, kvh, split, 4 * g + i, D);
+    if (4 * g + i < ncols) {
 #pragma unroll
-      for (int dd = 0; dd < DS; dd++) rec[16 * (DS * wave + dd) + j] = O[dd][i];
+      for (int dd = 0; dd < DS; dd++) rbase[offs[i] + 16 * dd] = O[dd][i];
     }
   }
-  if (wave == 0 && lane < a.GQ) {
-    float* rec = a.part + attn_rec(a, seq, row, kvh, split, lane, D);
-    rec[D] = m;
-    rec[D + 1] = l_tot;
+  if (wave == 0 && lane < ncols) {
+    rbase[my_off + D] = m;
+    rbase[my_off + D + 1] = l_tot;
+  }
+  // the split holding P stores the rows of this workgroup (P .. Pl), last:
+  // nothing waits for these stores
+  if constexpr (FIN) {
+    for (int rr = row; rr <= rlast; rr++) {
+      const int Pr = base + rr;
+      if (holds_p) {
+        const long so = (long)(Pr % a.R) * D;
+        for (int d = threadIdx.x; d < D; d += 256) {
+          kb[so + d] = newK[rr * D + d];
+          vb[so + d] = newV[rr * D + d];
+        }
+      }
+    }
   }
 }
 
@@ -1057,16 +1150,6 @@ __global__ void __launch_bounds__(256) k_fd_ring_ds(AttnArgs a) {
 // transposing reads of a 16-lane group then touch distinct banks for any row
 // pitch that is a multiple of 512 bytes).
 Q4_DEV int fds_swz(int r) { return (r & 3) | (((r >> 3) & 1) << 2); }
-
-// A workgroup barrier that orders LDS only: this wave's LDS operations
-// have completed (lgkmcnt 0) before it arrives.  __syncthreads' release fence
-// would also wait for every global load in flight, the prefetches included.
-Q4_DEV void lds_barrier() {
-  __asm__ __volatile__("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(0xC07F);         // vmcnt 63, expcnt 7, lgkmcnt 0
-  __builtin_amdgcn_s_barrier();
-  __asm__ __volatile__("" ::: "memory");
-}
 
 // waits until at most N vector memory instructions of this wave are in flight
 template <int N>
@@ -1501,14 +1584,26 @@ __global__ void __launch_bounds__(512) k_fd_full_ds(AttnArgs a) {
 // takes splits w, w + 4, ... (S <= MAXS).  Every load of the workgroup is
 // issued before the first use (split indices past S are clamped and their
 // weight is zero), and the four wave sums meet in LDS in a fixed order.
+//
+// TAIL (a block of rows whose ring splits cover each group of a.rpw rows up
+// to the position P of its first row; one sequence, the finished queries in
+// a.fin.q_out): row r also attends positions P + 1 .. P + (r mod rpw), rows
+// formed in this step and already in the cache.  Each is one more term of
+// the sums, with m its score, l = 1 and O its V row; the score is q . k
+// over the whole head (dims dealt to the 256 threads, the wave sums added
+// in a fixed order), scaled as the partial kernels scale theirs.
 constexpr int kMaxSplits = 256;
+constexpr int kMaxTail = 3;                    // rows of a block (at most 4) past its first
 
-template <int D, int MAXS>
+template <int D, int MAXS, bool TAIL = false>
 __global__ void __launch_bounds__(256) k_fd_combine(AttnArgs a, float* out32, uint16_t* out16) {
   constexpr int PER = MAXS / 4;
+  constexpr int TD = (D + 255) / 256;          // TAIL: head dims per thread
   __shared__ float wsp[MAXS];
   __shared__ float red[4][64];
   __shared__ float rm[4], rl[4];
+  __shared__ float tred[4][kMaxTail];
+  const int pos_w = TAIL ? pos_issue(a) : 0;
   const int idx = blockIdx.x;
   const int h = a.kvh_major ? (idx % a.Hkv) * a.GQ + (idx / a.Hkv) % a.GQ : idx % a.Hq, sr = idx / a.Hq;
   const int seq = sr / a.n_rows, row = sr - seq * a.n_rows;
@@ -1524,11 +1619,47 @@ __global__ void __launch_bounds__(256) k_fd_combine(AttnArgs a, float* out32, ui
   float ov[PER];
 #pragma unroll
   for (int i = 0; i < PER; i++) ov[i] = a.part[r0 + (long)min(wave + 4 * i, S - 1) * rs + d];
+  // TAIL: the query, and the keys and this lane's V elements of the rows
+  // past the group's first
+  int nt = 0;
+  float tq[TD], tk[kMaxTail][TD], tv[kMaxTail];
+  if constexpr (TAIL) {
+    nt = row % a.rpw;
+    const int Pf = pos_take(a, pos_w, seq) + row - nt;
+    const uint16_t* qr = a.fin.q_out + ((long)row * a.Hq + h) * D;
+    const uint16_t* kb = a.k + (long)kvh * a.R * D;
+    const uint16_t* vb = a.v + (long)kvh * a.R * D;
+#pragma unroll
+    for (int i = 0; i < TD; i++) tq[i] = tid + 256 * i < D ? h2f(qr[tid + 256 * i]) : 0.f;
+#pragma unroll
+    for (int e = 0; e < kMaxTail; e++) {
+      const long so = (long)((Pf + 1 + min(e, max(nt - 1, 0))) % a.R) * D;
+#pragma unroll
+      for (int i = 0; i < TD; i++) tk[e][i] = tid + 256 * i < D ? h2f(kb[so + tid + 256 * i]) : 0.f;
+      tv[e] = h2f(vb[so + d]);
+    }
+#pragma unroll
+    for (int e = 0; e < kMaxTail; e++) {
+      float part = 0.f;
+#pragma unroll
+      for (int i = 0; i < TD; i++) part = fmaf(tq[i], tk[e][i], part);
+      part = wave_sum(part);
+      if (lane == 0) tred[wave][e] = part;
+    }
+  }
   const float m = own ? m_raw : -INFINITY;
   float M = wave_max(m);
   if (lane == 0) rm[wave] = M;
   __syncthreads();
   M = fmaxf(fmaxf(rm[0], rm[1]), fmaxf(rm[2], rm[3]));
+  float ts[kMaxTail];
+  if constexpr (TAIL) {
+#pragma unroll
+    for (int e = 0; e < kMaxTail; e++) {
+      ts[e] = e < nt ? (((tred[0][e] + tred[1][e]) + tred[2][e]) + tred[3][e]) * a.scale_log2 : -INFINITY;
+      M = fmaxf(M, ts[e]);
+    }
+  }
   const float w = (own && m != -INFINITY) ? exp2f(m - M) : 0.f;
   if (tid < MAXS) wsp[tid] = w;
   float L = wave_sum(w * (own ? l_raw : 0.f));
@@ -1542,6 +1673,16 @@ __global__ void __launch_bounds__(256) k_fd_combine(AttnArgs a, float* out32, ui
   __syncthreads();
   if (wave == 0) {
     o = ((red[0][lane] + red[1][lane]) + red[2][lane]) + red[3][lane];
+    if constexpr (TAIL) {
+#pragma unroll
+      for (int e = 0; e < kMaxTail; e++) {
+        if (e < nt) {
+          const float we = exp2f(ts[e] - M);
+          L += we;
+          o = fmaf(we, tv[e], o);
+        }
+      }
+    }
     o *= (L > 0.f) ? 1.0f / L : 0.f;
     const long oi = (((long)seq * a.n_rows + row) * a.Hq + h) * D + d;
     if (out32) out32[oi] = o;

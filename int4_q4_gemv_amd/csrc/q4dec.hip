@@ -138,9 +138,6 @@ q4_status set_attrs() {
   e = e != hipSuccess ? e : max_lds(&k_fd_partial<512, false, true>, (int)fd_lds_bytes<512>());
   e = e != hipSuccess ? e : max_lds(&k_fd_partial<128, true, true>, (int)fd_lds_bytes<128>());
   e = e != hipSuccess ? e : max_lds(&k_fd_partial<512, true, true>, (int)fd_lds_bytes<512>());
-  e = e != hipSuccess ? e : max_lds(&k_fd_ring_ds<128>, (int)ds_lds_bytes<128>());
-  e = e != hipSuccess ? e : max_lds(&k_fd_ring_ds<256>, (int)ds_lds_bytes<256>());
-  e = e != hipSuccess ? e : max_lds(&k_fd_ring_ds<512>, (int)ds_lds_bytes<512>());
   e = e != hipSuccess ? e : max_lds(&k_fd_rows4<128>, (int)rows4_lds_bytes<128>());
   e = e != hipSuccess ? e : max_lds(&k_fd_rows4<256>, (int)rows4_lds_bytes<256>());
   e = e != hipSuccess ? e : max_lds(&k_fd_rows4<512>, (int)rows4_lds_bytes<512>());
@@ -158,10 +155,14 @@ q4_status set_attrs() {
   return Q4_OK;
 }
 
+// tail: rows of a block past each group's first (ring splits of several rows
+// per workgroup, S <= 32)
 template <int D>
-void launch_combine(const AttnArgs& a, int n_seq, float* out32, uint16_t* out16, hipStream_t st) {
+void launch_combine(const AttnArgs& a, int n_seq, float* out32, uint16_t* out16, hipStream_t st, bool tail = false) {
   const dim3 cgrid(n_seq * a.n_rows * a.Hq, D / 64);  // 256 threads each
-  if (a.S <= 16) hipLaunchKernelGGL((k_fd_combine<D, 16>), cgrid, dim3(256), 0, st, a, out32, out16);
+  if (tail && a.S <= 16) hipLaunchKernelGGL((k_fd_combine<D, 16, true>), cgrid, dim3(256), 0, st, a, out32, out16);
+  else if (tail) hipLaunchKernelGGL((k_fd_combine<D, 32, true>), cgrid, dim3(256), 0, st, a, out32, out16);
+  else if (a.S <= 16) hipLaunchKernelGGL((k_fd_combine<D, 16>), cgrid, dim3(256), 0, st, a, out32, out16);
   else if (a.S <= 32) hipLaunchKernelGGL((k_fd_combine<D, 32>), cgrid, dim3(256), 0, st, a, out32, out16);
   else if (a.S <= 64) hipLaunchKernelGGL((k_fd_combine<D, 64>), cgrid, dim3(256), 0, st, a, out32, out16);
   else hipLaunchKernelGGL((k_fd_combine<D, kMaxSplits>), cgrid, dim3(256), 0, st, a, out32, out16);
@@ -206,15 +207,26 @@ void launch_rows4(const AttnArgs& a, int D, int n_seq, uint16_t* out16, hipStrea
 
 // Ring layers whose splits hold at most one tile, one row per workgroup:
 // the head dimension dealt to the 4 waves of a workgroup.
+// With several rows per workgroup (a.rpw > 1) their columns share the tile.
 template <int D>
 void launch_ring_ds_d(const AttnArgs& a, int n_seq, float* out32, uint16_t* out16, hipStream_t st) {
-  const dim3 grid(a.kvh_major ? a.Hkv : a.S, a.kvh_major ? a.S : a.Hkv, n_seq * a.n_rows);
-  hipLaunchKernelGGL(k_fd_ring_ds<D>, grid, dim3(256), ds_lds_bytes<D>(), st, a);
-  launch_combine<D>(a, n_seq, out32, out16, st);
+  const int rpw = a.rpw > 1 ? a.rpw : 1;
+  const dim3 grid(a.kvh_major ? a.Hkv : a.S, a.kvh_major ? a.S : a.Hkv, n_seq * (int)ceil_div(a.n_rows, rpw));
+  const size_t lds = 0;                       // static LDS only
+  if (rpw > 1) hipLaunchKernelGGL((k_fd_ring_ds<D, true, true>), grid, dim3(256), lds, st, a);
+  else if (a.fin_on) hipLaunchKernelGGL((k_fd_ring_ds<D, false, true>), grid, dim3(256), lds, st, a);
+  else hipLaunchKernelGGL((k_fd_ring_ds<D, false, false>), grid, dim3(256), lds, st, a);
+  launch_combine<D>(a, n_seq, out32, out16, st, rpw > 1);
 }
 
+// every split holds at most one tile of the first row's window.  Several
+// rows per workgroup: with the finishing prologue and its query export (the
+// combine adds each row's positions past the first row's from the cache),
+// one sequence, at most 32 splits and kMaxTail rows past a group's first.
 bool ring_ds_ok(const AttnArgs& a, int D) {
-  return a.ring && D >= 128 && (long)a.S * 32 >= a.W && a.rpw <= 1 && !a.vrow;
+  return a.ring && D >= 128 && (long)a.S * 32 >= a.W && !a.vrow &&
+         (a.rpw <= 1 || (a.fin_on && a.fin.q_out && a.GQ * a.rpw <= 16 && a.S <= 32 &&
+                         std::min(a.rpw, a.n_rows) - 1 <= kMaxTail));
 }
 
 // Full layers, one row per workgroup: 8 waves, the head dimension dealt
@@ -365,6 +377,48 @@ StepPtrs step_ptrs(const StepLayout& L, void* ws) {
   return p;
 }
 
+// Attention of a block of rows that the one-launch path does not take: every
+// row finished first (queries to q16, K/V rows into the caches), then the
+// rows' attention over the caches, sharing K/V tiles.
+void enqueue_chunk_attn(const q4dec_model* m, const StepLayout& L, const StepPtrs& P, const q4dec_layer& ly, int n,
+                        bool full, int D, int Hkv, bool vrow, const float2* rope_l, int cs_ld, hipStream_t st) {
+  const int Hq = m->n_heads;
+  {
+    ChunkFinArgs f{};
+    f.qkv = P.qkv; f.ldq = L.qkv_ld; f.ny = 1; f.y_split = 0;
+    f.Hq = Hq; f.Hkv = Hkv; f.ring = full ? 0 : 1; f.R = m->ring;
+    f.v_norm = ly.v_norm; f.vrow = vrow ? 1 : 0;
+    f.q_norm = ly.q_norm; f.k_norm = ly.k_norm;
+    f.theta = full ? m->full_theta : m->sl_theta;
+    f.rot_pairs = full ? m->full_rot_pairs : m->sl_rot_pairs;
+    f.eps = m->eps; f.pos0 = 0; f.sp = P.sp; f.rope_cs = rope_l; f.cs_ld = cs_ld;
+    f.q16 = P.q16; f.kc = ly.k_cache; f.vc = ly.v_cache;
+    const dim3 grid(n, Hq + 2 * Hkv);
+    switch (D) {
+      case 64: hipLaunchKernelGGL(k_chunk_finish<64>, grid, dim3(64), 0, st, f); break;
+      case 128: hipLaunchKernelGGL(k_chunk_finish<128>, grid, dim3(64), 0, st, f); break;
+      case 256: hipLaunchKernelGGL(k_chunk_finish<256>, grid, dim3(64), 0, st, f); break;
+      default: hipLaunchKernelGGL(k_chunk_finish<512>, grid, dim3(64), 0, st, f); break;
+    }
+  }
+  // then the rows' attention over the caches, sharing K/V tiles
+  AttnArgs a{};
+  a.q = P.q16; a.k = ly.k_cache; a.v = ly.v_cache; a.seq_stride = 0;
+  a.Hq = Hq; a.Hkv = Hkv; a.GQ = Hq / Hkv;
+  a.ring = full ? 0 : 1; a.R = m->ring; a.W = m->window;
+  a.n_rows = n; a.S = full ? L.S_full : L.S_ring4;
+  a.scale_log2 = (full ? m->full_scale : m->sl_scale) * 1.4426950408889634f;
+  a.sp = P.sp; a.part = P.apart;
+  a.fin_on = 0;
+  a.kvh_major = full ? 0 : 1;
+  if (vrow) {
+    a.vrow = 1; a.k = ly.v_cache; a.kw = ly.k_norm; a.theta = m->full_theta; a.krot = m->full_rot_pairs;
+  }
+  a.rpw = 16 % a.GQ == 0 ? 16 / a.GQ : 1;
+  if (a.rpw <= 1 && !vrow && full && D >= 128) launch_rows4(a, D, 1, P.o, st);
+  else launch_fd(a, D, 1, nullptr, P.o, st);
+}
+
 // Launch sequence of one step (every kernel reads positions, the row count
 // and the output pointers from the device-side StepParams, so the sequence is
 // position- and output-free):
@@ -429,7 +483,10 @@ q4_status enqueue_layers(const q4dec_model* m, const StepLayout& L, const StepPt
     const int cs_ld = m->sl_head_dim / 2 + m->full_head_dim / 2;
     if (gemvs_only) {
       // attention skipped
-    } else if (B == 1) {
+    } else {
+      // rows finished inside the attention kernels: each workgroup forms the
+      // queries of its columns and the K/V rows of this step in its range, and
+      // stores each of its rows whose position lies there
       AttnArgs a{};
       a.q = nullptr; a.k = ly.k_cache; a.v = ly.v_cache; a.seq_stride = 0;
       a.Hq = Hq; a.Hkv = Hkv; a.GQ = Hq / Hkv;
@@ -446,43 +503,11 @@ q4_status enqueue_layers(const q4dec_model* m, const StepLayout& L, const StepPt
       a.fin.v_norm = ly.v_norm; a.fin.rot_pairs = full ? m->full_rot_pairs : m->sl_rot_pairs;
       a.fin.rope_cs = rope_l; a.fin.cs_ld = cs_ld; a.fin.eps = m->eps;
       a.fin.q_out = P.q16;
-      launch_fd(a, D, 1, nullptr, P.o, st);
-    } else {
-      // every row finished first: queries to q16, K/V rows into the caches
-      {
-        ChunkFinArgs f{};
-        f.qkv = P.qkv; f.ldq = L.qkv_ld; f.ny = 1; f.y_split = 0;
-        f.Hq = Hq; f.Hkv = Hkv; f.ring = full ? 0 : 1; f.R = m->ring;
-        f.v_norm = ly.v_norm; f.vrow = vrow ? 1 : 0;
-        f.q_norm = ly.q_norm; f.k_norm = ly.k_norm;
-        f.theta = full ? m->full_theta : m->sl_theta;
-        f.rot_pairs = full ? m->full_rot_pairs : m->sl_rot_pairs;
-        f.eps = m->eps; f.pos0 = 0; f.sp = P.sp; f.rope_cs = rope_l; f.cs_ld = cs_ld;
-        f.q16 = P.q16; f.kc = ly.k_cache; f.vc = ly.v_cache;
-        const dim3 grid(n, Hq + 2 * Hkv);
-        switch (D) {
-          case 64: hipLaunchKernelGGL(k_chunk_finish<64>, grid, dim3(64), 0, st, f); break;
-          case 128: hipLaunchKernelGGL(k_chunk_finish<128>, grid, dim3(64), 0, st, f); break;
-          case 256: hipLaunchKernelGGL(k_chunk_finish<256>, grid, dim3(64), 0, st, f); break;
-          default: hipLaunchKernelGGL(k_chunk_finish<512>, grid, dim3(64), 0, st, f); break;
-        }
-      }
-      // then the rows' attention over the caches, sharing K/V tiles
-      AttnArgs a{};
-      a.q = P.q16; a.k = ly.k_cache; a.v = ly.v_cache; a.seq_stride = 0;
-      a.Hq = Hq; a.Hkv = Hkv; a.GQ = Hq / Hkv;
-      a.ring = full ? 0 : 1; a.R = m->ring; a.W = m->window;
-      a.n_rows = n; a.S = full ? L.S_full : L.S_ring4;
-      a.scale_log2 = (full ? m->full_scale : m->sl_scale) * 1.4426950408889634f;
-      a.sp = P.sp; a.part = P.apart;
-      a.fin_on = 0;
-      a.kvh_major = full ? 0 : 1;
-      if (vrow) {
-        a.vrow = 1; a.k = ly.v_cache; a.kw = ly.k_norm; a.theta = m->full_theta; a.krot = m->full_rot_pairs;
-      }
-      a.rpw = 16 % a.GQ == 0 ? 16 / a.GQ : 1;
-      if (a.rpw <= 1 && !vrow && full && D >= 128) launch_rows4(a, D, 1, P.o, st);
-      else launch_fd(a, D, 1, nullptr, P.o, st);
+      // a block of rows: on a ring layer their columns share each tile of one
+      // workgroup (16 / GQ rows); elsewhere every row is finished first
+      if (B > 1) a.rpw = 16 % a.GQ == 0 ? 16 / a.GQ : 1;
+      if (B == 1 || (!full && a.rpw > 1 && ring_ds_ok(a, D))) launch_fd(a, D, 1, nullptr, P.o, st);
+      else enqueue_chunk_attn(m, L, P, ly, n, full, D, Hkv, vrow, rope_l, cs_ld, st);
     }
     // ---- output projection
     {

@@ -448,13 +448,18 @@ def test_12b_two_layer_composition(orc, full48, stream, n):
 
 
 @pytest.mark.timeout(600)
-def test_12b_verify_block_across_the_ring_end(orc, full48, stream):
-    """A width-4 verify block at positions 2046 .. 2049 (ring slots 2046, 2047,
-    0, 1) through 12B sliding layers and a full layer, stage by stage."""
+@pytest.mark.parametrize("pos", [2046, 1022, 0])
+def test_12b_verify_block_across_the_ring_end(orc, full48, stream, pos):
+    """A width-4 verify block through 12B sliding layers and a full layer,
+    stage by stage: at positions 2046 .. 2049 (ring slots 2046, 2047, 0, 1);
+    at 1022 .. 1025 (the first two rows see every earlier position, the last
+    two windows start at 1 and 2: the splits divide a union of unequal
+    windows); at 0 .. 3 (most splits empty)."""
     gm, om = full48
     restore_caches(gm)
     cfg = gm.cfg
-    pos, n = 2046, 4
+    n = 4
+    print(f"12b verify block at {pos}", flush=True)
     toks = synth.tokens(cfg, n, 7)
     for l in (0, 4, 5):
         g1 = sub_model(gm, [l])
