@@ -1629,15 +1629,24 @@ __global__ void __launch_bounds__(256) k_fd_combine(AttnArgs a, float* out32, ui
     const uint16_t* qr = a.fin.q_out + ((long)row * a.Hq + h) * D;
     const uint16_t* kb = a.k + (long)kvh * a.R * D;
     const uint16_t* vb = a.v + (long)kvh * a.R * D;
+    // loads without conditions (a dim past D reads dim D - 1 and its query
+    // element is zeroed after the load), so none waits inside a branch
 #pragma unroll
-    for (int i = 0; i < TD; i++) tq[i] = tid + 256 * i < D ? h2f(qr[tid + 256 * i]) : 0.f;
+    for (int i = 0; i < TD; i++) {
+      const float qv = h2f(qr[min(tid + 256 * i, D - 1)]);
+      tq[i] = tid + 256 * i < D ? qv : 0.f;
+    }
 #pragma unroll
     for (int e = 0; e < kMaxTail; e++) {
       const long so = (long)((Pf + 1 + min(e, max(nt - 1, 0))) % a.R) * D;
 #pragma unroll
-      for (int i = 0; i < TD; i++) tk[e][i] = tid + 256 * i < D ? h2f(kb[so + tid + 256 * i]) : 0.f;
+      for (int i = 0; i < TD; i++) tk[e][i] = h2f(kb[so + min(tid + 256 * i, D - 1)]);
       tv[e] = h2f(vb[so + d]);
     }
+    // every load above is issued before the first sum waits (left to itself
+    // the compiler moves each load down to its use, past the cross-lane sums,
+    // and the loads then wait for one another)
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int e = 0; e < kMaxTail; e++) {
       float part = 0.f;
