@@ -1198,9 +1198,7 @@ __global__ void __launch_bounds__(512) k_fd_full_ds(AttnArgs a) {
   const int j = lane & 15, g = lane >> 4;
   const bool col_ok = j < a.GQ;
 
-  int base;
-  if (a.sp) base = *(const __attribute__((address_space(1))) int*)(&a.sp->pos0);
-  else base = a.pos0[seq];
+  const int pos_w = pos_issue(a);             // the step's first position, issued first
 
   // ---- queries of a call without the finishing prologue: issued first, so
   // that no K/V load is ahead of them
@@ -1244,7 +1242,7 @@ __global__ void __launch_bounds__(512) k_fd_full_ds(AttnArgs a) {
   }
   __builtin_amdgcn_sched_barrier(0);
 
-  base = __builtin_amdgcn_readfirstlane(base);
+  const int base = pos_take(a, pos_w, seq);
   const int P = base + row;
   // this split's tiles: split, split + S, ... of the 32-position tiles
   // covering 0 .. P (positions past P are masked)
@@ -1341,22 +1339,17 @@ __global__ void __launch_bounds__(512) k_fd_full_ds(AttnArgs a) {
     }
   }
   lds_barrier();                              // finished rows and the VR tables are in
-  if (a.fin_on) {
-    const AttnFin& f = a.fin;
-    if (f.q_out && split == 0) {
-      constexpr int CH = D / 8;
-      for (int i = threadIdx.x; i < a.GQ * CH; i += 512) {
-        const int jq = i / CH, c = i - jq * CH;
-        *reinterpret_cast<u4v*>(f.q_out + ((long)row * a.Hq + kvh * a.GQ + jq) * D + c * 8) =
-            *reinterpret_cast<const u4v*>(q16 + jq * D + c * 8);
-      }
-    }
-    if (owns(P)) {                            // the row's own position goes to the cache
-      const long so = (long)P * D;
-      for (int d = threadIdx.x; d < D; d += 512) {
-        if (!VR) kb[so + d] = newK[row * D + d];
-        vb[so + d] = newV[row * D + d];
-      }
+  // split 0 exports the finished queries, from registers at the end (the
+  // scores take their LDS; stores issued here would be waited for by every
+  // later wait of the wave): thread t holds 16-byte chunks t and t + 512
+  constexpr int QCH = 16 * D / 8;             // chunks of 16 finished heads
+  u4v qexp[(QCH + 511) / 512];
+  const bool q_exp = a.fin_on && a.fin.q_out && split == 0;
+  if (q_exp) {
+#pragma unroll
+    for (int e = 0; e < (QCH + 511) / 512; e++) {
+      const int ci = threadIdx.x + 512 * e;
+      qexp[e] = ci < a.GQ * (D / 8) ? *reinterpret_cast<const u4v*>(q16 + ci * 8) : (u4v){0u, 0u, 0u, 0u};
     }
   }
   // ---- queries of this wave's k steps as the MFMA B operand (VR: in the
@@ -1559,22 +1552,40 @@ __global__ void __launch_bounds__(512) k_fd_full_ds(AttnArgs a) {
   }
   __syncthreads();
   if (grp == 0) {
+    // one scalar base, 32-bit offsets (head c's record lies c (D + 4) on)
+    float* rbase = a.part + attn_rec(a, seq, row, kvh, split, 0, D);
 #pragma unroll
     for (int i = 0; i < 4; i++) {
       if (4 * g + i < a.GQ) {
-        float* rec = a.part + attn_rec(a, seq, row, kvh, split, 4 * g + i, D);
+        const unsigned o = (unsigned)((4 * g + i) * (D + 4) + 16 * DS * w + j);
 #pragma unroll
         for (int dd = 0; dd < DS; dd++)
-          rec[16 * (DS * w + dd) + j] = O[dd][i] * fw[i] + ob[(w * DS + dd) * 64 + lane][i];
+          rbase[o + 16 * dd] = O[dd][i] * fw[i] + ob[(w * DS + dd) * 64 + lane][i];
       }
     }
     if (w == 0 && lane < a.GQ) {
       const float M = fmaxf(wm[0][lane], wm[1][lane]);
       float l = 0.f;
       if (M != -INFINITY) l = exp2f(wm[0][lane] - M) * wl[0][lane] + exp2f(wm[1][lane] - M) * wl[1][lane];
-      float* rec = a.part + attn_rec(a, seq, row, kvh, split, lane, D);
-      rec[D] = M;
-      rec[D + 1] = l;
+      rbase[lane * (D + 4) + D] = M;
+      rbase[lane * (D + 4) + D + 1] = l;
+    }
+  }
+  // ---- last, so that nothing waits for them: the queries' export and the
+  // row's own position into the cache
+  if (q_exp) {
+#pragma unroll
+    for (int e = 0; e < (QCH + 511) / 512; e++) {
+      const int ci = threadIdx.x + 512 * e;
+      if (ci < a.GQ * (D / 8))
+        *reinterpret_cast<u4v*>(a.fin.q_out + ((long)row * a.Hq + kvh * a.GQ) * D + ci * 8) = qexp[e];
+    }
+  }
+  if (a.fin_on && owns(P)) {
+    const long so = (long)P * D;
+    for (int d = threadIdx.x; d < D; d += 512) {
+      if (!VR) kb[so + d] = newK[row * D + d];
+      vb[so + d] = newV[row * D + d];
     }
   }
 }
