@@ -11,7 +11,7 @@ at three shapes, context-131072 and width-4 verify figures, the attention
 kernels alone, and the CPU oracle timed on the host cores on a bounded
 sample.
 
-  python bench.py [--gpus 1] [--steps K] [--warmup W] [--mode full|gemv|step|verify|traffic|prefill|attn_traffic]
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--mode full|gemv|step|verify|traffic|prefill|attn_traffic|gemv_lds]
 """
 import argparse
 import json
@@ -30,7 +30,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--mode", default="full", choices=["full", "gemv", "step", "verify", "traffic", "prefill", "attn_traffic"])
+    ap.add_argument("--mode", default="full", choices=["full", "gemv", "step", "verify", "traffic", "prefill", "attn_traffic", "gemv_lds"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     return ap.parse_args()
 
@@ -307,6 +307,21 @@ def traffic_launches(q4, torch, model):
     torch.cuda.synchronize()
 
 
+def gemv_lds_launches(q4, torch):
+    """What the GEMV LDS counter run profiles, eagerly: the standalone
+    15360 x 3840 product at batch 1, then at batch 4, three dispatches each."""
+    N, K = 15360, 3840
+    g = torch.Generator(device="cuda").manual_seed(1)
+    w = torch.randn(N, K, device="cuda", generator=g) * 0.05
+    packed = q4.q4_pack(w)
+    del w
+    for B in (1, 4):
+        x = (torch.randn(B, K, device="cuda", generator=g) * 0.5).half()
+        for _ in range(3):
+            q4.q4_gemv(packed, N, K, x)
+    torch.cuda.synchronize()
+
+
 def attention_traffic_launches(q4, torch):
     """What the attention counter runs profile, eagerly (one dispatch per
     kernel): a plain device copy of COPY_BYTES (calibration), then twice each
@@ -466,6 +481,12 @@ def main():
     from dataclasses import replace
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.mode == "gemv_lds":
+        stream = torch.cuda.Stream()
+        with torch.cuda.stream(stream):
+            gemv_lds_launches(q4, torch)
+        print(json.dumps({"mode": "gemv_lds"}))
+        return
     if args.mode == "attn_traffic":
         stream = torch.cuda.Stream()
         with torch.cuda.stream(stream):

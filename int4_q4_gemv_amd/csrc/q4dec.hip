@@ -427,13 +427,15 @@ void enqueue_chunk_attn(const q4dec_model* m, const StepLayout& L, const StepPtr
 // projection, post-attention residual and pre-FF norm, gate/up with GELU *
 // up, down projection; then the final norm, the tied head and the argmax
 // read-out.  Attention of one row finishes q/k/v in the partial kernel's
-// prologue.  A width-4 verify block first finishes every row in its own
-// launch (queries to q16, K/V rows into the caches), then its rows share
-// each K/V tile: on a ring layer as MFMA columns of one workgroup ((row,
-// query head) pairs), on a full layer through the 4-row kernel (one wave per
-// row over tiles staged once in LDS), so the block reads each cached
-// position once (Gemma-4-12B-CoreAI card, "v5/ -- ring extent R = 2W": one
-// pass per block; gemma-4-E4B-CoreAI card, ring3/: the GQA fold).
+// prologue.  The rows of a width-4 verify block share each K/V tile, so the
+// block reads each cached position once (Gemma-4-12B-CoreAI card, "v5/ --
+// ring extent R = 2W": one pass per block; gemma-4-E4B-CoreAI card, ring3/:
+// the GQA fold): on a ring layer as MFMA columns of one workgroup ((row,
+// query head) pairs) of the head-dimension-split kernel, which also finishes
+// the rows, the combine adding each row's positions past the first row's;
+// on a full layer every row is finished first in its own launch (queries to
+// q16, K/V rows into the cache), then the 4-row kernel (one wave per row
+// over tiles staged once in LDS) reads them.
 // Buffers: x of attention (xf), of the MLP (xf2) and of the head (xh) are
 // kept apart, so after a step the workspace holds the last layer's stages.
 // gemvs_only: only the q/k/v, output and down products (the step's most
