@@ -238,3 +238,30 @@ def test_prefill_full_layer_rows4_d256(orc, stream):
         check_cache_rows(cfg, gm, om, pos0, n, f"rows4 D=256 n={n}")
         gm, om = build_pair(orc, cfg, 24, pos0)
         check_layers_alone(gm, om, toks, pos0, f"rows4 D=256 n={n}")
+
+
+def test_one_kv_head_wide_sliding_layers(orc, stream):
+    """Sliding layers with one KV head of 256 dims under 16 query heads, and
+    full layers of 128 dims (the sliding head wider than the full one, so the
+    ring layers size the attention records): the chunk's ring attention takes
+    one row per workgroup (16 query heads fill the MFMA columns) and the
+    4-row kernel stays on the full layers.  The prefill chunk (64 and 29
+    rows) and a width-4 verify block against the oracle."""
+    cfg = dataclasses.replace(synth.TOY, n_heads=16, sl_kv_heads=1, sl_head_dim=256, full_head_dim=128)
+    for n, pos0 in ((64, 100), (29, 3)):
+        print(f"one KV head, wide sliding layers: chunk n={n} pos0={pos0}", flush=True)
+        gm, om = build_pair(orc, cfg, 25, pos0)
+        toks = synth.tokens(cfg, n, 25)
+        logits, am, h = gm.prefill(toks, pos0, want_hidden=True)
+        torch.cuda.synchronize()
+        ref, _ = om.decode_step(toks, pos0)
+        assert_close(logits, ref[-1], what=f"one KV head chunk logits n={n}")
+        check_cache_rows(cfg, gm, om, pos0, n, f"one KV head chunk n={n}")
+    print("one KV head, wide sliding layers: verify block", flush=True)
+    gm, om = build_pair(orc, cfg, 25, 150)
+    toks = synth.tokens(cfg, 4, 26)
+    logits, am = gm.step(toks, 150)
+    torch.cuda.synchronize()
+    ref, _ = om.decode_step(toks, 150)
+    assert_close(logits, ref, what="one KV head verify logits")
+    check_argmax(logits, am, ref, 4e-3)
