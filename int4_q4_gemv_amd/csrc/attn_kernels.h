@@ -1552,15 +1552,21 @@ __global__ void __launch_bounds__(512) k_fd_full_ds(AttnArgs a) {
   }
   __syncthreads();
   if (grp == 0) {
-    // one scalar base, 32-bit offsets (head c's record lies c (D + 4) on)
+    // one scalar base, 32-bit offsets (head c's record lies c (D + 4) on);
+    // O / l in fp16 (k_fd_combine, H16), m and l in fp32
     float* rbase = a.part + attn_rec(a, seq, row, kvh, split, 0, D);
+    uint16_t* rb16 = reinterpret_cast<uint16_t*>(rbase);
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-      if (4 * g + i < a.GQ) {
-        const unsigned o = (unsigned)((4 * g + i) * (D + 4) + 16 * DS * w + j);
+      const int hc = 4 * g + i;
+      const float M = fmaxf(wm[0][hc], wm[1][hc]);
+      const float lh = M == -INFINITY ? 0.f : exp2f(wm[0][hc] - M) * wl[0][hc] + exp2f(wm[1][hc] - M) * wl[1][hc];
+      const float inv = lh > 0.f ? 1.0f / lh : 0.f;
+      if (hc < a.GQ) {
+        const unsigned o = (unsigned)(2 * hc * (D + 4) + 16 * DS * w + j);
 #pragma unroll
         for (int dd = 0; dd < DS; dd++)
-          rbase[o + 16 * dd] = O[dd][i] * fw[i] + ob[(w * DS + dd) * 64 + lane][i];
+          rb16[o + 16 * dd] = f2h((O[dd][i] * fw[i] + ob[(w * DS + dd) * 64 + lane][i]) * inv);
       }
     }
     if (w == 0 && lane < a.GQ) {
@@ -1603,10 +1609,14 @@ __global__ void __launch_bounds__(512) k_fd_full_ds(AttnArgs a) {
 // the sums, with m its score, l = 1 and O its V row; the score is q . k
 // over the whole head (dims dealt to the 256 threads, the wave sums added
 // in a fixed order), scaled as the partial kernels scale theirs.
+//
+// H16 (the full layers' kernels k_fd_full_ds and k_fd_rows4): a record holds
+// O / l in fp16 at its start (m and l stay fp32 at D, D + 1), half the bytes
+// of the records written and read; split s then weighs 2^(m_s - M) l_s.
 constexpr int kMaxSplits = 256;
 constexpr int kMaxTail = 3;                    // rows of a block (at most 4) past its first
 
-template <int D, int MAXS, bool TAIL = false>
+template <int D, int MAXS, bool TAIL = false, bool H16 = false>
 __global__ void __launch_bounds__(256) k_fd_combine(AttnArgs a, float* out32, uint16_t* out16) {
   constexpr int PER = MAXS / 4;
   constexpr int TD = (D + 255) / 256;          // TAIL: head dims per thread
@@ -1629,7 +1639,10 @@ __global__ void __launch_bounds__(256) k_fd_combine(AttnArgs a, float* out32, ui
   const float m_raw = a.part[mo], l_raw = a.part[mo + 1];
   float ov[PER];
 #pragma unroll
-  for (int i = 0; i < PER; i++) ov[i] = a.part[r0 + (long)min(wave + 4 * i, S - 1) * rs + d];
+  for (int i = 0; i < PER; i++) {
+    const long ro = r0 + (long)min(wave + 4 * i, S - 1) * rs;
+    ov[i] = H16 ? h2f(reinterpret_cast<const uint16_t*>(a.part + ro)[d]) : a.part[ro + d];
+  }
   // TAIL: the query, and the keys and this lane's V elements of the rows
   // past the group's first
   int nt = 0;
@@ -1681,7 +1694,7 @@ __global__ void __launch_bounds__(256) k_fd_combine(AttnArgs a, float* out32, ui
     }
   }
   const float w = (own && m != -INFINITY) ? exp2f(m - M) : 0.f;
-  if (tid < MAXS) wsp[tid] = w;
+  if (tid < MAXS) wsp[tid] = H16 ? w * l_raw : w;     // H16: the records hold O / l
   float L = wave_sum(w * (own ? l_raw : 0.f));
   if (lane == 0) rl[wave] = L;
   __syncthreads();

@@ -412,19 +412,23 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) k
   }
   if (!live) return;
   float l_tot = rows_sum(l_part);
+  // records with O / l in fp16 (k_fd_combine, H16): half the bytes of the
+  // 4 rows' records, which this kernel writes and the combine reads
+  float* rbase = a.part + attn_rec(a, seq, row, kvh, split, 0, D);
 #pragma unroll
   for (int i = 0; i < 4; i++) {
     const int col = 4 * g + i;
+    const float lc = __shfl(l_tot, col, 64);
+    const float inv = lc > 0.f ? 1.0f / lc : 0.f;
     if (col < a.GQ) {
-      float* rec = a.part + attn_rec(a, seq, row, kvh, split, col, D);
+      uint16_t* rec = reinterpret_cast<uint16_t*>(rbase + col * (D + 4));
 #pragma unroll
-      for (int d = 0; d < NDS; d++) rec[16 * d + j] = O[d][i];
+      for (int d = 0; d < NDS; d++) rec[16 * d + j] = f2h(O[d][i] * inv);
     }
   }
   if (lane < a.GQ) {
-    float* rec = a.part + attn_rec(a, seq, row, kvh, split, lane, D);
-    rec[D] = m_run;
-    rec[D + 1] = l_tot;
+    rbase[lane * (D + 4) + D] = m_run;
+    rbase[lane * (D + 4) + D + 1] = l_tot;
   }
 }
 

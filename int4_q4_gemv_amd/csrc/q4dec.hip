@@ -156,11 +156,16 @@ q4_status set_attrs() {
 }
 
 // tail: rows of a block past each group's first (ring splits of several rows
-// per workgroup, S <= 32)
+// per workgroup, S <= 32); h16: records holding O / l in fp16 (the full
+// layers' kernels)
 template <int D>
-void launch_combine(const AttnArgs& a, int n_seq, float* out32, uint16_t* out16, hipStream_t st, bool tail = false) {
+void launch_combine(const AttnArgs& a, int n_seq, float* out32, uint16_t* out16, hipStream_t st, bool tail = false,
+                    bool h16 = false) {
   const dim3 cgrid(n_seq * a.n_rows * a.Hq, D / 64);  // 256 threads each
-  if (tail && a.S <= 16) hipLaunchKernelGGL((k_fd_combine<D, 16, true>), cgrid, dim3(256), 0, st, a, out32, out16);
+  if (h16 && a.S <= 32) hipLaunchKernelGGL((k_fd_combine<D, 32, false, true>), cgrid, dim3(256), 0, st, a, out32, out16);
+  else if (h16 && a.S <= 64) hipLaunchKernelGGL((k_fd_combine<D, 64, false, true>), cgrid, dim3(256), 0, st, a, out32, out16);
+  else if (h16) hipLaunchKernelGGL((k_fd_combine<D, kMaxSplits, false, true>), cgrid, dim3(256), 0, st, a, out32, out16);
+  else if (tail && a.S <= 16) hipLaunchKernelGGL((k_fd_combine<D, 16, true>), cgrid, dim3(256), 0, st, a, out32, out16);
   else if (tail) hipLaunchKernelGGL((k_fd_combine<D, 32, true>), cgrid, dim3(256), 0, st, a, out32, out16);
   else if (a.S <= 16) hipLaunchKernelGGL((k_fd_combine<D, 16>), cgrid, dim3(256), 0, st, a, out32, out16);
   else if (a.S <= 32) hipLaunchKernelGGL((k_fd_combine<D, 32>), cgrid, dim3(256), 0, st, a, out32, out16);
@@ -194,7 +199,7 @@ template <int D>
 void launch_rows4_d(const AttnArgs& a, int n_seq, uint16_t* out16, hipStream_t st) {
   const dim3 grid(a.S, a.Hkv, n_seq * (int)ceil_div(a.n_rows, 4));
   hipLaunchKernelGGL(k_fd_rows4<D>, grid, dim3(256), rows4_lds_bytes<D>(), st, a);
-  launch_combine<D>(a, n_seq, nullptr, out16, st);
+  launch_combine<D>(a, n_seq, nullptr, out16, st, false, true);
 }
 
 void launch_rows4(const AttnArgs& a, int D, int n_seq, uint16_t* out16, hipStream_t st) {
@@ -236,7 +241,7 @@ void launch_full_ds_d(const AttnArgs& a, int n_seq, float* out32, uint16_t* out1
   const dim3 grid(a.S, a.Hkv, n_seq * a.n_rows);
   if (a.vrow) hipLaunchKernelGGL((k_fd_full_ds<D, true>), grid, dim3(512), 0, st, a);
   else hipLaunchKernelGGL((k_fd_full_ds<D, false>), grid, dim3(512), 0, st, a);
-  launch_combine<D>(a, n_seq, out32, out16, st);
+  launch_combine<D>(a, n_seq, out32, out16, st, false, true);
 }
 
 bool full_ds_ok(const AttnArgs& a, int D) { return !a.ring && (D == 256 || D == 512) && a.rpw <= 1; }
