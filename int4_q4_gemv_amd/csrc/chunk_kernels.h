@@ -263,13 +263,10 @@ __global__ void __launch_bounds__(256) k_q4_gemm(GemmArgs a) {
 // banks), V rows in the layout of k_fd_partial's transposing PV reads.  Each
 // wave runs the online softmax of its own row over the union of the 4 rows'
 // ranges (positions outside its row's range are masked) and writes its row's
-// (O, m, l) records; the combine is k_fd_combine's.  One tile at a time: two
-// workgroups share a CU (66 KB of LDS at D = 512), so one's loads overlap the
-// other's arithmetic.
+// (O, m, l) records; the combine is k_fd_combine's.  Two tiles in flight:
+// the next tile is staged while the current one is computed (132 KB of LDS
+// at D = 512, one workgroup per CU).
 Q4_DEV int kswz(int r) { return (r & 3) | (((r >> 3) & 3) << 2); }
-
-template <int D>
-constexpr size_t rows4_lds_bytes() { return (size_t)32 * D * 2 + (size_t)32 * fd_vpitch<D>() * 2; }
 
 template <int D>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) k_fd_rows4(AttnArgs a) {
@@ -277,9 +274,10 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) k
   constexpr int VROW = fd_vpitch<D>();
   constexpr int NDS = D / 16, NKS = D / 32;
   constexpr int CPR = D / 8, RPI = 64 / CPR;      // 16-byte chunks per row, rows per 1 KB load
-  extern __shared__ __align__(16) unsigned char smem_r[];
-  uint16_t* kt = reinterpret_cast<uint16_t*>(smem_r);   // [32][D]
-  uint16_t* vt = kt + 32 * D;                           // [32][VROW]
+  __shared__ __align__(16) uint16_t kA[32 * D];        // tile buffer A: K rows [32][D]
+  __shared__ __align__(16) uint16_t vA[32 * VROW];     // ... V rows [32][VROW]
+  __shared__ __align__(16) uint16_t kB[32 * D];        // tile buffer B
+  __shared__ __align__(16) uint16_t vB[32 * VROW];
   const int split = blockIdx.x, kvh = blockIdx.y;
   const int ngrp = (a.n_rows + 3) / 4;
   const int seq = blockIdx.z / ngrp, row0 = (blockIdx.z - seq * ngrp) * 4;
@@ -321,7 +319,16 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) k
 #pragma unroll
   for (int d = 0; d < NDS; d++) O[d] = (f4_t){0.f, 0.f, 0.f, 0.f};
 
-  for (int t0 = st; t0 < en; t0 += 32) {
+  // Two tile buffers, each a pair of LDS objects of its own: the next tile's
+  // rows are loaded straight to LDS while the current one is computed.  The
+  // loop is unrolled by two so that every LDS access names its buffer (the
+  // compiler then waits for the other buffer's loads only where they are
+  // read: the explicit counts below).  Every round issues its loads, a tile
+  // past the split's end reading row 0, so the counts are the same on every
+  // path.  (The queries' registers are first used with tiles in flight: that
+  // first use waits for both.)
+  constexpr int NL = 2 * (8 / RPI);                // loads of a tile per thread
+  auto issue = [&](uint16_t* kt, uint16_t* vt, int t0) {
     // cache rows of the tile: tile row r at slot (t0 + r) mod R (rings hold
     // at least 32 slots), rows past en read row 0 and are masked
     const int s0 = __builtin_amdgcn_readfirstlane(ringf ? t0 % Rr : t0);
@@ -330,24 +337,20 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) k
       const int sl = ringf && r >= Rr - s0 ? s0 + r - Rr : s0 + r;
       return r < nv ? (long)sl * D : 0l;
     };
-    __syncthreads();                               // the previous tile's reads are done
     // wave w stages tile rows 8w .. 8w+7 of K and of V, 1 KB per instruction
-    {
-      const int rl = lane / CPR, pc = lane % CPR;
+    const int rl = lane / CPR, pc = lane % CPR;
 #pragma unroll
-      for (int i = 0; i < 8 / RPI; i++) {
-        const int r = 8 * wave + RPI * i + rl;
-        const int ck = pc ^ kswz(r);
-        __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint32_t*>(kb + row_at(r) + ck * 8),
-                                         reinterpret_cast<uint32_t*>(kt + (8 * wave + RPI * i) * D), 16, 0, 0);
-        const int cv = pc ^ (2 * vswz<D>(r));
-        __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint32_t*>(vb + row_at(r) + cv * 8),
-                                         reinterpret_cast<uint32_t*>(vt + (8 * wave + RPI * i) * VROW), 16, 0, 0);
-      }
+    for (int i = 0; i < 8 / RPI; i++) {
+      const int r = 8 * wave + RPI * i + rl;
+      const int ck = pc ^ kswz(r);
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint32_t*>(kb + row_at(r) + ck * 8),
+                                       reinterpret_cast<uint32_t*>(kt + (8 * wave + RPI * i) * D), 16, 0, 0);
+      const int cv = pc ^ (2 * vswz<D>(r));
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint32_t*>(vb + row_at(r) + cv * 8),
+                                       reinterpret_cast<uint32_t*>(vt + (8 * wave + RPI * i) * VROW), 16, 0, 0);
     }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (!live) continue;                           // wave-uniform; it still joins every barrier
+  };
+  auto compute = [&](const uint16_t* kt, const uint16_t* vt, int t0) {
     // S^T = K Q^T: MFMA row r of half h <-> tile position 8 (r / 4) + 4h + r % 4
     const int ra = 8 * (j >> 2) + (j & 3);
     f4_t s0v = {0.f, 0.f, 0.f, 0.f}, s1v = {0.f, 0.f, 0.f, 0.f};
@@ -409,7 +412,23 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) k
       O[d] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ahi, Bv, O[d], 0, 0, 0);
       O[d] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Alo, Bv, O[d], 0, 0, 0);
     }
+  };
+  const int ntile = st < en ? (en - st + 31) / 32 : 0;
+  issue(kA, vA, st);
+  for (int t = 0; t < ntile; t += 2) {
+    issue(kB, vB, st + 32 * (t + 1));               // tile t + 1 (or row 0 past the end)
+    wait_vm<NL>();                                  // this wave's rows of tile t are in
+    lds_barrier();
+    if (live) compute(kA, vA, st + 32 * t);         // wave-uniform; every wave joins every barrier
+    lds_barrier();                                  // buffer A is free
+    if (t + 1 >= ntile) break;
+    issue(kA, vA, st + 32 * (t + 2));
+    wait_vm<NL>();
+    lds_barrier();
+    if (live) compute(kB, vB, st + 32 * (t + 1));
+    lds_barrier();
   }
+  __builtin_amdgcn_s_waitcnt(0);                    // no load past the end still in flight at exit
   if (!live) return;
   float l_tot = rows_sum(l_part);
   // records with O / l in fp16 (k_fd_combine, H16): half the bytes of the

@@ -138,9 +138,6 @@ q4_status set_attrs() {
   e = e != hipSuccess ? e : max_lds(&k_fd_partial<512, false, true>, (int)fd_lds_bytes<512>());
   e = e != hipSuccess ? e : max_lds(&k_fd_partial<128, true, true>, (int)fd_lds_bytes<128>());
   e = e != hipSuccess ? e : max_lds(&k_fd_partial<512, true, true>, (int)fd_lds_bytes<512>());
-  e = e != hipSuccess ? e : max_lds(&k_fd_rows4<128>, (int)rows4_lds_bytes<128>());
-  e = e != hipSuccess ? e : max_lds(&k_fd_rows4<256>, (int)rows4_lds_bytes<256>());
-  e = e != hipSuccess ? e : max_lds(&k_fd_rows4<512>, (int)rows4_lds_bytes<512>());
   e = e != hipSuccess ? e : max_lds(&k_q4_gemm<EPI_STORE, 1, kChunkRunQ>, (int)kGemmLds);
   e = e != hipSuccess ? e : max_lds(&k_q4_gemm<EPI_STORE, 2, kChunkRunQ>, (int)kGemmLds);
   e = e != hipSuccess ? e : max_lds(&k_q4_gemm<EPI_GATEUP, 1, kChunkRunQ>, (int)kGemmLds);
@@ -198,7 +195,7 @@ void launch_fd_d(const AttnArgs& a, int n_seq, float* out32, uint16_t* out16, hi
 template <int D>
 void launch_rows4_d(const AttnArgs& a, int n_seq, uint16_t* out16, hipStream_t st) {
   const dim3 grid(a.S, a.Hkv, n_seq * (int)ceil_div(a.n_rows, 4));
-  hipLaunchKernelGGL(k_fd_rows4<D>, grid, dim3(256), rows4_lds_bytes<D>(), st, a);
+  hipLaunchKernelGGL(k_fd_rows4<D>, grid, dim3(256), 0, st, a);   // static LDS only
   launch_combine<D>(a, n_seq, nullptr, out16, st, false, true);
 }
 
