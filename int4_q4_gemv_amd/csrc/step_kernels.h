@@ -29,9 +29,16 @@ struct BeginArgs {
 // fma with the double nearest 2 pi (k * 2.5e-16 rad of error, under 1e-10 for
 // positions below 2^20), and its cos and sin are taken in fp32.  Every
 // attention workgroup of the step reads them from this table instead of
-// recomputing them.  Workgroup 0 also publishes the step parameters.
+// recomputing them.  Workgroup 0 also publishes the step parameters.  The
+// embedding row (H <= 4096, H % 32 == 0: at most two 16-byte chunks per
+// thread) is loaded first, so its latency overlaps the table's arithmetic.
 __global__ void __launch_bounds__(256) k_step_begin(BeginArgs a) {
   const int b = blockIdx.x, tid = threadIdx.x;
+  const u4v* e8 = reinterpret_cast<const u4v*>(a.E + (long)a.tokens[b] * a.H);
+  const int nch = a.H / 8;
+  u4v ev[2];
+#pragma unroll
+  for (int c = 0; c < 2; c++) ev[c] = e8[min(tid + 256 * c, nch - 1)];
   if (b == 0) {
     if (tid == 0) {
       a.sp->pos0 = a.pos0;
@@ -62,9 +69,22 @@ __global__ void __launch_bounds__(256) k_step_begin(BeginArgs a) {
     }
     a.rope_cs[(long)b * ld + i] = c;
   }
-  const uint16_t* e = a.E + (long)a.tokens[b] * a.H;
-  float* h = a.h + (long)b * a.H;
-  for (int i = tid; i < a.H; i += 256) h[i] = h2f(e[i]) * a.emb_scale;
+  float4* h4 = reinterpret_cast<float4*>(a.h + (long)b * a.H);
+#pragma unroll
+  for (int c = 0; c < 2; c++) {
+    const int k = tid + 256 * c;
+    if (k < nch) {
+      const uint32_t w[4] = {ev[c].x, ev[c].y, ev[c].z, ev[c].w};
+      float f[8];
+#pragma unroll
+      for (int q = 0; q < 4; q++) {
+        f[2 * q] = h2f((uint16_t)(w[q] & 0xFFFF)) * a.emb_scale;
+        f[2 * q + 1] = h2f((uint16_t)(w[q] >> 16)) * a.emb_scale;
+      }
+      h4[2 * k] = make_float4(f[0], f[1], f[2], f[3]);
+      h4[2 * k + 1] = make_float4(f[4], f[5], f[6], f[7]);
+    }
+  }
 }
 
 }  // namespace q4k
