@@ -744,28 +744,6 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D <= 2
   }
 }
 
-// Ring layers whose splits hold at most one 32-position tile (S * 32 >= W).
-// With one tile per workgroup, k_fd_partial streams it from one wave while
-// the other three wait; here the head dimension is dealt to the 4 waves
-// instead.  Wave w loads the keys' dims [w D/4, (w+1) D/4) of all 32
-// positions (its D/128 QK k steps) and V rows 8w .. 8w+7 of the tile into
-// one shared LDS tile; the waves' partial scores meet in LDS and are added
-// in a fixed order, every wave runs the same softmax on the sums, and wave w
-// forms O for its own D/4 dims over the 32 rows.  A wave then has a quarter
-// of the tile in flight (8 KB at D = 256) rather than one wave holding all of
-// it, and that is what keeps the memory pipeline full when a CU holds one
-// workgroup.  Splits, masking, the finishing prologue, the records and the
-// combine are those of k_fd_partial (one tile, no merge of waves).
-//
-// MR (a.rpw rows per workgroup, with the finishing prologue): as in
-// k_fd_partial, the MFMA columns are (row, query head) pairs masked to their
-// own row's window.  The splits divide the first row's window (S * 32 >=
-// W); a later row's own positions past it (formed in this step, at most
-// rpw - 1) are added by the combine (k_fd_combine, TAIL) from the cache.  The
-// workgroup forms the queries of all its columns and the K/V rows of the
-// step in its range; the split holding the first row's position finishes and
-// stores all the workgroup's rows: a block of rows then needs no launch of
-// its own to finish them.
 // A workgroup barrier that orders LDS only: this wave's LDS operations
 // have completed (lgkmcnt 0) before it arrives.  __syncthreads' release fence
 // would also wait for every global load in flight, the prefetches included.
@@ -794,6 +772,29 @@ Q4_DEV int pos_take(const AttnArgs& a, int loaded, int seq) {
   return __builtin_amdgcn_readfirstlane(a.sp ? loaded : a.pos0[seq]);
 }
 
+// Ring layers whose splits hold at most one 32-position tile (S * 32 >= W).
+// With one tile per workgroup, k_fd_partial streams it from one wave while
+// the other three wait; here the head dimension is dealt to the 4 waves
+// instead.  Wave w loads the keys' dims [w D/4, (w+1) D/4) of all 32
+// positions (its D/128 QK k steps) and V rows 8w .. 8w+7 of the tile into
+// one shared LDS tile; the waves' partial scores meet in LDS and are added
+// in a fixed order, every wave runs the same softmax on the sums, and wave w
+// forms O for its own D/4 dims over the 32 rows.  A wave then has a quarter
+// of the tile in flight (8 KB at D = 256) rather than one wave holding all of
+// it, and that is what keeps the memory pipeline full when a CU holds one
+// workgroup.  Splits, masking, the finishing prologue (FIN), the records and
+// the combine are those of k_fd_partial (one tile, no merge of waves).  The
+// LDS objects the kernel uses, static and separate, total ds_lds_bytes.
+//
+// MR (a.rpw rows per workgroup, with the finishing prologue): as in
+// k_fd_partial, the MFMA columns are (row, query head) pairs masked to their
+// own row's window.  The splits divide the first row's window (S * 32 >=
+// W); a later row's own positions past it (formed in this step, at most
+// rpw - 1) are added by the combine (k_fd_combine, TAIL) from the cache.  The
+// workgroup forms the queries of all its columns and the K/V rows of the
+// step in its range; the split holding the first row's position finishes and
+// stores all the workgroup's rows: a block of rows then needs no launch of
+// its own to finish them.
 template <int D>
 constexpr size_t ds_lds_bytes() {
   return (size_t)32 * fd_vpitch<D>() * 2 + (size_t)2 * 4 * D * 2 + (size_t)16 * D * 2 + (size_t)4 * 2 * 64 * 16;
