@@ -263,21 +263,24 @@ __global__ void __launch_bounds__(256) k_q4_gemm(GemmArgs a) {
 // banks), V rows in the layout of k_fd_partial's transposing PV reads.  Each
 // wave runs the online softmax of its own row over the union of the 4 rows'
 // ranges (positions outside its row's range are masked) and writes its row's
-// (O, m, l) records; the combine is k_fd_combine's.  Two tiles in flight:
-// the next tile is staged while the current one is computed (132 KB of LDS
-// at D = 512, one workgroup per CU).
+// (O, m, l) records; the combine is k_fd_combine's.  NB = 2: two tiles in
+// flight, the next one staged while the current one is computed (132 KB of
+// LDS at D = 512, one workgroup per CU: for grids up to one workgroup per
+// CU).  NB = 1: one tile at a time (66 KB), so two workgroups share a CU and
+// one's loads overlap the other's arithmetic (larger grids: a prefill chunk).
 Q4_DEV int kswz(int r) { return (r & 3) | (((r >> 3) & 3) << 2); }
 
-template <int D>
+template <int D, int NB>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) k_fd_rows4(AttnArgs a) {
+  static_assert(NB == 1 || NB == 2, "one or two tile buffers");
   static_assert(D >= 128, "a K row holds at least 16 chunks");
   constexpr int VROW = fd_vpitch<D>();
   constexpr int NDS = D / 16, NKS = D / 32;
   constexpr int CPR = D / 8, RPI = 64 / CPR;      // 16-byte chunks per row, rows per 1 KB load
   __shared__ __align__(16) uint16_t kA[32 * D];        // tile buffer A: K rows [32][D]
   __shared__ __align__(16) uint16_t vA[32 * VROW];     // ... V rows [32][VROW]
-  __shared__ __align__(16) uint16_t kB[32 * D];        // tile buffer B
-  __shared__ __align__(16) uint16_t vB[32 * VROW];
+  __shared__ __align__(16) uint16_t kB[NB == 2 ? 32 * D : 8];   // tile buffer B (NB = 2)
+  __shared__ __align__(16) uint16_t vB[NB == 2 ? 32 * VROW : 8];
   const int split = blockIdx.x, kvh = blockIdx.y;
   const int ngrp = (a.n_rows + 3) / 4;
   const int seq = blockIdx.z / ngrp, row0 = (blockIdx.z - seq * ngrp) * 4;
@@ -414,6 +417,15 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) k
     }
   };
   const int ntile = st < en ? (en - st + 31) / 32 : 0;
+  if constexpr (NB == 1) {
+    for (int t = 0; t < ntile; t++) {
+      issue(kA, vA, st + 32 * t);
+      wait_vm<0>();
+      lds_barrier();
+      if (live) compute(kA, vA, st + 32 * t);
+      lds_barrier();                                // the tile's reads are done
+    }
+  } else {
   issue(kA, vA, st);
   for (int t = 0; t < ntile; t += 2) {
     issue(kB, vB, st + 32 * (t + 1));               // tile t + 1 (or row 0 past the end)
@@ -427,6 +439,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) k
     lds_barrier();
     if (live) compute(kB, vB, st + 32 * (t + 1));
     lds_barrier();
+  }
   }
   __builtin_amdgcn_s_waitcnt(0);                    // no load past the end still in flight at exit
   if (!live) return;

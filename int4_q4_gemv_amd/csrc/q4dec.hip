@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstring>
 #include <map>
@@ -190,12 +191,28 @@ void launch_fd_d(const AttnArgs& a, int n_seq, float* out32, uint16_t* out16, hi
   launch_combine<D>(a, n_seq, out32, out16, st);
 }
 
+// Compute units of the current device (queried once per device).
+int num_cus() {
+  static std::atomic<int> cus[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = cus[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cus[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
 // The chunk's full layers: 4 rows per workgroup over shared K/V tiles, then
 // the combine.
 template <int D>
 void launch_rows4_d(const AttnArgs& a, int n_seq, uint16_t* out16, hipStream_t st) {
   const dim3 grid(a.S, a.Hkv, n_seq * (int)ceil_div(a.n_rows, 4));
-  hipLaunchKernelGGL(k_fd_rows4<D>, grid, dim3(256), 0, st, a);   // static LDS only
+  // two tile buffers while the grid fits one workgroup per CU, else one (two
+  // workgroups per CU); static LDS only
+  if ((long)grid.x * grid.y * grid.z <= num_cus()) hipLaunchKernelGGL((k_fd_rows4<D, 2>), grid, dim3(256), 0, st, a);
+  else hipLaunchKernelGGL((k_fd_rows4<D, 1>), grid, dim3(256), 0, st, a);
   launch_combine<D>(a, n_seq, nullptr, out16, st, false, true);
 }
 
