@@ -271,7 +271,7 @@ __global__ void __launch_bounds__(256) k_q4_gemm(GemmArgs a) {
 Q4_DEV int kswz(int r) { return (r & 3) | (((r >> 3) & 3) << 2); }
 
 template <int D, int NB>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) k_fd_rows4(AttnArgs a) {
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NB == 1 ? 2 : 1))) k_fd_rows4(AttnArgs a) {
   static_assert(NB == 1 || NB == 2, "one or two tile buffers");
   static_assert(D >= 128, "a K row holds at least 16 chunks");
   constexpr int VROW = fd_vpitch<D>();

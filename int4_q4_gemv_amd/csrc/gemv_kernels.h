@@ -457,7 +457,6 @@ struct HeadArgs {
   const StepParams* sp;    // decode step: the logits pointer is read from here
   unsigned long long* best;  // [4], zeroed before the kernel
   int n_rows;
-  int rows_per_wave;
 };
 
 template <int B>
@@ -481,12 +480,12 @@ __global__ void __launch_bounds__(256) k_head(HeadArgs a) {
   unsigned long long best[B];
 #pragma unroll
   for (int bb = 0; bb < B; bb++) best[bb] = 0ull;
-  const long gw = (long)blockIdx.x * 4 + wave;
-  const long r0 = gw * a.rows_per_wave;
-  for (int rr = 0; rr < a.rows_per_wave; rr += 2) {
-    const long ra = r0 + rr, rb = r0 + rr + 1;
-    if (ra >= a.V) break;
-    const bool hasb = (rr + 1 < a.rows_per_wave) && rb < a.V;
+  // wave gw takes rows 2 gw, 2 gw + 1, then 2 (gw + nw), ...: in each
+  // iteration the grid's waves together read one contiguous stretch of E
+  const long gw = (long)blockIdx.x * 4 + wave, nw = (long)gridDim.x * 4;
+  for (long ra = 2 * gw; ra < a.V; ra += 2 * nw) {
+    const long rb = ra + 1;
+    const bool hasb = rb < a.V;
     u4v ea[8], eb[8];
 #pragma unroll
     for (int j = 0; j < 8; j++) {

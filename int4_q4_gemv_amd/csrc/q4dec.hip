@@ -204,6 +204,12 @@ int num_cus() {
   return n;
 }
 
+// k_head's grid: as many workgroups of 4 waves as are resident at once
+// (per_cu of them per CU: 4 at batch 1, 2 at batch 4, by the kernel's
+// registers), so that none starts after the first have finished; each wave
+// takes two rows per iteration
+int head_grid(long vocab, int per_cu) { return (int)std::min<long>((long)num_cus() * per_cu, ceil_div(vocab, 8)); }
+
 // The chunk's full layers: 4 rows per workgroup over shared K/V tiles, then
 // the combine.
 template <int D>
@@ -590,10 +596,7 @@ q4_status enqueue_layers(const q4dec_model* m, const StepLayout& L, const StepPt
     HeadArgs a{};
     a.E = m->embed; a.x = P.xh; a.V = m->vocab; a.H = H; a.softcap = m->softcap;
     a.sp = P.sp; a.best = P.best; a.n_rows = n;
-    const int waves = 8192;
-    a.rows_per_wave = (int)std::max<long>(2, ceil_div(m->vocab, waves));
-    if (a.rows_per_wave & 1) a.rows_per_wave++;
-    const int grid = (int)ceil_div(ceil_div(m->vocab, a.rows_per_wave), 4);
+    const int grid = head_grid(m->vocab, B == 1 ? 4 : 2);
     hipLaunchKernelGGL((k_head<B>), dim3(grid), dim3(256), 0, st, a);
     hipLaunchKernelGGL(k_argmax_out, dim3(1), dim3(64), 0, st, P.best, n, nullptr, P.sp);
   }
@@ -954,10 +957,7 @@ q4_status enqueue_chunk(const q4dec_model* m, const ChunkLayout& L, void* ws, co
     HeadArgs a{};
     a.E = m->embed; a.x = xf + (size_t)(n - 1) * H; a.V = m->vocab; a.H = H; a.softcap = m->softcap;
     a.logits = logits; a.best = best; a.n_rows = 1;
-    const int waves = 8192;
-    a.rows_per_wave = (int)std::max<long>(2, ceil_div(m->vocab, waves));
-    if (a.rows_per_wave & 1) a.rows_per_wave++;
-    const int grid = (int)ceil_div(ceil_div(m->vocab, a.rows_per_wave), 4);
+    const int grid = head_grid(m->vocab, 4);
     hipLaunchKernelGGL((k_head<1>), dim3(grid), dim3(256), 0, st, a);
     hipLaunchKernelGGL(k_argmax_out, dim3(1), dim3(64), 0, st, best, 1, argmax, nullptr);
   }
