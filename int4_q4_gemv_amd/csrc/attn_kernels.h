@@ -803,6 +803,7 @@ constexpr size_t ds_lds_bytes() {
 template <int D, bool MR = false, bool FIN = false>
 __global__ void __launch_bounds__(256) k_fd_ring_ds(AttnArgs a) {
   static_assert(D >= 128 && D <= 512, "a wave takes whole QK k steps");
+  kernarg_fetch<0, 64, 128>();                // the argument lines this kernel reads
   constexpr int VROW = fd_vpitch<D>();
   constexpr int KS = D / 128;                 // QK k steps of a wave
   constexpr int DS = D / 64;                  // PV dim steps of a wave
@@ -1169,6 +1170,7 @@ constexpr int fds_qx_halves() { return 16 * D > 8192 ? 16 * D : 8192; }
 template <int D, bool VR>
 __global__ void __launch_bounds__(512) k_fd_full_ds(AttnArgs a) {
   static_assert(D == 256 || D == 512, "a wave's k steps pair with their RoPE partners");
+  kernarg_fetch<0, 64, 128, 192>();           // the argument lines this kernel reads
   constexpr int G = 2;                        // wave groups
   constexpr int KS = D / 128;                 // QK k steps of a wave (global step w + 4k)
   constexpr int DS = D / 64;                  // PV dim steps of a wave (global DS w + dd)
@@ -1598,6 +1600,9 @@ __global__ void __launch_bounds__(512) k_fd_full_ds(AttnArgs a) {
 }
 
 // out[seq][row][h][d] = sum_s O_s 2^(m_s - M) / sum_s l_s 2^(m_s - M).
+// The output pointers come before the argument struct: after it they would
+// lie in a 64-byte argument line of their own (the struct ends in the
+// positions of the API path), one more memory round trip of the kernel.
 // Grid (n_seq * n_rows * Hq, D / 64), 256 threads: lane = output dim, wave w
 // takes splits w, w + 4, ... (S <= MAXS).  Every load of the workgroup is
 // issued before the first use (split indices past S are clamped and their
@@ -1618,7 +1623,7 @@ constexpr int kMaxSplits = 256;
 constexpr int kMaxTail = 3;                    // rows of a block (at most 4) past its first
 
 template <int D, int MAXS, bool TAIL = false, bool H16 = false>
-__global__ void __launch_bounds__(256) k_fd_combine(AttnArgs a, float* out32, uint16_t* out16) {
+__global__ void __launch_bounds__(256) k_fd_combine(float* out32, uint16_t* out16, AttnArgs a) {
   constexpr int PER = MAXS / 4;
   constexpr int TD = (D + 255) / 256;          // TAIL: head dims per thread
   __shared__ float wsp[MAXS];

@@ -526,6 +526,7 @@ struct ChunkFinArgs {
 // row's position.  The products' S runs are added in order first.
 template <int D>
 __global__ void __launch_bounds__(64) k_chunk_finish(ChunkFinArgs a) {
+  kernarg_fetch<0, 64, 128>();                // the argument lines this kernel reads
   constexpr int FE = D / 64, FEH = fin_h<D>();
   const int row = blockIdx.x, job = blockIdx.y;
   const int lane = threadIdx.x;

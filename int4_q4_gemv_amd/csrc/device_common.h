@@ -109,3 +109,41 @@ Q4_DEV uint32_t f32_order_key(float f) {
   uint32_t u = __builtin_bit_cast(uint32_t, f);
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
+
+// Fetches the 64-byte lines of the kernel's arguments that hold the fields a
+// kernel reads, in one round of scalar loads (one byte offset inside each
+// line), waited for inside the same asm block.  Left to itself the compiler
+// requests the argument fields in several rounds, each waiting for the one
+// before (an early exit test first, or fields far down a large argument
+// struct only where they are used), and every round that touches a line not
+// yet fetched is a memory round trip of its own, ~0.3 us on the path to the
+// kernel's first load.  After this call every argument read is a scalar
+// cache hit.  Call it first in the kernel: the scheduling barrier keeps the
+// kernel's own argument loads after it.
+template <int O0, int O1, int O2>
+Q4_DEV void kernarg_fetch() {
+  const auto kp = __builtin_amdgcn_kernarg_segment_ptr();
+  uint32_t t0, t1, t2;
+  asm volatile(
+      "s_load_dword %0, %3, %4\n\t"
+      "s_load_dword %1, %3, %5\n\t"
+      "s_load_dword %2, %3, %6\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&s"(t0), "=&s"(t1), "=&s"(t2)
+      : "s"(kp), "i"(O0), "i"(O1), "i"(O2));
+  __builtin_amdgcn_sched_barrier(0);          // the kernel's own argument loads stay below
+}
+template <int O0, int O1, int O2, int O3>
+Q4_DEV void kernarg_fetch() {
+  const auto kp = __builtin_amdgcn_kernarg_segment_ptr();
+  uint32_t t0, t1, t2, t3;
+  asm volatile(
+      "s_load_dword %0, %4, %5\n\t"
+      "s_load_dword %1, %4, %6\n\t"
+      "s_load_dword %2, %4, %7\n\t"
+      "s_load_dword %3, %4, %8\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&s"(t0), "=&s"(t1), "=&s"(t2), "=&s"(t3)
+      : "s"(kp), "i"(O0), "i"(O1), "i"(O2), "i"(O3));
+  __builtin_amdgcn_sched_barrier(0);          // the kernel's own argument loads stay below
+}

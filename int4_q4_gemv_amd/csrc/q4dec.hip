@@ -160,15 +160,15 @@ template <int D>
 void launch_combine(const AttnArgs& a, int n_seq, float* out32, uint16_t* out16, hipStream_t st, bool tail = false,
                     bool h16 = false) {
   const dim3 cgrid(n_seq * a.n_rows * a.Hq, D / 64);  // 256 threads each
-  if (h16 && a.S <= 32) hipLaunchKernelGGL((k_fd_combine<D, 32, false, true>), cgrid, dim3(256), 0, st, a, out32, out16);
-  else if (h16 && a.S <= 64) hipLaunchKernelGGL((k_fd_combine<D, 64, false, true>), cgrid, dim3(256), 0, st, a, out32, out16);
-  else if (h16) hipLaunchKernelGGL((k_fd_combine<D, kMaxSplits, false, true>), cgrid, dim3(256), 0, st, a, out32, out16);
-  else if (tail && a.S <= 16) hipLaunchKernelGGL((k_fd_combine<D, 16, true>), cgrid, dim3(256), 0, st, a, out32, out16);
-  else if (tail) hipLaunchKernelGGL((k_fd_combine<D, 32, true>), cgrid, dim3(256), 0, st, a, out32, out16);
-  else if (a.S <= 16) hipLaunchKernelGGL((k_fd_combine<D, 16>), cgrid, dim3(256), 0, st, a, out32, out16);
-  else if (a.S <= 32) hipLaunchKernelGGL((k_fd_combine<D, 32>), cgrid, dim3(256), 0, st, a, out32, out16);
-  else if (a.S <= 64) hipLaunchKernelGGL((k_fd_combine<D, 64>), cgrid, dim3(256), 0, st, a, out32, out16);
-  else hipLaunchKernelGGL((k_fd_combine<D, kMaxSplits>), cgrid, dim3(256), 0, st, a, out32, out16);
+  if (h16 && a.S <= 32) hipLaunchKernelGGL((k_fd_combine<D, 32, false, true>), cgrid, dim3(256), 0, st, out32, out16, a);
+  else if (h16 && a.S <= 64) hipLaunchKernelGGL((k_fd_combine<D, 64, false, true>), cgrid, dim3(256), 0, st, out32, out16, a);
+  else if (h16) hipLaunchKernelGGL((k_fd_combine<D, kMaxSplits, false, true>), cgrid, dim3(256), 0, st, out32, out16, a);
+  else if (tail && a.S <= 16) hipLaunchKernelGGL((k_fd_combine<D, 16, true>), cgrid, dim3(256), 0, st, out32, out16, a);
+  else if (tail) hipLaunchKernelGGL((k_fd_combine<D, 32, true>), cgrid, dim3(256), 0, st, out32, out16, a);
+  else if (a.S <= 16) hipLaunchKernelGGL((k_fd_combine<D, 16>), cgrid, dim3(256), 0, st, out32, out16, a);
+  else if (a.S <= 32) hipLaunchKernelGGL((k_fd_combine<D, 32>), cgrid, dim3(256), 0, st, out32, out16, a);
+  else if (a.S <= 64) hipLaunchKernelGGL((k_fd_combine<D, 64>), cgrid, dim3(256), 0, st, out32, out16, a);
+  else hipLaunchKernelGGL((k_fd_combine<D, kMaxSplits>), cgrid, dim3(256), 0, st, out32, out16, a);
 }
 
 template <int D>
