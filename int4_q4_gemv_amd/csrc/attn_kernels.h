@@ -744,16 +744,6 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D <= 2
   }
 }
 
-// A workgroup barrier that orders LDS only: this wave's LDS operations
-// have completed (lgkmcnt 0) before it arrives.  __syncthreads' release fence
-// would also wait for every global load in flight, the prefetches included.
-Q4_DEV void lds_barrier() {
-  __asm__ __volatile__("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(0xC07F);         // vmcnt 63, expcnt 7, lgkmcnt 0
-  __builtin_amdgcn_s_barrier();
-  __asm__ __volatile__("" ::: "memory");
-}
-
 // The step's first position, read in two parts: pos_issue loads the word
 // that holds it with the step parameters on the device (else any valid word:
 // the records), by a vector load through an address the compiler cannot prove

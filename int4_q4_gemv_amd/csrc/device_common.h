@@ -147,3 +147,13 @@ Q4_DEV void kernarg_fetch() {
       : "s"(kp), "i"(O0), "i"(O1), "i"(O2), "i"(O3));
   __builtin_amdgcn_sched_barrier(0);          // the kernel's own argument loads stay below
 }
+
+// A workgroup barrier that orders LDS only: this wave's LDS operations
+// have completed (lgkmcnt 0) before it arrives.  __syncthreads' release fence
+// would also wait for every global load in flight, the prefetches included.
+Q4_DEV void lds_barrier() {
+  __asm__ __volatile__("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);         // vmcnt 63, expcnt 7, lgkmcnt 0
+  __builtin_amdgcn_s_barrier();
+  __asm__ __volatile__("" ::: "memory");
+}

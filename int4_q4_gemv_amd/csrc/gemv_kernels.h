@@ -66,19 +66,19 @@ struct NormIn {
 
 enum { EPI_STORE = 0, EPI_GATEUP = 1 };
 
+// The fields are ordered without padding holes, so that the arguments fill
+// three 64-byte lines: the kernel reads them in one round, where a fourth
+// line, fetched later, was one more memory round trip of every launch.
 struct GemvArgs {
   GemvSeg seg[3];
   int nseg;
   int K, NQ, W;           // K, quads per row, waves per matrix tile
   int NQs;                // quads per split (blockIdx.y = split; NQ when unsplit)
+  int ra_n;               // read-ahead: float4 per array (below)
   long y_split;           // EPI_STORE: floats between the partial products
   const uint16_t* x;      // fp16 [rows][ldx]
-  int ldx;
   float* y;               // EPI_STORE: fp32 [rows][ldy]
-  int ldy;
   uint16_t* a_out;        // EPI_GATEUP: fp16 [rows][inter] = GELU(gate) * up
-  int inter;
-  int n_rows;             // rows of x (<= B)
   // Read-ahead for the one-workgroup launch that follows (the RMSNorm rows):
   // two fp32 arrays of ra_n float4 (its norm weights) are read by workgroups
   // 0, 8, 16, .. so that they sit in the L2 of the XCD that runs workgroup 0
@@ -86,8 +86,12 @@ struct GemvArgs {
   // contents outlive a launch).  Performance only; NULL: none.
   const float4* ra0;
   const float4* ra1;
-  int ra_n;
+  int ldx;
+  int ldy;
+  int inter;
+  int n_rows;             // rows of x (<= B)
 };
+static_assert(sizeof(GemvArgs) <= 192, "GemvArgs fills at most three 64-byte lines");
 
 Q4_DEV float gelu_tanh(float g) {
   const float k0 = 0.7978845608028654f;
@@ -112,15 +116,18 @@ Q4_DEV void dq_word(uint32_t q, h2_t& v0, h2_t& v1, h2_t& v2, h2_t& v3) {
   v3 = as_h2(and_or(t, 0x00F000F0u, 0x54005400u)) - b64;
 }
 
-// Block-wide sum for any blockDim.x multiple of 64 (<= 1024); red: 16 floats.
-Q4_DEV float block_sum_dyn(float v, float* red) {
+// Block-wide sum of NT threads (NT / 64 waves) in a fixed order, through LDS
+// slots red[0 .. NT/64) that no other sum of the kernel uses (so no barrier
+// guards their reuse), behind a barrier that orders LDS only (the global
+// loads still in flight stay in flight).
+template <int NT>
+Q4_DEV float block_sum_once(float v, float* red) {
   v = wave_sum(v);
-  const int w = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[w] = v;
-  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  lds_barrier();
   float s = 0.f;
-  for (int i = 0; i < nw; i++) s += red[i];
+#pragma unroll
+  for (int i = 0; i < NT / 64; i++) s += red[i];
   return s;
 }
 
@@ -182,6 +189,10 @@ __global__ void __launch_bounds__((B == 1 || FMT == 1) ? 1024 : 512) k_q4_gemv(G
   // unsplit runs) is staged after the weights.
   const int nrow = a.n_rows;
   const int n8 = ldxs / 8;
+  // threads of the workgroup, from the arguments (the launch derives the
+  // block from them too): blockDim is an argument past the struct, in a line
+  // the kernel would fetch on its own
+  const int nthr = 64 * (EPI == EPI_GATEUP ? 2 * a.W : a.W);
   const int kx = qs0 * UC + threadIdx.x * 8;
   u4v xr[B];
 #pragma unroll
@@ -214,7 +225,9 @@ __global__ void __launch_bounds__((B == 1 || FMT == 1) ? 1024 : 512) k_q4_gemv(G
   // of wave 0 of workgroups 0, 8, 16, ..
   float rav = 0.f;
   {
-    const int id = blockIdx.y * gridDim.x + blockIdx.x;
+    // (the launches that read ahead have one segment, whose tiles are the
+    // grid's x extent: the grid size itself is an argument past the struct)
+    const int id = blockIdx.y * sg0.T + blockIdx.x;
     const int line = (id >> 3) * 64 + lane;
     if (a.ra0 && (id & 7) == 0 && threadIdx.x < 64 && line * 4 < a.ra_n)
       rav = a.ra0[line * 4].x + a.ra1[line * 4].x;
@@ -229,7 +242,7 @@ __global__ void __launch_bounds__((B == 1 || FMT == 1) ? 1024 : 512) k_q4_gemv(G
     }
 #pragma unroll
     for (int bb = 0; bb < B; bb++)
-      for (int i = threadIdx.x + blockDim.x; i < n8; i += blockDim.x) {
+      for (int i = threadIdx.x + nthr; i < n8; i += nthr) {
         const int k = qs0 * UC + i * 8;
         u4v v = {0u, 0u, 0u, 0u};
         if (bb < nrow && k < a.K) v = *reinterpret_cast<const u4v*>(a.x + (long)bb * a.ldx + k);
@@ -408,7 +421,7 @@ __global__ void __launch_bounds__(512) k_norm_rows(NormIn p, uint16_t* x) {
   }
   float inv_y = 0.f;
   if (y) {
-    ss = block_sum_dyn(ss, nred);
+    ss = block_sum_once<NT>(ss, nred);
     inv_y = 1.0f / sqrtf(ss / (float)H + p.eps);
   }
   float ss2 = 0.f;
@@ -424,7 +437,7 @@ __global__ void __launch_bounds__(512) k_norm_rows(NormIn p, uint16_t* x) {
       ss2 += v * v;
     }
   }
-  ss2 = block_sum_dyn(ss2, nred);
+  ss2 = block_sum_once<NT>(ss2, nred + NT / 64);
   const float inv_h = 1.0f / sqrtf(ss2 / (float)H + p.eps);
   float4* hd = p.h_dst ? reinterpret_cast<float4*>(p.h_dst + (long)b * H) : nullptr;
   uint2* xo = reinterpret_cast<uint2*>(x + (long)b * H);

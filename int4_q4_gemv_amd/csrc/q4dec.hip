@@ -74,19 +74,20 @@ GemvPlan gemv_plan(int N, int K, int max_waves, int split_cols = 0, int fmt = 0)
 
 size_t gemv_lds(int B, const GemvPlan& p) { return (size_t)B * (p.NQs * unit_cols(p.fmt) + (B > 1 ? 8 : 0)) * 2; }
 
-// grid: (tiles, splits); waves: per workgroup (both halves for EPI_GATEUP)
+// grid: (tiles, splits); block: a.W waves (2 a.W for EPI_GATEUP, both
+// halves), as the kernel assumes
 template <int B, int EPI, int FMT>
-void launch_gemv_f(const GemvArgs& a, const GemvPlan& p, int tiles, int waves, size_t lds, hipStream_t st) {
-  const dim3 g(tiles, p.S), blk(64 * waves);
+void launch_gemv_f(const GemvArgs& a, const GemvPlan& p, int tiles, size_t lds, hipStream_t st) {
+  const dim3 g(tiles, p.S), blk(64 * (EPI == EPI_GATEUP ? 2 * a.W : a.W));
   if (p.CQ == 16) hipLaunchKernelGGL((k_q4_gemv<B, EPI, 16, FMT>), g, blk, lds, st, a);
   else if (p.CQ == 8) hipLaunchKernelGGL((k_q4_gemv<B, EPI, 8, FMT>), g, blk, lds, st, a);
   else hipLaunchKernelGGL((k_q4_gemv<B, EPI, 4, FMT>), g, blk, lds, st, a);
 }
 
 template <int B, int EPI>
-void launch_gemv(const GemvArgs& a, const GemvPlan& p, int tiles, int waves, size_t lds, hipStream_t st) {
-  if (p.fmt == 0) launch_gemv_f<B, EPI, 0>(a, p, tiles, waves, lds, st);
-  else launch_gemv_f<B, EPI, 1>(a, p, tiles, waves, lds, st);
+void launch_gemv(const GemvArgs& a, const GemvPlan& p, int tiles, size_t lds, hipStream_t st) {
+  if (p.fmt == 0) launch_gemv_f<B, EPI, 0>(a, p, tiles, lds, st);
+  else launch_gemv_f<B, EPI, 1>(a, p, tiles, lds, st);
 }
 
 void fill_seg(GemvSeg& s, const void* packed, int N, int K, int tile0, int out_off, int fmt = 0) {
@@ -502,7 +503,7 @@ q4_status enqueue_layers(const q4dec_model* m, const StepLayout& L, const StepPt
       a.K = H; a.NQ = pl.NQ; a.W = pl.W; a.NQs = pl.NQs;
       a.x = P.xf; a.ldx = H;
       a.y = P.qkv; a.ldy = L.qkv_ld; a.n_rows = n;
-      launch_gemv<B, EPI_STORE>(a, pl, t0, pl.W, gemv_lds(B, pl), st);
+      launch_gemv<B, EPI_STORE>(a, pl, t0, gemv_lds(B, pl), st);
     }
     // ---- attention: q/k/v finishing, split-K partials, combine
     const bool vrow = full && m->kv_format == 1;
@@ -548,7 +549,7 @@ q4_status enqueue_layers(const q4dec_model* m, const StepLayout& L, const StepPt
       a.ra0 = reinterpret_cast<const float4*>(ly.post_attn_norm);   // read by the next norm
       a.ra1 = reinterpret_cast<const float4*>(ly.pre_ff_norm);
       a.ra_n = H / 4;
-      launch_gemv<B, EPI_STORE>(a, pl, a.seg[0].T, pl.W, gemv_lds(B, pl), st);
+      launch_gemv<B, EPI_STORE>(a, pl, a.seg[0].T, gemv_lds(B, pl), st);
     }
     // ---- gate/up with GELU(gate) * up; post-attention residual + pre-FF norm in the prologue
     if (!gemvs_only) {
@@ -565,7 +566,7 @@ q4_status enqueue_layers(const q4dec_model* m, const StepLayout& L, const StepPt
       a.K = H; a.NQ = pl.NQ; a.W = pl.W; a.NQs = pl.NQs;
       a.x = P.xf2; a.ldx = H;
       a.a_out = P.a; a.inter = I; a.n_rows = n;
-      launch_gemv<B, EPI_GATEUP>(a, pl, a.seg[0].T, 2 * pl.W, gemv_lds(B, pl), st);
+      launch_gemv<B, EPI_GATEUP>(a, pl, a.seg[0].T, gemv_lds(B, pl), st);
     }
     // ---- down projection
     {
@@ -579,7 +580,7 @@ q4_status enqueue_layers(const q4dec_model* m, const StepLayout& L, const StepPt
       a.ra0 = reinterpret_cast<const float4*>(ly.post_ff_norm);      // read by the next norm
       a.ra1 = reinterpret_cast<const float4*>(l + 1 < m->n_layers ? m->layers[l + 1].attn_norm : m->final_norm);
       a.ra_n = H / 4;
-      launch_gemv<B, EPI_STORE>(a, pl, a.seg[0].T, pl.W, gemv_lds(B, pl), st);
+      launch_gemv<B, EPI_STORE>(a, pl, a.seg[0].T, gemv_lds(B, pl), st);
     }
   }
   if (gemvs_only) return launch_status();
@@ -1143,8 +1144,8 @@ q4_status q4_gemv(const void* packed, int N, int K, const uint16_t* x, int B, fl
   a.nseg = 1;
   a.K = K; a.NQ = p.NQ; a.W = p.W; a.NQs = p.NQs;
   a.x = x; a.ldx = K; a.y = y; a.ldy = N; a.n_rows = B;
-  if (B == 1) launch_gemv<1, EPI_STORE>(a, p, p.T, p.W, gemv_lds(1, p), S(stream));
-  else launch_gemv<4, EPI_STORE>(a, p, p.T, p.W, gemv_lds(4, p), S(stream));
+  if (B == 1) launch_gemv<1, EPI_STORE>(a, p, p.T, gemv_lds(1, p), S(stream));
+  else launch_gemv<4, EPI_STORE>(a, p, p.T, gemv_lds(4, p), S(stream));
   return launch_status();
 }
 
@@ -1202,8 +1203,8 @@ q4_status q8_gemv(const void* packed, int N, int K, const uint16_t* x, int B, fl
   a.nseg = 1;
   a.K = K; a.NQ = p.NQ; a.W = p.W; a.NQs = p.NQs;
   a.x = x; a.ldx = K; a.y = y; a.ldy = N; a.n_rows = B;
-  if (B == 1) launch_gemv<1, EPI_STORE>(a, p, p.T, p.W, gemv_lds(1, p), S(stream));
-  else launch_gemv<4, EPI_STORE>(a, p, p.T, p.W, gemv_lds(4, p), S(stream));
+  if (B == 1) launch_gemv<1, EPI_STORE>(a, p, p.T, gemv_lds(1, p), S(stream));
+  else launch_gemv<4, EPI_STORE>(a, p, p.T, gemv_lds(4, p), S(stream));
   return launch_status();
 }
 
