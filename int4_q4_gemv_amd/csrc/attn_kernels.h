@@ -809,25 +809,29 @@ __global__ void __launch_bounds__(256) k_fd_ring_ds(AttnArgs a) {
   uint16_t* newV = nkv + 4 * D;
   static_assert(ds_lds_bytes<D>() <= 160 * 1024, "LDS of one workgroup");
 
+  // ---- the step's first position, issued before anything else (a valid
+  // word for every workgroup, so also ahead of the early exit below)
+  const int pos_w = pos_issue(a);
+
   const int split = a.kvh_major ? blockIdx.y : blockIdx.x, kvh = a.kvh_major ? blockIdx.x : blockIdx.y;
-  // rows of this workgroup: row .. rlast (one unless MR); its columns
+  // rows of this workgroup: row .. rlast (one unless MR); its columns.  All
+  // the rows in one workgroup (or one row): no division ahead of the loads
   const int rpw = MR && a.rpw > 1 ? a.rpw : 1;
-  int seq, row;
-  if constexpr (MR) {
-    const int nrg = (a.n_rows + rpw - 1) / rpw;
-    seq = blockIdx.z / nrg;
-    row = (blockIdx.z - seq * nrg) * rpw;
-  } else {
-    seq = blockIdx.z / a.n_rows;
-    row = blockIdx.z - seq * a.n_rows;
+  int seq = blockIdx.z, row = 0;
+  if (a.n_rows > rpw) {
+    if constexpr (MR) {
+      const int nrg = (a.n_rows + rpw - 1) / rpw;
+      seq = blockIdx.z / nrg;
+      row = (blockIdx.z - seq * nrg) * rpw;
+    } else {
+      seq = blockIdx.z / a.n_rows;
+      row = blockIdx.z - seq * a.n_rows;
+    }
   }
   if (row >= a.n_rows) return;
   const int rlast = MR ? min(a.n_rows, row + rpw) - 1 : row;
   const int ncols = a.GQ * (rlast - row + 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-
-  // ---- the step's first position, issued first
-  const int pos_w = pos_issue(a);
 
   // ---- inputs of the finishing prologue (FIN): jobs dealt round-robin to
   // the waves (this workgroup's columns, then k and v of rows 0 .. rlast).
@@ -1184,14 +1188,18 @@ __global__ void __launch_bounds__(512) k_fd_full_ds(AttnArgs a) {
   f4_t* sx = reinterpret_cast<f4_t*>(qx);     // [G][4 waves][2][64] partial scores
   auto rebuilt = [](int s) { return VR && (s < RS || (s >= HS && s < HS + RS)); };
 
+  const int pos_w = pos_issue(a);             // the step's first position, issued first
+
   const int split = blockIdx.x, kvh = blockIdx.y;
-  const int seq = blockIdx.z / a.n_rows, row = blockIdx.z - seq * a.n_rows;
+  int seq = blockIdx.z, row = 0;              // one row: no division ahead of the loads
+  if (a.n_rows > 1) {
+    seq = blockIdx.z / a.n_rows;
+    row = blockIdx.z - seq * a.n_rows;
+  }
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int grp = wave >> 2, w = wave & 3;
   const int j = lane & 15, g = lane >> 4;
   const bool col_ok = j < a.GQ;
-
-  const int pos_w = pos_issue(a);             // the step's first position, issued first
 
   // ---- queries of a call without the finishing prologue: issued first, so
   // that no K/V load is ahead of them
@@ -1593,7 +1601,7 @@ __global__ void __launch_bounds__(512) k_fd_full_ds(AttnArgs a) {
 // The output pointers come before the argument struct: after it they would
 // lie in a 64-byte argument line of their own (the struct ends in the
 // positions of the API path), one more memory round trip of the kernel.
-// Grid (n_seq * n_rows * Hq, D / 64), 256 threads: lane = output dim, wave w
+// Grid (Hkv, GQ, n_seq * n_rows * D / 64), 256 threads: lane = output dim, wave w
 // takes splits w, w + 4, ... (S <= MAXS).  Every load of the workgroup is
 // issued before the first use (split indices past S are clamped and their
 // weight is zero), and the four wave sums meet in LDS in a fixed order.
@@ -1621,23 +1629,37 @@ __global__ void __launch_bounds__(256) k_fd_combine(float* out32, uint16_t* out1
   __shared__ float rm[4], rl[4];
   __shared__ float tred[4][kMaxTail];
   const int pos_w = TAIL ? pos_issue(a) : 0;
-  const int idx = blockIdx.x;
-  const int h = a.kvh_major ? (idx % a.Hkv) * a.GQ + (idx / a.Hkv) % a.GQ : idx % a.Hq, sr = idx / a.Hq;
-  const int seq = sr / a.n_rows, row = sr - seq * a.n_rows;
-  const int kvh = h / a.GQ, col = h - kvh * a.GQ;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const long r0 = attn_rec(a, seq, row, kvh, 0, col, D);
-  const long rs = (long)a.GQ * (D + 4);                // stride between splits
-  const int d = blockIdx.y * 64 + lane;
+  // grid (Hkv, GQ, rows x D / 64), KV heads fastest: with 8 KV heads the
+  // workgroups of one KV head run on the XCD whose L2 holds its records (the
+  // ring partial enumerates KV heads fastest too; workgroups go round-robin
+  // over the 8 XCDs).  No index needs a division by a runtime value but the
+  // row's, and only with several rows: the divisions otherwise ran ahead of
+  // the first load
+  constexpr int NDC = D / 64;
+  const int kvh = blockIdx.x, col = blockIdx.y, h = kvh * a.GQ + col;
+  const int sr = blockIdx.z / NDC, dc = blockIdx.z % NDC;
+  int seq = sr, row = 0;
+  if (a.n_rows > 1) {
+    seq = sr / a.n_rows;
+    row = sr - seq * a.n_rows;
+  }
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // one scalar base and 32-bit offsets (a split's records lie rs floats
+  // apart, S rs < 2^31): the split index of each load is wave-uniform, so
+  // its offset is scalar arithmetic, not a per-lane 64-bit multiply
+  const float* rb = a.part + attn_rec(a, seq, row, kvh, 0, col, D);
+  const int rs = a.GQ * (D + 4);                       // stride between splits
+  const int d = dc * 64 + lane;
   const int S = a.S;
   const bool own = tid < S;
-  const long mo = r0 + (long)min(tid, S - 1) * rs + D;
-  const float m_raw = a.part[mo], l_raw = a.part[mo + 1];
+  const unsigned mo = (unsigned)(min(tid, S - 1) * rs + D);
+  const float m_raw = rb[mo], l_raw = rb[mo + 1];
   float ov[PER];
 #pragma unroll
   for (int i = 0; i < PER; i++) {
-    const long ro = r0 + (long)min(wave + 4 * i, S - 1) * rs;
-    ov[i] = H16 ? h2f(reinterpret_cast<const uint16_t*>(a.part + ro)[d]) : a.part[ro + d];
+    const unsigned ro = (unsigned)(min(wave + 4 * i, S - 1) * rs);
+    ov[i] = H16 ? h2f(reinterpret_cast<const uint16_t*>(rb + ro)[d]) : rb[ro + d];
   }
   // TAIL: the query, and the keys and this lane's V elements of the rows
   // past the group's first

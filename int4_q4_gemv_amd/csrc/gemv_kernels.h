@@ -160,7 +160,7 @@ __global__ void __launch_bounds__((B == 1 || FMT == 1) ? 1024 : 512) k_q4_gemv(G
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int g = lane >> 4;
-  const int half = (EPI == EPI_GATEUP) ? wave / a.W : 0;
+  const int half = (EPI == EPI_GATEUP && wave >= a.W) ? 1 : 0;   // wave < 2 W
   const int wq = wave - half * a.W;
   const int tile = blockIdx.x, split = blockIdx.y;
   // every segment descriptor is read in one round of scalar loads and the

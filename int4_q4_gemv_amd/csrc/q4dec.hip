@@ -160,7 +160,7 @@ q4_status set_attrs() {
 template <int D>
 void launch_combine(const AttnArgs& a, int n_seq, float* out32, uint16_t* out16, hipStream_t st, bool tail = false,
                     bool h16 = false) {
-  const dim3 cgrid(n_seq * a.n_rows * a.Hq, D / 64);  // 256 threads each
+  const dim3 cgrid(a.Hkv, a.GQ, n_seq * a.n_rows * (D / 64));  // 256 threads each
   if (h16 && a.S <= 32) hipLaunchKernelGGL((k_fd_combine<D, 32, false, true>), cgrid, dim3(256), 0, st, out32, out16, a);
   else if (h16 && a.S <= 64) hipLaunchKernelGGL((k_fd_combine<D, 64, false, true>), cgrid, dim3(256), 0, st, out32, out16, a);
   else if (h16) hipLaunchKernelGGL((k_fd_combine<D, kMaxSplits, false, true>), cgrid, dim3(256), 0, st, out32, out16, a);
