@@ -378,28 +378,31 @@ __global__ void __launch_bounds__(512) k_norm_rows(NormIn p, uint16_t* x) {
   __shared__ float nred[16];
   const int b = blockIdx.x;               // grid: the rows of the step
   const int H = p.H, tid = threadIdx.x, n4 = H / 4;
-  const float* y = p.y ? p.y + (long)b * H : nullptr;
-  const float4* hs = reinterpret_cast<const float4*>(p.h_src + (long)b * H);
-  const float4* y0 = y ? reinterpret_cast<const float4*>(y) : hs;
-  const long ys4 = p.y_split / 4;
-  const float4* yp[MAXY];
+  // scalar bases and 32-bit element offsets (rows x H and the partials'
+  // stride stay far below 2^31): 64-bit pointer arithmetic per partial took
+  // most of the scalar instructions ahead of the first load
+  const bool hy = p.y != nullptr;
+  const float* y = hy ? p.y : nullptr;
+  const float* ybase = hy ? p.y : p.h_src;   // partials past ny read the residual, times 0
+  const unsigned rb = (unsigned)(b * H);     // this row's first element
+  const unsigned ys = (unsigned)p.y_split;
+  unsigned yo[MAXY];
   float mj[MAXY];
 #pragma unroll
   for (int j = 0; j < MAXY; j++) {
-    yp[j] = p.ny > j ? y0 + j * ys4 : y0;
+    yo[j] = p.ny > j ? j * ys : 0u;
     mj[j] = p.ny > j ? 1.f : 0.f;
   }
-  const float4* wp4 = reinterpret_cast<const float4*>(y ? p.w_post : p.w_in);
-  const float4* wi4 = reinterpret_cast<const float4*>(p.w_in);
+  const float* wpb = hy ? p.w_post : p.w_in;
   float4 hv[C], ay[MAXY][C], wp[C], wi[C];
 #pragma unroll
   for (int c = 0; c < C; c++) {
-    const int k = min(tid + NT * c, n4 - 1);
-    hv[c] = hs[k];
+    const unsigned k4 = 4u * (unsigned)min(tid + NT * c, n4 - 1);
+    hv[c] = *reinterpret_cast<const float4*>(p.h_src + (rb + k4));
 #pragma unroll
-    for (int j = 0; j < MAXY; j++) ay[j][c] = yp[j][k];
-    wp[c] = wp4[k];
-    wi[c] = wi4[k];
+    for (int j = 0; j < MAXY; j++) ay[j][c] = *reinterpret_cast<const float4*>(ybase + (yo[j] + rb + k4));
+    wp[c] = *reinterpret_cast<const float4*>(wpb + k4);
+    wi[c] = *reinterpret_cast<const float4*>(p.w_in + k4);
   }
   __builtin_amdgcn_sched_barrier(0);
   // partial sums in the order ((a0 + a1) + a2) + ..; out-of-range elements 0
