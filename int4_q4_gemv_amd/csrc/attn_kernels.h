@@ -1127,16 +1127,20 @@ __global__ void __launch_bounds__(256) k_fd_ring_ds(AttnArgs a) {
 // forms O for its own D/4 dims.  At the end group 1 hands its rescaled O to
 // group 0 through LDS, which writes the split's records.
 //
-// Loads in flight: V rows go straight to LDS two rounds ahead (the even
-// rounds' tiles in one array, the odd rounds' in another, each refilled once
-// the round reading it has passed its last barrier), K elements to registers
-// one round ahead (issued as soon as the round's scores are formed).  With
-// one row per position the keys are read from the tile's V rows in LDS once
-// every wave's rows have landed, so the cache is read once and no key load
-// is on the round's path.  The V
-// arrays are LDS objects of their own: the compiler then knows that the LDS
-// accesses to the scores, the queries and the step's rows do not touch the
-// rows still arriving, and waits for those only where they are read.  Every
+// Loads in flight: a round's K elements (to registers) and V rows (straight
+// to LDS) are issued as soon as the previous round's scores are formed, so
+// they arrive during that round's softmax and PV; the even rounds' V rows
+// sit in one array, the odd rounds' in another.  A round starts by waiting
+// for all of its wave's loads, then a barrier.  With one row per position the
+// keys are read from the tile's V rows in LDS once every wave's rows have
+// landed, so the cache is read once and no key load is on the round's path.
+// The V arrays are LDS objects of their own, and the direct loads and the PV
+// reads go through restrict pointers (lds_dma16, lds_tr8): the compiler then
+// knows that the LDS accesses to the scores, the queries, the step's rows
+// and the round's own V rows do not touch the rows still arriving in the
+// other array, and does not wait for those (it otherwise waited for every
+// load in flight before the PV reads, so the next round's tiles could not
+// overlap this round's PV).  Every
 // round issues the same loads whether or not the group has such a tile
 // (without one, all lanes read row 0: one line per instruction), so the
 // count of loads in flight, and with it each wait, is the same on every path.
@@ -1160,6 +1164,26 @@ template <int N> struct fds_ic { static constexpr int v = N; };
 // queries [16][D], reused for the partial scores [2 groups][4 waves][2][64] float4
 template <int D>
 constexpr int fds_qx_halves() { return 16 * D > 8192 ? 16 * D : 8192; }
+
+// LDS accesses through restrict pointers of inlined helpers carry alias-scope
+// metadata, which the compiler's wait insertion needs before it will tell a
+// read of one LDS buffer from a direct-to-LDS load into another buffer (it
+// then waits for the loads into the buffer read only; without the metadata it
+// waits for every direct load in flight).  The waits that make a buffer's
+// loads complete before it is read stay explicit in the kernels.
+// One 16-byte direct-to-LDS load per lane.
+__device__ __attribute__((always_inline)) inline void lds_dma16(const uint16_t* src, uint16_t* __restrict__ dst) {
+  __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint32_t*>(src), reinterpret_cast<uint32_t*>(dst), 16, 0, 0);
+}
+// Transposing reads of two 4 x 16-bit groups (rows p and p + off_hi) as one
+// 8-half MFMA operand.
+__device__ __attribute__((always_inline)) inline h8_t lds_tr8(const uint16_t* __restrict__ p, int off_hi) {
+  typedef short s4_t __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) s4_t lds_s4;
+  const s4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(p));
+  const s4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(p + off_hi));
+  return __builtin_bit_cast(h8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
 
 template <int D, bool VR>
 __global__ void __launch_bounds__(512) k_fd_full_ds(AttnArgs a) {
@@ -1299,13 +1323,11 @@ __global__ void __launch_bounds__(512) k_fd_full_ds(AttnArgs a) {
     for (int i = 0; i < NVS; i++) {
       const int r0 = 8 * w + RPI * i, r = r0 + rl;
       const uint16_t* src = real ? vb + row_at(t0, r) + (pc ^ (2 * fds_swz(r))) * 8 : vb;
-      __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint32_t*>(src),
-                                       reinterpret_cast<uint32_t*>(vl + r0 * D), 16, 0, 0);
+      lds_dma16(src, vl + r0 * D);
     }
   };
   load_k(tile0(grp), grp < ntile);
   load_v(vA, tile0(grp), grp < ntile);
-  load_v(vB, tile0(grp + G), grp + G < ntile);
   if constexpr (VR) {
     const int i = threadIdx.x;
     if (i < NR) {
@@ -1395,9 +1417,9 @@ __global__ void __launch_bounds__(512) k_fd_full_ds(AttnArgs a) {
     const int ti = G * rd + grp;
     const bool act = ti < ntile;              // group-uniform
     const int t0 = tile0(ti);
-    // this round's K and V rows have landed; the next round's V rows (the
-    // youngest loads) may stay in flight
-    wait_vm<NVS>();
+    // this round's K and V rows have landed (they were issued with the last
+    // round's scores; nothing of the next round is in flight yet)
+    wait_vm<0>();
     if constexpr (VR) {
       lds_barrier();                          // every wave's V rows of the tile are in
       if (act) lds_k(vl);
@@ -1462,7 +1484,13 @@ __global__ void __launch_bounds__(512) k_fd_full_ds(AttnArgs a) {
       sxw[lane] = p0;
       sxw[64 + lane] = p1;
     }
-    load_k(tile0(ti + G), ti + G < ntile);    // the registers are free once the scores are formed
+    // the next round's K and V rows, in flight through this round's softmax
+    // and PV: the K registers are free once the scores are formed, and the
+    // other V buffer since the last round's final barrier (its direct loads
+    // do not hold up the PV reads of this buffer: both go through restrict
+    // pointers, lds_dma16 and lds_tr8)
+    load_k(tile0(ti + G), ti + G < ntile);
+    load_v(b ? vA : vB, tile0(ti + G), ti + G < ntile);
     lds_barrier();
     if (act) {
       // full scores: the group's 4 parts added in a fixed order
@@ -1513,18 +1541,13 @@ __global__ void __launch_bounds__(512) k_fd_full_ds(AttnArgs a) {
       const uint16_t* vt = vl + (8 * g + (j >> 2)) * D + 4 * (j & 3);
 #pragma unroll
       for (int dd = 0; dd < DS; dd++) {
-        typedef short v4s_t __attribute__((ext_vector_type(4)));
-        typedef __attribute__((address_space(3))) v4s_t lds_v4s;
         const int cd = 16 * ((DS * w + dd) ^ sw);
-        const v4s_t vlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(vt + cd));
-        const v4s_t vhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(vt + 4 * D + cd));
-        const h8_t Bv = __builtin_bit_cast(h8_t, __builtin_shufflevector(vlo, vhi, 0, 1, 2, 3, 4, 5, 6, 7));
+        const h8_t Bv = lds_tr8(vt + cd, 4 * D);
         O[dd] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ahi, Bv, O[dd], 0, 0, 0);
         O[dd] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Alo, Bv, O[dd], 0, 0, 0);
       }
     }
     lds_barrier();                            // these V rows and the scores are free again
-    load_v(X, tile0(ti + 2 * G), ti + 2 * G < ntile);
   };
   for (int rd = 0; rd < nround; rd += 2) {
     body(fds_ic<0>{}, rd);
