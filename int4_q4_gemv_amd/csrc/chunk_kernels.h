@@ -470,15 +470,12 @@ struct ChunkEmbedArgs {
   int H;
   float emb_scale;         // sqrt(H)
   float* h;                // [n][H]
-  unsigned long long* best;  // [4] argmax slots of the head
   int tokens[kChunkRows];
 };
 
-// One workgroup per row: h = fp32(E[token]) * sqrt(H); workgroup 0 also
-// clears the head's argmax slots.
+// One workgroup per row: h = fp32(E[token]) * sqrt(H).
 __global__ void __launch_bounds__(256) k_chunk_embed(ChunkEmbedArgs a) {
   const int b = blockIdx.x;
-  if (b == 0 && threadIdx.x < 4) a.best[threadIdx.x] = 0ull;
   const uint16_t* e = a.E + (long)a.tokens[b] * a.H;
   float* h = a.h + (long)b * a.H;
   for (int i = threadIdx.x; i < a.H; i += 256) h[i] = h2f(e[i]) * a.emb_scale;

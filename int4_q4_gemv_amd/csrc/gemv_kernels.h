@@ -461,9 +461,13 @@ __global__ void __launch_bounds__(512) k_norm_rows(NormIn p, uint16_t* x) {
 // ------------------------------------------------------- fp16 tied head ----
 // z[b][r] = E[r] . x[b]; logits = c * tanh(z / c); greedy argmax with the
 // lowest index on ties (gemma4-12b card: tied embeddings, final softcap;
-// 128k card, Limitations: the head emits a greedy argmax id).  The argmax is
-// reduced with 64-bit atomicMax on (order key << 32 | ~index) and read out by
-// k_argmax_out after the kernel.
+// 128k card, Limitations: the head emits a greedy argmax id).  Each
+// workgroup stores its largest (order key << 32 | ~index) per row to a slot
+// of its own, and k_argmax_out takes the maximum over the workgroups (one
+// atomicMax per workgroup on a single word serialised ~1000 atomics at the
+// kernel's end).  The maximum does not depend on the order, so the lowest
+// index still wins ties.
+constexpr int kHeadSlots = 4096;   // head workgroups at most (slots of 4 rows each)
 struct HeadArgs {
   const uint16_t* E;       // [V][H]
   const uint16_t* x;       // [4][H]
@@ -471,7 +475,7 @@ struct HeadArgs {
   float softcap;
   float* logits;           // [n][V] or NULL (when sp is NULL)
   const StepParams* sp;    // decode step: the logits pointer is read from here
-  unsigned long long* best;  // [4], zeroed before the kernel
+  unsigned long long* best;  // [gridDim.x][4]: each workgroup's best key per row
   int n_rows;
 };
 
@@ -549,20 +553,41 @@ __global__ void __launch_bounds__(256) k_head(HeadArgs a) {
   if (threadIdx.x < B && threadIdx.x < n) {
     unsigned long long m = 0ull;
     for (int w = 0; w < 4; w++) m = sbest[w][threadIdx.x] > m ? sbest[w][threadIdx.x] : m;
-    atomicMax(a.best + threadIdx.x, m);
+    a.best[(long)blockIdx.x * 4 + threadIdx.x] = m;
   }
 }
 
-// Reads the argmax slots out and clears them for the next step (the output
-// from sp when it is set, else argmax).
-__global__ void k_argmax_out(unsigned long long* best, int n_rows, int32_t* argmax, const StepParams* sp) {
-  const int n = n_rows;
-  const int i = threadIdx.x;
+// The greedy id of each row from the head's per-workgroup slots (nb
+// workgroups; the output from sp when it is set, else argmax).  The slots are
+// written whole by every head launch, so nothing is cleared.
+__global__ void __launch_bounds__(256) k_argmax_out(const unsigned long long* best, int nb, int n_rows,
+                                                     int32_t* argmax, const StepParams* sp) {
+  // the maximum of the nb workgroups' keys per row (256 threads, every load
+  // issued before the first maximum), then the index it holds
+  __shared__ unsigned long long red[4][4];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   if (sp) argmax = sp->argmax;
-  if (i < 4) {
-    const unsigned long long m = best[i];
-    best[i] = 0ull;
-    if (i < n && argmax) argmax[i] = (int32_t)(0xFFFFFFFFu - (uint32_t)(m & 0xFFFFFFFFull));
+  unsigned long long m[4] = {0ull, 0ull, 0ull, 0ull};
+  for (int i = tid; i < nb; i += 256)
+#pragma unroll
+    for (int r = 0; r < 4; r++) {
+      const unsigned long long v = r < n_rows ? best[(long)i * 4 + r] : 0ull;
+      m[r] = v > m[r] ? v : m[r];
+    }
+#pragma unroll
+  for (int r = 0; r < 4; r++) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const unsigned long long v = __shfl_xor(m[r], o, 64);
+      m[r] = v > m[r] ? v : m[r];
+    }
+    if (lane == 0) red[wave][r] = m[r];
+  }
+  __syncthreads();
+  if (tid < 4 && tid < n_rows && argmax) {
+    unsigned long long k = 0ull;
+    for (int w = 0; w < 4; w++) k = red[w][tid] > k ? red[w][tid] : k;
+    argmax[tid] = (int32_t)(0xFFFFFFFFu - (uint32_t)(k & 0xFFFFFFFFull));
   }
 }
 

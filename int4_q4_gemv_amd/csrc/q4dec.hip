@@ -209,7 +209,9 @@ int num_cus() {
 // (per_cu of them per CU: 4 at batch 1, 2 at batch 4, by the kernel's
 // registers), so that none starts after the first have finished; each wave
 // takes two rows per iteration
-int head_grid(long vocab, int per_cu) { return (int)std::min<long>((long)num_cus() * per_cu, ceil_div(vocab, 8)); }
+int head_grid(long vocab, int per_cu) {
+  return (int)std::min<long>(std::min<long>((long)num_cus() * per_cu, ceil_div(vocab, 8)), kHeadSlots);
+}
 
 // The chunk's full layers: 4 rows per workgroup over shared K/V tiles, then
 // the combine.
@@ -358,7 +360,7 @@ StepLayout step_layout(const q4dec_model* m) {
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off = align256(off + bytes); return o; };
   L.sp = take(sizeof(StepParams));
-  L.best = take(sizeof(unsigned long long) * 4);
+  L.best = take(sizeof(unsigned long long) * 4 * kHeadSlots);   // the head's per-workgroup slots
   L.rope = take(sizeof(float2) * kMaxRows * (Ds / 2 + Df / 2));
   L.hA = take(sizeof(float) * kMaxRows * H);
   L.hB = take(sizeof(float) * kMaxRows * H);
@@ -599,7 +601,7 @@ q4_status enqueue_layers(const q4dec_model* m, const StepLayout& L, const StepPt
     a.sp = P.sp; a.best = P.best; a.n_rows = n;
     const int grid = head_grid(m->vocab, B == 1 ? 4 : 2);
     hipLaunchKernelGGL((k_head<B>), dim3(grid), dim3(256), 0, st, a);
-    hipLaunchKernelGGL(k_argmax_out, dim3(1), dim3(64), 0, st, P.best, n, nullptr, P.sp);
+    hipLaunchKernelGGL(k_argmax_out, dim3(1), dim3(256), 0, st, P.best, grid, n, nullptr, P.sp);
   }
   return launch_status();
 }
@@ -710,7 +712,6 @@ q4_status begin_step(const q4dec_model* m, const StepPtrs& P, const int32_t* tok
   b.sp = P.sp; b.pos0 = pos0; b.n = n;
   b.logits = logits; b.argmax = argmax;
   for (int i = 0; i < 4; i++) b.tokens[i] = i < n ? tokens[i] : 0;
-  b.best = P.best;
   b.E = m->embed; b.H = m->hidden; b.emb_scale = (float)std::sqrt((double)m->hidden);
   b.h = P.hA;
   b.rope_cs = P.rope; b.ns = m->sl_rot_pairs; b.nf = m->full_rot_pairs;
@@ -769,7 +770,7 @@ ChunkLayout chunk_layout(const q4dec_model* m) {
   const int Sq = std::max(L.p_qkv_s.S, L.p_qkv_f.S);
   size_t off = 0;
   auto take = [&](size_t bytes) { const size_t o = off; off = align256(off + bytes); return o; };
-  L.best = take(sizeof(unsigned long long) * 4);
+  L.best = take(sizeof(unsigned long long) * 4 * kHeadSlots);   // the head's per-workgroup slots
   L.hA = take(sizeof(float) * R * H);
   L.hB = take(sizeof(float) * R * H);
   L.qkv = take(sizeof(float) * Sq * R * L.qkv_ld);
@@ -816,7 +817,7 @@ q4_status enqueue_chunk(const q4dec_model* m, const ChunkLayout& L, void* ws, co
   const int H = m->hidden, I = m->inter, Hq = m->n_heads;
   {
     ChunkEmbedArgs e{};
-    e.E = m->embed; e.H = H; e.emb_scale = std::sqrt((float)H); e.h = hA; e.best = best;
+    e.E = m->embed; e.H = H; e.emb_scale = std::sqrt((float)H); e.h = hA;
     for (int i = 0; i < n; i++) e.tokens[i] = tokens[i];
     hipLaunchKernelGGL(k_chunk_embed, dim3(n), dim3(256), 0, st, e);
   }
@@ -960,7 +961,7 @@ q4_status enqueue_chunk(const q4dec_model* m, const ChunkLayout& L, void* ws, co
     a.logits = logits; a.best = best; a.n_rows = 1;
     const int grid = head_grid(m->vocab, 4);
     hipLaunchKernelGGL((k_head<1>), dim3(grid), dim3(256), 0, st, a);
-    hipLaunchKernelGGL(k_argmax_out, dim3(1), dim3(64), 0, st, best, 1, argmax, nullptr);
+    hipLaunchKernelGGL(k_argmax_out, dim3(1), dim3(256), 0, st, best, grid, 1, argmax, nullptr);
   }
   return launch_status();
 }

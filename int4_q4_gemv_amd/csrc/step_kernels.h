@@ -12,7 +12,6 @@ struct BeginArgs {
   int tokens[4];
   float* logits;            // the step's outputs, published in sp
   int32_t* argmax;
-  unsigned long long* best; // [4] argmax slots
   const uint16_t* E;        // [vocab][H] fp16
   int H;
   float emb_scale;          // sqrt(H)
@@ -47,7 +46,6 @@ __global__ void __launch_bounds__(256) k_step_begin(BeginArgs a) {
       a.sp->logits = a.logits;
       a.sp->argmax = a.argmax;
     }
-    if (tid < 4) a.best[tid] = 0ull;
   }
   // every pair slot of both kinds is written (pairs past rot_pairs, which
   // are not rotated, get (1, 0)), so readers may load whole runs of it
