@@ -69,41 +69,6 @@ Q4_DEV float wave_max(float v) {
   return fmaxf(fmaxf(lane_f(v, 15), lane_f(v, 31)), fmaxf(lane_f(v, 47), lane_f(v, 63)));
 }
 
-// Block-wide sum for blockDim.x == NT (multiple of 64); `red` holds NT/64 floats.
-template <int NT>
-Q4_DEV float block_sum(float v, float* red) {
-  v = wave_sum(v);
-  const int w = threadIdx.x >> 6;
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[w] = v;
-  __syncthreads();
-  float s = 0.f;
-#pragma unroll
-  for (int i = 0; i < NT / 64; i++) s += red[i];
-  return s;
-}
-
-// Release the block's global writes, bump `counter`, and report whether this
-// block was the `expected`-th (last) arrival; the last one resets the counter
-// to zero and acquires every earlier arrival's writes.  Whole block must call.
-Q4_DEV bool last_arrival(unsigned* counter, unsigned expected, int* flag_lds) {
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    __threadfence();
-    unsigned prev = atomicAdd(counter, 1u);
-    int last = (prev == expected - 1);
-    if (last) {
-      atomicExch(counter, 0u);
-      __threadfence();
-    }
-    *flag_lds = last;
-  }
-  __syncthreads();
-  bool last = *flag_lds != 0;
-  if (last) __threadfence();
-  return last;
-}
-
 // Orderable key of an fp32 value (larger value -> larger key).
 Q4_DEV uint32_t f32_order_key(float f) {
   uint32_t u = __builtin_bit_cast(uint32_t, f);
