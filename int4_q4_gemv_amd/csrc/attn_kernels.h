@@ -793,6 +793,7 @@ constexpr size_t ds_lds_bytes() {
 template <int D, bool MR = false, bool FIN = false>
 __global__ void __launch_bounds__(256) k_fd_ring_ds(AttnArgs a) {
   static_assert(D >= 128 && D <= 512, "a wave takes whole QK k steps");
+  static_assert(sizeof(AttnArgs) >= 128 + 4, "argument lines fetched below lie inside the struct");
   kernarg_fetch<0, 64, 128>();                // the argument lines this kernel reads
   constexpr int VROW = fd_vpitch<D>();
   constexpr int KS = D / 128;                 // QK k steps of a wave
@@ -1188,6 +1189,7 @@ __device__ __attribute__((always_inline)) inline h8_t lds_tr8(const uint16_t* __
 template <int D, bool VR>
 __global__ void __launch_bounds__(512) k_fd_full_ds(AttnArgs a) {
   static_assert(D == 256 || D == 512, "a wave's k steps pair with their RoPE partners");
+  static_assert(sizeof(AttnArgs) >= 192 + 4, "argument lines fetched below lie inside the struct");
   kernarg_fetch<0, 64, 128, 192>();           // the argument lines this kernel reads
   constexpr int G = 2;                        // wave groups
   constexpr int KS = D / 128;                 // QK k steps of a wave (global step w + 4k)

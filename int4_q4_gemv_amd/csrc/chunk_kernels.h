@@ -523,6 +523,7 @@ struct ChunkFinArgs {
 // row's position.  The products' S runs are added in order first.
 template <int D>
 __global__ void __launch_bounds__(64) k_chunk_finish(ChunkFinArgs a) {
+  static_assert(sizeof(ChunkFinArgs) >= 128 + 4, "argument lines fetched below lie inside the struct");
   kernarg_fetch<0, 64, 128>();                // the argument lines this kernel reads
   constexpr int FE = D / 64, FEH = fin_h<D>();
   const int row = blockIdx.x, job = blockIdx.y;
